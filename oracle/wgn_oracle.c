@@ -1,0 +1,339 @@
+/*
+ * wgn_oracle.c -- plain, slow, obviously-correct CPU oracle for the decode-step
+ * weight stream.  TEST INFRASTRUCTURE ONLY: nothing in the product library
+ * links, includes or calls this file.  It shares no code, header, table or
+ * helper with the HIP path.
+ *
+ * What it computes (all arithmetic in IEEE binary64, sums in sequential k order):
+ *
+ *   RMSNorm   xh_k = R( x_k * (sum_j x_j^2 / K + eps)^(-1/2) * g_k )
+ *             -- "GPU Kernel Optimization" (fused RMSNorm README), section
+ *                "Architecture": mean of squares, reciprocal square root, then
+ *                the per-channel weight.  Also "One Token, Kernel by Kernel",
+ *                section "The setup": the model is RMSNorm-normalised.
+ *   LayerNorm xh_k = R( (x_k - mu) * (var + eps)^(-1/2) * gamma_k + beta_k ),
+ *             mu = mean, var = biased variance
+ *             -- "Making small PyTorch ops faster on a laptop GPU", section
+ *                "Beyond language models": the LayerNorm -> Linear -> GELU chain.
+ *   product   a_n = sum_k W[n][k] * xh_k   (W is [N][K] row-major)
+ *             -- "One Token, Kernel by Kernel", section "What one block
+ *                launches": one matrix-vector product per weight matrix at
+ *                batch 1, BF16 inputs and a wide accumulator.
+ *   epilogue  y = R( residual + epi(a + bias) ),
+ *             epi in { identity, GELU-tanh, SwiGLU: silu(a_gate) * a_up }
+ *             -- same page, "The setup" (SwiGLU MLP) and "What one block
+ *                launches" (the residual add is folded into a neighbouring
+ *                kernel); GELU from "Beyond language models" on the first page.
+ *   LM head   logits_v = sum_k W[v][k] * xh_k (never rounded),
+ *             idx = lowest v attaining the maximum
+ *             -- "One Token, Kernel by Kernel", sections "The setup" (greedy
+ *                argmax of the last logits) and "The whole step" (LM head
+ *                151,936 x 1,536 followed by an argmax).
+ *
+ * R() is round-to-nearest-even to BF16 (FP16 for the standalone FP16 norm rows),
+ * taken directly from the binary64 value (one rounding).  x-hat is rounded to
+ * BF16 before the product: that is the tensor the unfused pipeline stores
+ * between its norm kernel and its GEMV kernel.
+ *
+ * Threading: OpenMP over output rows only; every row's sum is sequential, so
+ * results are bit-identical for any thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- encodings */
+
+/* BF16 bits -> value: the upper half of an IEEE binary32. */
+double wgo_bf16_to_f64(uint16_t h)
+{
+    uint32_t u = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Encode a value that is exactly representable in binary32 and take its upper
+ * 16 bits (exact when the value is representable in BF16). */
+static uint16_t top16_of_float(double v)
+{
+    float f = (float)v;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* Round a binary64 value to the nearest BF16 value, ties to even.
+ * BF16: 8 significant bits, exponent range as binary32, subnormal spacing 2^-133. */
+uint16_t wgo_f64_to_bf16(double v)
+{
+    if (isnan(v)) return (uint16_t)0x7FC0;
+    if (isinf(v)) return v > 0 ? (uint16_t)0x7F80 : (uint16_t)0xFF80;
+    if (v == 0.0) return signbit(v) ? (uint16_t)0x8000 : (uint16_t)0x0000;
+    int ex;
+    (void)frexp(v, &ex);          /* |v| = m * 2^ex, m in [0.5, 1) */
+    int e = ex - 1;               /* floor(log2|v|) */
+    if (e < -126) e = -126;       /* subnormal range: fixed spacing */
+    double ulp = ldexp(1.0, e - 7);
+    double q = rint(v / ulp);     /* default rounding mode: nearest, ties to even */
+    double r = q * ulp;
+    const double maxbf = ldexp(255.0, 127 - 7);   /* (2 - 2^-7) * 2^127 */
+    if (fabs(r) > maxbf) return v > 0 ? (uint16_t)0x7F80 : (uint16_t)0xFF80;
+    if (r == 0.0) return signbit(v) ? (uint16_t)0x8000 : (uint16_t)0x0000;
+    return top16_of_float(r);
+}
+
+/* FP16 bits -> value. */
+double wgo_f16_to_f64(uint16_t h)
+{
+    int s = (h >> 15) & 1, E = (h >> 10) & 0x1F, M = h & 0x3FF;
+    double v;
+    if (E == 0x1F) v = M ? NAN : INFINITY;
+    else if (E == 0) v = ldexp((double)M, -24);
+    else v = ldexp(1024.0 + M, E - 25);
+    return s ? -v : v;
+}
+
+/* Round a binary64 value to the nearest FP16 value, ties to even.
+ * FP16: 11 significant bits, min normal 2^-14, subnormal spacing 2^-24, max 65504. */
+uint16_t wgo_f64_to_f16(double v)
+{
+    if (isnan(v)) return (uint16_t)0x7E00;
+    uint16_t sbit = signbit(v) ? 0x8000 : 0;
+    if (isinf(v)) return sbit | 0x7C00;
+    if (v == 0.0) return sbit;
+    double a = fabs(v);
+    int ex;
+    (void)frexp(a, &ex);
+    int e = ex - 1;
+    if (e < -14) e = -14;
+    double ulp = ldexp(1.0, e - 10);
+    double r = rint(a / ulp) * ulp;
+    if (r > 65504.0) return sbit | 0x7C00;
+    if (r == 0.0) return sbit;
+    (void)frexp(r, &ex);
+    e = ex - 1;
+    if (e < -14) {                                /* subnormal */
+        return sbit | (uint16_t)(r / ldexp(1.0, -24));
+    }
+    uint16_t E = (uint16_t)(e + 15);
+    uint16_t M = (uint16_t)((r / ldexp(1.0, e) - 1.0) * 1024.0);
+    return sbit | (uint16_t)(E << 10) | M;
+}
+
+/* ------------------------------------------------------------ elementwise */
+
+double wgo_gelu_tanh(double z)
+{
+    /* tanh approximation of GELU: 0.5 z (1 + tanh( sqrt(2/pi) (z + 0.044715 z^3) )) */
+    const double c = sqrt(2.0 / M_PI);
+    return 0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z)));
+}
+
+double wgo_silu(double z)
+{
+    return z / (1.0 + exp(-z));
+}
+
+/* ------------------------------------------------------------------ norms */
+
+enum { WGO_NORM_NONE = 0, WGO_NORM_RMS = 1, WGO_NORM_LAYER = 2 };
+enum { WGO_EPI_NONE = 0, WGO_EPI_GELU_TANH = 1, WGO_EPI_SWIGLU = 2 };
+
+/* Normalise one BF16 vector of length K and round the result to BF16.
+ * norm = NONE copies x.  gamma may be NULL (unit gain); beta may be NULL (zero). */
+void wgo_norm_bf16(int norm, const uint16_t *x, const uint16_t *gamma,
+                   const uint16_t *beta, int64_t K, double eps, uint16_t *xh)
+{
+    if (norm == WGO_NORM_NONE) {
+        memcpy(xh, x, (size_t)K * sizeof(uint16_t));
+        return;
+    }
+    if (norm == WGO_NORM_RMS) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = wgo_bf16_to_f64(x[k]);
+            ss += v * v;
+        }
+        double r = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k) {
+            double g = gamma ? wgo_bf16_to_f64(gamma[k]) : 1.0;
+            xh[k] = wgo_f64_to_bf16(wgo_bf16_to_f64(x[k]) * r * g);
+        }
+        return;
+    }
+    /* LayerNorm: mean, then biased variance about the mean (two passes). */
+    double s = 0.0;
+    for (int64_t k = 0; k < K; ++k) s += wgo_bf16_to_f64(x[k]);
+    double mu = s / (double)K;
+    double sv = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double d = wgo_bf16_to_f64(x[k]) - mu;
+        sv += d * d;
+    }
+    double r = 1.0 / sqrt(sv / (double)K + eps);
+    for (int64_t k = 0; k < K; ++k) {
+        double g = gamma ? wgo_bf16_to_f64(gamma[k]) : 1.0;
+        double b = beta ? wgo_bf16_to_f64(beta[k]) : 0.0;
+        xh[k] = wgo_f64_to_bf16((wgo_bf16_to_f64(x[k]) - mu) * r * g + b);
+    }
+}
+
+/* Un-rounded statistics helper used by the pin tests: returns the binary64
+ * normalised value before the final rounding (gain applied). */
+void wgo_norm_f64(int norm, const uint16_t *x, const uint16_t *gamma,
+                  const uint16_t *beta, int64_t K, double eps, double *out)
+{
+    if (norm == WGO_NORM_NONE) {
+        for (int64_t k = 0; k < K; ++k) out[k] = wgo_bf16_to_f64(x[k]);
+        return;
+    }
+    if (norm == WGO_NORM_RMS) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) { double v = wgo_bf16_to_f64(x[k]); ss += v * v; }
+        double r = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k)
+            out[k] = wgo_bf16_to_f64(x[k]) * r * (gamma ? wgo_bf16_to_f64(gamma[k]) : 1.0);
+        return;
+    }
+    double s = 0.0;
+    for (int64_t k = 0; k < K; ++k) s += wgo_bf16_to_f64(x[k]);
+    double mu = s / (double)K, sv = 0.0;
+    for (int64_t k = 0; k < K; ++k) { double d = wgo_bf16_to_f64(x[k]) - mu; sv += d * d; }
+    double r = 1.0 / sqrt(sv / (double)K + eps);
+    for (int64_t k = 0; k < K; ++k)
+        out[k] = (wgo_bf16_to_f64(x[k]) - mu) * r * (gamma ? wgo_bf16_to_f64(gamma[k]) : 1.0)
+                 + (beta ? wgo_bf16_to_f64(beta[k]) : 0.0);
+}
+
+/* ---------------------------------------------------------------- product */
+
+static int g_threads = 1;
+
+void wgo_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
+
+int wgo_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* acc[n] = sum_k W[n][k] * xh[k] for rows n in [0, N), sequential in k. */
+void wgo_matvec(const uint16_t *W, int64_t N, int64_t K, const uint16_t *xh, double *acc)
+{
+    double *xv = (double *)malloc((size_t)K * sizeof(double));
+    for (int64_t k = 0; k < K; ++k) xv[k] = wgo_bf16_to_f64(xh[k]);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+#endif
+    for (int64_t n = 0; n < N; ++n) {
+        const uint16_t *row = W + n * K;
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k) s += wgo_bf16_to_f64(row[k]) * xv[k];
+        acc[n] = s;
+    }
+    free(xv);
+}
+
+/* Same product for selected rows only (sampled parity at full size). */
+void wgo_matvec_rows(const uint16_t *W, int64_t K, const int64_t *rows, int64_t nrows,
+                     const uint16_t *xh, double *acc)
+{
+    for (int64_t i = 0; i < nrows; ++i) {
+        const uint16_t *row = W + rows[i] * K;
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k) s += wgo_bf16_to_f64(row[k]) * wgo_bf16_to_f64(xh[k]);
+        acc[i] = s;
+    }
+}
+
+/* ------------------------------------------------------------------ stage */
+
+/*
+ * One norm-fused product stage over `batch` activation rows.
+ *   x        [batch][x_stride] BF16, K used
+ *   W, W_up  [N][K] BF16 (W_up only for SwiGLU)
+ *   bias     [N] BF16 or NULL (added to the first accumulator)
+ *   residual [batch][res_stride] BF16 or NULL
+ *   y        [batch][y_stride] BF16 out
+ *   xh_out   [batch][K] BF16 out (the rounded normalised input), may be NULL
+ *   acc_out  [batch][N] binary64 out (epilogue input a+bias, or the gate value for
+ *            SwiGLU), may be NULL
+ */
+void wgo_stage(int norm, int epi, int64_t N, int64_t K, int64_t batch,
+               const uint16_t *x, int64_t x_stride,
+               const uint16_t *gamma, const uint16_t *beta, double eps,
+               const uint16_t *W, const uint16_t *W_up, const uint16_t *bias,
+               const uint16_t *residual, int64_t res_stride,
+               uint16_t *y, int64_t y_stride, uint16_t *xh_out, double *acc_out)
+{
+    uint16_t *xh = (uint16_t *)malloc((size_t)K * sizeof(uint16_t));
+    double *a = (double *)malloc((size_t)N * sizeof(double));
+    double *u = (epi == WGO_EPI_SWIGLU) ? (double *)malloc((size_t)N * sizeof(double)) : NULL;
+    for (int64_t b = 0; b < batch; ++b) {
+        wgo_norm_bf16(norm, x + b * x_stride, gamma, beta, K, eps, xh);
+        if (xh_out) memcpy(xh_out + b * K, xh, (size_t)K * sizeof(uint16_t));
+        wgo_matvec(W, N, K, xh, a);
+        if (u) wgo_matvec(W_up, N, K, xh, u);
+        for (int64_t n = 0; n < N; ++n) {
+            double z = a[n] + (bias ? wgo_bf16_to_f64(bias[n]) : 0.0);
+            double e;
+            if (epi == WGO_EPI_GELU_TANH) e = wgo_gelu_tanh(z);
+            else if (epi == WGO_EPI_SWIGLU) e = wgo_silu(z) * u[n];
+            else e = z;
+            if (residual) e += wgo_bf16_to_f64(residual[b * res_stride + n]);
+            y[b * y_stride + n] = wgo_f64_to_bf16(e);
+            if (acc_out) acc_out[b * N + n] = z;
+        }
+    }
+    free(xh); free(a); free(u);
+}
+
+/*
+ * Final RMSNorm + LM head + greedy argmax.
+ *   h [batch][h_stride] BF16, g [K] BF16, W [V][K] BF16
+ *   idx [batch] (lowest index attaining the maximum), maxv [batch],
+ *   logits [batch][V] binary64 (may be NULL)
+ */
+void wgo_lmhead_argmax(int norm, const uint16_t *h, int64_t h_stride, const uint16_t *g,
+                       double eps, const uint16_t *W, int64_t V, int64_t K, int64_t batch,
+                       int32_t *idx, double *maxv, double *logits)
+{
+    uint16_t *xh = (uint16_t *)malloc((size_t)K * sizeof(uint16_t));
+    double *l = (double *)malloc((size_t)V * sizeof(double));
+    for (int64_t b = 0; b < batch; ++b) {
+        wgo_norm_bf16(norm, h + b * h_stride, g, NULL, K, eps, xh);
+        wgo_matvec(W, V, K, xh, l);
+        int64_t best = 0;
+        for (int64_t v = 1; v < V; ++v)
+            if (l[v] > l[best]) best = v;        /* strict: ties keep the lowest index */
+        idx[b] = (int32_t)best;
+        maxv[b] = l[best];
+        if (logits) memcpy(logits + b * V, l, (size_t)V * sizeof(double));
+    }
+    free(xh); free(l);
+}
+
+/* Standalone RMSNorm over FP16 rows: y = R16( x * (mean x^2 + eps)^(-1/2) * g ). */
+void wgo_rmsnorm_rows_f16(const uint16_t *x, int64_t x_stride, const uint16_t *g, double eps,
+                          uint16_t *y, int64_t y_stride, int64_t rows, int64_t K)
+{
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+#endif
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t *xr = x + r * x_stride;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) { double v = wgo_f16_to_f64(xr[k]); ss += v * v; }
+        double inv = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k)
+            y[r * y_stride + k] = wgo_f64_to_f16(wgo_f16_to_f64(xr[k]) * inv * wgo_f16_to_f64(g[k]));
+    }
+}
