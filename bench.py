@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode-step weight stream on one MI355X.
+
+Default workload: one decode step of the 28-layer, hidden-1536 Llama-class
+decoder (BF16 weights, 3.09 GB) with final RMSNorm, 151936 x 1536 LM head and
+argmax, batch 1 -- one persistent kernel launch per step.  Inputs are seeded
+synthetic tensors already resident in HBM when timing starts.
+
+Prints ONE JSON line (rank 0) with the measured throughput (algorithmic bytes /
+step time), the roofline of the dominant kernel and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = ("decode-step weight-stream µs and achieved HBM GB/s (% of peak), "
+          "1.5B shapes, batch 1")
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_step_1536x28",
+                    choices=["decode_step_1536x28", "decoder_block_1536", "ln_gelu_chain_768x72",
+                             "rmsnorm_gemv_256", "rmsnorm_rows_960x1536_f16", "lmhead_151936"])
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--mode", type=int, default=0, help="0 persistent kernel, 1 one launch per phase")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="stream a 512 MB scrub buffer between timed steps (evicts the Infinity Cache)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the weight stream runs on a single "
+              "device); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import weight_gemv_norm_amd as W
+    from weight_gemv_norm_amd import steps
+    from synth import gen
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    wl = args.workload
+    B = args.batch if args.batch is not None else (4 if wl == "ln_gelu_chain_768x72" else 1)
+    print("[bench] workload %s batch %d mode %d" % (wl, B, args.mode), file=sys.stderr, flush=True)
+
+    # ----------------------------------------------------------- build work
+    chain = None
+    launch = None
+    nbytes = 0
+    cfg = {"workload": wl, "batch": B}
+    kernel_name = "chain_kernel"
+    if wl in ("decode_step_1536x28", "decoder_block_1536"):
+        inp = gen.make_stage_tensors(wl, device=dev, batch=B)
+        stages, bufs = steps.decoder_stages(inp, dev)
+        chain = W.Chain(stages, B, mode=args.mode)
+        nb = steps.decode_step_bytes(inp)
+        nbytes = nb["total"]
+        cfg.update({"hidden": gen.H, "intermediate": gen.I, "layers": len(inp["layers"]),
+                    "vocab": gen.V if "W_lm" in inp else None, "weight_bytes": nb["weights"],
+                    "algorithmic_bytes": nbytes, "phases": chain.num_phases,
+                    "launch": "persistent" if args.mode == 0 else "per-phase"})
+        launch = chain.run
+    elif wl == "ln_gelu_chain_768x72":
+        inp = gen.make_stage_tensors(wl, device=dev, batch=B)
+        stages, bufs = steps.ln_gelu_chain_stages(inp, dev)
+        chain = W.Chain(stages, B, mode=args.mode)
+        nbytes = sum(L["W"].numel() * 2 + (L["bias"].numel() + L["gamma"].numel() + L["beta"].numel()) * 2
+                     for L in inp["layers"]) + (len(inp["layers"]) + 1) * B * 768 * 2
+        cfg.update({"width": 768, "blocks": 72, "algorithmic_bytes": nbytes, "phases": chain.num_phases,
+                    "launch": "persistent" if args.mode == 0 else "per-phase"})
+        launch = chain.run
+    elif wl == "rmsnorm_gemv_256":
+        t = gen.make_stage_tensors(wl, device=dev, batch=B)
+        y = torch.empty((B, 256), dtype=torch.bfloat16, device=dev)
+        st = W.make_stage(t["W"], t["x"], y, norm=1, eps=t["eps"], gamma=t["g"])
+        nbytes = 256 * 256 * 2 + 256 * 2 + 2 * B * 256 * 2
+        cfg.update({"N": 256, "K": 256, "algorithmic_bytes": nbytes})
+        launch = lambda: W.gemv_norm(st, B)  # noqa: E731
+    elif wl == "lmhead_151936":
+        h = gen.normal((B, gen.H), 1.0, 1, device=dev)
+        g = gen.normal((gen.H,), 0.1, 2, mean=1.0, device=dev)
+        Wl = gen.normal((gen.V, gen.H), 0.02, 3, device=dev)
+        idx = torch.empty((B,), dtype=torch.int32, device=dev)
+        ws = W.workspace(W.lmhead_argmax_workspace_bytes(B))
+        nbytes = gen.V * gen.H * 2 + gen.H * 2 + B * gen.H * 2 + B * 4
+        cfg.update({"V": gen.V, "K": gen.H, "algorithmic_bytes": nbytes})
+        launch = lambda: W.lmhead_argmax(h, g, 1e-6, Wl, idx, ws=ws)  # noqa: E731
+    elif wl == "rmsnorm_rows_960x1536_f16":
+        t = gen.make_stage_tensors(wl, device=dev)
+        y = torch.empty_like(t["x"])
+        nbytes = 2 * 960 * 1536 * 2 + 1536 * 2
+        cfg.update({"rows": 960, "K": 1536, "dtype": "f16", "algorithmic_bytes": nbytes})
+        launch = lambda: W.rmsnorm_rows(t["x"], t["g"], t["eps"], y)  # noqa: E731
+        kernel_name = "rmsnorm_rows_kernel"
+
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+
+    # -------------------------------------------------------------- warm up
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    if chain is not None:
+        chain.check()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    # --------------------------------------------------------------- timing
+    stream = torch.cuda.current_stream()
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_all0.record(stream)
+    for i in range(K):
+        if scrub is not None:
+            scrub.add_(1)
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    if chain is not None:
+        chain.check()
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e3  # us
+    total_ms = t_all0.elapsed_time(t_all1)
+    us_step = float(np.mean(per))
+    us_med = float(np.median(per))
+    ms_per_step = total_ms / K if scrub is None else us_step / 1e3
+    gbs = nbytes / (us_step * 1e-6) / 1e9
+    print("[bench] timed %d steps: mean %.2f us, median %.2f us, min %.2f us, wall %.3f s"
+          % (K, us_step, us_med, float(per.min()), wall1 - wall0), file=sys.stderr, flush=True)
+
+    roofline = {"bound": "hbm", "kernel": kernel_name, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "traffic": None, "launch_us_mean": round(us_step, 3), "launch_us_median": round(us_med, 3),
+                "bytes_per_launch": nbytes}
+
+    # ----------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline and wl == "decode_step_1536x28":
+        cpu = cpu_baseline_decode(inp, bufs, nbytes)
+
+    out = {
+        "metric": METRIC if wl == "decode_step_1536x28" and B == 1 else METRIC.replace("batch 1", "batch %d" % B)
+        if wl == "decode_step_1536x28" else "%s weight-stream GB/s" % wl,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_step": round(us_step, 3),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normals, shapes of the pages' workload; no trained weights)",
+        "config": cfg,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "cold": bool(args.cold),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_decode(inp, bufs, nbytes):
+    """Time the CPU oracle (as it stands) on one full decode step of the same
+    workload: all 28 blocks and the LM head, free-running on its own outputs."""
+    from oracle import oracle as O
+    from synth.gen import bf16_bits_to_numpy as bb
+    print("[bench] cpu baseline: copying weights to host", file=sys.stderr, flush=True)
+    layers = [{k: bb(v) for k, v in L.items()} for L in inp["layers"]]
+    g_f, W_lm, h0 = bb(inp["g_f"]), bb(inp["W_lm"]), bb(inp["h"])
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    O.set_threads(threads)
+    eps = float(np.float32(inp["eps"]))
+    t0 = time.perf_counter()
+    h = h0
+    for L in layers:
+        for name in ("wq", "wk", "wv"):
+            O.stage(h, L[name], norm=O.NORM_RMS, eps=eps, gamma=L["g1"])
+        h1 = O.stage(L["a"], L["wo"], residual=h)
+        s = O.stage(h1, L["wg"], norm=O.NORM_RMS, eps=eps, gamma=L["g2"], epi=O.EPI_SWIGLU, W_up=L["wu"])
+        h = O.stage(s, L["wd"], residual=h1)
+    idx, _ = O.lmhead_argmax(h, g_f, W_lm, eps=eps)
+    dt = time.perf_counter() - t0
+    print("[bench] cpu baseline: one step %.2f s on %d threads" % (dt, threads), file=sys.stderr, flush=True)
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds_per_step": round(dt, 3),
+            "sample": "one full decode step (28 blocks + LM head + argmax, batch 1) free-running in the "
+                      "binary64 C oracle, OpenMP over rows"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * wgn.h -- C ABI of libwgn.so, the MI355X (gfx950) decode-step weight stream.
+ *
+ * The library computes chains of norm-fused weight-matrix x activation-vector
+ * products at batch 1..16, the way a batch-1 decode step spends nearly all of
+ * its time ("One Token, Kernel by Kernel: A Decode Step on a Laptop GPU",
+ * sections "TL;DR", "What one block launches" and "Step 2: every kernel class
+ * on the roofline": the weight matrix-vector products dominate the step and
+ * are bound by memory bandwidth).
+ *
+ * Conventions shared by every entry point
+ *  - Storage: BF16 values as 16-bit IEEE bfloat16 bit patterns; weights are
+ *    [N][K] row-major (K contiguous), activations are [batch][stride].
+ *  - Arithmetic: the normalised input x-hat is computed in FP32 and rounded once
+ *    to BF16; products accumulate in FP32 in an order fixed by the launch
+ *    configuration (so repeated calls are bit-identical); every epilogue runs on
+ *    the un-rounded FP32 accumulator and the stored output is rounded exactly
+ *    once (round to nearest even).
+ *  - Ownership: the caller owns every buffer (weights, activations, outputs,
+ *    workspace).  The library never allocates device memory inside a call and
+ *    keeps no hidden state other than its loaded kernels.
+ *  - Streams: every call is asynchronous on the caller's stream (a hipStream_t
+ *    passed as `wgn_stream`; NULL = the default stream) and reads no device
+ *    value on the host, except wgn_chain_create (one upload) and
+ *    wgn_chain_check (synchronises).
+ *  - Errors: every check runs on the host before anything is enqueued; a failed
+ *    check returns a negative wgn_status and enqueues nothing.  A failing HIP
+ *    launch returns WGN_E_HIP.  NaN/Inf inputs are not checked.
+ *  - Alignment: W, W_up, x, gamma and beta must be 16-byte aligned and x's row
+ *    stride a multiple of 8 elements (they are read with 128-bit loads); other
+ *    pointers need their element's natural alignment; K must be a multiple of 8.
+ *  - Workspace: device memory of at least wgn_*_workspace_bytes() bytes,
+ *    256-byte aligned, zero-filled once by the caller when allocated.  Calls
+ *    leave its counters at zero, so it can be reused and graph-captured.
+ *    Concurrent calls must not share a workspace.
+ */
+#ifndef WGN_H
+#define WGN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *wgn_stream; /* a hipStream_t */
+
+typedef enum wgn_status {
+    WGN_OK = 0,
+    WGN_E_ARG = -1,         /* null pointer, bad size, bad enum value */
+    WGN_E_ALIGN = -2,       /* pointer or stride violates the alignment rules */
+    WGN_E_UNSUPPORTED = -3, /* valid request this build does not implement */
+    WGN_E_WORKSPACE = -4,   /* workspace missing, misaligned or too small */
+    WGN_E_HIP = -5,         /* a HIP runtime call failed */
+    WGN_E_DEVICE = -6,      /* no usable gfx950 device */
+    WGN_E_TIMEOUT = -7      /* an in-kernel wait hit its bound (see wgn_chain_check) */
+} wgn_status;
+
+/* Normalisation prologue applied to a stage's input vector(s).
+ *  RMS:   x-hat = x * (mean(x^2) + eps)^(-1/2) * gamma
+ *         ("GPU Kernel Optimization" README, section "Architecture";
+ *          "One Token, Kernel by Kernel", section "The setup")
+ *  LAYER: x-hat = (x - mean) * (biased var + eps)^(-1/2) * gamma + beta
+ *         ("Making small PyTorch ops faster on a laptop GPU", section
+ *          "Beyond language models")
+ *  NONE:  x-hat = x                                                        */
+typedef enum wgn_norm_kind { WGN_NORM_NONE = 0, WGN_NORM_RMS = 1, WGN_NORM_LAYER = 2 } wgn_norm_kind;
+
+/* Epilogue on the FP32 accumulator a = W . x-hat (+ bias):
+ *  NONE:      y = R(residual + a)
+ *  GELU_TANH: y = R(residual + 0.5 a (1 + tanh(sqrt(2/pi)(a + 0.044715 a^3))))
+ *  SWIGLU:    y = R(residual + silu(a) * (W_up . x-hat)),  silu(z) = z / (1 + e^-z)
+ *             ("One Token, Kernel by Kernel", section "The setup": SwiGLU MLP)
+ *  ARGMAX:    logits = a (FP32, never rounded); y is int32 [batch]: the lowest
+ *             index attaining each row's maximum ("One Token, Kernel by
+ *             Kernel", sections "The setup" and "The whole step": LM head
+ *             followed by a greedy argmax over the logits)
+ * R() = round to nearest even BF16; residual is optional (NULL = 0).       */
+typedef enum wgn_epi_kind {
+    WGN_EPI_NONE = 0, WGN_EPI_GELU_TANH = 1, WGN_EPI_SWIGLU = 2, WGN_EPI_ARGMAX = 3
+} wgn_epi_kind;
+
+typedef enum wgn_dtype { WGN_BF16 = 0, WGN_FP16 = 1, WGN_FP32 = 2 } wgn_dtype;
+
+/* One norm-fused product stage: y = R(residual + epi(W . norm(x) + bias)). */
+typedef struct wgn_stage {
+    int32_t N;            /* output rows (weight rows), >= 1                          */
+    int32_t K;            /* input length, >= 8, multiple of 8                        */
+    const void *W;        /* [N][K] BF16 row-major                                    */
+    const void *W_up;     /* SWIGLU only: the "up" [N][K] BF16 matrix; else NULL      */
+    const void *bias;     /* [N] BF16 added to the accumulator, or NULL (not SWIGLU)  */
+    int32_t norm;         /* wgn_norm_kind                                            */
+    float eps;            /* norm epsilon                                             */
+    const void *gamma;    /* [K] BF16 gain (RMS, LAYER) or NULL = 1                   */
+    const void *beta;     /* [K] BF16 shift (LAYER) or NULL = 0                       */
+    int32_t epi;          /* wgn_epi_kind                                             */
+    const void *x;        /* [batch][x_stride] BF16 input                             */
+    int64_t x_stride;     /* elements between batch rows of x                         */
+    const void *residual; /* [batch][res_stride] BF16 or NULL (not ARGMAX)            */
+    int64_t res_stride;
+    void *y;              /* [batch][y_stride] BF16 output; ARGMAX: int32 [batch]     */
+    int64_t y_stride;     /* elements between batch rows of y (ignored for ARGMAX)    */
+    float *logits;        /* ARGMAX only: optional FP32 [batch][N] logits, or NULL    */
+    float *maxval;        /* ARGMAX only: optional FP32 [batch] maxima, or NULL       */
+} wgn_stage;
+
+/* ---------------------------------------------------------------- info */
+const char *wgn_status_string(int32_t status);
+int32_t wgn_version(void);
+/* Text of the last failing HIP call on this thread ("" if none): which call,
+ * the runtime's message and code.  Valid until the next failure. */
+const char *wgn_last_hip_error(void);
+/* Number of compute units of the current device (0 if none). */
+int32_t wgn_device_cu_count(void);
+
+/* ---------------------------------------------------------- one stage */
+/* Workspace bytes wgn_gemv_norm needs for this stage at this batch
+ * (0 unless epi == ARGMAX). */
+size_t wgn_gemv_norm_workspace_bytes(const wgn_stage *stage, int32_t batch);
+
+/* One norm-fused product, one kernel launch.  batch in [1, 16]; batch rows of
+ * x, residual and y are independent.  The normalisation prologue is computed
+ * by every workgroup from the whole input vector, so there is no separate
+ * norm kernel.  Returns WGN_OK or an error (nothing enqueued on error). */
+wgn_status wgn_gemv_norm(const wgn_stage *stage, int32_t batch,
+                         void *workspace, size_t ws_bytes, wgn_stream stream);
+
+/* Final norm + LM head + argmax in one launch ("One Token, Kernel by Kernel",
+ * section "The whole step").  h: [batch][h_stride] BF16; gamma: [K] BF16
+ * (RMS gain) or NULL for no norm; W_lm: [V][K] BF16.  Writes idx_out[batch]
+ * (int32, lowest index of the maximum), and optionally max_out[batch] and
+ * logits_out[batch][V] (FP32). */
+size_t wgn_lmhead_argmax_workspace_bytes(int32_t batch);
+wgn_status wgn_lmhead_argmax(const void *h, int64_t h_stride, int32_t batch, int32_t K,
+                             const void *gamma, float eps, const void *W_lm, int32_t V,
+                             int32_t *idx_out, float *max_out, float *logits_out,
+                             void *workspace, size_t ws_bytes, wgn_stream stream);
+
+/* Standalone RMSNorm over `rows` rows of length K, FP16 or BF16 in and out,
+ * FP32 statistics, one rounding ("GPU Kernel Optimization" README, section
+ * "Architecture": one program per row).  y may not alias x. */
+wgn_status wgn_rmsnorm_rows(const void *x, int64_t x_stride, const void *gamma, float eps,
+                            void *y, int64_t y_stride, int32_t rows, int32_t K,
+                            int32_t dtype, wgn_stream stream);
+
+/* --------------------------------------------------------------- chains */
+/* A chain is a list of stages in dependency order (a stage may read earlier
+ * stages' outputs), tuned and laid out once and then run many times, like the
+ * stage-list wrapper of "Making small PyTorch ops faster on a laptop GPU",
+ * section "Beyond language models".  Maximal runs of consecutive stages that
+ * do not touch each other's outputs form one phase; phases are separated by
+ * device-side completion counters inside one persistent kernel (mode 0) or by
+ * kernel boundaries (mode 1).  Weights must not be written by any stage.
+ * Every stage writes its own output buffer. */
+typedef struct wgn_chain wgn_chain;
+
+typedef struct wgn_chain_opts {
+    int32_t mode;        /* 0: one persistent launch (default); 1: one launch per phase */
+    int32_t grid;        /* workgroups; 0 = one per compute unit                       */
+    int32_t reserved[6]; /* must be zero                                               */
+} wgn_chain_opts;
+
+/* Workspace bytes for a chain over these stages (mode/grid as in opts, NULL = defaults). */
+size_t wgn_chain_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch,
+                                 const wgn_chain_opts *opts);
+
+/* Validate, group into phases, lay the device program out in the workspace
+ * (one host->device copy on `stream`, then a stream synchronisation) and
+ * return a host handle.  The stage buffers must stay valid while the chain is
+ * used.  Not for the hot loop. */
+wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t batch,
+                            const wgn_chain_opts *opts, void *workspace, size_t ws_bytes,
+                            wgn_stream stream, wgn_chain **out);
+
+/* Enqueue one run of the chain on `stream` (no host synchronisation). */
+wgn_status wgn_chain_run(const wgn_chain *chain, wgn_stream stream);
+
+/* Synchronise `stream` and report WGN_E_TIMEOUT if an in-kernel wait of an
+ * earlier run hit its bound (the counters are then reset); else WGN_OK. */
+wgn_status wgn_chain_check(const wgn_chain *chain, wgn_stream stream);
+
+int32_t wgn_chain_num_phases(const wgn_chain *chain);
+/* Phase index of each stage (array of n_stages). */
+wgn_status wgn_chain_stage_phases(const wgn_chain *chain, int32_t *phase_of_stage);
+void wgn_chain_destroy(wgn_chain *chain);
+
+/* create + run + destroy in one call (the create step synchronises `stream`). */
+wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t batch,
+                           const wgn_chain_opts *opts, void *workspace, size_t ws_bytes,
+                           wgn_stream stream);
+
+/* --------------------------------------------------------- host helpers */
+/* The first wave of `waves` whose even share of `units` work units contains
+ * unit `u` (exported so the partition rule can be tested on the host). */
+int32_t wgn_first_wave_of_unit(int32_t u, int32_t units, int32_t waves);
+
+/* Plan a chain on the host only (no device needed) for `grid` workgroups and
+ * emulate every workgroup and wave of its work partition: each weight unit must
+ * be streamed exactly once, each partial-sum slot written once and read by the
+ * epilogue, each row owned by one workgroup.  Returns the number of violations
+ * (0 = consistent) or a negative wgn_status if planning failed. */
+int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_t batch, int32_t grid);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WGN_H */

@@ -1,0 +1,184 @@
+"""GPU parity of whole chains (persistent kernel and one-launch-per-phase), per
+stage and teacher-forced, against the CPU oracle; plus the invariants the
+pages rely on: repeated runs and the two launch modes give the same bits."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from synth import gen
+from tests.gpu_util import assert_close_bf16, bits, check_argmax, say
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import weight_gemv_norm_amd as W
+    from weight_gemv_norm_amd import steps
+    from weight_gemv_norm_amd import _lib as L
+
+DEV = "cuda"
+EPS32 = float(np.float32(1e-6))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.lib()
+    yield
+
+
+def rows_sample(N, k=48, seed=0):
+    rng = np.random.default_rng(seed + N)
+    r = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, k)]))
+    return r
+
+
+def check_stage_rows(what, W_, x, y, rows=None, **kw):
+    """Oracle on the GPU's inputs; all rows, or the given row sample."""
+    Wb = W_ if rows is None else W_[torch.as_tensor(rows, device=DEV)]
+    up = kw.pop("W_up", None)
+    if up is not None and rows is not None:
+        up = up[torch.as_tensor(rows, device=DEV)]
+    res = kw.pop("residual", None)
+    if res is not None and rows is not None:
+        res = res[:, torch.as_tensor(rows, device=DEV)].contiguous()
+    g = kw.pop("gamma", None)
+    ref = O.stage(bits(x.contiguous()), bits(Wb.contiguous()), gamma=None if g is None else bits(g),
+                  W_up=None if up is None else bits(up.contiguous()),
+                  residual=None if res is None else bits(res), **kw)
+    yb = bits(y if rows is None else y[:, torch.as_tensor(rows, device=DEV)].contiguous())
+    return assert_close_bf16(yb, ref, what)
+
+
+def check_decoder(inp, bufs, layers_full, sample_other=True):
+    """Per-stage teacher-forced check of a decode step's buffers."""
+    worst = 0.0
+    for l, Ld in enumerate(inp["layers"]):
+        full = l in layers_full
+        if not full and not sample_other:
+            continue
+        h, h1, s, hn = bufs["h"][l], bufs["h1"][l], bufs["s"][l], bufs["h"][l + 1]
+        pick = (lambda N: None) if full else (lambda N: rows_sample(N, seed=l))
+        for name, key in (("q", "wq"), ("k", "wk"), ("v", "wv")):
+            worst = max(worst, check_stage_rows("L%d %s" % (l, name), Ld[key], h, bufs[name][l],
+                                                rows=pick(Ld[key].shape[0]), norm=O.NORM_RMS, eps=EPS32,
+                                                gamma=Ld["g1"]))
+        worst = max(worst, check_stage_rows("L%d o" % l, Ld["wo"], Ld["a"], h1, rows=pick(Ld["wo"].shape[0]),
+                                            norm=O.NORM_NONE, residual=h))
+        worst = max(worst, check_stage_rows("L%d gate/up" % l, Ld["wg"], h1, s, rows=pick(Ld["wg"].shape[0]),
+                                            norm=O.NORM_RMS, eps=EPS32, gamma=Ld["g2"], epi=O.EPI_SWIGLU,
+                                            W_up=Ld["wu"]))
+        worst = max(worst, check_stage_rows("L%d down" % l, Ld["wd"], s, hn, rows=pick(Ld["wd"].shape[0]),
+                                            norm=O.NORM_NONE, residual=h1))
+    if "W_lm" in inp:
+        hL = bufs["h"][-1]
+        ridx, rmx, rlog = O.lmhead_argmax(bits(hL), bits(inp["g_f"]), bits(inp["W_lm"]), eps=EPS32,
+                                          want_logits=True)
+        for b in range(hL.shape[0]):
+            check_argmax(int(bufs["idx"][b]), rlog[b], "lm head b=%d" % b)
+    return worst
+
+
+def snapshot(bufs):
+    out = []
+    for k in sorted(bufs):
+        v = bufs[k]
+        for t in (v if isinstance(v, list) else [v]):
+            if t is not None:
+                out.append(t.detach().clone())
+    return out
+
+
+def same_bits(a, b):
+    return all(torch.equal(x.view(torch.int8) if x.dtype != torch.int32 else x,
+                           y.view(torch.int8) if y.dtype != torch.int32 else y) for x, y in zip(a, b))
+
+
+# ---------------------------------------------------------------- workloads
+def test_decoder_block_1536_batch1():
+    """One Llama-style block at hidden 1536, batch 1: three phases."""
+    say("chain decoder_block_1536 B=1")
+    inp = gen.make_stage_tensors("decoder_block_1536", device=DEV)
+    stages, bufs = steps.decoder_stages(inp, DEV)
+    ch = W.Chain(stages, 1)
+    assert ch.num_phases == 3
+    assert ch.stage_phases() == [0, 0, 0, 0, 1, 2]
+    ch.run()
+    ch.check()
+    check_decoder(inp, bufs, layers_full={0})
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4])
+def test_small_decode_step_all_batches(B):
+    """Two full-width blocks + an LM head of 20000 rows, both launch modes."""
+    say("chain decode_step 2 layers V=20000 B=%d" % B)
+    inp = gen.make_stage_tensors("decode_step_1536x28", device=DEV, batch=B, n_layers=2, vocab=20000)
+    stages, bufs = steps.decoder_stages(inp, DEV)
+    ch = W.Chain(stages, B, mode=0)
+    assert ch.num_phases == 7
+    ch.run()
+    ch.check()
+    check_decoder(inp, bufs, layers_full={0, 1})
+    first = snapshot(bufs)
+    ch.run()
+    ch.check()
+    assert same_bits(first, snapshot(bufs)), "persistent rerun not bit-identical"
+    ch1 = W.Chain(stages, B, mode=1)
+    ch1.run()
+    torch.cuda.synchronize()
+    assert same_bits(first, snapshot(bufs)), "per-phase launches differ from the persistent kernel"
+
+
+@pytest.mark.parametrize("B", [4])
+def test_ln_gelu_chain_768x72(B):
+    """72 x [LayerNorm(768) -> Linear -> GELU-tanh], seeded LN params, per stage."""
+    say("chain ln_gelu_chain_768x72 B=%d" % B)
+    inp = gen.make_stage_tensors("ln_gelu_chain_768x72", device=DEV, batch=B, seeded_ln_params=True)
+    stages, bufs = steps.ln_gelu_chain_stages(inp, DEV)
+    ch = W.Chain(stages, B)
+    assert ch.num_phases == 72
+    ch.run()
+    ch.check()
+    xs = bufs["x"]
+    for i, Ld in enumerate(inp["layers"]):
+        ref = O.stage(bits(xs[i]), bits(Ld["W"]), norm=O.NORM_LAYER, eps=float(np.float32(1e-5)),
+                      gamma=bits(Ld["gamma"]), beta=bits(Ld["beta"]), bias=bits(Ld["bias"]),
+                      epi=O.EPI_GELU_TANH)
+        assert_close_bf16(bits(xs[i + 1]), ref, "ln-gelu layer %d" % i)
+
+
+def test_ln_gelu_chain_default_params():
+    """Default-initialised LayerNorm (gain 1, shift 0), batch 4, the benchmark's configuration."""
+    say("chain ln_gelu_chain_768x72 default LN B=4")
+    inp = gen.make_stage_tensors("ln_gelu_chain_768x72", device=DEV, batch=4)
+    stages, bufs = steps.ln_gelu_chain_stages(inp, DEV)
+    ch = W.Chain(stages, 4)
+    ch.run()
+    ch.check()
+    xs = bufs["x"]
+    for i in (0, 35, 71):
+        Ld = inp["layers"][i]
+        ref = O.stage(bits(xs[i]), bits(Ld["W"]), norm=O.NORM_LAYER, eps=float(np.float32(1e-5)),
+                      gamma=bits(Ld["gamma"]), beta=bits(Ld["beta"]), bias=bits(Ld["bias"]),
+                      epi=O.EPI_GELU_TANH)
+        assert_close_bf16(bits(xs[i + 1]), ref, "ln-gelu layer %d" % i)
+
+
+def test_full_decode_step_batch1():
+    """The 28-layer, 151936-vocab decode step at batch 1 in the benchmark's launch
+    configuration: layers 0, 13, 27 and the LM head checked in full, every other
+    stage on sampled rows."""
+    say("chain decode_step_1536x28 full B=1")
+    inp = gen.make_stage_tensors("decode_step_1536x28", device=DEV, batch=1)
+    stages, bufs = steps.decoder_stages(inp, DEV)
+    ch = W.Chain(stages, 1)
+    assert ch.num_phases == 28 * 3 + 1
+    ch.run()
+    ch.check()
+    first = snapshot(bufs)
+    check_decoder(inp, bufs, layers_full={0, 13, 27})
+    for _ in range(2):
+        ch.run()
+    ch.check()
+    assert same_bits(first, snapshot(bufs)), "decode step rerun not bit-identical"

@@ -1,0 +1,220 @@
+"""Host-side tests of libwgn.so (no GPU): the library loads, exports every
+symbol include/wgn.h declares, validates arguments before touching the device,
+and plans a work partition that covers every weight unit exactly once."""
+import os
+import re
+
+import pytest
+
+from weight_gemv_norm_amd import _lib as L
+from weight_gemv_norm_amd.api import partition_selftest, first_wave_of_unit
+from synth import gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "wgn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(wgn_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    names = header_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(0, -8, -1):
+        assert L.status_string(s) and L.status_string(s) != "unknown status"
+    assert L.status_string(-99) == "unknown status"
+
+
+def test_first_wave_formula_brute_force():
+    for U in range(1, 80):
+        for W in (1, 2, 3, 7, 8):
+            owner = []
+            for w in range(W):
+                if U >= W:
+                    lo, hi = (w * U) // W, ((w + 1) * U) // W
+                    assert hi > lo  # no empty wave when there is enough work
+                else:
+                    lo, hi = min(w, U), min(w + 1, U)
+                owner += [w] * (hi - lo)
+            assert len(owner) == U
+            for u in range(U):
+                assert first_wave_of_unit(u, U, W) == owner[u]
+    assert first_wave_of_unit(5, 5, 7) == -1
+
+
+# ------------------------------------------------------------- fake stages
+class Arena:
+    """Hands out fake, 256-byte aligned, non-overlapping device addresses."""
+
+    def __init__(self):
+        self.next = 1 << 40
+
+    def take(self, nbytes):
+        p = self.next
+        self.next += (nbytes + 4095) // 4096 * 4096 + 4096
+        return p
+
+
+def fake_stage(ar, N, K, B, norm=L.NORM_NONE, epi=L.EPI_NONE, x=None, residual=None, gamma=True,
+               bias=False, beta=False):
+    s = L.Stage()
+    s.N, s.K = N, K
+    s.W = ar.take(N * K * 2)
+    s.W_up = ar.take(N * K * 2) if epi == L.EPI_SWIGLU else None
+    s.bias = ar.take(N * 2) if bias else None
+    s.norm = norm
+    s.eps = 1e-6
+    s.gamma = ar.take(K * 2) if (gamma and norm != L.NORM_NONE) else None
+    s.beta = ar.take(K * 2) if (beta and norm == L.NORM_LAYER) else None
+    s.epi = epi
+    s.x = x if x is not None else ar.take(B * K * 2)
+    s.x_stride = K
+    s.residual = residual
+    s.res_stride = N if residual else 0
+    if epi == L.EPI_ARGMAX:
+        s.y = ar.take(B * 4)
+        s.y_stride = 0
+    else:
+        s.y = ar.take(B * N * 2)
+        s.y_stride = N
+    return s
+
+
+def fake_decoder(ar, B, n_layers, H=1536, I=8960, V=None):
+    stages = []
+    h = ar.take(B * H * 2)
+    for _ in range(n_layers):
+        q = fake_stage(ar, H, H, B, L.NORM_RMS, x=h)
+        k = fake_stage(ar, H // 6, H, B, L.NORM_RMS, x=h)
+        v = fake_stage(ar, H // 6, H, B, L.NORM_RMS, x=h)
+        k.gamma = v.gamma = q.gamma
+        o = fake_stage(ar, H, H, B, L.NORM_NONE, residual=h)
+        gu = fake_stage(ar, I, H, B, L.NORM_RMS, L.EPI_SWIGLU, x=o.y)
+        d = fake_stage(ar, H, I, B, L.NORM_NONE, x=gu.y, residual=o.y)
+        stages += [q, k, v, o, gu, d]
+        h = d.y
+    if V:
+        stages.append(fake_stage(ar, V, H, B, L.NORM_RMS, L.EPI_ARGMAX, x=h))
+    return stages
+
+
+@pytest.mark.parametrize("B", [1, 4])
+@pytest.mark.parametrize("grid", [256, 61, 32])
+def test_partition_decoder_block(B, grid):
+    ar = Arena()
+    stages = fake_decoder(ar, B, 1)
+    assert partition_selftest(stages, B, grid) == 0
+
+
+def test_partition_full_decode_step_shapes():
+    ar = Arena()
+    stages = fake_decoder(ar, 1, 2, V=151936)
+    assert partition_selftest(stages, 1, 256) == 0
+
+
+@pytest.mark.parametrize("K", [8, 24, 256, 520, 1536, 8960])
+@pytest.mark.parametrize("N", [1, 5, 97, 1000])
+def test_partition_ragged_shapes(N, K):
+    ar = Arena()
+    st = [fake_stage(ar, N, K, 2, L.NORM_RMS),
+          fake_stage(ar, max(1, N // 3), K, 2, L.NORM_NONE, L.EPI_SWIGLU)]
+    for grid in (1, 3, 64, 256):
+        r = partition_selftest(st, 2, grid)
+        # a grid too small for the per-workgroup partial sums is refused, never mis-planned
+        assert r == 0 or (r == L.E_UNSUPPORTED and grid <= 3), (grid, r)
+
+
+def test_partition_ln_chain():
+    ar = Arena()
+    x = ar.take(16 * 768 * 2)
+    st = []
+    for _ in range(5):
+        s = fake_stage(ar, 768, 768, 4, L.NORM_LAYER, L.EPI_GELU_TANH, x=x, bias=True, beta=True)
+        st.append(s)
+        x = s.y
+    assert partition_selftest(st, 4, 256) == 0
+
+
+# -------------------------------------------------------- argument checks
+def call_gemv(s, batch=1):
+    import ctypes
+    return L.lib().wgn_gemv_norm(ctypes.byref(s), batch, None, 0, None)
+
+
+def test_invalid_arguments_rejected_before_device():
+    ar = Arena()
+    good = fake_stage(ar, 64, 64, 1, L.NORM_RMS)
+    cases = []
+    s = fake_stage(ar, 64, 60, 1, L.NORM_RMS); cases.append((s, 1, L.E_ARG))          # K % 8
+    s = fake_stage(ar, 0, 64, 1); cases.append((s, 1, L.E_ARG))                        # N = 0
+    s = fake_stage(ar, 64, 64, 1); s.W = None; cases.append((s, 1, L.E_ARG))           # null W
+    s = fake_stage(ar, 64, 64, 1); s.W += 2; cases.append((s, 1, L.E_ALIGN))           # misaligned W
+    s = fake_stage(ar, 64, 64, 1); s.x += 8; cases.append((s, 1, L.E_ALIGN))           # misaligned x
+    s = fake_stage(ar, 64, 64, 2); s.x_stride = 68; cases.append((s, 2, L.E_ALIGN))    # stride % 8
+    s = fake_stage(ar, 64, 64, 1); s.epi = 7; cases.append((s, 1, L.E_ARG))            # bad enum
+    s = fake_stage(ar, 64, 64, 1, L.NORM_RMS, L.EPI_SWIGLU); s.W_up = None
+    cases.append((s, 1, L.E_ARG))                                                      # SwiGLU w/o up
+    s = fake_stage(ar, 64, 64, 1, L.NORM_NONE); s.gamma = ar.take(128)
+    cases.append((s, 1, L.E_ARG))                                                      # gain w/o norm
+    cases.append((good, 0, L.E_ARG))                                                   # batch 0
+    cases.append((good, 17, L.E_ARG))                                                  # batch > 16
+    s = fake_stage(ar, 64, 64, 1, L.NORM_RMS); s.eps = float("nan"); cases.append((s, 1, L.E_ARG))
+    for st, b, want in cases:
+        assert call_gemv(st, b) == want, (want,)
+
+
+def test_chain_rejects_weights_written_by_a_stage():
+    import ctypes
+    ar = Arena()
+    a = fake_stage(ar, 64, 64, 1)
+    b = fake_stage(ar, 64, 64, 1, x=a.y)
+    b.W = a.y  # a weight that an earlier stage writes
+    arr = L.stage_array([a, b])
+    assert L.lib().wgn_chain_workspace_bytes(arr, 2, 1, None) == 0
+    assert partition_selftest([a, b], 1, 4) == L.E_ARG
+
+
+def test_chain_phase_grouping_counts():
+    """Q/K/V/O form one phase, gate/up one, down one: 3 phases per layer, +1 for the LM head."""
+    import ctypes
+    ar = Arena()
+    st = fake_decoder(ar, 1, 3, V=1000)
+    assert partition_selftest(st, 1, 16) == 0
+    arr = L.stage_array(st)
+    assert L.lib().wgn_chain_workspace_bytes(arr, len(st), 1, None) > 0
+
+
+def test_rmsnorm_rows_argument_checks():
+    ar = Arena()
+    x, g, y = ar.take(4096), ar.take(4096), ar.take(4096)
+    f = L.lib().wgn_rmsnorm_rows
+    assert f(x, 64, g, 1e-6, y, 64, 4, 60, L.FP16, None) == L.E_ARG
+    assert f(x, 64, g, 1e-6, y, 64, 4, 64, 7, None) == L.E_ARG
+    assert f(x + 2, 64, g, 1e-6, y, 64, 4, 64, L.FP16, None) == L.E_ALIGN
+    assert f(x, 64, g, 1e-6, x + 64, 64, 4, 64, L.FP16, None) == L.E_ARG   # y overlaps x
+    assert f(x, 64, g, 1e-6, y, 64, 0, 64, L.FP16, None) == L.OK           # empty: no-op
+
+
+def test_workspace_size_scales_with_argmax():
+    import ctypes
+    ar = Arena()
+    s = fake_stage(ar, 1000, 64, 2, L.NORM_RMS, L.EPI_ARGMAX)
+    assert L.lib().wgn_gemv_norm_workspace_bytes(ctypes.byref(s), 2) > 0
+    s2 = fake_stage(ar, 1000, 64, 2, L.NORM_RMS)
+    assert L.lib().wgn_gemv_norm_workspace_bytes(ctypes.byref(s2), 2) == 0
+
+
+def test_decode_step_weight_bytes_match_library_shapes():
+    ar = Arena()
+    st = fake_decoder(ar, 1, gen.N_LAYERS, V=gen.V)
+    total = sum(s.N * s.K * 2 * (2 if s.epi == L.EPI_SWIGLU else 1) for s in st)
+    assert total == gen.decode_step_weight_bytes() == 3_087_138_816

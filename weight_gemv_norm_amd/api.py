@@ -1,0 +1,195 @@
+"""Thin Python binding of libwgn.so with the C-ABI's names.
+
+torch tensors are used only as device memory and streams: every step of the
+computation runs in the library's HIP kernels.  There is no fallback path: if
+the library is missing or a call fails, these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _lib as L
+from ._lib import (EPI_ARGMAX, EPI_GELU_TANH, EPI_NONE, EPI_SWIGLU, NORM_LAYER,  # noqa: F401
+                   NORM_NONE, NORM_RMS, BF16, FP16, ChainOpts, Stage, WgnError)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _row_stride(t: torch.Tensor) -> int:
+    if t.dim() == 1:
+        return t.shape[0]
+    assert t.dim() == 2 and t.stride(1) == 1, "activations must be [batch][stride] with unit inner stride"
+    return t.stride(0)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def make_stage(W: torch.Tensor, x: torch.Tensor, y: torch.Tensor, *, norm: int = NORM_NONE,
+               eps: float = 1e-6, gamma: Optional[torch.Tensor] = None,
+               beta: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+               epi: int = EPI_NONE, W_up: Optional[torch.Tensor] = None,
+               residual: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+               maxval: Optional[torch.Tensor] = None) -> Stage:
+    """Describe y = R(residual + epi(W . norm(x) + bias)) over device tensors."""
+    assert W.dim() == 2 and W.is_contiguous()
+    N, K = W.shape
+    s = Stage()
+    s.N, s.K = N, K
+    s.W = _ptr(W)
+    s.W_up = _ptr(W_up)
+    s.bias = _ptr(bias)
+    s.norm = norm
+    s.eps = eps
+    s.gamma = _ptr(gamma)
+    s.beta = _ptr(beta)
+    s.epi = epi
+    s.x = _ptr(x)
+    s.x_stride = _row_stride(x)
+    s.residual = _ptr(residual)
+    s.res_stride = _row_stride(residual) if residual is not None else 0
+    s.y = _ptr(y)
+    s.y_stride = _row_stride(y) if epi != EPI_ARGMAX else 0
+    s.logits = _ptr(logits)
+    s.maxval = _ptr(maxval)
+    return s
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """Zero-filled device workspace (256-byte aligned)."""
+    t = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    assert t.data_ptr() % 256 == 0
+    return t
+
+
+def device_cu_count() -> int:
+    return int(L.lib().wgn_device_cu_count())
+
+
+def gemv_norm_workspace_bytes(stage: Stage, batch: int) -> int:
+    return int(L.lib().wgn_gemv_norm_workspace_bytes(ctypes.byref(stage), batch))
+
+
+def gemv_norm(stage: Stage, batch: int, ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    st = L.lib().wgn_gemv_norm(ctypes.byref(stage), batch, _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(stream))
+    L.check(st, "wgn_gemv_norm")
+
+
+def lmhead_argmax_workspace_bytes(batch: int) -> int:
+    return int(L.lib().wgn_lmhead_argmax_workspace_bytes(batch))
+
+
+def lmhead_argmax(h: torch.Tensor, gamma: Optional[torch.Tensor], eps: float, W_lm: torch.Tensor,
+                  idx_out: torch.Tensor, max_out: Optional[torch.Tensor] = None,
+                  logits_out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                  stream=None) -> None:
+    h2 = h if h.dim() == 2 else h.view(1, -1)
+    B, K = h2.shape
+    V = W_lm.shape[0]
+    if ws is None:
+        ws = workspace(lmhead_argmax_workspace_bytes(B), h.device)
+    st = L.lib().wgn_lmhead_argmax(_ptr(h2), _row_stride(h2), B, K, _ptr(gamma), eps, _ptr(W_lm), V,
+                                   _ptr(idx_out), _ptr(max_out), _ptr(logits_out), _ptr(ws), ws.numel(),
+                                   _stream(stream))
+    L.check(st, "wgn_lmhead_argmax")
+
+
+def rmsnorm_rows(x: torch.Tensor, gamma: torch.Tensor, eps: float, y: torch.Tensor, stream=None) -> None:
+    assert x.dim() == 2 and x.dtype in (torch.float16, torch.bfloat16) and y.dtype == x.dtype
+    dtype = FP16 if x.dtype == torch.float16 else BF16
+    st = L.lib().wgn_rmsnorm_rows(_ptr(x), _row_stride(x), _ptr(gamma), eps, _ptr(y), _row_stride(y),
+                                  x.shape[0], x.shape[1], dtype, _stream(stream))
+    L.check(st, "wgn_rmsnorm_rows")
+
+
+def _opts(mode: int, grid: int) -> ChainOpts:
+    o = ChainOpts()
+    o.mode = mode
+    o.grid = grid
+    return o
+
+
+def chain_workspace_bytes(stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 0) -> int:
+    arr = L.stage_array(stages)
+    o = _opts(mode, grid)
+    return int(L.lib().wgn_chain_workspace_bytes(arr, len(stages), batch, ctypes.byref(o)))
+
+
+class Chain:
+    """A planned chain (wgn_chain_create); run() enqueues one pass."""
+
+    def __init__(self, stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 0,
+                 ws: Optional[torch.Tensor] = None, stream=None, device="cuda"):
+        self._arr = L.stage_array(stages)
+        self.n_stages = len(stages)
+        self.batch = batch
+        o = _opts(mode, grid)
+        need = L.lib().wgn_chain_workspace_bytes(self._arr, len(stages), batch, ctypes.byref(o))
+        if need == 0:
+            # planning failed: let create report the precise status
+            need = 256
+        self.ws = ws if ws is not None else workspace(need, device)
+        h = ctypes.c_void_p()
+        st = L.lib().wgn_chain_create(self._arr, len(stages), batch, ctypes.byref(o), _ptr(self.ws),
+                                      self.ws.numel(), _stream(stream), ctypes.byref(h))
+        L.check(st, "wgn_chain_create")
+        self._h = h
+
+    def run(self, stream=None) -> None:
+        L.check(L.lib().wgn_chain_run(self._h, _stream(stream)), "wgn_chain_run")
+
+    def check(self, stream=None) -> None:
+        L.check(L.lib().wgn_chain_check(self._h, _stream(stream)), "wgn_chain_check")
+
+    @property
+    def num_phases(self) -> int:
+        return int(L.lib().wgn_chain_num_phases(self._h))
+
+    def stage_phases(self) -> List[int]:
+        out = (ctypes.c_int32 * self.n_stages)()
+        L.check(L.lib().wgn_chain_stage_phases(self._h, out), "wgn_chain_stage_phases")
+        return list(out)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            L.lib().wgn_chain_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def layer_chain(stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 0,
+                ws: Optional[torch.Tensor] = None, stream=None, device="cuda") -> None:
+    arr = L.stage_array(stages)
+    o = _opts(mode, grid)
+    if ws is None:
+        ws = workspace(L.lib().wgn_chain_workspace_bytes(arr, len(stages), batch, ctypes.byref(o)), device)
+    st = L.lib().wgn_layer_chain(arr, len(stages), batch, ctypes.byref(o), _ptr(ws), ws.numel(),
+                                 _stream(stream))
+    L.check(st, "wgn_layer_chain")
+
+
+def partition_selftest(stages: Sequence[Stage], batch: int, grid: int) -> int:
+    arr = L.stage_array(stages)
+    return int(L.lib().wgn_partition_selftest(arr, len(stages), batch, grid))
+
+
+def first_wave_of_unit(u: int, units: int, waves: int) -> int:
+    return int(L.lib().wgn_first_wave_of_unit(u, units, waves))

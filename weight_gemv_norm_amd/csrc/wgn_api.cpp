@@ -1,0 +1,711 @@
+// wgn_api.cpp -- host side of libwgn.so: argument validation, grouping of a
+// stage list into phases, device-program layout, launches.
+//
+// Everything here runs before a kernel is enqueued; a failed check returns a
+// negative status and enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "../../include/wgn.h"
+#include "wgn_loader.h"
+
+namespace wgn {
+hipError_t launch_chain(int32_t batch, const KArgs &a, int32_t grid, size_t lds, hipStream_t s);
+hipError_t launch_rmsnorm_rows(const uint16_t *x, int64_t xs, const uint16_t *g, float eps, uint16_t *y, int64_t ys,
+                               int32_t rows, int32_t K, bool f16, hipStream_t s);
+}  // namespace wgn
+
+using namespace wgn;
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+// Record a failing HIP call's error for wgn_last_hip_error().
+hipError_t note(hipError_t e, const char *what) {
+    if (e != hipSuccess)
+        std::snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+    return e;
+}
+
+constexpr size_t LDS_BUDGET = 160 * 1024 - 256;  // gfx950 LDS per workgroup, minus static use
+constexpr int32_t VERSION = 1;
+
+struct DevInfo {
+    bool ok = false;
+    int32_t cus = 0;
+};
+
+DevInfo device_info() {
+    static std::mutex mu;
+    static DevInfo cache[16];
+    static bool have[16] = {false};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return DevInfo{};
+    std::lock_guard<std::mutex> lk(mu);
+    if (!have[dev]) {
+        hipDeviceProp_t prop;
+        DevInfo d;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+            d.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+            d.cus = prop.multiProcessorCount;
+        }
+        cache[dev] = d;
+        have[dev] = true;
+    }
+    return cache[dev];
+}
+
+inline bool a16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool a4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline bool a2(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+inline size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
+
+wgn_status check_stage(const wgn_stage &s, int32_t batch) {
+    if (batch < 1 || batch > MAX_BATCH) return WGN_E_ARG;
+    if (s.N < 1 || s.K < 8 || (s.K & 7)) return WGN_E_ARG;
+    if (!s.W || !s.x || !s.y) return WGN_E_ARG;
+    if (s.norm < NORM_NONE || s.norm > NORM_LAYER) return WGN_E_ARG;
+    if (s.epi < EPI_NONE || s.epi > EPI_ARGMAX) return WGN_E_ARG;
+    if (s.epi == EPI_SWIGLU && !s.W_up) return WGN_E_ARG;
+    if (s.epi != EPI_SWIGLU && s.W_up) return WGN_E_ARG;
+    if (s.epi == EPI_SWIGLU && s.bias) return WGN_E_UNSUPPORTED;
+    if (s.epi == EPI_ARGMAX && s.residual) return WGN_E_ARG;
+    if (s.epi != EPI_ARGMAX && (s.logits || s.maxval)) return WGN_E_ARG;
+    if (s.norm != NORM_LAYER && s.beta) return WGN_E_ARG;
+    if (s.norm == NORM_NONE && s.gamma) return WGN_E_ARG;
+    if (s.norm != NORM_NONE && !(s.eps >= 0.0f)) return WGN_E_ARG;
+    if (batch > 1 && s.x_stride < s.K) return WGN_E_ARG;
+    if (batch > 1 && s.epi != EPI_ARGMAX && s.y_stride < s.N) return WGN_E_ARG;
+    if (batch > 1 && s.residual && s.res_stride < s.N) return WGN_E_ARG;
+    if (!a16(s.W) || (s.W_up && !a16(s.W_up))) return WGN_E_ALIGN;
+    if (!a16(s.x) || (s.x_stride & 7)) return WGN_E_ALIGN;
+    if ((s.gamma && !a16(s.gamma)) || (s.beta && !a16(s.beta))) return WGN_E_ALIGN;
+    if ((s.bias && !a2(s.bias)) || (s.residual && !a2(s.residual))) return WGN_E_ALIGN;
+    if (s.epi == EPI_ARGMAX) {
+        if (!a4(s.y) || (s.logits && !a4(s.logits)) || (s.maxval && !a4(s.maxval))) return WGN_E_ALIGN;
+    } else if (!a2(s.y)) {
+        return WGN_E_ALIGN;
+    }
+    return WGN_OK;
+}
+
+// Byte ranges a stage reads (activations) and writes.
+struct Range {
+    uintptr_t lo, hi;
+};
+inline bool overlap(const Range &a, const Range &b) { return a.lo < b.hi && b.lo < a.hi; }
+inline Range rng(const void *p, size_t bytes) {
+    uintptr_t u = reinterpret_cast<uintptr_t>(p);
+    return Range{u, u + bytes};
+}
+
+void stage_ranges(const wgn_stage &s, int32_t B, std::vector<Range> &reads, std::vector<Range> &writes,
+                  std::vector<Range> &consts) {
+    reads.clear();
+    writes.clear();
+    consts.clear();
+    reads.push_back(rng(s.x, ((size_t)(B - 1) * s.x_stride + s.K) * 2));
+    if (s.residual) reads.push_back(rng(s.residual, ((size_t)(B - 1) * s.res_stride + s.N) * 2));
+    if (s.epi == EPI_ARGMAX) {
+        writes.push_back(rng(s.y, (size_t)B * 4));
+        if (s.logits) writes.push_back(rng(s.logits, (size_t)B * s.N * 4));
+        if (s.maxval) writes.push_back(rng(s.maxval, (size_t)B * 4));
+    } else {
+        writes.push_back(rng(s.y, ((size_t)(B - 1) * s.y_stride + s.N) * 2));
+    }
+    consts.push_back(rng(s.W, (size_t)s.N * s.K * 2));
+    if (s.W_up) consts.push_back(rng(s.W_up, (size_t)s.N * s.K * 2));
+    if (s.gamma) consts.push_back(rng(s.gamma, (size_t)s.K * 2));
+    if (s.beta) consts.push_back(rng(s.beta, (size_t)s.K * 2));
+    if (s.bias) consts.push_back(rng(s.bias, (size_t)s.N * 2));
+}
+
+bool any_overlap(const std::vector<Range> &a, const std::vector<Range> &b) {
+    for (const Range &x : a)
+        for (const Range &y : b)
+            if (overlap(x, y)) return true;
+    return false;
+}
+
+bool same_source(const DevSource &s, const wgn_stage &st) {
+    return s.x == (const uint16_t *)st.x && s.x_stride == st.x_stride && s.K == st.K && s.norm == st.norm &&
+           s.gamma == (const uint16_t *)st.gamma && s.beta == (const uint16_t *)st.beta &&
+           (st.norm == NORM_NONE || s.eps == st.eps);
+}
+
+// Host image of a device program.
+struct Program {
+    int32_t B = 1, G = 1;
+    std::vector<DevPhase> phases;
+    std::vector<DevStage> stages;
+    std::vector<DevSource> sources;
+    std::vector<int32_t> rowb;
+    std::vector<int32_t> phase_of_stage;
+    int32_t n_argmax = 0;
+    size_t lds_x_bytes = 0, lds_part_bytes = 0;
+};
+
+DevStage make_dev_stage(const wgn_stage &s) {
+    DevStage d;
+    std::memset(&d, 0, sizeof d);
+    d.W = (const uint16_t *)s.W;
+    d.W_up = (const uint16_t *)s.W_up;
+    d.bias = (const uint16_t *)s.bias;
+    d.residual = (const uint16_t *)s.residual;
+    d.y = s.y;
+    d.logits = s.logits;
+    d.maxval = s.maxval;
+    d.res_stride = s.res_stride;
+    d.y_stride = s.y_stride;
+    d.N = s.N;
+    d.K = s.K;
+    d.epi = s.epi;
+    d.nchunks = nchunks_of(s.K);
+    d.parts = s.epi == EPI_SWIGLU ? 2 : 1;
+    d.am_slot = -1;
+    return d;
+}
+
+DevSource make_dev_source(const wgn_stage &s) {
+    DevSource d;
+    std::memset(&d, 0, sizeof d);
+    d.x = (const uint16_t *)s.x;
+    d.gamma = (const uint16_t *)s.gamma;
+    d.beta = (const uint16_t *)s.beta;
+    d.x_stride = s.x_stride;
+    d.K = s.K;
+    d.norm = s.norm;
+    d.eps = s.eps;
+    return d;
+}
+
+// Cost-balanced split of a phase's rows over G workgroups (cost = weight bytes).
+void balance_rows(const std::vector<DevStage> &st, int32_t s0, int32_t ns, int32_t G, std::vector<int32_t> &out) {
+    int64_t total = 0;
+    for (int32_t i = 0; i < ns; ++i) total += (int64_t)st[s0 + i].N * st[s0 + i].parts * st[s0 + i].K;
+    int32_t nrows = 0;
+    for (int32_t i = 0; i < ns; ++i) nrows += st[s0 + i].N;
+    const size_t base = out.size();
+    out.resize(base + G + 1);
+    // walk rows once, assigning boundary g when the cumulative cost reaches g*total/G
+    int32_t g = 0, row = 0;
+    int64_t cum = 0;
+    for (int32_t i = 0; i < ns && g <= G; ++i) {
+        const int64_t c = (int64_t)st[s0 + i].parts * st[s0 + i].K;
+        for (int32_t r = 0; r < st[s0 + i].N; ++r, ++row) {
+            while (g <= G && cum >= (total * g) / G) out[base + g++] = row;
+            cum += c;
+        }
+    }
+    while (g <= G) out[base + g++] = nrows;
+    out[base + G] = nrows;
+}
+
+wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, Program &P) {
+    if (!stages || n < 1 || G < 1) return WGN_E_ARG;
+    for (int32_t i = 0; i < n; ++i) {
+        wgn_status st = check_stage(stages[i], B);
+        if (st != WGN_OK) return st;
+    }
+    if (B > MAX_BATCH_VALU) return WGN_E_UNSUPPORTED;
+    // weights and norm parameters must not be written by any stage
+    std::vector<Range> r, w, c, allw;
+    for (int32_t i = 0; i < n; ++i) {
+        stage_ranges(stages[i], B, r, w, c);
+        allw.insert(allw.end(), w.begin(), w.end());
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        stage_ranges(stages[i], B, r, w, c);
+        if (any_overlap(c, allw)) return WGN_E_ARG;
+    }
+    P = Program();
+    P.B = B;
+    P.G = G;
+    P.phase_of_stage.assign(n, -1);
+    std::vector<Range> ph_reads, ph_writes;
+    DevPhase cur;
+    std::memset(&cur, 0, sizeof cur);
+    bool open = false;
+    auto close_phase = [&]() {
+        if (!open) return;
+        cur.nstages = (int32_t)P.stages.size() - cur.stage0;
+        cur.nsrc = (int32_t)P.sources.size() - cur.src0;
+        int32_t xb = 0, maxch = 1, nrows = 0;
+        for (int32_t i = 0; i < cur.nsrc; ++i) {
+            P.sources[cur.src0 + i].lds_off = xb;
+            xb += nchunks_of(P.sources[cur.src0 + i].K) * UNIT;
+        }
+        for (int32_t i = 0; i < cur.nstages; ++i) {
+            DevStage &d = P.stages[cur.stage0 + i];
+            d.row_off = nrows;
+            nrows += d.N;
+            maxch = std::max(maxch, d.nchunks);
+        }
+        cur.xb = xb;
+        cur.nrows = nrows;
+        cur.jmax = std::min(STREAM_WAVES, maxch);
+        cur.rb_off = (int32_t)P.rowb.size();
+        balance_rows(P.stages, cur.stage0, cur.nstages, G, P.rowb);
+        int32_t max_rp = 0;
+        for (int32_t g = 0; g < G; ++g) {
+            int32_t r0 = P.rowb[cur.rb_off + g], r1 = P.rowb[cur.rb_off + g + 1], rp = 0;
+            for (int32_t i = 0; i < cur.nstages; ++i) {
+                StageSpan sp = stage_span(P.stages[cur.stage0 + i], r0, r1, 0, 0);
+                rp += sp.nrows * P.stages[cur.stage0 + i].parts;
+            }
+            max_rp = std::max(max_rp, rp);
+        }
+        P.lds_x_bytes = std::max(P.lds_x_bytes, al256((size_t)B * xb * 2));
+        P.lds_part_bytes = std::max(P.lds_part_bytes, (size_t)max_rp * cur.jmax * B * 4);
+        cur.wait = P.phases.empty() ? 0 : 1;
+        P.phases.push_back(cur);
+        open = false;
+    };
+    for (int32_t i = 0; i < n; ++i) {
+        const wgn_stage &s = stages[i];
+        stage_ranges(s, B, r, w, c);
+        bool conflict = open && (any_overlap(r, ph_writes) || any_overlap(w, ph_reads) || any_overlap(w, ph_writes));
+        // source capacity of the open phase
+        int32_t src_idx = -1;
+        if (open && !conflict) {
+            for (int32_t q = cur.src0; q < (int32_t)P.sources.size(); ++q)
+                if (same_source(P.sources[q], s)) src_idx = q - cur.src0;
+            if (src_idx < 0 && (int32_t)P.sources.size() - cur.src0 >= MAX_SRC) conflict = true;
+        }
+        if (conflict) close_phase();
+        if (!open) {
+            std::memset(&cur, 0, sizeof cur);
+            cur.stage0 = (int32_t)P.stages.size();
+            cur.src0 = (int32_t)P.sources.size();
+            ph_reads.clear();
+            ph_writes.clear();
+            open = true;
+            src_idx = -1;
+        }
+        if (src_idx < 0) {
+            P.sources.push_back(make_dev_source(s));
+            src_idx = (int32_t)P.sources.size() - 1 - cur.src0;
+        }
+        DevStage d = make_dev_stage(s);
+        d.src = src_idx;
+        if (s.epi == EPI_ARGMAX) d.am_slot = P.n_argmax++;
+        P.stages.push_back(d);
+        P.phase_of_stage[i] = (int32_t)P.phases.size();
+        ph_reads.insert(ph_reads.end(), r.begin(), r.end());
+        ph_writes.insert(ph_writes.end(), w.begin(), w.end());
+    }
+    close_phase();
+    if (P.lds_x_bytes + P.lds_part_bytes > LDS_BUDGET) return WGN_E_UNSUPPORTED;
+    return WGN_OK;
+}
+
+struct WsLayout {
+    size_t phases, stages, sources, rowb, ctr, tickets, err, am_part, total;
+};
+
+WsLayout ws_layout(const Program &P) {
+    WsLayout L;
+    size_t o = 0;
+    L.phases = o;
+    o += al256(P.phases.size() * sizeof(DevPhase));
+    L.stages = o;
+    o += al256(P.stages.size() * sizeof(DevStage));
+    L.sources = o;
+    o += al256(P.sources.size() * sizeof(DevSource));
+    L.rowb = o;
+    o += al256(P.rowb.size() * sizeof(int32_t));
+    L.ctr = o;
+    o += al256(P.phases.size() * sizeof(uint32_t));
+    L.tickets = o;
+    o += al256((size_t)(P.n_argmax + 1) * sizeof(uint32_t));
+    L.err = o;
+    o += 256;
+    L.am_part = o;
+    o += al256((size_t)P.n_argmax * P.G * P.B * sizeof(uint64_t));
+    L.total = o;
+    return L;
+}
+
+int32_t resolve_grid(const wgn_chain_opts *opts) {
+    int32_t g = opts ? opts->grid : 0;
+    if (g > 0) return g;
+    DevInfo d = device_info();
+    return d.cus > 0 ? d.cus : 256;
+}
+
+// ------------------------------------------------- single-stage launches
+struct SingleLaunch {
+    KArgs a;
+    int32_t G;
+    size_t lds;
+    size_t ws;
+};
+
+void single_geometry(const wgn_stage &s, int32_t B, int32_t cus, SingleLaunch &L) {
+    std::memset(&L.a, 0, sizeof L.a);
+    const int32_t parts = s.epi == EPI_SWIGLU ? 2 : 1;
+    const int64_t units = (int64_t)s.N * parts * nchunks_of(s.K);
+    int64_t g = (units + 2 * STREAM_WAVES - 1) / (2 * STREAM_WAVES);
+    g = std::max<int64_t>(1, std::min<int64_t>(g, cus));
+    g = std::min<int64_t>(g, s.N);
+    L.G = (int32_t)g;
+    const int32_t nch = nchunks_of(s.K);
+    const int32_t jmax = std::min(STREAM_WAVES, nch);
+    const int32_t rows_max = (int32_t)((s.N + L.G - 1) / L.G);
+    const size_t xbytes = al256((size_t)B * nch * UNIT * 2);
+    L.lds = xbytes + (size_t)rows_max * parts * jmax * B * 4;
+    L.a.lds_x_bytes = (int32_t)xbytes;
+    L.ws = s.epi == EPI_ARGMAX ? 256 + al256((size_t)L.G * B * sizeof(uint64_t)) : 0;
+    DevPhase &ph = L.a.iph;
+    ph.stage0 = 0;
+    ph.nstages = 1;
+    ph.src0 = 0;
+    ph.nsrc = 1;
+    ph.nrows = s.N;
+    ph.wait = 0;
+    ph.xb = nch * UNIT;
+    ph.rb_off = -1;
+    ph.jmax = jmax;
+    L.a.ist = make_dev_stage(s);
+    L.a.ist.src = 0;
+    L.a.ist.row_off = 0;
+    L.a.ist.am_slot = s.epi == EPI_ARGMAX ? 0 : -1;
+    L.a.isrc = make_dev_source(s);
+    L.a.isrc.lds_off = 0;
+    L.a.p0 = 0;
+    L.a.p1 = 1;
+    L.a.persistent = 0;
+    L.a.G = L.G;
+    L.a.n_argmax = s.epi == EPI_ARGMAX ? 1 : 0;
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+struct wgn_chain {
+    Program P;
+    KArgs a;
+    int32_t mode;
+    size_t lds;
+    void *ws;
+    WsLayout L;
+};
+
+extern "C" {
+
+const char *wgn_status_string(int32_t s) {
+    switch (s) {
+    case WGN_OK: return "ok";
+    case WGN_E_ARG: return "invalid argument";
+    case WGN_E_ALIGN: return "misaligned pointer or stride";
+    case WGN_E_UNSUPPORTED: return "unsupported request";
+    case WGN_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case WGN_E_HIP: return "HIP runtime error";
+    case WGN_E_DEVICE: return "no usable gfx950 device";
+    case WGN_E_TIMEOUT: return "in-kernel wait timed out";
+    default: return "unknown status";
+    }
+}
+
+int32_t wgn_version(void) { return VERSION; }
+
+const char *wgn_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t wgn_device_cu_count(void) { return device_info().cus; }
+
+int32_t wgn_first_wave_of_unit(int32_t u, int32_t units, int32_t waves) {
+    if (units <= 0 || waves <= 0 || u < 0 || u >= units) return -1;
+    return first_wave(u, units, waves);
+}
+
+size_t wgn_gemv_norm_workspace_bytes(const wgn_stage *stage, int32_t batch) {
+    if (!stage || check_stage(*stage, batch) != WGN_OK) return 0;
+    SingleLaunch L;
+    DevInfo d = device_info();
+    single_geometry(*stage, batch, d.cus > 0 ? d.cus : 256, L);
+    return L.ws;
+}
+
+wgn_status wgn_gemv_norm(const wgn_stage *stage, int32_t batch, void *workspace, size_t ws_bytes,
+                         wgn_stream stream) {
+    if (!stage) return WGN_E_ARG;
+    wgn_status st = check_stage(*stage, batch);
+    if (st != WGN_OK) return st;
+    if (batch > MAX_BATCH_VALU) return WGN_E_UNSUPPORTED;
+    DevInfo d = device_info();
+    if (!d.ok) return WGN_E_DEVICE;
+    SingleLaunch L;
+    single_geometry(*stage, batch, d.cus, L);
+    if (L.lds > LDS_BUDGET) return WGN_E_UNSUPPORTED;
+    if (L.ws) {
+        if (!workspace || ws_bytes < L.ws || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return WGN_E_WORKSPACE;
+        L.a.tickets = (uint32_t *)workspace;
+        L.a.err = (uint32_t *)((char *)workspace + 64);
+        L.a.am_part = (uint64_t *)((char *)workspace + 256);
+    }
+    hipError_t e = note(launch_chain(batch, L.a, L.G, L.lds, (hipStream_t)stream), "gemv_norm launch");
+    return e == hipSuccess ? WGN_OK : WGN_E_HIP;
+}
+
+size_t wgn_lmhead_argmax_workspace_bytes(int32_t batch) {
+    if (batch < 1 || batch > MAX_BATCH) return 0;
+    DevInfo d = device_info();
+    int32_t G = d.cus > 0 ? d.cus : 256;
+    return 256 + al256((size_t)G * batch * sizeof(uint64_t));
+}
+
+wgn_status wgn_lmhead_argmax(const void *h, int64_t h_stride, int32_t batch, int32_t K, const void *gamma,
+                             float eps, const void *W_lm, int32_t V, int32_t *idx_out, float *max_out,
+                             float *logits_out, void *workspace, size_t ws_bytes, wgn_stream stream) {
+    wgn_stage s;
+    std::memset(&s, 0, sizeof s);
+    s.N = V;
+    s.K = K;
+    s.W = W_lm;
+    s.norm = gamma ? NORM_RMS : NORM_NONE;
+    s.eps = eps;
+    s.gamma = gamma;
+    s.epi = EPI_ARGMAX;
+    s.x = h;
+    s.x_stride = h_stride;
+    s.y = idx_out;
+    s.logits = logits_out;
+    s.maxval = max_out;
+    return wgn_gemv_norm(&s, batch, workspace, ws_bytes, stream);
+}
+
+wgn_status wgn_rmsnorm_rows(const void *x, int64_t x_stride, const void *gamma, float eps, void *y,
+                            int64_t y_stride, int32_t rows, int32_t K, int32_t dtype, wgn_stream stream) {
+    if (!x || !gamma || !y || rows < 0 || K < 8 || (K & 7)) return WGN_E_ARG;
+    if (dtype != WGN_BF16 && dtype != WGN_FP16) return WGN_E_ARG;
+    if (!(eps >= 0.0f)) return WGN_E_ARG;
+    if (rows > 1 && (x_stride < K || y_stride < K)) return WGN_E_ARG;
+    if (!a16(x) || !a16(gamma) || !a16(y) || (x_stride & 7) || (y_stride & 7)) return WGN_E_ALIGN;
+    {
+        Range rx = rng(x, ((size_t)(rows > 0 ? rows - 1 : 0) * x_stride + K) * 2);
+        Range ry = rng(y, ((size_t)(rows > 0 ? rows - 1 : 0) * y_stride + K) * 2);
+        if (overlap(rx, ry)) return WGN_E_ARG;
+    }
+    if (rows == 0) return WGN_OK;
+    DevInfo d = device_info();
+    if (!d.ok) return WGN_E_DEVICE;
+    hipError_t e = note(launch_rmsnorm_rows((const uint16_t *)x, x_stride, (const uint16_t *)gamma, eps,
+                                            (uint16_t *)y, y_stride, rows, K, dtype == WGN_FP16, (hipStream_t)stream),
+                        "rmsnorm_rows launch");
+    return e == hipSuccess ? WGN_OK : WGN_E_HIP;
+}
+
+size_t wgn_chain_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch,
+                                 const wgn_chain_opts *opts) {
+    Program P;
+    if (plan(stages, n_stages, batch, resolve_grid(opts), P) != WGN_OK) return 0;
+    return ws_layout(P).total;
+}
+
+wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t batch, const wgn_chain_opts *opts,
+                            void *workspace, size_t ws_bytes, wgn_stream stream, wgn_chain **out) {
+    if (!out) return WGN_E_ARG;
+    *out = nullptr;
+    if (opts) {
+        if (opts->mode < 0 || opts->mode > 1 || opts->grid < 0) return WGN_E_ARG;
+        for (int i = 0; i < 6; ++i)
+            if (opts->reserved[i]) return WGN_E_ARG;
+    }
+    wgn_chain *c = new (std::nothrow) wgn_chain();
+    if (!c) return WGN_E_ARG;
+    wgn_status st = plan(stages, n_stages, batch, resolve_grid(opts), c->P);
+    if (st != WGN_OK) {
+        delete c;
+        return st;
+    }
+    DevInfo d = device_info();
+    if (!d.ok) {
+        delete c;
+        return WGN_E_DEVICE;
+    }
+    c->L = ws_layout(c->P);
+    if (!workspace || ws_bytes < c->L.total || (reinterpret_cast<uintptr_t>(workspace) & 255u)) {
+        delete c;
+        return WGN_E_WORKSPACE;
+    }
+    c->mode = opts ? opts->mode : 0;
+    c->ws = workspace;
+    c->lds = c->P.lds_x_bytes + c->P.lds_part_bytes;
+    // host image of the program, then one upload
+    std::vector<char> img(c->L.ctr, 0);
+    std::memcpy(img.data() + c->L.phases, c->P.phases.data(), c->P.phases.size() * sizeof(DevPhase));
+    std::memcpy(img.data() + c->L.stages, c->P.stages.data(), c->P.stages.size() * sizeof(DevStage));
+    std::memcpy(img.data() + c->L.sources, c->P.sources.data(), c->P.sources.size() * sizeof(DevSource));
+    std::memcpy(img.data() + c->L.rowb, c->P.rowb.data(), c->P.rowb.size() * sizeof(int32_t));
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    if (note(hipMemcpyAsync(ws, img.data(), img.size(), hipMemcpyHostToDevice, s), "chain upload") != hipSuccess ||
+        note(hipMemsetAsync(ws + c->L.ctr, 0, c->L.am_part - c->L.ctr, s), "chain counters") != hipSuccess ||
+        note(hipStreamSynchronize(s), "chain create sync") != hipSuccess) {
+        delete c;
+        return WGN_E_HIP;
+    }
+    KArgs &a = c->a;
+    std::memset(&a, 0, sizeof a);
+    a.phases = (const DevPhase *)(ws + c->L.phases);
+    a.stages = (const DevStage *)(ws + c->L.stages);
+    a.sources = (const DevSource *)(ws + c->L.sources);
+    a.rowb = (const int32_t *)(ws + c->L.rowb);
+    a.ctr = (uint32_t *)(ws + c->L.ctr);
+    a.tickets = (uint32_t *)(ws + c->L.tickets);
+    a.err = (uint32_t *)(ws + c->L.err);
+    a.am_part = (uint64_t *)(ws + c->L.am_part);
+    a.p0 = 0;
+    a.p1 = (int32_t)c->P.phases.size();
+    a.persistent = c->mode == 0 ? 1 : 0;
+    a.G = c->P.G;
+    a.n_argmax = c->P.n_argmax;
+    a.lds_x_bytes = (int32_t)c->P.lds_x_bytes;
+    a.ist.W = (const uint16_t *)stages[0].W;  // address used by empty (zero-length) loads
+    *out = c;
+    return WGN_OK;
+}
+
+wgn_status wgn_chain_run(const wgn_chain *c, wgn_stream stream) {
+    if (!c) return WGN_E_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    if (c->mode == 0) {
+        hipError_t e = note(launch_chain(c->P.B, c->a, c->P.G, c->lds, s), "chain launch");
+        return e == hipSuccess ? WGN_OK : WGN_E_HIP;
+    }
+    KArgs a = c->a;
+    for (int32_t p = 0; p < (int32_t)c->P.phases.size(); ++p) {
+        a.p0 = p;
+        a.p1 = p + 1;
+        hipError_t e = note(launch_chain(c->P.B, a, c->P.G, c->lds, s), "chain phase launch");
+        if (e != hipSuccess) return WGN_E_HIP;
+    }
+    return WGN_OK;
+}
+
+wgn_status wgn_chain_check(const wgn_chain *c, wgn_stream stream) {
+    if (!c) return WGN_E_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    if (note(hipStreamSynchronize(s), "chain check sync") != hipSuccess) return WGN_E_HIP;
+    uint32_t err = 0;
+    if (note(hipMemcpy(&err, (char *)c->ws + c->L.err, 4, hipMemcpyDeviceToHost), "chain check read") != hipSuccess)
+        return WGN_E_HIP;
+    if (!err) return WGN_OK;
+    if (note(hipMemset((char *)c->ws + c->L.ctr, 0, c->L.am_part - c->L.ctr), "chain reset") != hipSuccess)
+        return WGN_E_HIP;
+    return WGN_E_TIMEOUT;
+}
+
+int32_t wgn_chain_num_phases(const wgn_chain *c) { return c ? (int32_t)c->P.phases.size() : -1; }
+
+wgn_status wgn_chain_stage_phases(const wgn_chain *c, int32_t *out) {
+    if (!c || !out) return WGN_E_ARG;
+    for (size_t i = 0; i < c->P.phase_of_stage.size(); ++i) out[i] = c->P.phase_of_stage[i];
+    return WGN_OK;
+}
+
+void wgn_chain_destroy(wgn_chain *c) { delete c; }
+
+wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t batch, const wgn_chain_opts *opts,
+                           void *workspace, size_t ws_bytes, wgn_stream stream) {
+    wgn_chain *c = nullptr;
+    wgn_status st = wgn_chain_create(stages, n_stages, batch, opts, workspace, ws_bytes, stream, &c);
+    if (st != WGN_OK) return st;
+    st = wgn_chain_run(c, stream);
+    wgn_chain_destroy(c);
+    return st;
+}
+
+// Host emulation of the work partition of a planned chain: every unit of every
+// phase must be streamed by exactly one wave of exactly one workgroup, every
+// partial slot written once, and the epilogue must read exactly the slots the
+// waves write.  Returns the number of violations (0 = consistent), or a
+// negative status if planning failed.
+int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_t batch, int32_t grid) {
+    Program P;
+    wgn_status st = plan(stages, n_stages, batch, grid, P);
+    if (st != WGN_OK) return st;
+    KArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.phases = P.phases.data();
+    a.stages = P.stages.data();
+    a.sources = P.sources.data();
+    a.rowb = P.rowb.data();
+    a.G = P.G;
+    int32_t bad = 0;
+    for (int32_t p = 0; p < (int32_t)P.phases.size(); ++p) {
+        const DevPhase &ph = P.phases[p];
+        std::vector<int32_t> row_owner(ph.nrows, 0);
+        for (int32_t g = 0; g < P.G; ++g) {
+            const PhaseGeo G = phase_geo<true>(a, p, g);
+            if (G.r0 > G.r1 || G.r0 < 0 || G.r1 > ph.nrows) {
+                ++bad;
+                continue;
+            }
+            for (int32_t r = G.r0; r < G.r1; ++r) row_owner[r]++;
+            const int32_t U = G.U;
+            std::vector<uint32_t> slot_writes;
+            for (int32_t w = 0; w < STREAM_WAVES; ++w) {
+                const int32_t ub = U > 0 ? wave_begin(w, U, STREAM_WAVES) : 0;
+                const int32_t ue = U > 0 ? wave_begin(w + 1, U, STREAM_WAVES) : 0;
+                for (int32_t v = ub; v < ue; ++v) {
+                    const UnitDesc d = unit_desc<true>(a, G, v, ub, ue, w, P.B);
+                    if ((d.meta & 0x8000u) == 0 || d.nbytes == 0 || (d.nbytes & 15u)) {
+                        ++bad;
+                        continue;
+                    }
+                    if (d.meta & 0x4000u) slot_writes.push_back(d.meta >> 16);
+                    if (((d.meta & 0x3FFFu) << 4) + UNIT * 2u > (uint32_t)ph.xb * 2u) ++bad;
+                }
+                // units just outside the wave's share are invalid
+                if (unit_desc<true>(a, G, ue, ub, ue, w, P.B).nbytes != 0) ++bad;
+            }
+            // every unit of every owned row-part, once, with the right address
+            int32_t rp_base = 0, u_base = 0;
+            std::vector<uint32_t> slot_reads;
+            for (int32_t si = 0; si < ph.nstages; ++si) {
+                const DevStage &sg = P.stages[ph.stage0 + si];
+                StageSpan sp = stage_span(sg, G.r0, G.r1, 0, 0);
+                for (int32_t i = 0; i < sp.nrows; ++i)
+                    for (int32_t pt = 0; pt < sg.parts; ++pt) {
+                        const int32_t rp = rp_base + i * sg.parts + pt;
+                        const int32_t a0 = u_base + (i * sg.parts + pt) * sg.nchunks;
+                        for (int32_t c = 0; c < sg.nchunks; ++c) {
+                            const int32_t v = a0 + c;
+                            const int32_t w = first_wave(v, U, STREAM_WAVES);
+                            const int32_t ub = wave_begin(w, U, STREAM_WAVES), ue = wave_begin(w + 1, U, STREAM_WAVES);
+                            if (v < ub || v >= ue) ++bad;
+                            const UnitDesc d = unit_desc<true>(a, G, v, ub, ue, w, P.B);
+                            const uint16_t *rowp = (pt == 0 ? sg.W : sg.W_up) + (int64_t)(sp.row0 + i) * sg.K;
+                            if (d.ptr != (uint64_t)(uintptr_t)rowp + (uint64_t)c * UNIT * 2u) ++bad;
+                            if (d.nbytes != (uint32_t)(sg.K * 2 - c * UNIT * 2)) ++bad;
+                        }
+                        const int32_t span = first_wave(a0 + sg.nchunks - 1, U, STREAM_WAVES) -
+                                             first_wave(a0, U, STREAM_WAVES) + 1;
+                        if (span > ph.jmax) ++bad;
+                        for (int32_t j = 0; j < span; ++j) slot_reads.push_back((uint32_t)((rp * ph.jmax + j) * P.B));
+                    }
+                rp_base += sp.nrows * sg.parts;
+                u_base += sp.nrows * sg.parts * sg.nchunks;
+            }
+            if (u_base != U) ++bad;
+            std::sort(slot_writes.begin(), slot_writes.end());
+            std::sort(slot_reads.begin(), slot_reads.end());
+            if (slot_writes != slot_reads) ++bad;
+            if (!slot_writes.empty() && (size_t)(slot_writes.back() + P.B) * 4 > P.lds_part_bytes) ++bad;
+        }
+        for (int32_t r = 0; r < ph.nrows; ++r)
+            if (row_owner[r] != 1) ++bad;
+    }
+    return bad;
+}
+
+}  // extern "C"

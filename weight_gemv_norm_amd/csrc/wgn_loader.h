@@ -1,0 +1,132 @@
+// wgn_loader.h -- where each streamed weight unit comes from.
+//
+// A streaming wave walks its share of every phase's units in a fixed order.
+// Because weights never depend on activations, the walk can run ahead of the
+// computation and across phase boundaries: the kernel issues the loads of the
+// next block of units before it consumes the current block, so weight traffic
+// of phase p+1 is already in flight while the workgroup waits for phase p to
+// finish device-wide.  This is the prefetch-the-next-layer idea of "Making
+// small PyTorch ops faster on a laptop GPU" (section "Prefetching the next
+// layer while this one runs") moved inside one persistent kernel.
+//
+// unit_desc() maps one unit index to its weight address and its meta word.
+// On the device lane j of a wave evaluates it for the j-th unit of a block
+// (one evaluation per lane per block); the host planner's self-test evaluates
+// it for every unit to check the partition.
+#pragma once
+#include "wgn_prog.h"
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// Program descriptors are read-only for the kernel's lifetime: reading them
+// through the constant address space lets the compiler use scalar loads,
+// which never wait behind the vector loads of the weight stream.
+#define WGN_CONST_PTR(T, p) ((const __attribute__((address_space(4))) T *)(p))
+#else
+#define WGN_CONST_PTR(T, p) ((const T *)(p))
+#endif
+
+namespace wgn {
+
+template <bool CHAIN>
+WGN_HD DevPhase phase_of(const KArgs &a, int32_t p) {
+    if constexpr (CHAIN) return WGN_CONST_PTR(DevPhase, a.phases)[p];
+    else return a.iph;
+}
+template <bool CHAIN>
+WGN_HD DevStage stage_of(const KArgs &a, int32_t i) {
+    if constexpr (CHAIN) return WGN_CONST_PTR(DevStage, a.stages)[i];
+    else return a.ist;
+}
+template <bool CHAIN>
+WGN_HD DevSource source_of(const KArgs &a, int32_t i) {
+    if constexpr (CHAIN) return WGN_CONST_PTR(DevSource, a.sources)[i];
+    else return a.isrc;
+}
+
+// Geometry of one phase for one workgroup.
+struct PhaseGeo {
+    int32_t p;
+    int32_t r0, r1;        // rows owned in the phase's row space
+    int32_t U;             // units owned
+    int32_t jmax;
+    int32_t xb_bytes;      // LDS bytes per batch row of x-hat
+    int32_t stage0, nstages, src0;
+};
+
+template <bool CHAIN>
+WGN_HD PhaseGeo phase_geo(const KArgs &a, int32_t p, int32_t g) {
+    const DevPhase ph = phase_of<CHAIN>(a, p);
+    PhaseGeo G;
+    G.p = p;
+    if (ph.rb_off >= 0) {
+        G.r0 = WGN_CONST_PTR(int32_t, a.rowb)[ph.rb_off + g];
+        G.r1 = WGN_CONST_PTR(int32_t, a.rowb)[ph.rb_off + g + 1];
+    } else {
+        G.r0 = even_row_begin(g, ph.nrows, a.G);
+        G.r1 = even_row_begin(g + 1, ph.nrows, a.G);
+    }
+    G.jmax = ph.jmax;
+    G.xb_bytes = ph.xb * 2;
+    G.stage0 = ph.stage0;
+    G.nstages = ph.nstages;
+    G.src0 = ph.src0;
+    int32_t U = 0;
+    for (int32_t i = 0; i < ph.nstages; ++i) {
+        const DevStage st = stage_of<CHAIN>(a, ph.stage0 + i);
+        StageSpan sp = stage_span(st, G.r0, G.r1, 0, 0);
+        U += sp.nrows * st.parts * st.nchunks;
+    }
+    G.U = U;
+    return G;
+}
+
+struct UnitDesc {
+    uint64_t ptr;          // address of the unit's first byte (row start + chunk offset)
+    uint32_t nbytes;       // bytes of the row from ptr on (0 = invalid unit: loads return 0)
+    uint32_t meta;         // pack_meta(...)
+};
+
+// Descriptor of workgroup-local unit v of phase geometry G for stream wave w,
+// whose share of the phase is [u_beg, u_end).  B = batch.
+template <bool CHAIN>
+WGN_HD UnitDesc unit_desc(const KArgs &a, const PhaseGeo &G, int32_t v, int32_t u_beg, int32_t u_end, int32_t w,
+                          int32_t B) {
+    UnitDesc d;
+    d.ptr = 0;
+    d.nbytes = 0;
+    d.meta = 0;
+    if (v < u_beg || v >= u_end) return d;
+    int32_t base_u = 0, base_rp = 0;
+    for (int32_t i = 0; i < G.nstages; ++i) {
+        const DevStage st = stage_of<CHAIN>(a, G.stage0 + i);
+        const StageSpan sp = stage_span(st, G.r0, G.r1, 0, 0);
+        const int32_t per_row = st.parts * st.nchunks;
+        const int32_t su = sp.nrows * per_row;
+        if (v < base_u + su) {
+            const int32_t local = v - base_u;
+            const int32_t rk = local / per_row;
+            const int32_t rem = local - rk * per_row;
+            const int32_t part = rem / st.nchunks;
+            const int32_t chunk = rem - part * st.nchunks;
+            const int32_t row = sp.row0 + rk;
+            const uint32_t off = (uint32_t)chunk * (UNIT * 2u);
+            const uint16_t *rowp = (part == 0 ? st.W : st.W_up) + (int64_t)row * st.K;
+            d.ptr = (uint64_t)(uintptr_t)rowp + off;
+            d.nbytes = (uint32_t)st.K * 2u - off;
+            const int32_t rp = base_rp + rk * st.parts + part;
+            const int32_t ua = v - chunk;
+            const int32_t j = ua < u_beg ? w - first_wave(ua, G.U, STREAM_WAVES) : 0;
+            const uint32_t slot = (uint32_t)((rp * G.jmax + j) * B);
+            const DevSource src = source_of<CHAIN>(a, G.src0 + st.src);
+            const uint32_t xoff = (uint32_t)src.lds_off * 2u + off;
+            const bool seg_end = (chunk == st.nchunks - 1) || (v == u_end - 1);
+            d.meta = pack_meta(xoff, seg_end, true, slot);
+            return d;
+        }
+        base_u += su;
+        base_rp += sp.nrows * st.parts;
+    }
+    return d;
+}
+
+}  // namespace wgn

@@ -1,0 +1,151 @@
+// wgn_prog.h -- device program layout and the work-partition rules, shared by
+// the host planner (wgn_api.cpp) and the kernels (wgn_kernels.hip).
+//
+// Work decomposition of one phase (a set of mutually independent stages):
+//  * rows of all stages in the phase form one "row space"; every workgroup (WG)
+//    owns a contiguous, cost-balanced run of whole rows;
+//  * a row of a SwiGLU stage has two "row-parts" (gate, up), other rows one;
+//  * a row-part is streamed as ceil(K/512) "units": one unit = 512 consecutive
+//    K elements of one weight row = 64 lanes x 16 bytes, one 128-bit load per
+//    lane, fully coalesced (1 KB per wave-load);
+//  * the WG's units are split evenly over its streaming waves (a row-part may
+//    be split across neighbouring waves); each wave reduces its part of a
+//    row-part across lanes and writes the partial to an LDS slot indexed by
+//    (row-part, wave - first wave of that row-part), and the WG's control wave
+//    sums the slots in wave order.  The order of every FP32 sum is therefore
+//    fixed by (grid, shape) alone and results are bit-reproducible.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define WGN_HD __host__ __device__ inline
+#else
+#define WGN_HD inline
+#endif
+
+namespace wgn {
+
+constexpr int UNIT = 512;            // K elements per unit (64 lanes x 8 BF16)
+constexpr int MAX_SRC = 4;           // distinct normalised inputs per phase
+constexpr int STREAM_WAVES = 7;      // weight-streaming waves per WG
+constexpr int WAVES = STREAM_WAVES + 1;   // + one control wave
+constexpr int THREADS = WAVES * 64;
+constexpr int MAX_BATCH = 16;
+constexpr int MAX_BATCH_VALU = 4;
+constexpr uint64_t WAIT_TICKS = 200000000ull;  // 2 s at the 100 MHz real-time clock
+
+enum { NORM_NONE = 0, NORM_RMS = 1, NORM_LAYER = 2 };
+enum { EPI_NONE = 0, EPI_GELU_TANH = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
+
+// A normalised input vector ("source") of a phase, staged as BF16 in LDS.
+struct DevSource {
+    const uint16_t *x;
+    const uint16_t *gamma;
+    const uint16_t *beta;
+    int64_t x_stride;
+    int32_t K;
+    int32_t norm;
+    float eps;
+    int32_t lds_off;       // element offset inside one batch row of the LDS x-hat area
+};
+
+struct DevStage {
+    const uint16_t *W;
+    const uint16_t *W_up;
+    const uint16_t *bias;
+    const uint16_t *residual;
+    void *y;
+    float *logits;
+    float *maxval;
+    int64_t res_stride;
+    int64_t y_stride;
+    int32_t N, K;
+    int32_t epi;
+    int32_t src;           // source index inside the phase
+    int32_t nchunks;       // ceil(K / UNIT)
+    int32_t parts;         // 2 for SwiGLU, else 1
+    int32_t row_off;       // first row of this stage in the phase's row space
+    int32_t am_slot;       // argmax slot (ARGMAX only)
+};
+
+struct DevPhase {
+    int32_t stage0, nstages;
+    int32_t src0, nsrc;
+    int32_t nrows;         // rows in the phase's row space
+    int32_t wait;          // wait for every WG to finish the previous phase
+    int32_t xb;            // LDS x-hat elements per batch row
+    int32_t rb_off;        // offset of this phase's G+1 row bounds; -1 = even split
+    int32_t jmax;          // partial slots per row-part
+    int32_t pad;
+};
+
+// Kernel arguments (passed by value).  A chain points at a program in device
+// memory; a single-stage call carries its one phase/stage/source inline.
+struct KArgs {
+    const DevPhase *phases;
+    const DevStage *stages;
+    const DevSource *sources;
+    const int32_t *rowb;
+    uint32_t *ctr;         // [nphases] completion counters (persistent mode)
+    uint32_t *tickets;     // [n_argmax] argmax tickets, then [1] done ticket
+    uint64_t *am_part;     // [n_argmax][G][batch] packed (value, index) keys
+    uint32_t *err;         // error word
+    int32_t p0, p1;        // phases of this launch
+    int32_t persistent;
+    int32_t G;
+    int32_t n_argmax;
+    int32_t lds_x_bytes;   // offset of the partial area in dynamic LDS
+    DevPhase iph;
+    DevStage ist;
+    DevSource isrc;
+};
+
+// ---------------------------------------------------------- partition rules
+// Even split of U units over W waves.  With U >= W every wave gets at least one
+// unit; with U < W waves 0..U-1 get one unit each and the rest none, so empty
+// waves never sit inside a row-part (the epilogue sums one slot per wave that
+// covers a row-part, and every such wave writes its slot).
+WGN_HD int32_t wave_begin(int32_t w, int32_t U, int32_t W) {
+    if (U < W) return w < U ? w : U;
+    return (int32_t)(((int64_t)w * U) / W);
+}
+// The wave whose range [wave_begin(w), wave_begin(w+1)) holds unit u (0 <= u < U).
+WGN_HD int32_t first_wave(int32_t u, int32_t U, int32_t W) {
+    if (U < W) return u;
+    return (int32_t)(((int64_t)(u + 1) * W + U - 1) / U) - 1;
+}
+WGN_HD int32_t even_row_begin(int32_t g, int32_t nrows, int32_t G) {
+    return (int32_t)(((int64_t)g * nrows) / G);
+}
+WGN_HD int32_t nchunks_of(int32_t K) { return (K + UNIT - 1) / UNIT; }
+
+// Meta word of one streamed unit (wave-uniform):
+//   bits  0..13  x-hat byte offset / 16
+//   bit   14     last unit of this wave's share of its row-part
+//   bit   15     unit is valid
+//   bits 16..31  partial slot index (in floats, already multiplied by batch)
+WGN_HD uint32_t pack_meta(uint32_t xoff_bytes, bool seg_end, bool valid, uint32_t slot) {
+    return ((xoff_bytes >> 4) & 0x3FFFu) | (seg_end ? 0x4000u : 0u) | (valid ? 0x8000u : 0u) |
+           (slot << 16);
+}
+
+// Per-(WG, stage) geometry inside a phase.
+struct StageSpan {
+    int32_t row0, nrows;   // stage-local first row and count owned by this WG
+    int32_t rp_base;       // WG-local row-part index of its first row-part
+    int32_t u_base;        // WG-local unit index of its first unit
+};
+
+WGN_HD StageSpan stage_span(const DevStage &st, int32_t r0, int32_t r1, int32_t rp_base,
+                            int32_t u_base) {
+    StageSpan s;
+    int32_t lo = r0 > st.row_off ? r0 : st.row_off;
+    int32_t hi = r1 < st.row_off + st.N ? r1 : st.row_off + st.N;
+    s.row0 = lo - st.row_off;
+    s.nrows = hi > lo ? hi - lo : 0;
+    s.rp_base = rp_base;
+    s.u_base = u_base;
+    return s;
+}
+
+}  // namespace wgn
