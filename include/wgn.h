@@ -158,7 +158,8 @@ typedef struct wgn_chain wgn_chain;
 typedef struct wgn_chain_opts {
     int32_t mode;        /* 0: one persistent launch (default); 1: one launch per phase */
     int32_t grid;        /* workgroups; 0 = one per compute unit                       */
-    int32_t reserved[6]; /* must be zero                                               */
+    int32_t trace;       /* 1: record per-phase, per-workgroup timestamps (see below)  */
+    int32_t reserved[5]; /* must be zero                                               */
 } wgn_chain_opts;
 
 /* Workspace bytes for a chain over these stages (mode/grid as in opts, NULL = defaults). */
@@ -181,6 +182,19 @@ wgn_status wgn_chain_run(const wgn_chain *chain, wgn_stream stream);
 wgn_status wgn_chain_check(const wgn_chain *chain, wgn_stream stream);
 
 int32_t wgn_chain_num_phases(const wgn_chain *chain);
+int32_t wgn_chain_grid(const wgn_chain *chain);
+
+/* Trace of the last run of a chain created with opts.trace = 1: for every
+ * phase p and workgroup g, WGN_TRACE_POINTS timestamps of the device's 100 MHz
+ * real-time clock at out[(p * grid + g) * WGN_TRACE_POINTS + i]:
+ *   0 phase start, 1 previous phase complete device-wide, 2 x-hat staged,
+ *   3 weight stream of the phase done, 4 outputs stored, 5 completion released
+ *   (control wave); 6 first streaming wave passes the phase's x-hat barrier,
+ *   7 it has issued its loads ahead of that barrier, 8 it has consumed its
+ *   last block of the phase.
+ * Synchronises `stream`; n_out = number of uint64 slots available. */
+#define WGN_TRACE_POINTS 9
+wgn_status wgn_chain_trace(const wgn_chain *chain, wgn_stream stream, uint64_t *out, size_t n_out);
 /* Phase index of each stage (array of n_stages). */
 wgn_status wgn_chain_stage_phases(const wgn_chain *chain, int32_t *phase_of_stage);
 void wgn_chain_destroy(wgn_chain *chain);

@@ -1,0 +1,215 @@
+"""Host model of the persistent kernel's in-workgroup schedule (no GPU).
+
+The chain kernel runs one control wave and several weight-streaming waves per
+workgroup; they meet only at workgroup barriers.  The LDS areas they share are
+written by one side and read by the other between barriers:
+
+* run lists (one LDS buffer per phase, DESC_BUFS buffers in a ring), written by
+  the control wave DESC_AHEAD phases ahead and read by the streaming waves when
+  they issue weight loads (up to two blocks beyond the one they consume);
+* x-hat (written by the control wave, read by the streaming waves);
+* partial sums (written by the streaming waves, read by the control wave's
+  epilogue).
+
+This file re-states the loops of both wave kinds as event lists and checks, for
+random numbers of blocks per phase, that every read of an LDS area is separated
+from the write that produced it and from the write that replaces it by at least
+one barrier, and that both kinds of wave pass the same number of barriers.  The
+two constants below mirror wgn_prog.h; the test reads them from the header so a
+change there is modelled here.
+"""
+import os
+import random
+import re
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_constant(name):
+    src = open(os.path.join(ROOT, "weight_gemv_norm_amd", "csrc", "wgn_prog.h")).read()
+    m = re.search(r"constexpr int %s = (\d+);" % name, src)
+    assert m, name
+    return int(m.group(1))
+
+
+DESC_BUFS = header_constant("DESC_BUFS")
+DESC_AHEAD = header_constant("DESC_AHEAD")
+
+
+class Wave:
+    def __init__(self):
+        self.epoch = 0          # barriers passed so far
+        self.events = []        # (epoch, kind, phase)
+
+    def barrier(self):
+        self.epoch += 1
+
+    def ev(self, kind, phase):
+        self.events.append((self.epoch, kind, phase))
+
+
+def control_events(p0, p1, desc_ahead=DESC_AHEAD):
+    """The control wave's loop: builds, x-hat writes, partial reads."""
+    c = Wave()
+    for q in range(p0, min(p1, p0 + desc_ahead)):
+        c.ev("build", q)
+    c.barrier()
+    for p in range(p0, p1):
+        if p + desc_ahead < p1:
+            c.ev("build", p + desc_ahead)
+        c.ev("read_runs", p)       # header and run list of phase p (epilogue inputs)
+        c.ev("write_xhat", p)
+        c.barrier()                # x-hat ready
+        c.barrier()                # partials complete
+        c.ev("read_part", p)       # epilogue
+        c.ev("read_runs", p)
+    return c
+
+
+def stream_events(p0, p1, nblocks):
+    """One streaming wave's loop with two blocks in flight.  nblocks[p] >= 1 is
+    the number of blocks the wave walks in phase p (an empty share is one empty
+    block)."""
+    s = Wave()
+
+    class St:
+        pass
+
+    S = St()
+    S.p = p0
+    S.k = 0            # blocks of phase S.p already loaded
+    S.done = False
+
+    def begin_phase(p):
+        S.p, S.k = p, 0
+        s.ev("read_runs", p)       # header copied into registers
+
+    def load_block():
+        if S.done:
+            return ("empty", None, False)
+        p = S.p
+        s.ev("read_runs", p)       # lane-parallel unit descriptors
+        S.k += 1
+        last = S.k >= nblocks[p]
+        if last:
+            if p + 1 < p1:
+                begin_phase(p + 1)
+            else:
+                S.done = True
+        return ("blk", p, last)
+
+    def consume(blk):
+        kind, p, last = blk
+        if kind == "blk":
+            s.ev("read_xhat", p)
+            s.ev("write_part", p)  # any block may end a row-part segment
+
+    s.barrier()                    # run lists of the first phases are in LDS
+    begin_phase(p0)
+    A = load_block()
+    Bb = load_block()
+    s.barrier()                    # x-hat of the first phase
+    p = p0
+    ok = True
+    while ok and p < p1:
+        consume(A)
+        endA = A[2]
+        if endA:
+            s.barrier()            # partials of phase p
+        A = load_block()
+        if endA:
+            p += 1
+            if p < p1:
+                s.barrier()        # x-hat of phase p
+        consume(Bb)
+        endB = Bb[2]
+        if endB:
+            s.barrier()
+        Bb = load_block()
+        if endB:
+            p += 1
+            if p < p1:
+                s.barrier()
+    return s
+
+
+def check_schedule(p0, p1, nblocks, desc_bufs=DESC_BUFS, desc_ahead=DESC_AHEAD):
+    c = control_events(p0, p1, desc_ahead)
+    waves = [stream_events(p0, p1, nb) for nb in nblocks]
+    errors = []
+    for s in waves:
+        if s.epoch != c.epoch:
+            errors.append("barrier count %d != %d" % (s.epoch, c.epoch))
+    build_epoch = {q: e for e, k, q in c.events if k == "build"}
+    xhat_epoch = {q: e for e, k, q in c.events if k == "write_xhat"}
+    part_read = {q: e for e, k, q in c.events if k == "read_part"}
+    for q in range(p0, p1):
+        if q not in build_epoch:
+            errors.append("phase %d never built" % q)
+    # streaming-wave reads need a barrier after the build; the control wave
+    # reads its own builds in program order, so only the overwrite matters there
+    for s in waves:
+        for e, k, q in s.events:
+            if k != "read_runs":
+                continue
+            if not e > build_epoch[q]:
+                errors.append("runs %d read in epoch %d, built in epoch %d" % (q, e, build_epoch[q]))
+            nxt = q + desc_bufs
+            if nxt in build_epoch and not e < build_epoch[nxt]:
+                errors.append("runs %d read in epoch %d, overwritten by %d in epoch %d"
+                              % (q, e, nxt, build_epoch[nxt]))
+    build_pos = {q: i for i, (e, k, q) in enumerate(c.events) if k == "build"}
+    for i, (e, k, q) in enumerate(c.events):
+        if k == "read_runs":
+            if not build_pos[q] < i or (q + desc_bufs in build_pos and not i < build_pos[q + desc_bufs]):
+                errors.append("control wave reads runs %d out of order" % q)
+    for s in waves:
+        for e, k, q in s.events:
+            if k == "read_xhat":
+                if not e > xhat_epoch[q]:
+                    errors.append("x-hat %d read before it is written" % q)
+                if q + 1 in xhat_epoch and not e < xhat_epoch[q + 1]:
+                    errors.append("x-hat %d read after phase %d overwrote it" % (q, q + 1))
+            if k == "write_part":
+                if not e < part_read[q]:
+                    errors.append("partials of %d written after the epilogue read them" % q)
+                if q - 1 in part_read and not e > part_read[q - 1]:
+                    errors.append("partials of %d written before the epilogue of %d" % (q, q - 1))
+    return errors
+
+
+def test_schedule_random_block_counts():
+    rng = random.Random(1234)
+    for _ in range(3000):
+        P = rng.randint(1, 12)
+        W = rng.randint(1, 7)
+        nb = [[rng.choice([1, 1, 1, 2, 3, 5]) for _ in range(P)] for _ in range(W)]
+        errs = check_schedule(0, P, nb)
+        assert not errs, (P, nb, errs[:3])
+
+
+def test_schedule_exhaustive_small():
+    import itertools
+    for P in range(1, 7):
+        for nb in itertools.product([1, 2, 3], repeat=P):
+            errs = check_schedule(0, P, [list(nb), [1] * P])
+            assert not errs, (nb, errs[:3])
+
+
+def test_schedule_launch_window():
+    """A launch may cover phases [p0, p1) of a longer program."""
+    for p0, p1 in [(3, 4), (2, 9), (5, 6)]:
+        nb = [[1] * 9, [2] * 9]
+        assert not check_schedule(p0, p1, nb)
+
+
+def test_model_detects_building_too_late():
+    """Two phases of look-ahead into three buffers is too little when a wave
+    walks a one-block phase: the model must flag it."""
+    errs = check_schedule(0, 6, [[1, 1, 1, 1, 1, 1]], desc_bufs=3, desc_ahead=2)
+    assert any("built in epoch" in e for e in errs), errs
+
+
+def test_model_detects_ring_too_small():
+    errs = check_schedule(0, 8, [[1] * 8], desc_bufs=3, desc_ahead=3)
+    assert any("overwritten" in e for e in errs), errs

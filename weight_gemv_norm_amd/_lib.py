@@ -5,8 +5,10 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libwgn.so")
+# WGN_LIB_PATH selects another build of the same library (tuning experiments).
+LIB_PATH = os.environ.get("WGN_LIB_PATH") or os.path.join(HERE, "libwgn.so")
 
+TRACE_POINTS = 9
 OK, E_ARG, E_ALIGN, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_DEVICE, E_TIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7
 NORM_NONE, NORM_RMS, NORM_LAYER = 0, 1, 2
 EPI_NONE, EPI_GELU_TANH, EPI_SWIGLU, EPI_ARGMAX = 0, 1, 2, 3
@@ -36,7 +38,7 @@ class Stage(ctypes.Structure):
 
 class ChainOpts(ctypes.Structure):
     """Mirror of wgn_chain_opts."""
-    _fields_ = [("mode", I32), ("grid", I32), ("reserved", I32 * 6)]
+    _fields_ = [("mode", I32), ("grid", I32), ("trace", I32), ("reserved", I32 * 5)]
 
 
 class WgnError(RuntimeError):
@@ -77,6 +79,8 @@ def lib() -> ctypes.CDLL:
         "wgn_chain_run": ([P, P], I32),
         "wgn_chain_check": ([P, P], I32),
         "wgn_chain_num_phases": ([P], I32),
+        "wgn_chain_grid": ([P], I32),
+        "wgn_chain_trace": ([P, P, ctypes.POINTER(ctypes.c_uint64), SZ], I32),
         "wgn_chain_stage_phases": ([P, ctypes.POINTER(I32)], I32),
         "wgn_chain_destroy": ([P], None),
         "wgn_layer_chain": ([SP, I32, I32, OP, P, SZ, P], I32),

@@ -115,10 +115,11 @@ def rmsnorm_rows(x: torch.Tensor, gamma: torch.Tensor, eps: float, y: torch.Tens
     L.check(st, "wgn_rmsnorm_rows")
 
 
-def _opts(mode: int, grid: int) -> ChainOpts:
+def _opts(mode: int, grid: int, trace: bool = False) -> ChainOpts:
     o = ChainOpts()
     o.mode = mode
     o.grid = grid
+    o.trace = 1 if trace else 0
     return o
 
 
@@ -132,11 +133,11 @@ class Chain:
     """A planned chain (wgn_chain_create); run() enqueues one pass."""
 
     def __init__(self, stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 0,
-                 ws: Optional[torch.Tensor] = None, stream=None, device="cuda"):
+                 ws: Optional[torch.Tensor] = None, stream=None, device="cuda", trace: bool = False):
         self._arr = L.stage_array(stages)
         self.n_stages = len(stages)
         self.batch = batch
-        o = _opts(mode, grid)
+        o = _opts(mode, grid, trace)
         need = L.lib().wgn_chain_workspace_bytes(self._arr, len(stages), batch, ctypes.byref(o))
         if need == 0:
             # planning failed: let create report the precise status
@@ -157,6 +158,20 @@ class Chain:
     @property
     def num_phases(self) -> int:
         return int(L.lib().wgn_chain_num_phases(self._h))
+
+    @property
+    def grid(self) -> int:
+        return int(L.lib().wgn_chain_grid(self._h))
+
+    def trace(self, stream=None):
+        """Timestamps of the last run, shape [phases][grid][TRACE_POINTS], in 10 ns ticks."""
+        import numpy as np
+        n = self.num_phases * self.grid * L.TRACE_POINTS
+        out = np.zeros(n, dtype=np.uint64)
+        st = L.lib().wgn_chain_trace(self._h, _stream(stream),
+                                     out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), n)
+        L.check(st, "wgn_chain_trace")
+        return out.reshape(self.num_phases, self.grid, L.TRACE_POINTS)
 
     def stage_phases(self) -> List[int]:
         out = (ctypes.c_int32 * self.n_stages)()

@@ -19,17 +19,19 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-o", tmp] + SOURCES
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile libwgn.so.  `defines` (e.g. ["WGN_DEPTH=8"]) override the
+    kernel's tuning constants for experimental builds written to `out`."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + ["-o", tmp] + SOURCES
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libwgn.so")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def stale() -> bool:

@@ -150,8 +150,19 @@ struct Program {
     std::vector<int32_t> rowb;
     std::vector<int32_t> phase_of_stage;
     int32_t n_argmax = 0;
-    size_t lds_x_bytes = 0, lds_part_bytes = 0;
+    size_t lds_x_bytes = 0, lds_part_bytes = 0, lds_prm_bytes = 0, lds_epi_bytes = 0;
+    // dynamic LDS layout: [x-hat][partials][gains/shifts][epilogue inputs]
+    size_t prm_off() const { return lds_x_bytes + al16(lds_part_bytes); }
+    size_t epi_off() const { return prm_off() + al16(lds_prm_bytes); }
+    size_t desc_off() const { return epi_off() + al16(lds_epi_bytes); }
+    // + 6 streaming-wave trace timestamps
+    size_t lds_total() const { return desc_off() + (size_t)DESC_BUFS * RUN_BUF_BYTES + 6 * 8; }
+    static size_t al16(size_t v) { return (v + 15) & ~size_t(15); }
 };
+
+// LDS bytes of the gain/shift area of one source (gain then shift, padded to
+// whole units), matching the device's layout.
+inline size_t prm_bytes_of(int32_t K) { return (size_t)nchunks_of(K) * UNIT * 2 * 2; }
 
 DevStage make_dev_stage(const wgn_stage &s) {
     DevStage d;
@@ -263,8 +274,12 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, Progra
             }
             max_rp = std::max(max_rp, rp);
         }
+        size_t prm = 0;
+        for (int32_t i = 0; i < cur.nsrc; ++i) prm += prm_bytes_of(P.sources[cur.src0 + i].K);
         P.lds_x_bytes = std::max(P.lds_x_bytes, al256((size_t)B * xb * 2));
         P.lds_part_bytes = std::max(P.lds_part_bytes, (size_t)max_rp * cur.jmax * B * 4);
+        P.lds_prm_bytes = std::max(P.lds_prm_bytes, prm);
+        P.lds_epi_bytes = std::max(P.lds_epi_bytes, (size_t)max_rp * (1 + B) * 4);
         cur.wait = P.phases.empty() ? 0 : 1;
         P.phases.push_back(cur);
         open = false;
@@ -279,6 +294,7 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, Progra
             for (int32_t q = cur.src0; q < (int32_t)P.sources.size(); ++q)
                 if (same_source(P.sources[q], s)) src_idx = q - cur.src0;
             if (src_idx < 0 && (int32_t)P.sources.size() - cur.src0 >= MAX_SRC) conflict = true;
+            if ((int32_t)P.stages.size() - cur.stage0 >= MAX_RUNS) conflict = true;
         }
         if (conflict) close_phase();
         if (!open) {
@@ -303,15 +319,16 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, Progra
         ph_writes.insert(ph_writes.end(), w.begin(), w.end());
     }
     close_phase();
-    if (P.lds_x_bytes + P.lds_part_bytes > LDS_BUDGET) return WGN_E_UNSUPPORTED;
+    if (P.lds_total() > LDS_BUDGET) return WGN_E_UNSUPPORTED;
     return WGN_OK;
 }
 
 struct WsLayout {
-    size_t phases, stages, sources, rowb, ctr, tickets, err, am_part, total;
+    // ctr..am_part is the synchronisation area (flags, run counter, tickets, error word)
+    size_t phases, stages, sources, rowb, ctr, run, tickets, err, am_part, trace, total;
 };
 
-WsLayout ws_layout(const Program &P) {
+WsLayout ws_layout(const Program &P, bool trace) {
     WsLayout L;
     size_t o = 0;
     L.phases = o;
@@ -323,13 +340,17 @@ WsLayout ws_layout(const Program &P) {
     L.rowb = o;
     o += al256(P.rowb.size() * sizeof(int32_t));
     L.ctr = o;
-    o += al256(P.phases.size() * sizeof(uint32_t));
+    o += al256(P.phases.size() * (size_t)flag_row(P.G) * sizeof(uint32_t));
+    L.run = o;
+    o += 256;
     L.tickets = o;
     o += al256((size_t)(P.n_argmax + 1) * sizeof(uint32_t));
     L.err = o;
     o += 256;
     L.am_part = o;
     o += al256((size_t)P.n_argmax * P.G * P.B * sizeof(uint64_t));
+    L.trace = o;
+    if (trace) o += al256(P.phases.size() * (size_t)P.G * TRACE_POINTS * sizeof(uint64_t));
     L.total = o;
     return L;
 }
@@ -361,8 +382,14 @@ void single_geometry(const wgn_stage &s, int32_t B, int32_t cus, SingleLaunch &L
     const int32_t jmax = std::min(STREAM_WAVES, nch);
     const int32_t rows_max = (int32_t)((s.N + L.G - 1) / L.G);
     const size_t xbytes = al256((size_t)B * nch * UNIT * 2);
-    L.lds = xbytes + (size_t)rows_max * parts * jmax * B * 4;
+    const size_t part = Program::al16((size_t)rows_max * parts * jmax * B * 4);
+    const size_t prm = Program::al16(prm_bytes_of(s.K));
+    const size_t epi = Program::al16((size_t)rows_max * parts * (1 + B) * 4);
+    L.lds = xbytes + part + prm + epi + (size_t)DESC_BUFS * RUN_BUF_BYTES + 6 * 8;
     L.a.lds_x_bytes = (int32_t)xbytes;
+    L.a.lds_prm_off = (int32_t)(xbytes + part);
+    L.a.lds_epi_off = (int32_t)(xbytes + part + prm);
+    L.a.lds_desc_off = (int32_t)(xbytes + part + prm + epi);
     L.ws = s.epi == EPI_ARGMAX ? 256 + al256((size_t)L.G * B * sizeof(uint64_t)) : 0;
     DevPhase &ph = L.a.iph;
     ph.stage0 = 0;
@@ -393,6 +420,7 @@ void single_geometry(const wgn_stage &s, int32_t B, int32_t cus, SingleLaunch &L
 struct wgn_chain {
     Program P;
     KArgs a;
+    bool trace;
     int32_t mode;
     size_t lds;
     void *ws;
@@ -507,7 +535,7 @@ size_t wgn_chain_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int3
                                  const wgn_chain_opts *opts) {
     Program P;
     if (plan(stages, n_stages, batch, resolve_grid(opts), P) != WGN_OK) return 0;
-    return ws_layout(P).total;
+    return ws_layout(P, opts && opts->trace).total;
 }
 
 wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t batch, const wgn_chain_opts *opts,
@@ -515,8 +543,9 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     if (!out) return WGN_E_ARG;
     *out = nullptr;
     if (opts) {
-        if (opts->mode < 0 || opts->mode > 1 || opts->grid < 0) return WGN_E_ARG;
-        for (int i = 0; i < 6; ++i)
+        if (opts->mode < 0 || opts->mode > 1 || opts->grid < 0 || opts->trace < 0 || opts->trace > 1)
+            return WGN_E_ARG;
+        for (int i = 0; i < 5; ++i)
             if (opts->reserved[i]) return WGN_E_ARG;
     }
     wgn_chain *c = new (std::nothrow) wgn_chain();
@@ -531,14 +560,15 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
         delete c;
         return WGN_E_DEVICE;
     }
-    c->L = ws_layout(c->P);
+    c->trace = opts && opts->trace;
+    c->L = ws_layout(c->P, c->trace);
     if (!workspace || ws_bytes < c->L.total || (reinterpret_cast<uintptr_t>(workspace) & 255u)) {
         delete c;
         return WGN_E_WORKSPACE;
     }
     c->mode = opts ? opts->mode : 0;
     c->ws = workspace;
-    c->lds = c->P.lds_x_bytes + c->P.lds_part_bytes;
+    c->lds = c->P.lds_total();
     // host image of the program, then one upload
     std::vector<char> img(c->L.ctr, 0);
     std::memcpy(img.data() + c->L.phases, c->P.phases.data(), c->P.phases.size() * sizeof(DevPhase));
@@ -559,16 +589,21 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     a.stages = (const DevStage *)(ws + c->L.stages);
     a.sources = (const DevSource *)(ws + c->L.sources);
     a.rowb = (const int32_t *)(ws + c->L.rowb);
-    a.ctr = (uint32_t *)(ws + c->L.ctr);
+    a.flags = (uint32_t *)(ws + c->L.ctr);
+    a.run = (uint32_t *)(ws + c->L.run);
     a.tickets = (uint32_t *)(ws + c->L.tickets);
     a.err = (uint32_t *)(ws + c->L.err);
     a.am_part = (uint64_t *)(ws + c->L.am_part);
+    a.trace = c->trace ? (uint64_t *)(ws + c->L.trace) : nullptr;
     a.p0 = 0;
     a.p1 = (int32_t)c->P.phases.size();
     a.persistent = c->mode == 0 ? 1 : 0;
     a.G = c->P.G;
     a.n_argmax = c->P.n_argmax;
     a.lds_x_bytes = (int32_t)c->P.lds_x_bytes;
+    a.lds_prm_off = (int32_t)c->P.prm_off();
+    a.lds_epi_off = (int32_t)c->P.epi_off();
+    a.lds_desc_off = (int32_t)c->P.desc_off();
     a.ist.W = (const uint16_t *)stages[0].W;  // address used by empty (zero-length) loads
     *out = c;
     return WGN_OK;
@@ -599,12 +634,30 @@ wgn_status wgn_chain_check(const wgn_chain *c, wgn_stream stream) {
     if (note(hipMemcpy(&err, (char *)c->ws + c->L.err, 4, hipMemcpyDeviceToHost), "chain check read") != hipSuccess)
         return WGN_E_HIP;
     if (!err) return WGN_OK;
-    if (note(hipMemset((char *)c->ws + c->L.ctr, 0, c->L.am_part - c->L.ctr), "chain reset") != hipSuccess)
+    // an aborted run left flags and tickets behind: clear them (the run
+    // counter is kept; flags from the aborted run are erased)
+    char *w = (char *)c->ws;
+    if (note(hipMemset(w + c->L.ctr, 0, c->L.run - c->L.ctr), "chain reset flags") != hipSuccess ||
+        note(hipMemset(w + c->L.tickets, 0, c->L.am_part - c->L.tickets), "chain reset tickets") != hipSuccess)
         return WGN_E_HIP;
     return WGN_E_TIMEOUT;
 }
 
 int32_t wgn_chain_num_phases(const wgn_chain *c) { return c ? (int32_t)c->P.phases.size() : -1; }
+
+int32_t wgn_chain_grid(const wgn_chain *c) { return c ? c->P.G : -1; }
+
+wgn_status wgn_chain_trace(const wgn_chain *c, wgn_stream stream, uint64_t *out, size_t n_out) {
+    if (!c || !out) return WGN_E_ARG;
+    if (!c->trace) return WGN_E_UNSUPPORTED;
+    const size_t n = c->P.phases.size() * (size_t)c->P.G * TRACE_POINTS;
+    if (n_out < n) return WGN_E_ARG;
+    if (note(hipStreamSynchronize((hipStream_t)stream), "trace sync") != hipSuccess) return WGN_E_HIP;
+    if (note(hipMemcpy(out, (char *)c->ws + c->L.trace, n * sizeof(uint64_t), hipMemcpyDeviceToHost),
+             "trace read") != hipSuccess)
+        return WGN_E_HIP;
+    return WGN_OK;
+}
 
 wgn_status wgn_chain_stage_phases(const wgn_chain *c, int32_t *out) {
     if (!c || !out) return WGN_E_ARG;
@@ -651,13 +704,17 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
                 continue;
             }
             for (int32_t r = G.r0; r < G.r1; ++r) row_owner[r]++;
-            const int32_t U = G.U;
+            RunHdr h;
+            Run runs[MAX_RUNS];
+            make_runs<true>(a, p, g, h, runs);
+            const int32_t U = h.U;
+            if (U != G.U) ++bad;
             std::vector<uint32_t> slot_writes;
             for (int32_t w = 0; w < STREAM_WAVES; ++w) {
                 const int32_t ub = U > 0 ? wave_begin(w, U, STREAM_WAVES) : 0;
                 const int32_t ue = U > 0 ? wave_begin(w + 1, U, STREAM_WAVES) : 0;
                 for (int32_t v = ub; v < ue; ++v) {
-                    const UnitDesc d = unit_desc<true>(a, G, v, ub, ue, w, P.B);
+                    const UnitDesc d = unit_desc_runs(h, runs, v, ub, ue, w, P.B);
                     if ((d.meta & 0x8000u) == 0 || d.nbytes == 0 || (d.nbytes & 15u)) {
                         ++bad;
                         continue;
@@ -666,14 +723,21 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
                     if (((d.meta & 0x3FFFu) << 4) + UNIT * 2u > (uint32_t)ph.xb * 2u) ++bad;
                 }
                 // units just outside the wave's share are invalid
-                if (unit_desc<true>(a, G, ue, ub, ue, w, P.B).nbytes != 0) ++bad;
+                if (unit_desc_runs(h, runs, ue, ub, ue, w, P.B).nbytes != 0) ++bad;
             }
             // every unit of every owned row-part, once, with the right address
-            int32_t rp_base = 0, u_base = 0;
+            int32_t rp_base = 0, u_base = 0, nrun = 0;
+            if (h.nruns != ph.nstages) ++bad;
             std::vector<uint32_t> slot_reads;
             for (int32_t si = 0; si < ph.nstages; ++si) {
                 const DevStage &sg = P.stages[ph.stage0 + si];
                 StageSpan sp = stage_span(sg, G.r0, G.r1, 0, 0);
+                {
+                    const Run &r = runs[nrun++];
+                    if (r.stage != ph.stage0 + si || r.nrows != sp.nrows || (sp.nrows && r.row0 != sp.row0) ||
+                        r.u_base != u_base || r.rp_base != rp_base || r.epi != sg.epi || r.y != sg.y)
+                        ++bad;
+                }
                 for (int32_t i = 0; i < sp.nrows; ++i)
                     for (int32_t pt = 0; pt < sg.parts; ++pt) {
                         const int32_t rp = rp_base + i * sg.parts + pt;
@@ -683,7 +747,7 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
                             const int32_t w = first_wave(v, U, STREAM_WAVES);
                             const int32_t ub = wave_begin(w, U, STREAM_WAVES), ue = wave_begin(w + 1, U, STREAM_WAVES);
                             if (v < ub || v >= ue) ++bad;
-                            const UnitDesc d = unit_desc<true>(a, G, v, ub, ue, w, P.B);
+                            const UnitDesc d = unit_desc_runs(h, runs, v, ub, ue, w, P.B);
                             const uint16_t *rowp = (pt == 0 ? sg.W : sg.W_up) + (int64_t)(sp.row0 + i) * sg.K;
                             if (d.ptr != (uint64_t)(uintptr_t)rowp + (uint64_t)c * UNIT * 2u) ++bad;
                             if (d.nbytes != (uint32_t)(sg.K * 2 - c * UNIT * 2)) ++bad;
@@ -696,6 +760,7 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
                 rp_base += sp.nrows * sg.parts;
                 u_base += sp.nrows * sg.parts * sg.nchunks;
             }
+            if (nrun != h.nruns) ++bad;
             if (u_base != U) ++bad;
             std::sort(slot_writes.begin(), slot_writes.end());
             std::sort(slot_reads.begin(), slot_reads.end());

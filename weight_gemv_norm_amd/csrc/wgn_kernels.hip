@@ -29,7 +29,21 @@ namespace wgn {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int DEPTH = 16;                 // units per block (loads in flight per block)
+#ifndef WGN_DEPTH
+#define WGN_DEPTH 16
+#endif
+#ifndef WGN_WEIGHT_AUX
+#define WGN_WEIGHT_AUX 2  // nt: weights are streamed once
+#endif
+constexpr int DEPTH = WGN_DEPTH;          // units per block (loads in flight per block)
+constexpr int WEIGHT_AUX = WGN_WEIGHT_AUX;  // cache policy of the weight loads (streamed once)
+// Cache policy of every access to data that another workgroup produces or
+// consumes inside the same launch (stage outputs, completion flags, argmax
+// partials): sc0|sc1, the system-coherent level.  Stores are written through
+// and loads are served from the coherent level, so data written on one XCD
+// is visible to another without L2 write-back/invalidate fences (which cost
+// several microseconds per phase boundary on this chip).
+constexpr int COH = 17;
 constexpr uint32_t RSRC_W3 = 0x00020000u; // buffer descriptor word 3 for raw dword loads
 
 // ------------------------------------------------------------------ numerics
@@ -117,6 +131,10 @@ __device__ __forceinline__ void abort_flag_set(int32_t v) {
 
 __device__ __forceinline__ uint32_t lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
+__device__ __forceinline__ void trace_point(const KArgs &a, int32_t p, int32_t g, int i, uint32_t lane) {
+    if (a.trace && lane == 0) a.trace[((size_t)p * a.G + g) * TRACE_POINTS + i] = wall_clock64();
+}
+
 // ------------------------------------------------------------ streaming waves
 struct BlockMeta {
     uint32_t meta_v;       // lane j holds the meta word of the block's unit j
@@ -125,26 +143,36 @@ struct BlockMeta {
 };
 
 struct StreamState {
-    PhaseGeo G;
+    const char *desc;      // LDS run-list buffers
+    RunHdr h;              // header of the current phase's run list
+    const Run *runs;       // run list of the current phase (LDS)
+    int32_t p;
     int32_t u, u_beg, u_end;
     int32_t g, w, p1;
     bool done_all;
 };
 
-template <bool CHAIN>
-__device__ __forceinline__ void stream_begin_phase(const KArgs &a, StreamState &S, int32_t p) {
-    S.G = phase_geo<CHAIN>(a, p, S.g);
-    S.u_beg = S.G.U > 0 ? wave_begin(S.w, S.G.U, STREAM_WAVES) : 0;
-    S.u_end = S.G.U > 0 ? wave_begin(S.w + 1, S.G.U, STREAM_WAVES) : 0;
+__device__ __forceinline__ const char *run_buf(const char *desc, int32_t p) {
+    return desc + (p % DESC_BUFS) * RUN_BUF_BYTES;
+}
+
+__device__ __forceinline__ void stream_begin_phase(StreamState &S, int32_t p) {
+    const char *buf = run_buf(S.desc, p);
+    S.h = *(const RunHdr *)buf;
+    S.runs = (const Run *)(buf + sizeof(RunHdr));
+    S.p = p;
+    S.u_beg = S.h.U > 0 ? wave_begin(S.w, S.h.U, STREAM_WAVES) : 0;
+    S.u_end = S.h.U > 0 ? wave_begin(S.w + 1, S.h.U, STREAM_WAVES) : 0;
     S.u = S.u_beg;
 }
 
 // Issue DEPTH unit loads (a block never spans a phase boundary).  Lane j first
-// computes the descriptor of unit j; each load then takes its base address and
-// length from lane j through v_readlane.  Invalid slots load from an empty
-// range (no memory traffic, value 0), so every block issues the same number of
-// loads and the compiler's vmcnt accounting stays exact.
-template <int B, bool CHAIN>
+// computes the descriptor of unit j from the phase's run list in LDS; each
+// load then takes its base address and length from lane j through
+// v_readlane.  Invalid slots load from an empty range (no memory traffic,
+// value 0), so every block issues the same number of loads and the
+// compiler's vmcnt bookkeeping stays exact.
+template <int B>
 __device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4 (&d)[DEPTH], BlockMeta &bm,
                                            uint32_t lane) {
     UnitDesc ud;
@@ -152,11 +180,11 @@ __device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4
     ud.nbytes = 0;
     ud.meta = 0;
     if (!S.done_all && lane < (uint32_t)DEPTH)
-        ud = unit_desc<CHAIN>(a, S.G, S.u + (int32_t)lane, S.u_beg, S.u_end, S.w, B);
+        ud = unit_desc_runs(S.h, S.runs, S.u + (int32_t)lane, S.u_beg, S.u_end, S.w, B);
     if (ud.nbytes == 0) ud.ptr = (uint64_t)(uintptr_t)a.ist.W;
     const uint32_t plo = (uint32_t)ud.ptr, phi = (uint32_t)(ud.ptr >> 32);
     bm.meta_v = ud.meta;
-    bm.xb_bytes = S.done_all ? 0 : S.G.xb_bytes;
+    bm.xb_bytes = S.done_all ? 0 : S.h.xb_bytes;
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
         const uint32_t lo = __builtin_amdgcn_readlane(plo, j);
@@ -164,7 +192,7 @@ __device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4
         const uint32_t nb = __builtin_amdgcn_readlane(ud.nbytes, j);
         const void *base = (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
         __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)nb, (int)RSRC_W3);
-        d[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(lane * 16u), 0, 0);
+        d[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(lane * 16u), 0, WEIGHT_AUX);
     }
     if (S.done_all) {
         bm.last = false;  // past the final phase: nothing to synchronise
@@ -173,7 +201,7 @@ __device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4
     S.u = S.u + DEPTH < S.u_end ? S.u + DEPTH : S.u_end;
     bm.last = S.u >= S.u_end;
     if (bm.last) {
-        if (S.G.p + 1 < S.p1) stream_begin_phase<CHAIN>(a, S, S.G.p + 1);
+        if (S.p + 1 < S.p1) stream_begin_phase(S, S.p + 1);
         else S.done_all = true;
     }
 }
@@ -212,41 +240,61 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
     const char *xh = lds;
     float *part = (float *)(lds + a.lds_x_bytes);
     StreamState S;
+    S.desc = lds + a.lds_desc_off;
     S.g = g;
     S.w = w;
     S.p1 = a.p1;
     S.done_all = false;
-    stream_begin_phase<CHAIN>(a, S, a.p0);
+    wg_barrier();  // run lists of the first phases are in LDS
+    stream_begin_phase(S, a.p0);
     u32x4 dA[DEPTH], dB[DEPTH];
     BlockMeta mA, mB;
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.0f;
 
-    load_block<B, CHAIN>(a, S, dA, mA, lane);
+    // Two blocks are always in flight: a buffer is refilled as soon as it has
+    // been consumed.  When a block ends a phase, the refill is issued before
+    // waiting for the next phase's x-hat, so the weight stream keeps running
+    // through the device-wide phase boundary, and the first block of the next
+    // phase (loaded long before) is consumed as soon as x-hat is ready.
+    // The loop has no early exit and no global stores: past the final phase
+    // it only meets empty blocks (no barriers, no partial writes), which keeps
+    // the compiler's vmcnt bookkeeping exact.
+    uint64_t *tl = (uint64_t *)(lds + a.lds_desc_off + DESC_BUFS * RUN_BUF_BYTES);  // trace slots
+    const bool tw = a.trace && w == 0 && lane == 0;
+    load_block<B>(a, S, dA, mA, lane);
+    load_block<B>(a, S, dB, mB, lane);
     wg_barrier();  // x-hat of the first phase is ready
     bool ok = abort_flag_get() == 0;
     int32_t p = a.p0;
-    // Two blocks per iteration (register double buffering) and a single exit
-    // at the bottom, so the compiler sees one straight-line pipeline.
+    if (tw) tl[(p & 1) * 3 + 0] = wall_clock64();
     while (ok && p < a.p1) {
-        load_block<B, CHAIN>(a, S, dB, mB, lane);
         consume_block<B>(dA, mA, acc, xh, part, lane);
-        if (mA.last) {
+        const bool endA = mA.last;
+        if (endA) {
+            if (tw) tl[(p & 1) * 3 + 2] = wall_clock64();
             wg_barrier();  // partials of phase p are complete
-            if (++p < a.p1) {
-                wg_barrier();  // x-hat of phase p+1 is ready
-                ok = abort_flag_get() == 0;
-            }
         }
-        load_block<B, CHAIN>(a, S, dA, mA, lane);
+        load_block<B>(a, S, dA, mA, lane);
+        if (endA && ++p < a.p1) {
+            if (tw) tl[(p & 1) * 3 + 1] = wall_clock64();
+            wg_barrier();  // x-hat of phase p is ready
+            ok = abort_flag_get() == 0;
+            if (tw) tl[(p & 1) * 3 + 0] = wall_clock64();
+        }
         consume_block<B>(dB, mB, acc, xh, part, lane);
-        if (ok && mB.last) {
+        const bool endB = ok && mB.last;
+        if (endB) {
+            if (tw) tl[(p & 1) * 3 + 2] = wall_clock64();
             wg_barrier();
-            if (++p < a.p1) {
-                wg_barrier();
-                ok = abort_flag_get() == 0;
-            }
+        }
+        load_block<B>(a, S, dB, mB, lane);
+        if (endB && ++p < a.p1) {
+            if (tw) tl[(p & 1) * 3 + 1] = wall_clock64();
+            wg_barrier();
+            ok = abort_flag_get() == 0;
+            if (tw) tl[(p & 1) * 3 + 0] = wall_clock64();
         }
     }
 }
@@ -254,32 +302,85 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
 // --------------------------------------------------------------- control wave
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *(const u32x4 *)p; }
 
-// Stage every source of phase ph into LDS as BF16 x-hat (FP32 statistics).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7FFFFFFF, (int)RSRC_W3);
+}
+
+#define WGN_GAS __attribute__((address_space(1)))
+#define WGN_LAS __attribute__((address_space(3)))
+
+// Copy n8 16-byte chunks of global memory into LDS (lane i of iteration it
+// moves chunk it*64+i to dst + (it*64+i)*16).  Asynchronous: the caller waits.
+template <int AUX>
+__device__ __forceinline__ void copy_to_lds(const uint16_t *src, char *dst, int32_t n8, uint32_t lane) {
+    for (int32_t it = 0; it * 64 < n8; ++it) {
+        if (it * 64 + (int32_t)lane < n8)
+            __builtin_amdgcn_global_load_lds((const WGN_GAS void *)(src + ((size_t)it * 64 + lane) * 8),
+                                             (WGN_LAS void *)(dst + it * 1024), 16, 0, AUX);
+    }
+}
+
+// LDS bytes of the gain/shift area of one source (gain, then shift; padded).
+__device__ __forceinline__ int32_t prm_bytes(const DevSource &src) { return nchunks_of(src.K) * UNIT * 2 * 2; }
+
+// Issued before the device-wide wait: the norm gains and shifts do not depend
+// on any earlier phase, so their latency overlaps the wait.
+template <bool CHAIN>
+__device__ void prefetch_params(const KArgs &a, const DevPhase &ph, char *prm, uint32_t lane) {
+    int32_t off = 0;
+    for (int32_t si = 0; si < ph.nsrc; ++si) {
+        const DevSource src = source_of<CHAIN>(a, ph.src0 + si);
+        const int32_t n8 = src.K >> 3;
+        if (src.norm != NORM_NONE && src.gamma) copy_to_lds<0>(src.gamma, prm + off, n8, lane);
+        if (src.norm == NORM_LAYER && src.beta) copy_to_lds<0>(src.beta, prm + off + prm_bytes(src) / 2, n8, lane);
+        off += prm_bytes(src);
+    }
+}
+
+// Staging of the phase's inputs as BF16 x-hat in LDS (FP32 statistics): all
+// input chunks are requested at once (one memory round trip) together with the
+// epilogue's bias/residual values, then the statistics and the normalisation
+// run out of LDS.
 template <int B, bool CHAIN>
-__device__ void prepare_sources(const KArgs &a, const DevPhase &ph, char *xh, uint32_t lane) {
+__device__ void issue_source_loads(const KArgs &a, const DevPhase &ph, char *xh, uint32_t lane) {
+    for (int32_t si = 0; si < ph.nsrc; ++si) {
+        const DevSource src = source_of<CHAIN>(a, ph.src0 + si);
+        const int32_t n8 = src.K >> 3;
+        const int32_t padded8 = nchunks_of(src.K) * (UNIT / 8);
+        for (int b = 0; b < B; ++b) {
+            char *dst = xh + ((size_t)b * ph.xb + src.lds_off) * 2;
+            copy_to_lds<COH>(src.x + (int64_t)b * src.x_stride, dst, n8, lane);
+            for (int32_t i = n8 + lane; i < padded8; i += 64) *(u32x4 *)(dst + i * 16) = (u32x4){0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+// Statistics and normalisation out of LDS, after the copies have landed.
+template <int B, bool CHAIN>
+__device__ void finish_sources(const KArgs &a, const DevPhase &ph, char *xh, const char *prm, uint32_t lane) {
+    int32_t poff = 0;
     for (int32_t si = 0; si < ph.nsrc; ++si) {
         const DevSource src = source_of<CHAIN>(a, ph.src0 + si);
         const int32_t K = src.K;
         const int32_t n8 = K >> 3;
-        const int32_t padded8 = nchunks_of(K) * (UNIT / 8);
         const float invK = 1.0f / (float)K;
+        const char *gp = prm + poff;
+        const char *bp = prm + poff + prm_bytes(src) / 2;
+        poff += prm_bytes(src);
+        if (src.norm == NORM_NONE) continue;
         for (int b = 0; b < B; ++b) {
             uint16_t *dst = (uint16_t *)(xh + ((size_t)b * ph.xb + src.lds_off) * 2);
-            const uint16_t *xr = src.x + (int64_t)b * src.x_stride;
             float s1 = 0.0f, s2 = 0.0f;
             for (int32_t i = lane; i < n8; i += 64) {
-                u32x4 v = ld16(xr + i * 8);
-                *(u32x4 *)(dst + i * 8) = v;
-                uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+                const u32x4 v = *(const u32x4 *)(dst + i * 8);
+                const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float lo = bf2f(vv[e] & 0xFFFFu), hi = bf2f(vv[e] >> 16);
+                    const float lo = bf2f(vv[e] & 0xFFFFu), hi = bf2f(vv[e] >> 16);
                     s1 += lo + hi;
                     s2 += lo * lo + hi * hi;
                 }
             }
-            for (int32_t i = n8 + lane; i < padded8; i += 64) *(u32x4 *)(dst + i * 8) = (u32x4){0u, 0u, 0u, 0u};
-            if (src.norm == NORM_NONE) continue;
             float mean = 0.0f, rstd;
             if (src.norm == NORM_RMS) {
                 s2 = wave_sum(s2);
@@ -289,11 +390,11 @@ __device__ void prepare_sources(const KArgs &a, const DevPhase &ph, char *xh, ui
                 mean = s1 * invK;
                 float sv = 0.0f;
                 for (int32_t i = lane; i < n8; i += 64) {
-                    u32x4 v = *(const u32x4 *)(dst + i * 8);
-                    uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+                    const u32x4 v = *(const u32x4 *)(dst + i * 8);
+                    const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        float lo = bf2f(vv[e] & 0xFFFFu) - mean, hi = bf2f(vv[e] >> 16) - mean;
+                        const float lo = bf2f(vv[e] & 0xFFFFu) - mean, hi = bf2f(vv[e] >> 16) - mean;
                         sv += lo * lo + hi * hi;
                     }
                 }
@@ -301,17 +402,19 @@ __device__ void prepare_sources(const KArgs &a, const DevPhase &ph, char *xh, ui
                 rstd = 1.0f / sqrtf(sv * invK + src.eps);
             }
             for (int32_t i = lane; i < n8; i += 64) {
-                u32x4 v = *(const u32x4 *)(dst + i * 8);
-                u32x4 gv = src.gamma ? ld16(src.gamma + i * 8)
-                                     : (u32x4){0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-                u32x4 bv = (src.norm == NORM_LAYER && src.beta) ? ld16(src.beta + i * 8) : (u32x4){0u, 0u, 0u, 0u};
-                uint32_t vv[4] = {v.x, v.y, v.z, v.w}, gg[4] = {gv.x, gv.y, gv.z, gv.w},
-                         bb[4] = {bv.x, bv.y, bv.z, bv.w};
+                const u32x4 v = *(const u32x4 *)(dst + i * 8);
+                const u32x4 gv = src.gamma ? *(const u32x4 *)(gp + i * 16)
+                                           : (u32x4){0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+                const u32x4 bv = (src.norm == NORM_LAYER && src.beta) ? *(const u32x4 *)(bp + i * 16)
+                                                                      : (u32x4){0u, 0u, 0u, 0u};
+                const uint32_t vv[4] = {v.x, v.y, v.z, v.w}, gg[4] = {gv.x, gv.y, gv.z, gv.w},
+                               bb[4] = {bv.x, bv.y, bv.z, bv.w};
                 uint32_t o[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float lo = (bf2f(vv[e] & 0xFFFFu) - mean) * rstd * bf2f(gg[e] & 0xFFFFu) + bf2f(bb[e] & 0xFFFFu);
-                    float hi = (bf2f(vv[e] >> 16) - mean) * rstd * bf2f(gg[e] >> 16) + bf2f(bb[e] >> 16);
+                    const float lo =
+                        (bf2f(vv[e] & 0xFFFFu) - mean) * rstd * bf2f(gg[e] & 0xFFFFu) + bf2f(bb[e] & 0xFFFFu);
+                    const float hi = (bf2f(vv[e] >> 16) - mean) * rstd * bf2f(gg[e] >> 16) + bf2f(bb[e] >> 16);
                     o[e] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
                 }
                 *(u32x4 *)(dst + i * 8) = (u32x4){o[0], o[1], o[2], o[3]};
@@ -320,37 +423,70 @@ __device__ void prepare_sources(const KArgs &a, const DevPhase &ph, char *xh, ui
     }
 }
 
+// While the streaming waves stream, stage the epilogue's bias and residual
+// values of this workgroup's rows into LDS (row-part rp's entry holds the
+// bias and then the residual of each batch row, as FP32).
+template <int B, bool CHAIN>
+__device__ void stage_epilogue_inputs(const KArgs &a, const RunHdr &h, const Run *runs, float *epi, uint32_t lane) {
+    for (int32_t ri = 0; ri < h.nruns; ++ri) {
+        const Run &r = runs[ri];
+        const uint16_t *bias = r.bias;
+        const uint16_t *res = r.residual;
+        if (!bias && !res) continue;
+        const int64_t res_stride = r.res_stride;
+        const int32_t row0 = r.row0, nrows = r.nrows, rp_base = r.rp_base, parts = r.parts;
+        const __amdgpu_buffer_rsrc_t rr = rsrc_of(res);
+        for (int32_t i = lane; i < nrows; i += 64) {
+            const int32_t n = row0 + i;
+            float *e = epi + (size_t)(rp_base + i * parts) * (1 + B);
+            e[0] = bias ? bf2f(bias[n]) : 0.0f;
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+                e[1 + b] = res ? bf2f(__builtin_amdgcn_raw_buffer_load_b16(
+                                      rr, (int)(((int64_t)b * res_stride + n) * 2), 0, COH))
+                               : 0.0f;
+        }
+    }
+}
+
 // Merge the per-workgroup argmax keys of one ARGMAX stage (called by the last
 // workgroup to arrive) and write the index / maximum outputs.
 template <int B>
-__device__ void argmax_merge(const KArgs &a, const DevStage &st, uint32_t lane) {
+__device__ void argmax_merge(const KArgs &a, int32_t am_slot, void *y, float *maxval, uint32_t lane) {
     for (int b = 0; b < B; ++b) {
         uint64_t best = 0;
         for (int32_t gg = lane; gg < a.G; gg += 64) {
-            uint64_t k = __hip_atomic_load(&a.am_part[((size_t)st.am_slot * a.G + gg) * B + b], __ATOMIC_RELAXED,
+            uint64_t k = __hip_atomic_load(&a.am_part[((size_t)am_slot * a.G + gg) * B + b], __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
             best = k > best ? k : best;
         }
         best = wave_max_u64(best);
         if (lane == 0) {
-            ((int32_t *)st.y)[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
-            if (st.maxval) st.maxval[b] = unorderable((uint32_t)(best >> 32));
+            __builtin_amdgcn_raw_buffer_store_b32(0xFFFFFFFFu - (uint32_t)best, rsrc_of(y), b * 4, 0, COH);
+            if (maxval)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(unorderable((uint32_t)(best >> 32))),
+                                                      rsrc_of(maxval), b * 4, 0, COH);
         }
     }
 }
 
 template <int B, bool CHAIN>
-__device__ void epilogue(const KArgs &a, const PhaseGeo &G, int32_t g, const float *part, uint32_t lane) {
-    int32_t rp_base = 0, u_base = 0;
-    for (int32_t si = 0; si < G.nstages; ++si) {
-        const DevStage st = stage_of<CHAIN>(a, G.stage0 + si);
-        const StageSpan sp = stage_span(st, G.r0, G.r1, 0, 0);
-        const int32_t parts = st.parts, nch = st.nchunks;
+__device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32_t g, const float *part,
+                         const float *epi, uint32_t lane) {
+    for (int32_t ri = 0; ri < h.nruns; ++ri) {
+        const Run &r = runs[ri];
+        const int32_t parts = r.parts, nch = r.nchunks, epi_kind = r.epi, row0 = r.row0, nrows = r.nrows;
+        const int32_t rp_base = r.rp_base, u_base = r.u_base;
+        const bool has_res = r.residual != nullptr, has_bias = r.bias != nullptr;
+        const int64_t y_stride = r.y_stride;
+        const int32_t N = r.N;
+        float *logits = r.logits;
+        const __amdgpu_buffer_rsrc_t ry = rsrc_of(r.y);
         uint64_t best[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) best[b] = 0;
-        for (int32_t i = lane; i < sp.nrows; i += 64) {
-            const int32_t n = sp.row0 + i;
+        for (int32_t i = lane; i < nrows; i += 64) {
+            const int32_t n = row0 + i;
             float acc0[B], acc1[B];
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
@@ -358,8 +494,8 @@ __device__ void epilogue(const KArgs &a, const PhaseGeo &G, int32_t g, const flo
                 const int32_t rp = rp_base + i * parts + pt;
                 const int32_t a0 = u_base + (i * parts + pt) * nch;
                 const int32_t span =
-                    first_wave(a0 + nch - 1, G.U, STREAM_WAVES) - first_wave(a0, G.U, STREAM_WAVES) + 1;
-                const float *pp = part + (size_t)rp * G.jmax * B;
+                    first_wave(a0 + nch - 1, h.U, STREAM_WAVES) - first_wave(a0, h.U, STREAM_WAVES) + 1;
+                const float *pp = part + (size_t)rp * h.jmax * B;
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
                     float s = pp[b];
@@ -368,61 +504,105 @@ __device__ void epilogue(const KArgs &a, const PhaseGeo &G, int32_t g, const flo
                     else acc1[b] = s;
                 }
             }
-            const float bias = st.bias ? bf2f(st.bias[n]) : 0.0f;
+            const float *ep = epi + (size_t)(rp_base + i * parts) * (1 + B);
+            const float bias = has_bias ? ep[0] : 0.0f;
 #pragma unroll
             for (int b = 0; b < B; ++b) {
                 const float z = acc0[b] + bias;
-                if (st.epi == EPI_ARGMAX) {
-                    if (st.logits) st.logits[(size_t)b * st.N + n] = z;
+                if (epi_kind == EPI_ARGMAX) {
+                    if (logits) logits[(size_t)b * N + n] = z;
                     const uint64_t key = ((uint64_t)orderable(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
                     best[b] = key > best[b] ? key : best[b];
                     continue;
                 }
                 float e;
-                if (st.epi == EPI_GELU_TANH) e = gelu_tanh(z);
-                else if (st.epi == EPI_SWIGLU) e = silu(z) * acc1[b];
+                if (epi_kind == EPI_GELU_TANH) e = gelu_tanh(z);
+                else if (epi_kind == EPI_SWIGLU) e = silu(z) * acc1[b];
                 else e = z;
-                if (st.residual) e += bf2f(st.residual[(int64_t)b * st.res_stride + n]);
-                ((uint16_t *)st.y)[(int64_t)b * st.y_stride + n] = f2bf(e);
+                if (has_res) e += ep[1 + b];
+                __builtin_amdgcn_raw_buffer_store_b16(f2bf(e), ry, (int)(((int64_t)b * y_stride + n) * 2), 0, COH);
             }
         }
-        if (st.epi == EPI_ARGMAX) {
+        if (epi_kind == EPI_ARGMAX) {
+            const int32_t am_slot = r.am_slot;
 #pragma unroll
             for (int b = 0; b < B; ++b) {
                 const uint64_t k = wave_max_u64(best[b]);
                 if (lane == 0)
-                    __hip_atomic_store(&a.am_part[((size_t)st.am_slot * a.G + g) * B + b], k, __ATOMIC_RELAXED,
+                    __hip_atomic_store(&a.am_part[((size_t)am_slot * a.G + g) * B + b], k, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
             }
-            release_agent();
+            // the partial keys are agent-scope atomic stores; once they have
+            // completed, the ticket tells the last workgroup to merge them
+            __builtin_amdgcn_s_waitcnt(0);
             uint32_t old = 0;
             if (lane == 0)
-                old = __hip_atomic_fetch_add(&a.tickets[st.am_slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                old = __hip_atomic_fetch_add(&a.tickets[am_slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             old = __shfl(old, 0);
             if (old == (uint32_t)(a.G - 1)) {
-                acquire_agent();
-                argmax_merge<B>(a, st, lane);
+                argmax_merge<B>(a, am_slot, r.y, r.maxval, lane);
                 if (lane == 0)
-                    __hip_atomic_store(&a.tickets[st.am_slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&a.tickets[am_slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        rp_base += sp.nrows * parts;
-        u_base += sp.nrows * parts * nch;
     }
+}
+
+// Write phase q's run list for workgroup g into its LDS buffer.
+template <bool CHAIN>
+__device__ void build_runs(const KArgs &a, int32_t q, int32_t g, char *desc, uint32_t lane) {
+    // every lane computes the same list; the runs go straight into LDS
+    char *buf = desc + (q % DESC_BUFS) * RUN_BUF_BYTES;
+    RunHdr h;
+    make_runs<CHAIN>(a, q, g, h, (Run *)(buf + sizeof(RunHdr)));
+    *(RunHdr *)buf = h;
+    (void)lane;
 }
 
 template <int B, bool CHAIN>
 __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
     const uint32_t lane = lane_id();
     const float *part = (const float *)(lds + a.lds_x_bytes);
+    char *prm = lds + a.lds_prm_off;
+    float *epi = (float *)(lds + a.lds_epi_off);
+    char *desc = lds + a.lds_desc_off;
     if (lane == 0) abort_flag_set(0);
+    const uint32_t flag_val =
+        a.persistent ? __hip_atomic_load(a.run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
+    // Run lists are built DESC_AHEAD (3) phases ahead into DESC_BUFS (4) LDS
+    // buffers.  A streaming wave keeps two blocks in flight beyond the one it
+    // consumes, so right after phase q's partials barrier it may load phase
+    // q+2's block and read phase q+3's list header; iteration q builds that
+    // list before its own x-hat barrier of phase q.  A buffer is rebuilt
+    // (iteration q rebuilds phase q-1's) only after every wave has passed the
+    // partials barrier of the phase it held.  (This schedule is modelled and
+    // checked on the host by tests/test_schedule.py.)
+    for (int32_t q = a.p0; q < a.p1 && q < a.p0 + DESC_AHEAD; ++q) build_runs<CHAIN>(a, q, g, desc, lane);
+    wg_barrier();
     for (int32_t p = a.p0; p < a.p1; ++p) {
         const DevPhase ph = phase_of<CHAIN>(a, p);
+        trace_point(a, p, g, 0, lane);
+        // descriptors, run lists and gains do not depend on the previous
+        // phase: prepare them before waiting for it
+        if (p + DESC_AHEAD < a.p1) build_runs<CHAIN>(a, p + DESC_AHEAD, g, desc, lane);
+        const char *rb = desc + (p % DESC_BUFS) * RUN_BUF_BYTES;
+        const RunHdr h = *(const RunHdr *)rb;
+        const Run *runs = (const Run *)(rb + sizeof(RunHdr));
+        prefetch_params<CHAIN>(a, ph, prm, lane);
         if (a.persistent && p > a.p0 && ph.wait) {
+            // every workgroup's flag of phase p-1 must carry this run's value
+            const __amdgpu_buffer_rsrc_t rf = rsrc_of(a.flags + (size_t)(p - 1) * flag_row(a.G));
             const uint64_t t0 = wall_clock64();
             bool timed_out = false;
-            while (__hip_atomic_load(&a.ctr[p - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)a.G) {
-                __builtin_amdgcn_s_sleep(1);
+            for (;;) {
+                bool ok = true;
+                for (int32_t i = (int32_t)lane * 4; i < a.G; i += 256) {
+                    const u32x4 f = __builtin_amdgcn_raw_buffer_load_b128(rf, i * 4, 0, COH);
+                    const uint32_t ff[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ok &= (i + e >= a.G) || ff[e] == flag_val;
+                }
+                if (__all(ok)) break;
                 if (wall_clock64() - t0 > WAIT_TICKS) {
                     timed_out = true;
                     break;
@@ -436,32 +616,43 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
                 wg_barrier();  // releases the streaming waves, which then exit
                 return;
             }
-            acquire_agent();
         }
-        prepare_sources<B, CHAIN>(a, ph, lds, lane);
+        trace_point(a, p, g, 1, lane);
+        issue_source_loads<B, CHAIN>(a, ph, lds, lane);
+        stage_epilogue_inputs<B, CHAIN>(a, h, runs, epi, lane);
+        __builtin_amdgcn_s_waitcnt(0);  // inputs, gains and epilogue values have landed
+        finish_sources<B, CHAIN>(a, ph, lds, prm, lane);
+        trace_point(a, p, g, 2, lane);
         wg_barrier();  // x-hat ready
         wg_barrier();  // partials complete
-        const PhaseGeo G = phase_geo<CHAIN>(a, p, g);
-        epilogue<B, CHAIN>(a, G, g, part, lane);
-        if (a.persistent) {
-            release_agent();
-            if (lane == 0) __hip_atomic_fetch_add(&a.ctr[p], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        trace_point(a, p, g, 3, lane);
+        if (a.trace && lane < 3) {
+            const uint64_t *tl = (const uint64_t *)(lds + a.lds_desc_off + DESC_BUFS * RUN_BUF_BYTES);
+            a.trace[((size_t)p * a.G + g) * TRACE_POINTS + 6 + lane] = tl[(p & 1) * 3 + lane];
         }
+        epilogue<B, CHAIN>(a, h, runs, g, part, epi, lane);
+        trace_point(a, p, g, 4, lane);
+        if (a.persistent) {
+            // outputs are written through (coherent stores); once they have
+            // completed, publish this workgroup's flag for phase p
+            __builtin_amdgcn_s_waitcnt(0);
+            if (lane == 0)
+                __builtin_amdgcn_raw_buffer_store_b32(flag_val, rsrc_of(a.flags + (size_t)p * flag_row(a.G)), g * 4, 0, COH);
+        }
+        trace_point(a, p, g, 5, lane);
     }
     if (a.persistent) {
-        // The last workgroup to finish resets the counters so the next run (or
-        // graph replay) starts from zero; every other workgroup is past all of
-        // its waits by then.
-        release_agent();
+        // The last workgroup to finish advances the run counter, so the next
+        // run (or graph replay) publishes flags with a new value; every other
+        // workgroup is past all of its waits by then.
+        __builtin_amdgcn_s_waitcnt(0);
         uint32_t old = 0;
         if (lane == 0)
             old = __hip_atomic_fetch_add(&a.tickets[a.n_argmax], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         old = __shfl(old, 0);
-        if (old == (uint32_t)(a.G - 1)) {
-            acquire_agent();
-            for (int32_t p = a.p0 + (int32_t)lane; p < a.p1; p += 64)
-                __hip_atomic_store(&a.ctr[p], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (lane == 0) __hip_atomic_store(&a.tickets[a.n_argmax], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == (uint32_t)(a.G - 1) && lane == 0) {
+            __hip_atomic_store(a.run, flag_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.tickets[a.n_argmax], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

@@ -9,10 +9,12 @@
 // small PyTorch ops faster on a laptop GPU" (section "Prefetching the next
 // layer while this one runs") moved inside one persistent kernel.
 //
-// unit_desc() maps one unit index to its weight address and its meta word.
-// On the device lane j of a wave evaluates it for the j-th unit of a block
-// (one evaluation per lane per block); the host planner's self-test evaluates
-// it for every unit to check the partition.
+// make_runs() reduces a phase to the workgroup's "run list" (one entry per
+// stage with rows in the workgroup); unit_desc_runs() maps one unit index to
+// its weight address and its meta word.  On the device, the control wave
+// builds run lists three phases ahead into LDS and lane j of a streaming wave
+// evaluates unit_desc_runs() for the j-th unit of a block; the host planner's
+// self-test runs the same two functions for every unit to check the partition.
 #pragma once
 #include "wgn_prog.h"
 
@@ -80,51 +82,83 @@ WGN_HD PhaseGeo phase_geo(const KArgs &a, int32_t p, int32_t g) {
     return G;
 }
 
+// Run list of phase p for workgroup g: one entry per stage of the phase, in
+// order (nrows = 0 when the workgroup owns none of its rows; an argmax stage
+// still takes part in the merge then).
+template <bool CHAIN>
+WGN_HD void make_runs(const KArgs &a, int32_t p, int32_t g, RunHdr &h, Run *runs) {
+    const PhaseGeo G = phase_geo<CHAIN>(a, p, g);
+    h.U = G.U;
+    h.jmax = G.jmax;
+    h.xb_bytes = G.xb_bytes;
+    int32_t n = 0, u_base = 0, rp_base = 0;
+    for (int32_t i = 0; i < G.nstages && n < MAX_RUNS; ++i) {
+        const DevStage st = stage_of<CHAIN>(a, G.stage0 + i);
+        const StageSpan sp = stage_span(st, G.r0, G.r1, 0, 0);
+        Run r;
+        r.W = st.W;
+        r.W_up = st.W_up;
+        r.K = st.K;
+        r.nchunks = st.nchunks;
+        r.parts = st.parts;
+        r.row0 = sp.row0;
+        r.nrows = sp.nrows;
+        r.u_base = u_base;
+        r.rp_base = rp_base;
+        r.xoff = (uint32_t)source_of<CHAIN>(a, G.src0 + st.src).lds_off * 2u;
+        r.stage = G.stage0 + i;
+        r.epi = st.epi;
+        r.N = st.N;
+        r.am_slot = st.am_slot;
+        r.bias = st.bias;
+        r.residual = st.residual;
+        r.y = st.y;
+        r.logits = st.logits;
+        r.maxval = st.maxval;
+        r.res_stride = st.res_stride;
+        r.y_stride = st.y_stride;
+        runs[n++] = r;
+        u_base += sp.nrows * st.parts * st.nchunks;
+        rp_base += sp.nrows * st.parts;
+    }
+    h.nruns = n;
+}
+
 struct UnitDesc {
     uint64_t ptr;          // address of the unit's first byte (row start + chunk offset)
     uint32_t nbytes;       // bytes of the row from ptr on (0 = invalid unit: loads return 0)
     uint32_t meta;         // pack_meta(...)
 };
 
-// Descriptor of workgroup-local unit v of phase geometry G for stream wave w,
-// whose share of the phase is [u_beg, u_end).  B = batch.
-template <bool CHAIN>
-WGN_HD UnitDesc unit_desc(const KArgs &a, const PhaseGeo &G, int32_t v, int32_t u_beg, int32_t u_end, int32_t w,
-                          int32_t B) {
+// Descriptor of WG-local unit v from a run list (the form the kernel uses).
+WGN_HD UnitDesc unit_desc_runs(const RunHdr &h, const Run *runs, int32_t v, int32_t u_beg, int32_t u_end,
+                               int32_t w, int32_t B) {
     UnitDesc d;
     d.ptr = 0;
     d.nbytes = 0;
     d.meta = 0;
     if (v < u_beg || v >= u_end) return d;
-    int32_t base_u = 0, base_rp = 0;
-    for (int32_t i = 0; i < G.nstages; ++i) {
-        const DevStage st = stage_of<CHAIN>(a, G.stage0 + i);
-        const StageSpan sp = stage_span(st, G.r0, G.r1, 0, 0);
-        const int32_t per_row = st.parts * st.nchunks;
-        const int32_t su = sp.nrows * per_row;
-        if (v < base_u + su) {
-            const int32_t local = v - base_u;
+    for (int32_t i = 0; i < h.nruns; ++i) {
+        const Run &r = runs[i];
+        const int32_t per_row = r.parts * r.nchunks;
+        if (v < r.u_base + r.nrows * per_row) {
+            const int32_t local = v - r.u_base;
             const int32_t rk = local / per_row;
             const int32_t rem = local - rk * per_row;
-            const int32_t part = rem / st.nchunks;
-            const int32_t chunk = rem - part * st.nchunks;
-            const int32_t row = sp.row0 + rk;
+            const int32_t part = rem / r.nchunks;
+            const int32_t chunk = rem - part * r.nchunks;
             const uint32_t off = (uint32_t)chunk * (UNIT * 2u);
-            const uint16_t *rowp = (part == 0 ? st.W : st.W_up) + (int64_t)row * st.K;
+            const uint16_t *rowp = (part == 0 ? r.W : r.W_up) + (int64_t)(r.row0 + rk) * r.K;
             d.ptr = (uint64_t)(uintptr_t)rowp + off;
-            d.nbytes = (uint32_t)st.K * 2u - off;
-            const int32_t rp = base_rp + rk * st.parts + part;
+            d.nbytes = (uint32_t)r.K * 2u - off;
+            const int32_t rp = r.rp_base + rk * r.parts + part;
             const int32_t ua = v - chunk;
-            const int32_t j = ua < u_beg ? w - first_wave(ua, G.U, STREAM_WAVES) : 0;
-            const uint32_t slot = (uint32_t)((rp * G.jmax + j) * B);
-            const DevSource src = source_of<CHAIN>(a, G.src0 + st.src);
-            const uint32_t xoff = (uint32_t)src.lds_off * 2u + off;
-            const bool seg_end = (chunk == st.nchunks - 1) || (v == u_end - 1);
-            d.meta = pack_meta(xoff, seg_end, true, slot);
+            const int32_t j = ua < u_beg ? w - first_wave(ua, h.U, STREAM_WAVES) : 0;
+            const uint32_t slot = (uint32_t)((rp * h.jmax + j) * B);
+            const bool seg_end = (chunk == r.nchunks - 1) || (v == u_end - 1);
+            d.meta = pack_meta(r.xoff + off, seg_end, true, slot);
             return d;
         }
-        base_u += su;
-        base_rp += sp.nrows * st.parts;
     }
     return d;
 }

@@ -27,11 +27,18 @@ namespace wgn {
 
 constexpr int UNIT = 512;            // K elements per unit (64 lanes x 8 BF16)
 constexpr int MAX_SRC = 4;           // distinct normalised inputs per phase
-constexpr int STREAM_WAVES = 7;      // weight-streaming waves per WG
+#ifndef WGN_STREAM_WAVES
+#define WGN_STREAM_WAVES 7
+#endif
+constexpr int STREAM_WAVES = WGN_STREAM_WAVES;  // weight-streaming waves per WG
 constexpr int WAVES = STREAM_WAVES + 1;   // + one control wave
 constexpr int THREADS = WAVES * 64;
 constexpr int MAX_BATCH = 16;
 constexpr int MAX_BATCH_VALU = 4;
+constexpr int TRACE_POINTS = 9;
+constexpr int MAX_RUNS = 16;         // stages per phase (the planner splits larger phases)
+constexpr int DESC_BUFS = 4;         // phases whose run lists are resident in LDS at once
+constexpr int DESC_AHEAD = 3;        // the control wave builds phase p+DESC_AHEAD's list in iteration p
 constexpr uint64_t WAIT_TICKS = 200000000ull;  // 2 s at the 100 MHz real-time clock
 
 enum { NORM_NONE = 0, NORM_RMS = 1, NORM_LAYER = 2 };
@@ -86,15 +93,20 @@ struct KArgs {
     const DevStage *stages;
     const DevSource *sources;
     const int32_t *rowb;
-    uint32_t *ctr;         // [nphases] completion counters (persistent mode)
+    uint32_t *flags;       // [nphases][G] completion flags (persistent mode)
+    uint32_t *run;         // run counter: a run's flags carry the value run + 1
     uint32_t *tickets;     // [n_argmax] argmax tickets, then [1] done ticket
     uint64_t *am_part;     // [n_argmax][G][batch] packed (value, index) keys
     uint32_t *err;         // error word
+    uint64_t *trace;       // [nphases][G][TRACE_POINTS] timestamps, or null
     int32_t p0, p1;        // phases of this launch
     int32_t persistent;
     int32_t G;
     int32_t n_argmax;
     int32_t lds_x_bytes;   // offset of the partial area in dynamic LDS
+    int32_t lds_prm_off;   // offset of the norm gain/shift area
+    int32_t lds_epi_off;   // offset of the staged epilogue inputs (bias, residual)
+    int32_t lds_desc_off;  // offset of the per-phase run lists (DESC_BUFS buffers)
     DevPhase iph;
     DevStage ist;
     DevSource isrc;
@@ -118,6 +130,8 @@ WGN_HD int32_t even_row_begin(int32_t g, int32_t nrows, int32_t G) {
     return (int32_t)(((int64_t)g * nrows) / G);
 }
 WGN_HD int32_t nchunks_of(int32_t K) { return (K + UNIT - 1) / UNIT; }
+// Words per phase in the flag array (rows padded for 16-byte loads).
+WGN_HD int32_t flag_row(int32_t G) { return (G + 3) & ~3; }
 
 // Meta word of one streamed unit (wave-uniform):
 //   bits  0..13  x-hat byte offset / 16
@@ -128,6 +142,29 @@ WGN_HD uint32_t pack_meta(uint32_t xoff_bytes, bool seg_end, bool valid, uint32_
     return ((xoff_bytes >> 4) & 0x3FFFu) | (seg_end ? 0x4000u : 0u) | (valid ? 0x8000u : 0u) |
            (slot << 16);
 }
+
+// One stage's rows inside one workgroup's share of a phase, as the streaming
+// waves need it (built once per phase, read from LDS on the hot path).
+struct Run {
+    const uint16_t *W;
+    const uint16_t *W_up;
+    int32_t K, nchunks, parts, row0;   // row0: stage-local first row
+    int32_t nrows, u_base, rp_base;    // WG-local first unit / row-part (nrows may be 0)
+    uint32_t xoff;                     // LDS byte offset of the stage's source in a batch row
+    int32_t stage;                     // global stage index
+    // epilogue fields (read by the control wave)
+    int32_t epi, N, am_slot;
+    const uint16_t *bias;
+    const uint16_t *residual;
+    void *y;
+    float *logits;
+    float *maxval;
+    int64_t res_stride, y_stride;
+};
+struct RunHdr {
+    int32_t nruns, U, jmax, xb_bytes;
+};
+constexpr int RUN_BUF_BYTES = (int)(sizeof(RunHdr) + MAX_RUNS * sizeof(Run));
 
 // Per-(WG, stage) geometry inside a phase.
 struct StageSpan {
