@@ -36,6 +36,12 @@ def parse():
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--mode", type=int, default=0, help="0 persistent kernel, 1 one launch per phase")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after warm-up, run one plain device copy of this many MiB (the known-size "
+                         "reference for HBM byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
+                    help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a run with "
+                         "--calib-copy-mib into the traffic summary that later runs report; no GPU used")
     ap.add_argument("--cold", action="store_true",
                     help="stream a 512 MB scrub buffer between timed steps (evicts the Infinity Cache)")
     return ap.parse_args()
@@ -43,6 +49,10 @@ def parse():
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, workload=args.workload, batch=args.batch or 1,
+                      copy_mib=args.calib_copy_mib)
+        return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the weight stream runs on a single "
               "device); --gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -117,6 +127,13 @@ def main():
     if chain is not None:
         chain.check()
     print("[bench] warmup done", file=sys.stderr, flush=True)
+    if args.calib_copy_mib:
+        ca = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        cb = torch.empty_like(ca)
+        torch.cuda.synchronize()
+        cb.copy_(ca)
+        torch.cuda.synchronize()
+        del ca, cb
 
     # --------------------------------------------------------------- timing
     stream = torch.cuda.current_stream()
@@ -150,7 +167,7 @@ def main():
 
     roofline = {"bound": "hbm", "kernel": kernel_name, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                "traffic": None, "launch_us_mean": round(us_step, 3), "launch_us_median": round(us_med, 3),
+                "traffic": recorded_traffic(wl, B, kernel_name), "launch_us_mean": round(us_step, 3), "launch_us_median": round(us_med, 3),
                 "bytes_per_launch": nbytes}
 
     # ----------------------------------------------------------- CPU oracle
@@ -181,10 +198,97 @@ def main():
     }
     print(json.dumps(out), flush=True)
 
+# ------------------------------------------------------------ HBM counters
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "weight_gemv_norm_amd", "csrc")
 
-def cpu_baseline_decode(inp, bufs, nbytes):
-    """Time the CPU oracle (as it stands) on one full decode step of the same
-    workload: all 28 blocks and the LM head, free-running on its own outputs."""
+
+def kernel_sources_digest() -> str:
+    """SHA-256 over the kernel sources: recorded counter figures are reported
+    only while the kernels are unchanged since they were taken."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_file(workload, batch, kernel):
+    return os.path.join(ROOT, "profiles", "%s_%s_b%d_hbm_traffic.txt" % (kernel, workload, batch))
+
+
+def recorded_traffic(workload, batch, kernel):
+    path = traffic_file(workload, batch, kernel)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != kernel_sources_digest():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def _pmc_rows(path, counter):
+    import csv
+    rows = []
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") == counter:
+            rows.append((r["Kernel_Name"], int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_pmc(fetch_csv, write_csv, out_txt, workload, batch, copy_mib):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the chain kernel, scaled by
+    what the same counters read for a plain copy of copy_mib MiB."""
+    assert copy_mib > 0, "--calib-copy-mib of the profiled run is needed"
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _pmc_rows(path, counter)
+        # per dispatch, the counter summed over its instances
+        per = {}
+        for name, d, v in rows:
+            per.setdefault((name, d), 0.0)
+            per[(name, d)] += v
+        kern = [v for (n, d), v in per.items() if "chain_kernel" in n]
+        copies = [v for (n, d), v in per.items() if "copyBuffer" in n or "copy_kernel" in n]
+        assert kern and copies, (counter, len(kern), len(copies))
+        copy_kib = max(copies)  # the calibration copy is the largest copy of the run
+        scale = (copy_mib * 1024.0) / copy_kib
+        out[counter] = (float(np.median(kern)), copy_kib, scale, len(kern))
+    fetch = out["FETCH_SIZE"][0] * out["FETCH_SIZE"][2] * 1024
+    write = out["WRITE_SIZE"][0] * out["WRITE_SIZE"][2] * 1024
+    with open(out_txt, "w") as f:
+        f.write("# HBM traffic of chain_kernel, %s, batch %d (rocprofv3 --pmc, one counter per run)\n"
+                % (workload, batch))
+        f.write("# commands (from the repository root):\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            f.write("#   rocprofv3 --pmc %s --output-format csv -d gpurun_out/pmc_%s -o run -- python bench.py "
+                    "--workload %s --batch %d --steps 10 --warmup 3 --no-cpu-baseline --calib-copy-mib %d\n"
+                    % (c, c.lower(), workload, batch, copy_mib))
+        f.write("# calibration: a plain device copy of %d MiB reads and writes %d KiB\n"
+                % (copy_mib, copy_mib * 1024))
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            k, cp, sc, n = out[c]
+            f.write("%s_kib_per_dispatch_median: %.1f\n" % (c.lower(), k))
+            f.write("%s_dispatches: %d\n" % (c.lower(), n))
+            f.write("%s_copy_kib: %.1f\n" % (c.lower(), cp))
+            f.write("%s_scale: %.5f\n" % (c.lower(), sc))
+        f.write("fetch_bytes_per_launch: %d\n" % int(fetch))
+        f.write("write_bytes_per_launch: %d\n" % int(write))
+        f.write("traffic_bytes_per_launch: %d\n" % int(fetch + write))
+        f.write("kernel_sources_sha256: %s\n" % kernel_sources_digest())
+    print(open(out_txt).read())
+
+
+def cpu_baseline_decode(inp, bufs, nbytes, budget_s=12.0, max_steps=45):
+    """Time the CPU oracle (as it stands) on whole decode steps of the same
+    workload (all 28 blocks and the LM head, free-running on its own outputs),
+    repeated until about budget_s seconds of CPU work have been spent."""
     from oracle import oracle as O
     from synth.gen import bf16_bits_to_numpy as bb
     print("[bench] cpu baseline: copying weights to host", file=sys.stderr, flush=True)
@@ -193,21 +297,31 @@ def cpu_baseline_decode(inp, bufs, nbytes):
     threads = max(1, min(os.cpu_count() or 1, 16))
     O.set_threads(threads)
     eps = float(np.float32(inp["eps"]))
+
+    def one_step():
+        h = h0
+        for L in layers:
+            for name in ("wq", "wk", "wv"):
+                O.stage(h, L[name], norm=O.NORM_RMS, eps=eps, gamma=L["g1"])
+            h1 = O.stage(L["a"], L["wo"], residual=h)
+            s = O.stage(h1, L["wg"], norm=O.NORM_RMS, eps=eps, gamma=L["g2"], epi=O.EPI_SWIGLU, W_up=L["wu"])
+            h = O.stage(s, L["wd"], residual=h1)
+        return O.lmhead_argmax(h, g_f, W_lm, eps=eps)[0]
+
     t0 = time.perf_counter()
-    h = h0
-    for L in layers:
-        for name in ("wq", "wk", "wv"):
-            O.stage(h, L[name], norm=O.NORM_RMS, eps=eps, gamma=L["g1"])
-        h1 = O.stage(L["a"], L["wo"], residual=h)
-        s = O.stage(h1, L["wg"], norm=O.NORM_RMS, eps=eps, gamma=L["g2"], epi=O.EPI_SWIGLU, W_up=L["wu"])
-        h = O.stage(s, L["wd"], residual=h1)
-    idx, _ = O.lmhead_argmax(h, g_f, W_lm, eps=eps)
-    dt = time.perf_counter() - t0
-    print("[bench] cpu baseline: one step %.2f s on %d threads" % (dt, threads), file=sys.stderr, flush=True)
+    n = 0
+    while n < max_steps:
+        one_step()
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    print("[bench] cpu baseline: %d steps, %.3f s per step on %d threads" % (n, dt, threads),
+          file=sys.stderr, flush=True)
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seconds_per_step": round(dt, 3),
-            "sample": "one full decode step (28 blocks + LM head + argmax, batch 1) free-running in the "
-                      "binary64 C oracle, OpenMP over rows"}
+            "seconds_per_step": round(dt, 4), "us_per_step": round(dt * 1e6, 1),
+            "sample": "%d full decode steps (28 blocks + LM head + argmax, batch 1), free-running in the "
+                      "binary64 C oracle with OpenMP over rows; value = algorithmic bytes / mean step time" % n}
 
 
 if __name__ == "__main__":
