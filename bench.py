@@ -35,6 +35,8 @@ def parse():
                              "rmsnorm_gemv_256", "rmsnorm_rows_960x1536_f16", "lmhead_151936"])
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--mode", type=int, default=0, help="0 persistent kernel, 1 one launch per phase")
+    ap.add_argument("--path", type=int, default=0,
+                    help="0 auto (vector path for batch <= 4, matrix cores above), 1 vector, 2 matrix cores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after warm-up, run one plain device copy of this many MiB (the known-size "
@@ -77,18 +79,19 @@ def main():
     if wl in ("decode_step_1536x28", "decoder_block_1536"):
         inp = gen.make_stage_tensors(wl, device=dev, batch=B)
         stages, bufs = steps.decoder_stages(inp, dev)
-        chain = W.Chain(stages, B, mode=args.mode)
+        chain = W.Chain(stages, B, mode=args.mode, path=args.path)
         nb = steps.decode_step_bytes(inp)
         nbytes = nb["total"]
         cfg.update({"hidden": gen.H, "intermediate": gen.I, "layers": len(inp["layers"]),
                     "vocab": gen.V if "W_lm" in inp else None, "weight_bytes": nb["weights"],
                     "algorithmic_bytes": nbytes, "phases": chain.num_phases,
-                    "launch": "persistent" if args.mode == 0 else "per-phase"})
+                    "launch": "persistent" if args.mode == 0 else "per-phase",
+                    "path": "matrix" if (args.path == 2 or (args.path == 0 and B > 4)) else "vector"})
         launch = chain.run
     elif wl == "ln_gelu_chain_768x72":
         inp = gen.make_stage_tensors(wl, device=dev, batch=B)
         stages, bufs = steps.ln_gelu_chain_stages(inp, dev)
-        chain = W.Chain(stages, B, mode=args.mode)
+        chain = W.Chain(stages, B, mode=args.mode, path=args.path)
         nbytes = sum(L["W"].numel() * 2 + (L["bias"].numel() + L["gamma"].numel() + L["beta"].numel()) * 2
                      for L in inp["layers"]) + (len(inp["layers"]) + 1) * B * 768 * 2
         cfg.update({"width": 768, "blocks": 72, "algorithmic_bytes": nbytes, "phases": chain.num_phases,

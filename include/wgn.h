@@ -122,7 +122,12 @@ size_t wgn_gemv_norm_workspace_bytes(const wgn_stage *stage, int32_t batch);
 /* One norm-fused product, one kernel launch.  batch in [1, 16]; batch rows of
  * x, residual and y are independent.  The normalisation prologue is computed
  * by every workgroup from the whole input vector, so there is no separate
- * norm kernel.  Returns WGN_OK or an error (nothing enqueued on error). */
+ * norm kernel.  Batches up to 4 use the vector (v_dot2) path, larger batches
+ * the matrix-core path (v_mfma_f32_16x16x32_bf16, batch padded to 16 inside
+ * the kernel; padded rows are never stored).  A stage whose batch x K inputs
+ * do not fit in the 160 KB of LDS returns WGN_E_UNSUPPORTED here: a chain
+ * (wgn_layer_chain, even of one stage) streams such a stage in K windows.
+ * Returns WGN_OK or an error (nothing enqueued on error). */
 wgn_status wgn_gemv_norm(const wgn_stage *stage, int32_t batch,
                          void *workspace, size_t ws_bytes, wgn_stream stream);
 
@@ -159,7 +164,9 @@ typedef struct wgn_chain_opts {
     int32_t mode;        /* 0: one persistent launch (default); 1: one launch per phase */
     int32_t grid;        /* workgroups; 0 = one per compute unit                       */
     int32_t trace;       /* 1: record per-phase, per-workgroup timestamps (see below)  */
-    int32_t reserved[5]; /* must be zero                                               */
+    int32_t path;        /* 0: auto (vector path for batch <= 4, matrix cores above);   */
+                         /* 1: vector path (batch <= 4 only); 2: matrix-core path       */
+    int32_t reserved[4]; /* must be zero                                               */
 } wgn_chain_opts;
 
 /* Workspace bytes for a chain over these stages (mode/grid as in opts, NULL = defaults). */
@@ -209,12 +216,23 @@ wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t ba
  * unit `u` (exported so the partition rule can be tested on the host). */
 int32_t wgn_first_wave_of_unit(int32_t u, int32_t units, int32_t waves);
 
-/* Plan a chain on the host only (no device needed) for `grid` workgroups and
- * emulate every workgroup and wave of its work partition: each weight unit must
- * be streamed exactly once, each partial-sum slot written once and read by the
- * epilogue, each row owned by one workgroup.  Returns the number of violations
- * (0 = consistent) or a negative wgn_status if planning failed. */
-int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_t batch, int32_t grid);
+/* Plan a chain on the host only (no device needed; grid and path from opts,
+ * NULL or grid 0 = 256 workgroups) and return its number of phases, or a
+ * negative wgn_status.  If phase_of_stage is not NULL it receives, per stage,
+ * the phase that writes its output (for a stage streamed in K windows, the
+ * last window). */
+int32_t wgn_plan_phases(const wgn_stage *stages, int32_t n_stages, int32_t batch,
+                        const wgn_chain_opts *opts, int32_t *phase_of_stage);
+
+/* Plan a chain on the host only (no device needed) for opts->grid workgroups
+ * (0 or NULL opts: 256) on the path opts->path selects, and emulate every
+ * workgroup and wave of its work partition: each weight unit must be streamed
+ * exactly once with the right address, each partial-sum slot written once and
+ * read by the epilogue, each row owned by one workgroup, every LDS area inside
+ * the budget.  Returns the number of violations (0 = consistent) or a
+ * negative wgn_status if planning failed. */
+int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_t batch,
+                               const wgn_chain_opts *opts);
 
 #ifdef __cplusplus
 }

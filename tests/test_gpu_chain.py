@@ -109,14 +109,16 @@ def test_decoder_block_1536_batch1():
     check_decoder(inp, bufs, layers_full={0})
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 4])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 16])
 def test_small_decode_step_all_batches(B):
-    """Two full-width blocks + an LM head of 20000 rows, both launch modes."""
+    """Two full-width blocks + an LM head of 20000 rows, both launch modes;
+    batch > 4 runs on the matrix cores, batch 16 streams the down projection
+    in K windows."""
     say("chain decode_step 2 layers V=20000 B=%d" % B)
     inp = gen.make_stage_tensors("decode_step_1536x28", device=DEV, batch=B, n_layers=2, vocab=20000)
     stages, bufs = steps.decoder_stages(inp, DEV)
     ch = W.Chain(stages, B, mode=0)
-    assert ch.num_phases == 7
+    assert ch.num_phases == (9 if B > 8 else 7)
     ch.run()
     ch.check()
     check_decoder(inp, bufs, layers_full={0, 1})
@@ -130,7 +132,7 @@ def test_small_decode_step_all_batches(B):
     assert same_bits(first, snapshot(bufs)), "per-phase launches differ from the persistent kernel"
 
 
-@pytest.mark.parametrize("B", [4])
+@pytest.mark.parametrize("B", [4, 16])
 def test_ln_gelu_chain_768x72(B):
     """72 x [LayerNorm(768) -> Linear -> GELU-tanh], seeded LN params, per stage."""
     say("chain ln_gelu_chain_768x72 B=%d" % B)
@@ -165,19 +167,20 @@ def test_ln_gelu_chain_default_params():
         assert_close_bf16(bits(xs[i + 1]), ref, "ln-gelu layer %d" % i)
 
 
-def test_full_decode_step_batch1():
-    """The 28-layer, 151936-vocab decode step at batch 1 in the benchmark's launch
-    configuration: layers 0, 13, 27 and the LM head checked in full, every other
-    stage on sampled rows."""
-    say("chain decode_step_1536x28 full B=1")
-    inp = gen.make_stage_tensors("decode_step_1536x28", device=DEV, batch=1)
+@pytest.mark.parametrize("B", [1, 4, 8, 16])
+def test_full_decode_step(B):
+    """The 28-layer, 151936-vocab decode step in the benchmark's launch
+    configuration at batch 1, 4, 8, 16: layers 0, 13, 27 and the LM head
+    checked in full, every other stage on sampled rows."""
+    say("chain decode_step_1536x28 full B=%d" % B)
+    inp = gen.make_stage_tensors("decode_step_1536x28", device=DEV, batch=B)
     stages, bufs = steps.decoder_stages(inp, DEV)
-    ch = W.Chain(stages, 1)
-    assert ch.num_phases == 28 * 3 + 1
+    ch = W.Chain(stages, B)
+    assert ch.num_phases == 28 * (4 if B > 8 else 3) + 1
     ch.run()
     ch.check()
     first = snapshot(bufs)
-    check_decoder(inp, bufs, layers_full={0, 13, 27})
+    check_decoder(inp, bufs, layers_full={0, 13, 27} if B <= 4 else {0, 27})
     for _ in range(2):
         ch.run()
     ch.check()

@@ -71,6 +71,15 @@ CASES = [
     (1536, 8960, 1, O.NORM_NONE, O.EPI_NONE, False, True),
     (513, 1024, 4, O.NORM_LAYER, O.EPI_NONE, True, True),
     (8960, 1536, 1, O.NORM_RMS, O.EPI_SWIGLU, False, False),
+    # matrix-core path (batch > 4): ragged tiles (N % 16), K tails, every epilogue
+    (1, 8, 5, O.NORM_RMS, O.EPI_NONE, False, False),
+    (37, 264, 8, O.NORM_LAYER, O.EPI_GELU_TANH, True, False),
+    (1000, 520, 16, O.NORM_NONE, O.EPI_NONE, False, True),
+    (300, 1536, 7, O.NORM_RMS, O.EPI_SWIGLU, False, True),
+    (1536, 8960, 8, O.NORM_NONE, O.EPI_NONE, False, True),
+    (513, 1024, 16, O.NORM_LAYER, O.EPI_NONE, True, True),
+    (8960, 1536, 16, O.NORM_RMS, O.EPI_SWIGLU, False, False),
+    (17, 4096, 12, O.NORM_RMS, O.EPI_NONE, True, True),
 ]
 
 
@@ -100,6 +109,52 @@ def test_gemv_norm_shapes(case):
     assert_close_bf16(g, r, "gemv_norm %r" % (case,))
 
 
+def test_gemv_norm_too_large_for_lds_needs_a_chain():
+    """Batch 16 x K 8960 inputs do not fit in LDS: one launch refuses, a
+    one-stage chain streams the stage in K windows."""
+    say("gemv_norm 1536x8960 B=16 via K windows")
+    N, K, B = 1536, 8960, 16
+    Wt = rnd((N, K), 0.02, 901)
+    x = rnd((B, K), 1.0, 902)
+    res = rnd((B, N), 1.0, 903)
+    y = torch.empty((B, N), dtype=torch.bfloat16, device=DEV)
+    st = W.make_stage(Wt, x, y, residual=res)
+    with pytest.raises(W.WgnError):
+        W.gemv_norm(st, B)
+    ch = W.Chain([st], B)
+    assert ch.num_phases >= 2
+    ch.run()
+    ch.check()
+    g, r = oracle_stage_from_gpu(None, Wt, x, y, norm=O.NORM_NONE, residual=res)
+    assert_close_bf16(g, r, "down 1536x8960 B=16 K windows")
+
+
+@pytest.mark.parametrize("B", [1, 3, 4])
+def test_matrix_core_path_at_small_batch(B):
+    """The matrix-core path is selectable at any batch; same tolerance."""
+    say("chain path=matrix B=%d" % B)
+    cases = [(300, 1536, O.NORM_RMS, O.EPI_SWIGLU), (37, 264, O.NORM_LAYER, O.EPI_GELU_TANH),
+             (1536, 8960, O.NORM_NONE, O.EPI_NONE)]
+    for N, K, norm, epi in cases:
+        seed = N + K + B
+        Wt = rnd((N, K), 0.05, seed + 1)
+        Wu = rnd((N, K), 0.05, seed + 2) if epi == O.EPI_SWIGLU else None
+        x = rnd((B, K), 1.0, seed + 3, mean=0.3 if norm == O.NORM_LAYER else 0.0)
+        gamma = rnd((K,), 0.1, seed + 4, mean=1.0) if norm != O.NORM_NONE else None
+        beta = rnd((K,), 0.02, seed + 5) if norm == O.NORM_LAYER else None
+        bias = rnd((N,), 0.02, seed + 6) if epi == O.EPI_GELU_TANH else None
+        res = rnd((B, N), 1.0, seed + 7) if epi == O.EPI_NONE else None
+        y = torch.empty((B, N), dtype=torch.bfloat16, device=DEV)
+        eps = 1e-5 if norm == O.NORM_LAYER else 1e-6
+        st = W.make_stage(Wt, x, y, norm=norm, eps=eps, gamma=gamma, beta=beta, bias=bias, epi=epi, W_up=Wu,
+                          residual=res)
+        W.layer_chain([st], B, path=W.api.PATH_MATRIX)
+        torch.cuda.synchronize()
+        g, r = oracle_stage_from_gpu(None, Wt, x, y, norm=norm, eps=eps, gamma=gamma, beta=beta, bias=bias,
+                                     epi=epi, W_up=Wu, residual=res)
+        assert_close_bf16(g, r, "matrix path N=%d K=%d B=%d" % (N, K, B))
+
+
 def test_gemv_norm_identity_and_zero_weights():
     """Identity weights return x-hat; zero weights return the residual bit for bit."""
     say("gemv_norm identity / zero weights")
@@ -119,8 +174,9 @@ def test_gemv_norm_identity_and_zero_weights():
 
 # --------------------------------------------------------------------- LM head
 def test_lmhead_argmax_full_vocab():
-    """Final RMSNorm + LM head 151936 x 1536 + argmax at batch 1..2, plus logits."""
-    for B in (1, 2):
+    """Final RMSNorm + LM head 151936 x 1536 + argmax at batch 1, 2 (vector
+    path) and 8, 16 (matrix-core path), plus logits."""
+    for B in (1, 2, 8, 16):
         say("lmhead_argmax V=151936 B=%d" % B)
         h = rnd((B, gen.H), 1.0, 100 + B)
         g = rnd((gen.H,), 0.1, 200, mean=1.0)

@@ -7,7 +7,7 @@ import re
 import pytest
 
 from weight_gemv_norm_amd import _lib as L
-from weight_gemv_norm_amd.api import partition_selftest, first_wave_of_unit
+from weight_gemv_norm_amd.api import partition_selftest, first_wave_of_unit, plan_phases
 from synth import gen
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -107,30 +107,71 @@ def fake_decoder(ar, B, n_layers, H=1536, I=8960, V=None):
     return stages
 
 
-@pytest.mark.parametrize("B", [1, 4])
+@pytest.mark.parametrize("B,path", [(1, 0), (4, 0), (1, 2), (4, 2), (5, 0), (8, 0), (16, 0)])
 @pytest.mark.parametrize("grid", [256, 61, 32])
-def test_partition_decoder_block(B, grid):
+def test_partition_decoder_block(B, path, grid):
     ar = Arena()
     stages = fake_decoder(ar, B, 1)
-    assert partition_selftest(stages, B, grid) == 0
+    assert partition_selftest(stages, B, grid, path) == 0
 
 
-def test_partition_full_decode_step_shapes():
+@pytest.mark.parametrize("B", [1, 8, 16])
+def test_partition_full_decode_step_shapes(B):
     ar = Arena()
-    stages = fake_decoder(ar, 1, 2, V=151936)
-    assert partition_selftest(stages, 1, 256) == 0
+    stages = fake_decoder(ar, B, 2, V=151936)
+    assert partition_selftest(stages, B, 256) == 0
 
 
+@pytest.mark.parametrize("path", [0, 2])
 @pytest.mark.parametrize("K", [8, 24, 256, 520, 1536, 8960])
-@pytest.mark.parametrize("N", [1, 5, 97, 1000])
-def test_partition_ragged_shapes(N, K):
+@pytest.mark.parametrize("N", [1, 5, 17, 97, 1000])
+def test_partition_ragged_shapes(N, K, path):
     ar = Arena()
     st = [fake_stage(ar, N, K, 2, L.NORM_RMS),
           fake_stage(ar, max(1, N // 3), K, 2, L.NORM_NONE, L.EPI_SWIGLU)]
     for grid in (1, 3, 64, 256):
-        r = partition_selftest(st, 2, grid)
+        r = partition_selftest(st, 2, grid, path)
         # a grid too small for the per-workgroup partial sums is refused, never mis-planned
         assert r == 0 or (r == L.E_UNSUPPORTED and grid <= 3), (grid, r)
+
+
+def test_vector_path_refuses_large_batch():
+    ar = Arena()
+    st = [fake_stage(ar, 64, 64, 8, L.NORM_RMS)]
+    assert partition_selftest(st, 8, 16, 1) == L.E_UNSUPPORTED
+    assert partition_selftest(st, 8, 16, 0) == 0
+
+
+@pytest.mark.parametrize("B", [9, 12, 16])
+@pytest.mark.parametrize("grid", [256, 40])
+def test_partition_k_windows(B, grid):
+    """The 8960-long down-projection input does not fit in LDS at batch > 8:
+    that phase is streamed in K windows with the row sums carried between
+    them; the residual enters in the last window only."""
+    ar = Arena()
+    h = ar.take(B * 1536 * 2)
+    s = ar.take(B * 8960 * 2)
+    d = fake_stage(ar, 1536, 8960, B, L.NORM_NONE, x=s, residual=h)
+    assert partition_selftest([d], B, grid) == 0
+    n, where = plan_phases([d], B, grid)
+    assert n >= 2 and where == [n - 1]
+    if grid == 256:
+        assert n == 2
+    gu = fake_stage(ar, 8960, 1536, B, L.NORM_RMS, L.EPI_SWIGLU, x=h)
+    gu.y = s
+    assert partition_selftest([gu, d], B, grid) == 0
+    assert plan_phases([gu, d], B, grid) == (n + 1, [0, n])
+    # at batch 8 the whole input fits: no windows
+    d8 = fake_stage(ar, 1536, 8960, 8, L.NORM_NONE, x=s, residual=h)
+    assert plan_phases([d8], 8, grid) == (1, [0])
+
+
+def test_normalised_input_too_large_is_refused():
+    """A norm needs the whole input in LDS for its statistics, so a normalised
+    input that does not fit cannot be windowed."""
+    ar = Arena()
+    st = fake_stage(ar, 64, 8960, 16, L.NORM_RMS)
+    assert partition_selftest([st], 16, 64) == L.E_UNSUPPORTED
 
 
 def test_partition_ln_chain():

@@ -38,7 +38,7 @@ class Stage(ctypes.Structure):
 
 class ChainOpts(ctypes.Structure):
     """Mirror of wgn_chain_opts."""
-    _fields_ = [("mode", I32), ("grid", I32), ("trace", I32), ("reserved", I32 * 5)]
+    _fields_ = [("mode", I32), ("grid", I32), ("trace", I32), ("path", I32), ("reserved", I32 * 4)]
 
 
 class WgnError(RuntimeError):
@@ -85,7 +85,8 @@ def lib() -> ctypes.CDLL:
         "wgn_chain_destroy": ([P], None),
         "wgn_layer_chain": ([SP, I32, I32, OP, P, SZ, P], I32),
         "wgn_first_wave_of_unit": ([I32, I32, I32], I32),
-        "wgn_partition_selftest": ([SP, I32, I32, I32], I32),
+        "wgn_partition_selftest": ([SP, I32, I32, OP], I32),
+        "wgn_plan_phases": ([SP, I32, I32, OP, ctypes.POINTER(I32)], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)

@@ -115,17 +115,22 @@ def rmsnorm_rows(x: torch.Tensor, gamma: torch.Tensor, eps: float, y: torch.Tens
     L.check(st, "wgn_rmsnorm_rows")
 
 
-def _opts(mode: int, grid: int, trace: bool = False) -> ChainOpts:
+PATH_AUTO, PATH_VECTOR, PATH_MATRIX = 0, 1, 2
+
+
+def _opts(mode: int, grid: int, trace: bool = False, path: int = PATH_AUTO) -> ChainOpts:
     o = ChainOpts()
     o.mode = mode
     o.grid = grid
     o.trace = 1 if trace else 0
+    o.path = path
     return o
 
 
-def chain_workspace_bytes(stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 0) -> int:
+def chain_workspace_bytes(stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 0,
+                          path: int = PATH_AUTO) -> int:
     arr = L.stage_array(stages)
-    o = _opts(mode, grid)
+    o = _opts(mode, grid, path=path)
     return int(L.lib().wgn_chain_workspace_bytes(arr, len(stages), batch, ctypes.byref(o)))
 
 
@@ -133,11 +138,12 @@ class Chain:
     """A planned chain (wgn_chain_create); run() enqueues one pass."""
 
     def __init__(self, stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 0,
-                 ws: Optional[torch.Tensor] = None, stream=None, device="cuda", trace: bool = False):
+                 ws: Optional[torch.Tensor] = None, stream=None, device="cuda", trace: bool = False,
+                 path: int = PATH_AUTO):
         self._arr = L.stage_array(stages)
         self.n_stages = len(stages)
         self.batch = batch
-        o = _opts(mode, grid, trace)
+        o = _opts(mode, grid, trace, path)
         need = L.lib().wgn_chain_workspace_bytes(self._arr, len(stages), batch, ctypes.byref(o))
         if need == 0:
             # planning failed: let create report the precise status
@@ -191,9 +197,9 @@ class Chain:
 
 
 def layer_chain(stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 0,
-                ws: Optional[torch.Tensor] = None, stream=None, device="cuda") -> None:
+                ws: Optional[torch.Tensor] = None, stream=None, device="cuda", path: int = PATH_AUTO) -> None:
     arr = L.stage_array(stages)
-    o = _opts(mode, grid)
+    o = _opts(mode, grid, path=path)
     if ws is None:
         ws = workspace(L.lib().wgn_chain_workspace_bytes(arr, len(stages), batch, ctypes.byref(o)), device)
     st = L.lib().wgn_layer_chain(arr, len(stages), batch, ctypes.byref(o), _ptr(ws), ws.numel(),
@@ -201,9 +207,21 @@ def layer_chain(stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 
     L.check(st, "wgn_layer_chain")
 
 
-def partition_selftest(stages: Sequence[Stage], batch: int, grid: int) -> int:
+def partition_selftest(stages: Sequence[Stage], batch: int, grid: int, path: int = PATH_AUTO) -> int:
     arr = L.stage_array(stages)
-    return int(L.lib().wgn_partition_selftest(arr, len(stages), batch, grid))
+    o = _opts(0, grid, path=path)
+    return int(L.lib().wgn_partition_selftest(arr, len(stages), batch, ctypes.byref(o)))
+
+
+def plan_phases(stages: Sequence[Stage], batch: int, grid: int = 0, path: int = PATH_AUTO):
+    """Host-only planning: (number of phases, phase of each stage's output)."""
+    arr = L.stage_array(stages)
+    o = _opts(0, grid, path=path)
+    out = (ctypes.c_int32 * len(stages))()
+    n = int(L.lib().wgn_plan_phases(arr, len(stages), batch, ctypes.byref(o), out))
+    if n < 0:
+        raise WgnError(n, "wgn_plan_phases")
+    return n, list(out)
 
 
 def first_wave_of_unit(u: int, units: int, waves: int) -> int:

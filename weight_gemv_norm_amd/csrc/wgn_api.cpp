@@ -17,7 +17,7 @@
 #include "wgn_loader.h"
 
 namespace wgn {
-hipError_t launch_chain(int32_t batch, const KArgs &a, int32_t grid, size_t lds, hipStream_t s);
+hipError_t launch_chain(int32_t batch, bool tile, const KArgs &a, int32_t grid, size_t lds, hipStream_t s);
 hipError_t launch_rmsnorm_rows(const uint16_t *x, int64_t xs, const uint16_t *g, float eps, uint16_t *y, int64_t ys,
                                int32_t rows, int32_t K, bool f16, hipStream_t s);
 }  // namespace wgn
@@ -71,6 +71,7 @@ inline size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 wgn_status check_stage(const wgn_stage &s, int32_t batch) {
     if (batch < 1 || batch > MAX_BATCH) return WGN_E_ARG;
     if (s.N < 1 || s.K < 8 || (s.K & 7)) return WGN_E_ARG;
+    if (s.K > (1 << 24)) return WGN_E_UNSUPPORTED;  // 16 rows x K x 2 bytes must fit 32-bit buffer offsets
     if (!s.W || !s.x || !s.y) return WGN_E_ARG;
     if (s.norm < NORM_NONE || s.norm > NORM_LAYER) return WGN_E_ARG;
     if (s.epi < EPI_NONE || s.epi > EPI_ARGMAX) return WGN_E_ARG;
@@ -144,19 +145,17 @@ bool same_source(const DevSource &s, const wgn_stage &st) {
 // Host image of a device program.
 struct Program {
     int32_t B = 1, G = 1;
+    bool tile = false;                   // matrix-core streaming path
     std::vector<DevPhase> phases;
     std::vector<DevStage> stages;
     std::vector<DevSource> sources;
     std::vector<int32_t> rowb;
     std::vector<int32_t> phase_of_stage;
+    std::vector<int32_t> group_end;      // per phase: one past the last phase of its launch group
+    std::vector<int32_t> part_bytes;     // per phase: bytes of its partial-slot area
     int32_t n_argmax = 0;
-    size_t lds_x_bytes = 0, lds_part_bytes = 0, lds_prm_bytes = 0, lds_epi_bytes = 0;
-    // dynamic LDS layout: [x-hat][partials][gains/shifts][epilogue inputs]
-    size_t prm_off() const { return lds_x_bytes + al16(lds_part_bytes); }
-    size_t epi_off() const { return prm_off() + al16(lds_prm_bytes); }
-    size_t desc_off() const { return epi_off() + al16(lds_epi_bytes); }
-    // + 6 streaming-wave trace timestamps
-    size_t lds_total() const { return desc_off() + (size_t)DESC_BUFS * RUN_BUF_BYTES + 6 * 8; }
+    size_t lds_end = LDS_DYN_OFF;        // dynamic LDS bytes of the largest phase
+    size_t lds_total() const { return lds_end; }
     static size_t al16(size_t v) { return (v + 15) & ~size_t(15); }
 };
 
@@ -220,13 +219,101 @@ void balance_rows(const std::vector<DevStage> &st, int32_t s0, int32_t ns, int32
     out[base + G] = nrows;
 }
 
-wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, Program &P) {
+// Exact partial-slot demand of a phase under its workgroup partition: the
+// largest number of waves any row-part segment spans (slots per row-part) and
+// the largest number of row-parts any workgroup owns.
+struct PhaseStats {
+    int32_t jmax = 1, max_rp = 0;
+};
+
+PhaseStats phase_stats(const std::vector<DevStage> &st, const std::vector<int32_t> &rowb, const DevPhase &ph,
+                       int32_t G, bool tile) {
+    PhaseStats S;
+    for (int32_t g = 0; g < G; ++g) {
+        const int32_t r0 = ph.rb_off >= 0 ? rowb[ph.rb_off + g] : even_row_begin(g, ph.nrows, G);
+        const int32_t r1 = ph.rb_off >= 0 ? rowb[ph.rb_off + g + 1] : even_row_begin(g + 1, ph.nrows, G);
+        int32_t U = 0, rp = 0;
+        for (int32_t i = 0; i < ph.nstages; ++i) {
+            const DevStage &d = st[ph.stage0 + i];
+            const StageSpan sp = stage_span(d, r0, r1, 0, 0);
+            U += units_of(sp.nrows, d.parts, d.nchunks, tile);
+            rp += sp.nrows * d.parts;
+        }
+        S.max_rp = std::max(S.max_rp, rp);
+        int32_t u_base = 0;
+        for (int32_t i = 0; i < ph.nstages; ++i) {
+            const DevStage &d = st[ph.stage0 + i];
+            const StageSpan sp = stage_span(d, r0, r1, 0, 0);
+            const int32_t nseg = (tile ? (sp.nrows + TILE_ROWS - 1) / TILE_ROWS : sp.nrows) * d.parts;
+            for (int32_t sg = 0; sg < nseg; ++sg) {
+                const int32_t a0 = u_base + sg * d.nchunks;
+                const int32_t span =
+                    first_wave(a0 + d.nchunks - 1, U, STREAM_WAVES) - first_wave(a0, U, STREAM_WAVES) + 1;
+                S.jmax = std::max(S.jmax, span);
+            }
+            u_base += nseg * d.nchunks;
+        }
+    }
+    return S;
+}
+
+// Place a phase's LDS areas after the fixed ones; false if they do not fit.
+bool layout_phase(const Program &P, DevPhase &ph, const PhaseStats &S, bool carry, size_t &end_out,
+                  int32_t &part_bytes) {
+    const size_t nb = (size_t)P.B;
+    size_t prm = 0;
+    bool epi_in = false;
+    for (int32_t i = 0; i < ph.nsrc; ++i)
+        if (P.sources[ph.src0 + i].norm != NORM_NONE) prm += prm_bytes_of(P.sources[ph.src0 + i].K);
+    for (int32_t i = 0; i < ph.nstages; ++i) {
+        const DevStage &d = P.stages[ph.stage0 + i];
+        if ((d.bias || d.residual) && !(d.carry & CARRY_OUT)) epi_in = true;
+    }
+    const size_t x = al256(nb * (size_t)ph.xb * 2);
+    const size_t part = Program::al16((size_t)S.max_rp * S.jmax * nb * 4);
+    const size_t epi = epi_in ? Program::al16((size_t)S.max_rp * (1 + nb) * 4) : 0;
+    const size_t cy = carry ? Program::al16((size_t)S.max_rp * nb * 4) : 0;
+    size_t o = LDS_DYN_OFF;
+    ph.x_off = (int32_t)o;
+    o += x;
+    ph.part_off = (int32_t)o;
+    o += part;
+    ph.prm_off = (int32_t)o;
+    o += Program::al16(prm);
+    ph.epi_off = (int32_t)o;
+    o += epi;
+    ph.carry_off = (int32_t)o;
+    o += cy;
+    ph.jmax = S.jmax;
+    end_out = o;
+    part_bytes = (int32_t)part;
+    return o <= LDS_BUDGET && o < (1u << 18);
+}
+
+// x-hat row stride (elements) of a phase: its sources back to back, each
+// padded to whole units; on the matrix-core path one extra 16-byte step keeps
+// the 16 batch rows read by one instruction in distinct LDS banks.
+int32_t xb_of(Program &P, DevPhase &ph) {
+    int32_t xb = 0;
+    for (int32_t i = 0; i < ph.nsrc; ++i) {
+        P.sources[ph.src0 + i].lds_off = xb;
+        xb += nchunks_of(P.sources[ph.src0 + i].K) * UNIT;
+    }
+    return P.tile ? xb + 8 : xb;
+}
+
+// Phase selection of the matrix-core path.
+bool use_tile(int32_t B, int32_t path) { return path == 2 || (path == 0 && B > MAX_BATCH_VALU); }
+
+wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_t path, Program &P) {
     if (!stages || n < 1 || G < 1) return WGN_E_ARG;
     for (int32_t i = 0; i < n; ++i) {
         wgn_status st = check_stage(stages[i], B);
         if (st != WGN_OK) return st;
     }
-    if (B > MAX_BATCH_VALU) return WGN_E_UNSUPPORTED;
+    if (path < 0 || path > 2) return WGN_E_ARG;
+    const bool tile = use_tile(B, path);
+    if (!tile && B > MAX_BATCH_VALU) return WGN_E_UNSUPPORTED;
     // weights and norm parameters must not be written by any stage
     std::vector<Range> r, w, c, allw;
     for (int32_t i = 0; i < n; ++i) {
@@ -240,51 +327,119 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, Progra
     P = Program();
     P.B = B;
     P.G = G;
+    P.tile = tile;
     P.phase_of_stage.assign(n, -1);
     std::vector<Range> ph_reads, ph_writes;
+    std::vector<int32_t> users;  // caller stage indices of the open phase
     DevPhase cur;
     std::memset(&cur, 0, sizeof cur);
     bool open = false;
+    wgn_status fail = WGN_OK;
+    auto push_phase = [&](DevPhase &ph, const PhaseStats &S, bool carry) -> bool {
+        size_t end = 0;
+        int32_t pb = 0;
+        if (!layout_phase(P, ph, S, carry, end, pb)) return false;
+        P.lds_end = std::max(P.lds_end, end);
+        P.phases.push_back(ph);
+        P.part_bytes.push_back(pb);
+        return true;
+    };
     auto close_phase = [&]() {
-        if (!open) return;
+        if (!open || fail != WGN_OK) return;
+        open = false;
         cur.nstages = (int32_t)P.stages.size() - cur.stage0;
         cur.nsrc = (int32_t)P.sources.size() - cur.src0;
-        int32_t xb = 0, maxch = 1, nrows = 0;
-        for (int32_t i = 0; i < cur.nsrc; ++i) {
-            P.sources[cur.src0 + i].lds_off = xb;
-            xb += nchunks_of(P.sources[cur.src0 + i].K) * UNIT;
-        }
+        int32_t nrows = 0, maxch = 1;
         for (int32_t i = 0; i < cur.nstages; ++i) {
             DevStage &d = P.stages[cur.stage0 + i];
             d.row_off = nrows;
             nrows += d.N;
             maxch = std::max(maxch, d.nchunks);
         }
-        cur.xb = xb;
         cur.nrows = nrows;
-        cur.jmax = std::min(STREAM_WAVES, maxch);
+        cur.xb = xb_of(P, cur);
         cur.rb_off = (int32_t)P.rowb.size();
         balance_rows(P.stages, cur.stage0, cur.nstages, G, P.rowb);
-        int32_t max_rp = 0;
-        for (int32_t g = 0; g < G; ++g) {
-            int32_t r0 = P.rowb[cur.rb_off + g], r1 = P.rowb[cur.rb_off + g + 1], rp = 0;
-            for (int32_t i = 0; i < cur.nstages; ++i) {
-                StageSpan sp = stage_span(P.stages[cur.stage0 + i], r0, r1, 0, 0);
-                rp += sp.nrows * P.stages[cur.stage0 + i].parts;
-            }
-            max_rp = std::max(max_rp, rp);
-        }
-        size_t prm = 0;
-        for (int32_t i = 0; i < cur.nsrc; ++i) prm += prm_bytes_of(P.sources[cur.src0 + i].K);
-        P.lds_x_bytes = std::max(P.lds_x_bytes, al256((size_t)B * xb * 2));
-        P.lds_part_bytes = std::max(P.lds_part_bytes, (size_t)max_rp * cur.jmax * B * 4);
-        P.lds_prm_bytes = std::max(P.lds_prm_bytes, prm);
-        P.lds_epi_bytes = std::max(P.lds_epi_bytes, (size_t)max_rp * (1 + B) * 4);
         cur.wait = P.phases.empty() ? 0 : 1;
-        P.phases.push_back(cur);
-        open = false;
+        const int32_t first = (int32_t)P.phases.size();
+        DevPhase whole = cur;
+        if (push_phase(whole, phase_stats(P.stages, P.rowb, whole, G, tile), false)) {
+            P.group_end.push_back(first + 1);
+            for (int32_t u : users) P.phase_of_stage[u] = first;
+            return;
+        }
+        // The inputs do not fit in LDS: stream the phase in K windows.  Only a
+        // phase with one un-normalised input can be windowed (a norm needs the
+        // whole vector for its statistics).
+        const DevSource src0 = P.sources[cur.src0];
+        if (cur.nsrc != 1 || src0.norm != NORM_NONE) {
+            fail = WGN_E_UNSUPPORTED;
+            return;
+        }
+        const std::vector<DevStage> orig(P.stages.begin() + cur.stage0, P.stages.end());
+        const int32_t nch = nchunks_of(src0.K);
+        for (int32_t nw = nch - 1; nw >= 1; --nw) {
+            const int32_t S = (nch + nw - 1) / nw;
+            P.stages.resize(cur.stage0);
+            P.sources.resize(cur.src0);
+            std::vector<DevPhase> win;
+            PhaseStats worst;
+            for (int32_t s = 0; s < S; ++s) {
+                const int32_t c0 = s * nw, cn = std::min(nw, nch - c0);
+                DevPhase ph = cur;
+                ph.stage0 = (int32_t)P.stages.size();
+                ph.src0 = (int32_t)P.sources.size();
+                ph.nsrc = 1;
+                ph.wait = s == 0 ? cur.wait : 0;
+                DevSource sw = src0;
+                sw.x = src0.x + (size_t)c0 * UNIT;
+                sw.K = std::min(nw * UNIT, src0.K - c0 * UNIT);
+                P.sources.push_back(sw);
+                for (const DevStage &o : orig) {
+                    DevStage d = o;
+                    d.c0 = c0;
+                    d.nchunks = cn;
+                    d.carry = (s > 0 ? CARRY_IN : 0) | (s < S - 1 ? CARRY_OUT : 0);
+                    if (s < S - 1) {
+                        d.bias = nullptr;    // bias and residual enter in the last window only
+                        d.residual = nullptr;
+                        d.am_slot = -1;
+                    }
+                    P.stages.push_back(d);
+                }
+                ph.xb = xb_of(P, ph);
+                const PhaseStats st = phase_stats(P.stages, P.rowb, ph, G, tile);
+                worst.jmax = std::max(worst.jmax, st.jmax);
+                worst.max_rp = std::max(worst.max_rp, st.max_rp);
+                win.push_back(ph);
+            }
+            // every window uses one layout: x-hat sized by the first (widest)
+            // window, epilogue inputs by the last
+            DevPhase probe = win[S - 1];
+            probe.xb = win[0].xb;
+            size_t end = 0;
+            int32_t pb = 0;
+            if (!layout_phase(P, probe, worst, true, end, pb)) continue;
+            for (DevPhase &ph : win) {
+                ph.xb = probe.xb;
+                ph.x_off = probe.x_off;
+                ph.part_off = probe.part_off;
+                ph.prm_off = probe.prm_off;
+                ph.epi_off = probe.epi_off;
+                ph.carry_off = probe.carry_off;
+                ph.jmax = probe.jmax;
+                P.phases.push_back(ph);
+                P.part_bytes.push_back(pb);
+            }
+            P.lds_end = std::max(P.lds_end, end);
+            const int32_t last = first + S - 1;
+            for (int32_t s = 0; s < S; ++s) P.group_end.push_back(last + 1);
+            for (int32_t u : users) P.phase_of_stage[u] = last;
+            return;
+        }
+        fail = WGN_E_UNSUPPORTED;
     };
-    for (int32_t i = 0; i < n; ++i) {
+    for (int32_t i = 0; i < n && fail == WGN_OK; ++i) {
         const wgn_stage &s = stages[i];
         stage_ranges(s, B, r, w, c);
         bool conflict = open && (any_overlap(r, ph_writes) || any_overlap(w, ph_reads) || any_overlap(w, ph_writes));
@@ -297,12 +452,14 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, Progra
             if ((int32_t)P.stages.size() - cur.stage0 >= MAX_RUNS) conflict = true;
         }
         if (conflict) close_phase();
+        if (fail != WGN_OK) break;
         if (!open) {
             std::memset(&cur, 0, sizeof cur);
             cur.stage0 = (int32_t)P.stages.size();
             cur.src0 = (int32_t)P.sources.size();
             ph_reads.clear();
             ph_writes.clear();
+            users.clear();
             open = true;
             src_idx = -1;
         }
@@ -314,12 +471,12 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, Progra
         d.src = src_idx;
         if (s.epi == EPI_ARGMAX) d.am_slot = P.n_argmax++;
         P.stages.push_back(d);
-        P.phase_of_stage[i] = (int32_t)P.phases.size();
+        users.push_back(i);
         ph_reads.insert(ph_reads.end(), r.begin(), r.end());
         ph_writes.insert(ph_writes.end(), w.begin(), w.end());
     }
     close_phase();
-    if (P.lds_total() > LDS_BUDGET) return WGN_E_UNSUPPORTED;
+    if (fail != WGN_OK) return fail;
     return WGN_OK;
 }
 
@@ -366,52 +523,59 @@ int32_t resolve_grid(const wgn_chain_opts *opts) {
 struct SingleLaunch {
     KArgs a;
     int32_t G;
+    bool tile;
     size_t lds;
     size_t ws;
 };
 
-void single_geometry(const wgn_stage &s, int32_t B, int32_t cus, SingleLaunch &L) {
+// Geometry of a one-stage, one-phase launch (rows split evenly); false if its
+// LDS areas do not fit (such a stage needs K windows, i.e. a chain).
+bool single_geometry(const wgn_stage &s, int32_t B, int32_t cus, SingleLaunch &L) {
     std::memset(&L.a, 0, sizeof L.a);
+    L.tile = use_tile(B, 0);
     const int32_t parts = s.epi == EPI_SWIGLU ? 2 : 1;
-    const int64_t units = (int64_t)s.N * parts * nchunks_of(s.K);
-    int64_t g = (units + 2 * STREAM_WAVES - 1) / (2 * STREAM_WAVES);
+    const int32_t nch = nchunks_of(s.K);
+    const int64_t units = (int64_t)units_of(s.N, parts, nch, L.tile);
+    // about two units per streaming wave
+    const int64_t per_wg = 2 * STREAM_WAVES;
+    int64_t g = (units + per_wg - 1) / per_wg;
     g = std::max<int64_t>(1, std::min<int64_t>(g, cus));
     g = std::min<int64_t>(g, s.N);
     L.G = (int32_t)g;
-    const int32_t nch = nchunks_of(s.K);
-    const int32_t jmax = std::min(STREAM_WAVES, nch);
-    const int32_t rows_max = (int32_t)((s.N + L.G - 1) / L.G);
-    const size_t xbytes = al256((size_t)B * nch * UNIT * 2);
-    const size_t part = Program::al16((size_t)rows_max * parts * jmax * B * 4);
-    const size_t prm = Program::al16(prm_bytes_of(s.K));
-    const size_t epi = Program::al16((size_t)rows_max * parts * (1 + B) * 4);
-    L.lds = xbytes + part + prm + epi + (size_t)DESC_BUFS * RUN_BUF_BYTES + 6 * 8;
-    L.a.lds_x_bytes = (int32_t)xbytes;
-    L.a.lds_prm_off = (int32_t)(xbytes + part);
-    L.a.lds_epi_off = (int32_t)(xbytes + part + prm);
-    L.a.lds_desc_off = (int32_t)(xbytes + part + prm + epi);
-    L.ws = s.epi == EPI_ARGMAX ? 256 + al256((size_t)L.G * B * sizeof(uint64_t)) : 0;
+    Program P;
+    P.B = B;
+    P.G = L.G;
+    P.tile = L.tile;
+    P.stages.push_back(make_dev_stage(s));
+    P.sources.push_back(make_dev_source(s));
     DevPhase &ph = L.a.iph;
+    std::memset(&ph, 0, sizeof ph);
     ph.stage0 = 0;
     ph.nstages = 1;
     ph.src0 = 0;
     ph.nsrc = 1;
     ph.nrows = s.N;
     ph.wait = 0;
-    ph.xb = nch * UNIT;
     ph.rb_off = -1;
-    ph.jmax = jmax;
-    L.a.ist = make_dev_stage(s);
+    ph.xb = xb_of(P, ph);
+    const PhaseStats S = phase_stats(P.stages, P.rowb, ph, L.G, L.tile);
+    size_t end = 0;
+    int32_t pb = 0;
+    const bool fits = layout_phase(P, ph, S, false, end, pb);
+    L.lds = end;
+    L.ws = s.epi == EPI_ARGMAX ? 256 + al256((size_t)L.G * B * sizeof(uint64_t)) : 0;
+    L.a.ist = P.stages[0];
     L.a.ist.src = 0;
     L.a.ist.row_off = 0;
     L.a.ist.am_slot = s.epi == EPI_ARGMAX ? 0 : -1;
-    L.a.isrc = make_dev_source(s);
-    L.a.isrc.lds_off = 0;
+    L.a.isrc = P.sources[0];
     L.a.p0 = 0;
     L.a.p1 = 1;
     L.a.persistent = 0;
     L.a.G = L.G;
+    L.a.nb = B;
     L.a.n_argmax = s.epi == EPI_ARGMAX ? 1 : 0;
+    return fits;
 }
 
 }  // namespace
@@ -426,6 +590,10 @@ struct wgn_chain {
     void *ws;
     WsLayout L;
 };
+
+namespace {
+int32_t opts_path(const wgn_chain_opts *opts) { return opts ? opts->path : 0; }
+}  // namespace
 
 extern "C" {
 
@@ -458,7 +626,7 @@ size_t wgn_gemv_norm_workspace_bytes(const wgn_stage *stage, int32_t batch) {
     if (!stage || check_stage(*stage, batch) != WGN_OK) return 0;
     SingleLaunch L;
     DevInfo d = device_info();
-    single_geometry(*stage, batch, d.cus > 0 ? d.cus : 256, L);
+    if (!single_geometry(*stage, batch, d.cus > 0 ? d.cus : 256, L)) return 0;
     return L.ws;
 }
 
@@ -467,19 +635,18 @@ wgn_status wgn_gemv_norm(const wgn_stage *stage, int32_t batch, void *workspace,
     if (!stage) return WGN_E_ARG;
     wgn_status st = check_stage(*stage, batch);
     if (st != WGN_OK) return st;
-    if (batch > MAX_BATCH_VALU) return WGN_E_UNSUPPORTED;
     DevInfo d = device_info();
     if (!d.ok) return WGN_E_DEVICE;
     SingleLaunch L;
-    single_geometry(*stage, batch, d.cus, L);
-    if (L.lds > LDS_BUDGET) return WGN_E_UNSUPPORTED;
+    if (!single_geometry(*stage, batch, d.cus, L)) return WGN_E_UNSUPPORTED;
     if (L.ws) {
         if (!workspace || ws_bytes < L.ws || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return WGN_E_WORKSPACE;
         L.a.tickets = (uint32_t *)workspace;
         L.a.err = (uint32_t *)((char *)workspace + 64);
         L.a.am_part = (uint64_t *)((char *)workspace + 256);
     }
-    hipError_t e = note(launch_chain(batch, L.a, L.G, L.lds, (hipStream_t)stream), "gemv_norm launch");
+    L.a.ist.W = (const uint16_t *)stage->W;
+    hipError_t e = note(launch_chain(batch, L.tile, L.a, L.G, L.lds, (hipStream_t)stream), "gemv_norm launch");
     return e == hipSuccess ? WGN_OK : WGN_E_HIP;
 }
 
@@ -534,7 +701,7 @@ wgn_status wgn_rmsnorm_rows(const void *x, int64_t x_stride, const void *gamma, 
 size_t wgn_chain_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch,
                                  const wgn_chain_opts *opts) {
     Program P;
-    if (plan(stages, n_stages, batch, resolve_grid(opts), P) != WGN_OK) return 0;
+    if (plan(stages, n_stages, batch, resolve_grid(opts), opts_path(opts), P) != WGN_OK) return 0;
     return ws_layout(P, opts && opts->trace).total;
 }
 
@@ -543,14 +710,15 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     if (!out) return WGN_E_ARG;
     *out = nullptr;
     if (opts) {
-        if (opts->mode < 0 || opts->mode > 1 || opts->grid < 0 || opts->trace < 0 || opts->trace > 1)
+        if (opts->mode < 0 || opts->mode > 1 || opts->grid < 0 || opts->trace < 0 || opts->trace > 1 ||
+            opts->path < 0 || opts->path > 2)
             return WGN_E_ARG;
-        for (int i = 0; i < 5; ++i)
+        for (int i = 0; i < 4; ++i)
             if (opts->reserved[i]) return WGN_E_ARG;
     }
     wgn_chain *c = new (std::nothrow) wgn_chain();
     if (!c) return WGN_E_ARG;
-    wgn_status st = plan(stages, n_stages, batch, resolve_grid(opts), c->P);
+    wgn_status st = plan(stages, n_stages, batch, resolve_grid(opts), opts_path(opts), c->P);
     if (st != WGN_OK) {
         delete c;
         return st;
@@ -600,10 +768,7 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     a.persistent = c->mode == 0 ? 1 : 0;
     a.G = c->P.G;
     a.n_argmax = c->P.n_argmax;
-    a.lds_x_bytes = (int32_t)c->P.lds_x_bytes;
-    a.lds_prm_off = (int32_t)c->P.prm_off();
-    a.lds_epi_off = (int32_t)c->P.epi_off();
-    a.lds_desc_off = (int32_t)c->P.desc_off();
+    a.nb = c->P.B;
     a.ist.W = (const uint16_t *)stages[0].W;  // address used by empty (zero-length) loads
     *out = c;
     return WGN_OK;
@@ -613,14 +778,16 @@ wgn_status wgn_chain_run(const wgn_chain *c, wgn_stream stream) {
     if (!c) return WGN_E_ARG;
     hipStream_t s = (hipStream_t)stream;
     if (c->mode == 0) {
-        hipError_t e = note(launch_chain(c->P.B, c->a, c->P.G, c->lds, s), "chain launch");
+        hipError_t e = note(launch_chain(c->P.B, c->P.tile, c->a, c->P.G, c->lds, s), "chain launch");
         return e == hipSuccess ? WGN_OK : WGN_E_HIP;
     }
+    // one launch per phase; the K windows of one phase share a launch (their
+    // running sums live in LDS)
     KArgs a = c->a;
-    for (int32_t p = 0; p < (int32_t)c->P.phases.size(); ++p) {
+    for (int32_t p = 0; p < (int32_t)c->P.phases.size(); p = c->P.group_end[p]) {
         a.p0 = p;
-        a.p1 = p + 1;
-        hipError_t e = note(launch_chain(c->P.B, a, c->P.G, c->lds, s), "chain phase launch");
+        a.p1 = c->P.group_end[p];
+        hipError_t e = note(launch_chain(c->P.B, c->P.tile, a, c->P.G, c->lds, s), "chain phase launch");
         if (e != hipSuccess) return WGN_E_HIP;
     }
     return WGN_OK;
@@ -677,15 +844,31 @@ wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t ba
     return st;
 }
 
-// Host emulation of the work partition of a planned chain: every unit of every
-// phase must be streamed by exactly one wave of exactly one workgroup, every
-// partial slot written once, and the epilogue must read exactly the slots the
-// waves write.  Returns the number of violations (0 = consistent), or a
-// negative status if planning failed.
-int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_t batch, int32_t grid) {
+int32_t wgn_plan_phases(const wgn_stage *stages, int32_t n_stages, int32_t batch, const wgn_chain_opts *opts,
+                        int32_t *phase_of_stage) {
     Program P;
-    wgn_status st = plan(stages, n_stages, batch, grid, P);
+    const int32_t grid = opts && opts->grid > 0 ? opts->grid : 256;
+    wgn_status st = plan(stages, n_stages, batch, grid, opts_path(opts), P);
     if (st != WGN_OK) return st;
+    if (phase_of_stage)
+        for (int32_t i = 0; i < n_stages; ++i) phase_of_stage[i] = P.phase_of_stage[i];
+    return (int32_t)P.phases.size();
+}
+
+// Host emulation of the work partition of a planned chain: every unit of every
+// phase must be streamed by exactly one wave of exactly one workgroup, with the
+// right address; every partial slot must be written once and lie inside its
+// phase's area; the epilogue must read exactly the slots the waves write; the
+// LDS areas must be ordered and inside the budget.  Returns the number of
+// violations (0 = consistent), or a negative status if planning failed.
+int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_t batch,
+                               const wgn_chain_opts *opts) {
+    Program P;
+    const int32_t grid = opts && opts->grid > 0 ? opts->grid : 256;
+    wgn_status st = plan(stages, n_stages, batch, grid, opts_path(opts), P);
+    if (st != WGN_OK) return st;
+    const bool tile = P.tile;
+    const int32_t nb = P.B;
     KArgs a;
     std::memset(&a, 0, sizeof a);
     a.phases = P.phases.data();
@@ -693,12 +876,18 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
     a.sources = P.sources.data();
     a.rowb = P.rowb.data();
     a.G = P.G;
+    a.nb = nb;
     int32_t bad = 0;
+    if (P.lds_total() > LDS_BUDGET) ++bad;
     for (int32_t p = 0; p < (int32_t)P.phases.size(); ++p) {
         const DevPhase &ph = P.phases[p];
+        if (!(ph.x_off >= LDS_DYN_OFF && ph.part_off >= ph.x_off + nb * ph.xb * 2 && ph.prm_off >= ph.part_off &&
+              ph.epi_off >= ph.prm_off && ph.carry_off >= ph.epi_off && (size_t)ph.carry_off <= P.lds_total()))
+            ++bad;
+        if (P.group_end[p] <= p || P.group_end[p] > (int32_t)P.phases.size()) ++bad;
         std::vector<int32_t> row_owner(ph.nrows, 0);
         for (int32_t g = 0; g < P.G; ++g) {
-            const PhaseGeo G = phase_geo<true>(a, p, g);
+            const PhaseGeo G = phase_geo<true>(a, p, g, tile);
             if (G.r0 > G.r1 || G.r0 < 0 || G.r1 > ph.nrows) {
                 ++bad;
                 continue;
@@ -706,7 +895,7 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
             for (int32_t r = G.r0; r < G.r1; ++r) row_owner[r]++;
             RunHdr h;
             Run runs[MAX_RUNS];
-            make_runs<true>(a, p, g, h, runs);
+            make_runs<true>(a, p, g, tile, h, runs);
             const int32_t U = h.U;
             if (U != G.U) ++bad;
             std::vector<uint32_t> slot_writes;
@@ -714,58 +903,95 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
                 const int32_t ub = U > 0 ? wave_begin(w, U, STREAM_WAVES) : 0;
                 const int32_t ue = U > 0 ? wave_begin(w + 1, U, STREAM_WAVES) : 0;
                 for (int32_t v = ub; v < ue; ++v) {
-                    const UnitDesc d = unit_desc_runs(h, runs, v, ub, ue, w, P.B);
-                    if ((d.meta & 0x8000u) == 0 || d.nbytes == 0 || (d.nbytes & 15u)) {
-                        ++bad;
-                        continue;
+                    if (tile) {
+                        const TileDesc d = unit_desc_tile(h, runs, v, ub, ue, w, nb);
+                        if (!d.valid || d.nrec == 0 || (d.nrec & 15u) || d.rows < 1 || d.rows > TILE_ROWS) {
+                            ++bad;
+                            continue;
+                        }
+                        if (d.seg_end)
+                            for (int32_t row = 0; row < d.rows; ++row)
+                                for (int32_t b = 0; b < nb; ++b)
+                                    slot_writes.push_back((uint32_t)(d.slot0 + row * d.slot_stride + b));
+                        if (d.xoff + UNIT * 2u > (uint32_t)ph.xb * 2u) ++bad;
+                    } else {
+                        const UnitDesc d = unit_desc_runs(h, runs, v, ub, ue, w, nb);
+                        if ((d.meta & 0x8000u) == 0 || d.nbytes == 0 || (d.nbytes & 15u)) {
+                            ++bad;
+                            continue;
+                        }
+                        if (d.meta & 0x4000u)
+                            for (int32_t b = 0; b < nb; ++b) slot_writes.push_back((d.meta >> 16) + (uint32_t)b);
+                        if (((d.meta & 0x3FFFu) << 4) + UNIT * 2u > (uint32_t)ph.xb * 2u) ++bad;
                     }
-                    if (d.meta & 0x4000u) slot_writes.push_back(d.meta >> 16);
-                    if (((d.meta & 0x3FFFu) << 4) + UNIT * 2u > (uint32_t)ph.xb * 2u) ++bad;
                 }
                 // units just outside the wave's share are invalid
-                if (unit_desc_runs(h, runs, ue, ub, ue, w, P.B).nbytes != 0) ++bad;
+                if (tile ? unit_desc_tile(h, runs, ue, ub, ue, w, nb).valid
+                         : unit_desc_runs(h, runs, ue, ub, ue, w, nb).nbytes != 0)
+                    ++bad;
             }
             // every unit of every owned row-part, once, with the right address
-            int32_t rp_base = 0, u_base = 0, nrun = 0;
+            int32_t rp_base = 0, u_base = 0;
             if (h.nruns != ph.nstages) ++bad;
             std::vector<uint32_t> slot_reads;
-            for (int32_t si = 0; si < ph.nstages; ++si) {
+            for (int32_t si = 0; si < ph.nstages && si < h.nruns; ++si) {
                 const DevStage &sg = P.stages[ph.stage0 + si];
-                StageSpan sp = stage_span(sg, G.r0, G.r1, 0, 0);
-                {
-                    const Run &r = runs[nrun++];
-                    if (r.stage != ph.stage0 + si || r.nrows != sp.nrows || (sp.nrows && r.row0 != sp.row0) ||
-                        r.u_base != u_base || r.rp_base != rp_base || r.epi != sg.epi || r.y != sg.y)
-                        ++bad;
+                const StageSpan sp = stage_span(sg, G.r0, G.r1, 0, 0);
+                const Run &rn = runs[si];
+                if (rn.stage != ph.stage0 + si || rn.nrows != sp.nrows || (sp.nrows && rn.row0 != sp.row0) ||
+                    rn.u_base != u_base || rn.rp_base != rp_base || rn.epi != sg.epi || rn.y != sg.y ||
+                    rn.c0 != sg.c0 || rn.carry != sg.carry)
+                    ++bad;
+                const int32_t ntiles = (sp.nrows + TILE_ROWS - 1) / TILE_ROWS;
+                const int32_t nseg = (tile ? ntiles : sp.nrows) * sg.parts;
+                for (int32_t sgi = 0; sgi < nseg; ++sgi) {
+                    const int32_t grp = sgi / sg.parts, pt = sgi % sg.parts;
+                    const uint16_t *Wp = pt == 0 ? sg.W : sg.W_up;
+                    for (int32_t c = 0; c < sg.nchunks; ++c) {
+                        const int32_t v = u_base + sgi * sg.nchunks + c;
+                        const int32_t w = first_wave(v, U, STREAM_WAVES);
+                        const int32_t ub = wave_begin(w, U, STREAM_WAVES), ue = wave_begin(w + 1, U, STREAM_WAVES);
+                        if (v < ub || v >= ue) ++bad;
+                        const uint32_t koff = (uint32_t)(sg.c0 + c) * UNIT * 2u;
+                        if (tile) {
+                            const TileDesc d = unit_desc_tile(h, runs, v, ub, ue, w, nb);
+                            const int32_t rows = std::min(TILE_ROWS, sp.nrows - grp * TILE_ROWS);
+                            const uint16_t *tp = Wp + (int64_t)(sp.row0 + grp * TILE_ROWS) * sg.K;
+                            if (d.ptr != (uint64_t)(uintptr_t)tp + koff) ++bad;
+                            if (d.rows != rows || d.nrec != (uint32_t)(rows * sg.K * 2) - koff) ++bad;
+                            if (d.kval != sg.K - (sg.c0 + c) * UNIT || d.rstride != sg.K * 2) ++bad;
+                        } else {
+                            const UnitDesc d = unit_desc_runs(h, runs, v, ub, ue, w, nb);
+                            const uint16_t *rowp = Wp + (int64_t)(sp.row0 + grp) * sg.K;
+                            if (d.ptr != (uint64_t)(uintptr_t)rowp + koff) ++bad;
+                            if (d.nbytes != (uint32_t)(sg.K * 2) - koff) ++bad;
+                        }
+                    }
                 }
+                // the epilogue walks rows; each row-part reads its slots
                 for (int32_t i = 0; i < sp.nrows; ++i)
                     for (int32_t pt = 0; pt < sg.parts; ++pt) {
                         const int32_t rp = rp_base + i * sg.parts + pt;
-                        const int32_t a0 = u_base + (i * sg.parts + pt) * sg.nchunks;
-                        for (int32_t c = 0; c < sg.nchunks; ++c) {
-                            const int32_t v = a0 + c;
-                            const int32_t w = first_wave(v, U, STREAM_WAVES);
-                            const int32_t ub = wave_begin(w, U, STREAM_WAVES), ue = wave_begin(w + 1, U, STREAM_WAVES);
-                            if (v < ub || v >= ue) ++bad;
-                            const UnitDesc d = unit_desc_runs(h, runs, v, ub, ue, w, P.B);
-                            const uint16_t *rowp = (pt == 0 ? sg.W : sg.W_up) + (int64_t)(sp.row0 + i) * sg.K;
-                            if (d.ptr != (uint64_t)(uintptr_t)rowp + (uint64_t)c * UNIT * 2u) ++bad;
-                            if (d.nbytes != (uint32_t)(sg.K * 2 - c * UNIT * 2)) ++bad;
-                        }
+                        const int32_t a0 = first_unit_of_rowpart(rn, i, pt, tile);
                         const int32_t span = first_wave(a0 + sg.nchunks - 1, U, STREAM_WAVES) -
                                              first_wave(a0, U, STREAM_WAVES) + 1;
                         if (span > ph.jmax) ++bad;
-                        for (int32_t j = 0; j < span; ++j) slot_reads.push_back((uint32_t)((rp * ph.jmax + j) * P.B));
+                        for (int32_t j = 0; j < span; ++j)
+                            for (int32_t b = 0; b < nb; ++b)
+                                slot_reads.push_back((uint32_t)((rp * ph.jmax + j) * nb + b));
                     }
                 rp_base += sp.nrows * sg.parts;
-                u_base += sp.nrows * sg.parts * sg.nchunks;
+                u_base += units_of(sp.nrows, sg.parts, sg.nchunks, tile);
             }
-            if (nrun != h.nruns) ++bad;
             if (u_base != U) ++bad;
             std::sort(slot_writes.begin(), slot_writes.end());
             std::sort(slot_reads.begin(), slot_reads.end());
             if (slot_writes != slot_reads) ++bad;
-            if (!slot_writes.empty() && (size_t)(slot_writes.back() + P.B) * 4 > P.lds_part_bytes) ++bad;
+            if (std::adjacent_find(slot_writes.begin(), slot_writes.end()) != slot_writes.end()) ++bad;
+            if (!slot_writes.empty() && (size_t)(slot_writes.back() + 1) * 4 > (size_t)P.part_bytes[p]) ++bad;
+            if ((size_t)rp_base * nb * 4 > (size_t)(ph.prm_off - ph.part_off) && !slot_writes.empty() &&
+                (size_t)rp_base * ph.jmax * nb * 4 > (size_t)P.part_bytes[p])
+                ++bad;
         }
         for (int32_t r = 0; r < ph.nrows; ++r)
             if (row_owner[r] != 1) ++bad;

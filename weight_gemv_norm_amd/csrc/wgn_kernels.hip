@@ -28,6 +28,8 @@ namespace wgn {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #ifndef WGN_DEPTH
 #define WGN_DEPTH 16
@@ -137,8 +139,14 @@ __device__ __forceinline__ void trace_point(const KArgs &a, int32_t p, int32_t g
 
 // ------------------------------------------------------------ streaming waves
 struct BlockMeta {
-    uint32_t meta_v;       // lane j holds the meta word of the block's unit j
+    uint32_t meta_v;       // vector path: lane j holds the meta word of the block's unit j
     int32_t xb_bytes;      // LDS bytes per batch row of x-hat in this block's phase
+    int32_t x_off;         // LDS offset of the phase's x-hat
+    int32_t part_off;      // LDS offset of the phase's partial slots
+    // matrix-core path (one unit per block; wave-uniform)
+    uint32_t xoff;         // chunk offset inside a batch row of x-hat
+    int32_t rows, slot0, slot_stride;
+    bool seg_end;
     bool last;             // last block of this wave in its phase
 };
 
@@ -166,9 +174,22 @@ __device__ __forceinline__ void stream_begin_phase(StreamState &S, int32_t p) {
     S.u = S.u_beg;
 }
 
-// Issue DEPTH unit loads (a block never spans a phase boundary).  Lane j first
-// computes the descriptor of unit j from the phase's run list in LDS; each
-// load then takes its base address and length from lane j through
+__device__ __forceinline__ void stream_advance(StreamState &S, BlockMeta &bm, int32_t step) {
+    if (S.done_all) {
+        bm.last = false;  // past the final phase: nothing to synchronise
+        return;
+    }
+    S.u = S.u + step < S.u_end ? S.u + step : S.u_end;
+    bm.last = S.u >= S.u_end;
+    if (bm.last) {
+        if (S.p + 1 < S.p1) stream_begin_phase(S, S.p + 1);
+        else S.done_all = true;
+    }
+}
+
+// Vector path: issue DEPTH unit loads (a block never spans a phase boundary).
+// Lane j first computes the descriptor of unit j from the phase's run list in
+// LDS; each load then takes its base address and length from lane j through
 // v_readlane.  Invalid slots load from an empty range (no memory traffic,
 // value 0), so every block issues the same number of loads and the
 // compiler's vmcnt bookkeeping stays exact.
@@ -185,6 +206,8 @@ __device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4
     const uint32_t plo = (uint32_t)ud.ptr, phi = (uint32_t)(ud.ptr >> 32);
     bm.meta_v = ud.meta;
     bm.xb_bytes = S.done_all ? 0 : S.h.xb_bytes;
+    bm.x_off = S.h.x_off;
+    bm.part_off = S.h.part_off;
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
         const uint32_t lo = __builtin_amdgcn_readlane(plo, j);
@@ -194,25 +217,18 @@ __device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4
         __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)nb, (int)RSRC_W3);
         d[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(lane * 16u), 0, WEIGHT_AUX);
     }
-    if (S.done_all) {
-        bm.last = false;  // past the final phase: nothing to synchronise
-        return;
-    }
-    S.u = S.u + DEPTH < S.u_end ? S.u + DEPTH : S.u_end;
-    bm.last = S.u >= S.u_end;
-    if (bm.last) {
-        if (S.p + 1 < S.p1) stream_begin_phase(S, S.p + 1);
-        else S.done_all = true;
-    }
+    stream_advance(S, bm, DEPTH);
 }
 
 // Every slot of a block is consumed unconditionally (an invalid slot holds
-// zeros and points at x-hat offset 0, which is initialised in every phase), so
-// every load is waited for in issue order on every path and the compiler's
-// vmcnt bookkeeping stays exact.
+// zeros and points at the start of x-hat, which is initialised in every
+// phase), so every load is waited for in issue order on every path and the
+// compiler's vmcnt bookkeeping stays exact.
 template <int B>
 __device__ __forceinline__ void consume_block(const u32x4 (&d)[DEPTH], const BlockMeta &bm, float (&acc)[B],
-                                              const char *xh, float *part, uint32_t lane) {
+                                              const char *lds, uint32_t lane) {
+    const char *xh = lds + bm.x_off;
+    float *part = (float *)(lds + bm.part_off);
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
         const uint32_t m = __builtin_amdgcn_readlane(bm.meta_v, j);
@@ -234,13 +250,101 @@ __device__ __forceinline__ void consume_block(const u32x4 (&d)[DEPTH], const Blo
     }
 }
 
-template <int B, bool CHAIN>
+// Matrix-core path: one unit (16 row-parts x 512 K) per block.  Load t of
+// lane l reads 16 bytes of row l % 16 at K offset 8 (l / 16) + 32 t: the A
+// operand of v_mfma_f32_16x16x32_bf16.  Lanes past the end of their row read
+// an out-of-range offset (value 0, no traffic); rows past the tile's last
+// valid row fall outside the buffer's range the same way.
+__device__ __forceinline__ void load_tile(const KArgs &a, StreamState &S, u32x4 (&d)[DEPTH], BlockMeta &bm,
+                                          uint32_t lane) {
+    TileDesc td;
+    td.valid = false;
+    if (!S.done_all) td = unit_desc_tile(S.h, S.runs, S.u, S.u_beg, S.u_end, S.w, a.nb);
+    const bool valid = !S.done_all && td.valid;
+    const uint64_t ptr = valid ? td.ptr : (uint64_t)(uintptr_t)a.ist.W;
+    const uint32_t plo = __builtin_amdgcn_readfirstlane((uint32_t)ptr);
+    const uint32_t phi = __builtin_amdgcn_readfirstlane((uint32_t)(ptr >> 32));
+    const uint32_t nrec = __builtin_amdgcn_readfirstlane(valid ? td.nrec : 0u);
+    const void *base = (const void *)(uintptr_t)(((uint64_t)phi << 32) | plo);
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)nrec, (int)RSRC_W3);
+    const uint32_t q = lane >> 4;
+    const uint32_t lane_off = (lane & 15u) * (uint32_t)(valid ? td.rstride : 0) + q * 16u;
+    const int32_t kv = (valid ? td.kval : 0) - 8 * (int32_t)q;  // K elements from this lane's first position
+#pragma unroll
+    for (int t = 0; t < DEPTH; ++t) {
+        const uint32_t off = 32 * t < kv ? lane_off + 64u * (uint32_t)t : 0x80000000u;
+        d[t] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, WEIGHT_AUX);
+    }
+    bm.xb_bytes = S.h.xb_bytes;
+    bm.x_off = S.h.x_off;
+    bm.part_off = S.h.part_off;
+    bm.xoff = valid ? td.xoff : 0u;
+    bm.rows = valid ? td.rows : 0;
+    bm.slot0 = valid ? td.slot0 : 0;
+    bm.slot_stride = valid ? td.slot_stride : 0;
+    bm.seg_end = valid && td.seg_end;
+    stream_advance(S, bm, 1);
+}
+
+__device__ __forceinline__ void consume_tile(const u32x4 (&d)[DEPTH], const BlockMeta &bm, f32x4 &acc,
+                                             const char *lds, uint32_t lane, int32_t nb) {
+    const uint32_t q = lane >> 4, j = lane & 15u;
+    const uint32_t jr = (int32_t)j < nb ? j : (uint32_t)(nb - 1);  // batch rows past nb: results unused
+    const char *xp = lds + bm.x_off + jr * (uint32_t)bm.xb_bytes + bm.xoff + q * 16u;
+#pragma unroll
+    for (int t = 0; t < DEPTH; ++t) {
+        const u32x4 xv = *(const u32x4 *)(xp + 64 * t);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, d[t]), __builtin_bit_cast(bf16x8, xv),
+                                                      acc, 0, 0, 0);
+    }
+    if (bm.seg_end) {
+        // lane l holds rows 4 (l / 16) + r, batch row l % 16
+        float *part = (float *)(lds + bm.part_off);
+        const float av[4] = {acc[0], acc[1], acc[2], acc[3]};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int32_t row = 4 * (int32_t)q + r;
+            if (row < bm.rows && (int32_t)j < nb) part[bm.slot0 + row * bm.slot_stride + (int32_t)j] = av[r];
+        }
+        acc = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    }
+}
+
+template <int B, bool TILE>
+struct Acc;
+template <int B>
+struct Acc<B, false> {
+    float v[B];
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int b = 0; b < B; ++b) v[b] = 0.0f;
+    }
+};
+template <int B>
+struct Acc<B, true> {
+    f32x4 v;
+    __device__ __forceinline__ void zero() { v = (f32x4){0.0f, 0.0f, 0.0f, 0.0f}; }
+};
+
+template <int B, bool TILE>
+__device__ __forceinline__ void load_any(const KArgs &a, StreamState &S, u32x4 (&d)[DEPTH], BlockMeta &bm,
+                                         uint32_t lane) {
+    if constexpr (TILE) load_tile(a, S, d, bm, lane);
+    else load_block<B>(a, S, d, bm, lane);
+}
+template <int B, bool TILE>
+__device__ __forceinline__ void consume_any(const KArgs &a, const u32x4 (&d)[DEPTH], const BlockMeta &bm,
+                                            Acc<B, TILE> &acc, const char *lds, uint32_t lane) {
+    if constexpr (TILE) consume_tile(d, bm, acc.v, lds, lane, a.nb);
+    else consume_block<B>(d, bm, acc.v, lds, lane);
+}
+
+template <int B, bool CHAIN, bool TILE>
 __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
+    static_assert(!TILE || DEPTH * 32 == UNIT, "a matrix-core unit is DEPTH loads of 32 K elements");
     const uint32_t lane = lane_id();
-    const char *xh = lds;
-    float *part = (float *)(lds + a.lds_x_bytes);
     StreamState S;
-    S.desc = lds + a.lds_desc_off;
+    S.desc = lds + LDS_DESC_OFF;
     S.g = g;
     S.w = w;
     S.p1 = a.p1;
@@ -249,9 +353,8 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
     stream_begin_phase(S, a.p0);
     u32x4 dA[DEPTH], dB[DEPTH];
     BlockMeta mA, mB;
-    float acc[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+    Acc<B, TILE> acc;
+    acc.zero();
 
     // Two blocks are always in flight: a buffer is refilled as soon as it has
     // been consumed.  When a block ends a phase, the refill is issued before
@@ -261,35 +364,35 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
     // The loop has no early exit and no global stores: past the final phase
     // it only meets empty blocks (no barriers, no partial writes), which keeps
     // the compiler's vmcnt bookkeeping exact.
-    uint64_t *tl = (uint64_t *)(lds + a.lds_desc_off + DESC_BUFS * RUN_BUF_BYTES);  // trace slots
+    uint64_t *tl = (uint64_t *)(lds + LDS_TRACE_OFF);  // trace slots
     const bool tw = a.trace && w == 0 && lane == 0;
-    load_block<B>(a, S, dA, mA, lane);
-    load_block<B>(a, S, dB, mB, lane);
+    load_any<B, TILE>(a, S, dA, mA, lane);
+    load_any<B, TILE>(a, S, dB, mB, lane);
     wg_barrier();  // x-hat of the first phase is ready
     bool ok = abort_flag_get() == 0;
     int32_t p = a.p0;
     if (tw) tl[(p & 1) * 3 + 0] = wall_clock64();
     while (ok && p < a.p1) {
-        consume_block<B>(dA, mA, acc, xh, part, lane);
+        consume_any<B, TILE>(a, dA, mA, acc, lds, lane);
         const bool endA = mA.last;
         if (endA) {
             if (tw) tl[(p & 1) * 3 + 2] = wall_clock64();
             wg_barrier();  // partials of phase p are complete
         }
-        load_block<B>(a, S, dA, mA, lane);
+        load_any<B, TILE>(a, S, dA, mA, lane);
         if (endA && ++p < a.p1) {
             if (tw) tl[(p & 1) * 3 + 1] = wall_clock64();
             wg_barrier();  // x-hat of phase p is ready
             ok = abort_flag_get() == 0;
             if (tw) tl[(p & 1) * 3 + 0] = wall_clock64();
         }
-        consume_block<B>(dB, mB, acc, xh, part, lane);
+        consume_any<B, TILE>(a, dB, mB, acc, lds, lane);
         const bool endB = ok && mB.last;
         if (endB) {
             if (tw) tl[(p & 1) * 3 + 2] = wall_clock64();
             wg_barrier();
         }
-        load_block<B>(a, S, dB, mB, lane);
+        load_any<B, TILE>(a, S, dB, mB, lane);
         if (endB && ++p < a.p1) {
             if (tw) tl[(p & 1) * 3 + 1] = wall_clock64();
             wg_barrier();
@@ -333,7 +436,7 @@ __device__ void prefetch_params(const KArgs &a, const DevPhase &ph, char *prm, u
         const int32_t n8 = src.K >> 3;
         if (src.norm != NORM_NONE && src.gamma) copy_to_lds<0>(src.gamma, prm + off, n8, lane);
         if (src.norm == NORM_LAYER && src.beta) copy_to_lds<0>(src.beta, prm + off + prm_bytes(src) / 2, n8, lane);
-        off += prm_bytes(src);
+        if (src.norm != NORM_NONE) off += prm_bytes(src);
     }
 }
 
@@ -343,11 +446,14 @@ __device__ void prefetch_params(const KArgs &a, const DevPhase &ph, char *prm, u
 // run out of LDS.
 template <int B, bool CHAIN>
 __device__ void issue_source_loads(const KArgs &a, const DevPhase &ph, char *xh, uint32_t lane) {
+    const int32_t nb = a.nb;
     for (int32_t si = 0; si < ph.nsrc; ++si) {
         const DevSource src = source_of<CHAIN>(a, ph.src0 + si);
         const int32_t n8 = src.K >> 3;
         const int32_t padded8 = nchunks_of(src.K) * (UNIT / 8);
+#pragma unroll
         for (int b = 0; b < B; ++b) {
+            if (b >= nb) break;
             char *dst = xh + ((size_t)b * ph.xb + src.lds_off) * 2;
             copy_to_lds<COH>(src.x + (int64_t)b * src.x_stride, dst, n8, lane);
             for (int32_t i = n8 + lane; i < padded8; i += 64) *(u32x4 *)(dst + i * 16) = (u32x4){0u, 0u, 0u, 0u};
@@ -358,17 +464,19 @@ __device__ void issue_source_loads(const KArgs &a, const DevPhase &ph, char *xh,
 // Statistics and normalisation out of LDS, after the copies have landed.
 template <int B, bool CHAIN>
 __device__ void finish_sources(const KArgs &a, const DevPhase &ph, char *xh, const char *prm, uint32_t lane) {
+    const int32_t nb = a.nb;
     int32_t poff = 0;
     for (int32_t si = 0; si < ph.nsrc; ++si) {
         const DevSource src = source_of<CHAIN>(a, ph.src0 + si);
+        if (src.norm == NORM_NONE) continue;
         const int32_t K = src.K;
         const int32_t n8 = K >> 3;
         const float invK = 1.0f / (float)K;
         const char *gp = prm + poff;
         const char *bp = prm + poff + prm_bytes(src) / 2;
         poff += prm_bytes(src);
-        if (src.norm == NORM_NONE) continue;
         for (int b = 0; b < B; ++b) {
+            if (b >= nb) break;
             uint16_t *dst = (uint16_t *)(xh + ((size_t)b * ph.xb + src.lds_off) * 2);
             float s1 = 0.0f, s2 = 0.0f;
             for (int32_t i = lane; i < n8; i += 64) {
@@ -428,35 +536,38 @@ __device__ void finish_sources(const KArgs &a, const DevPhase &ph, char *xh, con
 // bias and then the residual of each batch row, as FP32).
 template <int B, bool CHAIN>
 __device__ void stage_epilogue_inputs(const KArgs &a, const RunHdr &h, const Run *runs, float *epi, uint32_t lane) {
+    const int32_t nb = a.nb;
     for (int32_t ri = 0; ri < h.nruns; ++ri) {
         const Run &r = runs[ri];
         const uint16_t *bias = r.bias;
         const uint16_t *res = r.residual;
-        if (!bias && !res) continue;
+        if ((!bias && !res) || (r.carry & CARRY_OUT)) continue;
         const int64_t res_stride = r.res_stride;
         const int32_t row0 = r.row0, nrows = r.nrows, rp_base = r.rp_base, parts = r.parts;
         const __amdgpu_buffer_rsrc_t rr = rsrc_of(res);
         for (int32_t i = lane; i < nrows; i += 64) {
             const int32_t n = row0 + i;
-            float *e = epi + (size_t)(rp_base + i * parts) * (1 + B);
+            float *e = epi + (size_t)(rp_base + i * parts) * (1 + nb);
             e[0] = bias ? bf2f(bias[n]) : 0.0f;
 #pragma unroll
-            for (int b = 0; b < B; ++b)
+            for (int b = 0; b < B; ++b) {
+                if (b >= nb) break;
                 e[1 + b] = res ? bf2f(__builtin_amdgcn_raw_buffer_load_b16(
-                                      rr, (int)(((int64_t)b * res_stride + n) * 2), 0, COH))
+                                     rr, (int)(((int64_t)b * res_stride + n) * 2), 0, COH))
                                : 0.0f;
+            }
         }
     }
 }
 
 // Merge the per-workgroup argmax keys of one ARGMAX stage (called by the last
 // workgroup to arrive) and write the index / maximum outputs.
-template <int B>
 __device__ void argmax_merge(const KArgs &a, int32_t am_slot, void *y, float *maxval, uint32_t lane) {
-    for (int b = 0; b < B; ++b) {
+    const int32_t nb = a.nb;
+    for (int b = 0; b < nb; ++b) {
         uint64_t best = 0;
         for (int32_t gg = lane; gg < a.G; gg += 64) {
-            uint64_t k = __hip_atomic_load(&a.am_part[((size_t)am_slot * a.G + gg) * B + b], __ATOMIC_RELAXED,
+            uint64_t k = __hip_atomic_load(&a.am_part[((size_t)am_slot * a.G + gg) * nb + b], __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
             best = k > best ? k : best;
         }
@@ -470,13 +581,17 @@ __device__ void argmax_merge(const KArgs &a, int32_t am_slot, void *y, float *ma
     }
 }
 
-template <int B, bool CHAIN>
+// Sum the partial slots of every row-part (in wave order, after the carry of
+// earlier K windows), then either carry the sums to the next K window or
+// apply the epilogue and store the outputs.
+template <int B, bool CHAIN, bool TILE>
 __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32_t g, const float *part,
-                         const float *epi, uint32_t lane) {
+                         const float *epi, float *carry, uint32_t lane) {
+    const int32_t nb = a.nb;
     for (int32_t ri = 0; ri < h.nruns; ++ri) {
         const Run &r = runs[ri];
         const int32_t parts = r.parts, nch = r.nchunks, epi_kind = r.epi, row0 = r.row0, nrows = r.nrows;
-        const int32_t rp_base = r.rp_base, u_base = r.u_base;
+        const int32_t rp_base = r.rp_base, cy = r.carry;
         const bool has_res = r.residual != nullptr, has_bias = r.bias != nullptr;
         const int64_t y_stride = r.y_stride;
         const int32_t N = r.N;
@@ -492,22 +607,26 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
             for (int pt = 0; pt < 2; ++pt) {
                 if (pt >= parts) break;
                 const int32_t rp = rp_base + i * parts + pt;
-                const int32_t a0 = u_base + (i * parts + pt) * nch;
+                const int32_t a0 = first_unit_of_rowpart(r, i, pt, TILE);
                 const int32_t span =
                     first_wave(a0 + nch - 1, h.U, STREAM_WAVES) - first_wave(a0, h.U, STREAM_WAVES) + 1;
-                const float *pp = part + (size_t)rp * h.jmax * B;
+                const float *pp = part + (size_t)rp * h.jmax * nb;
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
-                    float s = pp[b];
-                    for (int32_t j = 1; j < span; ++j) s += pp[j * B + b];
+                    if (b >= nb) break;
+                    float s = (cy & CARRY_IN) ? carry[rp * nb + b] + pp[b] : pp[b];
+                    for (int32_t j = 1; j < span; ++j) s += pp[j * nb + b];
+                    if (cy & CARRY_OUT) carry[rp * nb + b] = s;
                     if (pt == 0) acc0[b] = s;
                     else acc1[b] = s;
                 }
             }
-            const float *ep = epi + (size_t)(rp_base + i * parts) * (1 + B);
+            if (cy & CARRY_OUT) continue;
+            const float *ep = epi + (size_t)(rp_base + i * parts) * (1 + nb);
             const float bias = has_bias ? ep[0] : 0.0f;
 #pragma unroll
             for (int b = 0; b < B; ++b) {
+                if (b >= nb) break;
                 const float z = acc0[b] + bias;
                 if (epi_kind == EPI_ARGMAX) {
                     if (logits) logits[(size_t)b * N + n] = z;
@@ -523,13 +642,14 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
                 __builtin_amdgcn_raw_buffer_store_b16(f2bf(e), ry, (int)(((int64_t)b * y_stride + n) * 2), 0, COH);
             }
         }
-        if (epi_kind == EPI_ARGMAX) {
+        if (epi_kind == EPI_ARGMAX && !(cy & CARRY_OUT)) {
             const int32_t am_slot = r.am_slot;
 #pragma unroll
             for (int b = 0; b < B; ++b) {
+                if (b >= nb) break;
                 const uint64_t k = wave_max_u64(best[b]);
                 if (lane == 0)
-                    __hip_atomic_store(&a.am_part[((size_t)am_slot * a.G + g) * B + b], k, __ATOMIC_RELAXED,
+                    __hip_atomic_store(&a.am_part[((size_t)am_slot * a.G + g) * nb + b], k, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
             }
             // the partial keys are agent-scope atomic stores; once they have
@@ -540,7 +660,7 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
                 old = __hip_atomic_fetch_add(&a.tickets[am_slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             old = __shfl(old, 0);
             if (old == (uint32_t)(a.G - 1)) {
-                argmax_merge<B>(a, am_slot, r.y, r.maxval, lane);
+                argmax_merge(a, am_slot, r.y, r.maxval, lane);
                 if (lane == 0)
                     __hip_atomic_store(&a.tickets[am_slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -549,23 +669,19 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
 }
 
 // Write phase q's run list for workgroup g into its LDS buffer.
-template <bool CHAIN>
-__device__ void build_runs(const KArgs &a, int32_t q, int32_t g, char *desc, uint32_t lane) {
+template <bool CHAIN, bool TILE>
+__device__ void build_runs(const KArgs &a, int32_t q, int32_t g, char *desc) {
     // every lane computes the same list; the runs go straight into LDS
     char *buf = desc + (q % DESC_BUFS) * RUN_BUF_BYTES;
     RunHdr h;
-    make_runs<CHAIN>(a, q, g, h, (Run *)(buf + sizeof(RunHdr)));
+    make_runs<CHAIN>(a, q, g, TILE, h, (Run *)(buf + sizeof(RunHdr)));
     *(RunHdr *)buf = h;
-    (void)lane;
 }
 
-template <int B, bool CHAIN>
+template <int B, bool CHAIN, bool TILE>
 __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
     const uint32_t lane = lane_id();
-    const float *part = (const float *)(lds + a.lds_x_bytes);
-    char *prm = lds + a.lds_prm_off;
-    float *epi = (float *)(lds + a.lds_epi_off);
-    char *desc = lds + a.lds_desc_off;
+    char *desc = lds + LDS_DESC_OFF;
     if (lane == 0) abort_flag_set(0);
     const uint32_t flag_val =
         a.persistent ? __hip_atomic_load(a.run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
@@ -577,14 +693,19 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
     // (iteration q rebuilds phase q-1's) only after every wave has passed the
     // partials barrier of the phase it held.  (This schedule is modelled and
     // checked on the host by tests/test_schedule.py.)
-    for (int32_t q = a.p0; q < a.p1 && q < a.p0 + DESC_AHEAD; ++q) build_runs<CHAIN>(a, q, g, desc, lane);
+    for (int32_t q = a.p0; q < a.p1 && q < a.p0 + DESC_AHEAD; ++q) build_runs<CHAIN, TILE>(a, q, g, desc);
     wg_barrier();
     for (int32_t p = a.p0; p < a.p1; ++p) {
         const DevPhase ph = phase_of<CHAIN>(a, p);
+        char *xh = lds + ph.x_off;
+        const float *part = (const float *)(lds + ph.part_off);
+        char *prm = lds + ph.prm_off;
+        float *epi = (float *)(lds + ph.epi_off);
+        float *carry = (float *)(lds + ph.carry_off);
         trace_point(a, p, g, 0, lane);
         // descriptors, run lists and gains do not depend on the previous
         // phase: prepare them before waiting for it
-        if (p + DESC_AHEAD < a.p1) build_runs<CHAIN>(a, p + DESC_AHEAD, g, desc, lane);
+        if (p + DESC_AHEAD < a.p1) build_runs<CHAIN, TILE>(a, p + DESC_AHEAD, g, desc);
         const char *rb = desc + (p % DESC_BUFS) * RUN_BUF_BYTES;
         const RunHdr h = *(const RunHdr *)rb;
         const Run *runs = (const Run *)(rb + sizeof(RunHdr));
@@ -618,19 +739,19 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
             }
         }
         trace_point(a, p, g, 1, lane);
-        issue_source_loads<B, CHAIN>(a, ph, lds, lane);
+        issue_source_loads<B, CHAIN>(a, ph, xh, lane);
         stage_epilogue_inputs<B, CHAIN>(a, h, runs, epi, lane);
         __builtin_amdgcn_s_waitcnt(0);  // inputs, gains and epilogue values have landed
-        finish_sources<B, CHAIN>(a, ph, lds, prm, lane);
+        finish_sources<B, CHAIN>(a, ph, xh, prm, lane);
         trace_point(a, p, g, 2, lane);
         wg_barrier();  // x-hat ready
         wg_barrier();  // partials complete
         trace_point(a, p, g, 3, lane);
         if (a.trace && lane < 3) {
-            const uint64_t *tl = (const uint64_t *)(lds + a.lds_desc_off + DESC_BUFS * RUN_BUF_BYTES);
+            const uint64_t *tl = (const uint64_t *)(lds + LDS_TRACE_OFF);
             a.trace[((size_t)p * a.G + g) * TRACE_POINTS + 6 + lane] = tl[(p & 1) * 3 + lane];
         }
-        epilogue<B, CHAIN>(a, h, runs, g, part, epi, lane);
+        epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane);
         trace_point(a, p, g, 4, lane);
         if (a.persistent) {
             // outputs are written through (coherent stores); once they have
@@ -657,13 +778,13 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
     }
 }
 
-template <int B, bool CHAIN>
+template <int B, bool CHAIN, bool TILE>
 __global__ __launch_bounds__(THREADS, 1) void chain_kernel(KArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int32_t g = blockIdx.x;
     const int32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (w < STREAM_WAVES) stream_wave<B, CHAIN>(a, g, w, lds);
-    else control_wave<B, CHAIN>(a, g, lds);
+    if (w < STREAM_WAVES) stream_wave<B, CHAIN, TILE>(a, g, w, lds);
+    else control_wave<B, CHAIN, TILE>(a, g, lds);
 }
 
 // ------------------------------------------------------- standalone norm rows
@@ -754,33 +875,35 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t *x, in
 // ------------------------------------------------------------ host launchers
 namespace wgn {
 
-template <int B, bool CHAIN>
+template <int B, bool CHAIN, bool TILE>
 static hipError_t launch_chain_b(const KArgs &a, int32_t grid, size_t lds, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
         // 160 KB of LDS per workgroup on gfx950, minus the kernel's static LDS
-        hipError_t e = hipFuncSetAttribute((const void *)chain_kernel<B, CHAIN>,
+        hipError_t e = hipFuncSetAttribute((const void *)chain_kernel<B, CHAIN, TILE>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((chain_kernel<B, CHAIN>), dim3(grid), dim3(THREADS), lds, s, a);
+    hipLaunchKernelGGL((chain_kernel<B, CHAIN, TILE>), dim3(grid), dim3(THREADS), lds, s, a);
     return hipGetLastError();
 }
 
 template <bool CHAIN>
-static hipError_t launch_chain_c(int32_t batch, const KArgs &a, int32_t grid, size_t lds, hipStream_t s) {
+static hipError_t launch_chain_c(int32_t batch, bool tile, const KArgs &a, int32_t grid, size_t lds, hipStream_t s) {
+    if (tile) return batch <= MAX_BATCH ? launch_chain_b<MAX_BATCH, CHAIN, true>(a, grid, lds, s) : hipErrorInvalidValue;
     switch (batch) {
-    case 1: return launch_chain_b<1, CHAIN>(a, grid, lds, s);
-    case 2: return launch_chain_b<2, CHAIN>(a, grid, lds, s);
-    case 3: return launch_chain_b<3, CHAIN>(a, grid, lds, s);
-    case 4: return launch_chain_b<4, CHAIN>(a, grid, lds, s);
+    case 1: return launch_chain_b<1, CHAIN, false>(a, grid, lds, s);
+    case 2: return launch_chain_b<2, CHAIN, false>(a, grid, lds, s);
+    case 3: return launch_chain_b<3, CHAIN, false>(a, grid, lds, s);
+    case 4: return launch_chain_b<4, CHAIN, false>(a, grid, lds, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_chain(int32_t batch, const KArgs &a, int32_t grid, size_t lds, hipStream_t s) {
-    return a.phases ? launch_chain_c<true>(batch, a, grid, lds, s) : launch_chain_c<false>(batch, a, grid, lds, s);
+hipError_t launch_chain(int32_t batch, bool tile, const KArgs &a, int32_t grid, size_t lds, hipStream_t s) {
+    return a.phases ? launch_chain_c<true>(batch, tile, a, grid, lds, s)
+                    : launch_chain_c<false>(batch, tile, a, grid, lds, s);
 }
 
 hipError_t launch_rmsnorm_rows(const uint16_t *x, int64_t xs, const uint16_t *g, float eps, uint16_t *y, int64_t ys,

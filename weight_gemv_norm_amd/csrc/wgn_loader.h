@@ -10,11 +10,12 @@
 // layer while this one runs") moved inside one persistent kernel.
 //
 // make_runs() reduces a phase to the workgroup's "run list" (one entry per
-// stage with rows in the workgroup); unit_desc_runs() maps one unit index to
-// its weight address and its meta word.  On the device, the control wave
-// builds run lists three phases ahead into LDS and lane j of a streaming wave
-// evaluates unit_desc_runs() for the j-th unit of a block; the host planner's
-// self-test runs the same two functions for every unit to check the partition.
+// stage of the phase); unit_desc_runs() (vector path) and unit_desc_tile()
+// (matrix-core path) map one unit index to its weight address and the data
+// the wave needs to consume it.  On the device, the control wave builds run
+// lists three phases ahead into LDS and the streaming waves evaluate the unit
+// descriptors of their next block from them; the host planner's self-test
+// runs the same functions for every unit to check the partition.
 #pragma once
 #include "wgn_prog.h"
 
@@ -53,10 +54,11 @@ struct PhaseGeo {
     int32_t jmax;
     int32_t xb_bytes;      // LDS bytes per batch row of x-hat
     int32_t stage0, nstages, src0;
+    int32_t x_off, part_off;
 };
 
 template <bool CHAIN>
-WGN_HD PhaseGeo phase_geo(const KArgs &a, int32_t p, int32_t g) {
+WGN_HD PhaseGeo phase_geo(const KArgs &a, int32_t p, int32_t g, bool tile) {
     const DevPhase ph = phase_of<CHAIN>(a, p);
     PhaseGeo G;
     G.p = p;
@@ -72,11 +74,13 @@ WGN_HD PhaseGeo phase_geo(const KArgs &a, int32_t p, int32_t g) {
     G.stage0 = ph.stage0;
     G.nstages = ph.nstages;
     G.src0 = ph.src0;
+    G.x_off = ph.x_off;
+    G.part_off = ph.part_off;
     int32_t U = 0;
     for (int32_t i = 0; i < ph.nstages; ++i) {
         const DevStage st = stage_of<CHAIN>(a, ph.stage0 + i);
         StageSpan sp = stage_span(st, G.r0, G.r1, 0, 0);
-        U += sp.nrows * st.parts * st.nchunks;
+        U += units_of(sp.nrows, st.parts, st.nchunks, tile);
     }
     G.U = U;
     return G;
@@ -86,11 +90,14 @@ WGN_HD PhaseGeo phase_geo(const KArgs &a, int32_t p, int32_t g) {
 // order (nrows = 0 when the workgroup owns none of its rows; an argmax stage
 // still takes part in the merge then).
 template <bool CHAIN>
-WGN_HD void make_runs(const KArgs &a, int32_t p, int32_t g, RunHdr &h, Run *runs) {
-    const PhaseGeo G = phase_geo<CHAIN>(a, p, g);
+WGN_HD void make_runs(const KArgs &a, int32_t p, int32_t g, bool tile, RunHdr &h, Run *runs) {
+    const PhaseGeo G = phase_geo<CHAIN>(a, p, g, tile);
     h.U = G.U;
     h.jmax = G.jmax;
     h.xb_bytes = G.xb_bytes;
+    h.x_off = G.x_off;
+    h.part_off = G.part_off;
+    h.pad0 = h.pad1 = 0;
     int32_t n = 0, u_base = 0, rp_base = 0;
     for (int32_t i = 0; i < G.nstages && n < MAX_RUNS; ++i) {
         const DevStage st = stage_of<CHAIN>(a, G.stage0 + i);
@@ -105,6 +112,8 @@ WGN_HD void make_runs(const KArgs &a, int32_t p, int32_t g, RunHdr &h, Run *runs
         r.nrows = sp.nrows;
         r.u_base = u_base;
         r.rp_base = rp_base;
+        r.c0 = st.c0;
+        r.carry = st.carry;
         r.xoff = (uint32_t)source_of<CHAIN>(a, G.src0 + st.src).lds_off * 2u;
         r.stage = G.stage0 + i;
         r.epi = st.epi;
@@ -118,7 +127,7 @@ WGN_HD void make_runs(const KArgs &a, int32_t p, int32_t g, RunHdr &h, Run *runs
         r.res_stride = st.res_stride;
         r.y_stride = st.y_stride;
         runs[n++] = r;
-        u_base += sp.nrows * st.parts * st.nchunks;
+        u_base += units_of(sp.nrows, st.parts, st.nchunks, tile);
         rp_base += sp.nrows * st.parts;
     }
     h.nruns = n;
@@ -147,7 +156,7 @@ WGN_HD UnitDesc unit_desc_runs(const RunHdr &h, const Run *runs, int32_t v, int3
             const int32_t rem = local - rk * per_row;
             const int32_t part = rem / r.nchunks;
             const int32_t chunk = rem - part * r.nchunks;
-            const uint32_t off = (uint32_t)chunk * (UNIT * 2u);
+            const uint32_t off = (uint32_t)(r.c0 + chunk) * (UNIT * 2u);
             const uint16_t *rowp = (part == 0 ? r.W : r.W_up) + (int64_t)(r.row0 + rk) * r.K;
             d.ptr = (uint64_t)(uintptr_t)rowp + off;
             d.nbytes = (uint32_t)r.K * 2u - off;
@@ -156,11 +165,79 @@ WGN_HD UnitDesc unit_desc_runs(const RunHdr &h, const Run *runs, int32_t v, int3
             const int32_t j = ua < u_beg ? w - first_wave(ua, h.U, STREAM_WAVES) : 0;
             const uint32_t slot = (uint32_t)((rp * h.jmax + j) * B);
             const bool seg_end = (chunk == r.nchunks - 1) || (v == u_end - 1);
-            d.meta = pack_meta(r.xoff + off, seg_end, true, slot);
+            d.meta = pack_meta(r.xoff + (uint32_t)chunk * (UNIT * 2u), seg_end, true, slot);
             return d;
         }
     }
     return d;
+}
+
+// Matrix-core unit: TILE_ROWS consecutive row-parts (one part of one stage) x
+// 512 K elements.  Wave-uniform; lane l then loads row l % 16 at K offset
+// 8 * (l / 16) + 32 t for t = 0..15.
+struct TileDesc {
+    uint64_t ptr;          // first byte of the tile's first row at this chunk
+    uint32_t nrec;         // bytes from ptr to the end of the tile's last row (0 = invalid unit)
+    int32_t kval;          // K elements of a row from this chunk on
+    uint32_t xoff;         // LDS byte offset of the chunk inside a batch row of x-hat
+    int32_t rows;          // valid rows of the tile (1..16)
+    int32_t rstride;       // row stride in bytes (K * 2)
+    int32_t slot0;         // partial slot of the tile's first row (floats, batch included)
+    int32_t slot_stride;   // slot distance between consecutive rows of the tile
+    bool seg_end;          // last unit of this wave's share of the tile's row-parts
+    bool valid;
+};
+
+WGN_HD TileDesc unit_desc_tile(const RunHdr &h, const Run *runs, int32_t v, int32_t u_beg, int32_t u_end,
+                               int32_t w, int32_t nb) {
+    TileDesc d;
+    d.ptr = 0;
+    d.nrec = 0;
+    d.kval = 0;
+    d.xoff = 0;
+    d.rows = 0;
+    d.rstride = 0;
+    d.slot0 = 0;
+    d.slot_stride = 0;
+    d.seg_end = false;
+    d.valid = false;
+    if (v < u_beg || v >= u_end) return d;
+    for (int32_t i = 0; i < h.nruns; ++i) {
+        const Run &r = runs[i];
+        const int32_t per_tile = r.parts * r.nchunks;
+        const int32_t ntiles = (r.nrows + TILE_ROWS - 1) / TILE_ROWS;
+        if (v < r.u_base + ntiles * per_tile) {
+            const int32_t local = v - r.u_base;
+            const int32_t ti = local / per_tile;
+            const int32_t rem = local - ti * per_tile;
+            const int32_t part = rem / r.nchunks;
+            const int32_t chunk = rem - part * r.nchunks;
+            const int32_t rows = r.nrows - ti * TILE_ROWS < TILE_ROWS ? r.nrows - ti * TILE_ROWS : TILE_ROWS;
+            const int32_t kc = (r.c0 + chunk) * UNIT;
+            const uint16_t *base = (part == 0 ? r.W : r.W_up) + (int64_t)(r.row0 + ti * TILE_ROWS) * r.K;
+            d.ptr = (uint64_t)(uintptr_t)base + (uint64_t)kc * 2u;
+            d.nrec = (uint32_t)rows * (uint32_t)r.K * 2u - (uint32_t)kc * 2u;
+            d.kval = r.K - kc;
+            d.xoff = r.xoff + (uint32_t)chunk * (UNIT * 2u);
+            d.rows = rows;
+            d.rstride = r.K * 2;
+            const int32_t rp0 = r.rp_base + ti * TILE_ROWS * r.parts + part;
+            const int32_t ua = v - chunk;
+            const int32_t j = ua < u_beg ? w - first_wave(ua, h.U, STREAM_WAVES) : 0;
+            d.slot0 = (rp0 * h.jmax + j) * nb;
+            d.slot_stride = r.parts * h.jmax * nb;
+            d.seg_end = (chunk == r.nchunks - 1) || (v == u_end - 1);
+            d.valid = true;
+            return d;
+        }
+    }
+    return d;
+}
+
+// First unit (WG-local index) of row i, part pt of a run.
+WGN_HD int32_t first_unit_of_rowpart(const Run &r, int32_t i, int32_t pt, bool tile) {
+    return tile ? r.u_base + ((i / TILE_ROWS) * r.parts + pt) * r.nchunks
+                : r.u_base + (i * r.parts + pt) * r.nchunks;
 }
 
 }  // namespace wgn

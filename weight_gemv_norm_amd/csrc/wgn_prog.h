@@ -5,15 +5,26 @@
 //  * rows of all stages in the phase form one "row space"; every workgroup (WG)
 //    owns a contiguous, cost-balanced run of whole rows;
 //  * a row of a SwiGLU stage has two "row-parts" (gate, up), other rows one;
-//  * a row-part is streamed as ceil(K/512) "units": one unit = 512 consecutive
-//    K elements of one weight row = 64 lanes x 16 bytes, one 128-bit load per
-//    lane, fully coalesced (1 KB per wave-load);
+//  * row-parts are streamed in "units" of 512 consecutive K elements:
+//      - vector path (batch <= 4): a unit is one row-part's 512 elements =
+//        64 lanes x 16 bytes, one 128-bit load per lane, fully coalesced;
+//        a block of 16 units is 16 independent loads;
+//      - matrix-core path (any batch, used for batch > 4): a unit is a tile of
+//        16 consecutive row-parts x 512 elements, streamed as 16 loads in
+//        which lane l reads 16 bytes of row l%16 (64 contiguous bytes per row
+//        per load) -- exactly the A operand of v_mfma_f32_16x16x32_bf16; a
+//        block is one such unit;
 //  * the WG's units are split evenly over its streaming waves (a row-part may
 //    be split across neighbouring waves); each wave reduces its part of a
-//    row-part across lanes and writes the partial to an LDS slot indexed by
-//    (row-part, wave - first wave of that row-part), and the WG's control wave
-//    sums the slots in wave order.  The order of every FP32 sum is therefore
-//    fixed by (grid, shape) alone and results are bit-reproducible.
+//    row-part and writes the partial to an LDS slot indexed by (row-part,
+//    wave - first wave of that row-part), and the WG's control wave sums the
+//    slots in wave order.  The order of every FP32 sum is therefore fixed by
+//    (grid, shape) alone and results are bit-reproducible;
+//  * a phase whose inputs do not fit in LDS (the 8960-long down-projection
+//    input at batch 16) is split into "K windows": consecutive phases over
+//    the same rows, each streaming a window of the K chunks; partial row sums
+//    are carried in LDS from one window to the next and only the last window
+//    runs the epilogue.
 #pragma once
 #include <stdint.h>
 
@@ -34,7 +45,8 @@ constexpr int STREAM_WAVES = WGN_STREAM_WAVES;  // weight-streaming waves per WG
 constexpr int WAVES = STREAM_WAVES + 1;   // + one control wave
 constexpr int THREADS = WAVES * 64;
 constexpr int MAX_BATCH = 16;
-constexpr int MAX_BATCH_VALU = 4;
+constexpr int MAX_BATCH_VALU = 4;   // largest batch of the vector path
+constexpr int TILE_ROWS = 16;        // row-parts per matrix-core unit
 constexpr int TRACE_POINTS = 9;
 constexpr int MAX_RUNS = 16;         // stages per phase (the planner splits larger phases)
 constexpr int DESC_BUFS = 4;         // phases whose run lists are resident in LDS at once
@@ -73,7 +85,12 @@ struct DevStage {
     int32_t parts;         // 2 for SwiGLU, else 1
     int32_t row_off;       // first row of this stage in the phase's row space
     int32_t am_slot;       // argmax slot (ARGMAX only)
+    int32_t c0;            // first K chunk streamed (K windows; 0 otherwise)
+    int32_t carry;         // CARRY_IN | CARRY_OUT (K windows; 0 otherwise)
 };
+// K-window carry: CARRY_OUT = this window ends in the LDS carry instead of an
+// epilogue; CARRY_IN = the row sums start from the carry.
+enum { CARRY_IN = 1, CARRY_OUT = 2 };
 
 struct DevPhase {
     int32_t stage0, nstages;
@@ -83,6 +100,11 @@ struct DevPhase {
     int32_t xb;            // LDS x-hat elements per batch row
     int32_t rb_off;        // offset of this phase's G+1 row bounds; -1 = even split
     int32_t jmax;          // partial slots per row-part
+    int32_t x_off;         // LDS byte offset of x-hat (row stride xb elements)
+    int32_t part_off;      // LDS byte offset of the partial slots
+    int32_t prm_off;       // LDS byte offset of the norm gains/shifts
+    int32_t epi_off;       // LDS byte offset of the staged bias/residual values
+    int32_t carry_off;     // LDS byte offset of the K-window carry (row-parts x batch FP32)
     int32_t pad;
 };
 
@@ -103,10 +125,7 @@ struct KArgs {
     int32_t persistent;
     int32_t G;
     int32_t n_argmax;
-    int32_t lds_x_bytes;   // offset of the partial area in dynamic LDS
-    int32_t lds_prm_off;   // offset of the norm gain/shift area
-    int32_t lds_epi_off;   // offset of the staged epilogue inputs (bias, residual)
-    int32_t lds_desc_off;  // offset of the per-phase run lists (DESC_BUFS buffers)
+    int32_t nb;            // batch rows
     DevPhase iph;
     DevStage ist;
     DevSource isrc;
@@ -130,6 +149,10 @@ WGN_HD int32_t even_row_begin(int32_t g, int32_t nrows, int32_t G) {
     return (int32_t)(((int64_t)g * nrows) / G);
 }
 WGN_HD int32_t nchunks_of(int32_t K) { return (K + UNIT - 1) / UNIT; }
+// Units of nrows rows (row-parts per row: parts) with nch chunks each.
+WGN_HD int32_t units_of(int32_t nrows, int32_t parts, int32_t nch, bool tile) {
+    return (tile ? (nrows + TILE_ROWS - 1) / TILE_ROWS : nrows) * parts * nch;
+}
 // Words per phase in the flag array (rows padded for 16-byte loads).
 WGN_HD int32_t flag_row(int32_t G) { return (G + 3) & ~3; }
 
@@ -148,8 +171,9 @@ WGN_HD uint32_t pack_meta(uint32_t xoff_bytes, bool seg_end, bool valid, uint32_
 struct Run {
     const uint16_t *W;
     const uint16_t *W_up;
-    int32_t K, nchunks, parts, row0;   // row0: stage-local first row
+    int32_t K, nchunks, parts, row0;   // row0: stage-local first row; K: row length
     int32_t nrows, u_base, rp_base;    // WG-local first unit / row-part (nrows may be 0)
+    int32_t c0, carry;                 // first K chunk of the window; CARRY_* bits
     uint32_t xoff;                     // LDS byte offset of the stage's source in a batch row
     int32_t stage;                     // global stage index
     // epilogue fields (read by the control wave)
@@ -162,9 +186,20 @@ struct Run {
     int64_t res_stride, y_stride;
 };
 struct RunHdr {
-    int32_t nruns, U, jmax, xb_bytes;
+    int32_t nruns, U, jmax, xb_bytes;  // xb_bytes: x-hat row stride
+    int32_t x_off, part_off;           // LDS byte offsets of x-hat and the partial slots
+    int32_t pad0, pad1;
 };
 constexpr int RUN_BUF_BYTES = (int)(sizeof(RunHdr) + MAX_RUNS * sizeof(Run));
+// Fixed part of the dynamic LDS: the run-list ring, then six streaming-wave
+// trace timestamps.  The per-phase areas (x-hat, partials, gains, epilogue
+// inputs, K-window carry) follow at offsets the plan gives each phase; areas
+// of different phases may overlap, since the control wave writes phase p+1's
+// areas only after it has finished reading phase p's, and the streaming waves
+// touch x-hat and partials only between a phase's two barriers.
+constexpr int LDS_DESC_OFF = 0;
+constexpr int LDS_TRACE_OFF = DESC_BUFS * RUN_BUF_BYTES;
+constexpr int LDS_DYN_OFF = (LDS_TRACE_OFF + 48 + 255) & ~255;
 
 // Per-(WG, stage) geometry inside a phase.
 struct StageSpan {
