@@ -88,6 +88,44 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Sum over aligned groups of lpr lanes (lpr = 4, 8, 16, 32 or 64, wave-uniform);
+// every lane of a group gets the same bits.  lpr = 64 is exactly wave_sum.
+__device__ __forceinline__ float group_sum(float v, int32_t lpr) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    if (lpr >= 8) v += dpp<0x141>(v);
+    if (lpr >= 16) v += dpp<0x140>(v);
+    if (lpr >= 32) v += __shfl_xor(v, 16);
+    if (lpr >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// The same over groups of lpr lanes for FP64 values (butterfly order).
+__device__ __forceinline__ double group_sum_f64(double v, int32_t lpr) {
+    for (int32_t o = 1; o < lpr; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Lane -> (batch row, slot) split used by the control wave: batch rows are
+// padded to a power of two P <= 16; lane l serves batch row l % P and the
+// (l / P)-th of every 64 / P consecutive items (norm chunks, output rows).
+struct LaneSplit {
+    int32_t P, shift;      // P = 1 << shift >= batch
+    int32_t b;             // batch row of this lane
+    int32_t i0, step;      // first item and item stride of this lane
+    bool active;           // b < batch
+};
+__device__ __forceinline__ LaneSplit lane_split(int32_t nb, uint32_t lane) {
+    LaneSplit L;
+    L.shift = nb <= 1 ? 0 : 32 - __builtin_clz((uint32_t)(nb - 1));
+    L.P = 1 << L.shift;
+    L.b = (int32_t)(lane & (uint32_t)(L.P - 1));
+    L.i0 = (int32_t)(lane >> L.shift);
+    L.step = 64 >> L.shift;
+    L.active = L.b < nb;
+    return L;
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     for (int o = 32; o >= 1; o >>= 1) {
         uint64_t t = __shfl_xor(v, o);
@@ -461,72 +499,84 @@ __device__ void issue_source_loads(const KArgs &a, const DevPhase &ph, char *xh,
     }
 }
 
-// Statistics and normalisation out of LDS, after the copies have landed.
+// Statistics and normalisation out of LDS, after the copies have landed.  All
+// batch rows are normalised at once: each row gets an aligned group of
+// 64 / P lanes (P = batch rounded up to a power of two) that walks the row's
+// 16-byte chunks and reduces with group_sum.
 template <int B, bool CHAIN>
 __device__ void finish_sources(const KArgs &a, const DevPhase &ph, char *xh, const char *prm, uint32_t lane) {
     const int32_t nb = a.nb;
+    const int32_t shift = nb <= 1 ? 0 : 32 - __builtin_clz((uint32_t)(nb - 1));
+    const int32_t lpr = 64 >> shift;                       // lanes per batch row
+    const int32_t row = (int32_t)(lane >> (6 - shift));   // batch row of this lane
+    const int32_t sub = (int32_t)(lane & (uint32_t)(lpr - 1));
+    const bool active = row < nb;
     int32_t poff = 0;
     for (int32_t si = 0; si < ph.nsrc; ++si) {
         const DevSource src = source_of<CHAIN>(a, ph.src0 + si);
         if (src.norm == NORM_NONE) continue;
         const int32_t K = src.K;
-        const int32_t n8 = K >> 3;
-        const float invK = 1.0f / (float)K;
+        const int32_t n8 = active ? K >> 3 : 0;
         const char *gp = prm + poff;
         const char *bp = prm + poff + prm_bytes(src) / 2;
         poff += prm_bytes(src);
-        for (int b = 0; b < B; ++b) {
-            if (b >= nb) break;
-            uint16_t *dst = (uint16_t *)(xh + ((size_t)b * ph.xb + src.lds_off) * 2);
-            float s1 = 0.0f, s2 = 0.0f;
-            for (int32_t i = lane; i < n8; i += 64) {
+        uint16_t *dst = (uint16_t *)(xh + ((size_t)(active ? row : 0) * ph.xb + src.lds_off) * 2);
+        // Statistics in FP64: a square of a BF16 value is exact in FP32 and
+        // the FP64 sums are as good as exact, so x-hat carries only the FP32
+        // rounding of its final products and matches a correctly rounded
+        // normalisation except in rare last-bit cases.
+        const bool layer = src.norm == NORM_LAYER;
+        double s1 = 0.0, s2 = 0.0;  // sum (LayerNorm) or sum of squares (RMSNorm)
+        for (int32_t i = sub; i < n8; i += lpr) {
+            const u32x4 v = *(const u32x4 *)(dst + i * 8);
+            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+            double c = 0.0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = bf2f(vv[e] & 0xFFFFu), hi = bf2f(vv[e] >> 16);
+                c += layer ? (double)lo + (double)hi : (double)(lo * lo) + (double)(hi * hi);
+            }
+            if (layer) s1 += c;
+            else s2 += c;
+        }
+        float mean = 0.0f, rstd;
+        if (src.norm == NORM_RMS) {
+            s2 = group_sum_f64(s2, lpr);
+            rstd = (float)(1.0 / sqrt(s2 / (double)K + (double)src.eps));
+        } else {
+            s1 = group_sum_f64(s1, lpr);
+            const double mean64 = s1 / (double)K;
+            double sv = 0.0;
+            for (int32_t i = sub; i < n8; i += lpr) {
                 const u32x4 v = *(const u32x4 *)(dst + i * 8);
                 const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float lo = bf2f(vv[e] & 0xFFFFu), hi = bf2f(vv[e] >> 16);
-                    s1 += lo + hi;
-                    s2 += lo * lo + hi * hi;
+                    const double lo = (double)bf2f(vv[e] & 0xFFFFu) - mean64, hi = (double)bf2f(vv[e] >> 16) - mean64;
+                    sv += lo * lo + hi * hi;
                 }
             }
-            float mean = 0.0f, rstd;
-            if (src.norm == NORM_RMS) {
-                s2 = wave_sum(s2);
-                rstd = 1.0f / sqrtf(s2 * invK + src.eps);
-            } else {
-                s1 = wave_sum(s1);
-                mean = s1 * invK;
-                float sv = 0.0f;
-                for (int32_t i = lane; i < n8; i += 64) {
-                    const u32x4 v = *(const u32x4 *)(dst + i * 8);
-                    const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+            sv = group_sum_f64(sv, lpr);
+            mean = (float)mean64;
+            rstd = (float)(1.0 / sqrt(sv / (double)K + (double)src.eps));
+        }
+        for (int32_t i = sub; i < n8; i += lpr) {
+            const u32x4 v = *(const u32x4 *)(dst + i * 8);
+            const u32x4 gv = src.gamma ? *(const u32x4 *)(gp + i * 16)
+                                       : (u32x4){0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+            const u32x4 bv = (src.norm == NORM_LAYER && src.beta) ? *(const u32x4 *)(bp + i * 16)
+                                                                  : (u32x4){0u, 0u, 0u, 0u};
+            const uint32_t vv[4] = {v.x, v.y, v.z, v.w}, gg[4] = {gv.x, gv.y, gv.z, gv.w},
+                           bb[4] = {bv.x, bv.y, bv.z, bv.w};
+            uint32_t o[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float lo = bf2f(vv[e] & 0xFFFFu) - mean, hi = bf2f(vv[e] >> 16) - mean;
-                        sv += lo * lo + hi * hi;
-                    }
-                }
-                sv = wave_sum(sv);
-                rstd = 1.0f / sqrtf(sv * invK + src.eps);
+            for (int e = 0; e < 4; ++e) {
+                const float lo =
+                    (bf2f(vv[e] & 0xFFFFu) - mean) * rstd * bf2f(gg[e] & 0xFFFFu) + bf2f(bb[e] & 0xFFFFu);
+                const float hi = (bf2f(vv[e] >> 16) - mean) * rstd * bf2f(gg[e] >> 16) + bf2f(bb[e] >> 16);
+                o[e] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
             }
-            for (int32_t i = lane; i < n8; i += 64) {
-                const u32x4 v = *(const u32x4 *)(dst + i * 8);
-                const u32x4 gv = src.gamma ? *(const u32x4 *)(gp + i * 16)
-                                           : (u32x4){0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-                const u32x4 bv = (src.norm == NORM_LAYER && src.beta) ? *(const u32x4 *)(bp + i * 16)
-                                                                      : (u32x4){0u, 0u, 0u, 0u};
-                const uint32_t vv[4] = {v.x, v.y, v.z, v.w}, gg[4] = {gv.x, gv.y, gv.z, gv.w},
-                               bb[4] = {bv.x, bv.y, bv.z, bv.w};
-                uint32_t o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float lo =
-                        (bf2f(vv[e] & 0xFFFFu) - mean) * rstd * bf2f(gg[e] & 0xFFFFu) + bf2f(bb[e] & 0xFFFFu);
-                    const float hi = (bf2f(vv[e] >> 16) - mean) * rstd * bf2f(gg[e] >> 16) + bf2f(bb[e] >> 16);
-                    o[e] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
-                }
-                *(u32x4 *)(dst + i * 8) = (u32x4){o[0], o[1], o[2], o[3]};
-            }
+            *(u32x4 *)(dst + i * 8) = (u32x4){o[0], o[1], o[2], o[3]};
         }
     }
 }
@@ -537,25 +587,22 @@ __device__ void finish_sources(const KArgs &a, const DevPhase &ph, char *xh, con
 template <int B, bool CHAIN>
 __device__ void stage_epilogue_inputs(const KArgs &a, const RunHdr &h, const Run *runs, float *epi, uint32_t lane) {
     const int32_t nb = a.nb;
+    const LaneSplit ls = lane_split(nb, lane);
     for (int32_t ri = 0; ri < h.nruns; ++ri) {
         const Run &r = runs[ri];
         const uint16_t *bias = r.bias;
         const uint16_t *res = r.residual;
-        if ((!bias && !res) || (r.carry & CARRY_OUT)) continue;
+        if ((!bias && !res) || (r.carry & CARRY_OUT) || !ls.active) continue;
         const int64_t res_stride = r.res_stride;
         const int32_t row0 = r.row0, nrows = r.nrows, rp_base = r.rp_base, parts = r.parts;
         const __amdgpu_buffer_rsrc_t rr = rsrc_of(res);
-        for (int32_t i = lane; i < nrows; i += 64) {
+        for (int32_t i = ls.i0; i < nrows; i += ls.step) {
             const int32_t n = row0 + i;
             float *e = epi + (size_t)(rp_base + i * parts) * (1 + nb);
-            e[0] = bias ? bf2f(bias[n]) : 0.0f;
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                if (b >= nb) break;
-                e[1 + b] = res ? bf2f(__builtin_amdgcn_raw_buffer_load_b16(
-                                     rr, (int)(((int64_t)b * res_stride + n) * 2), 0, COH))
-                               : 0.0f;
-            }
+            if (ls.b == 0) e[0] = bias ? bf2f(bias[n]) : 0.0f;
+            e[1 + ls.b] = res ? bf2f(__builtin_amdgcn_raw_buffer_load_b16(
+                                    rr, (int)(((int64_t)ls.b * res_stride + n) * 2), 0, COH))
+                              : 0.0f;
         }
     }
 }
@@ -583,26 +630,28 @@ __device__ void argmax_merge(const KArgs &a, int32_t am_slot, void *y, float *ma
 
 // Sum the partial slots of every row-part (in wave order, after the carry of
 // earlier K windows), then either carry the sums to the next K window or
-// apply the epilogue and store the outputs.
+// apply the epilogue and store the outputs.  Lane l serves batch row l % P of
+// every (64 / P)-th output row (P = batch rounded up to a power of two).
 template <int B, bool CHAIN, bool TILE>
 __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32_t g, const float *part,
                          const float *epi, float *carry, uint32_t lane) {
     const int32_t nb = a.nb;
+    const LaneSplit ls = lane_split(nb, lane);
+    const int32_t b = ls.b;
     for (int32_t ri = 0; ri < h.nruns; ++ri) {
         const Run &r = runs[ri];
-        const int32_t parts = r.parts, nch = r.nchunks, epi_kind = r.epi, row0 = r.row0, nrows = r.nrows;
+        const int32_t parts = r.parts, nch = r.nchunks, epi_kind = r.epi, row0 = r.row0;
+        const int32_t nrows = ls.active ? r.nrows : 0;
         const int32_t rp_base = r.rp_base, cy = r.carry;
         const bool has_res = r.residual != nullptr, has_bias = r.bias != nullptr;
         const int64_t y_stride = r.y_stride;
         const int32_t N = r.N;
         float *logits = r.logits;
         const __amdgpu_buffer_rsrc_t ry = rsrc_of(r.y);
-        uint64_t best[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) best[b] = 0;
-        for (int32_t i = lane; i < nrows; i += 64) {
+        uint64_t best = 0;
+        for (int32_t i = ls.i0; i < nrows; i += ls.step) {
             const int32_t n = row0 + i;
-            float acc0[B], acc1[B];
+            float acc[2];
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
                 if (pt >= parts) break;
@@ -610,48 +659,38 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
                 const int32_t a0 = first_unit_of_rowpart(r, i, pt, TILE);
                 const int32_t span =
                     first_wave(a0 + nch - 1, h.U, STREAM_WAVES) - first_wave(a0, h.U, STREAM_WAVES) + 1;
-                const float *pp = part + (size_t)rp * h.jmax * nb;
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    if (b >= nb) break;
-                    float s = (cy & CARRY_IN) ? carry[rp * nb + b] + pp[b] : pp[b];
-                    for (int32_t j = 1; j < span; ++j) s += pp[j * nb + b];
-                    if (cy & CARRY_OUT) carry[rp * nb + b] = s;
-                    if (pt == 0) acc0[b] = s;
-                    else acc1[b] = s;
-                }
+                const float *pp = part + (size_t)rp * h.jmax * nb + b;
+                float s = (cy & CARRY_IN) ? carry[rp * nb + b] + pp[0] : pp[0];
+                for (int32_t j = 1; j < span; ++j) s += pp[j * nb];
+                if (cy & CARRY_OUT) carry[rp * nb + b] = s;
+                acc[pt] = s;
             }
             if (cy & CARRY_OUT) continue;
             const float *ep = epi + (size_t)(rp_base + i * parts) * (1 + nb);
-            const float bias = has_bias ? ep[0] : 0.0f;
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                if (b >= nb) break;
-                const float z = acc0[b] + bias;
-                if (epi_kind == EPI_ARGMAX) {
-                    if (logits) logits[(size_t)b * N + n] = z;
-                    const uint64_t key = ((uint64_t)orderable(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
-                    best[b] = key > best[b] ? key : best[b];
-                    continue;
-                }
-                float e;
-                if (epi_kind == EPI_GELU_TANH) e = gelu_tanh(z);
-                else if (epi_kind == EPI_SWIGLU) e = silu(z) * acc1[b];
-                else e = z;
-                if (has_res) e += ep[1 + b];
-                __builtin_amdgcn_raw_buffer_store_b16(f2bf(e), ry, (int)(((int64_t)b * y_stride + n) * 2), 0, COH);
+            const float z = acc[0] + (has_bias ? ep[0] : 0.0f);
+            if (epi_kind == EPI_ARGMAX) {
+                if (logits) logits[(size_t)b * N + n] = z;
+                const uint64_t key = ((uint64_t)orderable(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
+                best = key > best ? key : best;
+                continue;
             }
+            float e;
+            if (epi_kind == EPI_GELU_TANH) e = gelu_tanh(z);
+            else if (epi_kind == EPI_SWIGLU) e = silu(z) * acc[1];
+            else e = z;
+            if (has_res) e += ep[1 + b];
+            __builtin_amdgcn_raw_buffer_store_b16(f2bf(e), ry, (int)(((int64_t)b * y_stride + n) * 2), 0, COH);
         }
         if (epi_kind == EPI_ARGMAX && !(cy & CARRY_OUT)) {
             const int32_t am_slot = r.am_slot;
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                if (b >= nb) break;
-                const uint64_t k = wave_max_u64(best[b]);
-                if (lane == 0)
-                    __hip_atomic_store(&a.am_part[((size_t)am_slot * a.G + g) * nb + b], k, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+            // maximum over the lanes serving the same batch row
+            for (int32_t o = ls.P; o < 64; o <<= 1) {
+                const uint64_t t = __shfl_xor(best, o);
+                best = t > best ? t : best;
             }
+            if ((int32_t)lane < nb)
+                __hip_atomic_store(&a.am_part[((size_t)am_slot * a.G + g) * nb + lane], best, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             // the partial keys are agent-scope atomic stores; once they have
             // completed, the ticket tells the last workgroup to merge them
             __builtin_amdgcn_s_waitcnt(0);
