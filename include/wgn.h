@@ -157,7 +157,20 @@ wgn_status wgn_rmsnorm_rows(const void *x, int64_t x_stride, const void *gamma, 
  * do not touch each other's outputs form one phase; phases are separated by
  * device-side completion counters inside one persistent kernel (mode 0) or by
  * kernel boundaries (mode 1).  Weights must not be written by any stage.
- * Every stage writes its own output buffer. */
+ * Every stage writes its own output buffer.
+ *
+ * Hoisting (default; opts.no_fuse = 1 turns it off): a stage whose input no
+ * stage of the chain writes and whose epilogue is a plain residual add, the
+ * residual being an earlier stage D's output, is split: its product runs in
+ * the phase before D's and leaves FP32 row sums in the workspace, and its
+ * residual add (one rounding of D's output + the sums + its bias) runs in D's
+ * epilogue.  Same function, one device-wide phase boundary less per such
+ * stage -- in a decoder block the attention output projection, whose residual
+ * is the previous block's output ("One Token, Kernel by Kernel", section
+ * "What one block launches": the residual add folded into a neighbouring
+ * kernel).  wgn_chain_stage_phases reports the phase that writes each output.
+ * A stage whose inputs do not fit in LDS (an un-normalised input of batch x K
+ * BF16 over about 150 KB) is streamed in K windows over consecutive phases. */
 typedef struct wgn_chain wgn_chain;
 
 typedef struct wgn_chain_opts {
@@ -166,7 +179,8 @@ typedef struct wgn_chain_opts {
     int32_t trace;       /* 1: record per-phase, per-workgroup timestamps (see below)  */
     int32_t path;        /* 0: auto (vector path for batch <= 4, matrix cores above);   */
                          /* 1: vector path (batch <= 4 only); 2: matrix-core path       */
-    int32_t reserved[4]; /* must be zero                                               */
+    int32_t no_fuse;     /* 1: keep every stage whole (no hoisting, see below)          */
+    int32_t reserved[3]; /* must be zero                                               */
 } wgn_chain_opts;
 
 /* Workspace bytes for a chain over these stages (mode/grid as in opts, NULL = defaults). */

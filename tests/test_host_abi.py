@@ -161,9 +161,53 @@ def test_partition_k_windows(B, grid):
     gu.y = s
     assert partition_selftest([gu, d], B, grid) == 0
     assert plan_phases([gu, d], B, grid) == (n + 1, [0, n])
-    # at batch 8 the whole input fits: no windows
+    # at batch 8 on the full grid the whole input fits: no windows
     d8 = fake_stage(ar, 1536, 8960, 8, L.NORM_NONE, x=s, residual=h)
-    assert plan_phases([d8], 8, grid) == (1, [0])
+    if grid == 256:
+        assert plan_phases([d8], 8, grid) == (1, [0])
+
+
+def test_hoisting_of_the_output_projection():
+    """O's product depends on nothing and its residual is the previous block's
+    output: it moves into the phase before that block's down projection, and
+    its residual add runs in the down projection's epilogue."""
+    ar = Arena()
+    st = fake_decoder(ar, 1, 3, V=1000)
+    assert plan_phases(st, 1, 64, fuse=False) == (10, [0, 0, 0, 0, 1, 2, 3, 3, 3, 3, 4, 5, 6, 6, 6, 6, 7, 8, 9])
+    n, where = plan_phases(st, 1, 64)
+    assert n == 8
+    assert where == [0, 0, 0, 0, 1, 2,   # block 0: O's residual is the chain input, nothing to hoist
+                     3, 3, 3, 2, 3, 4,   # block 1: O written in block 0's down phase
+                     5, 5, 5, 4, 5, 6,   # block 2
+                     7]
+    for B, path in ((1, 0), (4, 0), (8, 0), (16, 0), (1, 2)):
+        stb = fake_decoder(Arena(), B, 3, V=1000)
+        assert partition_selftest(stb, B, 64, path) == 0
+        assert partition_selftest(stb, B, 256, path) == 0
+
+
+def test_hoisting_respects_hazards():
+    ar = Arena()
+    # the residual's producer is in the first phase: no earlier phase for the product
+    h = ar.take(1536 * 2)
+    a = fake_stage(ar, 1536, 1536, 1, x=h)
+    o = fake_stage(ar, 1536, 1536, 1, residual=a.y)
+    assert plan_phases([a, o], 1, 64) == (2, [0, 1])
+    # an input that a stage of the chain writes is not hoisted
+    ar = Arena()
+    st = fake_decoder(ar, 1, 2)
+    st[9].x = st[4].y  # layer-1 O reads the layer-0 SwiGLU output
+    n, where = plan_phases(st, 1, 64)
+    assert where[9] > where[5]  # O of layer 1 stays after layer 0's down projection
+    assert partition_selftest(st, 1, 64) == 0
+    # a stage between the residual's producer and O that reads O's output blocks the rewrite
+    ar = Arena()
+    st = fake_decoder(ar, 1, 2)
+    spy = fake_stage(ar, 64, 1536, 1, x=st[9].y)  # reads h1 of layer 1 before O writes it
+    chain = st[:6] + [spy] + st[6:]
+    n2, where2 = plan_phases(chain, 1, 64)
+    assert where2[10] > where2[5]
+    assert partition_selftest(chain, 1, 64) == 0
 
 
 def test_normalised_input_too_large_is_refused():

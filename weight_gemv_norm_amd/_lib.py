@@ -38,7 +38,8 @@ class Stage(ctypes.Structure):
 
 class ChainOpts(ctypes.Structure):
     """Mirror of wgn_chain_opts."""
-    _fields_ = [("mode", I32), ("grid", I32), ("trace", I32), ("path", I32), ("reserved", I32 * 4)]
+    _fields_ = [("mode", I32), ("grid", I32), ("trace", I32), ("path", I32), ("no_fuse", I32),
+                ("reserved", I32 * 3)]
 
 
 class WgnError(RuntimeError):

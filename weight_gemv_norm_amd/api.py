@@ -118,12 +118,13 @@ def rmsnorm_rows(x: torch.Tensor, gamma: torch.Tensor, eps: float, y: torch.Tens
 PATH_AUTO, PATH_VECTOR, PATH_MATRIX = 0, 1, 2
 
 
-def _opts(mode: int, grid: int, trace: bool = False, path: int = PATH_AUTO) -> ChainOpts:
+def _opts(mode: int, grid: int, trace: bool = False, path: int = PATH_AUTO, fuse: bool = True) -> ChainOpts:
     o = ChainOpts()
     o.mode = mode
     o.grid = grid
     o.trace = 1 if trace else 0
     o.path = path
+    o.no_fuse = 0 if fuse else 1
     return o
 
 
@@ -139,11 +140,11 @@ class Chain:
 
     def __init__(self, stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 0,
                  ws: Optional[torch.Tensor] = None, stream=None, device="cuda", trace: bool = False,
-                 path: int = PATH_AUTO):
+                 path: int = PATH_AUTO, fuse: bool = True):
         self._arr = L.stage_array(stages)
         self.n_stages = len(stages)
         self.batch = batch
-        o = _opts(mode, grid, trace, path)
+        o = _opts(mode, grid, trace, path, fuse)
         need = L.lib().wgn_chain_workspace_bytes(self._arr, len(stages), batch, ctypes.byref(o))
         if need == 0:
             # planning failed: let create report the precise status
@@ -207,16 +208,17 @@ def layer_chain(stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 
     L.check(st, "wgn_layer_chain")
 
 
-def partition_selftest(stages: Sequence[Stage], batch: int, grid: int, path: int = PATH_AUTO) -> int:
+def partition_selftest(stages: Sequence[Stage], batch: int, grid: int, path: int = PATH_AUTO,
+                       fuse: bool = True) -> int:
     arr = L.stage_array(stages)
-    o = _opts(0, grid, path=path)
+    o = _opts(0, grid, path=path, fuse=fuse)
     return int(L.lib().wgn_partition_selftest(arr, len(stages), batch, ctypes.byref(o)))
 
 
-def plan_phases(stages: Sequence[Stage], batch: int, grid: int = 0, path: int = PATH_AUTO):
+def plan_phases(stages: Sequence[Stage], batch: int, grid: int = 0, path: int = PATH_AUTO, fuse: bool = True):
     """Host-only planning: (number of phases, phase of each stage's output)."""
     arr = L.stage_array(stages)
-    o = _opts(0, grid, path=path)
+    o = _opts(0, grid, path=path, fuse=fuse)
     out = (ctypes.c_int32 * len(stages))()
     n = int(L.lib().wgn_plan_phases(arr, len(stages), batch, ctypes.byref(o), out))
     if n < 0:

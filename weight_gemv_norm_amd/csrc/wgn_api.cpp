@@ -142,6 +142,14 @@ bool same_source(const DevSource &s, const wgn_stage &st) {
            (st.norm == NORM_NONE || s.eps == st.eps);
 }
 
+// A stage pointer into the workspace's FP32 row-sum area (what = 0: the
+// stage's own output y; 1: its fused residual add's addend post_F).
+struct FFix {
+    int32_t stage;
+    size_t off;
+    int32_t what;
+};
+
 // Host image of a device program.
 struct Program {
     int32_t B = 1, G = 1;
@@ -153,6 +161,8 @@ struct Program {
     std::vector<int32_t> phase_of_stage;
     std::vector<int32_t> group_end;      // per phase: one past the last phase of its launch group
     std::vector<int32_t> part_bytes;     // per phase: bytes of its partial-slot area
+    std::vector<FFix> f_fix;             // pointers into the FP32 row-sum area, set at creation
+    size_t f_bytes = 0;                  // bytes of that workspace area
     int32_t n_argmax = 0;
     size_t lds_end = LDS_DYN_OFF;        // dynamic LDS bytes of the largest phase
     size_t lds_total() const { return lds_end; }
@@ -305,7 +315,60 @@ int32_t xb_of(Program &P, DevPhase &ph) {
 // Phase selection of the matrix-core path.
 bool use_tile(int32_t B, int32_t path) { return path == 2 || (path == 0 && B > MAX_BATCH_VALU); }
 
-wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_t path, Program &P) {
+// A stage as the planner places it: a caller's stage, possibly rewritten.
+struct PStage {
+    wgn_stage s;
+    int32_t user = -1;          // caller index whose output this stage writes
+    bool product_only = false;  // writes FP32 row sums to the workspace (EPI_F32)
+    int32_t post = -1;          // caller index of a stage whose residual add runs in this epilogue
+    size_t f_off = 0;           // workspace offset of those FP32 sums
+};
+
+// Cross-stage rewrite ("hoisting"): a stage S whose input vector no stage of
+// the chain writes and whose epilogue is a plain residual add, with the
+// residual being the output of an earlier stage D, is split in two.  Its
+// product runs in the phase before D's (it depends on nothing) and leaves FP32
+// row sums in the workspace; its residual add runs in D's epilogue on D's
+// freshly rounded output.  The result is the same function (one rounding of
+// residual + sums), and the dependency D -> S -> (readers of S) loses a
+// device-wide phase boundary.  In a decoder block this is the attention
+// output projection, whose residual is the previous block's output.
+void find_hoists(const wgn_stage *st, int32_t n, int32_t B, std::vector<int32_t> &into, std::vector<int32_t> &post_of) {
+    into.assign(n, -1);
+    post_of.assign(n, -1);
+    std::vector<std::vector<Range>> R(n), Wr(n), C(n);
+    for (int32_t i = 0; i < n; ++i) stage_ranges(st[i], B, R[i], Wr[i], C[i]);
+    for (int32_t s = 0; s < n; ++s) {
+        const wgn_stage &S = st[s];
+        if (S.epi != EPI_NONE || !S.residual) continue;
+        const Range rx = rng(S.x, ((size_t)(B - 1) * S.x_stride + S.K) * 2);
+        const Range rres = rng(S.residual, ((size_t)(B - 1) * S.res_stride + S.N) * 2);
+        const Range ry = rng(S.y, ((size_t)(B - 1) * S.y_stride + S.N) * 2);
+        bool x_written = false;
+        for (int32_t t = 0; t < n && !x_written; ++t)
+            for (const Range &w : Wr[t]) x_written |= overlap(w, rx);
+        if (x_written) continue;
+        int32_t D = -1;
+        for (int32_t t = s - 1; t >= 0 && D < 0; --t)
+            for (const Range &w : Wr[t])
+                if (overlap(w, rres)) D = t;
+        if (D < 0) continue;
+        const wgn_stage &Ds = st[D];
+        if (Ds.epi == EPI_ARGMAX || Ds.y != S.residual || Ds.N != S.N || post_of[D] >= 0 || into[D] >= 0) continue;
+        if (B > 1 && Ds.y_stride != S.res_stride) continue;
+        bool ok = !overlap(ry, rng(Ds.x, ((size_t)(B - 1) * Ds.x_stride + Ds.K) * 2));
+        if (Ds.residual) ok &= !overlap(ry, rng(Ds.residual, ((size_t)(B - 1) * Ds.res_stride + Ds.N) * 2));
+        for (int32_t t = D + 1; t < s && ok; ++t) {
+            for (const Range &r : R[t]) ok &= !overlap(r, ry);
+            for (const Range &w : Wr[t]) ok &= !overlap(w, ry) && !overlap(w, rres);
+        }
+        if (!ok) continue;
+        into[s] = D;
+        post_of[D] = s;
+    }
+}
+
+wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_t path, bool fuse, Program &P) {
     if (!stages || n < 1 || G < 1) return WGN_E_ARG;
     for (int32_t i = 0; i < n; ++i) {
         wgn_status st = check_stage(stages[i], B);
@@ -324,16 +387,111 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
         stage_ranges(stages[i], B, r, w, c);
         if (any_overlap(c, allw)) return WGN_E_ARG;
     }
+    std::vector<int32_t> into, post_of;
+    if (fuse) find_hoists(stages, n, B, into, post_of);
+    else into.assign(n, -1), post_of.assign(n, -1);
+
+    // Group the stages (hoisted ones removed) into phase lists, then place the
+    // hoisted products; a product that finds no room, or whose phase then does
+    // not fit in LDS, undoes its hoist and the plan starts over.
+  replan:
+    std::vector<PStage> ps;
+    std::vector<std::vector<int32_t>> lists;
+    for (;;) {
+        ps.clear();
+        lists.clear();
+        std::vector<int32_t> phase_of_ps;
+        std::vector<Range> ph_reads, ph_writes;
+        std::vector<int32_t> pos(n, -1);
+        for (int32_t i = 0; i < n; ++i) {
+            if (into[i] >= 0) continue;
+            PStage p;
+            p.s = stages[i];
+            p.user = i;
+            p.post = post_of[i];
+            stage_ranges(stages[i], B, r, w, c);
+            if (p.post >= 0) {
+                const wgn_stage &S = stages[p.post];
+                w.push_back(rng(S.y, ((size_t)(B - 1) * S.y_stride + S.N) * 2));
+            }
+            bool conflict = lists.empty() || any_overlap(r, ph_writes) || any_overlap(w, ph_reads) ||
+                            any_overlap(w, ph_writes);
+            if (!conflict) {
+                std::vector<DevSource> srcs;
+                for (int32_t q : lists.back()) {
+                    bool have = false;
+                    for (const DevSource &d : srcs) have |= same_source(d, ps[q].s);
+                    if (!have) srcs.push_back(make_dev_source(ps[q].s));
+                }
+                bool have = false;
+                for (const DevSource &d : srcs) have |= same_source(d, stages[i]);
+                if ((!have && (int32_t)srcs.size() >= MAX_SRC) || (int32_t)lists.back().size() >= MAX_RUNS)
+                    conflict = true;
+            }
+            if (conflict) {
+                lists.emplace_back();
+                ph_reads.clear();
+                ph_writes.clear();
+            }
+            pos[i] = (int32_t)ps.size();
+            lists.back().push_back((int32_t)ps.size());
+            phase_of_ps.push_back((int32_t)lists.size() - 1);
+            ps.push_back(p);
+            ph_reads.insert(ph_reads.end(), r.begin(), r.end());
+            ph_writes.insert(ph_writes.end(), w.begin(), w.end());
+        }
+        bool undone = false;
+        for (int32_t s = 0; s < n; ++s) {
+            if (into[s] < 0) continue;
+            const int32_t D = into[s];
+            bool placed = false;
+            for (int32_t q = phase_of_ps[pos[D]] - 1; q >= 0 && !placed; --q) {
+                std::vector<DevSource> srcs;
+                for (int32_t k : lists[q]) {
+                    bool have = false;
+                    for (const DevSource &d : srcs) have |= same_source(d, ps[k].s);
+                    if (!have) srcs.push_back(make_dev_source(ps[k].s));
+                }
+                bool have = false;
+                for (const DevSource &d : srcs) have |= same_source(d, stages[s]);
+                if ((!have && (int32_t)srcs.size() >= MAX_SRC) || (int32_t)lists[q].size() >= MAX_RUNS) continue;
+                PStage p;
+                p.s = stages[s];
+                p.user = s;
+                p.s.epi = EPI_NONE;
+                p.s.residual = nullptr;
+                p.s.res_stride = 0;
+                p.s.bias = nullptr;
+                p.product_only = true;
+                lists[q].push_back((int32_t)ps.size());
+                ps.push_back(p);
+                placed = true;
+            }
+            if (!placed) {
+                into[s] = -1;
+                post_of[D] = -1;
+                undone = true;
+            }
+        }
+        if (!undone) break;
+    }
+    // workspace areas of the FP32 row sums
     P = Program();
     P.B = B;
     P.G = G;
     P.tile = tile;
     P.phase_of_stage.assign(n, -1);
-    std::vector<Range> ph_reads, ph_writes;
-    std::vector<int32_t> users;  // caller stage indices of the open phase
-    DevPhase cur;
-    std::memset(&cur, 0, sizeof cur);
-    bool open = false;
+    for (PStage &p : ps) {
+        if (!p.product_only) continue;
+        p.f_off = P.f_bytes;
+        P.f_bytes += al256((size_t)B * p.s.N * 4);
+    }
+    for (PStage &p : ps) {
+        if (p.post < 0) continue;
+        for (const PStage &q : ps)
+            if (q.product_only && q.user == p.post) p.f_off = q.f_off;
+    }
+
     wgn_status fail = WGN_OK;
     auto push_phase = [&](DevPhase &ph, const PhaseStats &S, bool carry) -> bool {
         size_t end = 0;
@@ -344,17 +502,48 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
         P.part_bytes.push_back(pb);
         return true;
     };
-    auto close_phase = [&]() {
-        if (!open || fail != WGN_OK) return;
-        open = false;
+    for (const std::vector<int32_t> &lst : lists) {
+        DevPhase cur;
+        std::memset(&cur, 0, sizeof cur);
+        cur.stage0 = (int32_t)P.stages.size();
+        cur.src0 = (int32_t)P.sources.size();
+        std::vector<int32_t> users;
+        for (int32_t k : lst) {
+            const PStage &p = ps[k];
+            int32_t src_idx = -1;
+            for (int32_t q = cur.src0; q < (int32_t)P.sources.size(); ++q)
+                if (same_source(P.sources[q], p.s)) src_idx = q - cur.src0;
+            if (src_idx < 0) {
+                P.sources.push_back(make_dev_source(p.s));
+                src_idx = (int32_t)P.sources.size() - 1 - cur.src0;
+            }
+            DevStage d = make_dev_stage(p.s);
+            d.src = src_idx;
+            if (p.s.epi == EPI_ARGMAX) d.am_slot = P.n_argmax++;
+            if (p.product_only) {
+                d.epi = EPI_F32;
+                d.y = nullptr;
+                d.y_stride = p.s.N;
+                P.f_fix.push_back({(int32_t)P.stages.size(), p.f_off, 0});
+            }
+            if (p.post >= 0) {
+                const wgn_stage &S = stages[p.post];
+                d.post_y = S.y;
+                d.post_stride = S.y_stride;
+                d.post_bias = (const uint16_t *)S.bias;
+                P.f_fix.push_back({(int32_t)P.stages.size(), p.f_off, 1});
+                users.push_back(p.post);
+            }
+            P.stages.push_back(d);
+            if (p.user >= 0 && !p.product_only) users.push_back(p.user);
+        }
         cur.nstages = (int32_t)P.stages.size() - cur.stage0;
         cur.nsrc = (int32_t)P.sources.size() - cur.src0;
-        int32_t nrows = 0, maxch = 1;
+        int32_t nrows = 0;
         for (int32_t i = 0; i < cur.nstages; ++i) {
             DevStage &d = P.stages[cur.stage0 + i];
             d.row_off = nrows;
             nrows += d.N;
-            maxch = std::max(maxch, d.nchunks);
         }
         cur.nrows = nrows;
         cur.xb = xb_of(P, cur);
@@ -366,22 +555,39 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
         if (push_phase(whole, phase_stats(P.stages, P.rowb, whole, G, tile), false)) {
             P.group_end.push_back(first + 1);
             for (int32_t u : users) P.phase_of_stage[u] = first;
-            return;
+            continue;
         }
+        // A hoisted product made this phase too large: undo that hoist.
+        bool undo = false;
+        for (int32_t k : lst)
+            if (ps[k].product_only) {
+                post_of[into[ps[k].user]] = -1;
+                into[ps[k].user] = -1;
+                undo = true;
+            }
+        if (undo) goto replan;
         // The inputs do not fit in LDS: stream the phase in K windows.  Only a
         // phase with one un-normalised input can be windowed (a norm needs the
         // whole vector for its statistics).
         const DevSource src0 = P.sources[cur.src0];
         if (cur.nsrc != 1 || src0.norm != NORM_NONE) {
             fail = WGN_E_UNSUPPORTED;
-            return;
+            break;
         }
         const std::vector<DevStage> orig(P.stages.begin() + cur.stage0, P.stages.end());
+        std::vector<FFix> fix_keep;
+        for (const FFix &f : P.f_fix)
+            if (f.stage < cur.stage0) fix_keep.push_back(f);
+        std::vector<FFix> fix_here;
+        for (const FFix &f : P.f_fix)
+            if (f.stage >= cur.stage0) fix_here.push_back(f);
         const int32_t nch = nchunks_of(src0.K);
-        for (int32_t nw = nch - 1; nw >= 1; --nw) {
+        bool done = false;
+        for (int32_t nw = nch - 1; nw >= 1 && !done; --nw) {
             const int32_t S = (nch + nw - 1) / nw;
             P.stages.resize(cur.stage0);
             P.sources.resize(cur.src0);
+            P.f_fix = fix_keep;
             std::vector<DevPhase> win;
             PhaseStats worst;
             for (int32_t s = 0; s < S; ++s) {
@@ -395,15 +601,20 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
                 sw.x = src0.x + (size_t)c0 * UNIT;
                 sw.K = std::min(nw * UNIT, src0.K - c0 * UNIT);
                 P.sources.push_back(sw);
-                for (const DevStage &o : orig) {
-                    DevStage d = o;
+                for (size_t oi = 0; oi < orig.size(); ++oi) {
+                    DevStage d = orig[oi];
                     d.c0 = c0;
                     d.nchunks = cn;
                     d.carry = (s > 0 ? CARRY_IN : 0) | (s < S - 1 ? CARRY_OUT : 0);
                     if (s < S - 1) {
-                        d.bias = nullptr;    // bias and residual enter in the last window only
+                        d.bias = nullptr;    // bias, residual and fused adds enter in the last window only
                         d.residual = nullptr;
                         d.am_slot = -1;
+                        d.post_y = nullptr;
+                    } else {
+                        for (const FFix &f : fix_here)
+                            if (f.stage == cur.stage0 + (int32_t)oi)
+                                P.f_fix.push_back({(int32_t)P.stages.size(), f.off, f.what});
                     }
                     P.stages.push_back(d);
                 }
@@ -435,54 +646,20 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
             const int32_t last = first + S - 1;
             for (int32_t s = 0; s < S; ++s) P.group_end.push_back(last + 1);
             for (int32_t u : users) P.phase_of_stage[u] = last;
-            return;
+            done = true;
         }
-        fail = WGN_E_UNSUPPORTED;
-    };
-    for (int32_t i = 0; i < n && fail == WGN_OK; ++i) {
-        const wgn_stage &s = stages[i];
-        stage_ranges(s, B, r, w, c);
-        bool conflict = open && (any_overlap(r, ph_writes) || any_overlap(w, ph_reads) || any_overlap(w, ph_writes));
-        // source capacity of the open phase
-        int32_t src_idx = -1;
-        if (open && !conflict) {
-            for (int32_t q = cur.src0; q < (int32_t)P.sources.size(); ++q)
-                if (same_source(P.sources[q], s)) src_idx = q - cur.src0;
-            if (src_idx < 0 && (int32_t)P.sources.size() - cur.src0 >= MAX_SRC) conflict = true;
-            if ((int32_t)P.stages.size() - cur.stage0 >= MAX_RUNS) conflict = true;
+        if (!done) {
+            fail = WGN_E_UNSUPPORTED;
+            break;
         }
-        if (conflict) close_phase();
-        if (fail != WGN_OK) break;
-        if (!open) {
-            std::memset(&cur, 0, sizeof cur);
-            cur.stage0 = (int32_t)P.stages.size();
-            cur.src0 = (int32_t)P.sources.size();
-            ph_reads.clear();
-            ph_writes.clear();
-            users.clear();
-            open = true;
-            src_idx = -1;
-        }
-        if (src_idx < 0) {
-            P.sources.push_back(make_dev_source(s));
-            src_idx = (int32_t)P.sources.size() - 1 - cur.src0;
-        }
-        DevStage d = make_dev_stage(s);
-        d.src = src_idx;
-        if (s.epi == EPI_ARGMAX) d.am_slot = P.n_argmax++;
-        P.stages.push_back(d);
-        users.push_back(i);
-        ph_reads.insert(ph_reads.end(), r.begin(), r.end());
-        ph_writes.insert(ph_writes.end(), w.begin(), w.end());
     }
-    close_phase();
     if (fail != WGN_OK) return fail;
     return WGN_OK;
 }
 
 struct WsLayout {
     // ctr..am_part is the synchronisation area (flags, run counter, tickets, error word)
-    size_t phases, stages, sources, rowb, ctr, run, tickets, err, am_part, trace, total;
+    size_t phases, stages, sources, rowb, ctr, run, tickets, err, am_part, fsum, trace, total;
 };
 
 WsLayout ws_layout(const Program &P, bool trace) {
@@ -506,6 +683,8 @@ WsLayout ws_layout(const Program &P, bool trace) {
     o += 256;
     L.am_part = o;
     o += al256((size_t)P.n_argmax * P.G * P.B * sizeof(uint64_t));
+    L.fsum = o;
+    o += P.f_bytes;
     L.trace = o;
     if (trace) o += al256(P.phases.size() * (size_t)P.G * TRACE_POINTS * sizeof(uint64_t));
     L.total = o;
@@ -593,6 +772,15 @@ struct wgn_chain {
 
 namespace {
 int32_t opts_path(const wgn_chain_opts *opts) { return opts ? opts->path : 0; }
+bool opts_fuse(const wgn_chain_opts *opts) { return !(opts && opts->no_fuse); }
+
+// Point the stages' FP32 row-sum pointers into the workspace area at base.
+void patch_fsum(Program &P, char *base) {
+    for (const FFix &f : P.f_fix) {
+        if (f.what == 0) P.stages[f.stage].y = base + f.off;
+        else P.stages[f.stage].post_F = (const float *)(base + f.off);
+    }
+}
 }  // namespace
 
 extern "C" {
@@ -701,7 +889,7 @@ wgn_status wgn_rmsnorm_rows(const void *x, int64_t x_stride, const void *gamma, 
 size_t wgn_chain_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch,
                                  const wgn_chain_opts *opts) {
     Program P;
-    if (plan(stages, n_stages, batch, resolve_grid(opts), opts_path(opts), P) != WGN_OK) return 0;
+    if (plan(stages, n_stages, batch, resolve_grid(opts), opts_path(opts), opts_fuse(opts), P) != WGN_OK) return 0;
     return ws_layout(P, opts && opts->trace).total;
 }
 
@@ -711,14 +899,14 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     *out = nullptr;
     if (opts) {
         if (opts->mode < 0 || opts->mode > 1 || opts->grid < 0 || opts->trace < 0 || opts->trace > 1 ||
-            opts->path < 0 || opts->path > 2)
+            opts->path < 0 || opts->path > 2 || opts->no_fuse < 0 || opts->no_fuse > 1)
             return WGN_E_ARG;
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 3; ++i)
             if (opts->reserved[i]) return WGN_E_ARG;
     }
     wgn_chain *c = new (std::nothrow) wgn_chain();
     if (!c) return WGN_E_ARG;
-    wgn_status st = plan(stages, n_stages, batch, resolve_grid(opts), opts_path(opts), c->P);
+    wgn_status st = plan(stages, n_stages, batch, resolve_grid(opts), opts_path(opts), opts_fuse(opts), c->P);
     if (st != WGN_OK) {
         delete c;
         return st;
@@ -737,6 +925,7 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     c->mode = opts ? opts->mode : 0;
     c->ws = workspace;
     c->lds = c->P.lds_total();
+    patch_fsum(c->P, (char *)workspace + c->L.fsum);
     // host image of the program, then one upload
     std::vector<char> img(c->L.ctr, 0);
     std::memcpy(img.data() + c->L.phases, c->P.phases.data(), c->P.phases.size() * sizeof(DevPhase));
@@ -848,7 +1037,7 @@ int32_t wgn_plan_phases(const wgn_stage *stages, int32_t n_stages, int32_t batch
                         int32_t *phase_of_stage) {
     Program P;
     const int32_t grid = opts && opts->grid > 0 ? opts->grid : 256;
-    wgn_status st = plan(stages, n_stages, batch, grid, opts_path(opts), P);
+    wgn_status st = plan(stages, n_stages, batch, grid, opts_path(opts), opts_fuse(opts), P);
     if (st != WGN_OK) return st;
     if (phase_of_stage)
         for (int32_t i = 0; i < n_stages; ++i) phase_of_stage[i] = P.phase_of_stage[i];
@@ -865,7 +1054,8 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
                                const wgn_chain_opts *opts) {
     Program P;
     const int32_t grid = opts && opts->grid > 0 ? opts->grid : 256;
-    wgn_status st = plan(stages, n_stages, batch, grid, opts_path(opts), P);
+    wgn_status st = plan(stages, n_stages, batch, grid, opts_path(opts), opts_fuse(opts), P);
+    if (st == WGN_OK) patch_fsum(P, (char *)((uintptr_t)1 << 44));  // a fake workspace address
     if (st != WGN_OK) return st;
     const bool tile = P.tile;
     const int32_t nb = P.B;
@@ -898,6 +1088,8 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
             make_runs<true>(a, p, g, tile, h, runs);
             const int32_t U = h.U;
             if (U != G.U) ++bad;
+            for (int32_t u = 0; u < U; ++u)
+                if (first_wave_hdr(h, u) != first_wave(u, U, STREAM_WAVES)) ++bad;
             std::vector<uint32_t> slot_writes;
             for (int32_t w = 0; w < STREAM_WAVES; ++w) {
                 const int32_t ub = U > 0 ? wave_begin(w, U, STREAM_WAVES) : 0;

@@ -207,8 +207,8 @@ __device__ __forceinline__ void stream_begin_phase(StreamState &S, int32_t p) {
     S.h = *(const RunHdr *)buf;
     S.runs = (const Run *)(buf + sizeof(RunHdr));
     S.p = p;
-    S.u_beg = S.h.U > 0 ? wave_begin(S.w, S.h.U, STREAM_WAVES) : 0;
-    S.u_end = S.h.U > 0 ? wave_begin(S.w + 1, S.h.U, STREAM_WAVES) : 0;
+    S.u_beg = ((const RunHdr *)buf)->wb[S.w];  // indexed in LDS, not in registers
+    S.u_end = ((const RunHdr *)buf)->wb[S.w + 1];
     S.u = S.u_beg;
 }
 
@@ -581,9 +581,11 @@ __device__ void finish_sources(const KArgs &a, const DevPhase &ph, char *xh, con
     }
 }
 
-// While the streaming waves stream, stage the epilogue's bias and residual
-// values of this workgroup's rows into LDS (row-part rp's entry holds the
-// bias and then the residual of each batch row, as FP32).
+// While the streaming waves stream, stage the epilogue's inputs of this
+// workgroup's rows into LDS.  Row-part rp's record (EPI_REC(nb) floats) holds
+// the bias, then the residual of each batch row, then the addend of a fused
+// residual add of another stage (its FP32 row sums plus its bias).
+#define EPI_REC(nb) (1 + 2 * (nb))
 template <int B, bool CHAIN>
 __device__ void stage_epilogue_inputs(const KArgs &a, const RunHdr &h, const Run *runs, float *epi, uint32_t lane) {
     const int32_t nb = a.nb;
@@ -592,17 +594,24 @@ __device__ void stage_epilogue_inputs(const KArgs &a, const RunHdr &h, const Run
         const Run &r = runs[ri];
         const uint16_t *bias = r.bias;
         const uint16_t *res = r.residual;
-        if ((!bias && !res) || (r.carry & CARRY_OUT) || !ls.active) continue;
+        const float *pf = r.post_F;
+        if ((!bias && !res && !pf) || (r.carry & CARRY_OUT) || !ls.active) continue;
         const int64_t res_stride = r.res_stride;
-        const int32_t row0 = r.row0, nrows = r.nrows, rp_base = r.rp_base, parts = r.parts;
+        const int32_t row0 = r.row0, nrows = r.nrows, rp_base = r.rp_base, parts = r.parts, N = r.N;
+        const uint16_t *pbias = r.post_bias;
         const __amdgpu_buffer_rsrc_t rr = rsrc_of(res);
+        const __amdgpu_buffer_rsrc_t rf = rsrc_of(pf);
         for (int32_t i = ls.i0; i < nrows; i += ls.step) {
             const int32_t n = row0 + i;
-            float *e = epi + (size_t)(rp_base + i * parts) * (1 + nb);
+            float *e = epi + (size_t)(rp_base + i * parts) * EPI_REC(nb);
             if (ls.b == 0) e[0] = bias ? bf2f(bias[n]) : 0.0f;
             e[1 + ls.b] = res ? bf2f(__builtin_amdgcn_raw_buffer_load_b16(
                                     rr, (int)(((int64_t)ls.b * res_stride + n) * 2), 0, COH))
                               : 0.0f;
+            if (pf)
+                e[1 + nb + ls.b] =
+                    __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rf, (int)(((int64_t)ls.b * N + n) * 4), 0, COH)) +
+                    (pbias ? bf2f(pbias[n]) : 0.0f);
         }
     }
 }
@@ -648,6 +657,9 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
         const int32_t N = r.N;
         float *logits = r.logits;
         const __amdgpu_buffer_rsrc_t ry = rsrc_of(r.y);
+        const bool has_post = r.post_y != nullptr;
+        const __amdgpu_buffer_rsrc_t rpy = rsrc_of(r.post_y);
+        const int64_t post_stride = r.post_stride;
         uint64_t best = 0;
         for (int32_t i = ls.i0; i < nrows; i += ls.step) {
             const int32_t n = row0 + i;
@@ -657,8 +669,7 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
                 if (pt >= parts) break;
                 const int32_t rp = rp_base + i * parts + pt;
                 const int32_t a0 = first_unit_of_rowpart(r, i, pt, TILE);
-                const int32_t span =
-                    first_wave(a0 + nch - 1, h.U, STREAM_WAVES) - first_wave(a0, h.U, STREAM_WAVES) + 1;
+                const int32_t span = first_wave_hdr(h, a0 + nch - 1) - first_wave_hdr(h, a0) + 1;
                 const float *pp = part + (size_t)rp * h.jmax * nb + b;
                 float s = (cy & CARRY_IN) ? carry[rp * nb + b] + pp[0] : pp[0];
                 for (int32_t j = 1; j < span; ++j) s += pp[j * nb];
@@ -666,7 +677,12 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
                 acc[pt] = s;
             }
             if (cy & CARRY_OUT) continue;
-            const float *ep = epi + (size_t)(rp_base + i * parts) * (1 + nb);
+            if (epi_kind == EPI_F32) {
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[0]), ry,
+                                                      (int)(((int64_t)b * y_stride + n) * 4), 0, COH);
+                continue;
+            }
+            const float *ep = epi + (size_t)(rp_base + i * parts) * EPI_REC(nb);
             const float z = acc[0] + (has_bias ? ep[0] : 0.0f);
             if (epi_kind == EPI_ARGMAX) {
                 if (logits) logits[(size_t)b * N + n] = z;
@@ -679,7 +695,11 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
             else if (epi_kind == EPI_SWIGLU) e = silu(z) * acc[1];
             else e = z;
             if (has_res) e += ep[1 + b];
-            __builtin_amdgcn_raw_buffer_store_b16(f2bf(e), ry, (int)(((int64_t)b * y_stride + n) * 2), 0, COH);
+            const uint16_t o = f2bf(e);
+            __builtin_amdgcn_raw_buffer_store_b16(o, ry, (int)(((int64_t)b * y_stride + n) * 2), 0, COH);
+            if (has_post)
+                __builtin_amdgcn_raw_buffer_store_b16(f2bf(bf2f(o) + ep[1 + nb + b]), rpy,
+                                                      (int)(((int64_t)b * post_stride + n) * 2), 0, COH);
         }
         if (epi_kind == EPI_ARGMAX && !(cy & CARRY_OUT)) {
             const int32_t am_slot = r.am_slot;

@@ -98,6 +98,7 @@ WGN_HD void make_runs(const KArgs &a, int32_t p, int32_t g, bool tile, RunHdr &h
     h.x_off = G.x_off;
     h.part_off = G.part_off;
     h.pad0 = h.pad1 = 0;
+    for (int32_t w = 0; w <= STREAM_WAVES; ++w) h.wb[w] = G.U > 0 ? wave_begin(w, G.U, STREAM_WAVES) : 0;
     int32_t n = 0, u_base = 0, rp_base = 0;
     for (int32_t i = 0; i < G.nstages && n < MAX_RUNS; ++i) {
         const DevStage st = stage_of<CHAIN>(a, G.stage0 + i);
@@ -126,6 +127,10 @@ WGN_HD void make_runs(const KArgs &a, int32_t p, int32_t g, bool tile, RunHdr &h
         r.maxval = st.maxval;
         r.res_stride = st.res_stride;
         r.y_stride = st.y_stride;
+        r.post_y = st.post_y;
+        r.post_F = st.post_F;
+        r.post_bias = st.post_bias;
+        r.post_stride = st.post_stride;
         runs[n++] = r;
         u_base += units_of(sp.nrows, st.parts, st.nchunks, tile);
         rp_base += sp.nrows * st.parts;
@@ -162,7 +167,7 @@ WGN_HD UnitDesc unit_desc_runs(const RunHdr &h, const Run *runs, int32_t v, int3
             d.nbytes = (uint32_t)r.K * 2u - off;
             const int32_t rp = r.rp_base + rk * r.parts + part;
             const int32_t ua = v - chunk;
-            const int32_t j = ua < u_beg ? w - first_wave(ua, h.U, STREAM_WAVES) : 0;
+            const int32_t j = ua < u_beg ? w - first_wave_hdr(h, ua) : 0;
             const uint32_t slot = (uint32_t)((rp * h.jmax + j) * B);
             const bool seg_end = (chunk == r.nchunks - 1) || (v == u_end - 1);
             d.meta = pack_meta(r.xoff + (uint32_t)chunk * (UNIT * 2u), seg_end, true, slot);
@@ -223,7 +228,7 @@ WGN_HD TileDesc unit_desc_tile(const RunHdr &h, const Run *runs, int32_t v, int3
             d.rstride = r.K * 2;
             const int32_t rp0 = r.rp_base + ti * TILE_ROWS * r.parts + part;
             const int32_t ua = v - chunk;
-            const int32_t j = ua < u_beg ? w - first_wave(ua, h.U, STREAM_WAVES) : 0;
+            const int32_t j = ua < u_beg ? w - first_wave_hdr(h, ua) : 0;
             d.slot0 = (rp0 * h.jmax + j) * nb;
             d.slot_stride = r.parts * h.jmax * nb;
             d.seg_end = (chunk == r.nchunks - 1) || (v == u_end - 1);

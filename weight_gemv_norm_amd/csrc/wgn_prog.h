@@ -54,7 +54,8 @@ constexpr int DESC_AHEAD = 3;        // the control wave builds phase p+DESC_AHE
 constexpr uint64_t WAIT_TICKS = 200000000ull;  // 2 s at the 100 MHz real-time clock
 
 enum { NORM_NONE = 0, NORM_RMS = 1, NORM_LAYER = 2 };
-enum { EPI_NONE = 0, EPI_GELU_TANH = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
+enum { EPI_NONE = 0, EPI_GELU_TANH = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3,
+       EPI_F32 = 4 };  // internal: store the FP32 row sums (a product whose epilogue runs elsewhere)
 
 // A normalised input vector ("source") of a phase, staged as BF16 in LDS.
 struct DevSource {
@@ -87,6 +88,13 @@ struct DevStage {
     int32_t am_slot;       // argmax slot (ARGMAX only)
     int32_t c0;            // first K chunk streamed (K windows; 0 otherwise)
     int32_t carry;         // CARRY_IN | CARRY_OUT (K windows; 0 otherwise)
+    // A fused residual add of another stage ("post"): after storing its own
+    // output o, this stage also stores post_y = R(o + post_F + post_bias),
+    // where post_F holds that stage's FP32 row sums from an earlier phase.
+    void *post_y;
+    const float *post_F;
+    const uint16_t *post_bias;
+    int64_t post_stride;
 };
 // K-window carry: CARRY_OUT = this window ends in the LDS carry instead of an
 // epilogue; CARRY_IN = the row sums start from the carry.
@@ -184,12 +192,24 @@ struct Run {
     float *logits;
     float *maxval;
     int64_t res_stride, y_stride;
+    void *post_y;
+    const float *post_F;
+    const uint16_t *post_bias;
+    int64_t post_stride;
 };
 struct RunHdr {
     int32_t nruns, U, jmax, xb_bytes;  // xb_bytes: x-hat row stride
     int32_t x_off, part_off;           // LDS byte offsets of x-hat and the partial slots
     int32_t pad0, pad1;
+    int32_t wb[STREAM_WAVES + 1];      // wave_begin(w) for w = 0..STREAM_WAVES
 };
+// first_wave() from a header's wave boundaries (compares only, no division).
+WGN_HD int32_t first_wave_hdr(const RunHdr &h, int32_t u) {
+    int32_t w = 0;
+#pragma unroll
+    for (int32_t i = 1; i < STREAM_WAVES; ++i) w += h.wb[i] <= u ? 1 : 0;
+    return w;
+}
 constexpr int RUN_BUF_BYTES = (int)(sizeof(RunHdr) + MAX_RUNS * sizeof(Run));
 // Fixed part of the dynamic LDS: the run-list ring, then six streaming-wave
 // trace timestamps.  The per-phase areas (x-hat, partials, gains, epilogue
