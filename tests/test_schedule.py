@@ -27,13 +27,16 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def header_constant(name):
     src = open(os.path.join(ROOT, "weight_gemv_norm_amd", "csrc", "wgn_prog.h")).read()
-    m = re.search(r"constexpr int %s = (\d+);" % name, src)
+    m = re.search(r"constexpr int %s = (\d+);" % name, src) or re.search(r"#define WGN_%s (\d+)" % name, src)
     assert m, name
     return int(m.group(1))
 
 
 DESC_BUFS = header_constant("DESC_BUFS")
 DESC_AHEAD = header_constant("DESC_AHEAD")
+# 1 if the streaming waves refill only after the control wave has issued the
+# epilogue's stores (a third barrier per phase)
+EPI_BARRIER = header_constant("EPI_BARRIER")
 
 
 class Wave:
@@ -63,6 +66,8 @@ def control_events(p0, p1, desc_ahead=DESC_AHEAD):
         c.barrier()                # partials complete
         c.ev("read_part", p)       # epilogue
         c.ev("read_runs", p)
+        if EPI_BARRIER:
+            c.barrier()            # epilogue stores issued: streaming waves may refill
     return c
 
 
@@ -116,6 +121,8 @@ def stream_events(p0, p1, nblocks):
         endA = A[2]
         if endA:
             s.barrier()            # partials of phase p
+            if EPI_BARRIER:
+                s.barrier()        # epilogue stores of phase p issued
         A = load_block()
         if endA:
             p += 1
@@ -125,6 +132,8 @@ def stream_events(p0, p1, nblocks):
         endB = Bb[2]
         if endB:
             s.barrier()
+            if EPI_BARRIER:
+                s.barrier()
         Bb = load_block()
         if endB:
             p += 1

@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 
@@ -16,7 +17,24 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          # packed FP32 ops stay off: plain float code only
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-function", "-I", INCLUDE]
+         "-Wall", "-Wno-unused-function", "-I", INCLUDE,
+         # per-kernel register/scratch report, checked below
+         "-Rpass-analysis=kernel-resource-usage"]
+
+
+def kernel_resources(report: str):
+    """{kernel: {"VGPRs": n, "ScratchSize": n, ...}} from the compiler's
+    resource-usage remarks."""
+    out, cur = {}, None
+    for line in report.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[bytes/lane\])?: (\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = int(m.group(2))
+    return out
 
 
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
@@ -30,6 +48,16 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libwgn.so")
+    # The streaming kernels must keep everything in registers and LDS: a
+    # spill to scratch memory puts global-memory latency on the hot path.
+    res = kernel_resources(r.stderr)
+    spills = {k: v.get("ScratchSize") for k, v in res.items() if v.get("ScratchSize", 0) > 0}
+    if not res or spills:
+        os.unlink(tmp)
+        raise RuntimeError("libwgn.so kernels use scratch memory: %r" % (spills or "no resource report"))
+    with open(out + ".resources.txt", "w") as f:
+        for k in sorted(res):
+            f.write("%s %s\n" % (k, " ".join("%s=%d" % kv for kv in sorted(res[k].items()))))
     os.replace(tmp, out)
     return out
 

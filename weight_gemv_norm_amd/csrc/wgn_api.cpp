@@ -277,11 +277,11 @@ bool layout_phase(const Program &P, DevPhase &ph, const PhaseStats &S, bool carr
         if (P.sources[ph.src0 + i].norm != NORM_NONE) prm += prm_bytes_of(P.sources[ph.src0 + i].K);
     for (int32_t i = 0; i < ph.nstages; ++i) {
         const DevStage &d = P.stages[ph.stage0 + i];
-        if ((d.bias || d.residual) && !(d.carry & CARRY_OUT)) epi_in = true;
+        if ((d.bias || d.residual || d.post_y) && !(d.carry & CARRY_OUT)) epi_in = true;
     }
     const size_t x = al256(nb * (size_t)ph.xb * 2);
     const size_t part = Program::al16((size_t)S.max_rp * S.jmax * nb * 4);
-    const size_t epi = epi_in ? Program::al16((size_t)S.max_rp * (1 + nb) * 4) : 0;
+    const size_t epi = epi_in ? Program::al16((size_t)S.max_rp * epi_rec((int32_t)nb) * 4) : 0;
     const size_t cy = carry ? Program::al16((size_t)S.max_rp * nb * 4) : 0;
     size_t o = LDS_DYN_OFF;
     ph.x_off = (int32_t)o;
@@ -1176,6 +1176,16 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
                 u_base += units_of(sp.nrows, sg.parts, sg.nchunks, tile);
             }
             if (u_base != U) ++bad;
+            // the staged epilogue inputs and the K-window carry of every owned
+            // row-part fit their areas
+            bool staged = false, carried = false;
+            for (int32_t si = 0; si < ph.nstages; ++si) {
+                const DevStage &sg = P.stages[ph.stage0 + si];
+                staged |= (sg.bias || sg.residual || sg.post_y) && !(sg.carry & CARRY_OUT);
+                carried |= sg.carry != 0;
+            }
+            if (staged && (size_t)rp_base * epi_rec(nb) * 4 > (size_t)(ph.carry_off - ph.epi_off)) ++bad;
+            if (carried && ph.carry_off + (size_t)rp_base * nb * 4 > P.lds_total()) ++bad;
             std::sort(slot_writes.begin(), slot_writes.end());
             std::sort(slot_reads.begin(), slot_reads.end());
             if (slot_writes != slot_reads) ++bad;

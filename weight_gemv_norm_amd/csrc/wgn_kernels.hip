@@ -100,9 +100,21 @@ __device__ __forceinline__ float group_sum(float v, int32_t lpr) {
     return v;
 }
 
-// The same over groups of lpr lanes for FP64 values (butterfly order).
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v) {
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// The same steps as group_sum for FP64 values.
 __device__ __forceinline__ double group_sum_f64(double v, int32_t lpr) {
-    for (int32_t o = 1; o < lpr; o <<= 1) v += __shfl_xor(v, o);
+    v += dpp64<0xB1>(v);
+    v += dpp64<0x4E>(v);
+    if (lpr >= 8) v += dpp64<0x141>(v);
+    if (lpr >= 16) v += dpp64<0x140>(v);
+    if (lpr >= 32) v += __shfl_xor(v, 16);
+    if (lpr >= 64) v += __shfl_xor(v, 32);
     return v;
 }
 
@@ -416,6 +428,7 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
         if (endA) {
             if (tw) tl[(p & 1) * 3 + 2] = wall_clock64();
             wg_barrier();  // partials of phase p are complete
+            if (EPI_BARRIER) wg_barrier();  // the control wave has issued phase p's stores
         }
         load_any<B, TILE>(a, S, dA, mA, lane);
         if (endA && ++p < a.p1) {
@@ -429,6 +442,7 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
         if (endB) {
             if (tw) tl[(p & 1) * 3 + 2] = wall_clock64();
             wg_barrier();
+            if (EPI_BARRIER) wg_barrier();
         }
         load_any<B, TILE>(a, S, dB, mB, lane);
         if (endB && ++p < a.p1) {
@@ -582,10 +596,9 @@ __device__ void finish_sources(const KArgs &a, const DevPhase &ph, char *xh, con
 }
 
 // While the streaming waves stream, stage the epilogue's inputs of this
-// workgroup's rows into LDS.  Row-part rp's record (EPI_REC(nb) floats) holds
+// workgroup's rows into LDS.  Row-part rp's record (epi_rec(nb) floats) holds
 // the bias, then the residual of each batch row, then the addend of a fused
 // residual add of another stage (its FP32 row sums plus its bias).
-#define EPI_REC(nb) (1 + 2 * (nb))
 template <int B, bool CHAIN>
 __device__ void stage_epilogue_inputs(const KArgs &a, const RunHdr &h, const Run *runs, float *epi, uint32_t lane) {
     const int32_t nb = a.nb;
@@ -603,7 +616,7 @@ __device__ void stage_epilogue_inputs(const KArgs &a, const RunHdr &h, const Run
         const __amdgpu_buffer_rsrc_t rf = rsrc_of(pf);
         for (int32_t i = ls.i0; i < nrows; i += ls.step) {
             const int32_t n = row0 + i;
-            float *e = epi + (size_t)(rp_base + i * parts) * EPI_REC(nb);
+            float *e = epi + (size_t)(rp_base + i * parts) * epi_rec(nb);
             if (ls.b == 0) e[0] = bias ? bf2f(bias[n]) : 0.0f;
             e[1 + ls.b] = res ? bf2f(__builtin_amdgcn_raw_buffer_load_b16(
                                     rr, (int)(((int64_t)ls.b * res_stride + n) * 2), 0, COH))
@@ -637,92 +650,112 @@ __device__ void argmax_merge(const KArgs &a, int32_t am_slot, void *y, float *ma
     }
 }
 
-// Sum the partial slots of every row-part (in wave order, after the carry of
-// earlier K windows), then either carry the sums to the next K window or
-// apply the epilogue and store the outputs.  Lane l serves batch row l % P of
-// every (64 / P)-th output row (P = batch rounded up to a power of two).
+// Row sums of one output row (both parts of a SwiGLU row): the partial slots
+// in wave order, after the carry of earlier K windows; kept in the carry when
+// this window does not end the row.
+template <bool TILE>
+__device__ __forceinline__ void row_sums(const RunHdr &h, const Run &r, int32_t i, int32_t b, int32_t nb,
+                                         const float *part, float *carry, float (&acc)[2]) {
+    const int32_t parts = r.parts, nch = r.nchunks, cy = r.carry;
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+        if (pt >= parts) break;
+        const int32_t rp = r.rp_base + i * parts + pt;
+        const int32_t a0 = first_unit_of_rowpart(r, i, pt, TILE);
+        const int32_t span = first_wave_hdr(h, a0 + nch - 1) - first_wave_hdr(h, a0) + 1;
+        const float *pp = part + (size_t)rp * h.jmax * nb + b;
+        float s = (cy & CARRY_IN) ? carry[rp * nb + b] + pp[0] : pp[0];
+        for (int32_t j = 1; j < span; ++j) s += pp[j * nb];
+        if (cy & CARRY_OUT) carry[rp * nb + b] = s;
+        acc[pt] = s;
+    }
+}
+
+// Sum the partial slots of every output row, then either carry the sums to
+// the next K window or apply the epilogue and store the outputs.  Lane l
+// serves batch row l % P of every (64 / P)-th output row of the phase (all of
+// its stages at once; P = batch rounded up to a power of two).  Argmax stages
+// are reduced afterwards, one at a time.
 template <int B, bool CHAIN, bool TILE>
 __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32_t g, const float *part,
                          const float *epi, float *carry, uint32_t lane) {
     const int32_t nb = a.nb;
     const LaneSplit ls = lane_split(nb, lane);
     const int32_t b = ls.b;
+    // row starts are read from the LDS header: indexing the register copy with
+    // a per-lane index would move it to scratch memory
+    const int32_t *rstart = ((const RunHdr *)((const char *)runs - sizeof(RunHdr)))->rstart;
+    const int32_t total = ls.active ? rstart[MAX_RUNS] : 0;
+    for (int32_t k = ls.i0; k < total; k += ls.step) {
+        int32_t ri = 0;
+#pragma unroll
+        for (int32_t j = 1; j < MAX_RUNS; ++j) ri += rstart[j] <= k ? 1 : 0;
+        const Run &r = runs[ri];
+        const int32_t epi_kind = r.epi;
+        if (epi_kind == EPI_ARGMAX) continue;
+        const int32_t i = k - rstart[ri];
+        const int32_t n = r.row0 + i;
+        float acc[2];
+        row_sums<TILE>(h, r, i, b, nb, part, carry, acc);
+        if (r.carry & CARRY_OUT) continue;
+        if (epi_kind == EPI_F32) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[0]), rsrc_of(r.y),
+                                                  (int)(((int64_t)b * r.y_stride + n) * 4), 0, COH);
+            continue;
+        }
+        const float *ep = epi + (size_t)(r.rp_base + i * r.parts) * epi_rec(nb);
+        const float z = acc[0] + (r.bias ? ep[0] : 0.0f);
+        float e;
+        if (epi_kind == EPI_GELU_TANH) e = gelu_tanh(z);
+        else if (epi_kind == EPI_SWIGLU) e = silu(z) * acc[1];
+        else e = z;
+        if (r.residual) e += ep[1 + b];
+        const uint16_t o = f2bf(e);
+        __builtin_amdgcn_raw_buffer_store_b16(o, rsrc_of(r.y), (int)(((int64_t)b * r.y_stride + n) * 2), 0, COH);
+        if (r.post_y)
+            __builtin_amdgcn_raw_buffer_store_b16(f2bf(bf2f(o) + ep[1 + nb + b]), rsrc_of(r.post_y),
+                                                  (int)(((int64_t)b * r.post_stride + n) * 2), 0, COH);
+    }
     for (int32_t ri = 0; ri < h.nruns; ++ri) {
         const Run &r = runs[ri];
-        const int32_t parts = r.parts, nch = r.nchunks, epi_kind = r.epi, row0 = r.row0;
+        if (r.epi != EPI_ARGMAX) continue;
         const int32_t nrows = ls.active ? r.nrows : 0;
-        const int32_t rp_base = r.rp_base, cy = r.carry;
-        const bool has_res = r.residual != nullptr, has_bias = r.bias != nullptr;
-        const int64_t y_stride = r.y_stride;
-        const int32_t N = r.N;
+        const int32_t N = r.N, row0 = r.row0;
         float *logits = r.logits;
-        const __amdgpu_buffer_rsrc_t ry = rsrc_of(r.y);
-        const bool has_post = r.post_y != nullptr;
-        const __amdgpu_buffer_rsrc_t rpy = rsrc_of(r.post_y);
-        const int64_t post_stride = r.post_stride;
         uint64_t best = 0;
         for (int32_t i = ls.i0; i < nrows; i += ls.step) {
             const int32_t n = row0 + i;
             float acc[2];
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt) {
-                if (pt >= parts) break;
-                const int32_t rp = rp_base + i * parts + pt;
-                const int32_t a0 = first_unit_of_rowpart(r, i, pt, TILE);
-                const int32_t span = first_wave_hdr(h, a0 + nch - 1) - first_wave_hdr(h, a0) + 1;
-                const float *pp = part + (size_t)rp * h.jmax * nb + b;
-                float s = (cy & CARRY_IN) ? carry[rp * nb + b] + pp[0] : pp[0];
-                for (int32_t j = 1; j < span; ++j) s += pp[j * nb];
-                if (cy & CARRY_OUT) carry[rp * nb + b] = s;
-                acc[pt] = s;
-            }
-            if (cy & CARRY_OUT) continue;
-            if (epi_kind == EPI_F32) {
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[0]), ry,
-                                                      (int)(((int64_t)b * y_stride + n) * 4), 0, COH);
-                continue;
-            }
-            const float *ep = epi + (size_t)(rp_base + i * parts) * EPI_REC(nb);
-            const float z = acc[0] + (has_bias ? ep[0] : 0.0f);
-            if (epi_kind == EPI_ARGMAX) {
-                if (logits) logits[(size_t)b * N + n] = z;
-                const uint64_t key = ((uint64_t)orderable(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
-                best = key > best ? key : best;
-                continue;
-            }
-            float e;
-            if (epi_kind == EPI_GELU_TANH) e = gelu_tanh(z);
-            else if (epi_kind == EPI_SWIGLU) e = silu(z) * acc[1];
-            else e = z;
-            if (has_res) e += ep[1 + b];
-            const uint16_t o = f2bf(e);
-            __builtin_amdgcn_raw_buffer_store_b16(o, ry, (int)(((int64_t)b * y_stride + n) * 2), 0, COH);
-            if (has_post)
-                __builtin_amdgcn_raw_buffer_store_b16(f2bf(bf2f(o) + ep[1 + nb + b]), rpy,
-                                                      (int)(((int64_t)b * post_stride + n) * 2), 0, COH);
+            row_sums<TILE>(h, r, i, b, nb, part, carry, acc);
+            if (r.carry & CARRY_OUT) continue;
+            const float z = acc[0];
+            if (logits)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z), rsrc_of(logits),
+                                                      (int)(((int64_t)b * N + n) * 4), 0, 0);
+            const uint64_t key = ((uint64_t)orderable(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
+            best = key > best ? key : best;
         }
-        if (epi_kind == EPI_ARGMAX && !(cy & CARRY_OUT)) {
-            const int32_t am_slot = r.am_slot;
-            // maximum over the lanes serving the same batch row
-            for (int32_t o = ls.P; o < 64; o <<= 1) {
-                const uint64_t t = __shfl_xor(best, o);
-                best = t > best ? t : best;
-            }
-            if ((int32_t)lane < nb)
-                __hip_atomic_store(&a.am_part[((size_t)am_slot * a.G + g) * nb + lane], best, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            // the partial keys are agent-scope atomic stores; once they have
-            // completed, the ticket tells the last workgroup to merge them
-            __builtin_amdgcn_s_waitcnt(0);
-            uint32_t old = 0;
+        if (r.carry & CARRY_OUT) continue;
+        const int32_t am_slot = r.am_slot;
+        // maximum over the lanes serving the same batch row
+        for (int32_t o = ls.P; o < 64; o <<= 1) {
+            const uint64_t t = __shfl_xor(best, o);
+            best = t > best ? t : best;
+        }
+        if ((int32_t)lane < nb)
+            __hip_atomic_store(&a.am_part[((size_t)am_slot * a.G + g) * nb + lane], best, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        // the partial keys are agent-scope atomic stores; once they have
+        // completed, the ticket tells the last workgroup to merge them
+        __builtin_amdgcn_s_waitcnt(0);
+        uint32_t old = 0;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(&a.tickets[am_slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __shfl(old, 0);
+        if (old == (uint32_t)(a.G - 1)) {
+            argmax_merge(a, am_slot, r.y, r.maxval, lane);
             if (lane == 0)
-                old = __hip_atomic_fetch_add(&a.tickets[am_slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            old = __shfl(old, 0);
-            if (old == (uint32_t)(a.G - 1)) {
-                argmax_merge(a, am_slot, r.y, r.maxval, lane);
-                if (lane == 0)
-                    __hip_atomic_store(&a.tickets[am_slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+                __hip_atomic_store(&a.tickets[am_slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -731,10 +764,10 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
 template <bool CHAIN, bool TILE>
 __device__ void build_runs(const KArgs &a, int32_t q, int32_t g, char *desc) {
     // every lane computes the same list; the runs go straight into LDS
+    // the header is built in place too: its tables are indexed at run time,
+    // which a register copy could only do through scratch memory
     char *buf = desc + (q % DESC_BUFS) * RUN_BUF_BYTES;
-    RunHdr h;
-    make_runs<CHAIN>(a, q, g, TILE, h, (Run *)(buf + sizeof(RunHdr)));
-    *(RunHdr *)buf = h;
+    make_runs<CHAIN>(a, q, g, TILE, *(RunHdr *)buf, (Run *)(buf + sizeof(RunHdr)));
 }
 
 template <int B, bool CHAIN, bool TILE>
@@ -766,7 +799,7 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
         // phase: prepare them before waiting for it
         if (p + DESC_AHEAD < a.p1) build_runs<CHAIN, TILE>(a, p + DESC_AHEAD, g, desc);
         const char *rb = desc + (p % DESC_BUFS) * RUN_BUF_BYTES;
-        const RunHdr h = *(const RunHdr *)rb;
+        const RunHdr &h = *(const RunHdr *)rb;  // in LDS (a register copy passed by reference would go to scratch)
         const Run *runs = (const Run *)(rb + sizeof(RunHdr));
         prefetch_params<CHAIN>(a, ph, prm, lane);
         if (a.persistent && p > a.p0 && ph.wait) {
@@ -812,6 +845,7 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
         }
         epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane);
         trace_point(a, p, g, 4, lane);
+        if (EPI_BARRIER == 1) wg_barrier();  // stores issued: the streaming waves may refill
         if (a.persistent) {
             // outputs are written through (coherent stores); once they have
             // completed, publish this workgroup's flag for phase p
@@ -819,6 +853,7 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
             if (lane == 0)
                 __builtin_amdgcn_raw_buffer_store_b32(flag_val, rsrc_of(a.flags + (size_t)p * flag_row(a.G)), g * 4, 0, COH);
         }
+        if (EPI_BARRIER == 2) wg_barrier();  // flag issued too
         trace_point(a, p, g, 5, lane);
     }
     if (a.persistent) {

@@ -99,7 +99,8 @@ WGN_HD void make_runs(const KArgs &a, int32_t p, int32_t g, bool tile, RunHdr &h
     h.part_off = G.part_off;
     h.pad0 = h.pad1 = 0;
     for (int32_t w = 0; w <= STREAM_WAVES; ++w) h.wb[w] = G.U > 0 ? wave_begin(w, G.U, STREAM_WAVES) : 0;
-    int32_t n = 0, u_base = 0, rp_base = 0;
+    int32_t n = 0, u_base = 0, rp_base = 0, rows = 0;
+    h.rstart[0] = 0;
     for (int32_t i = 0; i < G.nstages && n < MAX_RUNS; ++i) {
         const DevStage st = stage_of<CHAIN>(a, G.stage0 + i);
         const StageSpan sp = stage_span(st, G.r0, G.r1, 0, 0);
@@ -134,7 +135,10 @@ WGN_HD void make_runs(const KArgs &a, int32_t p, int32_t g, bool tile, RunHdr &h
         runs[n++] = r;
         u_base += units_of(sp.nrows, st.parts, st.nchunks, tile);
         rp_base += sp.nrows * st.parts;
+        rows += sp.nrows;
+        h.rstart[n] = rows;
     }
+    for (int32_t i = n + 1; i <= MAX_RUNS; ++i) h.rstart[i] = rows;
     h.nruns = n;
 }
 

@@ -51,6 +51,13 @@ constexpr int TRACE_POINTS = 9;
 constexpr int MAX_RUNS = 16;         // stages per phase (the planner splits larger phases)
 constexpr int DESC_BUFS = 4;         // phases whose run lists are resident in LDS at once
 constexpr int DESC_AHEAD = 3;        // the control wave builds phase p+DESC_AHEAD's list in iteration p
+#ifndef WGN_EPI_BARRIER
+#define WGN_EPI_BARRIER 1
+#endif
+// 1: the streaming waves issue the loads that follow a phase's last block only
+// after the control wave has issued the phase's output stores (which would
+// otherwise queue behind them in the compute unit's memory pipeline)
+constexpr int EPI_BARRIER = WGN_EPI_BARRIER;
 constexpr uint64_t WAIT_TICKS = 200000000ull;  // 2 s at the 100 MHz real-time clock
 
 enum { NORM_NONE = 0, NORM_RMS = 1, NORM_LAYER = 2 };
@@ -202,7 +209,12 @@ struct RunHdr {
     int32_t x_off, part_off;           // LDS byte offsets of x-hat and the partial slots
     int32_t pad0, pad1;
     int32_t wb[STREAM_WAVES + 1];      // wave_begin(w) for w = 0..STREAM_WAVES
+    int32_t rstart[MAX_RUNS + 1];      // first WG-local output row of each run (cumulative nrows)
 };
+// Floats per row-part in the staged epilogue inputs: bias, then the residual
+// of each batch row, then the addend of a fused residual add per batch row.
+WGN_HD int32_t epi_rec(int32_t nb) { return 1 + 2 * nb; }
+
 // first_wave() from a header's wave boundaries (compares only, no division).
 WGN_HD int32_t first_wave_hdr(const RunHdr &h, int32_t u) {
     int32_t w = 0;
