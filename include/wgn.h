@@ -175,7 +175,8 @@ typedef struct wgn_chain wgn_chain;
 
 typedef struct wgn_chain_opts {
     int32_t mode;        /* 0: one persistent launch (default); 1: one launch per phase */
-    int32_t grid;        /* workgroups; 0 = one per compute unit                       */
+    int32_t grid;        /* workgroups; 0 = one per compute unit; mode 0: at most the   */
+                         /* compute units (all resident at once), and at most 2048     */
     int32_t trace;       /* 1: record per-phase, per-workgroup timestamps (see below)  */
     int32_t path;        /* 0: auto (vector path for batch <= 4, matrix cores above);   */
                          /* 1: vector path (batch <= 4 only); 2: matrix-core path       */

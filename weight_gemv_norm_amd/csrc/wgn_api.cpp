@@ -898,7 +898,8 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     if (!out) return WGN_E_ARG;
     *out = nullptr;
     if (opts) {
-        if (opts->mode < 0 || opts->mode > 1 || opts->grid < 0 || opts->trace < 0 || opts->trace > 1 ||
+        if (opts->mode < 0 || opts->mode > 1 || opts->grid < 0 || opts->grid > MAX_GRID || opts->trace < 0 ||
+            opts->trace > 1 ||
             opts->path < 0 || opts->path > 2 || opts->no_fuse < 0 || opts->no_fuse > 1)
             return WGN_E_ARG;
         for (int i = 0; i < 3; ++i)
@@ -915,6 +916,12 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     if (!d.ok) {
         delete c;
         return WGN_E_DEVICE;
+    }
+    // the persistent kernel needs every workgroup resident at once (one per
+    // compute unit: each takes the whole LDS)
+    if ((!opts || opts->mode == 0) && c->P.G > d.cus) {
+        delete c;
+        return WGN_E_ARG;
     }
     c->trace = opts && opts->trace;
     c->L = ws_layout(c->P, c->trace);

@@ -37,7 +37,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef WGN_WEIGHT_AUX
 #define WGN_WEIGHT_AUX 2  // nt: weights are streamed once
 #endif
-constexpr int DEPTH = WGN_DEPTH;          // units per block (loads in flight per block)
+constexpr int DEPTH = WGN_DEPTH;          // vector path: units per block (loads in flight per block)
+constexpr int TILE_LOADS = UNIT / 32;     // matrix-core path: loads per unit (= per block)
 constexpr int WEIGHT_AUX = WGN_WEIGHT_AUX;  // cache policy of the weight loads (streamed once)
 // Cache policy of every access to data that another workgroup produces or
 // consumes inside the same launch (stage outputs, completion flags, argmax
@@ -305,7 +306,7 @@ __device__ __forceinline__ void consume_block(const u32x4 (&d)[DEPTH], const Blo
 // operand of v_mfma_f32_16x16x32_bf16.  Lanes past the end of their row read
 // an out-of-range offset (value 0, no traffic); rows past the tile's last
 // valid row fall outside the buffer's range the same way.
-__device__ __forceinline__ void load_tile(const KArgs &a, StreamState &S, u32x4 (&d)[DEPTH], BlockMeta &bm,
+__device__ __forceinline__ void load_tile(const KArgs &a, StreamState &S, u32x4 (&d)[TILE_LOADS], BlockMeta &bm,
                                           uint32_t lane) {
     TileDesc td;
     td.valid = false;
@@ -321,7 +322,7 @@ __device__ __forceinline__ void load_tile(const KArgs &a, StreamState &S, u32x4 
     const uint32_t lane_off = (lane & 15u) * (uint32_t)(valid ? td.rstride : 0) + q * 16u;
     const int32_t kv = (valid ? td.kval : 0) - 8 * (int32_t)q;  // K elements from this lane's first position
 #pragma unroll
-    for (int t = 0; t < DEPTH; ++t) {
+    for (int t = 0; t < TILE_LOADS; ++t) {
         const uint32_t off = 32 * t < kv ? lane_off + 64u * (uint32_t)t : 0x80000000u;
         d[t] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, WEIGHT_AUX);
     }
@@ -336,13 +337,13 @@ __device__ __forceinline__ void load_tile(const KArgs &a, StreamState &S, u32x4 
     stream_advance(S, bm, 1);
 }
 
-__device__ __forceinline__ void consume_tile(const u32x4 (&d)[DEPTH], const BlockMeta &bm, f32x4 &acc,
+__device__ __forceinline__ void consume_tile(const u32x4 (&d)[TILE_LOADS], const BlockMeta &bm, f32x4 &acc,
                                              const char *lds, uint32_t lane, int32_t nb) {
     const uint32_t q = lane >> 4, j = lane & 15u;
     const uint32_t jr = (int32_t)j < nb ? j : (uint32_t)(nb - 1);  // batch rows past nb: results unused
     const char *xp = lds + bm.x_off + jr * (uint32_t)bm.xb_bytes + bm.xoff + q * 16u;
 #pragma unroll
-    for (int t = 0; t < DEPTH; ++t) {
+    for (int t = 0; t < TILE_LOADS; ++t) {
         const u32x4 xv = *(const u32x4 *)(xp + 64 * t);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, d[t]), __builtin_bit_cast(bf16x8, xv),
                                                       acc, 0, 0, 0);
@@ -376,14 +377,17 @@ struct Acc<B, true> {
     __device__ __forceinline__ void zero() { v = (f32x4){0.0f, 0.0f, 0.0f, 0.0f}; }
 };
 
+template <bool TILE>
+constexpr int block_loads() { return TILE ? TILE_LOADS : DEPTH; }
+
 template <int B, bool TILE>
-__device__ __forceinline__ void load_any(const KArgs &a, StreamState &S, u32x4 (&d)[DEPTH], BlockMeta &bm,
-                                         uint32_t lane) {
+__device__ __forceinline__ void load_any(const KArgs &a, StreamState &S, u32x4 (&d)[block_loads<TILE>()],
+                                         BlockMeta &bm, uint32_t lane) {
     if constexpr (TILE) load_tile(a, S, d, bm, lane);
     else load_block<B>(a, S, d, bm, lane);
 }
 template <int B, bool TILE>
-__device__ __forceinline__ void consume_any(const KArgs &a, const u32x4 (&d)[DEPTH], const BlockMeta &bm,
+__device__ __forceinline__ void consume_any(const KArgs &a, const u32x4 (&d)[block_loads<TILE>()], const BlockMeta &bm,
                                             Acc<B, TILE> &acc, const char *lds, uint32_t lane) {
     if constexpr (TILE) consume_tile(d, bm, acc.v, lds, lane, a.nb);
     else consume_block<B>(d, bm, acc.v, lds, lane);
@@ -391,7 +395,6 @@ __device__ __forceinline__ void consume_any(const KArgs &a, const u32x4 (&d)[DEP
 
 template <int B, bool CHAIN, bool TILE>
 __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
-    static_assert(!TILE || DEPTH * 32 == UNIT, "a matrix-core unit is DEPTH loads of 32 K elements");
     const uint32_t lane = lane_id();
     StreamState S;
     S.desc = lds + LDS_DESC_OFF;
@@ -401,7 +404,7 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
     S.done_all = false;
     wg_barrier();  // run lists of the first phases are in LDS
     stream_begin_phase(S, a.p0);
-    u32x4 dA[DEPTH], dB[DEPTH];
+    u32x4 dA[block_loads<TILE>()], dB[block_loads<TILE>()];
     BlockMeta mA, mB;
     Acc<B, TILE> acc;
     acc.zero();

@@ -168,8 +168,13 @@ WGN_HD int32_t nchunks_of(int32_t K) { return (K + UNIT - 1) / UNIT; }
 WGN_HD int32_t units_of(int32_t nrows, int32_t parts, int32_t nch, bool tile) {
     return (tile ? (nrows + TILE_ROWS - 1) / TILE_ROWS : nrows) * parts * nch;
 }
-// Words per phase in the flag array (rows padded for 16-byte loads).
+// Words per phase in the flag array (rows padded for 16-byte loads).  The
+// row is dense: one poll of all flags is one 16-byte load per lane.  (One
+// flag per 64-byte line avoids line sharing between writers but makes every
+// poll touch G lines, which costs more while the weight stream fills the
+// memory pipeline.)
 WGN_HD int32_t flag_row(int32_t G) { return (G + 3) & ~3; }
+constexpr int MAX_GRID = 2048;
 
 // Meta word of one streamed unit (wave-uniform):
 //   bits  0..13  x-hat byte offset / 16
