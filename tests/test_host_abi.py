@@ -210,6 +210,22 @@ def test_hoisting_respects_hazards():
     assert partition_selftest(chain, 1, 64) == 0
 
 
+def test_phase_split_at_stage_capacity():
+    """Twelve independent stages on one input exceed a phase's run-list
+    capacity (8 stages): the planner splits them over two phases."""
+    ar = Arena()
+    x = ar.take(1536 * 2)
+    st = [fake_stage(ar, 64 + i, 1536, 1, L.NORM_RMS, x=x) for i in range(12)]
+    for s in st[1:]:
+        s.gamma = st[0].gamma  # one normalised source for all
+    n, where = plan_phases(st, 1, 64)
+    assert n == 2 and where == [0] * 8 + [1] * 4
+    assert partition_selftest(st, 1, 64) == 0
+    # with a gain each, they are four distinct normalised inputs per phase at most
+    st2 = [fake_stage(ar, 64 + i, 1536, 1, L.NORM_RMS, x=x) for i in range(9)]
+    assert plan_phases(st2, 1, 64) == (3, [0] * 4 + [1] * 4 + [2])
+
+
 def test_normalised_input_too_large_is_refused():
     """A norm needs the whole input in LDS for its statistics, so a normalised
     input that does not fit cannot be windowed."""

@@ -51,8 +51,11 @@ class Wave:
         self.events.append((self.epoch, kind, phase))
 
 
-def control_events(p0, p1, desc_ahead=DESC_AHEAD):
-    """The control wave's loop: builds, x-hat writes, partial reads."""
+def control_events(p0, p1, desc_ahead=DESC_AHEAD, norm=None):
+    """The control wave's loop: builds, x-hat writes, partial reads.  norm[p]:
+    phase p has a normalised input, normalised by all waves between two extra
+    barriers (inputs landed; partial statistics written)."""
+    norm = norm or {}
     c = Wave()
     for q in range(p0, min(p1, p0 + desc_ahead)):
         c.ev("build", q)
@@ -61,7 +64,15 @@ def control_events(p0, p1, desc_ahead=DESC_AHEAD):
         if p + desc_ahead < p1:
             c.ev("build", p + desc_ahead)
         c.ev("read_runs", p)       # header and run list of phase p (epilogue inputs)
-        c.ev("write_xhat", p)
+        c.ev("write_xhat", p)      # raw inputs (and, without a norm, x-hat itself)
+        if norm.get(p):
+            c.ev("write_job", p)
+            c.barrier()            # inputs landed, norm job posted
+            c.ev("read_job", p)
+            c.ev("write_stats", p)
+            c.barrier()            # partial statistics written
+            c.ev("read_stats", p)
+            c.ev("write_xhat", p)  # normalised slice
         c.barrier()                # x-hat ready
         c.barrier()                # partials complete
         c.ev("read_part", p)       # epilogue
@@ -71,11 +82,24 @@ def control_events(p0, p1, desc_ahead=DESC_AHEAD):
     return c
 
 
-def stream_events(p0, p1, nblocks):
+def stream_events(p0, p1, nblocks, norm=None):
     """One streaming wave's loop with two blocks in flight.  nblocks[p] >= 1 is
     the number of blocks the wave walks in phase p (an empty share is one empty
     block)."""
+    norm = norm or {}
     s = Wave()
+
+    def norm_steps(p):
+        # before the x-hat barrier of phase p: the phase's header says whether
+        # the waves normalise together
+        s.ev("read_runs", p)
+        if norm.get(p):
+            s.barrier()
+            s.ev("read_job", p)
+            s.ev("write_stats", p)
+            s.barrier()
+            s.ev("read_stats", p)
+            s.ev("write_xhat", p)
 
     class St:
         pass
@@ -113,6 +137,7 @@ def stream_events(p0, p1, nblocks):
     begin_phase(p0)
     A = load_block()
     Bb = load_block()
+    norm_steps(p0)
     s.barrier()                    # x-hat of the first phase
     p = p0
     ok = True
@@ -127,6 +152,7 @@ def stream_events(p0, p1, nblocks):
         if endA:
             p += 1
             if p < p1:
+                norm_steps(p)
                 s.barrier()        # x-hat of phase p
         consume(Bb)
         endB = Bb[2]
@@ -138,19 +164,49 @@ def stream_events(p0, p1, nblocks):
         if endB:
             p += 1
             if p < p1:
+                norm_steps(p)
                 s.barrier()
     return s
 
 
-def check_schedule(p0, p1, nblocks, desc_bufs=DESC_BUFS, desc_ahead=DESC_AHEAD):
-    c = control_events(p0, p1, desc_ahead)
-    waves = [stream_events(p0, p1, nb) for nb in nblocks]
+def check_schedule(p0, p1, nblocks, desc_bufs=DESC_BUFS, desc_ahead=DESC_AHEAD, norm=None):
+    c = control_events(p0, p1, desc_ahead, norm)
+    waves = [stream_events(p0, p1, nb, norm) for nb in nblocks]
     errors = []
     for s in waves:
         if s.epoch != c.epoch:
             errors.append("barrier count %d != %d" % (s.epoch, c.epoch))
     build_epoch = {q: e for e, k, q in c.events if k == "build"}
-    xhat_epoch = {q: e for e, k, q in c.events if k == "write_xhat"}
+    xhat_epoch = {}
+    for e, k, q in c.events + [ev for w in waves for ev in w.events]:
+        if k == "write_xhat":
+            xhat_epoch[q] = max(xhat_epoch.get(q, -1), e)
+    xhat_first = {}
+    for e, k, q in c.events:
+        if k == "write_xhat":
+            xhat_first.setdefault(q, e)
+    job_w = {q: e for e, k, q in c.events if k == "write_job"}
+    stats_w = {}
+    for e, k, q in c.events + [ev for w in waves for ev in w.events]:
+        if k == "write_stats":
+            stats_w.setdefault(q, set()).add(e)
+    for w in [c] + waves:
+        for e, k, q in w.events:
+            if k == "read_job" and not (e > job_w[q] and (q + 1 not in job_w or e < job_w[q + 1])):
+                errors.append("norm job of %d read outside its lifetime" % q)
+            if k == "read_stats" and not all(e > ws for ws in stats_w[q]):
+                errors.append("statistics of %d read before all waves wrote them" % q)
+    # statistics of phase q are overwritten only after every read of phase q-1's
+    reads_stats = {}
+    for w in [c] + waves:
+        for e, k, q in w.events:
+            if k == "read_stats":
+                reads_stats.setdefault(q, []).append(e)
+    prev = None
+    for q in sorted(stats_w):
+        if prev is not None and not all(min(stats_w[q]) > r for r in reads_stats[prev]):
+            errors.append("statistics of %d overwritten while phase %d reads them" % (prev, q))
+        prev = q
     part_read = {q: e for e, k, q in c.events if k == "read_part"}
     for q in range(p0, p1):
         if q not in build_epoch:
@@ -177,7 +233,7 @@ def check_schedule(p0, p1, nblocks, desc_bufs=DESC_BUFS, desc_ahead=DESC_AHEAD):
             if k == "read_xhat":
                 if not e > xhat_epoch[q]:
                     errors.append("x-hat %d read before it is written" % q)
-                if q + 1 in xhat_epoch and not e < xhat_epoch[q + 1]:
+                if q + 1 in xhat_first and not e < xhat_first[q + 1]:
                     errors.append("x-hat %d read after phase %d overwrote it" % (q, q + 1))
             if k == "write_part":
                 if not e < part_read[q]:
@@ -203,6 +259,17 @@ def test_schedule_exhaustive_small():
         for nb in itertools.product([1, 2, 3], repeat=P):
             errs = check_schedule(0, P, [list(nb), [1] * P])
             assert not errs, (nb, errs[:3])
+
+
+def test_schedule_with_all_wave_norm():
+    rng = random.Random(99)
+    for _ in range(2000):
+        P = rng.randint(1, 10)
+        W = rng.randint(1, 7)
+        nb = [[rng.choice([1, 1, 2, 3]) for _ in range(P)] for _ in range(W)]
+        norm = {p: rng.random() < 0.6 for p in range(P)}
+        errs = check_schedule(0, P, nb, norm=norm)
+        assert not errs, (P, nb, norm, errs[:3])
 
 
 def test_schedule_launch_window():

@@ -188,6 +188,113 @@ __device__ __forceinline__ void trace_point(const KArgs &a, int32_t p, int32_t g
     if (a.trace && lane == 0) a.trace[((size_t)p * a.G + g) * TRACE_POINTS + i] = wall_clock64();
 }
 
+// ------------------------------------------------------ normalisation (all waves)
+// The inputs of a phase are normalised by all WAVES waves of the workgroup
+// together: batch rows (padded to a power of two P) are spread over the
+// waves -- a row over one or more whole waves when P <= WAVES, several rows
+// in one wave otherwise -- and every lane walks a strided share of its row's
+// 16-byte chunks.  Sum and sum of squares are accumulated in FP64 (a square
+// of a BF16 value is exact in FP32), reduced inside the wave, posted per wave
+// in LDS and combined in wave order after a barrier, so the statistics are
+// as good as exact and their order is fixed.
+__device__ __forceinline__ double2 *norm_stats(char *lds, int32_t j, int32_t w, int32_t slot) {
+    return (double2 *)(lds + LDS_STATS_OFF) + ((j * WAVES + w) * STATS_ROWS + slot);
+}
+
+// Step 1 (after the inputs have landed in LDS): partial statistics.
+__device__ void norm_all_stats(char *lds, int32_t w, uint32_t lane, int32_t nw) {
+    const NormHdr &J = *(const NormHdr *)(lds + LDS_NORM_OFF);
+    const NormSplit S = norm_split(J.nb, w, lane, nw);
+    for (int32_t j = 0; j < J.njobs; ++j) {
+        const NormJob &jb = J.job[j];
+        const bool layer = jb.norm == NORM_LAYER;
+        const int32_t n8 = S.active ? jb.K >> 3 : 0;
+        const uint16_t *src = (const uint16_t *)(lds + J.x_off + ((size_t)(S.active ? S.row : 0) * J.xb + jb.xoff) * 2);
+        double s1 = 0.0, s2 = 0.0;
+        for (int32_t i = S.sub; i < n8; i += S.lanes) {
+            const u32x4 v = *(const u32x4 *)(src + i * 8);
+            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+            double c1 = 0.0, c2 = 0.0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = bf2f(vv[e] & 0xFFFFu), hi = bf2f(vv[e] >> 16);
+                c2 += (double)(lo * lo) + (double)(hi * hi);
+                if (layer) c1 += (double)lo + (double)hi;
+            }
+            s1 += c1;
+            s2 += c2;
+        }
+        s1 = group_sum_f64(s1, S.lpr);
+        s2 = group_sum_f64(s2, S.lpr);
+        if (S.active && (S.sub % S.lpr) == 0) {
+            double2 st;
+            st.x = s1;
+            st.y = s2;
+            *norm_stats(lds, j, w, S.slot) = st;
+        }
+    }
+}
+
+// Step 2 (after every wave has posted its statistics): normalise this lane's
+// share and round to BF16 in place.
+__device__ void norm_all_apply(char *lds, int32_t w, uint32_t lane, int32_t nw) {
+    const NormHdr &J = *(const NormHdr *)(lds + LDS_NORM_OFF);
+    const NormSplit S = norm_split(J.nb, w, lane, nw);
+    if (!S.active) return;
+    for (int32_t j = 0; j < J.njobs; ++j) {
+        const NormJob &jb = J.job[j];
+        const int32_t K = jb.K, n8 = K >> 3;
+        double s1 = 0.0, s2 = 0.0;
+        for (int32_t ww = S.w0; ww < S.w1; ++ww) {
+            const double2 st = *norm_stats(lds, j, ww, S.rslot);
+            s1 += st.x;
+            s2 += st.y;
+        }
+        float mean = 0.0f, rstd;
+        if (jb.norm == NORM_RMS) {
+            rstd = (float)(1.0 / sqrt(s2 / (double)K + (double)jb.eps));
+        } else {
+            const double m = s1 / (double)K;
+            const double var = s2 / (double)K - m * m;  // biased; FP64 sums, see above
+            mean = (float)m;
+            rstd = (float)(1.0 / sqrt((var > 0.0 ? var : 0.0) + (double)jb.eps));
+        }
+        uint16_t *dst = (uint16_t *)(lds + J.x_off + ((size_t)S.row * J.xb + jb.xoff) * 2);
+        const char *gp = lds + jb.prm;
+        const char *bp = lds + jb.prm + jb.prm_half;
+        for (int32_t i = S.sub; i < n8; i += S.lanes) {
+            const u32x4 v = *(const u32x4 *)(dst + i * 8);
+            const u32x4 gv = jb.has_gamma ? *(const u32x4 *)(gp + i * 16)
+                                          : (u32x4){0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+            const u32x4 bv = jb.has_beta ? *(const u32x4 *)(bp + i * 16) : (u32x4){0u, 0u, 0u, 0u};
+            const uint32_t vv[4] = {v.x, v.y, v.z, v.w}, gg[4] = {gv.x, gv.y, gv.z, gv.w},
+                           bb[4] = {bv.x, bv.y, bv.z, bv.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo =
+                    (bf2f(vv[e] & 0xFFFFu) - mean) * rstd * bf2f(gg[e] & 0xFFFFu) + bf2f(bb[e] & 0xFFFFu);
+                const float hi = (bf2f(vv[e] >> 16) - mean) * rstd * bf2f(gg[e] >> 16) + bf2f(bb[e] >> 16);
+                o[e] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+            }
+            *(u32x4 *)(dst + i * 8) = (u32x4){o[0], o[1], o[2], o[3]};
+        }
+    }
+}
+
+// Both steps with their barriers; every wave calls this for a phase whose
+// run header says it has a normalised input, right before the x-hat barrier.
+// Used from batch 2 up: at batch 1 the control wave alone is quicker (the
+// streaming waves would first wait for their in-flight weight loads, which
+// the compiler cannot keep apart from the registers the norm needs).
+__device__ __forceinline__ void norm_all(char *lds, int32_t w, uint32_t lane) {
+    wg_barrier();  // inputs in LDS, jobs posted
+    norm_all_stats(lds, w, lane, WAVES);
+    wg_barrier();  // statistics of every wave posted
+    norm_all_apply(lds, w, lane, WAVES);
+}
+
+
 // ------------------------------------------------------------ streaming waves
 struct BlockMeta {
     uint32_t meta_v;       // vector path: lane j holds the meta word of the block's unit j
@@ -393,6 +500,9 @@ __device__ __forceinline__ void consume_any(const KArgs &a, const u32x4 (&d)[blo
     else consume_block<B>(d, bm, acc.v, lds, lane);
 }
 
+template <int B, bool TILE>
+constexpr bool all_wave_norm() { return TILE || B > 1; }
+
 template <int B, bool CHAIN, bool TILE>
 __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
     const uint32_t lane = lane_id();
@@ -421,6 +531,7 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
     const bool tw = a.trace && w == 0 && lane == 0;
     load_any<B, TILE>(a, S, dA, mA, lane);
     load_any<B, TILE>(a, S, dB, mB, lane);
+    if (all_wave_norm<B, TILE>() && ((const RunHdr *)run_buf(S.desc, a.p0))->has_norm) norm_all(lds, w, lane);
     wg_barrier();  // x-hat of the first phase is ready
     bool ok = abort_flag_get() == 0;
     int32_t p = a.p0;
@@ -436,6 +547,7 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
         load_any<B, TILE>(a, S, dA, mA, lane);
         if (endA && ++p < a.p1) {
             if (tw) tl[(p & 1) * 3 + 1] = wall_clock64();
+            if (all_wave_norm<B, TILE>() && ((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
             wg_barrier();  // x-hat of phase p is ready
             ok = abort_flag_get() == 0;
             if (tw) tl[(p & 1) * 3 + 0] = wall_clock64();
@@ -450,6 +562,7 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
         load_any<B, TILE>(a, S, dB, mB, lane);
         if (endB && ++p < a.p1) {
             if (tw) tl[(p & 1) * 3 + 1] = wall_clock64();
+            if (all_wave_norm<B, TILE>() && ((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
             wg_barrier();
             ok = abort_flag_get() == 0;
             if (tw) tl[(p & 1) * 3 + 0] = wall_clock64();
@@ -516,10 +629,12 @@ __device__ void issue_source_loads(const KArgs &a, const DevPhase &ph, char *xh,
     }
 }
 
-// Statistics and normalisation out of LDS, after the copies have landed.  All
-// batch rows are normalised at once: each row gets an aligned group of
-// 64 / P lanes (P = batch rounded up to a power of two) that walks the row's
-// 16-byte chunks and reduces with group_sum.
+// Vector path: the control wave normalises alone, out of LDS, after the
+// copies have landed.  All batch rows at once: each row gets an aligned group
+// of 64 / P lanes (P = batch rounded up to a power of two) that walks the
+// row's 16-byte chunks and reduces with group_sum_f64.  (The streaming waves
+// do not help here: they hold their in-flight weight blocks in nearly all of
+// their registers, and the compiler would make them wait for those loads.)
 template <int B, bool CHAIN>
 __device__ void finish_sources(const KArgs &a, const DevPhase &ph, char *xh, const char *prm, uint32_t lane) {
     const int32_t nb = a.nb;
@@ -596,6 +711,32 @@ __device__ void finish_sources(const KArgs &a, const DevPhase &ph, char *xh, con
             *(u32x4 *)(dst + i * 8) = (u32x4){o[0], o[1], o[2], o[3]};
         }
     }
+}
+
+// Post the phase's normalisation jobs for norm_all (one per normalised source).
+template <bool CHAIN>
+__device__ void post_norm_jobs(const KArgs &a, const DevPhase &ph, char *lds, uint32_t lane) {
+    NormHdr *J = (NormHdr *)(lds + LDS_NORM_OFF);
+    if (lane != 0) return;
+    int32_t n = 0, poff = 0;
+    for (int32_t si = 0; si < ph.nsrc; ++si) {
+        const DevSource src = source_of<CHAIN>(a, ph.src0 + si);
+        if (src.norm == NORM_NONE) continue;
+        NormJob &jb = J->job[n++];
+        jb.norm = src.norm;
+        jb.K = src.K;
+        jb.xoff = src.lds_off;
+        jb.prm = ph.prm_off + poff;
+        jb.prm_half = prm_bytes(src) / 2;
+        jb.eps = src.eps;
+        jb.has_gamma = src.gamma != nullptr;
+        jb.has_beta = src.norm == NORM_LAYER && src.beta != nullptr;
+        poff += prm_bytes(src);
+    }
+    J->njobs = n;
+    J->nb = a.nb;
+    J->x_off = ph.x_off;
+    J->xb = ph.xb;
 }
 
 // While the streaming waves stream, stage the epilogue's inputs of this
@@ -810,18 +951,38 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
             const __amdgpu_buffer_rsrc_t rf = rsrc_of(a.flags + (size_t)(p - 1) * flag_row(a.G));
             const uint64_t t0 = wall_clock64();
             bool timed_out = false;
-            for (;;) {
-                bool ok = true;
-                for (int32_t i = (int32_t)lane * 4; i < a.G; i += 256) {
-                    const u32x4 f = __builtin_amdgcn_raw_buffer_load_b128(rf, i * 4, 0, COH);
-                    const uint32_t ff[4] = {f.x, f.y, f.z, f.w};
+            if (FLAG_WORDS == 1) {
+                for (;;) {
+                    bool ok = true;
+                    for (int32_t i = (int32_t)lane * 4; i < a.G; i += 256) {
+                        const u32x4 f = __builtin_amdgcn_raw_buffer_load_b128(rf, i * 4, 0, COH);
+                        const uint32_t ff[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) ok &= (i + e >= a.G) || ff[e] == flag_val;
+                        for (int e = 0; e < 4; ++e) ok &= (i + e >= a.G) || ff[e] == flag_val;
+                    }
+                    if (__all(ok)) break;
+                    if (wall_clock64() - t0 > WAIT_TICKS) {
+                        timed_out = true;
+                        break;
+                    }
                 }
-                if (__all(ok)) break;
-                if (wall_clock64() - t0 > WAIT_TICKS) {
-                    timed_out = true;
-                    break;
+            } else {
+                // lane l watches flags l, l + 64, ... and re-reads only those
+                // it has not seen yet
+                const int32_t mine = a.G > (int32_t)lane ? (a.G - (int32_t)lane + 63) / 64 : 0;
+                const uint32_t need = mine >= 32 ? 0xFFFFFFFFu : (1u << mine) - 1u;
+                uint32_t seen = 0;
+                for (;;) {
+                    for (int32_t k = 0; k < mine; ++k)
+                        if (!(seen & (1u << k)) &&
+                            __builtin_amdgcn_raw_buffer_load_b32(rf, ((int32_t)lane + 64 * k) * FLAG_WORDS * 4, 0, COH) ==
+                                flag_val)
+                            seen |= 1u << k;
+                    if (__all((seen & need) == need)) break;
+                    if (wall_clock64() - t0 > WAIT_TICKS) {
+                        timed_out = true;
+                        break;
+                    }
                 }
             }
             if (timed_out) {
@@ -829,7 +990,13 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
                     abort_flag_set(1);
                     __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                wg_barrier();  // releases the streaming waves, which then exit
+                // meet the streaming waves at this phase's barriers (norm
+                // steps, x-hat); they then see the abort flag and exit
+                if (all_wave_norm<B, TILE>() && h.has_norm) {
+                    wg_barrier();
+                    wg_barrier();
+                }
+                wg_barrier();
                 return;
             }
         }
@@ -837,7 +1004,14 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
         issue_source_loads<B, CHAIN>(a, ph, xh, lane);
         stage_epilogue_inputs<B, CHAIN>(a, h, runs, epi, lane);
         __builtin_amdgcn_s_waitcnt(0);  // inputs, gains and epilogue values have landed
-        finish_sources<B, CHAIN>(a, ph, xh, prm, lane);
+        if (h.has_norm) {
+            if (all_wave_norm<B, TILE>()) {
+                post_norm_jobs<CHAIN>(a, ph, lds, lane);
+                norm_all(lds, STREAM_WAVES, lane);
+            } else {
+                finish_sources<B, CHAIN>(a, ph, lds + ph.x_off, lds + ph.prm_off, lane);
+            }
+        }
         trace_point(a, p, g, 2, lane);
         wg_barrier();  // x-hat ready
         wg_barrier();  // partials complete
@@ -854,7 +1028,8 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
             // completed, publish this workgroup's flag for phase p
             __builtin_amdgcn_s_waitcnt(0);
             if (lane == 0)
-                __builtin_amdgcn_raw_buffer_store_b32(flag_val, rsrc_of(a.flags + (size_t)p * flag_row(a.G)), g * 4, 0, COH);
+                __builtin_amdgcn_raw_buffer_store_b32(flag_val, rsrc_of(a.flags + (size_t)p * flag_row(a.G)),
+                                                      g * FLAG_WORDS * 4, 0, COH);
         }
         if (EPI_BARRIER == 2) wg_barrier();  // flag issued too
         trace_point(a, p, g, 5, lane);

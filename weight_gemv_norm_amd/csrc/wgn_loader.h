@@ -97,7 +97,13 @@ WGN_HD void make_runs(const KArgs &a, int32_t p, int32_t g, bool tile, RunHdr &h
     h.xb_bytes = G.xb_bytes;
     h.x_off = G.x_off;
     h.part_off = G.part_off;
-    h.pad0 = h.pad1 = 0;
+    h.pad1 = 0;
+    {
+        const DevPhase ph = phase_of<CHAIN>(a, p);
+        int32_t hn = 0;
+        for (int32_t i = 0; i < ph.nsrc; ++i) hn |= source_of<CHAIN>(a, ph.src0 + i).norm != NORM_NONE ? 1 : 0;
+        h.has_norm = hn;
+    }
     for (int32_t w = 0; w <= STREAM_WAVES; ++w) h.wb[w] = G.U > 0 ? wave_begin(w, G.U, STREAM_WAVES) : 0;
     int32_t n = 0, u_base = 0, rp_base = 0, rows = 0;
     h.rstart[0] = 0;

@@ -48,7 +48,7 @@ constexpr int MAX_BATCH = 16;
 constexpr int MAX_BATCH_VALU = 4;   // largest batch of the vector path
 constexpr int TILE_ROWS = 16;        // row-parts per matrix-core unit
 constexpr int TRACE_POINTS = 9;
-constexpr int MAX_RUNS = 16;         // stages per phase (the planner splits larger phases)
+constexpr int MAX_RUNS = 8;          // stages per phase (the planner splits larger phases)
 constexpr int DESC_BUFS = 4;         // phases whose run lists are resident in LDS at once
 constexpr int DESC_AHEAD = 3;        // the control wave builds phase p+DESC_AHEAD's list in iteration p
 #ifndef WGN_EPI_BARRIER
@@ -168,12 +168,15 @@ WGN_HD int32_t nchunks_of(int32_t K) { return (K + UNIT - 1) / UNIT; }
 WGN_HD int32_t units_of(int32_t nrows, int32_t parts, int32_t nch, bool tile) {
     return (tile ? (nrows + TILE_ROWS - 1) / TILE_ROWS : nrows) * parts * nch;
 }
-// Words per phase in the flag array (rows padded for 16-byte loads).  The
-// row is dense: one poll of all flags is one 16-byte load per lane.  (One
-// flag per 64-byte line avoids line sharing between writers but makes every
-// poll touch G lines, which costs more while the weight stream fills the
-// memory pipeline.)
-WGN_HD int32_t flag_row(int32_t G) { return (G + 3) & ~3; }
+// Completion flags: one per (phase, workgroup), FLAG_WORDS words apart.  With
+// FLAG_WORDS = 1 the row is dense and one poll of all flags is one 16-byte
+// load per lane; wider strides put fewer flags in one 64-byte line (writers
+// sharing a line delay each other) at the cost of more lines per poll.
+#ifndef WGN_FLAG_WORDS
+#define WGN_FLAG_WORDS 1
+#endif
+constexpr int FLAG_WORDS = WGN_FLAG_WORDS;
+WGN_HD int32_t flag_row(int32_t G) { return FLAG_WORDS == 1 ? (G + 3) & ~3 : G * FLAG_WORDS; }
 constexpr int MAX_GRID = 2048;
 
 // Meta word of one streamed unit (wave-uniform):
@@ -212,7 +215,8 @@ struct Run {
 struct RunHdr {
     int32_t nruns, U, jmax, xb_bytes;  // xb_bytes: x-hat row stride
     int32_t x_off, part_off;           // LDS byte offsets of x-hat and the partial slots
-    int32_t pad0, pad1;
+    int32_t has_norm;                  // the phase normalises an input (all waves take part)
+    int32_t pad1;
     int32_t wb[STREAM_WAVES + 1];      // wave_begin(w) for w = 0..STREAM_WAVES
     int32_t rstart[MAX_RUNS + 1];      // first WG-local output row of each run (cumulative nrows)
 };
@@ -234,9 +238,80 @@ constexpr int RUN_BUF_BYTES = (int)(sizeof(RunHdr) + MAX_RUNS * sizeof(Run));
 // of different phases may overlap, since the control wave writes phase p+1's
 // areas only after it has finished reading phase p's, and the streaming waves
 // touch x-hat and partials only between a phase's two barriers.
+// A normalisation job of a phase (one per normalised source), posted in LDS
+// by the control wave and run by all waves of the workgroup.
+struct NormJob {
+    int32_t norm, K;       // NORM_RMS / NORM_LAYER, input length
+    int32_t xoff;          // element offset of the source inside a batch row of x-hat
+    int32_t prm;           // LDS byte offset of the gain (the shift follows at prm + prm_half)
+    int32_t prm_half;
+    float eps;
+    int32_t has_gamma, has_beta;
+};
+struct NormHdr {
+    int32_t njobs, nb, x_off, xb;  // x-hat base (bytes) and row stride (elements)
+    NormJob job[MAX_SRC];
+};
+WGN_HD int32_t wgn_clz(uint32_t v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_clz(v);
+#else
+    int32_t n = 0;
+    while (n < 32 && !(v & 0x80000000u)) {
+        v <<= 1;
+        ++n;
+    }
+    return n;
+#endif
+}
+// How nw waves share the normalisation of nb batch rows (padded to a power of
+// two P): a row over one or more whole waves when P <= nw, several rows per
+// wave otherwise.  nw is WAVES when all waves of a workgroup normalise
+// together (matrix-core path), 1 when the control wave does it alone.
+struct NormSplit {
+    int32_t row, sub, lanes;   // batch row, lane index inside the row's lanes, lanes per row
+    int32_t lpr;               // lanes of this row inside this wave (group_sum width)
+    int32_t slot;              // statistics slot of this wave for its row
+    int32_t w0, w1, rslot;     // waves [w0, w1) holding the row's statistics, slot inside them
+    bool active;
+};
+WGN_HD NormSplit norm_split(int32_t nb, int32_t w, uint32_t lane, int32_t nw) {
+    NormSplit S;
+    const int32_t shift = nb <= 1 ? 0 : 32 - wgn_clz((uint32_t)(nb - 1));
+    const int32_t P = 1 << shift;
+    if (P <= nw) {
+        S.row = (w * P) / nw;  // the waves of row r are [ceil(r W / P), ceil((r + 1) W / P))
+        S.w0 = (S.row * nw + P - 1) / P;
+        S.w1 = ((S.row + 1) * nw + P - 1) / P;
+        S.lanes = (S.w1 - S.w0) * 64;
+        S.sub = (w - S.w0) * 64 + (int32_t)lane;
+        S.lpr = 64;
+        S.slot = 0;
+        S.rslot = 0;
+    } else {
+        int32_t rpw = (P + nw - 1) / nw;
+        rpw = 1 << (32 - wgn_clz((uint32_t)(rpw - 1)));
+        S.lpr = 64 / rpw;
+        S.row = w * rpw + (int32_t)lane / S.lpr;
+        S.sub = (int32_t)lane % S.lpr;
+        S.lanes = S.lpr;
+        S.slot = (int32_t)lane / S.lpr;
+        S.w0 = S.row / rpw;
+        S.w1 = S.w0 + 1;
+        S.rslot = S.row % rpw;
+    }
+    S.active = S.row < nb;
+    return S;
+}
+
+
 constexpr int LDS_DESC_OFF = 0;
 constexpr int LDS_TRACE_OFF = DESC_BUFS * RUN_BUF_BYTES;
-constexpr int LDS_DYN_OFF = (LDS_TRACE_OFF + 48 + 255) & ~255;
+constexpr int LDS_NORM_OFF = LDS_TRACE_OFF + 64;
+// partial statistics: [source][wave][batch row of that wave][sum, sum of squares], FP64
+constexpr int STATS_ROWS = 8;        // batch rows one wave may hold (16 rows over at least 2 waves)
+constexpr int LDS_STATS_OFF = (LDS_NORM_OFF + (int)sizeof(NormHdr) + 15) & ~15;
+constexpr int LDS_DYN_OFF = (LDS_STATS_OFF + MAX_SRC * WAVES * STATS_ROWS * 16 + 255) & ~255;
 
 // Per-(WG, stage) geometry inside a phase.
 struct StageSpan {
