@@ -34,6 +34,10 @@ def parse():
                     choices=["decode_step_1536x28", "decoder_block_1536", "ln_gelu_chain_768x72",
                              "rmsnorm_gemv_256", "rmsnorm_rows_960x1536_f16", "lmhead_151936"])
     ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None,
+                    help="decode-step workload: number of decoder blocks (default 28)")
+    ap.add_argument("--vocab", type=int, default=None,
+                    help="decode-step workload: LM-head rows (default 151936)")
     ap.add_argument("--mode", type=int, default=0, help="0 persistent kernel, 1 one launch per phase")
     ap.add_argument("--path", type=int, default=0,
                     help="0 auto (vector path for batch <= 4, matrix cores above), 1 vector, 2 matrix cores")
@@ -77,7 +81,7 @@ def main():
     cfg = {"workload": wl, "batch": B}
     kernel_name = "chain_kernel"
     if wl in ("decode_step_1536x28", "decoder_block_1536"):
-        inp = gen.make_stage_tensors(wl, device=dev, batch=B)
+        inp = gen.make_stage_tensors(wl, device=dev, batch=B, n_layers=args.layers, vocab=args.vocab)
         stages, bufs = steps.decoder_stages(inp, dev)
         chain = W.Chain(stages, B, mode=args.mode, path=args.path)
         nb = steps.decode_step_bytes(inp)

@@ -213,9 +213,10 @@ int32_t wgn_chain_grid(const wgn_chain *chain);
  *   3 weight stream of the phase done, 4 outputs stored, 5 completion released
  *   (control wave); 6 first streaming wave passes the phase's x-hat barrier,
  *   7 it has issued its loads ahead of that barrier, 8 it has consumed its
- *   last block of the phase.
+ *   last block of the phase, 9..11 it has consumed its first, second, third
+ *   block of the phase (0 if it has fewer).
  * Synchronises `stream`; n_out = number of uint64 slots available. */
-#define WGN_TRACE_POINTS 9
+#define WGN_TRACE_POINTS 12
 wgn_status wgn_chain_trace(const wgn_chain *chain, wgn_stream stream, uint64_t *out, size_t n_out);
 /* Phase index of each stage (array of n_stages). */
 wgn_status wgn_chain_stage_phases(const wgn_chain *chain, int32_t *phase_of_stage);

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # WGN_LIB_PATH selects another build of the same library (tuning experiments).
 LIB_PATH = os.environ.get("WGN_LIB_PATH") or os.path.join(HERE, "libwgn.so")
 
-TRACE_POINTS = 9
+TRACE_POINTS = 12
 OK, E_ARG, E_ALIGN, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_DEVICE, E_TIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7
 NORM_NONE, NORM_RMS, NORM_LAYER = 0, 1, 2
 EPI_NONE, EPI_GELU_TANH, EPI_SWIGLU, EPI_ARGMAX = 0, 1, 2, 3

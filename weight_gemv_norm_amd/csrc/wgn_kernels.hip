@@ -535,37 +535,44 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
     wg_barrier();  // x-hat of the first phase is ready
     bool ok = abort_flag_get() == 0;
     int32_t p = a.p0;
-    if (tw) tl[(p & 1) * 3 + 0] = wall_clock64();
+    if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
+    int32_t nblk = 0;  // blocks of phase p consumed (trace only)
     while (ok && p < a.p1) {
         consume_any<B, TILE>(a, dA, mA, acc, lds, lane);
+        if (tw && nblk < 3) tl[(p & 1) * 6 + 3 + nblk] = wall_clock64();
+        ++nblk;
         const bool endA = mA.last;
         if (endA) {
-            if (tw) tl[(p & 1) * 3 + 2] = wall_clock64();
+            if (tw) tl[(p & 1) * 6 + 2] = wall_clock64();
             wg_barrier();  // partials of phase p are complete
             if (EPI_BARRIER) wg_barrier();  // the control wave has issued phase p's stores
         }
         load_any<B, TILE>(a, S, dA, mA, lane);
+        if (endA) nblk = 0;
         if (endA && ++p < a.p1) {
-            if (tw) tl[(p & 1) * 3 + 1] = wall_clock64();
+            if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
             if (all_wave_norm<B, TILE>() && ((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
             wg_barrier();  // x-hat of phase p is ready
             ok = abort_flag_get() == 0;
-            if (tw) tl[(p & 1) * 3 + 0] = wall_clock64();
+            if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
         }
         consume_any<B, TILE>(a, dB, mB, acc, lds, lane);
+        if (tw && nblk < 3) tl[(p & 1) * 6 + 3 + nblk] = wall_clock64();
+        ++nblk;
         const bool endB = ok && mB.last;
         if (endB) {
-            if (tw) tl[(p & 1) * 3 + 2] = wall_clock64();
+            if (tw) tl[(p & 1) * 6 + 2] = wall_clock64();
             wg_barrier();
             if (EPI_BARRIER) wg_barrier();
         }
         load_any<B, TILE>(a, S, dB, mB, lane);
+        if (endB) nblk = 0;
         if (endB && ++p < a.p1) {
-            if (tw) tl[(p & 1) * 3 + 1] = wall_clock64();
+            if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
             if (all_wave_norm<B, TILE>() && ((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
             wg_barrier();
             ok = abort_flag_get() == 0;
-            if (tw) tl[(p & 1) * 3 + 0] = wall_clock64();
+            if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
         }
     }
 }
@@ -919,6 +926,7 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
     const uint32_t lane = lane_id();
     char *desc = lds + LDS_DESC_OFF;
     if (lane == 0) abort_flag_set(0);
+    if (a.trace && lane < 12) ((uint64_t *)(lds + LDS_TRACE_OFF))[lane] = 0;
     const uint32_t flag_val =
         a.persistent ? __hip_atomic_load(a.run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
     // Run lists are built DESC_AHEAD (3) phases ahead into DESC_BUFS (4) LDS
@@ -1016,9 +1024,10 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
         wg_barrier();  // x-hat ready
         wg_barrier();  // partials complete
         trace_point(a, p, g, 3, lane);
-        if (a.trace && lane < 3) {
-            const uint64_t *tl = (const uint64_t *)(lds + LDS_TRACE_OFF);
-            a.trace[((size_t)p * a.G + g) * TRACE_POINTS + 6 + lane] = tl[(p & 1) * 3 + lane];
+        if (a.trace && lane < 6) {
+            uint64_t *tl = (uint64_t *)(lds + LDS_TRACE_OFF);
+            a.trace[((size_t)p * a.G + g) * TRACE_POINTS + 6 + lane] = tl[(p & 1) * 6 + lane];
+            if (lane >= 3) tl[(p & 1) * 6 + lane] = 0;  // per-block slots: cleared for phase p + 2
         }
         epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane);
         trace_point(a, p, g, 4, lane);

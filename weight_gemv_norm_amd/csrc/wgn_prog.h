@@ -47,7 +47,7 @@ constexpr int THREADS = WAVES * 64;
 constexpr int MAX_BATCH = 16;
 constexpr int MAX_BATCH_VALU = 4;   // largest batch of the vector path
 constexpr int TILE_ROWS = 16;        // row-parts per matrix-core unit
-constexpr int TRACE_POINTS = 9;
+constexpr int TRACE_POINTS = 12;
 constexpr int MAX_RUNS = 8;          // stages per phase (the planner splits larger phases)
 constexpr int DESC_BUFS = 4;         // phases whose run lists are resident in LDS at once
 constexpr int DESC_AHEAD = 3;        // the control wave builds phase p+DESC_AHEAD's list in iteration p
@@ -307,7 +307,7 @@ WGN_HD NormSplit norm_split(int32_t nb, int32_t w, uint32_t lane, int32_t nw) {
 
 constexpr int LDS_DESC_OFF = 0;
 constexpr int LDS_TRACE_OFF = DESC_BUFS * RUN_BUF_BYTES;
-constexpr int LDS_NORM_OFF = LDS_TRACE_OFF + 64;
+constexpr int LDS_NORM_OFF = LDS_TRACE_OFF + 2 * 6 * 8;  // 6 streaming-wave timestamps per phase parity
 // partial statistics: [source][wave][batch row of that wave][sum, sum of squares], FP64
 constexpr int STATS_ROWS = 8;        // batch rows one wave may hold (16 rows over at least 2 waves)
 constexpr int LDS_STATS_OFF = (LDS_NORM_OFF + (int)sizeof(NormHdr) + 15) & ~15;
