@@ -140,7 +140,7 @@ def test_small_decode_step_all_batches(B):
     check_decoder(inp, bufs, layers_full={1})
 
 
-@pytest.mark.parametrize("B", [4, 16])
+@pytest.mark.parametrize("B", [1, 4, 16])
 def test_ln_gelu_chain_768x72(B):
     """72 x [LayerNorm(768) -> Linear -> GELU-tanh], seeded LN params, per stage."""
     say("chain ln_gelu_chain_768x72 B=%d" % B)
@@ -156,6 +156,42 @@ def test_ln_gelu_chain_768x72(B):
                       gamma=bits(Ld["gamma"]), beta=bits(Ld["beta"]), bias=bits(Ld["bias"]),
                       epi=O.EPI_GELU_TANH)
         assert_close_bf16(bits(xs[i + 1]), ref, "ln-gelu layer %d" % i)
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 8])
+def test_phase_with_several_normalised_sources(B):
+    """Independent stages over different inputs share one phase: RMSNorm and
+    LayerNorm sources of different lengths (one ragged, one with no gain) are
+    normalised together, then each stage is checked against the oracle."""
+    say("chain several sources B=%d" % B)
+    specs = [  # (N, K, norm, gamma, beta, epi)
+        (300, 1536, O.NORM_RMS, True, False, O.EPI_NONE),
+        (129, 768, O.NORM_LAYER, True, True, O.EPI_GELU_TANH),
+        (64, 264, O.NORM_LAYER, False, False, O.EPI_NONE),
+        (200, 520, O.NORM_RMS, False, False, O.EPI_NONE),
+    ]
+    stages, checks = [], []
+    for i, (N, K, norm, hg, hb, epi) in enumerate(specs):
+        seed = 900 + 10 * i
+        Wt = gen.normal((N, K), 0.05, seed + 1, device=DEV)
+        x = gen.normal((B, K), 1.0, seed + 2, mean=0.3 if norm == O.NORM_LAYER else 0.0, device=DEV)
+        g = gen.normal((K,), 0.1, seed + 3, mean=1.0, device=DEV) if hg else None
+        be = gen.normal((K,), 0.02, seed + 4, device=DEV) if hb else None
+        bias = gen.normal((N,), 0.02, seed + 5, device=DEV) if epi == O.EPI_GELU_TANH else None
+        y = torch.empty((B, N), dtype=torch.bfloat16, device=DEV)
+        eps = 1e-5 if norm == O.NORM_LAYER else 1e-6
+        stages.append(W.make_stage(Wt, x, y, norm=norm, eps=eps, gamma=g, beta=be, bias=bias, epi=epi))
+        checks.append((Wt, x, y, norm, eps, g, be, bias, epi))
+    ch = W.Chain(stages, B)
+    assert ch.num_phases == 1
+    ch.run()
+    ch.check()
+    torch.cuda.synchronize()
+    for i, (Wt, x, y, norm, eps, g, be, bias, epi) in enumerate(checks):
+        ref = O.stage(bits(x), bits(Wt), norm=norm, eps=float(np.float32(eps)), epi=epi,
+                      gamma=None if g is None else bits(g), beta=None if be is None else bits(be),
+                      bias=None if bias is None else bits(bias))
+        assert_close_bf16(bits(y), ref, "source %d" % i)
 
 
 def test_ln_gelu_chain_default_params():

@@ -71,6 +71,9 @@ CASES = [
     (1536, 8960, 1, O.NORM_NONE, O.EPI_NONE, False, True),
     (513, 1024, 4, O.NORM_LAYER, O.EPI_NONE, True, True),
     (8960, 1536, 1, O.NORM_RMS, O.EPI_SWIGLU, False, False),
+    # batch 1 LayerNorm (the control wave's own normalisation), ragged K
+    (37, 264, 1, O.NORM_LAYER, O.EPI_GELU_TANH, True, False),
+    (513, 1024, 1, O.NORM_LAYER, O.EPI_NONE, True, True),
     # matrix-core path (batch > 4): ragged tiles (N % 16), K tails, every epilogue
     (1, 8, 5, O.NORM_RMS, O.EPI_NONE, False, False),
     (37, 264, 8, O.NORM_LAYER, O.EPI_GELU_TANH, True, False),

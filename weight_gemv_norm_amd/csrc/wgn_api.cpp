@@ -13,7 +13,7 @@
 #include <new>
 #include <vector>
 
-#include "../../include/wgn.h"
+#include "wgn.h"
 #include "wgn_loader.h"
 
 namespace wgn {
@@ -1076,26 +1076,29 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
     a.nb = nb;
     int32_t bad = 0;
     if (P.lds_total() > LDS_BUDGET) ++bad;
-    // the all-wave normalisation split (batch 2 and up) covers every (batch
-    // row, lane-in-row) once, and each row's statistics sit in the waves the
-    // combine step reads
-    if (tile || nb > 1) {
+    // the all-wave normalisation split covers every (item, lane-in-item)
+    // once for every item count the kernel uses (items = (source, batch
+    // row) pairs, padded to a power of two, at most MAX_SRC x MAX_BATCH), and
+    // each item's statistics sit in the waves and slots the combine step reads
+    {
         const int32_t nw = WAVES;
-        std::vector<std::vector<int32_t>> cover(nb);
-        for (int32_t w = 0; w < nw; ++w)
-            for (uint32_t lane = 0; lane < 64; ++lane) {
-                const NormSplit S = norm_split(nb, w, lane, nw);
-                if (S.slot < 0 || S.slot >= STATS_ROWS || S.rslot < 0 || S.rslot >= STATS_ROWS) ++bad;
-                if (!S.active) continue;
-                if (w < S.w0 || w >= S.w1 || S.sub < 0 || S.sub >= S.lanes) ++bad;
-                if (S.w1 - S.w0 == 1 && S.slot != S.rslot) ++bad;
-                cover[S.row].push_back(S.sub);
+        for (int32_t nq = 1; nq <= MAX_SRC * MAX_BATCH; nq *= 2) {
+            std::vector<std::vector<int32_t>> cover(nq);
+            for (int32_t w = 0; w < nw; ++w)
+                for (uint32_t lane = 0; lane < 64; ++lane) {
+                    const NormSplit S = norm_split(nq, w, lane, nw);
+                    if (S.slot < 0 || S.slot >= STATS_ROWS || S.rslot < 0 || S.rslot >= STATS_ROWS) ++bad;
+                    if (!S.active) continue;
+                    if (w < S.w0 || w >= S.w1 || S.sub < 0 || S.sub >= S.lanes) ++bad;
+                    if (S.w1 - S.w0 == 1 && S.slot != S.rslot) ++bad;
+                    cover[S.row].push_back(S.sub);
+                }
+            for (int32_t r = 0; r < nq; ++r) {
+                std::sort(cover[r].begin(), cover[r].end());
+                for (size_t i = 0; i < cover[r].size(); ++i)
+                    if (cover[r][i] != (int32_t)i) ++bad;
+                if (cover[r].empty()) ++bad;
             }
-        for (int32_t r = 0; r < nb; ++r) {
-            std::sort(cover[r].begin(), cover[r].end());
-            for (size_t i = 0; i < cover[r].size(); ++i)
-                if (cover[r][i] != (int32_t)i) ++bad;
-            if (cover[r].empty()) ++bad;
         }
     }
     for (int32_t p = 0; p < (int32_t)P.phases.size(); ++p) {

@@ -52,12 +52,37 @@ constexpr uint32_t RSRC_W3 = 0x00020000u; // buffer descriptor word 3 for raw dw
 // ------------------------------------------------------------------ numerics
 __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
 
+// FP64 reciprocal and FP32-rounded reciprocal square root: the hardware's
+// FP64 estimates, each refined by two Newton-Raphson steps (every step
+// squares the relative error), leave only FP64 rounding before the final
+// FP32 rounding -- at a fraction of the latency of IEEE divide and sqrt.
+__device__ __forceinline__ double recip_f64(double k) {
+    double r = __builtin_amdgcn_rcp(k);
+    r = __builtin_fma(__builtin_fma(-k, r, 1.0), r, r);
+    r = __builtin_fma(__builtin_fma(-k, r, 1.0), r, r);
+    return r;
+}
+__device__ __forceinline__ float rsqrt_f64_to_f32(double v) {
+    double y = __builtin_amdgcn_rsq(v);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const double e = __builtin_fma(-v * y, y, 1.0);  // 1 - v y^2
+        y = __builtin_fma(0.5 * y, e, y);
+    }
+    return (float)y;
+}
+// (s / K + eps)^(-1/2) for an FP64 sum s over K values.
+__device__ __forceinline__ float inv_sqrt_mean(double s, int32_t K, float eps) {
+    return rsqrt_f64_to_f32(__builtin_fma(s, recip_f64((double)K), (double)eps));
+}
+
 // FP32 -> BF16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// FP32 -> BF16, round to nearest even (gfx950's v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// Two values packed as BF16 (lo in the low half), one instruction.
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Dot product of 8 BF16 pairs, FP32 accumulation (v_dot2c_f32_bf16).  The
@@ -70,6 +95,45 @@ __device__ __forceinline__ float dot8(const u32x4 &w, const u32x4 &x, float acc)
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa[i]), __builtin_bit_cast(bf16x2, xa[i]),
                                               acc, false);
     return acc;
+}
+
+// Statistic of one 16-byte chunk of 8 BF16 values: the sum of squares
+// (RMSNorm) or the sum (LayerNorm), formed in FP32 by v_dot2_f32_bf16 (the
+// products of BF16 values are exact in FP32) in two interleaved chains, and
+// widened to FP64 for the accumulation over chunks.
+__device__ __forceinline__ double chunk_stat(const u32x4 &v, bool layer) {
+    const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+    const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+    float a = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16x2 x = __builtin_bit_cast(bf16x2, vv[e]);
+        const bf16x2 y = layer ? one : x;
+        if (e & 1) b = __builtin_amdgcn_fdot2_f32_bf16(x, y, b, false);
+        else a = __builtin_amdgcn_fdot2_f32_bf16(x, y, a, false);
+    }
+    return (double)a + (double)b;
+}
+
+// x-hat of one chunk, rounded to BF16: ((x - mean) * rstd) * g + beta for
+// LayerNorm, (x * rstd) * g for RMSNorm (g = 1 and beta = 0 when absent).
+__device__ __forceinline__ u32x4 chunk_apply(const u32x4 &v, const u32x4 &gv, const u32x4 &bv, float mean,
+                                             float rstd, bool layer) {
+    const uint32_t vv[4] = {v.x, v.y, v.z, v.w}, gg[4] = {gv.x, gv.y, gv.z, gv.w}, bb[4] = {bv.x, bv.y, bv.z, bv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float lo = bf2f(vv[e] & 0xFFFFu), hi = bf2f(vv[e] >> 16);
+        if (layer) {
+            lo = (lo - mean) * rstd * bf2f(gg[e] & 0xFFFFu) + bf2f(bb[e] & 0xFFFFu);
+            hi = (hi - mean) * rstd * bf2f(gg[e] >> 16) + bf2f(bb[e] >> 16);
+        } else {
+            lo = lo * rstd * bf2f(gg[e] & 0xFFFFu);
+            hi = hi * rstd * bf2f(gg[e] >> 16);
+        }
+        o[e] = f2bf2(lo, hi);
+    }
+    return (u32x4){o[0], o[1], o[2], o[3]};
 }
 
 template <int CTRL>
@@ -86,6 +150,21 @@ __device__ __forceinline__ float wave_sum(float v) {
     v += dpp<0x140>(v);   // row_mirror
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Sum over the 64 lanes, complete in lane 63 only (the other lanes hold
+// partial sums).  The row sums of 16 lanes are formed as in wave_sum; the
+// rows are then combined with DPP row broadcasts -- lane 15 of rows 0 and 2
+// into rows 1 and 3, then lane 31 into rows 2 and 3 -- so no LDS permute (and
+// no wait on the LDS queue) is needed.  The order is fixed: reproducible.
+__device__ __forceinline__ float wave_sum_last(float v) {
+    v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);   // row_half_mirror
+    v += dpp<0x140>(v);   // row_mirror
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31
     return v;
 }
 
@@ -106,6 +185,28 @@ __device__ __forceinline__ double dpp64(double v) {
     const uint64_t u = __double_as_longlong(v);
     const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// A DPP row broadcast of an FP64 value into the rows of ROW_MASK (0 elsewhere).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp64_rows(double v) {
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// Sum of an FP64 value over the 64 lanes, returned to every lane from scalar
+// registers: row sums by DPP, rows combined by the row broadcasts (as in
+// wave_sum_last), then lane 63 read out -- no LDS permute.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp64<0xB1>(v);
+    v += dpp64<0x4E>(v);
+    v += dpp64<0x141>(v);
+    v += dpp64<0x140>(v);
+    v += dpp64_rows<0x142, 0xA>(v);  // row_bcast:15
+    v += dpp64_rows<0x143, 0xC>(v);  // row_bcast:31
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, 63), hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), 63);
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 // The same steps as group_sum for FP64 values.
@@ -190,48 +291,63 @@ __device__ __forceinline__ void trace_point(const KArgs &a, int32_t p, int32_t g
 
 // ------------------------------------------------------ normalisation (all waves)
 // The inputs of a phase are normalised by all WAVES waves of the workgroup
-// together: batch rows (padded to a power of two P) are spread over the
-// waves -- a row over one or more whole waves when P <= WAVES, several rows
-// in one wave otherwise -- and every lane walks a strided share of its row's
-// 16-byte chunks.  Sum and sum of squares are accumulated in FP64 (a square
-// of a BF16 value is exact in FP32), reduced inside the wave, posted per wave
-// in LDS and combined in wave order after a barrier, so the statistics are
+// together.  The work items are the (job, batch row) pairs -- item
+// q = j * Pb + b, Pb = batch rounded up to a power of two, the number of items
+// padded to a power of two -- and they are spread over the waves like rows by
+// norm_split: an item over one or more whole waves when there are at most
+// WAVES items, several items in one wave otherwise.  Each lane serves one
+// item and walks a strided share of its 16-byte chunks, so a wave carries one
+// job's latency chain, not one per job.  Sums are formed per chunk in FP32
+// (chunk_stat) and accumulated in FP64, reduced inside the wave, posted per
+// wave in LDS and combined in wave order after a barrier: the statistics are
 // as good as exact and their order is fixed.
-__device__ __forceinline__ double2 *norm_stats(char *lds, int32_t j, int32_t w, int32_t slot) {
-    return (double2 *)(lds + LDS_STATS_OFF) + ((j * WAVES + w) * STATS_ROWS + slot);
+__device__ __forceinline__ double2 *norm_stats(char *lds, int32_t w, int32_t slot) {
+    return (double2 *)(lds + LDS_STATS_OFF) + (w * STATS_ROWS + slot);
+}
+
+struct NormItem {
+    NormSplit S;
+    int32_t j, b;  // job and batch row of this lane's item
+    bool active;
+};
+__device__ __forceinline__ NormItem norm_item(const NormHdr &J, int32_t w, uint32_t lane, int32_t nw) {
+    NormItem it;
+    const int32_t lb = J.nb <= 1 ? 0 : 32 - wgn_clz((uint32_t)(J.nb - 1));
+    const int32_t lj = J.njobs <= 1 ? 0 : 32 - wgn_clz((uint32_t)(J.njobs - 1));
+    it.S = norm_split(1 << (lj + lb), w, lane, nw);
+    it.j = it.S.row >> lb;
+    it.b = it.S.row & ((1 << lb) - 1);
+    it.active = it.S.active && it.j < J.njobs && it.b < J.nb;
+    return it;
 }
 
 // Step 1 (after the inputs have landed in LDS): partial statistics.
 __device__ void norm_all_stats(char *lds, int32_t w, uint32_t lane, int32_t nw) {
     const NormHdr &J = *(const NormHdr *)(lds + LDS_NORM_OFF);
-    const NormSplit S = norm_split(J.nb, w, lane, nw);
-    for (int32_t j = 0; j < J.njobs; ++j) {
-        const NormJob &jb = J.job[j];
-        const bool layer = jb.norm == NORM_LAYER;
-        const int32_t n8 = S.active ? jb.K >> 3 : 0;
-        const uint16_t *src = (const uint16_t *)(lds + J.x_off + ((size_t)(S.active ? S.row : 0) * J.xb + jb.xoff) * 2);
-        double s1 = 0.0, s2 = 0.0;
-        for (int32_t i = S.sub; i < n8; i += S.lanes) {
-            const u32x4 v = *(const u32x4 *)(src + i * 8);
-            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-            double c1 = 0.0, c2 = 0.0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float lo = bf2f(vv[e] & 0xFFFFu), hi = bf2f(vv[e] >> 16);
-                c2 += (double)(lo * lo) + (double)(hi * hi);
-                if (layer) c1 += (double)lo + (double)hi;
-            }
-            s1 += c1;
-            s2 += c2;
-        }
+    const NormItem it = norm_item(J, w, lane, nw);
+    const NormSplit &S = it.S;
+    const NormJob &jb = J.job[it.active ? it.j : 0];
+    const bool layer = jb.norm == NORM_LAYER;
+    const int32_t n8 = it.active ? jb.K >> 3 : 0;
+    const uint16_t *src = (const uint16_t *)(lds + J.x_off + ((size_t)(it.active ? it.b : 0) * J.xb + jb.xoff) * 2);
+    double s1 = 0.0, s2 = 0.0;
+    for (int32_t i = S.sub; i < n8; i += S.lanes) {
+        const u32x4 v = *(const u32x4 *)(src + i * 8);
+        s2 += chunk_stat(v, false);
+        if (layer) s1 += chunk_stat(v, true);
+    }
+    if (S.lpr == 64) {
+        s1 = wave_sum_f64(s1);
+        s2 = wave_sum_f64(s2);
+    } else {
         s1 = group_sum_f64(s1, S.lpr);
         s2 = group_sum_f64(s2, S.lpr);
-        if (S.active && (S.sub % S.lpr) == 0) {
-            double2 st;
-            st.x = s1;
-            st.y = s2;
-            *norm_stats(lds, j, w, S.slot) = st;
-        }
+    }
+    if ((S.sub % S.lpr) == 0) {
+        double2 st;
+        st.x = s1;
+        st.y = s2;
+        *norm_stats(lds, w, S.slot) = st;
     }
 }
 
@@ -239,54 +355,42 @@ __device__ void norm_all_stats(char *lds, int32_t w, uint32_t lane, int32_t nw) 
 // share and round to BF16 in place.
 __device__ void norm_all_apply(char *lds, int32_t w, uint32_t lane, int32_t nw) {
     const NormHdr &J = *(const NormHdr *)(lds + LDS_NORM_OFF);
-    const NormSplit S = norm_split(J.nb, w, lane, nw);
-    if (!S.active) return;
-    for (int32_t j = 0; j < J.njobs; ++j) {
-        const NormJob &jb = J.job[j];
-        const int32_t K = jb.K, n8 = K >> 3;
-        double s1 = 0.0, s2 = 0.0;
-        for (int32_t ww = S.w0; ww < S.w1; ++ww) {
-            const double2 st = *norm_stats(lds, j, ww, S.rslot);
-            s1 += st.x;
-            s2 += st.y;
-        }
-        float mean = 0.0f, rstd;
-        if (jb.norm == NORM_RMS) {
-            rstd = (float)(1.0 / sqrt(s2 / (double)K + (double)jb.eps));
-        } else {
-            const double m = s1 / (double)K;
-            const double var = s2 / (double)K - m * m;  // biased; FP64 sums, see above
-            mean = (float)m;
-            rstd = (float)(1.0 / sqrt((var > 0.0 ? var : 0.0) + (double)jb.eps));
-        }
-        uint16_t *dst = (uint16_t *)(lds + J.x_off + ((size_t)S.row * J.xb + jb.xoff) * 2);
-        const char *gp = lds + jb.prm;
-        const char *bp = lds + jb.prm + jb.prm_half;
-        for (int32_t i = S.sub; i < n8; i += S.lanes) {
-            const u32x4 v = *(const u32x4 *)(dst + i * 8);
-            const u32x4 gv = jb.has_gamma ? *(const u32x4 *)(gp + i * 16)
-                                          : (u32x4){0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-            const u32x4 bv = jb.has_beta ? *(const u32x4 *)(bp + i * 16) : (u32x4){0u, 0u, 0u, 0u};
-            const uint32_t vv[4] = {v.x, v.y, v.z, v.w}, gg[4] = {gv.x, gv.y, gv.z, gv.w},
-                           bb[4] = {bv.x, bv.y, bv.z, bv.w};
-            uint32_t o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float lo =
-                    (bf2f(vv[e] & 0xFFFFu) - mean) * rstd * bf2f(gg[e] & 0xFFFFu) + bf2f(bb[e] & 0xFFFFu);
-                const float hi = (bf2f(vv[e] >> 16) - mean) * rstd * bf2f(gg[e] >> 16) + bf2f(bb[e] >> 16);
-                o[e] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
-            }
-            *(u32x4 *)(dst + i * 8) = (u32x4){o[0], o[1], o[2], o[3]};
-        }
+    const NormItem it = norm_item(J, w, lane, nw);
+    if (!it.active) return;
+    const NormSplit &S = it.S;
+    const NormJob &jb = J.job[it.j];
+    const int32_t K = jb.K, n8 = K >> 3;
+    double s1 = 0.0, s2 = 0.0;
+    for (int32_t ww = S.w0; ww < S.w1; ++ww) {
+        const double2 st = *norm_stats(lds, ww, S.rslot);
+        s1 += st.x;
+        s2 += st.y;
+    }
+    const bool layer = jb.norm == NORM_LAYER;
+    float mean = 0.0f, rstd;
+    if (!layer) {
+        rstd = inv_sqrt_mean(s2, K, jb.eps);
+    } else {
+        const double rk = recip_f64((double)K);
+        const double m = s1 * rk;
+        const double var = __builtin_fma(s2, rk, -m * m);  // biased; FP64 sums, see above
+        mean = (float)m;
+        rstd = rsqrt_f64_to_f32((var > 0.0 ? var : 0.0) + (double)jb.eps);
+    }
+    uint16_t *dst = (uint16_t *)(lds + J.x_off + ((size_t)it.b * J.xb + jb.xoff) * 2);
+    const char *gp = lds + jb.prm;
+    const char *bp = lds + jb.prm + jb.prm_half;
+    for (int32_t i = S.sub; i < n8; i += S.lanes) {
+        const u32x4 v = *(const u32x4 *)(dst + i * 8);
+        const u32x4 gv = jb.has_gamma ? *(const u32x4 *)(gp + i * 16)
+                                      : (u32x4){0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+        const u32x4 bv = jb.has_beta ? *(const u32x4 *)(bp + i * 16) : (u32x4){0u, 0u, 0u, 0u};
+        *(u32x4 *)(dst + i * 8) = chunk_apply(v, gv, bv, mean, rstd, layer);
     }
 }
 
 // Both steps with their barriers; every wave calls this for a phase whose
 // run header says it has a normalised input, right before the x-hat barrier.
-// Used from batch 2 up: at batch 1 the control wave alone is quicker (the
-// streaming waves would first wait for their in-flight weight loads, which
-// the compiler cannot keep apart from the registers the norm needs).
 __device__ __forceinline__ void norm_all(char *lds, int32_t w, uint32_t lane) {
     wg_barrier();  // inputs in LDS, jobs posted
     norm_all_stats(lds, w, lane, WAVES);
@@ -382,27 +486,47 @@ __device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4
 // zeros and points at the start of x-hat, which is initialised in every
 // phase), so every load is waited for in issue order on every path and the
 // compiler's vmcnt bookkeeping stays exact.
+//
+// Units are consumed in groups of G: the group's x-hat reads are issued
+// together, so one LDS latency covers G units, and a row-part that ends in
+// the block is reduced by wave_sum_last (DPP only) and its partial written by
+// lane 63.  G is the largest group whose x-hat values fit in the registers
+// left beside the two in-flight blocks.
+template <int B>
+constexpr int xhat_group() {
+    return (B == 1 && DEPTH % 16 == 0) ? 16 : (B == 2 && DEPTH % 4 == 0) ? 4 : 2;
+}
+
 template <int B>
 __device__ __forceinline__ void consume_block(const u32x4 (&d)[DEPTH], const BlockMeta &bm, float (&acc)[B],
                                               const char *lds, uint32_t lane) {
-    const char *xh = lds + bm.x_off;
+    constexpr int G = xhat_group<B>();
+    static_assert(DEPTH % G == 0, "block depth must be a multiple of the x-hat group");
+    const char *xh = lds + bm.x_off + lane * 16u;
     float *part = (float *)(lds + bm.part_off);
 #pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-        const uint32_t m = __builtin_amdgcn_readlane(bm.meta_v, j);
-        const char *xp = xh + ((m & 0x3FFFu) << 4) + lane * 16u;
+    for (int g0 = 0; g0 < DEPTH; g0 += G) {
+        u32x4 xv[G][B];
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            u32x4 xv = *(const u32x4 *)(xp + b * bm.xb_bytes);
-            acc[b] = dot8(d[j], xv, acc[b]);
+        for (int j = 0; j < G; ++j) {
+            const uint32_t m = __builtin_amdgcn_readlane(bm.meta_v, g0 + j);
+            const char *xp = xh + ((m & 0x3FFFu) << 4);
+#pragma unroll
+            for (int b = 0; b < B; ++b) xv[j][b] = *(const u32x4 *)(xp + b * bm.xb_bytes);
         }
-        if (m & 0x4000u) {
-            const uint32_t slot = m >> 16;
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                float s = wave_sum(acc[b]);
-                if (lane == 0) part[slot + b] = s;
-                acc[b] = 0.0f;
+        for (int j = 0; j < G; ++j) {
+            const uint32_t m = __builtin_amdgcn_readlane(bm.meta_v, g0 + j);
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[b] = dot8(d[g0 + j], xv[j][b], acc[b]);
+            if (m & 0x4000u) {
+                const uint32_t slot = m >> 16;
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const float sum = wave_sum_last(acc[b]);
+                    if (lane == 63) part[slot + b] = sum;
+                    acc[b] = 0.0f;
+                }
             }
         }
     }
@@ -500,9 +624,6 @@ __device__ __forceinline__ void consume_any(const KArgs &a, const u32x4 (&d)[blo
     else consume_block<B>(d, bm, acc.v, lds, lane);
 }
 
-template <int B, bool TILE>
-constexpr bool all_wave_norm() { return TILE || B > 1; }
-
 template <int B, bool CHAIN, bool TILE>
 __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
     const uint32_t lane = lane_id();
@@ -531,7 +652,7 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
     const bool tw = a.trace && w == 0 && lane == 0;
     load_any<B, TILE>(a, S, dA, mA, lane);
     load_any<B, TILE>(a, S, dB, mB, lane);
-    if (all_wave_norm<B, TILE>() && ((const RunHdr *)run_buf(S.desc, a.p0))->has_norm) norm_all(lds, w, lane);
+    if (((const RunHdr *)run_buf(S.desc, a.p0))->has_norm) norm_all(lds, w, lane);
     wg_barrier();  // x-hat of the first phase is ready
     bool ok = abort_flag_get() == 0;
     int32_t p = a.p0;
@@ -551,7 +672,7 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
         if (endA) nblk = 0;
         if (endA && ++p < a.p1) {
             if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
-            if (all_wave_norm<B, TILE>() && ((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
+            if (((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
             wg_barrier();  // x-hat of phase p is ready
             ok = abort_flag_get() == 0;
             if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
@@ -569,7 +690,7 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
         if (endB) nblk = 0;
         if (endB && ++p < a.p1) {
             if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
-            if (all_wave_norm<B, TILE>() && ((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
+            if (((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
             wg_barrier();
             ok = abort_flag_get() == 0;
             if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
@@ -580,8 +701,29 @@ __device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
 // --------------------------------------------------------------- control wave
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *(const u32x4 *)p; }
 
+// Buffer resource over 2 GB from base; a null base gets an empty range, so
+// loads through it return 0 and stores are dropped without a memory access.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base) {
-    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7FFFFFFF, (int)RSRC_W3);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, base ? 0x7FFFFFFF : 0, (int)RSRC_W3);
+}
+
+// A pointer every lane holds the same value of (read from a run list in LDS,
+// which all lanes build alike), moved to scalar registers.  Without this the
+// compiler must assume a per-lane value: a buffer access through it becomes a
+// loop over the distinct values, and a load in such a loop waits for every
+// load issued before it.
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (T *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int32_t uniform_i32(int32_t v) { return (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)v); }
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 #define WGN_GAS __attribute__((address_space(1)))
@@ -601,17 +743,60 @@ __device__ __forceinline__ void copy_to_lds(const uint16_t *src, char *dst, int3
 // LDS bytes of the gain/shift area of one source (gain, then shift; padded).
 __device__ __forceinline__ int32_t prm_bytes(const DevSource &src) { return nchunks_of(src.K) * UNIT * 2 * 2; }
 
-// Issued before the device-wide wait: the norm gains and shifts do not depend
-// on any earlier phase, so their latency overlaps the wait.
+// Issued before the device-wide wait (nothing here depends on an earlier
+// phase, so its latency overlaps the wait): the norm gains and shifts are
+// copied into LDS, and the phase's source table and normalisation job list
+// are written for the steps after the wait, which then read LDS instead of
+// the source descriptors (dependent scalar loads).  Both areas are free: the
+// previous phase's readers passed its x-hat barrier before this call.
 template <bool CHAIN>
-__device__ void prefetch_params(const KArgs &a, const DevPhase &ph, char *prm, uint32_t lane) {
-    int32_t off = 0;
+__device__ void prefetch_params(const KArgs &a, const DevPhase &ph, char *lds, uint32_t lane) {
+    char *prm = lds + ph.prm_off;
+    SrcInfo *T = (SrcInfo *)(lds + LDS_SRC_OFF);
+    NormHdr *J = (NormHdr *)(lds + LDS_NORM_OFF);
+    int32_t off = 0, nj = 0;
     for (int32_t si = 0; si < ph.nsrc; ++si) {
         const DevSource src = source_of<CHAIN>(a, ph.src0 + si);
         const int32_t n8 = src.K >> 3;
-        if (src.norm != NORM_NONE && src.gamma) copy_to_lds<0>(src.gamma, prm + off, n8, lane);
-        if (src.norm == NORM_LAYER && src.beta) copy_to_lds<0>(src.beta, prm + off + prm_bytes(src) / 2, n8, lane);
-        if (src.norm != NORM_NONE) off += prm_bytes(src);
+        const bool normed = src.norm != NORM_NONE;
+        const bool has_gamma = normed && src.gamma != nullptr;
+        const bool has_beta = src.norm == NORM_LAYER && src.beta != nullptr;
+        if (has_gamma) copy_to_lds<0>(src.gamma, prm + off, n8, lane);
+        if (has_beta) copy_to_lds<0>(src.beta, prm + off + prm_bytes(src) / 2, n8, lane);
+        if (lane == 0) {
+            SrcInfo &t = T[si];
+            t.x = src.x;
+            t.x_stride = src.x_stride;
+            t.K = src.K;
+            t.norm = src.norm;
+            t.eps = src.eps;
+            t.lds_off = src.lds_off;
+            t.prm = ph.prm_off + off;
+            t.prm_half = prm_bytes(src) / 2;
+            t.has_gamma = has_gamma;
+            t.has_beta = has_beta;
+            if (normed) {
+                NormJob &jb = J->job[nj];
+                jb.norm = src.norm;
+                jb.K = src.K;
+                jb.xoff = src.lds_off;
+                jb.prm = ph.prm_off + off;
+                jb.prm_half = prm_bytes(src) / 2;
+                jb.eps = src.eps;
+                jb.has_gamma = has_gamma;
+                jb.has_beta = has_beta;
+            }
+        }
+        if (normed) {
+            off += prm_bytes(src);
+            ++nj;
+        }
+    }
+    if (lane == 0) {
+        J->njobs = nj;
+        J->nb = a.nb;
+        J->x_off = ph.x_off;
+        J->xb = ph.xb;
     }
 }
 
@@ -620,131 +805,39 @@ __device__ void prefetch_params(const KArgs &a, const DevPhase &ph, char *prm, u
 // epilogue's bias/residual values, then the statistics and the normalisation
 // run out of LDS.
 template <int B, bool CHAIN>
-__device__ void issue_source_loads(const KArgs &a, const DevPhase &ph, char *xh, uint32_t lane) {
-    const int32_t nb = a.nb;
-    for (int32_t si = 0; si < ph.nsrc; ++si) {
-        const DevSource src = source_of<CHAIN>(a, ph.src0 + si);
-        const int32_t n8 = src.K >> 3;
-        const int32_t padded8 = nchunks_of(src.K) * (UNIT / 8);
+__device__ void issue_source_loads(const KArgs &a, const DevPhase &ph, const char *lds, char *xh, uint32_t lane) {
+    const SrcInfo *T = (const SrcInfo *)(lds + LDS_SRC_OFF);
+    const int32_t nb = a.nb, nsrc = ph.nsrc;
+    // every entry is read at once (one LDS round trip), then the copies issued
+    const uint16_t *x[MAX_SRC];
+    int64_t xs[MAX_SRC];
+    int32_t K[MAX_SRC], lo[MAX_SRC];
+#pragma unroll
+    for (int j = 0; j < MAX_SRC; ++j) {
+        x[j] = T[j].x;
+        xs[j] = T[j].x_stride;
+        K[j] = T[j].K;
+        lo[j] = T[j].lds_off;
+    }
+#pragma unroll
+    for (int j = 0; j < MAX_SRC; ++j) {
+        if (j >= nsrc) break;
+        const uint16_t *src = uniform_ptr(x[j]);
+        const int64_t stride = uniform_i64(xs[j]);
+        const int32_t n8 = uniform_i32(K[j]) >> 3;
+        const int32_t padded8 = nchunks_of(uniform_i32(K[j])) * (UNIT / 8);
+        const int32_t off = uniform_i32(lo[j]);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             if (b >= nb) break;
-            char *dst = xh + ((size_t)b * ph.xb + src.lds_off) * 2;
-            copy_to_lds<COH>(src.x + (int64_t)b * src.x_stride, dst, n8, lane);
+            char *dst = xh + ((size_t)b * ph.xb + off) * 2;
+            copy_to_lds<COH>(src + (int64_t)b * stride, dst, n8, lane);
             for (int32_t i = n8 + lane; i < padded8; i += 64) *(u32x4 *)(dst + i * 16) = (u32x4){0u, 0u, 0u, 0u};
         }
     }
 }
 
-// Vector path: the control wave normalises alone, out of LDS, after the
-// copies have landed.  All batch rows at once: each row gets an aligned group
-// of 64 / P lanes (P = batch rounded up to a power of two) that walks the
-// row's 16-byte chunks and reduces with group_sum_f64.  (The streaming waves
-// do not help here: they hold their in-flight weight blocks in nearly all of
-// their registers, and the compiler would make them wait for those loads.)
-template <int B, bool CHAIN>
-__device__ void finish_sources(const KArgs &a, const DevPhase &ph, char *xh, const char *prm, uint32_t lane) {
-    const int32_t nb = a.nb;
-    const int32_t shift = nb <= 1 ? 0 : 32 - __builtin_clz((uint32_t)(nb - 1));
-    const int32_t lpr = 64 >> shift;                       // lanes per batch row
-    const int32_t row = (int32_t)(lane >> (6 - shift));   // batch row of this lane
-    const int32_t sub = (int32_t)(lane & (uint32_t)(lpr - 1));
-    const bool active = row < nb;
-    int32_t poff = 0;
-    for (int32_t si = 0; si < ph.nsrc; ++si) {
-        const DevSource src = source_of<CHAIN>(a, ph.src0 + si);
-        if (src.norm == NORM_NONE) continue;
-        const int32_t K = src.K;
-        const int32_t n8 = active ? K >> 3 : 0;
-        const char *gp = prm + poff;
-        const char *bp = prm + poff + prm_bytes(src) / 2;
-        poff += prm_bytes(src);
-        uint16_t *dst = (uint16_t *)(xh + ((size_t)(active ? row : 0) * ph.xb + src.lds_off) * 2);
-        // Statistics in FP64: a square of a BF16 value is exact in FP32 and
-        // the FP64 sums are as good as exact, so x-hat carries only the FP32
-        // rounding of its final products and matches a correctly rounded
-        // normalisation except in rare last-bit cases.
-        const bool layer = src.norm == NORM_LAYER;
-        double s1 = 0.0, s2 = 0.0;  // sum (LayerNorm) or sum of squares (RMSNorm)
-        for (int32_t i = sub; i < n8; i += lpr) {
-            const u32x4 v = *(const u32x4 *)(dst + i * 8);
-            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-            double c = 0.0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float lo = bf2f(vv[e] & 0xFFFFu), hi = bf2f(vv[e] >> 16);
-                c += layer ? (double)lo + (double)hi : (double)(lo * lo) + (double)(hi * hi);
-            }
-            if (layer) s1 += c;
-            else s2 += c;
-        }
-        float mean = 0.0f, rstd;
-        if (src.norm == NORM_RMS) {
-            s2 = group_sum_f64(s2, lpr);
-            rstd = (float)(1.0 / sqrt(s2 / (double)K + (double)src.eps));
-        } else {
-            s1 = group_sum_f64(s1, lpr);
-            const double mean64 = s1 / (double)K;
-            double sv = 0.0;
-            for (int32_t i = sub; i < n8; i += lpr) {
-                const u32x4 v = *(const u32x4 *)(dst + i * 8);
-                const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const double lo = (double)bf2f(vv[e] & 0xFFFFu) - mean64, hi = (double)bf2f(vv[e] >> 16) - mean64;
-                    sv += lo * lo + hi * hi;
-                }
-            }
-            sv = group_sum_f64(sv, lpr);
-            mean = (float)mean64;
-            rstd = (float)(1.0 / sqrt(sv / (double)K + (double)src.eps));
-        }
-        for (int32_t i = sub; i < n8; i += lpr) {
-            const u32x4 v = *(const u32x4 *)(dst + i * 8);
-            const u32x4 gv = src.gamma ? *(const u32x4 *)(gp + i * 16)
-                                       : (u32x4){0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-            const u32x4 bv = (src.norm == NORM_LAYER && src.beta) ? *(const u32x4 *)(bp + i * 16)
-                                                                  : (u32x4){0u, 0u, 0u, 0u};
-            const uint32_t vv[4] = {v.x, v.y, v.z, v.w}, gg[4] = {gv.x, gv.y, gv.z, gv.w},
-                           bb[4] = {bv.x, bv.y, bv.z, bv.w};
-            uint32_t o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float lo =
-                    (bf2f(vv[e] & 0xFFFFu) - mean) * rstd * bf2f(gg[e] & 0xFFFFu) + bf2f(bb[e] & 0xFFFFu);
-                const float hi = (bf2f(vv[e] >> 16) - mean) * rstd * bf2f(gg[e] >> 16) + bf2f(bb[e] >> 16);
-                o[e] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
-            }
-            *(u32x4 *)(dst + i * 8) = (u32x4){o[0], o[1], o[2], o[3]};
-        }
-    }
-}
 
-// Post the phase's normalisation jobs for norm_all (one per normalised source).
-template <bool CHAIN>
-__device__ void post_norm_jobs(const KArgs &a, const DevPhase &ph, char *lds, uint32_t lane) {
-    NormHdr *J = (NormHdr *)(lds + LDS_NORM_OFF);
-    if (lane != 0) return;
-    int32_t n = 0, poff = 0;
-    for (int32_t si = 0; si < ph.nsrc; ++si) {
-        const DevSource src = source_of<CHAIN>(a, ph.src0 + si);
-        if (src.norm == NORM_NONE) continue;
-        NormJob &jb = J->job[n++];
-        jb.norm = src.norm;
-        jb.K = src.K;
-        jb.xoff = src.lds_off;
-        jb.prm = ph.prm_off + poff;
-        jb.prm_half = prm_bytes(src) / 2;
-        jb.eps = src.eps;
-        jb.has_gamma = src.gamma != nullptr;
-        jb.has_beta = src.norm == NORM_LAYER && src.beta != nullptr;
-        poff += prm_bytes(src);
-    }
-    J->njobs = n;
-    J->nb = a.nb;
-    J->x_off = ph.x_off;
-    J->xb = ph.xb;
-}
 
 // While the streaming waves stream, stage the epilogue's inputs of this
 // workgroup's rows into LDS.  Row-part rp's record (epi_rec(nb) floats) holds
@@ -754,28 +847,33 @@ template <int B, bool CHAIN>
 __device__ void stage_epilogue_inputs(const KArgs &a, const RunHdr &h, const Run *runs, float *epi, uint32_t lane) {
     const int32_t nb = a.nb;
     const LaneSplit ls = lane_split(nb, lane);
-    for (int32_t ri = 0; ri < h.nruns; ++ri) {
+    const int32_t nruns = uniform_i32(h.nruns);
+    for (int32_t ri = 0; ri < nruns; ++ri) {
         const Run &r = runs[ri];
-        const uint16_t *bias = r.bias;
-        const uint16_t *res = r.residual;
-        const float *pf = r.post_F;
-        if ((!bias && !res && !pf) || (r.carry & CARRY_OUT) || !ls.active) continue;
-        const int64_t res_stride = r.res_stride;
-        const int32_t row0 = r.row0, nrows = r.nrows, rp_base = r.rp_base, parts = r.parts, N = r.N;
-        const uint16_t *pbias = r.post_bias;
-        const __amdgpu_buffer_rsrc_t rr = rsrc_of(res);
-        const __amdgpu_buffer_rsrc_t rf = rsrc_of(pf);
+        const uint16_t *bias = uniform_ptr(r.bias);
+        const uint16_t *res = uniform_ptr(r.residual);
+        const float *pf = uniform_ptr(r.post_F);
+        if ((!bias && !res && !pf) || (uniform_i32(r.carry) & CARRY_OUT) || !ls.active) continue;
+        const int64_t res_stride = uniform_i64(r.res_stride);
+        const int32_t row0 = uniform_i32(r.row0), nrows = uniform_i32(r.nrows), rp_base = uniform_i32(r.rp_base),
+                      parts = uniform_i32(r.parts), N = uniform_i32(r.N);
+        const uint16_t *pbias = uniform_ptr(r.post_bias);
+        const __amdgpu_buffer_rsrc_t rb = rsrc_of(bias), rr = rsrc_of(res), rf = rsrc_of(pf), rpb = rsrc_of(pbias);
         for (int32_t i = ls.i0; i < nrows; i += ls.step) {
             const int32_t n = row0 + i;
             float *e = epi + (size_t)(rp_base + i * parts) * epi_rec(nb);
-            if (ls.b == 0) e[0] = bias ? bf2f(bias[n]) : 0.0f;
-            e[1 + ls.b] = res ? bf2f(__builtin_amdgcn_raw_buffer_load_b16(
-                                    rr, (int)(((int64_t)ls.b * res_stride + n) * 2), 0, COH))
-                              : 0.0f;
-            if (pf)
-                e[1 + nb + ls.b] =
-                    __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rf, (int)(((int64_t)ls.b * N + n) * 4), 0, COH)) +
-                    (pbias ? bf2f(pbias[n]) : 0.0f);
+            // All four loads are issued unconditionally (an absent input has
+            // an empty buffer range and reads 0), so they are in flight
+            // together.  Bias and post bias are constants (cached loads);
+            // residual and addend come from earlier phases (coherent loads).
+            const uint32_t bv = __builtin_amdgcn_raw_buffer_load_b16(rb, n * 2, 0, 0);
+            const uint32_t rv =
+                __builtin_amdgcn_raw_buffer_load_b16(rr, (int)(((int64_t)ls.b * res_stride + n) * 2), 0, COH);
+            const uint32_t fv = __builtin_amdgcn_raw_buffer_load_b32(rf, (int)(((int64_t)ls.b * N + n) * 4), 0, COH);
+            const uint32_t pv = __builtin_amdgcn_raw_buffer_load_b16(rpb, n * 2, 0, 0);
+            if (ls.b == 0) e[0] = bf2f(bv);
+            e[1 + ls.b] = bf2f(rv);
+            if (pf) e[1 + nb + ls.b] = __uint_as_float(fv) + bf2f(pv);
         }
     }
 }
@@ -871,8 +969,8 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
         const Run &r = runs[ri];
         if (r.epi != EPI_ARGMAX) continue;
         const int32_t nrows = ls.active ? r.nrows : 0;
-        const int32_t N = r.N, row0 = r.row0;
-        float *logits = r.logits;
+        const int32_t N = uniform_i32(r.N), row0 = uniform_i32(r.row0);
+        float *logits = uniform_ptr(r.logits);
         uint64_t best = 0;
         for (int32_t i = ls.i0; i < nrows; i += ls.step) {
             const int32_t n = row0 + i;
@@ -904,7 +1002,7 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
             old = __hip_atomic_fetch_add(&a.tickets[am_slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         old = __shfl(old, 0);
         if (old == (uint32_t)(a.G - 1)) {
-            argmax_merge(a, am_slot, r.y, r.maxval, lane);
+            argmax_merge(a, am_slot, uniform_ptr(r.y), uniform_ptr(r.maxval), lane);
             if (lane == 0)
                 __hip_atomic_store(&a.tickets[am_slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -943,7 +1041,6 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
         const DevPhase ph = phase_of<CHAIN>(a, p);
         char *xh = lds + ph.x_off;
         const float *part = (const float *)(lds + ph.part_off);
-        char *prm = lds + ph.prm_off;
         float *epi = (float *)(lds + ph.epi_off);
         float *carry = (float *)(lds + ph.carry_off);
         trace_point(a, p, g, 0, lane);
@@ -953,7 +1050,7 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
         const char *rb = desc + (p % DESC_BUFS) * RUN_BUF_BYTES;
         const RunHdr &h = *(const RunHdr *)rb;  // in LDS (a register copy passed by reference would go to scratch)
         const Run *runs = (const Run *)(rb + sizeof(RunHdr));
-        prefetch_params<CHAIN>(a, ph, prm, lane);
+        prefetch_params<CHAIN>(a, ph, lds, lane);
         if (a.persistent && p > a.p0 && ph.wait) {
             // every workgroup's flag of phase p-1 must carry this run's value
             const __amdgpu_buffer_rsrc_t rf = rsrc_of(a.flags + (size_t)(p - 1) * flag_row(a.G));
@@ -1000,7 +1097,7 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
                 }
                 // meet the streaming waves at this phase's barriers (norm
                 // steps, x-hat); they then see the abort flag and exit
-                if (all_wave_norm<B, TILE>() && h.has_norm) {
+                if (h.has_norm) {
                     wg_barrier();
                     wg_barrier();
                 }
@@ -1009,17 +1106,10 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
             }
         }
         trace_point(a, p, g, 1, lane);
-        issue_source_loads<B, CHAIN>(a, ph, xh, lane);
+        issue_source_loads<B, CHAIN>(a, ph, lds, xh, lane);
         stage_epilogue_inputs<B, CHAIN>(a, h, runs, epi, lane);
         __builtin_amdgcn_s_waitcnt(0);  // inputs, gains and epilogue values have landed
-        if (h.has_norm) {
-            if (all_wave_norm<B, TILE>()) {
-                post_norm_jobs<CHAIN>(a, ph, lds, lane);
-                norm_all(lds, STREAM_WAVES, lane);
-            } else {
-                finish_sources<B, CHAIN>(a, ph, lds + ph.x_off, lds + ph.prm_off, lane);
-            }
-        }
+        if (h.has_norm) norm_all(lds, STREAM_WAVES, lane);
         trace_point(a, p, g, 2, lane);
         wg_barrier();  // x-hat ready
         wg_barrier();  // partials complete

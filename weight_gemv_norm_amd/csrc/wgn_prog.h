@@ -26,6 +26,7 @@
 //    are carried in LDS from one window to the next and only the last window
 //    runs the epilogue.
 #pragma once
+#include <stddef.h>
 #include <stdint.h>
 
 #if defined(__HIPCC__)
@@ -266,8 +267,8 @@ WGN_HD int32_t wgn_clz(uint32_t v) {
 }
 // How nw waves share the normalisation of nb batch rows (padded to a power of
 // two P): a row over one or more whole waves when P <= nw, several rows per
-// wave otherwise.  nw is WAVES when all waves of a workgroup normalise
-// together (matrix-core path), 1 when the control wave does it alone.
+// wave otherwise.  nw (a power of two) is WAVES: all waves of a workgroup
+// normalise together.
 struct NormSplit {
     int32_t row, sub, lanes;   // batch row, lane index inside the row's lanes, lanes per row
     int32_t lpr;               // lanes of this row inside this wave (group_sum width)
@@ -276,30 +277,23 @@ struct NormSplit {
     bool active;
 };
 WGN_HD NormSplit norm_split(int32_t nb, int32_t w, uint32_t lane, int32_t nw) {
+    // nw is a power of two, so every quotient below is a shift.  The two
+    // cases are merged into one branch-free form: up = log2(rows per wave)
+    // (0 when a row spans whole waves), dn = log2(waves per row) (0 when a
+    // wave holds several rows).
     NormSplit S;
-    const int32_t shift = nb <= 1 ? 0 : 32 - wgn_clz((uint32_t)(nb - 1));
-    const int32_t P = 1 << shift;
-    if (P <= nw) {
-        S.row = (w * P) / nw;  // the waves of row r are [ceil(r W / P), ceil((r + 1) W / P))
-        S.w0 = (S.row * nw + P - 1) / P;
-        S.w1 = ((S.row + 1) * nw + P - 1) / P;
-        S.lanes = (S.w1 - S.w0) * 64;
-        S.sub = (w - S.w0) * 64 + (int32_t)lane;
-        S.lpr = 64;
-        S.slot = 0;
-        S.rslot = 0;
-    } else {
-        int32_t rpw = (P + nw - 1) / nw;
-        rpw = 1 << (32 - wgn_clz((uint32_t)(rpw - 1)));
-        S.lpr = 64 / rpw;
-        S.row = w * rpw + (int32_t)lane / S.lpr;
-        S.sub = (int32_t)lane % S.lpr;
-        S.lanes = S.lpr;
-        S.slot = (int32_t)lane / S.lpr;
-        S.w0 = S.row / rpw;
-        S.w1 = S.w0 + 1;
-        S.rslot = S.row % rpw;
-    }
+    const int32_t shift = nb <= 1 ? 0 : 32 - wgn_clz((uint32_t)(nb - 1));  // P = 1 << shift
+    const int32_t lognw = 31 - wgn_clz((uint32_t)nw);
+    const int32_t up = shift > lognw ? shift - lognw : 0;
+    const int32_t dn = shift > lognw ? 0 : lognw - shift;
+    S.lpr = 64 >> up;
+    S.row = ((w << up) >> dn) + (int32_t)(lane >> (6 - up));
+    S.w0 = (S.row >> up) << dn;
+    S.w1 = S.w0 + (1 << dn);
+    S.lanes = (64 >> up) << dn;
+    S.sub = (w - S.w0) * 64 + (int32_t)(lane & (uint32_t)(S.lpr - 1));
+    S.slot = (int32_t)(lane >> (6 - up));
+    S.rslot = S.row & ((1 << up) - 1);
     S.active = S.row < nb;
     return S;
 }
@@ -308,10 +302,27 @@ WGN_HD NormSplit norm_split(int32_t nb, int32_t w, uint32_t lane, int32_t nw) {
 constexpr int LDS_DESC_OFF = 0;
 constexpr int LDS_TRACE_OFF = DESC_BUFS * RUN_BUF_BYTES;
 constexpr int LDS_NORM_OFF = LDS_TRACE_OFF + 2 * 6 * 8;  // 6 streaming-wave timestamps per phase parity
-// partial statistics: [source][wave][batch row of that wave][sum, sum of squares], FP64
-constexpr int STATS_ROWS = 8;        // batch rows one wave may hold (16 rows over at least 2 waves)
+// partial statistics: [wave][normalisation item of that wave][sum, sum of squares], FP64;
+// items are (source, batch row) pairs, at most MAX_SRC * MAX_BATCH = 64 over WAVES waves
+constexpr int STATS_ROWS = 8;        // items one wave may hold
 constexpr int LDS_STATS_OFF = (LDS_NORM_OFF + (int)sizeof(NormHdr) + 15) & ~15;
-constexpr int LDS_DYN_OFF = (LDS_STATS_OFF + MAX_SRC * WAVES * STATS_ROWS * 16 + 255) & ~255;
+// The phase's sources as the control wave uses them after its wait, written
+// by that wave before the wait (one LDS read then replaces dependent scalar
+// loads of the source descriptors on the critical path).
+struct SrcInfo {
+    const uint16_t *x;
+    int64_t x_stride;
+    int32_t K, norm;
+    float eps;
+    int32_t lds_off;       // element offset inside one batch row of x-hat
+    int32_t prm, prm_half; // gain at LDS byte offset prm (the phase's area), shift at prm + prm_half
+    int32_t has_gamma, has_beta;
+};
+static_assert(sizeof(SrcInfo) == 48 && offsetof(SrcInfo, K) == 16 && offsetof(SrcInfo, prm) == 32,
+              "SrcInfo is read as three 16-byte words");
+static_assert(MAX_SRC * MAX_BATCH <= WAVES * STATS_ROWS, "normalisation items must fit the statistics slots");
+constexpr int LDS_SRC_OFF = (LDS_STATS_OFF + WAVES * STATS_ROWS * 16 + 15) & ~15;
+constexpr int LDS_DYN_OFF = (LDS_SRC_OFF + MAX_SRC * (int)sizeof(SrcInfo) + 255) & ~255;
 
 // Per-(WG, stage) geometry inside a phase.
 struct StageSpan {
