@@ -31,8 +31,12 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// 20 units: the larger phase of a decoder layer (Q, K, V, gate/up and the
+// next layer's hoisted O product: about 37 units per wave on 256 workgroups)
+// is then two blocks, both requested before the phase starts (measured on
+// the decode step: 16 and 24 are slower at batch 1 to 4)
 #ifndef WGN_DEPTH
-#define WGN_DEPTH 16
+#define WGN_DEPTH 20
 #endif
 #ifndef WGN_WEIGHT_AUX
 #define WGN_WEIGHT_AUX 2  // nt: weights are streamed once
@@ -494,7 +498,8 @@ __device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4
 // left beside the two in-flight blocks.
 template <int B>
 constexpr int xhat_group() {
-    return (B == 1 && DEPTH % 16 == 0) ? 16 : (B == 2 && DEPTH % 4 == 0) ? 4 : 2;
+    return (B == 1 && DEPTH % 16 == 0 && DEPTH <= 16) ? 16 : (B == 1 && DEPTH % 8 == 0) ? 8
+         : ((B == 1 || B == 2) && DEPTH % 4 == 0) ? 4 : 2;
 }
 
 template <int B>

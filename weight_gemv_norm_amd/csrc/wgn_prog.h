@@ -8,7 +8,7 @@
 //  * row-parts are streamed in "units" of 512 consecutive K elements:
 //      - vector path (batch <= 4): a unit is one row-part's 512 elements =
 //        64 lanes x 16 bytes, one 128-bit load per lane, fully coalesced;
-//        a block of 16 units is 16 independent loads;
+//        a block of DEPTH (20) units is 20 independent loads;
 //      - matrix-core path (any batch, used for batch > 4): a unit is a tile of
 //        16 consecutive row-parts x 512 elements, streamed as 16 loads in
 //        which lane l reads 16 bytes of row l%16 (64 contiguous bytes per row
