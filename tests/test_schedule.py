@@ -5,8 +5,10 @@ workgroup; they meet only at workgroup barriers.  The LDS areas they share are
 written by one side and read by the other between barriers:
 
 * run lists (one LDS buffer per phase, DESC_BUFS buffers in a ring), written by
-  the control wave DESC_AHEAD phases ahead and read by the streaming waves when
-  they issue weight loads (up to two blocks beyond the one they consume);
+  the control wave DESC_AHEAD phases ahead (at the end of an iteration, after
+  its flag store) and read by the streaming waves when they issue weight loads
+  (up to two blocks beyond the one they consume);
+* normalisation jobs, written at the end of the iteration before their phase;
 * x-hat (written by the control wave, read by the streaming waves);
 * partial sums (written by the streaming waves, read by the control wave's
   epilogue).
@@ -52,22 +54,23 @@ class Wave:
 
 
 def control_events(p0, p1, desc_ahead=DESC_AHEAD, norm=None):
-    """The control wave's loop: builds, x-hat writes, partial reads.  norm[p]:
-    phase p has a normalised input, normalised by all waves between two extra
-    barriers (inputs landed; partial statistics written)."""
+    """The control wave's loop: run-list builds, x-hat writes, partial reads.
+    Phase q's run list is written at the end of iteration q - desc_ahead
+    (after the flag store), and a phase's normalisation jobs at the end of the
+    iteration before it; the first ones before the loop.  norm[p]: phase p has
+    a normalised input, normalised by all waves between two extra barriers
+    (inputs landed; partial statistics written)."""
     norm = norm or {}
     c = Wave()
     for q in range(p0, min(p1, p0 + desc_ahead)):
         c.ev("build", q)
+    c.ev("write_job", p0)
     c.barrier()
     for p in range(p0, p1):
-        if p + desc_ahead < p1:
-            c.ev("build", p + desc_ahead)
         c.ev("read_runs", p)       # header and run list of phase p (epilogue inputs)
         c.ev("write_xhat", p)      # raw inputs (and, without a norm, x-hat itself)
         if norm.get(p):
-            c.ev("write_job", p)
-            c.barrier()            # inputs landed, norm job posted
+            c.barrier()            # inputs landed (the jobs were posted earlier)
             c.ev("read_job", p)
             c.ev("write_stats", p)
             c.barrier()            # partial statistics written
@@ -79,6 +82,11 @@ def control_events(p0, p1, desc_ahead=DESC_AHEAD, norm=None):
         c.ev("read_runs", p)
         if EPI_BARRIER:
             c.barrier()            # epilogue stores issued: streaming waves may refill
+        # after the flag store: later lists and the next phase's jobs
+        if p + desc_ahead < p1:
+            c.ev("build", p + desc_ahead)
+        if p + 1 < p1:
+            c.ev("write_job", p + 1)
     return c
 
 
@@ -280,12 +288,13 @@ def test_schedule_launch_window():
 
 
 def test_model_detects_building_too_late():
-    """Two phases of look-ahead into three buffers is too little when a wave
-    walks a one-block phase: the model must flag it."""
-    errs = check_schedule(0, 6, [[1, 1, 1, 1, 1, 1]], desc_bufs=3, desc_ahead=2)
+    """Lists written after the flag store need four phases of look-ahead:
+    three is too little when a wave walks one-block phases, and the model
+    must flag it."""
+    errs = check_schedule(0, 8, [[1] * 8], desc_bufs=4, desc_ahead=3)
     assert any("built in epoch" in e for e in errs), errs
 
 
 def test_model_detects_ring_too_small():
-    errs = check_schedule(0, 8, [[1] * 8], desc_bufs=3, desc_ahead=3)
+    errs = check_schedule(0, 8, [[1] * 8], desc_bufs=3, desc_ahead=4)
     assert any("overwritten" in e for e in errs), errs

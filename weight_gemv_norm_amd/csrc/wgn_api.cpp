@@ -659,7 +659,7 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
 
 struct WsLayout {
     // ctr..am_part is the synchronisation area (flags, run counter, tickets, error word)
-    size_t phases, stages, sources, rowb, ctr, run, tickets, err, am_part, fsum, trace, total;
+    size_t phases, stages, sources, rowb, runimg, phinfo, ctr, run, tickets, err, am_part, fsum, trace, total;
 };
 
 WsLayout ws_layout(const Program &P, bool trace) {
@@ -673,6 +673,10 @@ WsLayout ws_layout(const Program &P, bool trace) {
     o += al256(P.sources.size() * sizeof(DevSource));
     L.rowb = o;
     o += al256(P.rowb.size() * sizeof(int32_t));
+    L.runimg = o;  // every (phase, workgroup) run list, as the kernel would build it
+    o += al256(P.phases.size() * (size_t)P.G * RUN_BUF_STRIDE);
+    L.phinfo = o;  // every phase's source table and normalisation jobs
+    o += al256(P.phases.size() * (size_t)PHASE_INFO_BYTES);
     L.ctr = o;
     o += al256(P.phases.size() * (size_t)flag_row(P.G) * sizeof(uint32_t));
     L.run = o;
@@ -939,6 +943,27 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     std::memcpy(img.data() + c->L.stages, c->P.stages.data(), c->P.stages.size() * sizeof(DevStage));
     std::memcpy(img.data() + c->L.sources, c->P.sources.data(), c->P.sources.size() * sizeof(DevSource));
     std::memcpy(img.data() + c->L.rowb, c->P.rowb.data(), c->P.rowb.size() * sizeof(int32_t));
+    {
+        // Run lists and phase tables are functions of (phase, workgroup)
+        // alone: build them here, with the kernel's own code over the host
+        // copy of the program, instead of on the kernel's critical path.
+        KArgs h;
+        std::memset(&h, 0, sizeof h);
+        h.phases = c->P.phases.data();
+        h.stages = c->P.stages.data();
+        h.sources = c->P.sources.data();
+        h.rowb = c->P.rowb.data();
+        h.G = c->P.G;
+        h.nb = c->P.B;
+        for (int32_t q = 0; q < (int32_t)c->P.phases.size(); ++q) {
+            for (int32_t g = 0; g < c->P.G; ++g) {
+                char *buf = img.data() + c->L.runimg + ((size_t)q * c->P.G + g) * RUN_BUF_STRIDE;
+                make_runs<true>(h, q, g, c->P.tile, *(RunHdr *)buf, (Run *)(buf + sizeof(RunHdr)));
+            }
+            char *pi = img.data() + c->L.phinfo + (size_t)q * PHASE_INFO_BYTES;
+            make_phase_info<true>(h, q, (SrcInfo *)pi, *(NormHdr *)(pi + MAX_SRC * sizeof(SrcInfo)));
+        }
+    }
     hipStream_t s = (hipStream_t)stream;
     char *ws = (char *)workspace;
     if (note(hipMemcpyAsync(ws, img.data(), img.size(), hipMemcpyHostToDevice, s), "chain upload") != hipSuccess ||
@@ -953,6 +978,12 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     a.stages = (const DevStage *)(ws + c->L.stages);
     a.sources = (const DevSource *)(ws + c->L.sources);
     a.rowb = (const int32_t *)(ws + c->L.rowb);
+    // precomputed lists from batch 2 up (at batch 1 the kernel builds them
+    // while it waits for flags that arrive later anyway)
+    if (c->P.B > 1 || c->P.tile) {
+        a.runimg = ws + c->L.runimg;
+        a.phinfo = ws + c->L.phinfo;
+    }
     a.flags = (uint32_t *)(ws + c->L.ctr);
     a.run = (uint32_t *)(ws + c->L.run);
     a.tickets = (uint32_t *)(ws + c->L.tickets);

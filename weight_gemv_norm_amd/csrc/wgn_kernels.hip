@@ -51,6 +51,14 @@ constexpr int WEIGHT_AUX = WGN_WEIGHT_AUX;  // cache policy of the weight loads 
 // is visible to another without L2 write-back/invalidate fences (which cost
 // several microseconds per phase boundary on this chip).
 constexpr int COH = 17;
+#ifndef WGN_POLL_GAP
+#define WGN_POLL_GAP 0
+#endif
+#ifndef WGN_POLL_DELAY
+#define WGN_POLL_DELAY 0
+#endif
+// s_sleep units (64 clocks): between flag-row reads, and before the first
+constexpr int POLL_GAP = WGN_POLL_GAP, POLL_DELAY = WGN_POLL_DELAY;
 constexpr uint32_t RSRC_W3 = 0x00020000u; // buffer descriptor word 3 for raw dword loads
 
 // ------------------------------------------------------------------ numerics
@@ -427,7 +435,7 @@ struct StreamState {
 };
 
 __device__ __forceinline__ const char *run_buf(const char *desc, int32_t p) {
-    return desc + (p % DESC_BUFS) * RUN_BUF_BYTES;
+    return desc + (p % DESC_BUFS) * RUN_BUF_STRIDE;
 }
 
 __device__ __forceinline__ void stream_begin_phase(StreamState &S, int32_t p) {
@@ -630,7 +638,7 @@ __device__ __forceinline__ void consume_any(const KArgs &a, const u32x4 (&d)[blo
 }
 
 template <int B, bool CHAIN, bool TILE>
-__device__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
+__device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
     const uint32_t lane = lane_id();
     StreamState S;
     S.desc = lds + LDS_DESC_OFF;
@@ -749,60 +757,36 @@ __device__ __forceinline__ void copy_to_lds(const uint16_t *src, char *dst, int3
 __device__ __forceinline__ int32_t prm_bytes(const DevSource &src) { return nchunks_of(src.K) * UNIT * 2 * 2; }
 
 // Issued before the device-wide wait (nothing here depends on an earlier
-// phase, so its latency overlaps the wait): the norm gains and shifts are
-// copied into LDS, and the phase's source table and normalisation job list
-// are written for the steps after the wait, which then read LDS instead of
-// the source descriptors (dependent scalar loads).  Both areas are free: the
-// previous phase's readers passed its x-hat barrier before this call.
+// phase, so its latency overlaps the wait): the norm gains and shifts of the
+// phase's normalised sources are copied into their LDS areas, as the phase's
+// source table (already in LDS) lists them.
+__device__ void prefetch_params(const DevPhase &ph, char *lds, uint32_t lane) {
+    const SrcInfo *T = (const SrcInfo *)(lds + LDS_SRC_OFF);
+#pragma unroll
+    for (int32_t si = 0; si < MAX_SRC; ++si) {
+        if (si >= ph.nsrc) break;
+        const int32_t n8 = uniform_i32(T[si].K) >> 3;
+        const uint16_t *gamma = uniform_ptr(T[si].gamma), *beta = uniform_ptr(T[si].beta);
+        char *gp = lds + uniform_i32(T[si].prm);
+        if (gamma) copy_to_lds<0>(gamma, gp, n8, lane);
+        if (beta) copy_to_lds<0>(beta, gp + uniform_i32(T[si].prm_half), n8, lane);
+    }
+}
+
+// The phase's source table and normalisation job list, written to LDS
+// (LDS_SRC_OFF, LDS_NORM_OFF) by the control wave.
 template <bool CHAIN>
-__device__ void prefetch_params(const KArgs &a, const DevPhase &ph, char *lds, uint32_t lane) {
-    char *prm = lds + ph.prm_off;
-    SrcInfo *T = (SrcInfo *)(lds + LDS_SRC_OFF);
-    NormHdr *J = (NormHdr *)(lds + LDS_NORM_OFF);
-    int32_t off = 0, nj = 0;
-    for (int32_t si = 0; si < ph.nsrc; ++si) {
-        const DevSource src = source_of<CHAIN>(a, ph.src0 + si);
-        const int32_t n8 = src.K >> 3;
-        const bool normed = src.norm != NORM_NONE;
-        const bool has_gamma = normed && src.gamma != nullptr;
-        const bool has_beta = src.norm == NORM_LAYER && src.beta != nullptr;
-        if (has_gamma) copy_to_lds<0>(src.gamma, prm + off, n8, lane);
-        if (has_beta) copy_to_lds<0>(src.beta, prm + off + prm_bytes(src) / 2, n8, lane);
-        if (lane == 0) {
-            SrcInfo &t = T[si];
-            t.x = src.x;
-            t.x_stride = src.x_stride;
-            t.K = src.K;
-            t.norm = src.norm;
-            t.eps = src.eps;
-            t.lds_off = src.lds_off;
-            t.prm = ph.prm_off + off;
-            t.prm_half = prm_bytes(src) / 2;
-            t.has_gamma = has_gamma;
-            t.has_beta = has_beta;
-            if (normed) {
-                NormJob &jb = J->job[nj];
-                jb.norm = src.norm;
-                jb.K = src.K;
-                jb.xoff = src.lds_off;
-                jb.prm = ph.prm_off + off;
-                jb.prm_half = prm_bytes(src) / 2;
-                jb.eps = src.eps;
-                jb.has_gamma = has_gamma;
-                jb.has_beta = has_beta;
-            }
-        }
-        if (normed) {
-            off += prm_bytes(src);
-            ++nj;
-        }
+__device__ void write_phase_info(const KArgs &a, int32_t p, char *lds, uint32_t lane) {
+    if (CHAIN && a.phinfo) {
+        // precomputed (the table, then the jobs): asynchronous copies
+        constexpr int32_t nt = MAX_SRC * (int)sizeof(SrcInfo);
+        const uint16_t *src = (const uint16_t *)(a.phinfo + (size_t)p * PHASE_INFO_BYTES);
+        copy_to_lds<0>(src, lds + LDS_SRC_OFF, nt / 16, lane);
+        copy_to_lds<0>(src + nt / 2, lds + LDS_NORM_OFF, (int)sizeof(NormHdr) / 16, lane);
+        return;
     }
-    if (lane == 0) {
-        J->njobs = nj;
-        J->nb = a.nb;
-        J->x_off = ph.x_off;
-        J->xb = ph.xb;
-    }
+    // every lane computes the same tables
+    make_phase_info<CHAIN>(a, p, (SrcInfo *)(lds + LDS_SRC_OFF), *(NormHdr *)(lds + LDS_NORM_OFF));
 }
 
 // Staging of the phase's inputs as BF16 x-hat in LDS (FP32 statistics): all
@@ -1014,34 +998,84 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
     }
 }
 
-// Write phase q's run list for workgroup g into its LDS buffer.
+// Write phase q's run list for workgroup g into its LDS buffer: a copy of the
+// precomputed list for chains (asynchronous: memory to LDS), else built here.
 template <bool CHAIN, bool TILE>
-__device__ void build_runs(const KArgs &a, int32_t q, int32_t g, char *desc) {
+__device__ void build_runs(const KArgs &a, int32_t q, int32_t g, char *desc, uint32_t lane) {
+    char *buf = desc + (q % DESC_BUFS) * RUN_BUF_STRIDE;
+    if (CHAIN && a.runimg) {
+        copy_to_lds<0>((const uint16_t *)(a.runimg + ((size_t)q * a.G + g) * RUN_BUF_STRIDE), buf, RUN_BUF_STRIDE / 16,
+                       lane);
+        return;
+    }
     // every lane computes the same list; the runs go straight into LDS
     // the header is built in place too: its tables are indexed at run time,
     // which a register copy could only do through scratch memory
-    char *buf = desc + (q % DESC_BUFS) * RUN_BUF_BYTES;
     make_runs<CHAIN>(a, q, g, TILE, *(RunHdr *)buf, (Run *)(buf + sizeof(RunHdr)));
 }
 
+// A later phase's precomputed run list and phase info, read into registers
+// while the streaming waves consume and written to LDS after the flag store.
+constexpr int RL_CHUNKS = RUN_BUF_STRIDE / 16, PI_CHUNKS = PHASE_INFO_BYTES / 16;
+static_assert(RL_CHUNKS <= 128 && PI_CHUNKS <= 64, "two reads per lane for a run list, one for a phase info");
+struct AheadRegs {
+    u32x4 rl0, rl1, pi;
+};
+__device__ __forceinline__ void ahead_load(const KArgs &a, int32_t q_rl, int32_t q_pi, int32_t g, uint32_t lane,
+                                           AheadRegs &r) {
+    if (q_rl < a.p1) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.runimg + ((size_t)q_rl * a.G + g) * RUN_BUF_STRIDE), (short)0, RUN_BUF_STRIDE, (int)RSRC_W3);
+        r.rl0 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(lane * 16), 0, 0);
+        r.rl1 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)((64 + lane) * 16), 0, 0);  // past the end: 0
+    }
+    if (q_pi < a.p1) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.phinfo + (size_t)q_pi * PHASE_INFO_BYTES), (short)0, PHASE_INFO_BYTES, (int)RSRC_W3);
+        r.pi = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(lane * 16), 0, 0);
+    }
+}
+__device__ __forceinline__ void ahead_store(const KArgs &a, int32_t q_rl, int32_t q_pi, char *lds, uint32_t lane,
+                                            const AheadRegs &r) {
+    if (q_rl < a.p1) {
+        char *buf = lds + LDS_DESC_OFF + (q_rl % DESC_BUFS) * RUN_BUF_STRIDE;
+        *(u32x4 *)(buf + lane * 16) = r.rl0;
+        if ((int32_t)lane + 64 < RL_CHUNKS) *(u32x4 *)(buf + (64 + lane) * 16) = r.rl1;
+    }
+    if (q_pi < a.p1 && (int32_t)lane < PI_CHUNKS) {
+        constexpr int32_t nt = MAX_SRC * (int)sizeof(SrcInfo) / 16;
+        char *dst = (int32_t)lane < nt ? lds + LDS_SRC_OFF + lane * 16 : lds + LDS_NORM_OFF + (lane - nt) * 16;
+        *(u32x4 *)dst = r.pi;
+    }
+}
+
 template <int B, bool CHAIN, bool TILE>
-__device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
+__device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *lds) {
     const uint32_t lane = lane_id();
     char *desc = lds + LDS_DESC_OFF;
     if (lane == 0) abort_flag_set(0);
     if (a.trace && lane < 12) ((uint64_t *)(lds + LDS_TRACE_OFF))[lane] = 0;
     const uint32_t flag_val =
         a.persistent ? __hip_atomic_load(a.run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
-    // Run lists are built DESC_AHEAD (3) phases ahead into DESC_BUFS (4) LDS
-    // buffers.  A streaming wave keeps two blocks in flight beyond the one it
+    // Run lists: phase q's list is written at the end of iteration
+    // q - DESC_AHEAD (4), after the flag store, into one of DESC_BUFS (4) LDS
+    // buffers (the one phase q - 4 used, which every wave has finished with by
+    // then).  A streaming wave keeps two blocks in flight beyond the one it
     // consumes, so right after phase q's partials barrier it may load phase
-    // q+2's block and read phase q+3's list header; iteration q builds that
-    // list before its own x-hat barrier of phase q.  A buffer is rebuilt
-    // (iteration q rebuilds phase q-1's) only after every wave has passed the
-    // partials barrier of the phase it held.  (This schedule is modelled and
-    // checked on the host by tests/test_schedule.py.)
-    for (int32_t q = a.p0; q < a.p1 && q < a.p0 + DESC_AHEAD; ++q) build_runs<CHAIN, TILE>(a, q, g, desc);
+    // q+2's block and read phase q+3's list header; that list was written
+    // before the x-hat barrier of phase q.  A phase's source table and
+    // normalisation jobs are written at the end of the iteration before it.
+    // (This schedule is modelled and checked on the host by
+    // tests/test_schedule.py.)  From batch 2 up, chains read precomputed
+    // lists and tables into registers while the streaming waves consume, so
+    // none of this is on the path between a phase's flags and its x-hat; at
+    // batch 1 the flags arrive later than the lists are built here, and the
+    // reads would only add latency to the flag stores.
+    for (int32_t q = a.p0; q < a.p1 && q < a.p0 + DESC_AHEAD; ++q) build_runs<CHAIN, TILE>(a, q, g, desc, lane);
+    write_phase_info<CHAIN>(a, a.p0, lds, lane);
+    __builtin_amdgcn_s_waitcnt(0);  // copied lists and tables have landed
     wg_barrier();
+    const bool pre = CHAIN && a.runimg && a.phinfo;
     for (int32_t p = a.p0; p < a.p1; ++p) {
         const DevPhase ph = phase_of<CHAIN>(a, p);
         char *xh = lds + ph.x_off;
@@ -1049,18 +1083,18 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
         float *epi = (float *)(lds + ph.epi_off);
         float *carry = (float *)(lds + ph.carry_off);
         trace_point(a, p, g, 0, lane);
-        // descriptors, run lists and gains do not depend on the previous
-        // phase: prepare them before waiting for it
-        if (p + DESC_AHEAD < a.p1) build_runs<CHAIN, TILE>(a, p + DESC_AHEAD, g, desc);
-        const char *rb = desc + (p % DESC_BUFS) * RUN_BUF_BYTES;
+        const char *rb = desc + (p % DESC_BUFS) * RUN_BUF_STRIDE;
         const RunHdr &h = *(const RunHdr *)rb;  // in LDS (a register copy passed by reference would go to scratch)
         const Run *runs = (const Run *)(rb + sizeof(RunHdr));
-        prefetch_params<CHAIN>(a, ph, lds, lane);
+        // the gains do not depend on the previous phase: request them before
+        // waiting for it
+        prefetch_params(ph, lds, lane);
         if (a.persistent && p > a.p0 && ph.wait) {
             // every workgroup's flag of phase p-1 must carry this run's value
             const __amdgpu_buffer_rsrc_t rf = rsrc_of(a.flags + (size_t)(p - 1) * flag_row(a.G));
             const uint64_t t0 = wall_clock64();
             bool timed_out = false;
+            if (POLL_DELAY > 0) __builtin_amdgcn_s_sleep(POLL_DELAY);
             if (FLAG_WORDS == 1) {
                 for (;;) {
                     bool ok = true;
@@ -1075,6 +1109,9 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
                         timed_out = true;
                         break;
                     }
+                    // every workgroup polls the same few lines: spacing the
+                    // reads out keeps them from slowing the flag stores
+                    if (POLL_GAP > 0) __builtin_amdgcn_s_sleep(POLL_GAP);
                 }
             } else {
                 // lane l watches flags l, l + 64, ... and re-reads only those
@@ -1117,6 +1154,9 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
         if (h.has_norm) norm_all(lds, STREAM_WAVES, lane);
         trace_point(a, p, g, 2, lane);
         wg_barrier();  // x-hat ready
+        // later phases' run list and tables, read while the streaming waves consume
+        AheadRegs ahead;
+        if (pre) ahead_load(a, p + DESC_AHEAD, p + 1, g, lane, ahead);
         wg_barrier();  // partials complete
         trace_point(a, p, g, 3, lane);
         if (a.trace && lane < 6) {
@@ -1137,6 +1177,12 @@ __device__ void control_wave(const KArgs &a, int32_t g, char *lds) {
         }
         if (EPI_BARRIER == 2) wg_barrier();  // flag issued too
         trace_point(a, p, g, 5, lane);
+        if (pre) {
+            ahead_store(a, p + DESC_AHEAD, p + 1, lds, lane, ahead);
+        } else {
+            if (p + DESC_AHEAD < a.p1) build_runs<CHAIN, TILE>(a, p + DESC_AHEAD, g, desc, lane);
+            if (p + 1 < a.p1) write_phase_info<CHAIN>(a, p + 1, lds, lane);
+        }
     }
     if (a.persistent) {
         // The last workgroup to finish advances the run counter, so the next

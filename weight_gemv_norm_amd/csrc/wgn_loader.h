@@ -155,6 +155,75 @@ struct UnitDesc {
 };
 
 // Descriptor of WG-local unit v from a run list (the form the kernel uses).
+// A phase's source table (as the control wave uses it) and normalisation job
+// list (read by every wave), in source order; every normalised source gets
+// its gain (and shift) area in the phase's parameter area, in order.
+template <bool CHAIN>
+WGN_HD void make_phase_info(const KArgs &a, int32_t p, SrcInfo *T, NormHdr &J) {
+    const DevPhase ph = phase_of<CHAIN>(a, p);
+    int32_t off = 0, nj = 0;
+    for (int32_t si = 0; si < MAX_SRC; ++si) {
+        SrcInfo t;
+        t.x = nullptr;
+        t.x_stride = 0;
+        t.K = 0;
+        t.norm = NORM_NONE;
+        t.eps = 0.0f;
+        t.lds_off = 0;
+        t.prm = ph.prm_off;
+        t.prm_half = 0;
+        t.has_gamma = 0;
+        t.has_beta = 0;
+        t.gamma = nullptr;
+        t.beta = nullptr;
+        if (si < ph.nsrc) {
+            const DevSource src = source_of<CHAIN>(a, ph.src0 + si);
+            const bool normed = src.norm != NORM_NONE;
+            const int32_t pb = nchunks_of(src.K) * UNIT * 2 * 2;  // gain and shift, padded
+            t.x = src.x;
+            t.x_stride = src.x_stride;
+            t.K = src.K;
+            t.norm = src.norm;
+            t.eps = src.eps;
+            t.lds_off = src.lds_off;
+            t.prm = ph.prm_off + off;
+            t.prm_half = pb / 2;
+            t.has_gamma = normed && src.gamma != nullptr;
+            t.has_beta = src.norm == NORM_LAYER && src.beta != nullptr;
+            t.gamma = t.has_gamma ? src.gamma : nullptr;
+            t.beta = t.has_beta ? src.beta : nullptr;
+            if (normed) {
+                NormJob &jb = J.job[nj++];
+                jb.norm = src.norm;
+                jb.K = src.K;
+                jb.xoff = src.lds_off;
+                jb.prm = t.prm;
+                jb.prm_half = t.prm_half;
+                jb.eps = src.eps;
+                jb.has_gamma = t.has_gamma;
+                jb.has_beta = t.has_beta;
+                off += pb;
+            }
+        }
+        T[si] = t;
+    }
+    for (int32_t j = nj; j < MAX_SRC; ++j) {
+        NormJob &jb = J.job[j];
+        jb.norm = NORM_NONE;
+        jb.K = 0;
+        jb.xoff = 0;
+        jb.prm = 0;
+        jb.prm_half = 0;
+        jb.eps = 0.0f;
+        jb.has_gamma = 0;
+        jb.has_beta = 0;
+    }
+    J.njobs = nj;
+    J.nb = a.nb;
+    J.x_off = ph.x_off;
+    J.xb = ph.xb;
+}
+
 WGN_HD UnitDesc unit_desc_runs(const RunHdr &h, const Run *runs, int32_t v, int32_t u_beg, int32_t u_end,
                                int32_t w, int32_t B) {
     UnitDesc d;

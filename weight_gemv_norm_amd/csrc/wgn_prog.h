@@ -51,7 +51,7 @@ constexpr int TILE_ROWS = 16;        // row-parts per matrix-core unit
 constexpr int TRACE_POINTS = 12;
 constexpr int MAX_RUNS = 8;          // stages per phase (the planner splits larger phases)
 constexpr int DESC_BUFS = 4;         // phases whose run lists are resident in LDS at once
-constexpr int DESC_AHEAD = 3;        // the control wave builds phase p+DESC_AHEAD's list in iteration p
+constexpr int DESC_AHEAD = 4;        // the control wave writes phase p+DESC_AHEAD's list at the end of iteration p
 #ifndef WGN_EPI_BARRIER
 #define WGN_EPI_BARRIER 1
 #endif
@@ -137,6 +137,8 @@ struct KArgs {
     uint64_t *am_part;     // [n_argmax][G][batch] packed (value, index) keys
     uint32_t *err;         // error word
     uint64_t *trace;       // [nphases][G][TRACE_POINTS] timestamps, or null
+    const char *runimg;    // chains: [nphases][G] run lists, RUN_BUF_STRIDE bytes each (built on the host)
+    const char *phinfo;    // chains: [nphases] phase infos, PHASE_INFO_BYTES each (built on the host)
     int32_t p0, p1;        // phases of this launch
     int32_t persistent;
     int32_t G;
@@ -220,7 +222,12 @@ struct RunHdr {
     int32_t pad1;
     int32_t wb[STREAM_WAVES + 1];      // wave_begin(w) for w = 0..STREAM_WAVES
     int32_t rstart[MAX_RUNS + 1];      // first WG-local output row of each run (cumulative nrows)
+    int32_t pad2;                      // the runs that follow the header start 8-byte aligned
 };
+// Run lists are built on the host for chains and copied into LDS as bytes, so
+// the host and device compilations must agree on the layout.
+static_assert(sizeof(Run) == 160 && alignof(Run) == 8, "Run layout");
+static_assert(sizeof(RunHdr) == 104, "RunHdr layout");
 // Floats per row-part in the staged epilogue inputs: bias, then the residual
 // of each batch row, then the addend of a fused residual add per batch row.
 WGN_HD int32_t epi_rec(int32_t nb) { return 1 + 2 * nb; }
@@ -233,6 +240,9 @@ WGN_HD int32_t first_wave_hdr(const RunHdr &h, int32_t u) {
     return w;
 }
 constexpr int RUN_BUF_BYTES = (int)(sizeof(RunHdr) + MAX_RUNS * sizeof(Run));
+// stride of the LDS run-list buffers and of the precomputed run lists (whole
+// 16-byte chunks: they are copied 16 bytes per lane)
+constexpr int RUN_BUF_STRIDE = (RUN_BUF_BYTES + 15) & ~15;
 // Fixed part of the dynamic LDS: the run-list ring, then six streaming-wave
 // trace timestamps.  The per-phase areas (x-hat, partials, gains, epilogue
 // inputs, K-window carry) follow at offsets the plan gives each phase; areas
@@ -300,7 +310,7 @@ WGN_HD NormSplit norm_split(int32_t nb, int32_t w, uint32_t lane, int32_t nw) {
 
 
 constexpr int LDS_DESC_OFF = 0;
-constexpr int LDS_TRACE_OFF = DESC_BUFS * RUN_BUF_BYTES;
+constexpr int LDS_TRACE_OFF = DESC_BUFS * RUN_BUF_STRIDE;
 constexpr int LDS_NORM_OFF = LDS_TRACE_OFF + 2 * 6 * 8;  // 6 streaming-wave timestamps per phase parity
 // partial statistics: [wave][normalisation item of that wave][sum, sum of squares], FP64;
 // items are (source, batch row) pairs, at most MAX_SRC * MAX_BATCH = 64 over WAVES waves
@@ -317,9 +327,17 @@ struct SrcInfo {
     int32_t lds_off;       // element offset inside one batch row of x-hat
     int32_t prm, prm_half; // gain at LDS byte offset prm (the phase's area), shift at prm + prm_half
     int32_t has_gamma, has_beta;
+    const uint16_t *gamma; // null unless has_gamma
+    const uint16_t *beta;  // null unless has_beta
 };
-static_assert(sizeof(SrcInfo) == 48 && offsetof(SrcInfo, K) == 16 && offsetof(SrcInfo, prm) == 32,
-              "SrcInfo is read as three 16-byte words");
+static_assert(sizeof(SrcInfo) == 64 && offsetof(SrcInfo, K) == 16 && offsetof(SrcInfo, prm) == 32,
+              "SrcInfo is read as 16-byte words");
+static_assert(sizeof(NormHdr) == 144, "NormHdr layout");
+// A phase's source table and normalisation job list, as one image (the
+// source table, then the job list): precomputed for chains, copied to
+// LDS_SRC_OFF and LDS_NORM_OFF.
+constexpr int PHASE_INFO_BYTES = MAX_SRC * (int)sizeof(SrcInfo) + (int)sizeof(NormHdr);
+static_assert(PHASE_INFO_BYTES % 16 == 0 && PHASE_INFO_BYTES <= 64 * 16, "phase info fits one 16-byte read per lane");
 static_assert(MAX_SRC * MAX_BATCH <= WAVES * STATS_ROWS, "normalisation items must fit the statistics slots");
 constexpr int LDS_SRC_OFF = (LDS_STATS_OFF + WAVES * STATS_ROWS * 16 + 15) & ~15;
 constexpr int LDS_DYN_OFF = (LDS_SRC_OFF + MAX_SRC * (int)sizeof(SrcInfo) + 255) & ~255;
