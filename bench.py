@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
                     help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a run with "
                          "--calib-copy-mib into the traffic summary that later runs report; no GPU used")
+    ap.add_argument("--prefetch", default="none", choices=["none", "tune"],
+                    help="with --mode 1: tune an Infinity-Cache prefetch plan (touch passes on a second "
+                         "stream, wgn_plan_tune) before timing, and time the plan it keeps")
+    ap.add_argument("--tune-reps", type=int, default=15, help="rounds of the prefetch tuner")
     ap.add_argument("--cold", action="store_true",
                     help="stream a 512 MB scrub buffer between timed steps (evicts the Infinity Cache)")
     return ap.parse_args()
@@ -126,6 +130,20 @@ def main():
         kernel_name = "rmsnorm_rows_kernel"
 
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+
+    if args.prefetch == "tune":
+        if chain is None or args.mode != 1:
+            print("bench.py: --prefetch tune needs a chain workload and --mode 1", file=sys.stderr)
+            sys.exit(2)
+        side = torch.cuda.Stream()
+        plan = chain.tune_plan(side, reps=args.tune_reps)
+        cfg["prefetch_plan"] = {"kept": bool(plan.prefetch), "distance": plan.distance, "blocks": plan.blocks,
+                                "frac_pct": plan.frac_pct, "plain_us": round(plan.plain_us, 3),
+                                "best_candidate_us": round(plan.best_us, 3),
+                                "speedup_ci95_lo": round(plan.speedup_lo, 4), "candidates": plan.candidates,
+                                "tune_reps": args.tune_reps}
+        print("[bench] prefetch plan: %s" % cfg["prefetch_plan"], file=sys.stderr, flush=True)
+        launch = (lambda: chain.run(plan=plan, side=side)) if plan.prefetch else chain.run  # noqa: E731
 
     # -------------------------------------------------------------- warm up
     for _ in range(args.warmup):

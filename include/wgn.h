@@ -227,6 +227,51 @@ wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t ba
                            const wgn_chain_opts *opts, void *workspace, size_t ws_bytes,
                            wgn_stream stream);
 
+/* -------------------------------------------------------- prefetch plans */
+/* Optional prefetch of later launches' weights into the GPU's memory-side
+ * Infinity Cache by a touch pass on a second stream, for chains created with
+ * one launch per phase (opts.mode = 1).  While launch i runs on `stream`, the
+ * pass reads the leading frac_pct % of every weight matrix of launch
+ * i + distance on `side`, with `blocks` workgroups of 256 threads ("Making
+ * small PyTorch ops faster on a laptop GPU", section "Prefetching the next
+ * layer while this one runs").  The pass only reads, so a run's outputs are
+ * bit-identical with and without a plan.  A persistent chain (mode 0) issues
+ * its next phases' weight loads from inside its kernel and takes no plan. */
+typedef struct wgn_plan {
+    int32_t prefetch;   /* 0: plain run (other fields ignored); 1: touch pass    */
+    int32_t distance;   /* launches ahead, 1..4                                   */
+    int32_t blocks;     /* workgroups of the touch pass, 1..1024                  */
+    int32_t frac_pct;   /* leading share of each weight matrix touched, 1..100    */
+    float plain_us;     /* set by wgn_plan_tune: mean time of a plain run         */
+    float best_us;      /* set by wgn_plan_tune: mean time of the best candidate  */
+    float speedup_lo;   /* set by wgn_plan_tune: lower end of the 95 % confidence */
+                        /* interval of (plain time / best candidate's time)       */
+    int32_t candidates; /* set by wgn_plan_tune: candidates measured              */
+} wgn_plan;
+
+/* Enqueue one run of a chain with a plan (no host synchronisation).  With
+ * prefetch = 1 the run forks `side` off `stream` before each launch (event
+ * record + wait) and ends with `stream` waiting for `side`, so later work on
+ * `stream` sees the whole run.  The weight ranges of each launch are laid out
+ * in the workspace by wgn_chain_create (at most 16 matrices per launch).
+ * Errors: WGN_E_ARG for a null chain or plan, fields out of range, or a null
+ * `side` or side == stream when prefetch = 1; WGN_E_UNSUPPORTED for a mode-0
+ * chain with prefetch = 1; WGN_E_HIP if a launch or event call fails. */
+wgn_status wgn_chain_run_plan(const wgn_chain *chain, const wgn_plan *plan, wgn_stream stream, wgn_stream side);
+
+/* Time plain runs of a mode-1 chain against the touch-pass candidates
+ * (distance 1 and 2, blocks 16, 64 and 256, frac 50 and 100 %) in `reps`
+ * interleaved rounds (3..200), and write the plan to keep: the candidate with
+ * the best mean speedup if the lower end of its 95 % confidence interval
+ * clears 1.01, else prefetch = 0 with the closest candidate's settings and
+ * figures ("Making small PyTorch ops faster on a laptop GPU", section
+ * "Measuring instead of predicting": one plan per chain here, timed on the
+ * chain's own weights).  Synchronises `stream`; the runs overwrite the
+ * chain's outputs.  Not for the hot loop.  Errors: WGN_E_ARG (null chain or
+ * out, reps out of range, null or equal streams), WGN_E_UNSUPPORTED (mode-0
+ * chain), WGN_E_HIP. */
+wgn_status wgn_plan_tune(const wgn_chain *chain, wgn_stream stream, wgn_stream side, int32_t reps, wgn_plan *out);
+
 /* --------------------------------------------------------- host helpers */
 /* The first wave of `waves` whose even share of `units` work units contains
  * unit `u` (exported so the partition rule can be tested on the host). */

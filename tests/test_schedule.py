@@ -24,6 +24,8 @@ import os
 import random
 import re
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
@@ -35,10 +37,17 @@ def header_constant(name):
 
 
 DESC_BUFS = header_constant("DESC_BUFS")
-DESC_AHEAD = header_constant("DESC_AHEAD")
+DESC_AHEAD = DESC_BUFS  # wgn_prog.h: DESC_AHEAD = WGN_DESC_BUFS
 # 1 if the streaming waves refill only after the control wave has issued the
 # epilogue's stores (a third barrier per phase)
 EPI_BARRIER = header_constant("EPI_BARRIER")
+# block buffers per streaming wave (vector path; the matrix-core path uses 2)
+SLOTS = header_constant("SLOTS")
+# 1 if the vector path issues a consumed block's refill while consuming the
+# next block: the run list is read when the refill is prepared, right after the
+# block is consumed (the same point as a burst refill without the third
+# barrier), and the loads themselves read no LDS
+INTERLEAVE = header_constant("INTERLEAVE")
 
 
 class Wave:
@@ -53,7 +62,7 @@ class Wave:
         self.events.append((self.epoch, kind, phase))
 
 
-def control_events(p0, p1, desc_ahead=DESC_AHEAD, norm=None):
+def control_events(p0, p1, desc_ahead=DESC_AHEAD, norm=None, epi_barrier=EPI_BARRIER):
     """The control wave's loop: run-list builds, x-hat writes, partial reads.
     Phase q's run list is written at the end of iteration q - desc_ahead
     (after the flag store), and a phase's normalisation jobs at the end of the
@@ -80,7 +89,7 @@ def control_events(p0, p1, desc_ahead=DESC_AHEAD, norm=None):
         c.barrier()                # partials complete
         c.ev("read_part", p)       # epilogue
         c.ev("read_runs", p)
-        if EPI_BARRIER:
+        if epi_barrier:
             c.barrier()            # epilogue stores issued: streaming waves may refill
         # after the flag store: later lists and the next phase's jobs
         if p + desc_ahead < p1:
@@ -90,24 +99,12 @@ def control_events(p0, p1, desc_ahead=DESC_AHEAD, norm=None):
     return c
 
 
-def stream_events(p0, p1, nblocks, norm=None):
-    """One streaming wave's loop with two blocks in flight.  nblocks[p] >= 1 is
+def stream_events(p0, p1, nblocks, norm=None, epi_barrier=EPI_BARRIER, slots=2):
+    """One streaming wave's loop with a ring of `slots` block buffers.  nblocks[p] >= 1 is
     the number of blocks the wave walks in phase p (an empty share is one empty
     block)."""
     norm = norm or {}
     s = Wave()
-
-    def norm_steps(p):
-        # before the x-hat barrier of phase p: the phase's header says whether
-        # the waves normalise together
-        s.ev("read_runs", p)
-        if norm.get(p):
-            s.barrier()
-            s.ev("read_job", p)
-            s.ev("write_stats", p)
-            s.barrier()
-            s.ev("read_stats", p)
-            s.ev("write_xhat", p)
 
     class St:
         pass
@@ -135,6 +132,18 @@ def stream_events(p0, p1, nblocks, norm=None):
                 S.done = True
         return ("blk", p, last)
 
+    def phase_start(p):
+        """Norm steps (if any) and the x-hat barrier of phase p."""
+        s.ev("read_runs", p)       # the phase's header: normalised input?
+        if norm.get(p):
+            s.barrier()            # inputs landed, jobs posted
+            s.ev("read_job", p)
+            s.ev("write_stats", p)
+            s.barrier()
+            s.ev("read_stats", p)
+            s.ev("write_xhat", p)
+        s.barrier()                # x-hat of phase p
+
     def consume(blk):
         kind, p, last = blk
         if kind == "blk":
@@ -143,43 +152,31 @@ def stream_events(p0, p1, nblocks, norm=None):
 
     s.barrier()                    # run lists of the first phases are in LDS
     begin_phase(p0)
-    A = load_block()
-    Bb = load_block()
-    norm_steps(p0)
-    s.barrier()                    # x-hat of the first phase
+    ring = [load_block() for _ in range(slots)]
+    phase_start(p0)
     p = p0
     ok = True
     while ok and p < p1:
-        consume(A)
-        endA = A[2]
-        if endA:
-            s.barrier()            # partials of phase p
-            if EPI_BARRIER:
-                s.barrier()        # epilogue stores of phase p issued
-        A = load_block()
-        if endA:
-            p += 1
-            if p < p1:
-                norm_steps(p)
-                s.barrier()        # x-hat of phase p
-        consume(Bb)
-        endB = Bb[2]
-        if endB:
-            s.barrier()
-            if EPI_BARRIER:
-                s.barrier()
-        Bb = load_block()
-        if endB:
-            p += 1
-            if p < p1:
-                norm_steps(p)
-                s.barrier()
+        for i in range(slots):
+            consume(ring[i])
+            end = ring[i][2]
+            if end:
+                s.barrier()        # partials of phase p
+                if epi_barrier:
+                    s.barrier()    # epilogue stores of phase p issued
+            ring[i] = load_block()
+            if end:
+                p += 1
+                if p < p1:
+                    phase_start(p)
     return s
 
 
-def check_schedule(p0, p1, nblocks, desc_bufs=DESC_BUFS, desc_ahead=DESC_AHEAD, norm=None):
-    c = control_events(p0, p1, desc_ahead, norm)
-    waves = [stream_events(p0, p1, nb, norm) for nb in nblocks]
+def check_schedule(p0, p1, nblocks, desc_bufs=DESC_BUFS, desc_ahead=DESC_AHEAD, norm=None,
+                   slots=SLOTS, interleave=INTERLEAVE):
+    epi = 0 if interleave else EPI_BARRIER
+    c = control_events(p0, p1, desc_ahead, norm, epi_barrier=epi)
+    waves = [stream_events(p0, p1, nb, norm, epi_barrier=epi, slots=slots) for nb in nblocks]
     errors = []
     for s in waves:
         if s.epoch != c.epoch:
@@ -278,6 +275,39 @@ def test_schedule_with_all_wave_norm():
         norm = {p: rng.random() < 0.6 for p in range(P)}
         errs = check_schedule(0, P, nb, norm=norm)
         assert not errs, (P, nb, norm, errs[:3])
+
+
+@pytest.mark.parametrize("slots", [2, 3, 4, 5])
+def test_schedule_slots_with_matching_ring(slots):
+    """A ring of DESC_BUFS = slots + 2 run lists, written that many phases
+    ahead, covers a wave with `slots` block buffers."""
+    rng = random.Random(7 + slots)
+    for _ in range(800):
+        P = rng.randint(1, 12)
+        W = rng.randint(1, 7)
+        nb = [[rng.choice([1, 1, 1, 2, 3, 5]) for _ in range(P)] for _ in range(W)]
+        norm = {p: rng.random() < 0.6 for p in range(P)}
+        errs = check_schedule(0, P, nb, desc_bufs=slots + 2, desc_ahead=slots + 2, norm=norm, slots=slots,
+                              interleave=0)
+        assert not errs, (P, nb, norm, errs[:3])
+
+
+@pytest.mark.parametrize("slots", [3, 4, 5])
+def test_schedule_interleaved_refills(slots):
+    rng = random.Random(11 + slots)
+    for _ in range(800):
+        P = rng.randint(1, 12)
+        W = rng.randint(1, 7)
+        nb = [[rng.choice([1, 1, 1, 2, 3, 5]) for _ in range(P)] for _ in range(W)]
+        norm = {p: rng.random() < 0.6 for p in range(P)}
+        errs = check_schedule(0, P, nb, desc_bufs=slots + 2, desc_ahead=slots + 2, norm=norm, slots=slots,
+                              interleave=1)
+        assert not errs, (P, nb, norm, errs[:3])
+
+
+def test_model_detects_short_ring_for_more_slots():
+    errs = check_schedule(0, 10, [[1] * 10], desc_bufs=4, desc_ahead=4, slots=4)
+    assert any("built in epoch" in e or "overwritten" in e for e in errs), errs
 
 
 def test_schedule_launch_window():

@@ -42,6 +42,12 @@ class ChainOpts(ctypes.Structure):
                 ("reserved", I32 * 3)]
 
 
+class Plan(ctypes.Structure):
+    """Mirror of wgn_plan."""
+    _fields_ = [("prefetch", I32), ("distance", I32), ("blocks", I32), ("frac_pct", I32),
+                ("plain_us", F32), ("best_us", F32), ("speedup_lo", F32), ("candidates", I32)]
+
+
 class WgnError(RuntimeError):
     def __init__(self, status: int, what: str):
         msg = "%s failed: %s (%d)" % (what, status_string(status), status)
@@ -85,6 +91,8 @@ def lib() -> ctypes.CDLL:
         "wgn_chain_stage_phases": ([P, ctypes.POINTER(I32)], I32),
         "wgn_chain_destroy": ([P], None),
         "wgn_layer_chain": ([SP, I32, I32, OP, P, SZ, P], I32),
+        "wgn_chain_run_plan": ([P, ctypes.POINTER(Plan), P, P], I32),
+        "wgn_plan_tune": ([P, P, P, I32, ctypes.POINTER(Plan)], I32),
         "wgn_first_wave_of_unit": ([I32, I32, I32], I32),
         "wgn_partition_selftest": ([SP, I32, I32, OP], I32),
         "wgn_plan_phases": ([SP, I32, I32, OP, ctypes.POINTER(I32)], I32),

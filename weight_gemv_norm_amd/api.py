@@ -13,7 +13,7 @@ import torch
 
 from . import _lib as L
 from ._lib import (EPI_ARGMAX, EPI_GELU_TANH, EPI_NONE, EPI_SWIGLU, NORM_LAYER,  # noqa: F401
-                   NORM_NONE, NORM_RMS, BF16, FP16, ChainOpts, Stage, WgnError)
+                   NORM_NONE, NORM_RMS, BF16, FP16, ChainOpts, Plan, Stage, WgnError)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -156,8 +156,21 @@ class Chain:
         L.check(st, "wgn_chain_create")
         self._h = h
 
-    def run(self, stream=None) -> None:
-        L.check(L.lib().wgn_chain_run(self._h, _stream(stream)), "wgn_chain_run")
+    def run(self, stream=None, plan: Optional[Plan] = None, side=None) -> None:
+        """One pass; with a prefetch plan (mode-1 chains), touch passes run on `side`."""
+        if plan is None:
+            L.check(L.lib().wgn_chain_run(self._h, _stream(stream)), "wgn_chain_run")
+        else:
+            L.check(L.lib().wgn_chain_run_plan(self._h, ctypes.byref(plan), _stream(stream),
+                                               _stream(side) if side is not None else None),
+                    "wgn_chain_run_plan")
+
+    def tune_plan(self, side, reps: int = 15, stream=None) -> Plan:
+        """wgn_plan_tune: measure prefetch candidates against plain runs."""
+        out = Plan()
+        L.check(L.lib().wgn_plan_tune(self._h, _stream(stream), _stream(side), reps, ctypes.byref(out)),
+                "wgn_plan_tune")
+        return out
 
     def check(self, stream=None) -> None:
         L.check(L.lib().wgn_chain_check(self._h, _stream(stream)), "wgn_chain_check")

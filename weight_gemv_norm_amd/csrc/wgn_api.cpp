@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -20,6 +21,7 @@ namespace wgn {
 hipError_t launch_chain(int32_t batch, bool tile, const KArgs &a, int32_t grid, size_t lds, hipStream_t s);
 hipError_t launch_rmsnorm_rows(const uint16_t *x, int64_t xs, const uint16_t *g, float eps, uint16_t *y, int64_t ys,
                                int32_t rows, int32_t K, bool f16, hipStream_t s);
+hipError_t launch_touch(const TouchRange *r, int32_t n, uint32_t frac_q16, int32_t blocks, hipStream_t s);
 }  // namespace wgn
 
 using namespace wgn;
@@ -659,7 +661,7 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
 
 struct WsLayout {
     // ctr..am_part is the synchronisation area (flags, run counter, tickets, error word)
-    size_t phases, stages, sources, rowb, runimg, phinfo, ctr, run, tickets, err, am_part, fsum, trace, total;
+    size_t phases, stages, sources, rowb, runimg, phinfo, touch, ctr, run, tickets, err, am_part, fsum, trace, total;
 };
 
 WsLayout ws_layout(const Program &P, bool trace) {
@@ -677,6 +679,8 @@ WsLayout ws_layout(const Program &P, bool trace) {
     o += al256(P.phases.size() * (size_t)P.G * RUN_BUF_STRIDE);
     L.phinfo = o;  // every phase's source table and normalisation jobs
     o += al256(P.phases.size() * (size_t)PHASE_INFO_BYTES);
+    L.touch = o;   // weight ranges of every launch group, for a prefetch plan's touch pass
+    o += al256(P.phases.size() * (size_t)MAX_TOUCH * sizeof(TouchRange));
     L.ctr = o;
     o += al256(P.phases.size() * (size_t)flag_row(P.G) * sizeof(uint32_t));
     L.run = o;
@@ -772,6 +776,15 @@ struct wgn_chain {
     size_t lds;
     void *ws;
     WsLayout L;
+    // mode 1: first phase of each launch, the number of weight ranges its
+    // touch pass reads (table in the workspace), and the events that fork a
+    // plan's touch passes off the main stream and join them back
+    std::vector<int32_t> launch0, touch_n;
+    std::vector<hipEvent_t> ev;
+    ~wgn_chain() {
+        for (hipEvent_t e : ev)
+            if (e) (void)hipEventDestroy(e);
+    }
 };
 
 namespace {
@@ -964,6 +977,35 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
             make_phase_info<true>(h, q, (SrcInfo *)pi, *(NormHdr *)(pi + MAX_SRC * sizeof(SrcInfo)));
         }
     }
+    // launch groups (mode 1) and the distinct weight matrices each reads
+    for (int32_t p = 0; p < (int32_t)c->P.phases.size(); p = c->P.group_end[p]) {
+        const int32_t li = (int32_t)c->launch0.size();
+        c->launch0.push_back(p);
+        TouchRange *t = (TouchRange *)(img.data() + c->L.touch) + (size_t)li * MAX_TOUCH;
+        int32_t n = 0;
+        for (int32_t q = p; q < c->P.group_end[p]; ++q) {
+            const DevPhase &ph = c->P.phases[q];
+            for (int32_t si = ph.stage0; si < ph.stage0 + ph.nstages; ++si) {
+                const DevStage &st = c->P.stages[si];
+                const uint64_t bytes = (uint64_t)st.N * (uint64_t)st.K * 2u;
+                for (const uint16_t *w : {st.W, st.W_up}) {
+                    if (!w || bytes == 0) continue;
+                    bool seen = false;
+                    for (int32_t k = 0; k < n; ++k) seen |= t[k].p == (const void *)w;
+                    if (!seen && n < MAX_TOUCH) t[n++] = TouchRange{(const void *)w, bytes};
+                }
+            }
+        }
+        c->touch_n.push_back(n);
+    }
+    if (c->mode == 1) {
+        c->ev.assign(c->launch0.size() + 1, nullptr);
+        for (hipEvent_t &e : c->ev)
+            if (note(hipEventCreateWithFlags(&e, hipEventDisableTiming), "plan events") != hipSuccess) {
+                delete c;
+                return WGN_E_HIP;
+            }
+    }
     hipStream_t s = (hipStream_t)stream;
     char *ws = (char *)workspace;
     if (note(hipMemcpyAsync(ws, img.data(), img.size(), hipMemcpyHostToDevice, s), "chain upload") != hipSuccess ||
@@ -1016,6 +1058,148 @@ wgn_status wgn_chain_run(const wgn_chain *c, wgn_stream stream) {
         a.p1 = c->P.group_end[p];
         hipError_t e = note(launch_chain(c->P.B, c->P.tile, a, c->P.G, c->lds, s), "chain phase launch");
         if (e != hipSuccess) return WGN_E_HIP;
+    }
+    return WGN_OK;
+}
+
+namespace {
+bool plan_fields_ok(const wgn_plan &pl) {
+    if (pl.prefetch < 0 || pl.prefetch > 1) return false;
+    if (!pl.prefetch) return true;
+    return pl.distance >= 1 && pl.distance <= 4 && pl.blocks >= 1 && pl.blocks <= 1024 && pl.frac_pct >= 1 &&
+           pl.frac_pct <= 100;
+}
+}  // namespace
+
+wgn_status wgn_chain_run_plan(const wgn_chain *c, const wgn_plan *plan, wgn_stream stream, wgn_stream side) {
+    if (!c || !plan || !plan_fields_ok(*plan)) return WGN_E_ARG;
+    if (!plan->prefetch) return wgn_chain_run(c, stream);
+    if (c->mode != 1) return WGN_E_UNSUPPORTED;
+    if (!side || side == stream) return WGN_E_ARG;
+    hipStream_t s = (hipStream_t)stream, sd = (hipStream_t)side;
+    const TouchRange *tab = (const TouchRange *)((const char *)c->ws + c->L.touch);
+    const uint32_t frac = (uint32_t)(((uint64_t)plan->frac_pct << 16) / 100u);
+    const int32_t nl = (int32_t)c->launch0.size(), d = plan->distance;
+    KArgs a = c->a;
+    bool forked = false;
+    for (int32_t li = 0; li < nl; ++li) {
+        // while launch li runs, the side stream reads launch li+d's weights;
+        // it starts once everything before launch li is done
+        if (li + d < nl && c->touch_n[li + d] > 0) {
+            if (note(hipEventRecord(c->ev[li], s), "plan fork") != hipSuccess ||
+                note(hipStreamWaitEvent(sd, c->ev[li], 0), "plan fork wait") != hipSuccess ||
+                note(launch_touch(tab + (size_t)(li + d) * MAX_TOUCH, c->touch_n[li + d], frac, plan->blocks, sd),
+                     "touch launch") != hipSuccess)
+                return WGN_E_HIP;
+            forked = true;
+        }
+        a.p0 = c->launch0[li];
+        a.p1 = c->P.group_end[a.p0];
+        if (note(launch_chain(c->P.B, c->P.tile, a, c->P.G, c->lds, s), "chain phase launch") != hipSuccess)
+            return WGN_E_HIP;
+    }
+    if (forked && (note(hipEventRecord(c->ev[nl], sd), "plan join") != hipSuccess ||
+                   note(hipStreamWaitEvent(s, c->ev[nl], 0), "plan join wait") != hipSuccess))
+        return WGN_E_HIP;
+    return WGN_OK;
+}
+
+namespace {
+// Two-sided 95 % Student t quantile for df degrees of freedom.
+double t975(int df) {
+    static const double t[] = {12.706, 4.303, 3.182, 2.776, 2.571, 2.447, 2.365, 2.306, 2.262, 2.228,
+                               2.201,  2.179, 2.160, 2.145, 2.131, 2.120, 2.110, 2.101, 2.093, 2.086,
+                               2.080,  2.074, 2.069, 2.064, 2.060, 2.056, 2.052, 2.048, 2.045, 2.042};
+    if (df < 1) return 1e9;
+    if (df <= 30) return t[df - 1];
+    return df <= 60 ? 2.000 : df <= 120 ? 1.980 : 1.960;
+}
+}  // namespace
+
+wgn_status wgn_plan_tune(const wgn_chain *c, wgn_stream stream, wgn_stream side, int32_t reps, wgn_plan *out) {
+    if (!c || !out || reps < 3 || reps > 200) return WGN_E_ARG;
+    if (c->mode != 1) return WGN_E_UNSUPPORTED;
+    if (!side || side == stream) return WGN_E_ARG;
+    std::vector<wgn_plan> cand;
+    wgn_plan plain{};
+    cand.push_back(plain);
+    for (int32_t d : {1, 2})
+        for (int32_t blocks : {16, 64, 256})
+            for (int32_t frac : {50, 100}) {
+                wgn_plan p{};
+                p.prefetch = 1;
+                p.distance = d;
+                p.blocks = blocks;
+                p.frac_pct = frac;
+                cand.push_back(p);
+            }
+    const size_t nc = cand.size();
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (note(hipEventCreate(&e0), "tune events") != hipSuccess) return WGN_E_HIP;
+    if (note(hipEventCreate(&e1), "tune events") != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return WGN_E_HIP;
+    }
+    std::vector<std::vector<double>> t(nc, std::vector<double>((size_t)reps, 0.0));
+    wgn_status st = WGN_OK;
+    for (int32_t w = 0; w < 2 && st == WGN_OK; ++w) st = wgn_chain_run(c, stream);  // warm-up
+    if (st == WGN_OK) st = wgn_chain_run_plan(c, &cand[1], stream, side);
+    for (int32_t r = 0; r < reps && st == WGN_OK; ++r) {
+        // every round times each candidate once, in a rotated order, so
+        // slow drifts of the clock or the memory affect all of them alike
+        for (size_t k = 0; k < nc && st == WGN_OK; ++k) {
+            const size_t ci = (k + (size_t)r) % nc;
+            float ms = 0.0f;
+            if (note(hipEventRecord(e0, s), "tune record") != hipSuccess) st = WGN_E_HIP;
+            if (st == WGN_OK) st = wgn_chain_run_plan(c, &cand[ci], stream, side);
+            if (st == WGN_OK && (note(hipEventRecord(e1, s), "tune record") != hipSuccess ||
+                                 note(hipEventSynchronize(e1), "tune sync") != hipSuccess ||
+                                 note(hipEventElapsedTime(&ms, e0, e1), "tune elapsed") != hipSuccess))
+                st = WGN_E_HIP;
+            t[ci][(size_t)r] = ms * 1000.0;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (st != WGN_OK) return st;
+    // speedup of candidate k in round r: plain time / candidate time (paired
+    // by round); keep the best mean only if its 95 % interval clears +1 %
+    double plain_mean = 0.0;
+    for (double v : t[0]) plain_mean += v;
+    plain_mean /= reps;
+    size_t best = 0;
+    double best_mean = 0.0, best_lo = 0.0, best_us = plain_mean;
+    for (size_t k = 1; k < nc; ++k) {
+        double m = 0.0, ss = 0.0, us = 0.0;
+        for (int32_t r = 0; r < reps; ++r) {
+            m += t[0][(size_t)r] / t[k][(size_t)r];
+            us += t[k][(size_t)r];
+        }
+        m /= reps;
+        for (int32_t r = 0; r < reps; ++r) {
+            const double dv = t[0][(size_t)r] / t[k][(size_t)r] - m;
+            ss += dv * dv;
+        }
+        const double sd = std::sqrt(ss / (reps - 1));
+        const double lo = m - t975(reps - 1) * sd / std::sqrt((double)reps);
+        if (best == 0 || m > best_mean) {
+            best = k;
+            best_mean = m;
+            best_lo = lo;
+            best_us = us / reps;
+        }
+    }
+    *out = best_lo > 1.01 ? cand[best] : plain;
+    out->plain_us = (float)plain_mean;
+    out->best_us = (float)best_us;
+    out->speedup_lo = (float)best_lo;
+    out->candidates = (int32_t)(nc - 1);
+    if (!(best_lo > 1.01)) {
+        // report which candidate came closest, with prefetch left off
+        out->distance = cand[best].distance;
+        out->blocks = cand[best].blocks;
+        out->frac_pct = cand[best].frac_pct;
     }
     return WGN_OK;
 }

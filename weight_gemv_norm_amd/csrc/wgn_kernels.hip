@@ -467,9 +467,14 @@ __device__ __forceinline__ void stream_advance(StreamState &S, BlockMeta &bm, in
 // v_readlane.  Invalid slots load from an empty range (no memory traffic,
 // value 0), so every block issues the same number of loads and the
 // compiler's vmcnt bookkeeping stays exact.
+// Per-lane unit addresses of a block whose loads have not been issued yet
+// (lane j: unit j), so that they can be issued one by one later.
+struct PendLoads {
+    uint32_t plo, phi, nb;
+};
+
 template <int B>
-__device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4 (&d)[DEPTH], BlockMeta &bm,
-                                           uint32_t lane) {
+__device__ __forceinline__ PendLoads prepare_block(const KArgs &a, StreamState &S, BlockMeta &bm, uint32_t lane) {
     UnitDesc ud;
     ud.ptr = 0;
     ud.nbytes = 0;
@@ -477,21 +482,34 @@ __device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4
     if (!S.done_all && lane < (uint32_t)DEPTH)
         ud = unit_desc_runs(S.h, S.runs, S.u + (int32_t)lane, S.u_beg, S.u_end, S.w, B);
     if (ud.nbytes == 0) ud.ptr = (uint64_t)(uintptr_t)a.ist.W;
-    const uint32_t plo = (uint32_t)ud.ptr, phi = (uint32_t)(ud.ptr >> 32);
+    PendLoads q;
+    q.plo = (uint32_t)ud.ptr;
+    q.phi = (uint32_t)(ud.ptr >> 32);
+    q.nb = ud.nbytes;
     bm.meta_v = ud.meta;
     bm.xb_bytes = S.done_all ? 0 : S.h.xb_bytes;
     bm.x_off = S.h.x_off;
     bm.part_off = S.h.part_off;
-#pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-        const uint32_t lo = __builtin_amdgcn_readlane(plo, j);
-        const uint32_t hi = __builtin_amdgcn_readlane(phi, j);
-        const uint32_t nb = __builtin_amdgcn_readlane(ud.nbytes, j);
-        const void *base = (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
-        __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)nb, (int)RSRC_W3);
-        d[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(lane * 16u), 0, WEIGHT_AUX);
-    }
     stream_advance(S, bm, DEPTH);
+    return q;
+}
+
+// Load unit j of a prepared block: 16 bytes per lane, 1 KB per wave.
+__device__ __forceinline__ u32x4 issue_unit(const PendLoads &q, int j, uint32_t lane) {
+    const uint32_t lo = __builtin_amdgcn_readlane(q.plo, j);
+    const uint32_t hi = __builtin_amdgcn_readlane(q.phi, j);
+    const uint32_t nb = __builtin_amdgcn_readlane(q.nb, j);
+    const void *base = (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)nb, (int)RSRC_W3);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)(lane * 16u), 0, WEIGHT_AUX);
+}
+
+template <int B>
+__device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4 (&d)[DEPTH], BlockMeta &bm,
+                                           uint32_t lane) {
+    const PendLoads q = prepare_block<B>(a, S, bm, lane);
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) d[j] = issue_unit(q, j, lane);
 }
 
 // Every slot of a block is consumed unconditionally (an invalid slot holds
@@ -510,9 +528,13 @@ constexpr int xhat_group() {
          : ((B == 1 || B == 2) && DEPTH % 4 == 0) ? 4 : 2;
 }
 
-template <int B>
+// IL: while consuming, also issue the loads of a prepared block q into dn,
+// one per consumed unit (after each group's x-hat reads), so that the compute
+// unit's memory pipeline receives a steady trickle instead of a burst.
+template <int B, bool IL = false>
 __device__ __forceinline__ void consume_block(const u32x4 (&d)[DEPTH], const BlockMeta &bm, float (&acc)[B],
-                                              const char *lds, uint32_t lane) {
+                                              const char *lds, uint32_t lane, const PendLoads *q = nullptr,
+                                              u32x4 *dn = nullptr) {
     constexpr int G = xhat_group<B>();
     static_assert(DEPTH % G == 0, "block depth must be a multiple of the x-hat group");
     const char *xh = lds + bm.x_off + lane * 16u;
@@ -526,6 +548,10 @@ __device__ __forceinline__ void consume_block(const u32x4 (&d)[DEPTH], const Blo
             const char *xp = xh + ((m & 0x3FFFu) << 4);
 #pragma unroll
             for (int b = 0; b < B; ++b) xv[j][b] = *(const u32x4 *)(xp + b * bm.xb_bytes);
+        }
+        if constexpr (IL) {
+#pragma unroll
+            for (int j = 0; j < G; ++j) dn[g0 + j] = issue_unit(*q, g0 + j, lane);
         }
 #pragma unroll
         for (int j = 0; j < G; ++j) {
@@ -637,8 +663,25 @@ __device__ __forceinline__ void consume_any(const KArgs &a, const u32x4 (&d)[blo
     else consume_block<B>(d, bm, acc.v, lds, lane);
 }
 
-template <int B, bool CHAIN, bool TILE>
-__device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
+template <bool TILE>
+constexpr int stream_slots() { return TILE ? 2 : SLOTS; }
+
+// Whether the streaming waves hold a phase's last refill until the control
+// wave has issued the phase's stores (a third barrier per phase).
+template <bool TILE>
+constexpr bool epi_barrier() { return EPI_BARRIER != 0 && (TILE || !INTERLEAVE); }
+
+// Vector path with interleaved refills.  Slot k's refill is prepared (run
+// list read, addresses computed) right after slot k is consumed and issued,
+// one load per unit, while slot k+1 is consumed; SLOTS - 2 blocks are fully
+// in flight beyond the one being consumed, plus the one being issued.  At a
+// phase end the prepared refill waits for the next phase's x-hat barrier, so
+// the control wave's stores, flag store, flag polls and input loads meet an
+// idle memory pipeline.
+template <int B, bool CHAIN>
+__device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_t w, char *lds) {
+    constexpr int NS = SLOTS;
+    static_assert(NS >= 2, "at least two block buffers");
     const uint32_t lane = lane_id();
     StreamState S;
     S.desc = lds + LDS_DESC_OFF;
@@ -648,23 +691,16 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
     S.done_all = false;
     wg_barrier();  // run lists of the first phases are in LDS
     stream_begin_phase(S, a.p0);
-    u32x4 dA[block_loads<TILE>()], dB[block_loads<TILE>()];
-    BlockMeta mA, mB;
-    Acc<B, TILE> acc;
-    acc.zero();
-
-    // Two blocks are always in flight: a buffer is refilled as soon as it has
-    // been consumed.  When a block ends a phase, the refill is issued before
-    // waiting for the next phase's x-hat, so the weight stream keeps running
-    // through the device-wide phase boundary, and the first block of the next
-    // phase (loaded long before) is consumed as soon as x-hat is ready.
-    // The loop has no early exit and no global stores: past the final phase
-    // it only meets empty blocks (no barriers, no partial writes), which keeps
-    // the compiler's vmcnt bookkeeping exact.
+    u32x4 d[NS][DEPTH];
+    BlockMeta m[NS];
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = 0.0f;
     uint64_t *tl = (uint64_t *)(lds + LDS_TRACE_OFF);  // trace slots
     const bool tw = a.trace && w == 0 && lane == 0;
-    load_any<B, TILE>(a, S, dA, mA, lane);
-    load_any<B, TILE>(a, S, dB, mB, lane);
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k) load_block<B>(a, S, d[k], m[k], lane);
+    PendLoads pq = prepare_block<B>(a, S, m[NS - 1], lane);
     if (((const RunHdr *)run_buf(S.desc, a.p0))->has_norm) norm_all(lds, w, lane);
     wg_barrier();  // x-hat of the first phase is ready
     bool ok = abort_flag_get() == 0;
@@ -672,41 +708,86 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
     if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
     int32_t nblk = 0;  // blocks of phase p consumed (trace only)
     while (ok && p < a.p1) {
-        consume_any<B, TILE>(a, dA, mA, acc, lds, lane);
-        if (tw && nblk < 3) tl[(p & 1) * 6 + 3 + nblk] = wall_clock64();
-        ++nblk;
-        const bool endA = mA.last;
-        if (endA) {
-            if (tw) tl[(p & 1) * 6 + 2] = wall_clock64();
-            wg_barrier();  // partials of phase p are complete
-            if (EPI_BARRIER) wg_barrier();  // the control wave has issued phase p's stores
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            consume_block<B, true>(d[k], m[k], acc, lds, lane, &pq, d[(k + NS - 1) % NS]);
+            if (tw && nblk < 3) tl[(p & 1) * 6 + 3 + nblk] = wall_clock64();
+            ++nblk;
+            const bool end = ok && m[k].last;
+            if (end) {
+                if (tw) tl[(p & 1) * 6 + 2] = wall_clock64();
+                wg_barrier();  // partials of phase p are complete
+            }
+            pq = prepare_block<B>(a, S, m[k], lane);
+            if (end) nblk = 0;
+            if (end && ++p < a.p1) {
+                if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
+                if (((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
+                wg_barrier();  // x-hat of phase p is ready
+                ok = abort_flag_get() == 0;
+                if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
+            }
         }
-        load_any<B, TILE>(a, S, dA, mA, lane);
-        if (endA) nblk = 0;
-        if (endA && ++p < a.p1) {
-            if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
-            if (((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
-            wg_barrier();  // x-hat of phase p is ready
-            ok = abort_flag_get() == 0;
-            if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
-        }
-        consume_any<B, TILE>(a, dB, mB, acc, lds, lane);
-        if (tw && nblk < 3) tl[(p & 1) * 6 + 3 + nblk] = wall_clock64();
-        ++nblk;
-        const bool endB = ok && mB.last;
-        if (endB) {
-            if (tw) tl[(p & 1) * 6 + 2] = wall_clock64();
-            wg_barrier();
-            if (EPI_BARRIER) wg_barrier();
-        }
-        load_any<B, TILE>(a, S, dB, mB, lane);
-        if (endB) nblk = 0;
-        if (endB && ++p < a.p1) {
-            if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
-            if (((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
-            wg_barrier();
-            ok = abort_flag_get() == 0;
-            if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
+    }
+}
+
+template <int B, bool CHAIN, bool TILE>
+__device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
+    constexpr int NS = stream_slots<TILE>();
+    const uint32_t lane = lane_id();
+    StreamState S;
+    S.desc = lds + LDS_DESC_OFF;
+    S.g = g;
+    S.w = w;
+    S.p1 = a.p1;
+    S.done_all = false;
+    wg_barrier();  // run lists of the first phases are in LDS
+    stream_begin_phase(S, a.p0);
+    u32x4 d[NS][block_loads<TILE>()];
+    BlockMeta m[NS];
+    Acc<B, TILE> acc;
+    acc.zero();
+
+    // A ring of NS block buffers: NS - 1 blocks are always in flight beyond the
+    // one being consumed, and a buffer is refilled as soon as it has been
+    // consumed.  When a block ends a phase, the refill is issued before
+    // waiting for the next phase's x-hat, so the weight stream keeps running
+    // through the device-wide phase boundary, and the next phase's first
+    // blocks (loaded long before) are consumed as soon as x-hat is ready.
+    // The loop has no early exit and no global stores: past the final phase
+    // it only meets empty blocks (no barriers, no partial writes), which keeps
+    // the compiler's vmcnt bookkeeping exact.
+    uint64_t *tl = (uint64_t *)(lds + LDS_TRACE_OFF);  // trace slots
+    const bool tw = a.trace && w == 0 && lane == 0;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) load_any<B, TILE>(a, S, d[k], m[k], lane);
+    if (((const RunHdr *)run_buf(S.desc, a.p0))->has_norm) norm_all(lds, w, lane);
+    wg_barrier();  // x-hat of the first phase is ready
+    bool ok = abort_flag_get() == 0;
+    int32_t p = a.p0;
+    if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
+    int32_t nblk = 0;  // blocks of phase p consumed (trace only)
+    while (ok && p < a.p1) {
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            consume_any<B, TILE>(a, d[k], m[k], acc, lds, lane);
+            if (tw && nblk < 3) tl[(p & 1) * 6 + 3 + nblk] = wall_clock64();
+            ++nblk;
+            const bool end = ok && m[k].last;
+            if (end) {
+                if (tw) tl[(p & 1) * 6 + 2] = wall_clock64();
+                wg_barrier();  // partials of phase p are complete
+                if (epi_barrier<TILE>()) wg_barrier();  // the control wave has issued phase p's stores
+            }
+            load_any<B, TILE>(a, S, d[k], m[k], lane);
+            if (end) nblk = 0;
+            if (end && ++p < a.p1) {
+                if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
+                if (((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
+                wg_barrier();  // x-hat of phase p is ready
+                ok = abort_flag_get() == 0;
+                if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
+            }
         }
     }
 }
@@ -1166,7 +1247,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
         }
         epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane);
         trace_point(a, p, g, 4, lane);
-        if (EPI_BARRIER == 1) wg_barrier();  // stores issued: the streaming waves may refill
+        if (epi_barrier<TILE>() && EPI_BARRIER == 1) wg_barrier();  // stores issued: the streaming waves may refill
         if (a.persistent) {
             // outputs are written through (coherent stores); once they have
             // completed, publish this workgroup's flag for phase p
@@ -1175,7 +1256,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
                 __builtin_amdgcn_raw_buffer_store_b32(flag_val, rsrc_of(a.flags + (size_t)p * flag_row(a.G)),
                                                       g * FLAG_WORDS * 4, 0, COH);
         }
-        if (EPI_BARRIER == 2) wg_barrier();  // flag issued too
+        if (epi_barrier<TILE>() && EPI_BARRIER == 2) wg_barrier();  // flag issued too
         trace_point(a, p, g, 5, lane);
         if (pre) {
             ahead_store(a, p + DESC_AHEAD, p + 1, lds, lane, ahead);
@@ -1205,8 +1286,41 @@ __global__ __launch_bounds__(THREADS, 1) void chain_kernel(KArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int32_t g = blockIdx.x;
     const int32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (w < STREAM_WAVES) stream_wave<B, CHAIN, TILE>(a, g, w, lds);
+    if (w < STREAM_WAVES) {
+        if constexpr (!TILE && INTERLEAVE) stream_wave_il<B, CHAIN>(a, g, w, lds);
+        else stream_wave<B, CHAIN, TILE>(a, g, w, lds);
+    }
     else control_wave<B, CHAIN, TILE>(a, g, lds);
+}
+
+// ------------------------------------------------------------- touch pass
+// Optional prefetch of a later launch's weights into the memory-side
+// Infinity Cache (256 MB), run on a second stream while the current launch
+// streams its own weights: the side-stream prefetch of "Making small PyTorch
+// ops faster on a laptop GPU", section "Prefetching the next layer while this
+// one runs", with the GPU's last-level cache in the place of L2.  Plain
+// (allocating) 128-bit loads of the leading frac_q16 / 65536 of every range;
+// the values only meet in a register, so the pass writes no memory at all.
+__global__ __launch_bounds__(256) void touch_kernel(const TouchRange *r, int32_t n, uint32_t frac_q16) {
+    const uint64_t nt = (uint64_t)gridDim.x * 256;
+    const uint64_t tid = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t acc = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const TouchRange t = r[i];
+        const uint64_t n16 = ((t.bytes >> 4) * frac_q16) >> 16;
+        const u32x4 *q = (const u32x4 *)t.p;
+        uint64_t j = tid;
+        for (; j + 3 * nt < n16; j += 4 * nt) {
+            const u32x4 v0 = q[j], v1 = q[j + nt], v2 = q[j + 2 * nt], v3 = q[j + 3 * nt];
+            acc ^= (v0.x ^ v0.y ^ v0.z ^ v0.w) ^ (v1.x ^ v1.y ^ v1.z ^ v1.w) ^ (v2.x ^ v2.y ^ v2.z ^ v2.w) ^
+                   (v3.x ^ v3.y ^ v3.z ^ v3.w);
+        }
+        for (; j < n16; j += nt) {
+            const u32x4 v = q[j];
+            acc ^= v.x ^ v.y ^ v.z ^ v.w;
+        }
+    }
+    __asm__ volatile("" ::"v"(acc));  // keeps the loads; nothing is stored
 }
 
 // ------------------------------------------------------- standalone norm rows
@@ -1326,6 +1440,11 @@ static hipError_t launch_chain_c(int32_t batch, bool tile, const KArgs &a, int32
 hipError_t launch_chain(int32_t batch, bool tile, const KArgs &a, int32_t grid, size_t lds, hipStream_t s) {
     return a.phases ? launch_chain_c<true>(batch, tile, a, grid, lds, s)
                     : launch_chain_c<false>(batch, tile, a, grid, lds, s);
+}
+
+hipError_t launch_touch(const TouchRange *r, int32_t n, uint32_t frac_q16, int32_t blocks, hipStream_t s) {
+    hipLaunchKernelGGL(touch_kernel, dim3(blocks), dim3(256), 0, s, r, n, frac_q16);
+    return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm_rows(const uint16_t *x, int64_t xs, const uint16_t *g, float eps, uint16_t *y, int64_t ys,

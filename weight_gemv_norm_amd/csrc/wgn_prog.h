@@ -50,8 +50,6 @@ constexpr int MAX_BATCH_VALU = 4;   // largest batch of the vector path
 constexpr int TILE_ROWS = 16;        // row-parts per matrix-core unit
 constexpr int TRACE_POINTS = 12;
 constexpr int MAX_RUNS = 8;          // stages per phase (the planner splits larger phases)
-constexpr int DESC_BUFS = 4;         // phases whose run lists are resident in LDS at once
-constexpr int DESC_AHEAD = 4;        // the control wave writes phase p+DESC_AHEAD's list at the end of iteration p
 #ifndef WGN_EPI_BARRIER
 #define WGN_EPI_BARRIER 1
 #endif
@@ -59,6 +57,31 @@ constexpr int DESC_AHEAD = 4;        // the control wave writes phase p+DESC_AHE
 // after the control wave has issued the phase's output stores (which would
 // otherwise queue behind them in the compute unit's memory pipeline)
 constexpr int EPI_BARRIER = WGN_EPI_BARRIER;
+#ifndef WGN_SLOTS
+#define WGN_SLOTS 2
+#endif
+// vector path: block buffers per streaming wave (SLOTS - 1 blocks in flight
+// beyond the one being consumed)
+constexpr int SLOTS = WGN_SLOTS;
+#ifndef WGN_INTERLEAVE
+#define WGN_INTERLEAVE 0
+#endif
+// 1 (vector path): a consumed block's refill is issued one load per unit
+// while the next block is consumed, instead of in one burst right away; a
+// phase's last refill then goes out only after the next phase's x-hat
+// barrier, so no third barrier is needed on that path
+constexpr int INTERLEAVE = WGN_INTERLEAVE;
+#ifndef WGN_DESC_BUFS
+#define WGN_DESC_BUFS 4
+#endif
+// Run lists resident in LDS at once (a ring), and how far ahead of its own
+// iteration the control wave writes one: phase p+DESC_AHEAD's list at the end
+// of iteration p.  A streaming wave reads lists up to SLOTS + 1 phases ahead
+// of the phase it consumes, hence the bound (checked by the host schedule
+// model for each setting).
+constexpr int DESC_BUFS = WGN_DESC_BUFS;
+constexpr int DESC_AHEAD = WGN_DESC_BUFS;
+static_assert(DESC_BUFS >= SLOTS + 2, "the run-list ring must cover the streaming waves' look-ahead");
 constexpr uint64_t WAIT_TICKS = 200000000ull;  // 2 s at the 100 MHz real-time clock
 
 enum { NORM_NONE = 0, NORM_RMS = 1, NORM_LAYER = 2 };
@@ -123,6 +146,14 @@ struct DevPhase {
     int32_t carry_off;     // LDS byte offset of the K-window carry (row-parts x batch FP32)
     int32_t pad;
 };
+
+// One contiguous byte range of weights read by the optional touch pass (the
+// Infinity-Cache prefetch of a later launch's weights on a second stream).
+struct TouchRange {
+    const void *p;
+    uint64_t bytes;        // a multiple of 16
+};
+constexpr int MAX_TOUCH = 2 * MAX_RUNS;  // weight matrices of one launch (W and W_up of each stage)
 
 // Kernel arguments (passed by value).  A chain points at a program in device
 // memory; a single-stage call carries its one phase/stage/source inline.
