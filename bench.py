@@ -129,6 +129,8 @@ def main():
         launch = lambda: W.rmsnorm_rows(t["x"], t["g"], t["eps"], y)  # noqa: E731
         kernel_name = "rmsnorm_rows_kernel"
 
+    if chain is not None:
+        cfg["ring"] = chain.ring
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
 
     if args.prefetch == "tune":

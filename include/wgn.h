@@ -181,7 +181,10 @@ typedef struct wgn_chain_opts {
     int32_t path;        /* 0: auto (vector path for batch <= 4, matrix cores above);   */
                          /* 1: vector path (batch <= 4 only); 2: matrix-core path       */
     int32_t no_fuse;     /* 1: keep every stage whole (no hoisting, see below)          */
-    int32_t reserved[3]; /* must be zero                                               */
+    int32_t ring;        /* vector path's block-buffer ring: 0 auto; 1: 2 x 20 units,   */
+                         /* burst refills; 2: 5 x 8 units, burst refills; 3: 4 x 10     */
+                         /* units, refills interleaved with compute (same results)      */
+    int32_t reserved[2]; /* must be zero                                               */
 } wgn_chain_opts;
 
 /* Workspace bytes for a chain over these stages (mode/grid as in opts, NULL = defaults). */
@@ -205,6 +208,10 @@ wgn_status wgn_chain_check(const wgn_chain *chain, wgn_stream stream);
 
 int32_t wgn_chain_num_phases(const wgn_chain *chain);
 int32_t wgn_chain_grid(const wgn_chain *chain);
+/* Ring the vector path's streaming waves use (0..2 = opts.ring - 1; the auto
+ * choice takes ring 1 when phases give a streaming wave fewer than 4 units on
+ * average, else ring 2 from batch 2 up and ring 0 at batch 1); -1 for null. */
+int32_t wgn_chain_ring(const wgn_chain *chain);
 
 /* Trace of the last run of a chain created with opts.trace = 1: for every
  * phase p and workgroup g, WGN_TRACE_POINTS timestamps of the device's 100 MHz

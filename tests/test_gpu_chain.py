@@ -140,6 +140,67 @@ def test_small_decode_step_all_batches(B):
     check_decoder(inp, bufs, layers_full={1})
 
 
+def zero_outputs(bufs):
+    for k, v in bufs.items():
+        if k in ("h", "x"):
+            v = v[1:]  # the chain's input
+        for t in (v if isinstance(v, list) else [v]):
+            if t is not None:
+                t.zero_()
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4])
+def test_rings_agree_decode(B):
+    """Every block-buffer ring of the vector path gives the same bits: the
+    rings change when loads are issued, not the order of any arithmetic.  The
+    oracle checks the first; persistent and per-phase launches both run."""
+    say("rings decode_step 2 layers V=20000 B=%d" % B)
+    inp = gen.make_stage_tensors("decode_step_1536x28", device=DEV, batch=B, n_layers=2, vocab=20000)
+    stages, bufs = steps.decoder_stages(inp, DEV)
+    assert W.Chain(stages, B).ring == (0 if B == 1 else 2)
+    ref = None
+    for ring in (1, 2, 3):
+        for mode in (0, 1):
+            ch = W.Chain(stages, B, mode=mode, ring=ring)
+            assert ch.ring == ring - 1
+            zero_outputs(bufs)
+            ch.run()
+            ch.check()
+            snap = snapshot(bufs)
+            if ref is None:
+                check_decoder(inp, bufs, layers_full={0, 1})
+                ref = snap
+            else:
+                assert same_bits(ref, snap), "ring %d mode %d differs" % (ring - 1, mode)
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_rings_agree_ln_chain(B):
+    """The LayerNorm chain (a fraction of a unit per wave and phase) chooses
+    ring 1 by itself; every ring gives the same bits, checked by the oracle."""
+    say("rings ln_gelu_chain_768x72 B=%d" % B)
+    inp = gen.make_stage_tensors("ln_gelu_chain_768x72", device=DEV, batch=B, seeded_ln_params=True)
+    stages, bufs = steps.ln_gelu_chain_stages(inp, DEV)
+    assert W.Chain(stages, B).ring == 1
+    ref = None
+    for ring in (2, 1, 3):
+        ch = W.Chain(stages, B, ring=ring)
+        zero_outputs(bufs)
+        ch.run()
+        ch.check()
+        snap = snapshot(bufs)
+        if ref is None:
+            xs = bufs["x"]
+            for i, Ld in enumerate(inp["layers"]):
+                r = O.stage(bits(xs[i]), bits(Ld["W"]), norm=O.NORM_LAYER, eps=float(np.float32(1e-5)),
+                            gamma=bits(Ld["gamma"]), beta=bits(Ld["beta"]), bias=bits(Ld["bias"]),
+                            epi=O.EPI_GELU_TANH)
+                assert_close_bf16(bits(xs[i + 1]), r, "ln-gelu ring %d layer %d" % (ring - 1, i))
+            ref = snap
+        else:
+            assert same_bits(ref, snap), "ring %d differs" % (ring - 1)
+
+
 @pytest.mark.parametrize("B", [1, 4, 16])
 def test_ln_gelu_chain_768x72(B):
     """72 x [LayerNorm(768) -> Linear -> GELU-tanh], seeded LN params, per stage."""

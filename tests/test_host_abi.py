@@ -294,6 +294,23 @@ def test_chain_phase_grouping_counts():
     assert L.lib().wgn_chain_workspace_bytes(arr, len(st), 1, None) > 0
 
 
+def test_chain_opts_ring_checked_before_device():
+    """opts.ring takes 0 (auto) to 3; anything else is refused before the
+    device is touched, as are non-zero reserved words."""
+    import ctypes
+    ar = Arena()
+    st = fake_decoder(ar, 1, 1, V=1000)
+    arr = L.stage_array(st)
+    ws = ar.take(1 << 20)
+    for ring, res in ((-1, 0), (4, 0), (0, 1), (2, 1)):
+        o = L.ChainOpts()
+        o.ring = ring
+        o.reserved[1] = res
+        h = ctypes.c_void_p()
+        got = L.lib().wgn_chain_create(arr, len(st), 1, ctypes.byref(o), ws, 1 << 20, None, ctypes.byref(h))
+        assert got == L.E_ARG, (ring, res, got)
+
+
 def test_rmsnorm_rows_argument_checks():
     ar = Arena()
     x, g, y = ar.take(4096), ar.take(4096), ar.take(4096)

@@ -36,18 +36,55 @@ def header_constant(name):
     return int(m.group(1))
 
 
-DESC_BUFS = header_constant("DESC_BUFS")
-DESC_AHEAD = DESC_BUFS  # wgn_prog.h: DESC_AHEAD = WGN_DESC_BUFS
+_PROG = open(os.path.join(ROOT, "weight_gemv_norm_amd", "csrc", "wgn_prog.h")).read()
+# wgn_prog.h sizes the run-list ring per block-buffer ring; the model mirrors
+# the two expressions (checked verbatim so that a change there fails here)
+assert "constexpr int desc_bufs(int r) { return ring_slots(r) + 2 <= 4 ? 4 : 8; }" in _PROG
+assert "constexpr int desc_ahead(int r) { return ring_slots(r) + 2; }" in _PROG
+
+
+def desc_bufs_of(slots):
+    return 4 if slots + 2 <= 4 else 8
+
+
+def desc_ahead_of(slots):
+    return slots + 2
+
+
+DESC_BUFS = 4    # ring 0 (two block buffers)
+DESC_AHEAD = 4
 # 1 if the streaming waves refill only after the control wave has issued the
 # epilogue's stores (a third barrier per phase)
 EPI_BARRIER = header_constant("EPI_BARRIER")
-# block buffers per streaming wave (vector path; the matrix-core path uses 2)
-SLOTS = header_constant("SLOTS")
-# 1 if the vector path issues a consumed block's refill while consuming the
-# next block: the run list is read when the refill is prepared, right after the
-# block is consumed (the same point as a burst refill without the third
-# barrier), and the loads themselves read no LDS
-INTERLEAVE = header_constant("INTERLEAVE")
+
+
+def ring_table():
+    """(slots, interleaved) of every ring, read from wgn_prog.h's ring_slots /
+    ring_interleaved (nested conditionals on r)."""
+    src = open(os.path.join(ROOT, "weight_gemv_norm_amd", "csrc", "wgn_prog.h")).read()
+    n = header_constant("NUM_RINGS")
+
+    def cond_fn(name):
+        m = re.search(r"constexpr \w+ %s\(int r\) \{ return (.*?); \}" % name, src)
+        assert m, name
+        expr = m.group(1)
+
+        def ev(e, r):
+            e = e.strip()
+            m2 = re.match(r"r == (\d+) \? (\w+) : (.*)$", e)
+            if m2:
+                return ev(m2.group(2), r) if r == int(m2.group(1)) else ev(m2.group(3), r)
+            m3 = re.match(r"r == (\d+)$", e)
+            if m3:
+                return r == int(m3.group(1))
+            return int(e) if e.isdigit() else {"true": True, "false": False}[e]
+        return lambda r: ev(expr, r)
+    slots, il = cond_fn("ring_slots"), cond_fn("ring_interleaved")
+    return [(slots(r), bool(il(r))) for r in range(n)]
+
+
+RINGS = ring_table()
+SLOTS, INTERLEAVE = RINGS[0]
 
 
 class Wave:
@@ -303,6 +340,26 @@ def test_schedule_interleaved_refills(slots):
         errs = check_schedule(0, P, nb, desc_bufs=slots + 2, desc_ahead=slots + 2, norm=norm, slots=slots,
                               interleave=1)
         assert not errs, (P, nb, norm, errs[:3])
+
+
+@pytest.mark.parametrize("ring", range(len(RINGS)))
+def test_schedule_every_ring_with_the_header_constants(ring):
+    """Each ring of the kernel, with the header's run-list ring size."""
+    slots, il = RINGS[ring]
+    bufs, ahead = desc_bufs_of(slots), desc_ahead_of(slots)
+    rng = random.Random(31 + ring)
+    for _ in range(1500):
+        P = rng.randint(1, 14)
+        W = rng.randint(1, 7)
+        nb = [[rng.choice([1, 1, 1, 2, 3, 5]) for _ in range(P)] for _ in range(W)]
+        norm = {p: rng.random() < 0.6 for p in range(P)}
+        errs = check_schedule(0, P, nb, desc_bufs=bufs, desc_ahead=ahead, norm=norm, slots=slots,
+                              interleave=int(il))
+        assert not errs, (ring, P, nb, norm, errs[:3])
+
+
+def test_ring_table_parsed():
+    assert RINGS == [(2, False), (5, False), (4, True)]
 
 
 def test_model_detects_short_ring_for_more_slots():

@@ -39,7 +39,7 @@ class Stage(ctypes.Structure):
 class ChainOpts(ctypes.Structure):
     """Mirror of wgn_chain_opts."""
     _fields_ = [("mode", I32), ("grid", I32), ("trace", I32), ("path", I32), ("no_fuse", I32),
-                ("reserved", I32 * 3)]
+                ("ring", I32), ("reserved", I32 * 2)]
 
 
 class Plan(ctypes.Structure):
@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
         "wgn_chain_check": ([P, P], I32),
         "wgn_chain_num_phases": ([P], I32),
         "wgn_chain_grid": ([P], I32),
+        "wgn_chain_ring": ([P], I32),
         "wgn_chain_trace": ([P, P, ctypes.POINTER(ctypes.c_uint64), SZ], I32),
         "wgn_chain_stage_phases": ([P, ctypes.POINTER(I32)], I32),
         "wgn_chain_destroy": ([P], None),

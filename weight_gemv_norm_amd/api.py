@@ -118,13 +118,15 @@ def rmsnorm_rows(x: torch.Tensor, gamma: torch.Tensor, eps: float, y: torch.Tens
 PATH_AUTO, PATH_VECTOR, PATH_MATRIX = 0, 1, 2
 
 
-def _opts(mode: int, grid: int, trace: bool = False, path: int = PATH_AUTO, fuse: bool = True) -> ChainOpts:
+def _opts(mode: int, grid: int, trace: bool = False, path: int = PATH_AUTO, fuse: bool = True,
+          ring: int = 0) -> ChainOpts:
     o = ChainOpts()
     o.mode = mode
     o.grid = grid
     o.trace = 1 if trace else 0
     o.path = path
     o.no_fuse = 0 if fuse else 1
+    o.ring = ring
     return o
 
 
@@ -140,11 +142,13 @@ class Chain:
 
     def __init__(self, stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 0,
                  ws: Optional[torch.Tensor] = None, stream=None, device="cuda", trace: bool = False,
-                 path: int = PATH_AUTO, fuse: bool = True):
+                 path: int = PATH_AUTO, fuse: bool = True, ring: int = 0):
+        """ring: 0 chooses the streaming waves' block-buffer ring by the chain's
+        shape; 1..3 force ring 0..2 (wgn_chain_opts.ring)."""
         self._arr = L.stage_array(stages)
         self.n_stages = len(stages)
         self.batch = batch
-        o = _opts(mode, grid, trace, path, fuse)
+        o = _opts(mode, grid, trace, path, fuse, ring)
         need = L.lib().wgn_chain_workspace_bytes(self._arr, len(stages), batch, ctypes.byref(o))
         if need == 0:
             # planning failed: let create report the precise status
@@ -182,6 +186,10 @@ class Chain:
     @property
     def grid(self) -> int:
         return int(L.lib().wgn_chain_grid(self._h))
+
+    @property
+    def ring(self) -> int:
+        return int(L.lib().wgn_chain_ring(self._h))
 
     def trace(self, stream=None):
         """Timestamps of the last run, shape [phases][grid][TRACE_POINTS], in 10 ns ticks."""

@@ -18,7 +18,8 @@
 #include "wgn_loader.h"
 
 namespace wgn {
-hipError_t launch_chain(int32_t batch, bool tile, const KArgs &a, int32_t grid, size_t lds, hipStream_t s);
+hipError_t launch_chain(int32_t batch, bool tile, int32_t ring, const KArgs &a, int32_t grid, size_t lds,
+                        hipStream_t s);
 hipError_t launch_rmsnorm_rows(const uint16_t *x, int64_t xs, const uint16_t *g, float eps, uint16_t *y, int64_t ys,
                                int32_t rows, int32_t K, bool f16, hipStream_t s);
 hipError_t launch_touch(const TouchRange *r, int32_t n, uint32_t frac_q16, int32_t blocks, hipStream_t s);
@@ -166,7 +167,7 @@ struct Program {
     std::vector<FFix> f_fix;             // pointers into the FP32 row-sum area, set at creation
     size_t f_bytes = 0;                  // bytes of that workspace area
     int32_t n_argmax = 0;
-    size_t lds_end = LDS_DYN_OFF;        // dynamic LDS bytes of the largest phase
+    size_t lds_end = 0;                  // dynamic LDS bytes of the largest phase (set with tile)
     size_t lds_total() const { return lds_end; }
     static size_t al16(size_t v) { return (v + 15) & ~size_t(15); }
 };
@@ -285,7 +286,7 @@ bool layout_phase(const Program &P, DevPhase &ph, const PhaseStats &S, bool carr
     const size_t part = Program::al16((size_t)S.max_rp * S.jmax * nb * 4);
     const size_t epi = epi_in ? Program::al16((size_t)S.max_rp * epi_rec((int32_t)nb) * 4) : 0;
     const size_t cy = carry ? Program::al16((size_t)S.max_rp * nb * 4) : 0;
-    size_t o = LDS_DYN_OFF;
+    size_t o = lds_dyn_off(path_desc_bufs(P.tile));
     ph.x_off = (int32_t)o;
     o += x;
     ph.part_off = (int32_t)o;
@@ -482,6 +483,7 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
     P.B = B;
     P.G = G;
     P.tile = tile;
+    P.lds_end = (size_t)lds_dyn_off(path_desc_bufs(tile));
     P.phase_of_stage.assign(n, -1);
     for (PStage &p : ps) {
         if (!p.product_only) continue;
@@ -733,6 +735,7 @@ bool single_geometry(const wgn_stage &s, int32_t B, int32_t cus, SingleLaunch &L
     P.B = B;
     P.G = L.G;
     P.tile = L.tile;
+    P.lds_end = (size_t)lds_dyn_off(path_desc_bufs(L.tile));
     P.stages.push_back(make_dev_stage(s));
     P.sources.push_back(make_dev_source(s));
     DevPhase &ph = L.a.iph;
@@ -773,6 +776,7 @@ struct wgn_chain {
     KArgs a;
     bool trace;
     int32_t mode;
+    int32_t ring;           // block-buffer ring of the vector path's streaming waves
     size_t lds;
     void *ws;
     WsLayout L;
@@ -790,6 +794,24 @@ struct wgn_chain {
 namespace {
 int32_t opts_path(const wgn_chain_opts *opts) { return opts ? opts->path : 0; }
 bool opts_fuse(const wgn_chain_opts *opts) { return !(opts && opts->no_fuse); }
+
+// The vector path's ring for a chain, by the shape that was measured fastest
+// with each (decode step at batch 1-4, LayerNorm chain): phases that give a
+// streaming wave fewer than 4 units on average want many phases in flight
+// (ring 1); otherwise batch 2-4 streams best with interleaved refills
+// (ring 2) and batch 1 with two large bursts (ring 0).
+int32_t auto_ring(const Program &P) {
+    if (P.tile || P.phases.empty()) return 0;
+    double units = 0.0;
+    for (const DevPhase &ph : P.phases)
+        for (int32_t si = ph.stage0; si < ph.stage0 + ph.nstages; ++si) {
+            const DevStage &st = P.stages[si];
+            units += (double)st.N * st.parts * st.nchunks;
+        }
+    const double per_wave = units / ((double)P.phases.size() * P.G * STREAM_WAVES);
+    if (per_wave < 4.0) return 1;
+    return P.B >= 2 ? 2 : 0;
+}
 
 // Point the stages' FP32 row-sum pointers into the workspace area at base.
 void patch_fsum(Program &P, char *base) {
@@ -851,7 +873,7 @@ wgn_status wgn_gemv_norm(const wgn_stage *stage, int32_t batch, void *workspace,
         L.a.am_part = (uint64_t *)((char *)workspace + 256);
     }
     L.a.ist.W = (const uint16_t *)stage->W;
-    hipError_t e = note(launch_chain(batch, L.tile, L.a, L.G, L.lds, (hipStream_t)stream), "gemv_norm launch");
+    hipError_t e = note(launch_chain(batch, L.tile, 0, L.a, L.G, L.lds, (hipStream_t)stream), "gemv_norm launch");
     return e == hipSuccess ? WGN_OK : WGN_E_HIP;
 }
 
@@ -917,9 +939,10 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     if (opts) {
         if (opts->mode < 0 || opts->mode > 1 || opts->grid < 0 || opts->grid > MAX_GRID || opts->trace < 0 ||
             opts->trace > 1 ||
-            opts->path < 0 || opts->path > 2 || opts->no_fuse < 0 || opts->no_fuse > 1)
+            opts->path < 0 || opts->path > 2 || opts->no_fuse < 0 || opts->no_fuse > 1 || opts->ring < 0 ||
+            opts->ring > NUM_RINGS)
             return WGN_E_ARG;
-        for (int i = 0; i < 3; ++i)
+        for (int i = 0; i < 2; ++i)
             if (opts->reserved[i]) return WGN_E_ARG;
     }
     wgn_chain *c = new (std::nothrow) wgn_chain();
@@ -947,6 +970,8 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
         return WGN_E_WORKSPACE;
     }
     c->mode = opts ? opts->mode : 0;
+    c->ring = opts && opts->ring > 0 ? opts->ring - 1 : auto_ring(c->P);
+    if (c->P.tile) c->ring = 0;
     c->ws = workspace;
     c->lds = c->P.lds_total();
     patch_fsum(c->P, (char *)workspace + c->L.fsum);
@@ -1047,7 +1072,7 @@ wgn_status wgn_chain_run(const wgn_chain *c, wgn_stream stream) {
     if (!c) return WGN_E_ARG;
     hipStream_t s = (hipStream_t)stream;
     if (c->mode == 0) {
-        hipError_t e = note(launch_chain(c->P.B, c->P.tile, c->a, c->P.G, c->lds, s), "chain launch");
+        hipError_t e = note(launch_chain(c->P.B, c->P.tile, c->ring, c->a, c->P.G, c->lds, s), "chain launch");
         return e == hipSuccess ? WGN_OK : WGN_E_HIP;
     }
     // one launch per phase; the K windows of one phase share a launch (their
@@ -1056,7 +1081,7 @@ wgn_status wgn_chain_run(const wgn_chain *c, wgn_stream stream) {
     for (int32_t p = 0; p < (int32_t)c->P.phases.size(); p = c->P.group_end[p]) {
         a.p0 = p;
         a.p1 = c->P.group_end[p];
-        hipError_t e = note(launch_chain(c->P.B, c->P.tile, a, c->P.G, c->lds, s), "chain phase launch");
+        hipError_t e = note(launch_chain(c->P.B, c->P.tile, c->ring, a, c->P.G, c->lds, s), "chain phase launch");
         if (e != hipSuccess) return WGN_E_HIP;
     }
     return WGN_OK;
@@ -1095,7 +1120,7 @@ wgn_status wgn_chain_run_plan(const wgn_chain *c, const wgn_plan *plan, wgn_stre
         }
         a.p0 = c->launch0[li];
         a.p1 = c->P.group_end[a.p0];
-        if (note(launch_chain(c->P.B, c->P.tile, a, c->P.G, c->lds, s), "chain phase launch") != hipSuccess)
+        if (note(launch_chain(c->P.B, c->P.tile, c->ring, a, c->P.G, c->lds, s), "chain phase launch") != hipSuccess)
             return WGN_E_HIP;
     }
     if (forked && (note(hipEventRecord(c->ev[nl], sd), "plan join") != hipSuccess ||
@@ -1225,6 +1250,8 @@ int32_t wgn_chain_num_phases(const wgn_chain *c) { return c ? (int32_t)c->P.phas
 
 int32_t wgn_chain_grid(const wgn_chain *c) { return c ? c->P.G : -1; }
 
+int32_t wgn_chain_ring(const wgn_chain *c) { return c ? c->ring : -1; }
+
 wgn_status wgn_chain_trace(const wgn_chain *c, wgn_stream stream, uint64_t *out, size_t n_out) {
     if (!c || !out) return WGN_E_ARG;
     if (!c->trace) return WGN_E_UNSUPPORTED;
@@ -1318,7 +1345,7 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
     }
     for (int32_t p = 0; p < (int32_t)P.phases.size(); ++p) {
         const DevPhase &ph = P.phases[p];
-        if (!(ph.x_off >= LDS_DYN_OFF && ph.part_off >= ph.x_off + nb * ph.xb * 2 && ph.prm_off >= ph.part_off &&
+        if (!(ph.x_off >= lds_dyn_off(path_desc_bufs(P.tile)) && ph.part_off >= ph.x_off + nb * ph.xb * 2 && ph.prm_off >= ph.part_off &&
               ph.epi_off >= ph.prm_off && ph.carry_off >= ph.epi_off && (size_t)ph.carry_off <= P.lds_total()))
             ++bad;
         if (P.group_end[p] <= p || P.group_end[p] > (int32_t)P.phases.size()) ++bad;

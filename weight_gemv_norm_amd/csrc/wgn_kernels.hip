@@ -31,17 +31,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// 20 units: the larger phase of a decoder layer (Q, K, V, gate/up and the
-// next layer's hoisted O product: about 37 units per wave on 256 workgroups)
-// is then two blocks, both requested before the phase starts (measured on
-// the decode step: 16 and 24 are slower at batch 1 to 4)
-#ifndef WGN_DEPTH
-#define WGN_DEPTH 20
-#endif
 #ifndef WGN_WEIGHT_AUX
 #define WGN_WEIGHT_AUX 2  // nt: weights are streamed once
 #endif
-constexpr int DEPTH = WGN_DEPTH;          // vector path: units per block (loads in flight per block)
 constexpr int TILE_LOADS = UNIT / 32;     // matrix-core path: loads per unit (= per block)
 constexpr int WEIGHT_AUX = WGN_WEIGHT_AUX;  // cache policy of the weight loads (streamed once)
 // Cache policy of every access to data that another workgroup produces or
@@ -431,15 +423,19 @@ struct StreamState {
     int32_t p;
     int32_t u, u_beg, u_end;
     int32_t g, w, p1;
+    int32_t dmask;         // run-list ring size - 1
     bool done_all;
 };
 
-__device__ __forceinline__ const char *run_buf(const char *desc, int32_t p) {
-    return desc + (p % DESC_BUFS) * RUN_BUF_STRIDE;
+__device__ __forceinline__ const char *run_buf(const char *desc, int32_t p, int32_t dmask) {
+    return desc + (p & dmask) * RUN_BUF_STRIDE;
+}
+__device__ __forceinline__ const char *run_buf_s(const StreamState &S, int32_t p) {
+    return run_buf(S.desc, p, S.dmask);
 }
 
 __device__ __forceinline__ void stream_begin_phase(StreamState &S, int32_t p) {
-    const char *buf = run_buf(S.desc, p);
+    const char *buf = run_buf_s(S, p);
     S.h = *(const RunHdr *)buf;
     S.runs = (const Run *)(buf + sizeof(RunHdr));
     S.p = p;
@@ -473,13 +469,13 @@ struct PendLoads {
     uint32_t plo, phi, nb;
 };
 
-template <int B>
+template <int B, int D>
 __device__ __forceinline__ PendLoads prepare_block(const KArgs &a, StreamState &S, BlockMeta &bm, uint32_t lane) {
     UnitDesc ud;
     ud.ptr = 0;
     ud.nbytes = 0;
     ud.meta = 0;
-    if (!S.done_all && lane < (uint32_t)DEPTH)
+    if (!S.done_all && lane < (uint32_t)D)
         ud = unit_desc_runs(S.h, S.runs, S.u + (int32_t)lane, S.u_beg, S.u_end, S.w, B);
     if (ud.nbytes == 0) ud.ptr = (uint64_t)(uintptr_t)a.ist.W;
     PendLoads q;
@@ -490,7 +486,7 @@ __device__ __forceinline__ PendLoads prepare_block(const KArgs &a, StreamState &
     bm.xb_bytes = S.done_all ? 0 : S.h.xb_bytes;
     bm.x_off = S.h.x_off;
     bm.part_off = S.h.part_off;
-    stream_advance(S, bm, DEPTH);
+    stream_advance(S, bm, D);
     return q;
 }
 
@@ -504,12 +500,12 @@ __device__ __forceinline__ u32x4 issue_unit(const PendLoads &q, int j, uint32_t 
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)(lane * 16u), 0, WEIGHT_AUX);
 }
 
-template <int B>
-__device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4 (&d)[DEPTH], BlockMeta &bm,
+template <int B, int D>
+__device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4 (&d)[D], BlockMeta &bm,
                                            uint32_t lane) {
-    const PendLoads q = prepare_block<B>(a, S, bm, lane);
+    const PendLoads q = prepare_block<B, D>(a, S, bm, lane);
 #pragma unroll
-    for (int j = 0; j < DEPTH; ++j) d[j] = issue_unit(q, j, lane);
+    for (int j = 0; j < D; ++j) d[j] = issue_unit(q, j, lane);
 }
 
 // Every slot of a block is consumed unconditionally (an invalid slot holds
@@ -522,25 +518,25 @@ __device__ __forceinline__ void load_block(const KArgs &a, StreamState &S, u32x4
 // the block is reduced by wave_sum_last (DPP only) and its partial written by
 // lane 63.  G is the largest group whose x-hat values fit in the registers
 // left beside the two in-flight blocks.
-template <int B>
+template <int B, int D>
 constexpr int xhat_group() {
-    return (B == 1 && DEPTH % 16 == 0 && DEPTH <= 16) ? 16 : (B == 1 && DEPTH % 8 == 0) ? 8
-         : ((B == 1 || B == 2) && DEPTH % 4 == 0) ? 4 : 2;
+    return (B == 1 && D % 16 == 0 && D <= 16) ? 16 : (B == 1 && D % 8 == 0) ? 8
+         : ((B == 1 || B == 2) && D % 4 == 0) ? 4 : 2;
 }
 
 // IL: while consuming, also issue the loads of a prepared block q into dn,
 // one per consumed unit (after each group's x-hat reads), so that the compute
 // unit's memory pipeline receives a steady trickle instead of a burst.
-template <int B, bool IL = false>
-__device__ __forceinline__ void consume_block(const u32x4 (&d)[DEPTH], const BlockMeta &bm, float (&acc)[B],
+template <int B, int D, bool IL = false>
+__device__ __forceinline__ void consume_block(const u32x4 (&d)[D], const BlockMeta &bm, float (&acc)[B],
                                               const char *lds, uint32_t lane, const PendLoads *q = nullptr,
                                               u32x4 *dn = nullptr) {
-    constexpr int G = xhat_group<B>();
-    static_assert(DEPTH % G == 0, "block depth must be a multiple of the x-hat group");
+    constexpr int G = xhat_group<B, D>();
+    static_assert(D % G == 0, "block depth must be a multiple of the x-hat group");
     const char *xh = lds + bm.x_off + lane * 16u;
     float *part = (float *)(lds + bm.part_off);
 #pragma unroll
-    for (int g0 = 0; g0 < DEPTH; g0 += G) {
+    for (int g0 = 0; g0 < D; g0 += G) {
         u32x4 xv[G][B];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
@@ -647,51 +643,49 @@ struct Acc<B, true> {
     __device__ __forceinline__ void zero() { v = (f32x4){0.0f, 0.0f, 0.0f, 0.0f}; }
 };
 
-template <bool TILE>
-constexpr int block_loads() { return TILE ? TILE_LOADS : DEPTH; }
+template <bool TILE, int R>
+constexpr int block_loads() { return TILE ? TILE_LOADS : ring_depth(R); }
 
-template <int B, bool TILE>
-__device__ __forceinline__ void load_any(const KArgs &a, StreamState &S, u32x4 (&d)[block_loads<TILE>()],
+template <int B, bool TILE, int R>
+__device__ __forceinline__ void load_any(const KArgs &a, StreamState &S, u32x4 (&d)[block_loads<TILE, R>()],
                                          BlockMeta &bm, uint32_t lane) {
     if constexpr (TILE) load_tile(a, S, d, bm, lane);
-    else load_block<B>(a, S, d, bm, lane);
+    else load_block<B, ring_depth(R)>(a, S, d, bm, lane);
 }
-template <int B, bool TILE>
-__device__ __forceinline__ void consume_any(const KArgs &a, const u32x4 (&d)[block_loads<TILE>()], const BlockMeta &bm,
-                                            Acc<B, TILE> &acc, const char *lds, uint32_t lane) {
+template <int B, bool TILE, int R>
+__device__ __forceinline__ void consume_any(const KArgs &a, const u32x4 (&d)[block_loads<TILE, R>()],
+                                            const BlockMeta &bm, Acc<B, TILE> &acc, const char *lds, uint32_t lane) {
     if constexpr (TILE) consume_tile(d, bm, acc.v, lds, lane, a.nb);
-    else consume_block<B>(d, bm, acc.v, lds, lane);
+    else consume_block<B, ring_depth(R)>(d, bm, acc.v, lds, lane);
 }
-
-template <bool TILE>
-constexpr int stream_slots() { return TILE ? 2 : SLOTS; }
 
 // Whether the streaming waves hold a phase's last refill until the control
 // wave has issued the phase's stores (a third barrier per phase).
-template <bool TILE>
-constexpr bool epi_barrier() { return EPI_BARRIER != 0 && (TILE || !INTERLEAVE); }
+template <bool TILE, int R>
+constexpr bool epi_barrier() { return EPI_BARRIER != 0 && (TILE || !ring_interleaved(R)); }
 
 // Vector path with interleaved refills.  Slot k's refill is prepared (run
 // list read, addresses computed) right after slot k is consumed and issued,
-// one load per unit, while slot k+1 is consumed; SLOTS - 2 blocks are fully
+// one load per unit, while slot k+1 is consumed; NS - 2 blocks are fully
 // in flight beyond the one being consumed, plus the one being issued.  At a
 // phase end the prepared refill waits for the next phase's x-hat barrier, so
 // the control wave's stores, flag store, flag polls and input loads meet an
 // idle memory pipeline.
-template <int B, bool CHAIN>
+template <int B, bool CHAIN, int R>
 __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_t w, char *lds) {
-    constexpr int NS = SLOTS;
+    constexpr int NS = ring_slots(R), D = ring_depth(R);
     static_assert(NS >= 2, "at least two block buffers");
     const uint32_t lane = lane_id();
     StreamState S;
     S.desc = lds + LDS_DESC_OFF;
+    S.dmask = desc_bufs(R) - 1;
     S.g = g;
     S.w = w;
     S.p1 = a.p1;
     S.done_all = false;
     wg_barrier();  // run lists of the first phases are in LDS
     stream_begin_phase(S, a.p0);
-    u32x4 d[NS][DEPTH];
+    u32x4 d[NS][D];
     BlockMeta m[NS];
     float acc[B];
 #pragma unroll
@@ -699,9 +693,9 @@ __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_
     uint64_t *tl = (uint64_t *)(lds + LDS_TRACE_OFF);  // trace slots
     const bool tw = a.trace && w == 0 && lane == 0;
 #pragma unroll
-    for (int k = 0; k < NS - 1; ++k) load_block<B>(a, S, d[k], m[k], lane);
-    PendLoads pq = prepare_block<B>(a, S, m[NS - 1], lane);
-    if (((const RunHdr *)run_buf(S.desc, a.p0))->has_norm) norm_all(lds, w, lane);
+    for (int k = 0; k < NS - 1; ++k) load_block<B, D>(a, S, d[k], m[k], lane);
+    PendLoads pq = prepare_block<B, D>(a, S, m[NS - 1], lane);
+    if (((const RunHdr *)run_buf_s(S, a.p0))->has_norm) norm_all(lds, w, lane);
     wg_barrier();  // x-hat of the first phase is ready
     bool ok = abort_flag_get() == 0;
     int32_t p = a.p0;
@@ -710,7 +704,7 @@ __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_
     while (ok && p < a.p1) {
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
-            consume_block<B, true>(d[k], m[k], acc, lds, lane, &pq, d[(k + NS - 1) % NS]);
+            consume_block<B, D, true>(d[k], m[k], acc, lds, lane, &pq, d[(k + NS - 1) % NS]);
             if (tw && nblk < 3) tl[(p & 1) * 6 + 3 + nblk] = wall_clock64();
             ++nblk;
             const bool end = ok && m[k].last;
@@ -718,11 +712,11 @@ __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_
                 if (tw) tl[(p & 1) * 6 + 2] = wall_clock64();
                 wg_barrier();  // partials of phase p are complete
             }
-            pq = prepare_block<B>(a, S, m[k], lane);
+            pq = prepare_block<B, D>(a, S, m[k], lane);
             if (end) nblk = 0;
             if (end && ++p < a.p1) {
                 if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
-                if (((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
+                if (((const RunHdr *)run_buf_s(S, p))->has_norm) norm_all(lds, w, lane);
                 wg_barrier();  // x-hat of phase p is ready
                 ok = abort_flag_get() == 0;
                 if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
@@ -731,19 +725,20 @@ __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_
     }
 }
 
-template <int B, bool CHAIN, bool TILE>
+template <int B, bool CHAIN, bool TILE, int R>
 __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
-    constexpr int NS = stream_slots<TILE>();
+    constexpr int NS = TILE ? 2 : ring_slots(R);
     const uint32_t lane = lane_id();
     StreamState S;
     S.desc = lds + LDS_DESC_OFF;
+    S.dmask = desc_bufs(R) - 1;
     S.g = g;
     S.w = w;
     S.p1 = a.p1;
     S.done_all = false;
     wg_barrier();  // run lists of the first phases are in LDS
     stream_begin_phase(S, a.p0);
-    u32x4 d[NS][block_loads<TILE>()];
+    u32x4 d[NS][block_loads<TILE, R>()];
     BlockMeta m[NS];
     Acc<B, TILE> acc;
     acc.zero();
@@ -760,8 +755,8 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
     uint64_t *tl = (uint64_t *)(lds + LDS_TRACE_OFF);  // trace slots
     const bool tw = a.trace && w == 0 && lane == 0;
 #pragma unroll
-    for (int k = 0; k < NS; ++k) load_any<B, TILE>(a, S, d[k], m[k], lane);
-    if (((const RunHdr *)run_buf(S.desc, a.p0))->has_norm) norm_all(lds, w, lane);
+    for (int k = 0; k < NS; ++k) load_any<B, TILE, R>(a, S, d[k], m[k], lane);
+    if (((const RunHdr *)run_buf_s(S, a.p0))->has_norm) norm_all(lds, w, lane);
     wg_barrier();  // x-hat of the first phase is ready
     bool ok = abort_flag_get() == 0;
     int32_t p = a.p0;
@@ -770,20 +765,20 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
     while (ok && p < a.p1) {
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
-            consume_any<B, TILE>(a, d[k], m[k], acc, lds, lane);
+            consume_any<B, TILE, R>(a, d[k], m[k], acc, lds, lane);
             if (tw && nblk < 3) tl[(p & 1) * 6 + 3 + nblk] = wall_clock64();
             ++nblk;
             const bool end = ok && m[k].last;
             if (end) {
                 if (tw) tl[(p & 1) * 6 + 2] = wall_clock64();
                 wg_barrier();  // partials of phase p are complete
-                if (epi_barrier<TILE>()) wg_barrier();  // the control wave has issued phase p's stores
+                if (epi_barrier<TILE, R>()) wg_barrier();  // the control wave has issued phase p's stores
             }
-            load_any<B, TILE>(a, S, d[k], m[k], lane);
+            load_any<B, TILE, R>(a, S, d[k], m[k], lane);
             if (end) nblk = 0;
             if (end && ++p < a.p1) {
                 if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
-                if (((const RunHdr *)run_buf(S.desc, p))->has_norm) norm_all(lds, w, lane);
+                if (((const RunHdr *)run_buf_s(S, p))->has_norm) norm_all(lds, w, lane);
                 wg_barrier();  // x-hat of phase p is ready
                 ok = abort_flag_get() == 0;
                 if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
@@ -996,7 +991,7 @@ __device__ __forceinline__ void row_sums(const RunHdr &h, const Run &r, int32_t 
 // its stages at once; P = batch rounded up to a power of two).  Argmax stages
 // are reduced afterwards, one at a time.
 template <int B, bool CHAIN, bool TILE>
-__device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32_t g, const float *part,
+__device__ __forceinline__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32_t g, const float *part,
                          const float *epi, float *carry, uint32_t lane) {
     const int32_t nb = a.nb;
     const LaneSplit ls = lane_split(nb, lane);
@@ -1081,9 +1076,9 @@ __device__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32
 
 // Write phase q's run list for workgroup g into its LDS buffer: a copy of the
 // precomputed list for chains (asynchronous: memory to LDS), else built here.
-template <bool CHAIN, bool TILE>
+template <bool CHAIN, bool TILE, int R>
 __device__ void build_runs(const KArgs &a, int32_t q, int32_t g, char *desc, uint32_t lane) {
-    char *buf = desc + (q % DESC_BUFS) * RUN_BUF_STRIDE;
+    char *buf = desc + (q & (desc_bufs(R) - 1)) * RUN_BUF_STRIDE;
     if (CHAIN && a.runimg) {
         copy_to_lds<0>((const uint16_t *)(a.runimg + ((size_t)q * a.G + g) * RUN_BUF_STRIDE), buf, RUN_BUF_STRIDE / 16,
                        lane);
@@ -1116,10 +1111,11 @@ __device__ __forceinline__ void ahead_load(const KArgs &a, int32_t q_rl, int32_t
         r.pi = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(lane * 16), 0, 0);
     }
 }
+template <int R>
 __device__ __forceinline__ void ahead_store(const KArgs &a, int32_t q_rl, int32_t q_pi, char *lds, uint32_t lane,
                                             const AheadRegs &r) {
     if (q_rl < a.p1) {
-        char *buf = lds + LDS_DESC_OFF + (q_rl % DESC_BUFS) * RUN_BUF_STRIDE;
+        char *buf = lds + LDS_DESC_OFF + (q_rl & (desc_bufs(R) - 1)) * RUN_BUF_STRIDE;
         *(u32x4 *)(buf + lane * 16) = r.rl0;
         if ((int32_t)lane + 64 < RL_CHUNKS) *(u32x4 *)(buf + (64 + lane) * 16) = r.rl1;
     }
@@ -1130,7 +1126,7 @@ __device__ __forceinline__ void ahead_store(const KArgs &a, int32_t q_rl, int32_
     }
 }
 
-template <int B, bool CHAIN, bool TILE>
+template <int B, bool CHAIN, bool TILE, int R>
 __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *lds) {
     const uint32_t lane = lane_id();
     char *desc = lds + LDS_DESC_OFF;
@@ -1139,10 +1135,10 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
     const uint32_t flag_val =
         a.persistent ? __hip_atomic_load(a.run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
     // Run lists: phase q's list is written at the end of iteration
-    // q - DESC_AHEAD (4), after the flag store, into one of DESC_BUFS (4) LDS
-    // buffers (the one phase q - 4 used, which every wave has finished with by
-    // then).  A streaming wave keeps two blocks in flight beyond the one it
-    // consumes, so right after phase q's partials barrier it may load phase
+    // q - AH, after the flag store, into one of NBUF LDS buffers (the one an
+    // earlier phase used, which every wave has finished with by then); AH is
+    // the ring's block buffers + 2 (4 for two buffers).  With two buffers a
+    // streaming wave may, right after phase q's partials barrier, load phase
     // q+2's block and read phase q+3's list header; that list was written
     // before the x-hat barrier of phase q.  A phase's source table and
     // normalisation jobs are written at the end of the iteration before it.
@@ -1152,7 +1148,9 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
     // none of this is on the path between a phase's flags and its x-hat; at
     // batch 1 the flags arrive later than the lists are built here, and the
     // reads would only add latency to the flag stores.
-    for (int32_t q = a.p0; q < a.p1 && q < a.p0 + DESC_AHEAD; ++q) build_runs<CHAIN, TILE>(a, q, g, desc, lane);
+    constexpr int AH = desc_ahead(R), NBUF = desc_bufs(R);
+    static_assert(NBUF <= path_desc_bufs(TILE), "the planner leaves room for this many run lists");
+    for (int32_t q = a.p0; q < a.p1 && q < a.p0 + AH; ++q) build_runs<CHAIN, TILE, R>(a, q, g, desc, lane);
     write_phase_info<CHAIN>(a, a.p0, lds, lane);
     __builtin_amdgcn_s_waitcnt(0);  // copied lists and tables have landed
     wg_barrier();
@@ -1164,7 +1162,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
         float *epi = (float *)(lds + ph.epi_off);
         float *carry = (float *)(lds + ph.carry_off);
         trace_point(a, p, g, 0, lane);
-        const char *rb = desc + (p % DESC_BUFS) * RUN_BUF_STRIDE;
+        const char *rb = desc + (p & (NBUF - 1)) * RUN_BUF_STRIDE;
         const RunHdr &h = *(const RunHdr *)rb;  // in LDS (a register copy passed by reference would go to scratch)
         const Run *runs = (const Run *)(rb + sizeof(RunHdr));
         // the gains do not depend on the previous phase: request them before
@@ -1237,7 +1235,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
         wg_barrier();  // x-hat ready
         // later phases' run list and tables, read while the streaming waves consume
         AheadRegs ahead;
-        if (pre) ahead_load(a, p + DESC_AHEAD, p + 1, g, lane, ahead);
+        if (pre) ahead_load(a, p + AH, p + 1, g, lane, ahead);
         wg_barrier();  // partials complete
         trace_point(a, p, g, 3, lane);
         if (a.trace && lane < 6) {
@@ -1247,7 +1245,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
         }
         epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane);
         trace_point(a, p, g, 4, lane);
-        if (epi_barrier<TILE>() && EPI_BARRIER == 1) wg_barrier();  // stores issued: the streaming waves may refill
+        if (epi_barrier<TILE, R>() && EPI_BARRIER == 1) wg_barrier();  // stores issued: the streaming waves may refill
         if (a.persistent) {
             // outputs are written through (coherent stores); once they have
             // completed, publish this workgroup's flag for phase p
@@ -1256,12 +1254,12 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
                 __builtin_amdgcn_raw_buffer_store_b32(flag_val, rsrc_of(a.flags + (size_t)p * flag_row(a.G)),
                                                       g * FLAG_WORDS * 4, 0, COH);
         }
-        if (epi_barrier<TILE>() && EPI_BARRIER == 2) wg_barrier();  // flag issued too
+        if (epi_barrier<TILE, R>() && EPI_BARRIER == 2) wg_barrier();  // flag issued too
         trace_point(a, p, g, 5, lane);
         if (pre) {
-            ahead_store(a, p + DESC_AHEAD, p + 1, lds, lane, ahead);
+            ahead_store<R>(a, p + AH, p + 1, lds, lane, ahead);
         } else {
-            if (p + DESC_AHEAD < a.p1) build_runs<CHAIN, TILE>(a, p + DESC_AHEAD, g, desc, lane);
+            if (p + AH < a.p1) build_runs<CHAIN, TILE, R>(a, p + AH, g, desc, lane);
             if (p + 1 < a.p1) write_phase_info<CHAIN>(a, p + 1, lds, lane);
         }
     }
@@ -1281,16 +1279,16 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
     }
 }
 
-template <int B, bool CHAIN, bool TILE>
+template <int B, bool CHAIN, bool TILE, int R>
 __global__ __launch_bounds__(THREADS, 1) void chain_kernel(KArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int32_t g = blockIdx.x;
     const int32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w < STREAM_WAVES) {
-        if constexpr (!TILE && INTERLEAVE) stream_wave_il<B, CHAIN>(a, g, w, lds);
-        else stream_wave<B, CHAIN, TILE>(a, g, w, lds);
+        if constexpr (!TILE && ring_interleaved(R)) stream_wave_il<B, CHAIN, R>(a, g, w, lds);
+        else stream_wave<B, CHAIN, TILE, R>(a, g, w, lds);
     }
-    else control_wave<B, CHAIN, TILE>(a, g, lds);
+    else control_wave<B, CHAIN, TILE, R>(a, g, lds);
 }
 
 // ------------------------------------------------------------- touch pass
@@ -1411,35 +1409,55 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t *x, in
 // ------------------------------------------------------------ host launchers
 namespace wgn {
 
-template <int B, bool CHAIN, bool TILE>
+template <int B, bool CHAIN, bool TILE, int R>
 static hipError_t launch_chain_b(const KArgs &a, int32_t grid, size_t lds, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
         // 160 KB of LDS per workgroup on gfx950, minus the kernel's static LDS
-        hipError_t e = hipFuncSetAttribute((const void *)chain_kernel<B, CHAIN, TILE>,
+        hipError_t e = hipFuncSetAttribute((const void *)chain_kernel<B, CHAIN, TILE, R>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((chain_kernel<B, CHAIN, TILE>), dim3(grid), dim3(THREADS), lds, s, a);
+    hipLaunchKernelGGL((chain_kernel<B, CHAIN, TILE, R>), dim3(grid), dim3(THREADS), lds, s, a);
     return hipGetLastError();
 }
 
-template <bool CHAIN>
-static hipError_t launch_chain_c(int32_t batch, bool tile, const KArgs &a, int32_t grid, size_t lds, hipStream_t s) {
-    if (tile) return batch <= MAX_BATCH ? launch_chain_b<MAX_BATCH, CHAIN, true>(a, grid, lds, s) : hipErrorInvalidValue;
-    switch (batch) {
-    case 1: return launch_chain_b<1, CHAIN, false>(a, grid, lds, s);
-    case 2: return launch_chain_b<2, CHAIN, false>(a, grid, lds, s);
-    case 3: return launch_chain_b<3, CHAIN, false>(a, grid, lds, s);
-    case 4: return launch_chain_b<4, CHAIN, false>(a, grid, lds, s);
+template <int B>
+static hipError_t launch_chain_ring(int32_t ring, const KArgs &a, int32_t grid, size_t lds, hipStream_t s) {
+    switch (ring) {
+    case 0: return launch_chain_b<B, true, false, 0>(a, grid, lds, s);
+    case 1: return launch_chain_b<B, true, false, 1>(a, grid, lds, s);
+    case 2: return launch_chain_b<B, true, false, 2>(a, grid, lds, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_chain(int32_t batch, bool tile, const KArgs &a, int32_t grid, size_t lds, hipStream_t s) {
-    return a.phases ? launch_chain_c<true>(batch, tile, a, grid, lds, s)
-                    : launch_chain_c<false>(batch, tile, a, grid, lds, s);
+// Chains run any ring on the vector path; single-stage calls (no program in
+// memory) and the matrix-core path use ring 0.
+hipError_t launch_chain(int32_t batch, bool tile, int32_t ring, const KArgs &a, int32_t grid, size_t lds,
+                        hipStream_t s) {
+    if (tile) {
+        if (batch > MAX_BATCH) return hipErrorInvalidValue;
+        return a.phases ? launch_chain_b<MAX_BATCH, true, true, 0>(a, grid, lds, s)
+                        : launch_chain_b<MAX_BATCH, false, true, 0>(a, grid, lds, s);
+    }
+    if (!a.phases) {
+        switch (batch) {
+        case 1: return launch_chain_b<1, false, false, 0>(a, grid, lds, s);
+        case 2: return launch_chain_b<2, false, false, 0>(a, grid, lds, s);
+        case 3: return launch_chain_b<3, false, false, 0>(a, grid, lds, s);
+        case 4: return launch_chain_b<4, false, false, 0>(a, grid, lds, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (batch) {
+    case 1: return launch_chain_ring<1>(ring, a, grid, lds, s);
+    case 2: return launch_chain_ring<2>(ring, a, grid, lds, s);
+    case 3: return launch_chain_ring<3>(ring, a, grid, lds, s);
+    case 4: return launch_chain_ring<4>(ring, a, grid, lds, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_touch(const TouchRange *r, int32_t n, uint32_t frac_q16, int32_t blocks, hipStream_t s) {

@@ -8,7 +8,8 @@
 //  * row-parts are streamed in "units" of 512 consecutive K elements:
 //      - vector path (batch <= 4): a unit is one row-part's 512 elements =
 //        64 lanes x 16 bytes, one 128-bit load per lane, fully coalesced;
-//        a block of DEPTH (20) units is 20 independent loads;
+//        a block of 8 to 20 units (the ring's depth) is as many independent
+//        loads;
 //      - matrix-core path (any batch, used for batch > 4): a unit is a tile of
 //        16 consecutive row-parts x 512 elements, streamed as 16 loads in
 //        which lane l reads 16 bytes of row l%16 (64 contiguous bytes per row
@@ -57,31 +58,36 @@ constexpr int MAX_RUNS = 8;          // stages per phase (the planner splits lar
 // after the control wave has issued the phase's output stores (which would
 // otherwise queue behind them in the compute unit's memory pipeline)
 constexpr int EPI_BARRIER = WGN_EPI_BARRIER;
-#ifndef WGN_SLOTS
-#define WGN_SLOTS 2
-#endif
-// vector path: block buffers per streaming wave (SLOTS - 1 blocks in flight
-// beyond the one being consumed)
-constexpr int SLOTS = WGN_SLOTS;
-#ifndef WGN_INTERLEAVE
-#define WGN_INTERLEAVE 0
-#endif
-// 1 (vector path): a consumed block's refill is issued one load per unit
-// while the next block is consumed, instead of in one burst right away; a
-// phase's last refill then goes out only after the next phase's x-hat
-// barrier, so no third barrier is needed on that path
-constexpr int INTERLEAVE = WGN_INTERLEAVE;
-#ifndef WGN_DESC_BUFS
-#define WGN_DESC_BUFS 4
-#endif
-// Run lists resident in LDS at once (a ring), and how far ahead of its own
-// iteration the control wave writes one: phase p+DESC_AHEAD's list at the end
-// of iteration p.  A streaming wave reads lists up to SLOTS + 1 phases ahead
-// of the phase it consumes, hence the bound (checked by the host schedule
-// model for each setting).
-constexpr int DESC_BUFS = WGN_DESC_BUFS;
-constexpr int DESC_AHEAD = WGN_DESC_BUFS;
-static_assert(DESC_BUFS >= SLOTS + 2, "the run-list ring must cover the streaming waves' look-ahead");
+// Block-buffer rings of the vector path's streaming waves (the matrix-core
+// path always uses ring 0's two buffers).  A wave keeps slots - 1 blocks of
+// `depth` units in flight beyond the one it consumes:
+//   ring 0: 2 buffers x 20 units, a consumed buffer refilled in one burst;
+//   ring 1: 5 buffers x 8 units, refilled in one burst;
+//   ring 2: 4 buffers x 10 units, a consumed buffer's loads issued one per
+//           unit while the next buffer is consumed (a phase's last refill
+//           then goes out after the next phase's x-hat barrier, so that path
+//           needs no third barrier).
+// Measured on the decode step and the LayerNorm chain: ring 0 is fastest at
+// batch 1 with large phases, ring 2 at batch 2-4 with large phases, ring 1
+// when phases give each wave only a few units (many phases in flight).
+constexpr int NUM_RINGS = 3;
+constexpr int ring_slots(int r) { return r == 1 ? 5 : r == 2 ? 4 : 2; }
+constexpr int ring_depth(int r) { return r == 1 ? 8 : r == 2 ? 10 : 20; }
+constexpr bool ring_interleaved(int r) { return r == 2; }
+constexpr int MAX_SLOTS = 5;
+// Run lists resident in LDS at once (a ring of desc_bufs(r), a power of two,
+// so the index is a mask), and how far ahead of its own iteration the control
+// wave writes one: phase p+desc_ahead(r)'s list at the end of iteration p.  A
+// streaming wave reads lists up to slots + 1 phases ahead of the phase it
+// consumes, hence slots + 2 (checked by the host schedule model for every
+// ring).  A larger look-ahead than needed costs: every list up to it is built
+// before the first phase starts, and at batch 1 those are built in place.
+constexpr int desc_bufs(int r) { return ring_slots(r) + 2 <= 4 ? 4 : 8; }
+constexpr int desc_ahead(int r) { return ring_slots(r) + 2; }
+constexpr int MAX_DESC_BUFS = 8;
+static_assert(desc_bufs(0) <= MAX_DESC_BUFS && desc_bufs(1) <= MAX_DESC_BUFS && desc_bufs(2) <= MAX_DESC_BUFS &&
+                  ring_slots(0) <= MAX_SLOTS && ring_slots(1) <= MAX_SLOTS && ring_slots(2) <= MAX_SLOTS,
+              "ring tables out of range");
 constexpr uint64_t WAIT_TICKS = 200000000ull;  // 2 s at the 100 MHz real-time clock
 
 enum { NORM_NONE = 0, NORM_RMS = 1, NORM_LAYER = 2 };
@@ -340,8 +346,7 @@ WGN_HD NormSplit norm_split(int32_t nb, int32_t w, uint32_t lane, int32_t nw) {
 }
 
 
-constexpr int LDS_DESC_OFF = 0;
-constexpr int LDS_TRACE_OFF = DESC_BUFS * RUN_BUF_STRIDE;
+constexpr int LDS_TRACE_OFF = 0;
 constexpr int LDS_NORM_OFF = LDS_TRACE_OFF + 2 * 6 * 8;  // 6 streaming-wave timestamps per phase parity
 // partial statistics: [wave][normalisation item of that wave][sum, sum of squares], FP64;
 // items are (source, batch row) pairs, at most MAX_SRC * MAX_BATCH = 64 over WAVES waves
@@ -371,7 +376,13 @@ constexpr int PHASE_INFO_BYTES = MAX_SRC * (int)sizeof(SrcInfo) + (int)sizeof(No
 static_assert(PHASE_INFO_BYTES % 16 == 0 && PHASE_INFO_BYTES <= 64 * 16, "phase info fits one 16-byte read per lane");
 static_assert(MAX_SRC * MAX_BATCH <= WAVES * STATS_ROWS, "normalisation items must fit the statistics slots");
 constexpr int LDS_SRC_OFF = (LDS_STATS_OFF + WAVES * STATS_ROWS * 16 + 15) & ~15;
-constexpr int LDS_DYN_OFF = (LDS_SRC_OFF + MAX_SRC * (int)sizeof(SrcInfo) + 255) & ~255;
+// The run-list ring comes last among the fixed areas; its size depends on the
+// streaming waves' ring, so the per-phase areas of a program start at
+// lds_dyn_off(run lists): the matrix-core path always streams with ring 0
+// (4 lists), the vector path leaves room for any ring.
+constexpr int LDS_DESC_OFF = (LDS_SRC_OFF + MAX_SRC * (int)sizeof(SrcInfo) + 15) & ~15;
+constexpr int lds_dyn_off(int nbufs) { return (LDS_DESC_OFF + nbufs * RUN_BUF_STRIDE + 255) & ~255; }
+constexpr int path_desc_bufs(bool tile) { return tile ? desc_bufs(0) : MAX_DESC_BUFS; }
 
 // Per-(WG, stage) geometry inside a phase.
 struct StageSpan {
