@@ -664,6 +664,14 @@ __device__ __forceinline__ void consume_any(const KArgs &a, const u32x4 (&d)[blo
 template <bool TILE, int R>
 constexpr bool epi_barrier() { return EPI_BARRIER != 0 && (TILE || !ring_interleaved(R)); }
 
+// Whether all waves share the epilogue's output rows (burst ring 0 only: at
+// the third barrier a streaming wave has just one older block in flight, so
+// waiting for its own stores costs little).
+template <bool TILE, int R>
+constexpr bool epi_share() {
+    return R == 0 && EPI_BARRIER == 1 && (EPI_SHARE == 2 || (EPI_SHARE == 1 && TILE));
+}
+
 // Vector path with interleaved refills.  Slot k's refill is prepared (run
 // list read, addresses computed) right after slot k is consumed and issued,
 // one load per unit, while slot k+1 is consumed; NS - 2 blocks are fully
@@ -772,6 +780,17 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
             if (end) {
                 if (tw) tl[(p & 1) * 6 + 2] = wall_clock64();
                 wg_barrier();  // partials of phase p are complete
+                if constexpr (epi_share<TILE, R>()) {
+                    // this wave's share of the phase's output rows; its stores
+                    // (and its one older block of weight loads) complete
+                    // before the third barrier
+                    const RunHdr &hh = *(const RunHdr *)run_buf_s(S, p);
+                    const Run *rr = (const Run *)((const char *)&hh + sizeof(RunHdr));
+                    epilogue<B, CHAIN, TILE>(a, hh, rr, g, (const float *)(lds + hh.part_off),
+                                             (const float *)(lds + hh.epi_off), (float *)(lds + hh.carry_off), lane,
+                                             w, WAVES, false);
+                    __builtin_amdgcn_s_waitcnt(0);
+                }
                 if (epi_barrier<TILE, R>()) wg_barrier();  // the control wave has issued phase p's stores
             }
             load_any<B, TILE, R>(a, S, d[k], m[k], lane);
@@ -992,15 +1011,17 @@ __device__ __forceinline__ void row_sums(const RunHdr &h, const Run &r, int32_t 
 // are reduced afterwards, one at a time.
 template <int B, bool CHAIN, bool TILE>
 __device__ __forceinline__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32_t g, const float *part,
-                         const float *epi, float *carry, uint32_t lane) {
+                         const float *epi, float *carry, uint32_t lane, int32_t wsel, int32_t nw, bool with_argmax) {
     const int32_t nb = a.nb;
     const LaneSplit ls = lane_split(nb, lane);
     const int32_t b = ls.b;
     // row starts are read from the LDS header: indexing the register copy with
     // a per-lane index would move it to scratch memory
     const int32_t *rstart = ((const RunHdr *)((const char *)runs - sizeof(RunHdr)))->rstart;
-    const int32_t total = ls.active ? rstart[MAX_RUNS] : 0;
-    for (int32_t k = ls.i0; k < total; k += ls.step) {
+    // this wave's share of the output rows: wave wsel of nw (none for nw = 0)
+    const int32_t total = ls.active && nw > 0 ? rstart[MAX_RUNS] : 0;
+    const int32_t kstep = ls.step * (nw > 0 ? nw : 1);
+    for (int32_t k = ls.i0 + ls.step * wsel; k < total; k += kstep) {
         int32_t ri = 0;
 #pragma unroll
         for (int32_t j = 1; j < MAX_RUNS; ++j) ri += rstart[j] <= k ? 1 : 0;
@@ -1030,7 +1051,7 @@ __device__ __forceinline__ void epilogue(const KArgs &a, const RunHdr &h, const 
             __builtin_amdgcn_raw_buffer_store_b16(f2bf(bf2f(o) + ep[1 + nb + b]), rsrc_of(r.post_y),
                                                   (int)(((int64_t)b * r.post_stride + n) * 2), 0, COH);
     }
-    for (int32_t ri = 0; ri < h.nruns; ++ri) {
+    for (int32_t ri = 0; with_argmax && ri < h.nruns; ++ri) {
         const Run &r = runs[ri];
         if (r.epi != EPI_ARGMAX) continue;
         const int32_t nrows = ls.active ? r.nrows : 0;
@@ -1243,9 +1264,19 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
             a.trace[((size_t)p * a.G + g) * TRACE_POINTS + 6 + lane] = tl[(p & 1) * 6 + lane];
             if (lane >= 3) tl[(p & 1) * 6 + lane] = 0;  // per-block slots: cleared for phase p + 2
         }
-        epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane);
-        trace_point(a, p, g, 4, lane);
-        if (epi_barrier<TILE, R>() && EPI_BARRIER == 1) wg_barrier();  // stores issued: the streaming waves may refill
+        if constexpr (epi_share<TILE, R>()) {
+            // every wave stores its share of the rows and waits for its own
+            // stores; after the barrier all of them have completed
+            epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane, STREAM_WAVES, WAVES, false);
+            __builtin_amdgcn_s_waitcnt(0);
+            trace_point(a, p, g, 4, lane);
+            wg_barrier();  // every wave's stores have completed: the streaming waves may refill
+            epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane, 0, 0, true);  // argmax stages
+        } else {
+            epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane, 0, 1, true);
+            trace_point(a, p, g, 4, lane);
+            if (epi_barrier<TILE, R>() && EPI_BARRIER == 1) wg_barrier();  // stores issued: the streaming waves may refill
+        }
         if (a.persistent) {
             // outputs are written through (coherent stores); once they have
             // completed, publish this workgroup's flag for phase p

@@ -97,9 +97,10 @@ WGN_HD void make_runs(const KArgs &a, int32_t p, int32_t g, bool tile, RunHdr &h
     h.xb_bytes = G.xb_bytes;
     h.x_off = G.x_off;
     h.part_off = G.part_off;
-    h.pad1 = 0;
     {
         const DevPhase ph = phase_of<CHAIN>(a, p);
+        h.epi_off = ph.epi_off;
+        h.carry_off = ph.carry_off;
         int32_t hn = 0;
         for (int32_t i = 0; i < ph.nsrc; ++i) hn |= source_of<CHAIN>(a, ph.src0 + i).norm != NORM_NONE ? 1 : 0;
         h.has_norm = hn;

@@ -58,6 +58,13 @@ constexpr int MAX_RUNS = 8;          // stages per phase (the planner splits lar
 // after the control wave has issued the phase's output stores (which would
 // otherwise queue behind them in the compute unit's memory pipeline)
 constexpr int EPI_BARRIER = WGN_EPI_BARRIER;
+#ifndef WGN_EPI_SHARE
+#define WGN_EPI_SHARE 1
+#endif
+// Which kernels run the epilogue's output rows on all waves (each wave then
+// waits for its own stores before the third barrier, so the flag follows all
+// of them): 0 none, 1 the matrix-core path, 2 every burst-refill ring-0 kernel.
+constexpr int EPI_SHARE = WGN_EPI_SHARE;
 // Block-buffer rings of the vector path's streaming waves (the matrix-core
 // path always uses ring 0's two buffers).  A wave keeps slots - 1 blocks of
 // `depth` units in flight beyond the one it consumes:
@@ -256,10 +263,11 @@ struct RunHdr {
     int32_t nruns, U, jmax, xb_bytes;  // xb_bytes: x-hat row stride
     int32_t x_off, part_off;           // LDS byte offsets of x-hat and the partial slots
     int32_t has_norm;                  // the phase normalises an input (all waves take part)
-    int32_t pad1;
+    int32_t epi_off;                   // LDS byte offset of the staged epilogue inputs
     int32_t wb[STREAM_WAVES + 1];      // wave_begin(w) for w = 0..STREAM_WAVES
     int32_t rstart[MAX_RUNS + 1];      // first WG-local output row of each run (cumulative nrows)
-    int32_t pad2;                      // the runs that follow the header start 8-byte aligned
+    int32_t carry_off;                 // LDS byte offset of the K-window carry (also keeps the runs
+                                       // that follow the header 8-byte aligned)
 };
 // Run lists are built on the host for chains and copied into LDS as bytes, so
 // the host and device compilations must agree on the layout.
