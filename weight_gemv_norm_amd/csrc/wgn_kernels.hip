@@ -789,6 +789,8 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
                     epilogue<B, CHAIN, TILE>(a, hh, rr, g, (const float *)(lds + hh.part_off),
                                              (const float *)(lds + hh.epi_off), (float *)(lds + hh.carry_off), lane,
                                              w, WAVES, false);
+                    argmax_shared<TILE>(a, hh, rr, g, (const float *)(lds + hh.part_off), (float *)(lds + hh.carry_off),
+                                        lds, lane, w);
                     __builtin_amdgcn_s_waitcnt(0);
                 }
                 if (epi_barrier<TILE, R>()) wg_barrier();  // the control wave has issued phase p's stores
@@ -1095,6 +1097,76 @@ __device__ __forceinline__ void epilogue(const KArgs &a, const RunHdr &h, const 
     }
 }
 
+// Argmax stages of a phase, with every wave of the workgroup taking part:
+// each wave reduces its share of the rows to one key per batch row, posts it
+// in LDS (the normalisation statistics area, idle at this point of a phase),
+// and after a barrier the control wave combines the waves' keys in wave order
+// and publishes the workgroup's key as in the single-wave epilogue.  All
+// waves pass the same two barriers per argmax stage.
+template <bool TILE>
+__device__ __forceinline__ void argmax_shared(const KArgs &a, const RunHdr &h, const Run *runs, int32_t g,
+                                              const float *part, float *carry, char *lds, uint32_t lane, int32_t w) {
+    static_assert(WAVES * MAX_BATCH * 8 <= WAVES * STATS_ROWS * 16, "argmax keys fit the statistics area");
+    uint64_t *keys = (uint64_t *)(lds + LDS_STATS_OFF);
+    const int32_t nb = a.nb;
+    const LaneSplit ls = lane_split(nb, lane);
+    const int32_t b = ls.b;
+    const int32_t nr = uniform_i32(h.nruns);
+    for (int32_t ri = 0; ri < nr; ++ri) {
+        const Run &r = runs[ri];
+        if (uniform_i32(r.epi) != EPI_ARGMAX) continue;
+        const bool co = (uniform_i32(r.carry) & CARRY_OUT) != 0;
+        const int32_t nrows = ls.active ? r.nrows : 0;
+        const int32_t N = uniform_i32(r.N), row0 = uniform_i32(r.row0);
+        float *logits = uniform_ptr(r.logits);
+        uint64_t best = 0;
+        for (int32_t i = ls.i0 + ls.step * w; i < nrows; i += ls.step * WAVES) {
+            const int32_t n = row0 + i;
+            float acc[2];
+            row_sums<TILE>(h, r, i, b, nb, part, carry, acc);
+            if (co) continue;
+            const float z = acc[0];
+            if (logits)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z), rsrc_of(logits),
+                                                      (int)(((int64_t)b * N + n) * 4), 0, 0);
+            const uint64_t key = ((uint64_t)orderable(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
+            best = key > best ? key : best;
+        }
+        // maximum over the lanes serving the same batch row
+        for (int32_t o = ls.P; o < 64; o <<= 1) {
+            const uint64_t t = __shfl_xor(best, o);
+            best = t > best ? t : best;
+        }
+        if (!co && (int32_t)lane < nb) keys[w * nb + (int32_t)lane] = best;
+        wg_barrier();  // every wave's keys are posted
+        if (w == STREAM_WAVES && !co) {
+            const int32_t am_slot = uniform_i32(r.am_slot);
+            uint64_t k = 0;
+            if ((int32_t)lane < nb)
+                for (int32_t ww = 0; ww < WAVES; ++ww) {
+                    const uint64_t t = keys[ww * nb + (int32_t)lane];
+                    k = t > k ? t : k;
+                }
+            if ((int32_t)lane < nb)
+                __hip_atomic_store(&a.am_part[((size_t)am_slot * a.G + g) * nb + lane], k, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            // the partial keys are agent-scope atomic stores; once they have
+            // completed, the ticket tells the last workgroup to merge them
+            __builtin_amdgcn_s_waitcnt(0);
+            uint32_t old = 0;
+            if (lane == 0)
+                old = __hip_atomic_fetch_add(&a.tickets[am_slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __shfl(old, 0);
+            if (old == (uint32_t)(a.G - 1)) {
+                argmax_merge(a, am_slot, uniform_ptr(r.y), uniform_ptr(r.maxval), lane);
+                if (lane == 0)
+                    __hip_atomic_store(&a.tickets[am_slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        wg_barrier();  // the keys area may be reused
+    }
+}
+
 // Write phase q's run list for workgroup g into its LDS buffer: a copy of the
 // precomputed list for chains (asynchronous: memory to LDS), else built here.
 template <bool CHAIN, bool TILE, int R>
@@ -1268,10 +1340,10 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
             // every wave stores its share of the rows and waits for its own
             // stores; after the barrier all of them have completed
             epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane, STREAM_WAVES, WAVES, false);
+            argmax_shared<TILE>(a, h, runs, g, part, carry, lds, lane, STREAM_WAVES);
             __builtin_amdgcn_s_waitcnt(0);
             trace_point(a, p, g, 4, lane);
             wg_barrier();  // every wave's stores have completed: the streaming waves may refill
-            epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane, 0, 0, true);  // argmax stages
         } else {
             epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane, 0, 1, true);
             trace_point(a, p, g, 4, lane);
