@@ -99,7 +99,7 @@ class Wave:
         self.events.append((self.epoch, kind, phase))
 
 
-def control_events(p0, p1, desc_ahead=DESC_AHEAD, norm=None, epi_barrier=EPI_BARRIER):
+def control_events(p0, p1, desc_ahead=DESC_AHEAD, norm=None, epi_barrier=EPI_BARRIER, share=False):
     """The control wave's loop: run-list builds, x-hat writes, partial reads.
     Phase q's run list is written at the end of iteration q - desc_ahead
     (after the flag store), and a phase's normalisation jobs at the end of the
@@ -114,6 +114,8 @@ def control_events(p0, p1, desc_ahead=DESC_AHEAD, norm=None, epi_barrier=EPI_BAR
     c.barrier()
     for p in range(p0, p1):
         c.ev("read_runs", p)       # header and run list of phase p (epilogue inputs)
+        if share:
+            c.barrier()            # flags seen: every wave copies its share of the inputs
         c.ev("write_xhat", p)      # raw inputs (and, without a norm, x-hat itself)
         if norm.get(p):
             c.barrier()            # inputs landed (the jobs were posted earlier)
@@ -136,7 +138,7 @@ def control_events(p0, p1, desc_ahead=DESC_AHEAD, norm=None, epi_barrier=EPI_BAR
     return c
 
 
-def stream_events(p0, p1, nblocks, norm=None, epi_barrier=EPI_BARRIER, slots=2):
+def stream_events(p0, p1, nblocks, norm=None, epi_barrier=EPI_BARRIER, slots=2, share=False):
     """One streaming wave's loop with a ring of `slots` block buffers.  nblocks[p] >= 1 is
     the number of blocks the wave walks in phase p (an empty share is one empty
     block)."""
@@ -170,7 +172,11 @@ def stream_events(p0, p1, nblocks, norm=None, epi_barrier=EPI_BARRIER, slots=2):
         return ("blk", p, last)
 
     def phase_start(p):
-        """Norm steps (if any) and the x-hat barrier of phase p."""
+        """Input copies (shared), norm steps (if any) and the x-hat barrier of phase p."""
+        if share:
+            s.barrier()            # flags seen
+            s.ev("read_runs", p)   # the phase's x-hat offset and row stride
+            s.ev("write_xhat", p)  # this wave's share of the input copies
         s.ev("read_runs", p)       # the phase's header: normalised input?
         if norm.get(p):
             s.barrier()            # inputs landed, jobs posted
@@ -199,6 +205,9 @@ def stream_events(p0, p1, nblocks, norm=None, epi_barrier=EPI_BARRIER, slots=2):
             end = ring[i][2]
             if end:
                 s.barrier()        # partials of phase p
+                if share:
+                    s.ev("read_runs", p)   # this wave's share of the epilogue rows
+                    s.ev("read_part", p)
                 if epi_barrier:
                     s.barrier()    # epilogue stores of phase p issued
             ring[i] = load_block()
@@ -210,10 +219,11 @@ def stream_events(p0, p1, nblocks, norm=None, epi_barrier=EPI_BARRIER, slots=2):
 
 
 def check_schedule(p0, p1, nblocks, desc_bufs=DESC_BUFS, desc_ahead=DESC_AHEAD, norm=None,
-                   slots=SLOTS, interleave=INTERLEAVE):
+                   slots=SLOTS, interleave=INTERLEAVE, share=False):
+    """share: the matrix-core path's shared input copies and epilogue rows."""
     epi = 0 if interleave else EPI_BARRIER
-    c = control_events(p0, p1, desc_ahead, norm, epi_barrier=epi)
-    waves = [stream_events(p0, p1, nb, norm, epi_barrier=epi, slots=slots) for nb in nblocks]
+    c = control_events(p0, p1, desc_ahead, norm, epi_barrier=epi, share=share)
+    waves = [stream_events(p0, p1, nb, norm, epi_barrier=epi, slots=slots, share=share) for nb in nblocks]
     errors = []
     for s in waves:
         if s.epoch != c.epoch:
@@ -249,7 +259,12 @@ def check_schedule(p0, p1, nblocks, desc_bufs=DESC_BUFS, desc_ahead=DESC_AHEAD, 
         if prev is not None and not all(min(stats_w[q]) > r for r in reads_stats[prev]):
             errors.append("statistics of %d overwritten while phase %d reads them" % (prev, q))
         prev = q
-    part_read = {q: e for e, k, q in c.events if k == "read_part"}
+    part_first, part_last = {}, {}   # earliest and latest epilogue read of each phase's partials
+    for w in [c] + waves:
+        for e, k, q in w.events:
+            if k == "read_part":
+                part_first[q] = min(part_first.get(q, e), e)
+                part_last[q] = max(part_last.get(q, e), e)
     for q in range(p0, p1):
         if q not in build_epoch:
             errors.append("phase %d never built" % q)
@@ -278,9 +293,9 @@ def check_schedule(p0, p1, nblocks, desc_bufs=DESC_BUFS, desc_ahead=DESC_AHEAD, 
                 if q + 1 in xhat_first and not e < xhat_first[q + 1]:
                     errors.append("x-hat %d read after phase %d overwrote it" % (q, q + 1))
             if k == "write_part":
-                if not e < part_read[q]:
+                if not e < part_first[q]:
                     errors.append("partials of %d written after the epilogue read them" % q)
-                if q - 1 in part_read and not e > part_read[q - 1]:
+                if q - 1 in part_last and not e > part_last[q - 1]:
                     errors.append("partials of %d written before the epilogue of %d" % (q, q - 1))
     return errors
 
@@ -360,6 +375,20 @@ def test_schedule_every_ring_with_the_header_constants(ring):
 
 def test_ring_table_parsed():
     assert RINGS == [(2, False), (5, False), (4, True)]
+
+
+def test_schedule_matrix_core_path_with_shared_inputs_and_epilogue():
+    """The matrix-core path (ring 0, third barrier) with every wave copying
+    inputs after an extra barrier and summing epilogue rows after the
+    partials barrier."""
+    rng = random.Random(77)
+    for _ in range(2000):
+        P = rng.randint(1, 12)
+        W = rng.randint(1, 7)
+        nb = [[rng.choice([1, 1, 1, 2, 3, 5]) for _ in range(P)] for _ in range(W)]
+        norm = {p: rng.random() < 0.6 for p in range(P)}
+        errs = check_schedule(0, P, nb, desc_bufs=4, desc_ahead=4, norm=norm, slots=2, interleave=0, share=True)
+        assert not errs, (P, nb, norm, errs[:3])
 
 
 def test_model_detects_short_ring_for_more_slots():

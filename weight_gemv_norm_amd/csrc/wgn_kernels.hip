@@ -671,6 +671,15 @@ template <bool TILE, int R>
 constexpr bool epi_share() {
     return R == 0 && EPI_BARRIER == 1 && (EPI_SHARE == 2 || (EPI_SHARE == 1 && TILE));
 }
+// Whether all waves share the input copies of a phase (the matrix-core path):
+// one more barrier per phase (the flags have been seen), after which every
+// wave issues its share of the copies and waits for them -- on that path a
+// streaming wave then has only one block of weight loads in flight, issued
+// well before.
+template <bool TILE, int R>
+constexpr bool in_share() {
+    return IN_SHARE && TILE && R == 0;
+}
 
 // Vector path with interleaved refills.  Slot k's refill is prepared (run
 // list read, addresses computed) right after slot k is consumed and issued,
@@ -733,6 +742,24 @@ __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_
     }
 }
 
+template <int B, bool CHAIN>
+__device__ __forceinline__ void issue_source_loads(const KArgs &a, int32_t nsrc, int32_t xb, const char *lds,
+                                                   char *xh, uint32_t lane, int32_t w, int32_t nw, bool zero_tail);
+
+// A streaming wave's part of phase p's input copies (when the phase's header
+// asks for shared copies): after the barrier that follows the control wave's
+// wait for the flags, copy every WAVES-th 1 KB of the inputs and wait for
+// those copies (and this wave's older weight loads).
+template <int B, bool CHAIN>
+__device__ __forceinline__ void share_inputs(const KArgs &a, const StreamState &S, int32_t p, char *lds,
+                                             uint32_t lane, int32_t w) {
+    const RunHdr &hh = *(const RunHdr *)run_buf_s(S, p);
+    if (!hh.share_in) return;
+    wg_barrier();  // the control wave has seen phase p-1's flags
+    issue_source_loads<B, CHAIN>(a, MAX_SRC, hh.xb_bytes / 2, lds, lds + hh.x_off, lane, w, WAVES, false);
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
 template <int B, bool CHAIN, bool TILE, int R>
 __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w, char *lds) {
     constexpr int NS = TILE ? 2 : ring_slots(R);
@@ -764,6 +791,7 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
     const bool tw = a.trace && w == 0 && lane == 0;
 #pragma unroll
     for (int k = 0; k < NS; ++k) load_any<B, TILE, R>(a, S, d[k], m[k], lane);
+    if constexpr (in_share<TILE, R>()) share_inputs<B, CHAIN>(a, S, a.p0, lds, lane, w);
     if (((const RunHdr *)run_buf_s(S, a.p0))->has_norm) norm_all(lds, w, lane);
     wg_barrier();  // x-hat of the first phase is ready
     bool ok = abort_flag_get() == 0;
@@ -799,6 +827,7 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
             if (end) nblk = 0;
             if (end && ++p < a.p1) {
                 if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
+                if constexpr (in_share<TILE, R>()) share_inputs<B, CHAIN>(a, S, p, lds, lane, w);
                 if (((const RunHdr *)run_buf_s(S, p))->has_norm) norm_all(lds, w, lane);
                 wg_barrier();  // x-hat of phase p is ready
                 ok = abort_flag_get() == 0;
@@ -890,10 +919,17 @@ __device__ void write_phase_info(const KArgs &a, int32_t p, char *lds, uint32_t 
 // input chunks are requested at once (one memory round trip) together with the
 // epilogue's bias/residual values, then the statistics and the normalisation
 // run out of LDS.
+// Copy the phase's inputs (every batch row of every source, from the source
+// table in LDS) into x-hat with coherent LDS-DMA loads, 1 KB per wave
+// instruction.  The copies are numbered across sources and batch rows and
+// wave w of nw issues every nw-th one; the zero padding of each row's last
+// unit is written by the wave with zero_tail.  Asynchronous: the caller waits.
 template <int B, bool CHAIN>
-__device__ void issue_source_loads(const KArgs &a, const DevPhase &ph, const char *lds, char *xh, uint32_t lane) {
+__device__ __forceinline__ void issue_source_loads(const KArgs &a, int32_t nsrc, int32_t xb, const char *lds,
+                                                   char *xh, uint32_t lane, int32_t w, int32_t nw,
+                                                   bool zero_tail) {
     const SrcInfo *T = (const SrcInfo *)(lds + LDS_SRC_OFF);
-    const int32_t nb = a.nb, nsrc = ph.nsrc;
+    const int32_t nb = a.nb;
     // every entry is read at once (one LDS round trip), then the copies issued
     const uint16_t *x[MAX_SRC];
     int64_t xs[MAX_SRC];
@@ -905,6 +941,7 @@ __device__ void issue_source_loads(const KArgs &a, const DevPhase &ph, const cha
         K[j] = T[j].K;
         lo[j] = T[j].lds_off;
     }
+    int32_t base = 0;  // copies numbered so far
 #pragma unroll
     for (int j = 0; j < MAX_SRC; ++j) {
         if (j >= nsrc) break;
@@ -913,17 +950,24 @@ __device__ void issue_source_loads(const KArgs &a, const DevPhase &ph, const cha
         const int32_t n8 = uniform_i32(K[j]) >> 3;
         const int32_t padded8 = nchunks_of(uniform_i32(K[j])) * (UNIT / 8);
         const int32_t off = uniform_i32(lo[j]);
+        const int32_t nit = (n8 + 63) >> 6;
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             if (b >= nb) break;
-            char *dst = xh + ((size_t)b * ph.xb + off) * 2;
-            copy_to_lds<COH>(src + (int64_t)b * stride, dst, n8, lane);
-            for (int32_t i = n8 + lane; i < padded8; i += 64) *(u32x4 *)(dst + i * 16) = (u32x4){0u, 0u, 0u, 0u};
+            char *dst = xh + ((size_t)b * xb + off) * 2;
+            const uint16_t *sb = src + (int64_t)b * stride;
+            int32_t it = w - base % nw;
+            if (it < 0) it += nw;
+            for (; it < nit; it += nw)
+                if (it * 64 + (int32_t)lane < n8)
+                    __builtin_amdgcn_global_load_lds((const WGN_GAS void *)(sb + ((size_t)it * 64 + lane) * 8),
+                                                     (WGN_LAS void *)(dst + it * 1024), 16, 0, COH);
+            base += nit;
+            if (zero_tail)
+                for (int32_t i = n8 + lane; i < padded8; i += 64) *(u32x4 *)(dst + i * 16) = (u32x4){0u, 0u, 0u, 0u};
         }
     }
 }
-
-
 
 // While the streaming waves stream, stage the epilogue's inputs of this
 // workgroup's rows into LDS.  Row-part rp's record (epi_rec(nb) floats) holds
@@ -1309,8 +1353,10 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
                     abort_flag_set(1);
                     __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                // meet the streaming waves at this phase's barriers (norm
-                // steps, x-hat); they then see the abort flag and exit
+                // meet the streaming waves at this phase's barriers (input
+                // copies, norm steps, x-hat); they then see the abort flag and
+                // exit
+                if (in_share<TILE, R>() && h.share_in) wg_barrier();
                 if (h.has_norm) {
                     wg_barrier();
                     wg_barrier();
@@ -1320,7 +1366,12 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
             }
         }
         trace_point(a, p, g, 1, lane);
-        issue_source_loads<B, CHAIN>(a, ph, lds, xh, lane);
+        if (in_share<TILE, R>() && h.share_in) {
+            wg_barrier();  // the flags have been seen: every wave copies its share of the inputs
+            issue_source_loads<B, CHAIN>(a, ph.nsrc, ph.xb, lds, xh, lane, STREAM_WAVES, WAVES, true);
+        } else {
+            issue_source_loads<B, CHAIN>(a, ph.nsrc, ph.xb, lds, xh, lane, 0, 1, true);
+        }
         stage_epilogue_inputs<B, CHAIN>(a, h, runs, epi, lane);
         __builtin_amdgcn_s_waitcnt(0);  // inputs, gains and epilogue values have landed
         if (h.has_norm) norm_all(lds, STREAM_WAVES, lane);

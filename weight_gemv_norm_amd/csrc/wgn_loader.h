@@ -102,8 +102,15 @@ WGN_HD void make_runs(const KArgs &a, int32_t p, int32_t g, bool tile, RunHdr &h
         h.epi_off = ph.epi_off;
         h.carry_off = ph.carry_off;
         int32_t hn = 0;
-        for (int32_t i = 0; i < ph.nsrc; ++i) hn |= source_of<CHAIN>(a, ph.src0 + i).norm != NORM_NONE ? 1 : 0;
+        int64_t in_bytes = 0;
+        for (int32_t i = 0; i < ph.nsrc; ++i) {
+            const DevSource src = source_of<CHAIN>(a, ph.src0 + i);
+            hn |= src.norm != NORM_NONE ? 1 : 0;
+            in_bytes += (int64_t)src.K * a.nb * 2;
+        }
         h.has_norm = hn;
+        h.share_in = tile && in_bytes >= SHARE_IN_MIN_BYTES ? 1 : 0;
+        h.pad3 = 0;
     }
     for (int32_t w = 0; w <= STREAM_WAVES; ++w) h.wb[w] = G.U > 0 ? wave_begin(w, G.U, STREAM_WAVES) : 0;
     int32_t n = 0, u_base = 0, rp_base = 0, rows = 0;

@@ -65,6 +65,15 @@ constexpr int EPI_BARRIER = WGN_EPI_BARRIER;
 // waits for its own stores before the third barrier, so the flag follows all
 // of them): 0 none, 1 the matrix-core path, 2 every burst-refill ring-0 kernel.
 constexpr int EPI_SHARE = WGN_EPI_SHARE;
+#ifndef WGN_IN_SHARE
+#define WGN_IN_SHARE 1
+#endif
+// 1: on the matrix-core path all waves share the input copies of a phase
+// whose inputs are at least SHARE_IN_MIN_BYTES per workgroup (below that the
+// extra barrier and the streaming waves' wait for their newest weight loads
+// cost more than the copies take)
+constexpr int IN_SHARE = WGN_IN_SHARE;
+constexpr int SHARE_IN_MIN_BYTES = 32 * 1024;
 // Block-buffer rings of the vector path's streaming waves (the matrix-core
 // path always uses ring 0's two buffers).  A wave keeps slots - 1 blocks of
 // `depth` units in flight beyond the one it consumes:
@@ -266,13 +275,14 @@ struct RunHdr {
     int32_t epi_off;                   // LDS byte offset of the staged epilogue inputs
     int32_t wb[STREAM_WAVES + 1];      // wave_begin(w) for w = 0..STREAM_WAVES
     int32_t rstart[MAX_RUNS + 1];      // first WG-local output row of each run (cumulative nrows)
-    int32_t carry_off;                 // LDS byte offset of the K-window carry (also keeps the runs
-                                       // that follow the header 8-byte aligned)
+    int32_t carry_off;                 // LDS byte offset of the K-window carry
+    int32_t share_in;                  // matrix-core path: all waves copy the phase's inputs
+    int32_t pad3;                      // the runs that follow the header start 8-byte aligned
 };
 // Run lists are built on the host for chains and copied into LDS as bytes, so
 // the host and device compilations must agree on the layout.
 static_assert(sizeof(Run) == 160 && alignof(Run) == 8, "Run layout");
-static_assert(sizeof(RunHdr) == 104, "RunHdr layout");
+static_assert(sizeof(RunHdr) == 112, "RunHdr layout");
 // Floats per row-part in the staged epilogue inputs: bias, then the residual
 // of each batch row, then the addend of a fused residual add per batch row.
 WGN_HD int32_t epi_rec(int32_t nb) { return 1 + 2 * nb; }
