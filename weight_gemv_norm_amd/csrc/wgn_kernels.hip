@@ -678,7 +678,25 @@ constexpr bool epi_share() {
 // well before.
 template <bool TILE, int R>
 constexpr bool in_share() {
-    return IN_SHARE && TILE && R == 0;
+    return IN_SHARE && ((TILE && R == 0) || (IN_SHARE == 2 && !TILE && ring_interleaved(R)));
+}
+
+template <int B, bool CHAIN>
+__device__ __forceinline__ void issue_source_loads(const KArgs &a, int32_t nsrc, int32_t xb, const char *lds,
+                                                   char *xh, uint32_t lane, int32_t w, int32_t nw, bool zero_tail);
+
+// A streaming wave's part of phase p's input copies (when the phase's header
+// asks for shared copies): after the barrier that follows the control wave's
+// wait for the flags, copy every WAVES-th 1 KB of the inputs and wait for
+// those copies (and this wave's older weight loads).
+template <int B, bool CHAIN>
+__device__ __forceinline__ void share_inputs(const KArgs &a, const StreamState &S, int32_t p, char *lds,
+                                             uint32_t lane, int32_t w) {
+    const RunHdr &hh = *(const RunHdr *)run_buf_s(S, p);
+    if (!hh.share_in) return;
+    wg_barrier();  // the control wave has seen phase p-1's flags
+    issue_source_loads<B, CHAIN>(a, MAX_SRC, hh.xb_bytes / 2, lds, lds + hh.x_off, lane, w, WAVES, false);
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 // Vector path with interleaved refills.  Slot k's refill is prepared (run
@@ -712,6 +730,7 @@ __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_
 #pragma unroll
     for (int k = 0; k < NS - 1; ++k) load_block<B, D>(a, S, d[k], m[k], lane);
     PendLoads pq = prepare_block<B, D>(a, S, m[NS - 1], lane);
+    if constexpr (in_share<false, R>()) share_inputs<B, CHAIN>(a, S, a.p0, lds, lane, w);
     if (((const RunHdr *)run_buf_s(S, a.p0))->has_norm) norm_all(lds, w, lane);
     wg_barrier();  // x-hat of the first phase is ready
     bool ok = abort_flag_get() == 0;
@@ -733,6 +752,7 @@ __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_
             if (end) nblk = 0;
             if (end && ++p < a.p1) {
                 if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
+                if constexpr (in_share<false, R>()) share_inputs<B, CHAIN>(a, S, p, lds, lane, w);
                 if (((const RunHdr *)run_buf_s(S, p))->has_norm) norm_all(lds, w, lane);
                 wg_barrier();  // x-hat of phase p is ready
                 ok = abort_flag_get() == 0;
@@ -740,24 +760,6 @@ __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_
             }
         }
     }
-}
-
-template <int B, bool CHAIN>
-__device__ __forceinline__ void issue_source_loads(const KArgs &a, int32_t nsrc, int32_t xb, const char *lds,
-                                                   char *xh, uint32_t lane, int32_t w, int32_t nw, bool zero_tail);
-
-// A streaming wave's part of phase p's input copies (when the phase's header
-// asks for shared copies): after the barrier that follows the control wave's
-// wait for the flags, copy every WAVES-th 1 KB of the inputs and wait for
-// those copies (and this wave's older weight loads).
-template <int B, bool CHAIN>
-__device__ __forceinline__ void share_inputs(const KArgs &a, const StreamState &S, int32_t p, char *lds,
-                                             uint32_t lane, int32_t w) {
-    const RunHdr &hh = *(const RunHdr *)run_buf_s(S, p);
-    if (!hh.share_in) return;
-    wg_barrier();  // the control wave has seen phase p-1's flags
-    issue_source_loads<B, CHAIN>(a, MAX_SRC, hh.xb_bytes / 2, lds, lds + hh.x_off, lane, w, WAVES, false);
-    __builtin_amdgcn_s_waitcnt(0);
 }
 
 template <int B, bool CHAIN, bool TILE, int R>

@@ -109,7 +109,7 @@ WGN_HD void make_runs(const KArgs &a, int32_t p, int32_t g, bool tile, RunHdr &h
             in_bytes += (int64_t)src.K * a.nb * 2;
         }
         h.has_norm = hn;
-        h.share_in = tile && in_bytes >= SHARE_IN_MIN_BYTES ? 1 : 0;
+        h.share_in = in_bytes >= SHARE_IN_MIN_BYTES ? 1 : 0;
         h.pad3 = 0;
     }
     for (int32_t w = 0; w <= STREAM_WAVES; ++w) h.wb[w] = G.U > 0 ? wave_begin(w, G.U, STREAM_WAVES) : 0;

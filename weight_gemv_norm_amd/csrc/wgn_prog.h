@@ -66,12 +66,14 @@ constexpr int EPI_BARRIER = WGN_EPI_BARRIER;
 // of them): 0 none, 1 the matrix-core path, 2 every burst-refill ring-0 kernel.
 constexpr int EPI_SHARE = WGN_EPI_SHARE;
 #ifndef WGN_IN_SHARE
-#define WGN_IN_SHARE 1
+#define WGN_IN_SHARE 2
 #endif
-// 1: on the matrix-core path all waves share the input copies of a phase
-// whose inputs are at least SHARE_IN_MIN_BYTES per workgroup (below that the
-// extra barrier and the streaming waves' wait for their newest weight loads
-// cost more than the copies take)
+// All waves share the input copies of a phase whose inputs are at least
+// SHARE_IN_MIN_BYTES per workgroup (below that the extra barrier and the
+// streaming waves' wait for their newest weight loads cost more than the
+// copies take): 1 on the matrix-core path, 2 also on the interleaved ring
+// (batch 2-4); the burst rings keep one large block in flight at a phase
+// start and copy on the control wave alone.
 constexpr int IN_SHARE = WGN_IN_SHARE;
 constexpr int SHARE_IN_MIN_BYTES = 32 * 1024;
 // Block-buffer rings of the vector path's streaming waves (the matrix-core
