@@ -667,9 +667,12 @@ constexpr bool epi_barrier() { return EPI_BARRIER != 0 && (TILE || !ring_interle
 // Whether all waves share the epilogue's output rows (burst ring 0 only: at
 // the third barrier a streaming wave has just one older block in flight, so
 // waiting for its own stores costs little).
-template <bool TILE, int R>
+template <int B, bool TILE, int R>
 constexpr bool epi_share() {
-    return R == 0 && EPI_BARRIER == 1 && (EPI_SHARE == 2 || (EPI_SHARE == 1 && TILE));
+    // (the interleaved ring at batch 4 would spill: its streaming waves hold
+    // three blocks of weights across the epilogue)
+    return (R == 0 && EPI_BARRIER == 1 && (EPI_SHARE == 2 || (EPI_SHARE >= 1 && TILE))) ||
+           (EPI_SHARE == 3 && !TILE && ring_interleaved(R) && B <= 3);
 }
 // Whether all waves share the input copies of a phase (the matrix-core path):
 // one more barrier per phase (the flags have been seen), after which every
@@ -684,6 +687,13 @@ constexpr bool in_share() {
 template <int B, bool CHAIN>
 __device__ __forceinline__ void issue_source_loads(const KArgs &a, int32_t nsrc, int32_t xb, const char *lds,
                                                    char *xh, uint32_t lane, int32_t w, int32_t nw, bool zero_tail);
+template <int B, bool CHAIN, bool TILE>
+__device__ __forceinline__ void epilogue(const KArgs &a, const RunHdr &h, const Run *runs, int32_t g, const float *part,
+                                         const float *epi, float *carry, uint32_t lane, int32_t wsel, int32_t nw,
+                                         bool with_argmax);
+template <bool TILE>
+__device__ __forceinline__ void argmax_shared(const KArgs &a, const RunHdr &h, const Run *runs, int32_t g,
+                                              const float *part, float *carry, char *lds, uint32_t lane, int32_t w);
 
 // A streaming wave's part of phase p's input copies (when the phase's header
 // asks for shared copies): after the barrier that follows the control wave's
@@ -747,6 +757,20 @@ __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_
             if (end) {
                 if (tw) tl[(p & 1) * 6 + 2] = wall_clock64();
                 wg_barrier();  // partials of phase p are complete
+                if constexpr (epi_share<B, false, R>()) {
+                    // this wave's share of the phase's output rows and argmax
+                    // keys; its stores (and its weight loads in flight)
+                    // complete before the barrier after which the flag is set
+                    const RunHdr &hh = *(const RunHdr *)run_buf_s(S, p);
+                    const Run *rr = (const Run *)((const char *)&hh + sizeof(RunHdr));
+                    epilogue<B, CHAIN, false>(a, hh, rr, g, (const float *)(lds + hh.part_off),
+                                              (const float *)(lds + hh.epi_off), (float *)(lds + hh.carry_off), lane,
+                                              w, WAVES, false);
+                    argmax_shared<false>(a, hh, rr, g, (const float *)(lds + hh.part_off),
+                                         (float *)(lds + hh.carry_off), lds, lane, w);
+                    __builtin_amdgcn_s_waitcnt(0);
+                    wg_barrier();  // every wave's stores have completed
+                }
             }
             pq = prepare_block<B, D>(a, S, m[k], lane);
             if (end) nblk = 0;
@@ -810,7 +834,7 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
             if (end) {
                 if (tw) tl[(p & 1) * 6 + 2] = wall_clock64();
                 wg_barrier();  // partials of phase p are complete
-                if constexpr (epi_share<TILE, R>()) {
+                if constexpr (epi_share<B, TILE, R>()) {
                     // this wave's share of the phase's output rows; its stores
                     // (and its one older block of weight loads) complete
                     // before the third barrier
@@ -1389,7 +1413,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
             a.trace[((size_t)p * a.G + g) * TRACE_POINTS + 6 + lane] = tl[(p & 1) * 6 + lane];
             if (lane >= 3) tl[(p & 1) * 6 + lane] = 0;  // per-block slots: cleared for phase p + 2
         }
-        if constexpr (epi_share<TILE, R>()) {
+        if constexpr (epi_share<B, TILE, R>()) {
             // every wave stores its share of the rows and waits for its own
             // stores; after the barrier all of them have completed
             epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane, STREAM_WAVES, WAVES, false);

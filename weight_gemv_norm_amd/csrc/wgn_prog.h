@@ -59,11 +59,13 @@ constexpr int MAX_RUNS = 8;          // stages per phase (the planner splits lar
 // otherwise queue behind them in the compute unit's memory pipeline)
 constexpr int EPI_BARRIER = WGN_EPI_BARRIER;
 #ifndef WGN_EPI_SHARE
-#define WGN_EPI_SHARE 1
+#define WGN_EPI_SHARE 3
 #endif
-// Which kernels run the epilogue's output rows on all waves (each wave then
-// waits for its own stores before the third barrier, so the flag follows all
-// of them): 0 none, 1 the matrix-core path, 2 every burst-refill ring-0 kernel.
+// Which kernels run the epilogue's output rows (and argmax keys) on all waves
+// (each wave then waits for its own stores before a barrier, so the flag
+// follows all of them): 0 none, 1 the matrix-core path, 2 that and the burst
+// ring 0 at batch 1 (measured slower there), 3 the matrix-core path and the
+// interleaved ring at batch 2-3.
 constexpr int EPI_SHARE = WGN_EPI_SHARE;
 #ifndef WGN_IN_SHARE
 #define WGN_IN_SHARE 2
