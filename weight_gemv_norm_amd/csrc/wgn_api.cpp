@@ -242,17 +242,27 @@ struct PhaseStats {
 PhaseStats phase_stats(const std::vector<DevStage> &st, const std::vector<int32_t> &rowb, const DevPhase &ph,
                        int32_t G, bool tile) {
     PhaseStats S;
+    // The spans depend only on the workgroup's row count in each stage, and a
+    // partition has few distinct such tuples: each is evaluated once (a large
+    // single stage, e.g. an LM head, would otherwise cost a loop over every
+    // row of every workgroup on each call).
+    std::vector<std::vector<int32_t>> seen;
     for (int32_t g = 0; g < G; ++g) {
         const int32_t r0 = ph.rb_off >= 0 ? rowb[ph.rb_off + g] : even_row_begin(g, ph.nrows, G);
         const int32_t r1 = ph.rb_off >= 0 ? rowb[ph.rb_off + g + 1] : even_row_begin(g + 1, ph.nrows, G);
         int32_t U = 0, rp = 0;
+        std::vector<int32_t> key;
+        key.reserve(ph.nstages);
         for (int32_t i = 0; i < ph.nstages; ++i) {
             const DevStage &d = st[ph.stage0 + i];
             const StageSpan sp = stage_span(d, r0, r1, 0, 0);
             U += units_of(sp.nrows, d.parts, d.nchunks, tile);
             rp += sp.nrows * d.parts;
+            key.push_back(sp.nrows);
         }
         S.max_rp = std::max(S.max_rp, rp);
+        if (std::find(seen.begin(), seen.end(), key) != seen.end()) continue;
+        seen.push_back(key);
         int32_t u_base = 0;
         for (int32_t i = 0; i < ph.nstages; ++i) {
             const DevStage &d = st[ph.stage0 + i];
