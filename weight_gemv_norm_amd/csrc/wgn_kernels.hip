@@ -846,6 +846,13 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
                     argmax_shared<TILE>(a, hh, rr, g, (const float *)(lds + hh.part_off), (float *)(lds + hh.carry_off),
                                         lds, lane, w);
                     __builtin_amdgcn_s_waitcnt(0);
+                } else if constexpr (!TILE && R == 0 && !CHAIN) {
+                    // single-stage calls: argmax keys from every wave (in
+                    // chains at batch 1 the larger kernel measured slower)
+                    const RunHdr &hh = *(const RunHdr *)run_buf_s(S, p);
+                    const Run *rr = (const Run *)((const char *)&hh + sizeof(RunHdr));
+                    argmax_shared<false>(a, hh, rr, g, (const float *)(lds + hh.part_off), (float *)(lds + hh.carry_off),
+                                         lds, lane, w);
                 }
                 if (epi_barrier<TILE, R>()) wg_barrier();  // the control wave has issued phase p's stores
             }
@@ -1422,7 +1429,12 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
             trace_point(a, p, g, 4, lane);
             wg_barrier();  // every wave's stores have completed: the streaming waves may refill
         } else {
-            epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane, 0, 1, true);
+            if constexpr (!TILE && R == 0 && !CHAIN) {
+                epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane, 0, 1, false);
+                argmax_shared<false>(a, h, runs, g, part, carry, lds, lane, STREAM_WAVES);
+            } else {
+                epilogue<B, CHAIN, TILE>(a, h, runs, g, part, epi, carry, lane, 0, 1, true);
+            }
             trace_point(a, p, g, 4, lane);
             if (epi_barrier<TILE, R>() && EPI_BARRIER == 1) wg_barrier();  // stores issued: the streaming waves may refill
         }
