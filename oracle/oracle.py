@@ -10,8 +10,8 @@ BF16 and FP16 tensors are passed as ``uint16`` bit patterns.
 
 Every function below follows the definition stated in ``wgn_oracle.c``'s header,
 which cites the page passage each step comes from.  Parity status: the norm,
-product, epilogue and argmax definitions are pinned by the ``-m "not gpu"``
-tests in ``tests/test_oracle_pins.py`` (closed forms, invariants and exact
+product, epilogue, argmax and decode-attention definitions are pinned by the ``-m "not gpu"``
+tests in ``tests/test_oracle_pins.py`` and ``tests/test_oracle_attention.py`` (closed forms, invariants and exact
 rational brute force); the values for random inputs are "parity unpinned"
 beyond the oracle itself, because the pages print no worked numeric example.
 """
@@ -89,6 +89,8 @@ def _load():
         lib.wgo_lmhead_argmax.restype = None
         lib.wgo_rmsnorm_rows_f16.argtypes = [P, I64, P, D, P, I64, I64, I64]
         lib.wgo_rmsnorm_rows_f16.restype = None
+        lib.wgo_decode_attention.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, D, P, P]
+        lib.wgo_decode_attention.restype = None
         _lib = lib
         return lib
 
@@ -239,3 +241,29 @@ def rmsnorm_rows_f16(x, g, eps=1e-6):
     y = np.empty((R, K), dtype=np.uint16)
     _load().wgo_rmsnorm_rows_f16(_ptr(x), K, _ptr(_u16(g)), float(eps), _ptr(y), K, R, K)
     return y
+
+
+def decode_attention(q, k_new, v_new, k_cache, v_cache, pos, scale=None, want_f64=False):
+    """One new token of grouped-query attention over a static cache.
+
+    q [B][Hq][D], k_new/v_new [B][Hkv][D], caches [B][Hkv][S][D] (uint16 BF16
+    bits), pos int32 [B].  The caches are not modified: updated copies are
+    returned.  scale defaults to 1/sqrt(D).  Returns (out, k_cache', v_cache')
+    and, with want_f64, the un-rounded outputs as a fourth item.
+    """
+    q, k_new, v_new = _u16(q), _u16(k_new), _u16(v_new)
+    kc, vc = _u16(k_cache).copy(), _u16(v_cache).copy()
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    B, Hq, D = q.shape
+    B2, Hkv, S, D2 = kc.shape
+    assert B2 == B and D2 == D and vc.shape == kc.shape and Hq % Hkv == 0
+    assert k_new.shape == (B, Hkv, D) and v_new.shape == (B, Hkv, D) and pos.shape == (B,)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, Hq, D), dtype=np.uint16)
+    of = np.empty((B, Hq, D), dtype=np.float64) if want_f64 else None
+    _load().wgo_decode_attention(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kc), _ptr(vc), _ptr(pos),
+                                 B, Hq, Hkv, S, D, float(scale), _ptr(out), _ptr(of))
+    if want_f64:
+        return out, kc, vc, of
+    return out, kc, vc

@@ -29,6 +29,12 @@
  *             -- "One Token, Kernel by Kernel", sections "The setup" (greedy
  *                argmax of the last logits) and "The whole step" (LM head
  *                151,936 x 1,536 followed by an argmax).
+ *   attention out = R( softmax_t(scale * q . k_t) . v ) over cache slots
+ *             0 .. pos after the new key/value are written at slot pos;
+ *             query head h reads key/value head h / (q_heads / kv_heads)
+ *             -- "Making small PyTorch ops faster on a laptop GPU", section "A
+ *                full decode step is a different story", and "One Token, Kernel
+ *                by Kernel", section "The fix: Part 10's split-KV kernel".
  *
  * R() is round-to-nearest-even to BF16 (FP16 for the standalone FP16 norm rows),
  * taken directly from the binary64 value (one rounding).  x-hat is rounded to
@@ -335,5 +341,79 @@ void wgo_rmsnorm_rows_f16(const uint16_t *x, int64_t x_stride, const uint16_t *g
         double inv = 1.0 / sqrt(ss / (double)K + eps);
         for (int64_t k = 0; k < K; ++k)
             y[r * y_stride + k] = wgo_f64_to_f16(wgo_f16_to_f64(xr[k]) * inv * wgo_f16_to_f64(g[k]));
+    }
+}
+
+/* ------------------------------------------------------- decode attention */
+/*
+ * Attention of one new token over a static key/value cache, grouped-query.
+ *   -- "Making small PyTorch ops faster on a laptop GPU", section "A full
+ *      decode step is a different story": the new key and value are appended
+ *      to the cache, then the softmax is taken over every cached position.
+ *   -- "One Token, Kernel by Kernel", section "The fix: Part 10's split-KV
+ *      kernel": cache layout (batch, head, slot, dimension); the valid
+ *      positions are 0 .. pos, read per row; each key/value head serves a
+ *      group of query heads (12 query heads over 2 key/value heads in the
+ *      page's model, section "The setup").
+ *
+ *   q [batch][q_heads][d], k_new, v_new [batch][kv_heads][d]     BF16
+ *   k_cache, v_cache [batch][kv_heads][slots][d]                 BF16, updated
+ *   pos [batch]   slot of the new token.  A row whose pos lies outside
+ *                 [0, slots) appends nothing and its output is zero (the
+ *                 pages define no such case; this is the library's rule).
+ *   Query head h reads key/value head h / (q_heads / kv_heads).
+ *     s_t   = scale * sum_j q_j k_tj,  t = 0 .. pos
+ *     out_j = R( sum_t e^(s_t - m) v_tj / sum_t e^(s_t - m) ),  m = max_t s_t
+ *   out_f64 (may be NULL) receives the values before rounding.
+ */
+void wgo_decode_attention(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                          uint16_t *k_cache, uint16_t *v_cache, const int32_t *pos,
+                          int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t slots, int64_t d,
+                          double scale, uint16_t *out, double *out_f64)
+{
+    const int64_t group = q_heads / kv_heads;
+    /* the append comes first: the new token attends to itself */
+    for (int64_t b = 0; b < batch; ++b) {
+        if (pos[b] < 0 || pos[b] >= slots) continue;
+        for (int64_t g = 0; g < kv_heads; ++g) {
+            const int64_t row = ((b * kv_heads + g) * slots + pos[b]) * d;
+            memcpy(k_cache + row, k_new + (b * kv_heads + g) * d, (size_t)d * sizeof(uint16_t));
+            memcpy(v_cache + row, v_new + (b * kv_heads + g) * d, (size_t)d * sizeof(uint16_t));
+        }
+    }
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+#endif
+    for (int64_t bh = 0; bh < batch * q_heads; ++bh) {
+        const int64_t b = bh / q_heads, h = bh % q_heads, g = h / group;
+        uint16_t *o = out + bh * d;
+        double *of = out_f64 ? out_f64 + bh * d : NULL;
+        if (pos[b] < 0 || pos[b] >= slots) {
+            for (int64_t j = 0; j < d; ++j) { o[j] = 0; if (of) of[j] = 0.0; }
+            continue;
+        }
+        const int64_t n = pos[b] + 1;
+        const uint16_t *qh = q + bh * d;
+        const uint16_t *K = k_cache + (b * kv_heads + g) * slots * d;
+        const uint16_t *Vc = v_cache + (b * kv_heads + g) * slots * d;
+        double *s = (double *)malloc((size_t)n * sizeof(double));
+        double m = -INFINITY;
+        for (int64_t t = 0; t < n; ++t) {
+            double dot = 0.0;
+            for (int64_t j = 0; j < d; ++j)
+                dot += wgo_bf16_to_f64(qh[j]) * wgo_bf16_to_f64(K[t * d + j]);
+            s[t] = scale * dot;
+            if (s[t] > m) m = s[t];
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < n; ++t) { s[t] = exp(s[t] - m); l += s[t]; }
+        for (int64_t j = 0; j < d; ++j) {
+            double a = 0.0;
+            for (int64_t t = 0; t < n; ++t) a += s[t] * wgo_bf16_to_f64(Vc[t * d + j]);
+            const double v = a / l;
+            o[j] = wgo_f64_to_bf16(v);
+            if (of) of[j] = v;
+        }
+        free(s);
     }
 }
