@@ -32,7 +32,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_step_1536x28",
                     choices=["decode_step_1536x28", "decoder_block_1536", "ln_gelu_chain_768x72",
-                             "rmsnorm_gemv_256", "rmsnorm_rows_960x1536_f16", "lmhead_151936"])
+                             "rmsnorm_gemv_256", "rmsnorm_rows_960x1536_f16", "lmhead_151936",
+                             "decode_attention_12q2kv128"])
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None,
                     help="decode-step workload: number of decoder blocks (default 28)")
@@ -52,6 +53,8 @@ def parse():
                     help="with --mode 1: tune an Infinity-Cache prefetch plan (touch passes on a second "
                          "stream, wgn_plan_tune) before timing, and time the plan it keeps")
     ap.add_argument("--tune-reps", type=int, default=15, help="rounds of the prefetch tuner")
+    ap.add_argument("--slots", type=int, default=32768,
+                    help="decode-attention workload: cache slots (all valid: the new token takes the last)")
     ap.add_argument("--cold", action="store_true",
                     help="stream a 512 MB scrub buffer between timed steps (evicts the Infinity Cache)")
     return ap.parse_args()
@@ -129,6 +132,28 @@ def main():
         launch = lambda: W.rmsnorm_rows(t["x"], t["g"], t["eps"], y)  # noqa: E731
         kernel_name = "rmsnorm_rows_kernel"
 
+    elif wl == "decode_attention_12q2kv128":
+        # one decode step's attention: every layer has its own cache (28 x 33.5 MB
+        # at 32,768 slots and batch 1, well beyond the 256 MB Infinity Cache)
+        n_layers = args.layers or gen.N_LAYERS
+        S = args.slots
+        att = [gen.make_attention_tensors(B, S, [S - 1] * B, layer=l, nan_tail=False, device=dev)
+               for l in range(n_layers)]
+        att_out = [torch.empty_like(t["q"]) for t in att]
+        ws = W.workspace(W.decode_attention_workspace_bytes(B, gen.NQ, gen.NKV, S))
+        per_layer = (2 * B * gen.NKV * S * gen.HEAD_DIM * 2          # keys and values of the valid slots
+                     + 2 * B * gen.NQ * gen.HEAD_DIM * 2             # q in, output out
+                     + 2 * 2 * B * gen.NKV * gen.HEAD_DIM * 2)       # new key/value in, appended out
+        nbytes = per_layer * n_layers
+        cfg.update({"q_heads": gen.NQ, "kv_heads": gen.NKV, "head_dim": gen.HEAD_DIM, "slots": S,
+                    "valid_slots": S, "layers": n_layers, "launches_per_step": n_layers,
+                    "algorithmic_bytes": nbytes, "bytes_per_launch": per_layer})
+        kernel_name = "decode_attention_kernel"
+
+        def launch():
+            for t, o in zip(att, att_out):
+                W.decode_attention(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["pos"], o, ws=ws)
+
     if chain is not None:
         cfg["ring"] = chain.ring
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
@@ -192,19 +217,27 @@ def main():
     print("[bench] timed %d steps: mean %.2f us, median %.2f us, min %.2f us, wall %.3f s"
           % (K, us_step, us_med, float(per.min()), wall1 - wall0), file=sys.stderr, flush=True)
 
-    roofline = {"bound": "hbm", "kernel": kernel_name, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic(wl, B, kernel_name), "launch_us_mean": round(us_step, 3), "launch_us_median": round(us_med, 3),
-                "bytes_per_launch": nbytes}
+    launches = cfg.get("launches_per_step", 1)
+    # several launches per step run back to back on one stream: the average
+    # launch is the step time over the launches
+    l_mean, l_med = us_step / launches, us_med / launches
+    l_gbs = nbytes / launches / (l_mean * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": kernel_name, "achieved": round(l_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(l_gbs / HBM_PEAK_GBS, 4),
+                "traffic": recorded_traffic(wl, B, kernel_name), "launch_us_mean": round(l_mean, 3),
+                "launch_us_median": round(l_med, 3), "bytes_per_launch": nbytes // launches}
 
     # ----------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline and wl == "decode_step_1536x28":
         cpu = cpu_baseline_decode(inp, bufs, nbytes)
+    elif not args.no_cpu_baseline and wl == "decode_attention_12q2kv128":
+        cpu = cpu_baseline_attention(att, cfg["bytes_per_launch"])
 
     out = {
         "metric": METRIC if wl == "decode_step_1536x28" and B == 1 else METRIC.replace("batch 1", "batch %d" % B)
-        if wl == "decode_step_1536x28" else "%s weight-stream GB/s" % wl,
+        if wl == "decode_step_1536x28" else ("decode attention GB/s (keys and values read once per step)"
+                                             if wl == "decode_attention_12q2kv128" else "%s weight-stream GB/s" % wl),
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -349,6 +382,34 @@ def cpu_baseline_decode(inp, bufs, nbytes, budget_s=12.0, max_steps=45):
             "seconds_per_step": round(dt, 4), "us_per_step": round(dt * 1e6, 1),
             "sample": "%d full decode steps (28 blocks + LM head + argmax, batch 1), free-running in the "
                       "binary64 C oracle with OpenMP over rows; value = algorithmic bytes / mean step time" % n}
+
+
+def cpu_baseline_attention(att, bytes_per_layer, budget_s=10.0, max_reps=200):
+    """Time the CPU oracle (as it stands) on the attention of one layer of the
+    same workload (the same cache length, every slot valid), repeated until
+    about budget_s seconds of CPU work have been spent."""
+    from oracle import oracle as O
+    from synth.gen import bf16_bits_to_numpy as bb
+    t = att[0]
+    a = [bb(t[k]) for k in ("q", "k_new", "v_new", "k_cache", "v_cache")]
+    pos = t["pos"].cpu().numpy()
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    O.set_threads(threads)
+    t0 = time.perf_counter()
+    n = 0
+    while n < max_reps:
+        O.decode_attention(*a, pos)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    print("[bench] cpu baseline: %d layer calls, %.4f s each on %d threads" % (n, dt, threads),
+          file=sys.stderr, flush=True)
+    return {"value": round(bytes_per_layer / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds_per_layer": round(dt, 5),
+            "sample": "%d calls of one layer's attention (same cache length and batch) in the binary64 C "
+                      "oracle with OpenMP over query heads; value = algorithmic bytes per layer / mean call "
+                      "time" % n}
 
 
 if __name__ == "__main__":

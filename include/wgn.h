@@ -149,6 +149,41 @@ wgn_status wgn_rmsnorm_rows(const void *x, int64_t x_stride, const void *gamma, 
                             void *y, int64_t y_stride, int32_t rows, int32_t K,
                             int32_t dtype, wgn_stream stream);
 
+/* ------------------------------------------------------ decode attention */
+/* Attention of one new token over a static key/value cache, in one launch
+ * ("Making small PyTorch ops faster on a laptop GPU", section "A full decode
+ * step is a different story": the new key and value are appended, the softmax
+ * is FP32, the cache is split across workgroups and the last one to finish
+ * merges; "One Token, Kernel by Kernel", section "The fix: Part 10's split-KV
+ * kernel": cache layout (batch, head, slot, dimension), the valid length read
+ * on the device, each key/value head read once for its group of query heads).
+ *
+ *   q       [batch][q_heads][head_dim]          BF16, read
+ *   k_new   [batch][kv_heads][head_dim]         BF16, read (also v_new)
+ *   k_cache [batch][kv_heads][slots][head_dim]  BF16, read; slot pos[b] of row
+ *           b is overwritten with k_new (v_cache likewise with v_new)
+ *   pos     [batch] int32 in device memory: the new token's slot.  Slots
+ *           0 .. pos[b] are attended to; slots after it are never read.  A row
+ *           whose pos is outside [0, slots) appends nothing and gets zeros.
+ *   out     [batch][q_heads][head_dim] BF16: for query head h (key/value head
+ *           h / (q_heads / kv_heads)), R(sum_t softmax_t(scale * q.k_t) v_t).
+ *   All activation and cache pointers 16-byte aligned, pos 4-byte aligned;
+ *   out, the caches and the inputs may not overlap.
+ * head_dim must be 128 and q_heads / kv_heads at most 8 (WGN_E_UNSUPPORTED
+ * otherwise); slots in [1, 2^24].  The workspace (size from the query below,
+ * 256-byte aligned, zero-filled once at allocation) holds the partial results
+ * and arrival counters; every call leaves the counters zero.  A cache of at
+ * most 128 slots needs no workspace (NULL allowed).  Calls that share a
+ * workspace must not run concurrently.  Asynchronous on `stream`; nothing is
+ * enqueued when an argument check fails. */
+size_t wgn_decode_attention_workspace_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads,
+                                            int32_t slots, int32_t head_dim);
+wgn_status wgn_decode_attention(const void *q, const void *k_new, const void *v_new,
+                                void *k_cache, void *v_cache, const int32_t *pos,
+                                int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t slots,
+                                int32_t head_dim, float scale, void *out,
+                                void *workspace, size_t ws_bytes, wgn_stream stream);
+
 /* --------------------------------------------------------------- chains */
 /* A chain is a list of stages in dependency order (a stage may read earlier
  * stages' outputs), tuned and laid out once and then run many times, like the

@@ -168,3 +168,35 @@ def make_stage_tensors(workload: str, device="cpu", batch: Optional[int] = None,
 
 def layer_names() -> List[str]:
     return [n for n, _, _ in block_shapes()]
+
+
+# ----------------------------------------------------------- decode attention
+ATTN_WORKLOAD = 41
+
+
+def make_attention_tensors(batch: int, slots: int, pos, q_heads: int = NQ, kv_heads: int = NKV,
+                           head_dim: int = HEAD_DIM, seed: int = 0, layer: int = 0, nan_tail: bool = True,
+                           device="cpu") -> Dict[str, torch.Tensor]:
+    """One decode step's attention inputs: q [B][Hq][D], the new key/value
+    [B][Hkv][D] and a static cache [B][Hkv][slots][D], all N(0,1) in BF16, with
+    per-row positions pos (int32).  Slots after each row's position hold NaN
+    when nan_tail is set (a cache that is not yet written), so that any use of
+    them shows in the output.  The shapes follow the pages' model (12 query
+    heads over 2 key/value heads of 128 dimensions); the random values stand
+    in for a real prefill."""
+    s = lambda t: seed_of(ATTN_WORKLOAD * 1000 + seed, layer, t)  # noqa: E731
+    out = {
+        "q": normal((batch, q_heads, head_dim), 1.0, s(1), device=device),
+        "k_new": normal((batch, kv_heads, head_dim), 1.0, s(2), device=device),
+        "v_new": normal((batch, kv_heads, head_dim), 1.0, s(3), device=device),
+        "k_cache": normal((batch, kv_heads, slots, head_dim), 1.0, s(4), device=device),
+        "v_cache": normal((batch, kv_heads, slots, head_dim), 1.0, s(5), device=device),
+        "pos": torch.as_tensor(np.asarray(pos, dtype=np.int32).reshape(batch), device=device),
+    }
+    if nan_tail:
+        for b, p in enumerate(np.asarray(pos).reshape(batch)):
+            lo = max(int(p) + 1, 0)
+            if lo < slots:
+                out["k_cache"][b, :, lo:] = float("nan")
+                out["v_cache"][b, :, lo:] = float("nan")
+    return out

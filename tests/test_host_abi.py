@@ -336,3 +336,56 @@ def test_decode_step_weight_bytes_match_library_shapes():
     st = fake_decoder(ar, 1, gen.N_LAYERS, V=gen.V)
     total = sum(s.N * s.K * 2 * (2 if s.epi == L.EPI_SWIGLU else 1) for s in st)
     assert total == gen.decode_step_weight_bytes() == 3_087_138_816
+
+
+# ------------------------------------------------------------ decode attention
+def _att_call(**kw):
+    a = dict(q=0x10000, k_new=0x20000, v_new=0x30000, k_cache=0x1000000, v_cache=0x9000000, pos=0x40000,
+             batch=1, q_heads=12, kv_heads=2, slots=300, head_dim=128, scale=0.088, out=0x50000,
+             ws=0x100000000, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.lib().wgn_decode_attention(a["q"], a["k_new"], a["v_new"], a["k_cache"], a["v_cache"], a["pos"],
+                                        a["batch"], a["q_heads"], a["kv_heads"], a["slots"], a["head_dim"],
+                                        a["scale"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_attention_checks_arguments_before_the_device():
+    assert _att_call(q=None) == L.E_ARG
+    assert _att_call(pos=None) == L.E_ARG
+    assert _att_call(q_heads=12, kv_heads=5) == L.E_ARG
+    assert _att_call(slots=0) == L.E_ARG
+    assert _att_call(batch=0) == L.E_ARG
+    assert _att_call(scale=float("nan")) == L.E_ARG
+    assert _att_call(head_dim=64) == L.E_UNSUPPORTED
+    assert _att_call(q_heads=18, kv_heads=2) == L.E_UNSUPPORTED
+    assert _att_call(slots=(1 << 24) + 1) == L.E_UNSUPPORTED
+    assert _att_call(q=0x10008) == L.E_ALIGN
+    assert _att_call(pos=0x40002) == L.E_ALIGN
+    assert _att_call(out=0x1000000) == L.E_ARG                      # output inside the key cache
+    assert _att_call(v_cache=0x1000000 + 4096) == L.E_ARG           # the caches overlap
+    assert _att_call(ws=None) == L.E_WORKSPACE
+    assert _att_call(ws=0x100000010) == L.E_WORKSPACE
+    assert _att_call(ws_bytes=1000) == L.E_WORKSPACE
+
+
+def _tree(slots, chunk=128, fan=8):
+    counts = [-(-slots // chunk)]
+    while counts[-1] > 1:
+        counts.append(-(-counts[-1] // fan))
+    return counts
+
+
+@pytest.mark.parametrize("batch,hq,hkv,slots", [(1, 12, 2, 128), (1, 12, 2, 129), (1, 12, 2, 4096),
+                                                (1, 12, 2, 32768), (4, 12, 2, 32768), (2, 8, 1, 40000),
+                                                (3, 4, 4, 1 << 20)])
+def test_decode_attention_workspace_layout(batch, hq, hkv, slots):
+    """Partials for every level below the top (fan-in 8 over chunks of 128
+    slots), then one arrival counter per merged item; each area 256-byte
+    aligned."""
+    counts = _tree(slots)
+    G = hq // hkv
+    entry = ((G * 130 + 3) // 4 * 4) * 4
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    want = sum(al(batch * hkv * c * entry) for c in counts[:-1]) + sum(al(batch * hkv * c * 4) for c in counts[1:])
+    got = L.lib().wgn_decode_attention_workspace_bytes(batch, hq, hkv, slots, 128)
+    assert got == max(want, 256)

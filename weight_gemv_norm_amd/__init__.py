@@ -7,4 +7,5 @@ the first call does, and raises if the library was not built.
 from .api import (Chain, gemv_norm, gemv_norm_workspace_bytes, layer_chain, lmhead_argmax,  # noqa: F401
                   lmhead_argmax_workspace_bytes, make_stage, rmsnorm_rows, chain_workspace_bytes,
                   partition_selftest, first_wave_of_unit, workspace, device_cu_count, plan_phases,
-                  PATH_AUTO, PATH_VECTOR, PATH_MATRIX, Plan, WgnError)
+                  PATH_AUTO, PATH_VECTOR, PATH_MATRIX, Plan, WgnError, decode_attention,
+                  decode_attention_workspace_bytes)

@@ -115,6 +115,30 @@ def rmsnorm_rows(x: torch.Tensor, gamma: torch.Tensor, eps: float, y: torch.Tens
     L.check(st, "wgn_rmsnorm_rows")
 
 
+def decode_attention_workspace_bytes(batch: int, q_heads: int, kv_heads: int, slots: int,
+                                     head_dim: int = 128) -> int:
+    return int(L.lib().wgn_decode_attention_workspace_bytes(batch, q_heads, kv_heads, slots, head_dim))
+
+
+def decode_attention(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                     v_cache: torch.Tensor, pos: torch.Tensor, out: torch.Tensor, scale: Optional[float] = None,
+                     ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """wgn_decode_attention over contiguous device tensors: q/out [B][Hq][D],
+    k_new/v_new [B][Hkv][D], caches [B][Hkv][S][D] (all BF16), pos int32 [B]."""
+    B, Hq, D = q.shape
+    _, Hkv, S, _ = k_cache.shape
+    for t in (q, k_new, v_new, k_cache, v_cache, pos, out):
+        assert t.is_contiguous()
+    assert pos.dtype == torch.int32 and out.shape == q.shape
+    if scale is None:
+        scale = D ** -0.5
+    if ws is None:
+        ws = workspace(decode_attention_workspace_bytes(B, Hq, Hkv, S, D), q.device)
+    st = L.lib().wgn_decode_attention(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(pos),
+                                      B, Hq, Hkv, S, D, scale, _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
+    L.check(st, "wgn_decode_attention")
+
+
 PATH_AUTO, PATH_VECTOR, PATH_MATRIX = 0, 1, 2
 
 

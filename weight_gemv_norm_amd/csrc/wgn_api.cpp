@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "wgn.h"
+#include "wgn_attn.h"
 #include "wgn_loader.h"
 
 namespace wgn {
@@ -832,6 +833,42 @@ void patch_fsum(Program &P, char *base) {
 }
 }  // namespace
 
+
+// ------------------------------------------------------------ decode attention
+namespace {
+struct AttLayout {
+    int32_t top = 0;
+    int32_t count[ATT_MAX_LEVELS + 1] = {};
+    size_t part_off[ATT_MAX_LEVELS] = {};
+    size_t tick_off[ATT_MAX_LEVELS + 1] = {};
+    size_t total = 0;
+};
+
+// Shape checks shared by the workspace query and the call.
+wgn_status att_shape(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t slots, int32_t head_dim,
+                     AttLayout &L) {
+    if (batch < 1 || batch > 65535 || q_heads < 1 || kv_heads < 1 || kv_heads > 65535 || slots < 1)
+        return WGN_E_ARG;
+    if (q_heads % kv_heads) return WGN_E_ARG;
+    if (head_dim != ATT_D || q_heads / kv_heads > ATT_MAX_GROUP || slots > ATT_MAX_SLOTS) return WGN_E_UNSUPPORTED;
+    L.top = att_levels(slots, L.count);
+    if (L.top < 0) return WGN_E_UNSUPPORTED;
+    const size_t entry = (size_t)att_entry_floats(q_heads / kv_heads) * sizeof(float);
+    const size_t heads = (size_t)batch * kv_heads;
+    size_t off = 0;
+    for (int32_t l = 0; l < L.top; ++l) {
+        L.part_off[l] = off;
+        off += al256(heads * L.count[l] * entry);
+    }
+    for (int32_t l = 1; l <= L.top; ++l) {
+        L.tick_off[l] = off;
+        off += al256(heads * L.count[l] * sizeof(uint32_t));
+    }
+    L.total = std::max<size_t>(off, 256);
+    return WGN_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char *wgn_status_string(int32_t s) {
@@ -1483,6 +1520,62 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
             if (row_owner[r] != 1) ++bad;
     }
     return bad;
+}
+
+size_t wgn_decode_attention_workspace_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t slots,
+                                            int32_t head_dim) {
+    AttLayout L;
+    return att_shape(batch, q_heads, kv_heads, slots, head_dim, L) == WGN_OK ? L.total : 0;
+}
+
+wgn_status wgn_decode_attention(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                                const int32_t *pos, int32_t batch, int32_t q_heads, int32_t kv_heads,
+                                int32_t slots, int32_t head_dim, float scale, void *out, void *workspace,
+                                size_t ws_bytes, wgn_stream stream) {
+    AttLayout L;
+    wgn_status st = att_shape(batch, q_heads, kv_heads, slots, head_dim, L);
+    if (st != WGN_OK) return st;
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !pos || !out) return WGN_E_ARG;
+    if (!std::isfinite(scale)) return WGN_E_ARG;
+    if (!a16(q) || !a16(k_new) || !a16(v_new) || !a16(k_cache) || !a16(v_cache) || !a16(out) || !a4(pos))
+        return WGN_E_ALIGN;
+    {
+        const size_t cache = (size_t)batch * kv_heads * slots * ATT_D * 2;
+        const Range rk = rng(k_cache, cache), rv = rng(v_cache, cache);
+        const Range ro = rng(out, (size_t)batch * q_heads * ATT_D * 2);
+        const Range rin[4] = {rng(q, (size_t)batch * q_heads * ATT_D * 2),
+                              rng(k_new, (size_t)batch * kv_heads * ATT_D * 2),
+                              rng(v_new, (size_t)batch * kv_heads * ATT_D * 2), rng(pos, (size_t)batch * 4)};
+        if (overlap(rk, rv) || overlap(ro, rk) || overlap(ro, rv)) return WGN_E_ARG;
+        for (const Range &x : rin)
+            if (overlap(x, rk) || overlap(x, rv) || overlap(x, ro)) return WGN_E_ARG;
+    }
+    if (L.top > 0) {
+        if (!workspace || ((uintptr_t)workspace & 255)) return WGN_E_WORKSPACE;
+        if (ws_bytes < L.total) return WGN_E_WORKSPACE;
+    }
+    DevInfo d = device_info();
+    if (!d.ok) return WGN_E_DEVICE;
+    AttnArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = (const uint16_t *)q;
+    a.k_new = (const uint16_t *)k_new;
+    a.v_new = (const uint16_t *)v_new;
+    a.k_cache = (uint16_t *)k_cache;
+    a.v_cache = (uint16_t *)v_cache;
+    a.pos = pos;
+    a.out = (uint16_t *)out;
+    for (int32_t l = 0; l < L.top; ++l) a.part[l] = (float *)((char *)workspace + L.part_off[l]);
+    for (int32_t l = 1; l <= L.top; ++l) a.tick[l] = (uint32_t *)((char *)workspace + L.tick_off[l]);
+    for (int32_t l = 0; l <= ATT_MAX_LEVELS; ++l) a.count[l] = L.count[l];
+    a.top = L.top;
+    a.slots = slots;
+    a.hq = q_heads;
+    a.hkv = kv_heads;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+    hipError_t e = note(launch_decode_attention(a, q_heads / kv_heads, batch, (hipStream_t)stream),
+                        "decode_attention launch");
+    return e == hipSuccess ? WGN_OK : WGN_E_HIP;
 }
 
 }  // extern "C"
