@@ -263,15 +263,25 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "weight_gemv_norm_amd", "csrc")
 
 
-def kernel_sources_digest() -> str:
-    """SHA-256 over the kernel sources: recorded counter figures are reported
-    only while the kernels are unchanged since they were taken."""
+# The sources each kernel's recorded traffic depends on (its code and its host planner).
+KERNEL_SOURCES = {
+    "chain_kernel": ("wgn_api.cpp", "wgn_kernels.hip", "wgn_loader.h", "wgn_prog.h"),
+    "decode_attention_kernel": ("wgn_attn.h", "wgn_attn.hip"),
+}
+
+
+def kernel_of(workload: str) -> str:
+    return "decode_attention_kernel" if workload == "decode_attention_12q2kv128" else "chain_kernel"
+
+
+def kernel_sources_digest(kernel: str = "chain_kernel") -> str:
+    """SHA-256 over a kernel's sources: recorded counter figures are reported
+    only while the kernel is unchanged since they were taken."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            h.update(name.encode())
-            h.update(open(os.path.join(CSRC, name), "rb").read())
+    for name in KERNEL_SOURCES[kernel]:
+        h.update(name.encode())
+        h.update(open(os.path.join(CSRC, name), "rb").read())
     return h.hexdigest()
 
 
@@ -288,7 +298,7 @@ def recorded_traffic(workload, batch, kernel):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_sources_sha256") != kernel_sources_digest():
+    if kv.get("kernel_sources_sha256") != kernel_sources_digest(kernel):
         return None
     return int(kv["traffic_bytes_per_launch"])
 
@@ -303,9 +313,10 @@ def _pmc_rows(path, counter):
 
 
 def summarize_pmc(fetch_csv, write_csv, out_txt, workload, batch, copy_mib):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the chain kernel, scaled by
-    what the same counters read for a plain copy of copy_mib MiB."""
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the workload's kernel, scaled
+    by what the same counters read for a plain copy of copy_mib MiB."""
     assert copy_mib > 0, "--calib-copy-mib of the profiled run is needed"
+    kernel = kernel_of(workload)
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _pmc_rows(path, counter)
@@ -314,7 +325,7 @@ def summarize_pmc(fetch_csv, write_csv, out_txt, workload, batch, copy_mib):
         for name, d, v in rows:
             per.setdefault((name, d), 0.0)
             per[(name, d)] += v
-        kern = [v for (n, d), v in per.items() if "chain_kernel" in n]
+        kern = [v for (n, d), v in per.items() if kernel in n]
         copies = [v for (n, d), v in per.items() if "copyBuffer" in n or "copy_kernel" in n]
         assert kern and copies, (counter, len(kern), len(copies))
         copy_kib = max(copies)  # the calibration copy is the largest copy of the run
@@ -323,8 +334,8 @@ def summarize_pmc(fetch_csv, write_csv, out_txt, workload, batch, copy_mib):
     fetch = out["FETCH_SIZE"][0] * out["FETCH_SIZE"][2] * 1024
     write = out["WRITE_SIZE"][0] * out["WRITE_SIZE"][2] * 1024
     with open(out_txt, "w") as f:
-        f.write("# HBM traffic of chain_kernel, %s, batch %d (rocprofv3 --pmc, one counter per run)\n"
-                % (workload, batch))
+        f.write("# HBM traffic of %s, %s, batch %d (rocprofv3 --pmc, one counter per run)\n"
+                % (kernel, workload, batch))
         f.write("# commands (from the repository root):\n")
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             f.write("#   rocprofv3 --pmc %s --output-format csv -d gpurun_out/pmc_%s -o run -- python bench.py "
@@ -341,7 +352,7 @@ def summarize_pmc(fetch_csv, write_csv, out_txt, workload, batch, copy_mib):
         f.write("fetch_bytes_per_launch: %d\n" % int(fetch))
         f.write("write_bytes_per_launch: %d\n" % int(write))
         f.write("traffic_bytes_per_launch: %d\n" % int(fetch + write))
-        f.write("kernel_sources_sha256: %s\n" % kernel_sources_digest())
+        f.write("kernel_sources_sha256: %s\n" % kernel_sources_digest(kernel))
     print(open(out_txt).read())
 
 
