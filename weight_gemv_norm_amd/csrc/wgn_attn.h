@@ -16,8 +16,13 @@ constexpr int32_t ATT_D = 128;          // head dimension this kernel is written
 #ifndef WGN_ATT_FAN_LOG2
 #define WGN_ATT_FAN_LOG2 3
 #endif
+#ifndef WGN_ATT_WAVES
+#define WGN_ATT_WAVES 4
+#endif
 constexpr int32_t ATT_SLOTS_PER_WAVE = WGN_ATT_SLOTS_PER_WAVE;
-constexpr int32_t ATT_CHUNK = 4 * ATT_SLOTS_PER_WAVE;  // cache slots per workgroup (4 waves)
+constexpr int32_t ATT_WAVES = WGN_ATT_WAVES;                      // waves per workgroup
+constexpr int32_t ATT_THREADS = 64 * ATT_WAVES;
+constexpr int32_t ATT_CHUNK = ATT_WAVES * ATT_SLOTS_PER_WAVE;     // cache slots per workgroup
 constexpr int32_t ATT_FAN_LOG2 = WGN_ATT_FAN_LOG2;
 constexpr int32_t ATT_FAN = 1 << ATT_FAN_LOG2;  // partials merged by one workgroup
 constexpr int32_t ATT_MAX_LEVELS = 9;   // merge levels above the chunks
