@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--workload", default="decode_step_1536x28",
                     choices=["decode_step_1536x28", "decoder_block_1536", "ln_gelu_chain_768x72",
                              "rmsnorm_gemv_256", "rmsnorm_rows_960x1536_f16", "lmhead_151936",
-                             "decode_attention_12q2kv128"])
+                             "decode_attention_12q2kv128", "decode_step_attn_1536x28"])
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None,
                     help="decode-step workload: number of decoder blocks (default 28)")
@@ -53,8 +53,9 @@ def parse():
                     help="with --mode 1: tune an Infinity-Cache prefetch plan (touch passes on a second "
                          "stream, wgn_plan_tune) before timing, and time the plan it keeps")
     ap.add_argument("--tune-reps", type=int, default=15, help="rounds of the prefetch tuner")
-    ap.add_argument("--slots", type=int, default=32768,
-                    help="decode-attention workload: cache slots (all valid: the new token takes the last)")
+    ap.add_argument("--slots", type=int, default=None,
+                    help="decode-attention workload: cache slots (all valid: the new token takes the last; default 32768); "
+                         "decode step with attention: cache slots (default 1024, the new token at slot 960)")
     ap.add_argument("--cold", action="store_true",
                     help="stream a 512 MB scrub buffer between timed steps (evicts the Infinity Cache)")
     return ap.parse_args()
@@ -99,6 +100,28 @@ def main():
                     "launch": "persistent" if args.mode == 0 else "per-phase",
                     "path": "matrix" if (args.path == 2 or (args.path == 0 and B > 4)) else "vector"})
         launch = chain.run
+    elif wl == "decode_step_attn_1536x28":
+        # the decode step with computed attention: 1,024-slot caches, the new
+        # token at slot 960 (after a 960-token prompt) unless --slots says otherwise
+        S = args.slots or 1024
+        pos = min(960, S - 1)
+        inp = gen.make_stage_tensors("decode_step_1536x28", device=dev, batch=B, n_layers=args.layers,
+                                     vocab=args.vocab)
+        n_layers = len(inp["layers"])
+        caches = gen.make_kv_caches(B, S, [pos] * B, n_layers=n_layers, nan_tail=False, device=dev)
+        dstep = steps.DecodeStepWithAttention(inp, caches, dev, mode=args.mode)
+        nb = steps.decode_step_bytes(inp)
+        kv = n_layers * (2 * B * gen.NKV * (pos + 1) * gen.HEAD_DIM * 2 + 2 * 2 * B * gen.NKV * gen.HEAD_DIM * 2)
+        nbytes = nb["total"] + kv
+        cfg.update({"hidden": gen.H, "intermediate": gen.I, "layers": n_layers, "vocab": gen.V if "W_lm" in inp
+                    else None, "weight_bytes": nb["weights"], "kv_bytes": kv, "slots": S, "position": pos,
+                    "algorithmic_bytes": nbytes, "launches_per_step": dstep.n_launches,
+                    "launch": "persistent chains between attention launches"})
+        kernel_name = "chain_kernel+decode_attention_kernel"
+        # one HIP graph per step: 57 launches from Python would leave the GPU idle
+        dgraph = dstep.capture()
+        launch = dgraph.replay
+        cfg["graph"] = True
     elif wl == "ln_gelu_chain_768x72":
         inp = gen.make_stage_tensors(wl, device=dev, batch=B)
         stages, bufs = steps.ln_gelu_chain_stages(inp, dev)
@@ -136,7 +159,7 @@ def main():
         # one decode step's attention: every layer has its own cache (28 x 33.5 MB
         # at 32,768 slots and batch 1, well beyond the 256 MB Infinity Cache)
         n_layers = args.layers or gen.N_LAYERS
-        S = args.slots
+        S = args.slots or 32768
         att = [gen.make_attention_tensors(B, S, [S - 1] * B, layer=l, nan_tail=False, device=dev)
                for l in range(n_layers)]
         att_out = [torch.empty_like(t["q"]) for t in att]

@@ -200,3 +200,18 @@ def make_attention_tensors(batch: int, slots: int, pos, q_heads: int = NQ, kv_he
                 out["k_cache"][b, :, lo:] = float("nan")
                 out["v_cache"][b, :, lo:] = float("nan")
     return out
+
+
+def make_kv_caches(batch: int, slots: int, pos, n_layers: int = N_LAYERS, kv_heads: int = NKV,
+                   head_dim: int = HEAD_DIM, nan_tail: bool = True, device="cpu") -> List[Dict[str, torch.Tensor]]:
+    """Per-layer static caches [B][Hkv][slots][D] ~ N(0,1) in BF16 (slots after
+    each row's position NaN when nan_tail is set) and the positions, for a
+    decode step whose keys, values and queries come from the step itself.
+    The values stand in for a real prefill (the pages' model decodes after a
+    960-token prompt)."""
+    out = []
+    for l in range(n_layers):
+        t = make_attention_tensors(batch, slots, pos, q_heads=kv_heads, kv_heads=kv_heads, head_dim=head_dim,
+                                   seed=7, layer=l, nan_tail=nan_tail, device=device)
+        out.append({"k_cache": t["k_cache"], "v_cache": t["v_cache"], "pos": t["pos"]})
+    return out

@@ -140,3 +140,77 @@ def test_decode_attention_graph_replays():
         assert torch.equal(eager.view(torch.int16), out.view(torch.int16)), rep
         t["pos"] += 1                 # the next slot: NaN until this replay's append
         t["k_new"].mul_(0.5)
+
+
+@pytest.mark.parametrize("batch,pos", [(1, [960]), (2, [960, 37])])
+def test_decode_step_with_attention_teacher_forced(batch, pos):
+    """Two decoder blocks whose attention is computed (Q/K/V -> decode
+    attention over a 1,024-slot cache -> O -> MLP), then the LM head: every
+    stage is checked against the oracle on the GPU's own inputs to it, the
+    caches bit for bit, and the argmax."""
+    from weight_gemv_norm_amd import steps
+    from tests.gpu_util import check_argmax
+    say("decode step with attention batch %d pos %s" % (batch, pos))
+    dev = "cuda"
+    inp = gen.make_stage_tensors("decode_step_1536x28", device=dev, batch=batch, n_layers=2, vocab=4096)
+    caches = gen.make_kv_caches(batch, 1024, pos, n_layers=2, device=dev)
+    before = [(bits(c["k_cache"]), bits(c["v_cache"])) for c in caches]
+    step = steps.DecodeStepWithAttention(inp, caches, dev)
+    step.run()
+    torch.cuda.synchronize()
+    step.check()
+    b = step.bufs
+    eps = float(np.float32(inp["eps"]))
+    for l, L in enumerate(inp["layers"]):
+        h = bits(b["h"][l])
+        for name, w in (("q", "wq"), ("k", "wk"), ("v", "wv")):
+            ref = O.stage(h, bits(L[w]), norm=O.NORM_RMS, eps=eps, gamma=bits(L["g1"]))
+            assert_close_bf16(bits(b[name][l]), ref, "layer %d %s" % (l, name))
+        q = bits(b["q"][l]).reshape(batch, 12, 128)
+        kn = bits(b["k"][l]).reshape(batch, 2, 128)
+        vn = bits(b["v"][l]).reshape(batch, 2, 128)
+        ref_a, ref_k, ref_v = O.decode_attention(q, kn, vn, before[l][0], before[l][1],
+                                                 caches[l]["pos"].cpu().numpy())
+        assert_close_bf16(bits(b["a"][l]).reshape(batch, 12, 128), ref_a, "layer %d attention" % l)
+        np.testing.assert_array_equal(bits(caches[l]["k_cache"]), ref_k)
+        np.testing.assert_array_equal(bits(caches[l]["v_cache"]), ref_v)
+        ref = O.stage(bits(b["a"][l]), bits(L["wo"]), residual=h)
+        assert_close_bf16(bits(b["h1"][l]), ref, "layer %d O" % l)
+        ref = O.stage(bits(b["h1"][l]), bits(L["wg"]), norm=O.NORM_RMS, eps=eps, gamma=bits(L["g2"]),
+                      epi=O.EPI_SWIGLU, W_up=bits(L["wu"]))
+        assert_close_bf16(bits(b["s"][l]), ref, "layer %d gate/up" % l)
+        ref = O.stage(bits(b["s"][l]), bits(L["wd"]), residual=bits(b["h1"][l]))
+        assert_close_bf16(bits(b["h"][l + 1]), ref, "layer %d down" % l)
+    _, _, lg = O.lmhead_argmax(bits(b["h"][-1]), bits(inp["g_f"]), bits(inp["W_lm"]), eps=eps, want_logits=True)
+    for r in range(batch):
+        check_argmax(int(b["idx"][r]), lg[r], "argmax row %d" % r)
+
+
+def test_decode_step_with_attention_graph_replays_match_eager():
+    """The composed step captured in one HIP graph: three replays, with eager
+    work between them, each bit-identical to an eager run (every replay
+    appends the same key/value at the same slot, so the outputs repeat)."""
+    from weight_gemv_norm_amd import steps
+    say("decode step with attention: graph replays")
+    dev = "cuda"
+    inp = gen.make_stage_tensors("decode_step_1536x28", device=dev, batch=2, n_layers=2, vocab=4096)
+    caches = gen.make_kv_caches(2, 1024, [960, 500], n_layers=2, device=dev)
+    step = steps.DecodeStepWithAttention(inp, caches, dev)
+    step.run()
+    torch.cuda.synchronize()
+    eager = {k: [t.clone() for t in step.bufs[k]] for k in ("a", "h")}
+    idx = step.bufs["idx"].clone()
+    g = step.capture()
+    for rep in range(3):
+        for k in ("a", "h"):
+            for t in step.bufs[k][1:] if k == "h" else step.bufs[k]:
+                t.zero_()
+        step.bufs["idx"].fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ("a", "h"):
+            for x, y in zip(step.bufs[k], eager[k]):
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (rep, k)
+        assert torch.equal(step.bufs["idx"], idx), rep
+        step.check()

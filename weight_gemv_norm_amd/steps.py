@@ -71,6 +71,103 @@ def decoder_stages(inp: Dict, device, with_lmhead: bool = True, logits: bool = F
     return stages, bufs
 
 
+class DecodeStepWithAttention:
+    """A decode step whose attention is computed, not seeded: per layer the
+    Q/K/V products, wgn_decode_attention over that layer's static cache (the
+    new key/value appended at each row's position), then O, the SwiGLU MLP
+    and down ("One Token, Kernel by Kernel", sections "What one block
+    launches" and "The fix: Part 10's split-KV kernel").
+
+    Launches: one chain {Q, K, V of layer 0}; then per layer one attention
+    launch and one chain {O, gate/up, down, and the next layer's Q, K, V} (the
+    last chain ends with the final norm, LM head and argmax).  Every chain is
+    a persistent kernel of its own; attention is not yet a phase inside it.
+    Buffers: q/k/v/a/h1/s/h per layer as in decoder_stages, with a [B][Hq*D]
+    the attention output that feeds O."""
+
+    def __init__(self, inp: Dict, caches: List[Dict], device, mode: int = 0):
+        from . import api as W
+        B = inp["batch"]
+        eps = inp["eps"]
+        layers = inp["layers"]
+        h = inp["h"]
+        self.B, self.caches = B, caches
+        bufs = {"h": [h], "q": [], "k": [], "v": [], "a": [], "h1": [], "s": []}
+        qkv = []
+        for L in layers:
+            q = alloc(B, L["wq"].shape[0], device)
+            k = alloc(B, L["wk"].shape[0], device)
+            v = alloc(B, L["wv"].shape[0], device)
+            qkv.append([make_stage(L["wq"], h, q, norm=NORM_RMS, eps=eps, gamma=L["g1"]),
+                        make_stage(L["wk"], h, k, norm=NORM_RMS, eps=eps, gamma=L["g1"]),
+                        make_stage(L["wv"], h, v, norm=NORM_RMS, eps=eps, gamma=L["g1"])])
+            Hd = L["wq"].shape[1]
+            a = alloc(B, L["wo"].shape[1], device)
+            h1 = alloc(B, Hd, device)
+            s = alloc(B, L["wg"].shape[0], device)
+            hn = alloc(B, Hd, device)
+            for name, t in (("q", q), ("k", k), ("v", v), ("a", a), ("h1", h1), ("s", s)):
+                bufs[name].append(t)
+            bufs["h"].append(hn)
+            h = hn
+        tail = []
+        if "W_lm" in inp:
+            idx = torch.full((B,), -1, dtype=torch.int32, device=device)
+            mx = torch.empty((B,), dtype=torch.float32, device=device)
+            tail = [make_stage(inp["W_lm"], h, idx, norm=NORM_RMS, eps=eps, gamma=inp["g_f"], epi=EPI_ARGMAX,
+                               maxval=mx)]
+            bufs["idx"], bufs["maxval"] = idx, mx
+        self.bufs = bufs
+        self.chains = [W.Chain(qkv[0], B, mode=mode)]
+        self.attn = []
+        hd = 128  # head dimension of the attention kernel
+        NQ, NKV = layers[0]["wq"].shape[0] // hd, layers[0]["wk"].shape[0] // hd
+        for l, L in enumerate(layers):
+            h_in, h1, s, hn = bufs["h"][l], bufs["h1"][l], bufs["s"][l], bufs["h"][l + 1]
+            st = [make_stage(L["wo"], bufs["a"][l], h1, norm=NORM_NONE, residual=h_in),
+                  make_stage(L["wg"], h1, s, norm=NORM_RMS, eps=eps, gamma=L["g2"], epi=EPI_SWIGLU, W_up=L["wu"]),
+                  make_stage(L["wd"], s, hn, norm=NORM_NONE, residual=h1)]
+            st += qkv[l + 1] if l + 1 < len(layers) else tail
+            self.chains.append(W.Chain(st, B, mode=mode))
+            c = caches[l]
+            S = c["k_cache"].shape[2]
+            self.attn.append(dict(
+                q=bufs["q"][l].view(B, NQ, hd), k_new=bufs["k"][l].view(B, NKV, hd),
+                v_new=bufs["v"][l].view(B, NKV, hd), k_cache=c["k_cache"], v_cache=c["v_cache"], pos=c["pos"],
+                out=bufs["a"][l].view(B, NQ, hd),
+                ws=W.workspace(W.decode_attention_workspace_bytes(B, NQ, NKV, S, hd), device)))
+        self.n_launches = len(self.chains) + len(self.attn)
+
+    def run(self, stream=None) -> None:
+        from . import api as W
+        self.chains[0].run(stream)
+        for l, at in enumerate(self.attn):
+            W.decode_attention(at["q"], at["k_new"], at["v_new"], at["k_cache"], at["v_cache"], at["pos"],
+                               at["out"], ws=at["ws"], stream=stream)
+            self.chains[l + 1].run(stream)
+
+    def check(self, stream=None) -> None:
+        for c in self.chains:
+            c.check(stream)
+
+    def capture(self) -> "torch.cuda.CUDAGraph":
+        """The whole step captured once in a HIP graph ("One Token, Kernel by
+        Kernel", section "Step 3: where the 14.8 ms go": the step is replayed
+        as one graph): the 57 launches then cost one host call.  Every launch's arguments are fixed and no call enqueues a
+        memset, so replays are equivalent to run()."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.run(stream=s)  # first use of every launch path outside capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            self.run(stream=s)
+        torch.cuda.synchronize()
+        return g
+
+
 def ln_gelu_chain_stages(inp: Dict, device):
     """Stages of the LayerNorm -> Linear -> GELU-tanh chain.  Returns (stages, buffers)."""
     B = inp["batch"]
