@@ -10,8 +10,8 @@ BF16 and FP16 tensors are passed as ``uint16`` bit patterns.
 
 Every function below follows the definition stated in ``wgn_oracle.c``'s header,
 which cites the page passage each step comes from.  Parity status: the norm,
-product, epilogue, argmax and decode-attention definitions are pinned by the ``-m "not gpu"``
-tests in ``tests/test_oracle_pins.py`` and ``tests/test_oracle_attention.py`` (closed forms, invariants and exact
+product, epilogue, argmax, decode-attention and 4-bit product definitions are pinned by the ``-m "not gpu"``
+tests in ``tests/test_oracle_pins.py``, ``tests/test_oracle_attention.py`` and ``tests/test_oracle_int4.py`` (closed forms, invariants and exact
 rational brute force); the values for random inputs are "parity unpinned"
 beyond the oracle itself, because the pages print no worked numeric example.
 """
@@ -91,6 +91,8 @@ def _load():
         lib.wgo_rmsnorm_rows_f16.restype = None
         lib.wgo_decode_attention.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, D, P, P]
         lib.wgo_decode_attention.restype = None
+        lib.wgo_matvec_int4.argtypes = [P, P, P, I64, I64, P, I64, I64, P, P]
+        lib.wgo_matvec_int4.restype = None
         _lib = lib
         return lib
 
@@ -267,3 +269,20 @@ def decode_attention(q, k_new, v_new, k_cache, v_cache, pos, scale=None, want_f6
     if want_f64:
         return out, kc, vc, of
     return out, kc, vc
+
+
+def matvec_int4(W4, scales, zeros, x, want_acc=False):
+    """4-bit product: W4 uint8 [N][K/2] (low nibble = even k), scales/zeros
+    uint16 BF16 bits [N][K/128], x uint16 [B][K].  Returns y uint16 [B][N]
+    (and the binary64 sums with want_acc)."""
+    W4 = np.ascontiguousarray(W4, dtype=np.uint8)
+    x = _u16(np.atleast_2d(x))
+    N, K2 = W4.shape
+    B, K = x.shape
+    assert K2 * 2 == K and K % 128 == 0
+    sc, zr = _u16(scales), _u16(zeros)
+    assert sc.shape == (N, K // 128) and zr.shape == (N, K // 128)
+    y = np.empty((B, N), dtype=np.uint16)
+    acc = np.empty((B, N), dtype=np.float64) if want_acc else None
+    _load().wgo_matvec_int4(_ptr(W4), _ptr(sc), _ptr(zr), N, K, _ptr(x), K, B, _ptr(y), _ptr(acc))
+    return (y, acc) if want_acc else y

@@ -35,6 +35,8 @@
  *             -- "Making small PyTorch ops faster on a laptop GPU", section "A
  *                full decode step is a different story", and "One Token, Kernel
  *                by Kernel", section "The fix: Part 10's split-KV kernel".
+ *   4-bit     y = R( sum_k (s_g q_k + z_g) x_k ), 4-bit codes q in groups of 128
+ *             -- "One Token, Kernel by Kernel", section "4-bit weights".
  *
  * R() is round-to-nearest-even to BF16 (FP16 for the standalone FP16 norm rows),
  * taken directly from the binary64 value (one rounding).  x-hat is rounded to
@@ -415,5 +417,40 @@ void wgo_decode_attention(const uint16_t *q, const uint16_t *k_new, const uint16
             if (of) of[j] = v;
         }
         free(s);
+    }
+}
+
+/* ------------------------------------------------------- 4-bit weights */
+/*
+ * Product with 4-bit integer weights in groups of 128 along K.
+ *   -- "One Token, Kernel by Kernel", section "4-bit weights": every linear
+ *      layer quantised to 4-bit integers in groups of 128.  The pages give no
+ *      bit layout; the reading used here: row n of W4 holds K/2 bytes, byte j
+ *      carries k = 2j in its low nibble and k = 2j+1 in its high nibble; each
+ *      (row, group of 128) has a BF16 scale s and a BF16 zero z, and the
+ *      weight is w = s * q + z for the code q in 0..15.
+ *   y[b][n] = R( sum_k w[n][k] * x[b][k] ),  sequential in k, binary64.
+ *   x [batch][x_stride] BF16; y [batch][N] BF16.
+ */
+void wgo_matvec_int4(const uint8_t *W4, const uint16_t *scales, const uint16_t *zeros, int64_t N, int64_t K,
+                     const uint16_t *x, int64_t x_stride, int64_t batch, uint16_t *y, double *acc_out)
+{
+    const int64_t ng = K / 128;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+#endif
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < batch; ++b) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const uint8_t byte = W4[n * (K / 2) + k / 2];
+                const int q = (k & 1) ? (byte >> 4) : (byte & 15);
+                const double w = wgo_bf16_to_f64(scales[n * ng + k / 128]) * (double)q
+                               + wgo_bf16_to_f64(zeros[n * ng + k / 128]);
+                acc += w * wgo_bf16_to_f64(x[b * x_stride + k]);
+            }
+            y[b * N + n] = wgo_f64_to_bf16(acc);
+            if (acc_out) acc_out[b * N + n] = acc;
+        }
     }
 }
