@@ -33,7 +33,8 @@ def parse():
     ap.add_argument("--workload", default="decode_step_1536x28",
                     choices=["decode_step_1536x28", "decoder_block_1536", "ln_gelu_chain_768x72",
                              "rmsnorm_gemv_256", "rmsnorm_rows_960x1536_f16", "lmhead_151936",
-                             "decode_attention_12q2kv128", "decode_step_attn_1536x28"])
+                             "decode_attention_12q2kv128", "decode_step_attn_1536x28",
+                             "gemv_int4_lmhead_151936"])
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None,
                     help="decode-step workload: number of decoder blocks (default 28)")
@@ -122,6 +123,15 @@ def main():
         dgraph = dstep.capture()
         launch = dgraph.replay
         cfg["graph"] = True
+    elif wl == "gemv_int4_lmhead_151936":
+        # the LM head in 4-bit weights (groups of 128): the largest matrix of the step
+        t4 = gen.make_int4_weights(gen.V, gen.H, seed=1, device=dev)
+        x4 = gen.normal((B, gen.H), 1.0, 5, device=dev)
+        y4 = torch.empty((B, gen.V), dtype=torch.bfloat16, device=dev)
+        nbytes = gen.V * gen.H // 2 + 2 * gen.V * (gen.H // 128) * 2 + B * gen.H * 2 + B * gen.V * 2
+        cfg.update({"N": gen.V, "K": gen.H, "group": 128, "algorithmic_bytes": nbytes})
+        kernel_name = "gemv_int4_kernel"
+        launch = lambda: W.gemv_int4(x4, t4["W4"], t4["scales"], t4["zeros"], y4)  # noqa: E731
     elif wl == "ln_gelu_chain_768x72":
         inp = gen.make_stage_tensors(wl, device=dev, batch=B)
         stages, bufs = steps.ln_gelu_chain_stages(inp, dev)

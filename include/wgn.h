@@ -149,6 +149,23 @@ wgn_status wgn_rmsnorm_rows(const void *x, int64_t x_stride, const void *gamma, 
                             void *y, int64_t y_stride, int32_t rows, int32_t K,
                             int32_t dtype, wgn_stream stream);
 
+/* --------------------------------------------------------- 4-bit weights */
+/* Product with 4-bit integer weights in groups of 128 along K, one launch
+ * ("One Token, Kernel by Kernel", section "4-bit weights"; the pages give no
+ * bit layout, this is the library's):
+ *   W4     [N][K/2] bytes, byte j of a row holds the code of k = 2j in its
+ *          low nibble and of k = 2j+1 in its high nibble (codes 0..15)
+ *   scales, zeros  [N][K/128] BF16: the weight is w = scale * code + zero
+ *   x      [batch][x_stride] BF16;  y [batch][y_stride] BF16
+ *   y[b][n] = R( sum_k w[n][k] x[b][k] ), FP32 accumulation, one rounding.
+ * batch in [1, 8]; K a multiple of 128 with batch * K * 2.125 bytes <= 64 KB
+ * (x and its 32-input sums are staged in LDS), else WGN_E_UNSUPPORTED.  x and
+ * W4 16-byte aligned, x_stride a multiple of 8; y may not overlap the inputs.
+ * No workspace; asynchronous on `stream`; nothing is enqueued on error. */
+wgn_status wgn_gemv_int4(const void *x, int64_t x_stride, int32_t batch, int32_t K, const void *W4,
+                         const void *scales, const void *zeros, int32_t N, void *y, int64_t y_stride,
+                         wgn_stream stream);
+
 /* ------------------------------------------------------ decode attention */
 /* Attention of one new token over a static key/value cache, in one launch
  * ("Making small PyTorch ops faster on a laptop GPU", section "A full decode

@@ -215,3 +215,15 @@ def make_kv_caches(batch: int, slots: int, pos, n_layers: int = N_LAYERS, kv_hea
                                    seed=7, layer=l, nan_tail=nan_tail, device=device)
         out.append({"k_cache": t["k_cache"], "v_cache": t["v_cache"], "pos": t["pos"]})
     return out
+
+
+def make_int4_weights(N: int, K: int, seed: int = 0, device="cpu") -> Dict[str, torch.Tensor]:
+    """Synthetic 4-bit weights in groups of 128, shaped like a quantised
+    N(0, 0.02) matrix: codes uniform in 0..15 packed two per byte (low nibble
+    = even k), per-group scales near 0.1/15 and zeros near -0.05 (BF16)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed_of(43, seed, 0)))
+    W4 = torch.randint(0, 256, (N, K // 2), generator=g, dtype=torch.uint8)
+    sc = (torch.randn((N, K // 128), generator=g) * 0.001 + 0.1 / 15).abs().to(torch.bfloat16)
+    zr = (torch.randn((N, K // 128), generator=g) * 0.005 - 0.05).to(torch.bfloat16)
+    return {"W4": W4.to(device), "scales": sc.to(device), "zeros": zr.to(device)}

@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
         "wgn_lmhead_argmax_workspace_bytes": ([I32], SZ),
         "wgn_lmhead_argmax": ([P, I64, I32, I32, P, F32, P, I32, P, P, P, P, SZ, P], I32),
         "wgn_rmsnorm_rows": ([P, I64, P, F32, P, I64, I32, I32, I32, P], I32),
+        "wgn_gemv_int4": ([P, I64, I32, I32, P, P, P, I32, P, I64, P], I32),
         "wgn_decode_attention_workspace_bytes": ([I32, I32, I32, I32, I32], ctypes.c_size_t),
         "wgn_decode_attention": ([P, P, P, P, P, P, I32, I32, I32, I32, I32, F32, P, P, ctypes.c_size_t, P], I32),
         "wgn_chain_workspace_bytes": ([SP, I32, I32, OP], SZ),

@@ -115,6 +115,21 @@ def rmsnorm_rows(x: torch.Tensor, gamma: torch.Tensor, eps: float, y: torch.Tens
     L.check(st, "wgn_rmsnorm_rows")
 
 
+def gemv_int4(x: torch.Tensor, W4: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, y: torch.Tensor,
+              stream=None) -> None:
+    """wgn_gemv_int4: x [B][K] BF16, W4 [N][K/2] uint8 (low nibble = even k),
+    scales/zeros [N][K/128] BF16, y [B][N] BF16."""
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    y2 = y if y.dim() == 2 else y.view(1, -1)
+    B, K = x2.shape
+    N = W4.shape[0]
+    assert W4.dtype == torch.uint8 and W4.is_contiguous() and W4.shape[1] * 2 == K
+    assert scales.is_contiguous() and zeros.is_contiguous()
+    st = L.lib().wgn_gemv_int4(_ptr(x2), _row_stride(x2), B, K, _ptr(W4), _ptr(scales), _ptr(zeros), N, _ptr(y2),
+                               _row_stride(y2), _stream(stream))
+    L.check(st, "wgn_gemv_int4")
+
+
 def decode_attention_workspace_bytes(batch: int, q_heads: int, kv_heads: int, slots: int,
                                      head_dim: int = 128) -> int:
     return int(L.lib().wgn_decode_attention_workspace_bytes(batch, q_heads, kv_heads, slots, head_dim))

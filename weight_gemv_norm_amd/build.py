@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libwgn.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("wgn_kernels.hip", "wgn_attn.hip", "wgn_api.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("wgn_kernels.hip", "wgn_attn.hip", "wgn_int4.hip", "wgn_api.cpp")]
 HEADERS = [os.path.join(CSRC, f) for f in ("wgn_prog.h", "wgn_loader.h", "wgn_attn.h")] + [os.path.join(INCLUDE, "wgn.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

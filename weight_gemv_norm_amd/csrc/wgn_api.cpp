@@ -24,6 +24,10 @@ hipError_t launch_chain(int32_t batch, bool tile, int32_t ring, const KArgs &a, 
 hipError_t launch_rmsnorm_rows(const uint16_t *x, int64_t xs, const uint16_t *g, float eps, uint16_t *y, int64_t ys,
                                int32_t rows, int32_t K, bool f16, hipStream_t s);
 hipError_t launch_touch(const TouchRange *r, int32_t n, uint32_t frac_q16, int32_t blocks, hipStream_t s);
+size_t gemv_int4_lds_bytes(int32_t batch, int32_t K);
+hipError_t launch_gemv_int4(const uint16_t *x, int64_t xs, int32_t batch, int32_t K, const uint8_t *W4,
+                            const uint16_t *sc, const uint16_t *zr, int32_t N, uint16_t *y, int64_t ys,
+                            int32_t cus, hipStream_t s);
 }  // namespace wgn
 
 using namespace wgn;
@@ -1575,6 +1579,30 @@ wgn_status wgn_decode_attention(const void *q, const void *k_new, const void *v_
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
     hipError_t e = note(launch_decode_attention(a, q_heads / kv_heads, batch, (hipStream_t)stream),
                         "decode_attention launch");
+    return e == hipSuccess ? WGN_OK : WGN_E_HIP;
+}
+
+wgn_status wgn_gemv_int4(const void *x, int64_t x_stride, int32_t batch, int32_t K, const void *W4,
+                         const void *scales, const void *zeros, int32_t N, void *y, int64_t y_stride,
+                         wgn_stream stream) {
+    if (!x || !W4 || !scales || !zeros || !y) return WGN_E_ARG;
+    if (batch < 1 || batch > 8 || N < 1 || K < 128 || (K % 128)) return WGN_E_ARG;
+    if ((batch > 1 && (x_stride < K || y_stride < N)) || x_stride < 0 || y_stride < 0) return WGN_E_ARG;
+    if (!a16(x) || !a16(W4) || (x_stride & 7) || !a2(scales) || !a2(zeros) || !a2(y)) return WGN_E_ALIGN;
+    if (gemv_int4_lds_bytes(batch, K) > 65536) return WGN_E_UNSUPPORTED;
+    {
+        const Range ry = rng(y, ((size_t)(batch - 1) * y_stride + N) * 2);
+        const Range rin[4] = {rng(x, ((size_t)(batch - 1) * x_stride + K) * 2), rng(W4, (size_t)N * K / 2),
+                              rng(scales, (size_t)N * (K / 128) * 2), rng(zeros, (size_t)N * (K / 128) * 2)};
+        for (const Range &r : rin)
+            if (overlap(r, ry)) return WGN_E_ARG;
+    }
+    DevInfo d = device_info();
+    if (!d.ok) return WGN_E_DEVICE;
+    hipError_t e = note(launch_gemv_int4((const uint16_t *)x, x_stride, batch, K, (const uint8_t *)W4,
+                                         (const uint16_t *)scales, (const uint16_t *)zeros, N, (uint16_t *)y,
+                                         batch > 1 ? y_stride : N, d.cus > 0 ? d.cus : 256, (hipStream_t)stream),
+                        "gemv_int4 launch");
     return e == hipSuccess ? WGN_OK : WGN_E_HIP;
 }
 

@@ -1,0 +1,156 @@
+// Product with 4-bit weights in groups of 128 along K ("One Token, Kernel by
+// Kernel", section "4-bit weights"): y[b][n] = R(sum_k (s q + z) x[b][k]),
+// with q the 4-bit code (low nibble = even k), s and z the BF16 scale and zero
+// of (row n, group k/128).
+//
+// Each lane owns 16 bytes (32 codes, a quarter of a group) of a row per 1 KB
+// slice; a wave takes 4 rows at a time, all their loads issued before use.
+// Codes become BF16 pairs without conversion instructions: the byte permute
+// v_perm_b32 places one code in the mantissa of each half and an OR with
+// 0x4300 gives the BF16 values 128 + q, exact; v_dot2_f32_bf16 then forms
+// sum (128 + q) x in FP32.  With S = sum x over the lane's 32 inputs
+// (computed once per workgroup), the lane's share of the row is
+//   s * dot + (z - 128 s) * S  =  sum (s q + z) x.
+// x (all batch rows) and the 32-input sums are staged in LDS once per
+// workgroup; workgroups stride over row groups.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace wgn {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int I4_ROWS = 4;                   // rows per wave at a time
+constexpr int I4_WAVES = 4;
+constexpr uint32_t I4_MAGIC = 0x43004300u;   // BF16 128.0 in both halves
+
+__device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 64 lanes; every lane gets the same bits.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+template <int B>
+__global__ __launch_bounds__(64 * I4_WAVES) void gemv_int4_kernel(const uint16_t *x, int64_t xs, int32_t K,
+                                                                 const uint8_t *W4, const uint16_t *sc,
+                                                                 const uint16_t *zr, int32_t N, uint16_t *y,
+                                                                 int64_t ys) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    uint16_t *sx = (uint16_t *)lds;                        // [B][K] BF16
+    float *ssum = (float *)(lds + (size_t)B * K * 2);      // [B][K/32]
+    const int32_t tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int32_t K8 = K / 8, K32 = K / 32, half = K / 2, ng = K / 128;
+    for (int32_t i = tid; i < B * K8; i += 64 * I4_WAVES) {
+        const int32_t b = i / K8, j = i - b * K8;
+        *(u32x4 *)(sx + (size_t)b * K + j * 8) = *(const u32x4 *)(x + (size_t)b * xs + j * 8);
+    }
+    __syncthreads();
+    for (int32_t i = tid; i < B * K32; i += 64 * I4_WAVES) {
+        const int32_t b = i / K32, j = i - b * K32;
+        const uint32_t *p = (const uint32_t *)(sx + (size_t)b * K + j * 32);
+        float s = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) s += bf2f(p[m] & 0xFFFFu) + bf2f(p[m] >> 16);
+        ssum[i] = s;
+    }
+    __syncthreads();
+
+    const int32_t slices = (half + 1023) / 1024;
+    const int32_t groups = (N + I4_ROWS * I4_WAVES - 1) / (I4_ROWS * I4_WAVES);
+    for (int32_t rg = blockIdx.x; rg < groups; rg += gridDim.x) {
+        const int32_t n0 = (rg * I4_WAVES + w) * I4_ROWS;
+        float acc[I4_ROWS][B];
+#pragma unroll
+        for (int r = 0; r < I4_ROWS; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+        for (int32_t c = 0; c < slices; ++c) {
+            const int32_t byte0 = (c * 64 + lane) * 16;    // this lane's bytes within a row
+            const bool act = byte0 < half;
+            const int32_t kb = act ? byte0 * 2 : 0;        // first k of those bytes
+            const int32_t g = kb / 128;
+            u32x4 code[I4_ROWS];
+            float s[I4_ROWS], z[I4_ROWS];
+#pragma unroll
+            for (int r = 0; r < I4_ROWS; ++r) {
+                const int32_t n = min(n0 + r, N - 1);      // in range; rows past N are not stored
+                code[r] = *(const u32x4 *)(W4 + (size_t)n * half + (act ? byte0 : 0));
+                s[r] = bf2f(sc[(size_t)n * ng + g]);
+                z[r] = bf2f(zr[(size_t)n * ng + g]);
+            }
+            if (act) {
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const u32x4 *xp = (const u32x4 *)(sx + (size_t)b * K + kb);
+                    const u32x4 xv[4] = {xp[0], xp[1], xp[2], xp[3]};
+                    const float S = ssum[b * K32 + kb / 32];
+#pragma unroll
+                    for (int r = 0; r < I4_ROWS; ++r) {
+                        const uint32_t cw[4] = {code[r].x, code[r].y, code[r].z, code[r].w};
+                        float dot = 0.0f;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const uint32_t lo = cw[u] & 0x0F0F0F0Fu, hi = (cw[u] >> 4) & 0x0F0F0F0Fu;
+                            const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                // bytes [lo_j, 0, hi_j, 0]: codes of k = 2j (low half) and 2j+1 (high half)
+                                const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
+                                const uint32_t pair = __builtin_amdgcn_perm(hi, lo, sel) | I4_MAGIC;
+                                dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                                                      __builtin_bit_cast(bf16x2, xw[j]), dot, false);
+                            }
+                        }
+                        acc[r][b] += s[r] * dot + (z[r] - 128.0f * s[r]) * S;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < I4_ROWS; ++r) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const float t = wave_sum(acc[r][b]);
+                if (lane == 0 && n0 + r < N)
+                    y[(size_t)b * ys + n0 + r] = __builtin_bit_cast(uint16_t, (__bf16)t);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+size_t gemv_int4_lds_bytes(int32_t batch, int32_t K) { return (size_t)batch * K * 2 + (size_t)batch * (K / 32) * 4; }
+
+hipError_t launch_gemv_int4(const uint16_t *x, int64_t xs, int32_t batch, int32_t K, const uint8_t *W4,
+                            const uint16_t *sc, const uint16_t *zr, int32_t N, uint16_t *y, int64_t ys,
+                            int32_t cus, hipStream_t s) {
+    const int32_t groups = (N + I4_ROWS * I4_WAVES - 1) / (I4_ROWS * I4_WAVES);
+    const int32_t blocks = groups < 8 * cus ? groups : 8 * cus;
+    const size_t lds = gemv_int4_lds_bytes(batch, K);
+    dim3 grid(blocks), block(64 * I4_WAVES);
+    switch (batch) {
+#define WGN_I4_CASE(BB) \
+    case BB: hipLaunchKernelGGL(gemv_int4_kernel<BB>, grid, block, lds, s, x, xs, K, W4, sc, zr, N, y, ys); break;
+    WGN_I4_CASE(1) WGN_I4_CASE(2) WGN_I4_CASE(3) WGN_I4_CASE(4)
+    WGN_I4_CASE(5) WGN_I4_CASE(6) WGN_I4_CASE(7) WGN_I4_CASE(8)
+#undef WGN_I4_CASE
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace wgn
