@@ -22,7 +22,10 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int I4_ROWS = 4;                   // rows per wave at a time
+#ifndef WGN_I4_ROWS
+#define WGN_I4_ROWS 4
+#endif
+constexpr int I4_ROWS = WGN_I4_ROWS;         // rows per wave at a time
 constexpr int I4_WAVES = 4;
 constexpr uint32_t I4_MAGIC = 0x43004300u;   // BF16 128.0 in both halves
 
@@ -32,14 +35,16 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-// Sum over the 64 lanes; every lane gets the same bits.
-__device__ __forceinline__ float wave_sum(float v) {
+// Sum over the 64 lanes, complete in lane 63 only: rows of 16 lanes by DPP,
+// then DPP row broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2
+// and 3), so no LDS permute is on the path.
+__device__ __forceinline__ float wave_sum_last(float v) {
     v += dpp_f<0xB1>(v);
     v += dpp_f<0x4E>(v);
     v += dpp_f<0x141>(v);
     v += dpp_f<0x140>(v);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31
     return v;
 }
 
@@ -92,29 +97,42 @@ __global__ __launch_bounds__(64 * I4_WAVES) void gemv_int4_kernel(const uint16_t
                 z[r] = bf2f(zr[(size_t)n * ng + g]);
             }
             if (act) {
+                // x of every batch row for this lane's 32 inputs, and their sums
+                uint32_t xw[B][16];
+                float S[B];
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
                     const u32x4 *xp = (const u32x4 *)(sx + (size_t)b * K + kb);
-                    const u32x4 xv[4] = {xp[0], xp[1], xp[2], xp[3]};
-                    const float S = ssum[b * K32 + kb / 32];
 #pragma unroll
-                    for (int r = 0; r < I4_ROWS; ++r) {
-                        const uint32_t cw[4] = {code[r].x, code[r].y, code[r].z, code[r].w};
+                    for (int u = 0; u < 4; ++u) {
+                        const u32x4 v = xp[u];
+                        xw[b][4 * u] = v.x; xw[b][4 * u + 1] = v.y; xw[b][4 * u + 2] = v.z; xw[b][4 * u + 3] = v.w;
+                    }
+                    S[b] = ssum[b * K32 + kb / 32];
+                }
+#pragma unroll
+                for (int r = 0; r < I4_ROWS; ++r) {
+                    // the row's 16 code pairs as BF16 (128 + q) pairs, decoded once for all batch rows
+                    const uint32_t cw[4] = {code[r].x, code[r].y, code[r].z, code[r].w};
+                    uint32_t pr[16];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t lo = cw[u] & 0x0F0F0F0Fu, hi = (cw[u] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            // bytes [lo_j, 0, hi_j, 0]: codes of k = 2j (low half) and 2j+1 (high half)
+                            const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
+                            pr[4 * u + j] = __builtin_amdgcn_perm(hi, lo, sel) | I4_MAGIC;
+                        }
+                    }
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
                         float dot = 0.0f;
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const uint32_t lo = cw[u] & 0x0F0F0F0Fu, hi = (cw[u] >> 4) & 0x0F0F0F0Fu;
-                            const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                // bytes [lo_j, 0, hi_j, 0]: codes of k = 2j (low half) and 2j+1 (high half)
-                                const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
-                                const uint32_t pair = __builtin_amdgcn_perm(hi, lo, sel) | I4_MAGIC;
-                                dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
-                                                                      __builtin_bit_cast(bf16x2, xw[j]), dot, false);
-                            }
-                        }
-                        acc[r][b] += s[r] * dot + (z[r] - 128.0f * s[r]) * S;
+                        for (int m = 0; m < 16; ++m)
+                            dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr[m]),
+                                                                  __builtin_bit_cast(bf16x2, xw[b][m]), dot, false);
+                        acc[r][b] += s[r] * dot + (z[r] - 128.0f * s[r]) * S[b];
                     }
                 }
             }
@@ -123,8 +141,8 @@ __global__ __launch_bounds__(64 * I4_WAVES) void gemv_int4_kernel(const uint16_t
         for (int r = 0; r < I4_ROWS; ++r) {
 #pragma unroll
             for (int b = 0; b < B; ++b) {
-                const float t = wave_sum(acc[r][b]);
-                if (lane == 0 && n0 + r < N)
+                const float t = wave_sum_last(acc[r][b]);
+                if (lane == 63 && n0 + r < N)
                     y[(size_t)b * ys + n0 + r] = __builtin_bit_cast(uint16_t, (__bf16)t);
             }
         }
