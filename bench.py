@@ -300,11 +300,13 @@ CSRC = os.path.join(ROOT, "weight_gemv_norm_amd", "csrc")
 KERNEL_SOURCES = {
     "chain_kernel": ("wgn_api.cpp", "wgn_kernels.hip", "wgn_loader.h", "wgn_prog.h"),
     "decode_attention_kernel": ("wgn_attn.h", "wgn_attn.hip"),
+    "gemv_int4_kernel": ("wgn_int4.hip",),
 }
 
 
 def kernel_of(workload: str) -> str:
-    return "decode_attention_kernel" if workload == "decode_attention_12q2kv128" else "chain_kernel"
+    return {"decode_attention_12q2kv128": "decode_attention_kernel",
+            "gemv_int4_lmhead_151936": "gemv_int4_kernel"}.get(workload, "chain_kernel")
 
 
 def kernel_sources_digest(kernel: str = "chain_kernel") -> str:
