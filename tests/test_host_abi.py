@@ -389,3 +389,28 @@ def test_decode_attention_workspace_layout(batch, hq, hkv, slots):
     want = sum(al(batch * hkv * c * entry) for c in counts[:-1]) + sum(al(batch * hkv * c * 4) for c in counts[1:])
     got = L.lib().wgn_decode_attention_workspace_bytes(batch, hq, hkv, slots, 128)
     assert got == max(want, 256)
+
+
+# ------------------------------------------------------------ 4-bit weights
+def _i4_call(**kw):
+    a = dict(x=0x10000, x_stride=1536, batch=1, K=1536, W4=0x1000000, scales=0x2000000, zeros=0x3000000,
+             N=1536, y=0x4000000, y_stride=1536)
+    a.update(kw)
+    return L.lib().wgn_gemv_int4(a["x"], a["x_stride"], a["batch"], a["K"], a["W4"], a["scales"], a["zeros"],
+                                 a["N"], a["y"], a["y_stride"], None)
+
+
+def test_gemv_int4_checks_arguments_before_the_device():
+    assert _i4_call(x=None) == L.E_ARG
+    assert _i4_call(zeros=None) == L.E_ARG
+    assert _i4_call(K=1500, x_stride=1500) == L.E_ARG          # not a multiple of 128
+    assert _i4_call(batch=0) == L.E_ARG
+    assert _i4_call(batch=9) == L.E_ARG
+    assert _i4_call(N=0) == L.E_ARG
+    assert _i4_call(batch=2, x_stride=1000) == L.E_ARG         # rows overlap
+    assert _i4_call(x=0x10008) == L.E_ALIGN
+    assert _i4_call(W4=0x1000004) == L.E_ALIGN
+    assert _i4_call(batch=2, x_stride=1540, y_stride=1536) == L.E_ALIGN
+    assert _i4_call(scales=0x2000001) == L.E_ALIGN
+    assert _i4_call(batch=8, K=8960, x_stride=8960) == L.E_UNSUPPORTED   # x does not fit in LDS
+    assert _i4_call(y=0x1000000) == L.E_ARG                    # output over the codes
