@@ -26,7 +26,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #define WGN_I4_ROWS 4
 #endif
 constexpr int I4_ROWS = WGN_I4_ROWS;         // rows per wave at a time
-constexpr int I4_WAVES = 4;
+#ifndef WGN_I4_WAVES
+#define WGN_I4_WAVES 4
+#endif
+#ifndef WGN_I4_BLOCKS_PER_CU
+#define WGN_I4_BLOCKS_PER_CU 8
+#endif
+constexpr int I4_WAVES = WGN_I4_WAVES;
+constexpr int I4_BLOCKS_PER_CU = WGN_I4_BLOCKS_PER_CU;  // cap of the grid (workgroups stride over row groups)
 constexpr uint32_t I4_MAGIC = 0x43004300u;   // BF16 128.0 in both halves
 
 __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
@@ -157,7 +164,7 @@ hipError_t launch_gemv_int4(const uint16_t *x, int64_t xs, int32_t batch, int32_
                             const uint16_t *sc, const uint16_t *zr, int32_t N, uint16_t *y, int64_t ys,
                             int32_t cus, hipStream_t s) {
     const int32_t groups = (N + I4_ROWS * I4_WAVES - 1) / (I4_ROWS * I4_WAVES);
-    const int32_t blocks = groups < 8 * cus ? groups : 8 * cus;
+    const int32_t blocks = groups < I4_BLOCKS_PER_CU * cus ? groups : I4_BLOCKS_PER_CU * cus;
     const size_t lds = gemv_int4_lds_bytes(batch, K);
     dim3 grid(blocks), block(64 * I4_WAVES);
     switch (batch) {
