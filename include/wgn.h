@@ -119,7 +119,12 @@ int32_t wgn_device_cu_count(void);
  * (0 unless epi == ARGMAX). */
 size_t wgn_gemv_norm_workspace_bytes(const wgn_stage *stage, int32_t batch);
 
-/* One norm-fused product, one kernel launch.  batch in [1, 16]; batch rows of
+/* One norm-fused product, one kernel launch: the normalisation of "GPU Kernel
+ * Optimization" README, section "Architecture" (mean square, rsqrt and gain
+ * multiply fused into one pass) feeding the weight-matrix x activation-vector
+ * product that "One Token, Kernel by Kernel", section "What one block
+ * launches", runs as a norm kernel followed by a matrix-vector kernel; here
+ * both are one launch.  batch in [1, 16]; batch rows of
  * x, residual and y are independent.  The normalisation prologue is computed
  * by every workgroup from the whole input vector, so there is no separate
  * norm kernel.  Batches up to 4 use the vector (v_dot2) path, larger batches
@@ -158,7 +163,7 @@ wgn_status wgn_rmsnorm_rows(const void *x, int64_t x_stride, const void *gamma, 
  *   scales, zeros  [N][K/128] BF16: the weight is w = scale * code + zero
  *   x      [batch][x_stride] BF16;  y [batch][y_stride] BF16
  *   y[b][n] = R( sum_k w[n][k] x[b][k] ), FP32 accumulation, one rounding.
- * batch in [1, 8]; K a multiple of 128 with batch * K * 2.125 bytes <= 64 KB
+ * batch in [1, 8]; K a multiple of 128 with batch * K * 2.125 bytes <= 160 KB
  * (x and its 32-input sums are staged in LDS), else WGN_E_UNSUPPORTED.  x and
  * W4 16-byte aligned, x_stride a multiple of 8; y may not overlap the inputs.
  * No workspace; asynchronous on `stream`; nothing is enqueued on error. */
@@ -200,6 +205,22 @@ wgn_status wgn_decode_attention(const void *q, const void *k_new, const void *v_
                                 int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t slots,
                                 int32_t head_dim, float scale, void *out,
                                 void *workspace, size_t ws_bytes, wgn_stream stream);
+
+/* ------------------------------------------------------ read ceiling */
+/* Plain streaming read of `bytes` of device memory (a measurement, not a step
+ * of the method): the GPU's measured HBM read ceiling, against which the
+ * weight stream's bandwidth is reported beside the rated peak ("One Token,
+ * Kernel by Kernel", section "Step 2: every kernel class on the roofline": the
+ * pages measure their card's read ceiling and quote both).  Each 16-byte chunk
+ * of src is read once with a non-temporal 128-bit load; `grid` workgroups of
+ * `threads` threads (a multiple of 64, at most 1024), each lane keeping `depth`
+ * loads in flight (1, 2, 4, 8 or 16).  sink: one device uint32 that the kernel
+ * writes only when the folded value of a lane's loads equals a fixed pattern
+ * (it exists so the loads cannot be removed; its content is meaningless).
+ * src 16-byte aligned, bytes a non-zero multiple of 16.  Asynchronous on
+ * `stream`; nothing is enqueued on error. */
+wgn_status wgn_stream_read(const void *src, size_t bytes, int32_t grid, int32_t threads, int32_t depth,
+                           uint32_t *sink, wgn_stream stream);
 
 /* --------------------------------------------------------------- chains */
 /* A chain is a list of stages in dependency order (a stage may read earlier
@@ -255,8 +276,20 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
 wgn_status wgn_chain_run(const wgn_chain *chain, wgn_stream stream);
 
 /* Synchronise `stream` and report WGN_E_TIMEOUT if an in-kernel wait of an
- * earlier run hit its bound (the counters are then reset); else WGN_OK. */
+ * earlier run hit its bound (the counters are then reset); else WGN_OK.
+ * Once a wait has given up, the error word stays set and every later run of
+ * the chain (also a graph replay) exits at once without writing anything,
+ * until this call has reset the counters: a run never proceeds on the flags
+ * an aborted run left behind. */
 wgn_status wgn_chain_check(const wgn_chain *chain, wgn_stream stream);
+
+/* Bound of every in-kernel wait of later runs of this chain, in microseconds
+ * (a negative value restores the default of 2 s; 0 makes a wait give up at
+ * its first poll that does not find every flag).  Each wait polls, so every
+ * kernel still ends when the bound is hit; this is how tests force the
+ * time-out path from the host.  WGN_E_ARG for a null chain or a bound above
+ * the default.  Takes effect from the next wgn_chain_run. */
+wgn_status wgn_chain_set_wait_us(wgn_chain *chain, int64_t us);
 
 int32_t wgn_chain_num_phases(const wgn_chain *chain);
 int32_t wgn_chain_grid(const wgn_chain *chain);
@@ -281,10 +314,26 @@ wgn_status wgn_chain_trace(const wgn_chain *chain, wgn_stream stream, uint64_t *
 wgn_status wgn_chain_stage_phases(const wgn_chain *chain, int32_t *phase_of_stage);
 void wgn_chain_destroy(wgn_chain *chain);
 
-/* create + run + destroy in one call (the create step synchronises `stream`). */
+/* create + run + destroy in one call (the create step synchronises `stream`):
+ * the chain of layers that read weights, each a norm-fused product, of "One
+ * Token, Kernel by Kernel", sections "What one block launches" and "The whole
+ * step", run with a plan as "Making small PyTorch ops faster on a laptop GPU",
+ * section "Beyond language models", runs a stage list it has tuned once.
+ * plan: NULL or plan->prefetch == 0 runs the chain plainly; a prefetch plan
+ * (from wgn_plan_tune) needs opts->mode == 1 (WGN_E_UNSUPPORTED otherwise) and
+ * runs its touch passes on `side` (see wgn_chain_run_plan); side is ignored
+ * without one.  The workspace is sized by wgn_chain_workspace_bytes for the
+ * same opts (wgn_workspace_bytes covers every mode). */
 wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t batch,
-                           const wgn_chain_opts *opts, void *workspace, size_t ws_bytes,
-                           wgn_stream stream);
+                           const wgn_chain_opts *opts, const struct wgn_plan *plan, void *workspace,
+                           size_t ws_bytes, wgn_stream stream, wgn_stream side);
+
+/* One workspace size that serves every call of the library on these stages at
+ * this batch: a chain over them in either mode with default options, each
+ * stage alone through wgn_gemv_norm, and -- when V > 0 -- wgn_lmhead_argmax
+ * over V rows.  0 if the stages cannot be planned (a call on them would
+ * return its error). */
+size_t wgn_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch, int32_t V);
 
 /* -------------------------------------------------------- prefetch plans */
 /* Optional prefetch of later launches' weights into the GPU's memory-side
@@ -329,7 +378,18 @@ wgn_status wgn_chain_run_plan(const wgn_chain *chain, const wgn_plan *plan, wgn_
  * chain's outputs.  Not for the hot loop.  Errors: WGN_E_ARG (null chain or
  * out, reps out of range, null or equal streams), WGN_E_UNSUPPORTED (mode-0
  * chain), WGN_E_HIP. */
-wgn_status wgn_plan_tune(const wgn_chain *chain, wgn_stream stream, wgn_stream side, int32_t reps, wgn_plan *out);
+wgn_status wgn_chain_plan_tune(const wgn_chain *chain, wgn_stream stream, wgn_stream side, int32_t reps,
+                               wgn_plan *out);
+
+/* The same tuning for a stage list ("Making small PyTorch ops faster on a
+ * laptop GPU", section "Beyond language models": a list of stages is tuned
+ * once and the plan kept): plans a one-launch-per-phase chain over the stages
+ * in `workspace` (at least wgn_workspace_bytes(stages, n, batch, 0) bytes,
+ * zero-filled), tunes it in 15 rounds as wgn_chain_plan_tune and writes the
+ * plan to keep to *out.  Synchronises `stream`; overwrites the stages'
+ * outputs.  Errors as wgn_chain_create and wgn_chain_plan_tune. */
+wgn_status wgn_plan_tune(const wgn_stage *stages, int32_t n_stages, int32_t batch, wgn_plan *out,
+                         void *workspace, size_t ws_bytes, wgn_stream stream, wgn_stream side);
 
 /* --------------------------------------------------------- host helpers */
 /* The first wave of `waves` whose even share of `units` work units contains

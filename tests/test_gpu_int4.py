@@ -27,7 +27,8 @@ def _run(N, K, B, seed):
 
 
 @pytest.mark.parametrize("N,K,B", [(1, 128, 1), (17, 256, 1), (1536, 1536, 1), (256, 1536, 4), (8960, 1536, 1),
-                                   (8960, 1536, 8), (1536, 8960, 1), (1536, 8960, 3), (4099, 1536, 2),
+                                   (8960, 1536, 8), (1536, 8960, 1), (1536, 8960, 3), (1536, 8960, 4),
+                                   (1536, 8960, 8), (4099, 1536, 2),
                                    (300, 2176, 5)])
 def test_gemv_int4_matches_oracle(N, K, B):
     say("gemv_int4 N %d K %d batch %d" % (N, K, B))

@@ -412,5 +412,93 @@ def test_gemv_int4_checks_arguments_before_the_device():
     assert _i4_call(W4=0x1000004) == L.E_ALIGN
     assert _i4_call(batch=2, x_stride=1540, y_stride=1536) == L.E_ALIGN
     assert _i4_call(scales=0x2000001) == L.E_ALIGN
-    assert _i4_call(batch=8, K=8960, x_stride=8960) == L.E_UNSUPPORTED   # x does not fit in LDS
+    assert _i4_call(batch=8, K=9728, x_stride=9728) == L.E_UNSUPPORTED   # x does not fit in 160 KB of LDS
     assert _i4_call(y=0x1000000) == L.E_ARG                    # output over the codes
+
+
+def test_python_wrappers_check_tensor_shapes_before_the_library():
+    """The C ABI cannot see tensor sizes: the wrappers refuse mismatched
+    shapes and dtypes (CPU tensors here; the checks come before any call)."""
+    import torch
+    import weight_gemv_norm_amd as W
+    bf = torch.bfloat16
+    N, K = 64, 256
+    x = torch.zeros(1, K, dtype=bf)
+    W4 = torch.zeros(N, K // 2, dtype=torch.uint8)
+    sc = torch.zeros(N, K // 128, dtype=bf)
+    y = torch.zeros(1, N, dtype=bf)
+    bad = [dict(scales=torch.zeros(N, K // 64, dtype=bf)),            # wrong group count
+           dict(zeros=torch.zeros(N + 1, K // 128, dtype=bf)),        # wrong rows
+           dict(scales=torch.zeros(N, K // 128, dtype=torch.float32)),
+           dict(x=torch.zeros(1, K, dtype=torch.float16)),
+           dict(W4=torch.zeros(N, K // 4, dtype=torch.uint8)),         # codes for another K
+           dict(y=torch.zeros(1, N - 1, dtype=bf))]
+    for b in bad:
+        a = dict(x=x, W4=W4, scales=sc, zeros=sc.clone(), y=y)
+        a.update(b)
+        with pytest.raises(ValueError):
+            W.gemv_int4(a["x"], a["W4"], a["scales"], a["zeros"], a["y"])
+    with pytest.raises(ValueError):  # right shapes, but not on the GPU
+        W.gemv_int4(x, W4, sc, sc.clone(), y)
+
+    B, Hq, Hkv, S, D = 1, 12, 2, 256, 128
+    q = torch.zeros(B, Hq, D, dtype=bf)
+    kn = torch.zeros(B, Hkv, D, dtype=bf)
+    kc = torch.zeros(B, Hkv, S, D, dtype=bf)
+    pos = torch.zeros(B, dtype=torch.int32)
+    bad = [dict(k_new=torch.zeros(B, Hkv + 1, D, dtype=bf)),
+           dict(v_new=torch.zeros(B, Hkv, D, dtype=torch.float32)),
+           dict(v_cache=torch.zeros(B, Hkv, S - 1, D, dtype=bf)),
+           dict(pos=torch.zeros(B + 1, dtype=torch.int32)),
+           dict(pos=torch.zeros(B, dtype=torch.int64)),
+           dict(out=torch.zeros(B, Hq, D + 8, dtype=bf))]
+    for b in bad:
+        a = dict(q=q, k_new=kn, v_new=kn.clone(), k_cache=kc, v_cache=kc.clone(), pos=pos, out=q.clone())
+        a.update(b)
+        with pytest.raises(ValueError):
+            W.decode_attention(a["q"], a["k_new"], a["v_new"], a["k_cache"], a["v_cache"], a["pos"], a["out"])
+
+
+def test_stream_read_and_wait_bound_check_arguments():
+    f = L.lib().wgn_stream_read
+    assert f(None, 1024, 256, 256, 8, 0x1000, None) == L.E_ARG
+    assert f(0x10000, 1000, 256, 256, 8, 0x1000, None) == L.E_ARG       # not a multiple of 16
+    assert f(0x10000, 1024, 0, 256, 8, 0x1000, None) == L.E_ARG
+    assert f(0x10000, 1024, 256, 100, 8, 0x1000, None) == L.E_ARG       # not whole waves
+    assert f(0x10000, 1024, 256, 256, 3, 0x1000, None) == L.E_ARG       # depth not a power of two
+    assert f(0x10008, 1024, 256, 256, 8, 0x1000, None) == L.E_ALIGN
+    assert f(0x10000, 1024, 256, 256, 8, None, None) == L.E_ARG
+    assert L.lib().wgn_chain_set_wait_us(None, 0) == L.E_ARG
+
+
+def test_workspace_bytes_serves_every_call():
+    """wgn_workspace_bytes covers the chain in both modes, each stage alone and
+    the LM head; 0 when the stages cannot be planned."""
+    import ctypes
+    lib = L.lib()
+    for B in (1, 4, 16):
+        stages = fake_decoder(Arena(), B, 2, V=4096)
+        arr = L.stage_array(stages)
+        total = lib.wgn_workspace_bytes(arr, len(stages), B, 151936)
+        assert total > 0
+        for mode in (0, 1):
+            o = L.ChainOpts()
+            o.mode = mode
+            assert total >= lib.wgn_chain_workspace_bytes(arr, len(stages), B, ctypes.byref(o))
+        for st in stages:
+            assert total >= lib.wgn_gemv_norm_workspace_bytes(ctypes.byref(st), B)
+        assert total >= lib.wgn_lmhead_argmax_workspace_bytes(B)
+    assert lib.wgn_workspace_bytes(arr, len(stages), 17, 0) == 0   # batch out of range
+
+
+def test_layer_chain_and_plan_tune_check_arguments_before_the_device():
+    import ctypes
+    stages = fake_decoder(Arena(), 1, 1, V=4096)
+    arr = L.stage_array(stages)
+    lib = L.lib()
+    plan = L.Plan()
+    plan.prefetch, plan.distance, plan.blocks, plan.frac_pct = 1, 1, 16, 50
+    o = L.ChainOpts()  # mode 0: a persistent chain takes no prefetch plan
+    assert lib.wgn_layer_chain(arr, len(stages), 1, ctypes.byref(o), ctypes.byref(plan), 0x100000, 1 << 30,
+                               None, 0x1234) == L.E_UNSUPPORTED
+    assert lib.wgn_plan_tune(arr, len(stages), 1, None, 0x100000, 1 << 30, None, 0x1234) == L.E_ARG

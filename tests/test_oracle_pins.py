@@ -402,3 +402,88 @@ def test_rmsnorm_rows_f16_vs_numpy():
     ref = xv / np.sqrt(np.mean(xv * xv, axis=1, keepdims=True) + eps) * g.astype(np.float64)
     want = ref.astype(np.float16).view(np.uint16)
     assert np.array_equal(got, want)
+
+
+def test_swiglu_operand_order_asymmetric():
+    """SwiGLU reads the first matrix as the gate: s = R(silu(W x) * (W_up x))
+    ("One Token, Kernel by Kernel", section "The setup": SwiGLU MLP).  Gate and up
+    are different, both non-zero, so the swapped reading silu(W_up x) * (W x)
+    gives other bits; the cases are checked against exact rational sums and
+    60-digit decimal SiLU, and the swap is shown to fail the same check."""
+    N, K = 16, 32
+    x = rand_bf16((2, K))
+    W = rand_bf16((N, K), std=0.3)
+    cases = [rand_bf16((N, K), std=0.5)]  # an unrelated up matrix
+    onehot = np.zeros((N, K), dtype=np.uint16)
+    for n in range(N):
+        onehot[n, (5 * n + 3) % K] = 0x4000  # 2.0 at one column: up = 2 x_k exactly
+    cases.append(onehot)
+    for W_up in cases:
+        ys = O.stage(x, W, epi=O.EPI_SWIGLU, W_up=W_up)
+        swapped_differs = False
+        for b in range(2):
+            for n in range(N):
+                ag = sum(bf16_val(int(W[n, k])) * bf16_val(int(x[b, k])) for k in range(K))
+                au = sum(bf16_val(int(W_up[n, k])) * bf16_val(int(x[b, k])) for k in range(K))
+                want = rne_bf16_bits(dec_to_frac(dsilu(dec(ag)) * dec(au)))
+                swap = rne_bf16_bits(dec_to_frac(dsilu(dec(au)) * dec(ag)))
+                assert int(ys[b, n]) == want, (b, n)
+                swapped_differs |= swap != want
+        assert swapped_differs, "the case must tell the gate from the up matrix"
+
+
+def rne_f16_bits(fr: Fraction) -> int:
+    """Round an exact rational to IEEE binary16 (nearest, ties to even), integer math only."""
+    if fr == 0:
+        return 0
+    sign = 0x8000 if fr < 0 else 0
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -14)  # subnormals share the smallest normal exponent's ulp
+    ulp = Fraction(2) ** (e - 10)
+    q = a / ulp
+    fl = q.numerator // q.denominator
+    rem = q - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = fl * ulp
+    if r >= 65520:  # rounds past the largest finite value
+        return sign | 0x7C00
+    bits = int(np.array([float(r)], dtype=np.float16).view(np.uint16)[0])
+    assert Fraction(float(np.float16(float(r)))) == r  # exactly representable
+    return sign | bits
+
+
+def test_rmsnorm_rows_f16_eps_placement():
+    """The FP16 rows norm puts eps inside the root, y = R16(x (mean x^2 + eps)^-1/2 g)
+    ("GPU Kernel Optimization" README, section "Architecture": mean square, rsqrt,
+    weight multiply).  Rows of std 1e-3 make the mean square comparable to
+    eps = 1e-6, so eps outside the root, eps dropped or eps added after the
+    mean's division all give other bits; checked against exact FP16 inputs,
+    60-digit decimal arithmetic and integer-only rounding to FP16."""
+    R, K = 3, 96
+    x = (RNG.standard_normal((R, K)) * 1e-3).astype(np.float16)
+    g = (1 + 0.1 * RNG.standard_normal(K)).astype(np.float16)
+    eps32 = float(np.float32(1e-6))
+    got = O.rmsnorm_rows_f16(x.view(np.uint16), g.view(np.uint16), eps32)
+    xs = [[Fraction(float(v)) for v in row] for row in x]
+    gs = [Fraction(float(v)) for v in g]
+    deps = dec(Fraction(eps32))
+    alt_differs = {"outside": False, "dropped": False}
+    for r in range(R):
+        ms = dec(sum(v * v for v in xs[r]) / K)
+        assert abs(ms - deps) < 2 * deps, "mean square must be comparable to eps"
+        inv = 1 / (ms + deps).sqrt()
+        inv_out = 1 / (ms.sqrt() + deps)
+        inv_drop = 1 / ms.sqrt()
+        for k in range(K):
+            xk, gk = dec(xs[r][k]), dec(gs[k])
+            want = rne_f16_bits(dec_to_frac(xk * inv * gk))
+            assert int(got[r, k]) == want, (r, k)
+            alt_differs["outside"] |= rne_f16_bits(dec_to_frac(xk * inv_out * gk)) != want
+            alt_differs["dropped"] |= rne_f16_bits(dec_to_frac(xk * inv_drop * gk)) != want
+    assert all(alt_differs.values()), alt_differs

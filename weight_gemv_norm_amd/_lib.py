@@ -5,8 +5,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# WGN_LIB_PATH selects another build of the same library (tuning experiments).
-LIB_PATH = os.environ.get("WGN_LIB_PATH") or os.path.join(HERE, "libwgn.so")
+# The in-tree build only: the product never loads another library.
+LIB_PATH = os.path.join(HERE, "libwgn.so")
 
 TRACE_POINTS = 12
 OK, E_ARG, E_ALIGN, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_DEVICE, E_TIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7
@@ -82,21 +82,25 @@ def lib() -> ctypes.CDLL:
         "wgn_lmhead_argmax": ([P, I64, I32, I32, P, F32, P, I32, P, P, P, P, SZ, P], I32),
         "wgn_rmsnorm_rows": ([P, I64, P, F32, P, I64, I32, I32, I32, P], I32),
         "wgn_gemv_int4": ([P, I64, I32, I32, P, P, P, I32, P, I64, P], I32),
+        "wgn_stream_read": ([P, SZ, I32, I32, I32, P, P], I32),
         "wgn_decode_attention_workspace_bytes": ([I32, I32, I32, I32, I32], ctypes.c_size_t),
         "wgn_decode_attention": ([P, P, P, P, P, P, I32, I32, I32, I32, I32, F32, P, P, ctypes.c_size_t, P], I32),
         "wgn_chain_workspace_bytes": ([SP, I32, I32, OP], SZ),
         "wgn_chain_create": ([SP, I32, I32, OP, P, SZ, P, ctypes.POINTER(P)], I32),
         "wgn_chain_run": ([P, P], I32),
         "wgn_chain_check": ([P, P], I32),
+        "wgn_chain_set_wait_us": ([P, I64], I32),
         "wgn_chain_num_phases": ([P], I32),
         "wgn_chain_grid": ([P], I32),
         "wgn_chain_ring": ([P], I32),
         "wgn_chain_trace": ([P, P, ctypes.POINTER(ctypes.c_uint64), SZ], I32),
         "wgn_chain_stage_phases": ([P, ctypes.POINTER(I32)], I32),
         "wgn_chain_destroy": ([P], None),
-        "wgn_layer_chain": ([SP, I32, I32, OP, P, SZ, P], I32),
+        "wgn_layer_chain": ([SP, I32, I32, OP, ctypes.POINTER(Plan), P, SZ, P, P], I32),
+        "wgn_workspace_bytes": ([SP, I32, I32, I32], SZ),
         "wgn_chain_run_plan": ([P, ctypes.POINTER(Plan), P, P], I32),
-        "wgn_plan_tune": ([P, P, P, I32, ctypes.POINTER(Plan)], I32),
+        "wgn_chain_plan_tune": ([P, P, P, I32, ctypes.POINTER(Plan)], I32),
+        "wgn_plan_tune": ([SP, I32, I32, ctypes.POINTER(Plan), P, SZ, P, P], I32),
         "wgn_first_wave_of_unit": ([I32, I32, I32], I32),
         "wgn_partition_selftest": ([SP, I32, I32, OP], I32),
         "wgn_plan_phases": ([SP, I32, I32, OP, ctypes.POINTER(I32)], I32),

@@ -29,6 +29,19 @@ def _row_stride(t: torch.Tensor) -> int:
     return t.stride(0)
 
 
+def _need(cond: bool, msg: str) -> None:
+    """Argument check before any call into the library (the C ABI cannot see
+    tensor sizes, so a mismatch would read or write out of bounds)."""
+    if not cond:
+        raise ValueError(msg)
+
+
+def _same_device(*ts: torch.Tensor) -> None:
+    dev = ts[0].device
+    _need(dev.type == "cuda", "tensors must be on the GPU")
+    _need(all(t.device == dev for t in ts), "tensors must be on one device")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -122,12 +135,32 @@ def gemv_int4(x: torch.Tensor, W4: torch.Tensor, scales: torch.Tensor, zeros: to
     x2 = x if x.dim() == 2 else x.view(1, -1)
     y2 = y if y.dim() == 2 else y.view(1, -1)
     B, K = x2.shape
+    _need(W4.dim() == 2 and W4.dtype == torch.uint8 and W4.is_contiguous(), "W4 must be a contiguous uint8 [N][K/2]")
     N = W4.shape[0]
-    assert W4.dtype == torch.uint8 and W4.is_contiguous() and W4.shape[1] * 2 == K
-    assert scales.is_contiguous() and zeros.is_contiguous()
+    _need(W4.shape[1] * 2 == K, "W4 holds %d codes per row, x has K = %d" % (W4.shape[1] * 2, K))
+    _need(K % 128 == 0, "K must be a multiple of 128")
+    for name, t in (("scales", scales), ("zeros", zeros)):
+        _need(t.dtype == torch.bfloat16 and t.is_contiguous() and tuple(t.shape) == (N, K // 128),
+              "%s must be a contiguous BF16 [N][K/128] = [%d][%d], got %s %s" % (name, N, K // 128,
+                                                                         tuple(t.shape), t.dtype))
+    _need(x2.dtype == torch.bfloat16 and y2.dtype == torch.bfloat16, "x and y must be BF16")
+    _need(y2.shape[0] == B and y2.shape[1] >= N, "y must be [batch][>= N]")
+    _same_device(x2, W4, scales, zeros, y2)
     st = L.lib().wgn_gemv_int4(_ptr(x2), _row_stride(x2), B, K, _ptr(W4), _ptr(scales), _ptr(zeros), N, _ptr(y2),
                                _row_stride(y2), _stream(stream))
     L.check(st, "wgn_gemv_int4")
+
+
+def stream_read(src: torch.Tensor, grid: int, threads: int = 256, depth: int = 8,
+                sink: Optional[torch.Tensor] = None, stream=None) -> None:
+    """wgn_stream_read: one plain streaming read of src's bytes (the measured
+    read ceiling); sink is a device int32 tensor the kernel may write."""
+    assert src.is_contiguous()
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=src.device)
+    nbytes = src.numel() * src.element_size()
+    st = L.lib().wgn_stream_read(_ptr(src), nbytes, grid, threads, depth, _ptr(sink), _stream(stream))
+    L.check(st, "wgn_stream_read")
 
 
 def decode_attention_workspace_bytes(batch: int, q_heads: int, kv_heads: int, slots: int,
@@ -140,11 +173,21 @@ def decode_attention(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, 
                      ws: Optional[torch.Tensor] = None, stream=None) -> None:
     """wgn_decode_attention over contiguous device tensors: q/out [B][Hq][D],
     k_new/v_new [B][Hkv][D], caches [B][Hkv][S][D] (all BF16), pos int32 [B]."""
+    _need(q.dim() == 3 and k_cache.dim() == 4, "q must be [B][Hq][D] and k_cache [B][Hkv][S][D]")
     B, Hq, D = q.shape
     _, Hkv, S, _ = k_cache.shape
+    _need(tuple(k_cache.shape) == (B, Hkv, S, D), "k_cache must be [%d][Hkv][S][%d]" % (B, D))
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "v_cache must have k_cache's shape")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(tuple(t.shape) == (B, Hkv, D), "%s must be [%d][%d][%d], got %s" % (name, B, Hkv, D, tuple(t.shape)))
+    _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    _need(tuple(pos.shape) == (B,) and pos.dtype == torch.int32, "pos must be int32 [batch]")
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("out", out)):
+        _need(t.dtype == torch.bfloat16, "%s must be BF16" % name)
     for t in (q, k_new, v_new, k_cache, v_cache, pos, out):
-        assert t.is_contiguous()
-    assert pos.dtype == torch.int32 and out.shape == q.shape
+        _need(t.is_contiguous(), "every tensor must be contiguous")
+    _same_device(q, k_new, v_new, k_cache, v_cache, pos, out)
     if scale is None:
         scale = D ** -0.5
     if ws is None:
@@ -209,14 +252,18 @@ class Chain:
                     "wgn_chain_run_plan")
 
     def tune_plan(self, side, reps: int = 15, stream=None) -> Plan:
-        """wgn_plan_tune: measure prefetch candidates against plain runs."""
+        """wgn_chain_plan_tune: measure prefetch candidates against plain runs."""
         out = Plan()
-        L.check(L.lib().wgn_plan_tune(self._h, _stream(stream), _stream(side), reps, ctypes.byref(out)),
-                "wgn_plan_tune")
+        L.check(L.lib().wgn_chain_plan_tune(self._h, _stream(stream), _stream(side), reps, ctypes.byref(out)),
+                "wgn_chain_plan_tune")
         return out
 
     def check(self, stream=None) -> None:
         L.check(L.lib().wgn_chain_check(self._h, _stream(stream)), "wgn_chain_check")
+
+    def set_wait_us(self, us: int) -> None:
+        """wgn_chain_set_wait_us: bound of the in-kernel waits of later runs (-1 = default)."""
+        L.check(L.lib().wgn_chain_set_wait_us(self._h, int(us)), "wgn_chain_set_wait_us")
 
     @property
     def num_phases(self) -> int:
@@ -258,14 +305,37 @@ class Chain:
 
 
 def layer_chain(stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 0,
-                ws: Optional[torch.Tensor] = None, stream=None, device="cuda", path: int = PATH_AUTO) -> None:
+                ws: Optional[torch.Tensor] = None, stream=None, device="cuda", path: int = PATH_AUTO,
+                plan: Optional[Plan] = None, side=None) -> None:
+    """wgn_layer_chain: plan, run and release a chain in one call (a prefetch
+    plan needs mode 1 and a side stream)."""
     arr = L.stage_array(stages)
     o = _opts(mode, grid, path=path)
     if ws is None:
         ws = workspace(L.lib().wgn_chain_workspace_bytes(arr, len(stages), batch, ctypes.byref(o)), device)
-    st = L.lib().wgn_layer_chain(arr, len(stages), batch, ctypes.byref(o), _ptr(ws), ws.numel(),
-                                 _stream(stream))
+    st = L.lib().wgn_layer_chain(arr, len(stages), batch, ctypes.byref(o),
+                                 ctypes.byref(plan) if plan is not None else None, _ptr(ws), ws.numel(),
+                                 _stream(stream), _stream(side) if side is not None else None)
     L.check(st, "wgn_layer_chain")
+
+
+def workspace_bytes(stages: Sequence[Stage], batch: int, V: int = 0) -> int:
+    """wgn_workspace_bytes: one size serving every call on these stages (and an LM head of V rows)."""
+    arr = L.stage_array(stages)
+    return int(L.lib().wgn_workspace_bytes(arr, len(stages), batch, int(V)))
+
+
+def plan_tune(stages: Sequence[Stage], batch: int, side, ws: Optional[torch.Tensor] = None, stream=None,
+              device="cuda") -> Plan:
+    """wgn_plan_tune: tune a prefetch plan for a stage list (one-launch-per-phase chain)."""
+    arr = L.stage_array(stages)
+    if ws is None:
+        ws = workspace(workspace_bytes(stages, batch), device)
+    out = Plan()
+    st = L.lib().wgn_plan_tune(arr, len(stages), batch, ctypes.byref(out), _ptr(ws), ws.numel(), _stream(stream),
+                               _stream(side))
+    L.check(st, "wgn_plan_tune")
+    return out
 
 
 def partition_selftest(stages: Sequence[Stage], batch: int, grid: int, path: int = PATH_AUTO,

@@ -10,11 +10,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libwgn.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("wgn_kernels.hip", "wgn_attn.hip", "wgn_int4.hip", "wgn_api.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("wgn_kernels.hip", "wgn_attn.hip", "wgn_int4.hip", "wgn_read.hip", "wgn_api.cpp")]
 HEADERS = [os.path.join(CSRC, f) for f in ("wgn_prog.h", "wgn_loader.h", "wgn_attn.h")] + [os.path.join(INCLUDE, "wgn.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # packed FP32 ops stay off: plain float code only
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE,
@@ -39,18 +39,41 @@ def kernel_resources(report: str):
 
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     """Compile libwgn.so.  `defines` (e.g. ["WGN_DEPTH=8"]) override the
-    kernel's tuning constants for experimental builds written to `out`."""
+    kernel's tuning constants for experimental builds written to `out`.
+    Each source is compiled on its own (in parallel), then linked."""
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + ["-o", tmp] + SOURCES
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libwgn.so")
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = "%s.%s.o" % (tmp, os.path.splitext(os.path.basename(src))[0])
+        cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + ["-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        objs.append(obj)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+    report, failed = "", False
+    for p in procs:
+        so, se = p.communicate()
+        report += se
+        if p.returncode != 0:
+            sys.stderr.write(so + se)
+            failed = True
+    try:
+        if failed:
+            raise RuntimeError("hipcc failed building libwgn.so")
+        link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+        if verbose:
+            print(" ".join(link), flush=True)
+        r = subprocess.run(link, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("hipcc failed linking libwgn.so")
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.unlink(o)
     # The streaming kernels must keep everything in registers and LDS: a
     # spill to scratch memory puts global-memory latency on the hot path.
-    res = kernel_resources(r.stderr)
+    res = kernel_resources(report)
     spills = {k: v.get("ScratchSize") for k, v in res.items() if v.get("ScratchSize", 0) > 0}
     if not res or spills:
         os.unlink(tmp)

@@ -28,10 +28,15 @@ size_t gemv_int4_lds_bytes(int32_t batch, int32_t K);
 hipError_t launch_gemv_int4(const uint16_t *x, int64_t xs, int32_t batch, int32_t K, const uint8_t *W4,
                             const uint16_t *sc, const uint16_t *zr, int32_t N, uint16_t *y, int64_t ys,
                             int32_t cus, hipStream_t s);
+hipError_t launch_stream_read(const void *src, uint64_t n16, int32_t grid, int32_t threads, int32_t depth,
+                              uint32_t *sink, hipStream_t s);
 }  // namespace wgn
 
 using namespace wgn;
 
+#ifndef WGN_PRE_B1
+#define WGN_PRE_B1 0
+#endif
 namespace {
 
 thread_local char g_last_hip_error[256] = "";
@@ -779,6 +784,7 @@ bool single_geometry(const wgn_stage &s, int32_t B, int32_t cus, SingleLaunch &L
     L.a.persistent = 0;
     L.a.G = L.G;
     L.a.nb = B;
+    L.a.wait_ticks = WAIT_TICKS;
     L.a.n_argmax = s.epi == EPI_ARGMAX ? 1 : 0;
     return fits;
 }
@@ -1098,7 +1104,7 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     a.rowb = (const int32_t *)(ws + c->L.rowb);
     // precomputed lists from batch 2 up (at batch 1 the kernel builds them
     // while it waits for flags that arrive later anyway)
-    if (c->P.B > 1 || c->P.tile) {
+    if (c->P.B > 1 || c->P.tile || WGN_PRE_B1) {
         a.runimg = ws + c->L.runimg;
         a.phinfo = ws + c->L.phinfo;
     }
@@ -1114,6 +1120,7 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     a.G = c->P.G;
     a.n_argmax = c->P.n_argmax;
     a.nb = c->P.B;
+    a.wait_ticks = WAIT_TICKS;
     a.ist.W = (const uint16_t *)stages[0].W;  // address used by empty (zero-length) loads
     *out = c;
     return WGN_OK;
@@ -1192,7 +1199,8 @@ double t975(int df) {
 }
 }  // namespace
 
-wgn_status wgn_plan_tune(const wgn_chain *c, wgn_stream stream, wgn_stream side, int32_t reps, wgn_plan *out) {
+wgn_status wgn_chain_plan_tune(const wgn_chain *c, wgn_stream stream, wgn_stream side, int32_t reps,
+                               wgn_plan *out) {
     if (!c || !out || reps < 3 || reps > 200) return WGN_E_ARG;
     if (c->mode != 1) return WGN_E_UNSUPPORTED;
     if (!side || side == stream) return WGN_E_ARG;
@@ -1297,6 +1305,13 @@ wgn_status wgn_chain_check(const wgn_chain *c, wgn_stream stream) {
     return WGN_E_TIMEOUT;
 }
 
+wgn_status wgn_chain_set_wait_us(wgn_chain *c, int64_t us) {
+    if (!c) return WGN_E_ARG;
+    if (us > (int64_t)(WAIT_TICKS / 100) * 1000) return WGN_E_ARG;
+    c->a.wait_ticks = us < 0 ? WAIT_TICKS : (uint64_t)us * 100u;  // the real-time clock runs at 100 MHz
+    return WGN_OK;
+}
+
 int32_t wgn_chain_num_phases(const wgn_chain *c) { return c ? (int32_t)c->P.phases.size() : -1; }
 
 int32_t wgn_chain_grid(const wgn_chain *c) { return c ? c->P.G : -1; }
@@ -1324,13 +1339,47 @@ wgn_status wgn_chain_stage_phases(const wgn_chain *c, int32_t *out) {
 void wgn_chain_destroy(wgn_chain *c) { delete c; }
 
 wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t batch, const wgn_chain_opts *opts,
-                           void *workspace, size_t ws_bytes, wgn_stream stream) {
+                           const wgn_plan *plan, void *workspace, size_t ws_bytes, wgn_stream stream,
+                           wgn_stream side) {
+    const bool prefetch = plan && plan->prefetch;
+    if (prefetch && !(opts && opts->mode == 1)) return WGN_E_UNSUPPORTED;  // plans drive per-phase launches
     wgn_chain *c = nullptr;
     wgn_status st = wgn_chain_create(stages, n_stages, batch, opts, workspace, ws_bytes, stream, &c);
     if (st != WGN_OK) return st;
-    st = wgn_chain_run(c, stream);
+    st = prefetch ? wgn_chain_run_plan(c, plan, stream, side) : wgn_chain_run(c, stream);
     wgn_chain_destroy(c);
     return st;
+}
+
+wgn_status wgn_plan_tune(const wgn_stage *stages, int32_t n_stages, int32_t batch, wgn_plan *out, void *workspace,
+                         size_t ws_bytes, wgn_stream stream, wgn_stream side) {
+    if (!out) return WGN_E_ARG;
+    wgn_chain_opts o;
+    std::memset(&o, 0, sizeof o);
+    o.mode = 1;  // the touch pass prefetches the weights of later launches
+    wgn_chain *c = nullptr;
+    wgn_status st = wgn_chain_create(stages, n_stages, batch, &o, workspace, ws_bytes, stream, &c);
+    if (st != WGN_OK) return st;
+    st = wgn_chain_plan_tune(c, stream, side, 15, out);
+    wgn_chain_destroy(c);
+    return st;
+}
+
+size_t wgn_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch, int32_t V) {
+    size_t need = 0;
+    if (n_stages > 0) {
+        wgn_chain_opts o;
+        std::memset(&o, 0, sizeof o);
+        for (int32_t mode = 0; mode <= 1; ++mode) {
+            o.mode = mode;
+            const size_t b = wgn_chain_workspace_bytes(stages, n_stages, batch, &o);
+            if (b == 0) return 0;  // the stages cannot be planned
+            need = std::max(need, b);
+        }
+        for (int32_t i = 0; i < n_stages; ++i) need = std::max(need, wgn_gemv_norm_workspace_bytes(&stages[i], batch));
+    }
+    if (V > 0) need = std::max(need, wgn_lmhead_argmax_workspace_bytes(batch));
+    return need;
 }
 
 int32_t wgn_plan_phases(const wgn_stage *stages, int32_t n_stages, int32_t batch, const wgn_chain_opts *opts,
@@ -1589,7 +1638,7 @@ wgn_status wgn_gemv_int4(const void *x, int64_t x_stride, int32_t batch, int32_t
     if (batch < 1 || batch > 8 || N < 1 || K < 128 || (K % 128)) return WGN_E_ARG;
     if ((batch > 1 && (x_stride < K || y_stride < N)) || x_stride < 0 || y_stride < 0) return WGN_E_ARG;
     if (!a16(x) || !a16(W4) || (x_stride & 7) || !a2(scales) || !a2(zeros) || !a2(y)) return WGN_E_ALIGN;
-    if (gemv_int4_lds_bytes(batch, K) > 65536) return WGN_E_UNSUPPORTED;
+    if (gemv_int4_lds_bytes(batch, K) > 160 * 1024) return WGN_E_UNSUPPORTED;
     {
         const Range ry = rng(y, ((size_t)(batch - 1) * y_stride + N) * 2);
         const Range rin[4] = {rng(x, ((size_t)(batch - 1) * x_stride + K) * 2), rng(W4, (size_t)N * K / 2),
@@ -1603,6 +1652,19 @@ wgn_status wgn_gemv_int4(const void *x, int64_t x_stride, int32_t batch, int32_t
                                          (const uint16_t *)scales, (const uint16_t *)zeros, N, (uint16_t *)y,
                                          batch > 1 ? y_stride : N, d.cus > 0 ? d.cus : 256, (hipStream_t)stream),
                         "gemv_int4 launch");
+    return e == hipSuccess ? WGN_OK : WGN_E_HIP;
+}
+
+wgn_status wgn_stream_read(const void *src, size_t bytes, int32_t grid, int32_t threads, int32_t depth,
+                           uint32_t *sink, wgn_stream stream) {
+    if (!src || !sink || bytes == 0 || (bytes & 15)) return WGN_E_ARG;
+    if (grid < 1 || grid > 65536 || threads < 64 || threads > 1024 || (threads & 63)) return WGN_E_ARG;
+    if (depth != 1 && depth != 2 && depth != 4 && depth != 8 && depth != 16) return WGN_E_ARG;
+    if (!a16(src) || !a4(sink)) return WGN_E_ALIGN;
+    DevInfo d = device_info();
+    if (!d.ok) return WGN_E_DEVICE;
+    hipError_t e = note(launch_stream_read(src, (uint64_t)(bytes >> 4), grid, threads, depth, sink, (hipStream_t)stream),
+                        "stream_read launch");
     return e == hipSuccess ? WGN_OK : WGN_E_HIP;
 }
 

@@ -35,6 +35,7 @@ constexpr int I4_ROWS = WGN_I4_ROWS;         // rows per wave at a time
 constexpr int I4_WAVES = WGN_I4_WAVES;
 constexpr int I4_BLOCKS_PER_CU = WGN_I4_BLOCKS_PER_CU;  // cap of the grid (workgroups stride over row groups)
 constexpr uint32_t I4_MAGIC = 0x43004300u;   // BF16 128.0 in both halves
+constexpr int I4_MAX_LDS = 160 * 1024;       // dynamic LDS of one workgroup on gfx950
 
 __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
 
@@ -160,6 +161,19 @@ __global__ __launch_bounds__(64 * I4_WAVES) void gemv_int4_kernel(const uint16_t
 
 size_t gemv_int4_lds_bytes(int32_t batch, int32_t K) { return (size_t)batch * K * 2 + (size_t)batch * (K / 32) * 4; }
 
+// x and its sums may take the whole 160 KB of a gfx950 workgroup's LDS (the
+// down projection's 8960 inputs at batch 8 need 152 KB); the attribute is set
+// once per batch size before its first launch.
+template <int B>
+static hipError_t allow_full_lds() {
+    static bool done = false;
+    if (done) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute((const void *)gemv_int4_kernel<B>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, I4_MAX_LDS);
+    if (e == hipSuccess) done = true;
+    return e;
+}
+
 hipError_t launch_gemv_int4(const uint16_t *x, int64_t xs, int32_t batch, int32_t K, const uint8_t *W4,
                             const uint16_t *sc, const uint16_t *zr, int32_t N, uint16_t *y, int64_t ys,
                             int32_t cus, hipStream_t s) {
@@ -168,8 +182,13 @@ hipError_t launch_gemv_int4(const uint16_t *x, int64_t xs, int32_t batch, int32_
     const size_t lds = gemv_int4_lds_bytes(batch, K);
     dim3 grid(blocks), block(64 * I4_WAVES);
     switch (batch) {
-#define WGN_I4_CASE(BB) \
-    case BB: hipLaunchKernelGGL(gemv_int4_kernel<BB>, grid, block, lds, s, x, xs, K, W4, sc, zr, N, y, ys); break;
+#define WGN_I4_CASE(BB)                                                                                   \
+    case BB: {                                                                                            \
+        const hipError_t ea = allow_full_lds<BB>();                                                       \
+        if (ea != hipSuccess) return ea;                                                                  \
+        hipLaunchKernelGGL(gemv_int4_kernel<BB>, grid, block, lds, s, x, xs, K, W4, sc, zr, N, y, ys);    \
+        break;                                                                                            \
+    }
     WGN_I4_CASE(1) WGN_I4_CASE(2) WGN_I4_CASE(3) WGN_I4_CASE(4)
     WGN_I4_CASE(5) WGN_I4_CASE(6) WGN_I4_CASE(7) WGN_I4_CASE(8)
 #undef WGN_I4_CASE

@@ -729,6 +729,7 @@ __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_
     S.p1 = a.p1;
     S.done_all = false;
     wg_barrier();  // run lists of the first phases are in LDS
+    if (abort_flag_get()) return;  // an earlier run's wait gave up: nothing runs
     stream_begin_phase(S, a.p0);
     u32x4 d[NS][D];
     BlockMeta m[NS];
@@ -784,6 +785,7 @@ __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_
             }
         }
     }
+    __builtin_amdgcn_s_waitcnt(0);  // no load of this wave is left in flight when it ends
 }
 
 template <int B, bool CHAIN, bool TILE, int R>
@@ -792,12 +794,13 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
     const uint32_t lane = lane_id();
     StreamState S;
     S.desc = lds + LDS_DESC_OFF;
-    S.dmask = desc_bufs(R) - 1;
+    S.dmask = desc_bufs_k(TILE, R) - 1;
     S.g = g;
     S.w = w;
     S.p1 = a.p1;
     S.done_all = false;
     wg_barrier();  // run lists of the first phases are in LDS
+    if (abort_flag_get()) return;  // an earlier run's wait gave up: nothing runs
     stream_begin_phase(S, a.p0);
     u32x4 d[NS][block_loads<TILE, R>()];
     BlockMeta m[NS];
@@ -868,6 +871,7 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
             }
         }
     }
+    __builtin_amdgcn_s_waitcnt(0);  // no load of this wave is left in flight when it ends
 }
 
 // --------------------------------------------------------------- control wave
@@ -1248,7 +1252,7 @@ __device__ __forceinline__ void argmax_shared(const KArgs &a, const RunHdr &h, c
 // precomputed list for chains (asynchronous: memory to LDS), else built here.
 template <bool CHAIN, bool TILE, int R>
 __device__ void build_runs(const KArgs &a, int32_t q, int32_t g, char *desc, uint32_t lane) {
-    char *buf = desc + (q & (desc_bufs(R) - 1)) * RUN_BUF_STRIDE;
+    char *buf = desc + (q & (desc_bufs_k(TILE, R) - 1)) * RUN_BUF_STRIDE;
     if (CHAIN && a.runimg) {
         copy_to_lds<0>((const uint16_t *)(a.runimg + ((size_t)q * a.G + g) * RUN_BUF_STRIDE), buf, RUN_BUF_STRIDE / 16,
                        lane);
@@ -1281,11 +1285,11 @@ __device__ __forceinline__ void ahead_load(const KArgs &a, int32_t q_rl, int32_t
         r.pi = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(lane * 16), 0, 0);
     }
 }
-template <int R>
+template <bool TILE, int R>
 __device__ __forceinline__ void ahead_store(const KArgs &a, int32_t q_rl, int32_t q_pi, char *lds, uint32_t lane,
                                             const AheadRegs &r) {
     if (q_rl < a.p1) {
-        char *buf = lds + LDS_DESC_OFF + (q_rl & (desc_bufs(R) - 1)) * RUN_BUF_STRIDE;
+        char *buf = lds + LDS_DESC_OFF + (q_rl & (desc_bufs_k(TILE, R) - 1)) * RUN_BUF_STRIDE;
         *(u32x4 *)(buf + lane * 16) = r.rl0;
         if ((int32_t)lane + 64 < RL_CHUNKS) *(u32x4 *)(buf + (64 + lane) * 16) = r.rl1;
     }
@@ -1300,7 +1304,10 @@ template <int B, bool CHAIN, bool TILE, int R>
 __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *lds) {
     const uint32_t lane = lane_id();
     char *desc = lds + LDS_DESC_OFF;
-    if (lane == 0) abort_flag_set(0);
+    // A wait of an earlier run that gave up leaves the error word set and the
+    // flags and tickets of that run behind: until wgn_chain_check has cleared
+    // them, every launch exits at once and writes nothing.
+    const uint32_t prior = a.persistent ? __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
     if (a.trace && lane < 12) ((uint64_t *)(lds + LDS_TRACE_OFF))[lane] = 0;
     const uint32_t flag_val =
         a.persistent ? __hip_atomic_load(a.run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
@@ -1318,12 +1325,14 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
     // none of this is on the path between a phase's flags and its x-hat; at
     // batch 1 the flags arrive later than the lists are built here, and the
     // reads would only add latency to the flag stores.
-    constexpr int AH = desc_ahead(R), NBUF = desc_bufs(R);
+    constexpr int AH = desc_ahead(R), NBUF = desc_bufs_k(TILE, R);
     static_assert(NBUF <= path_desc_bufs(TILE), "the planner leaves room for this many run lists");
     for (int32_t q = a.p0; q < a.p1 && q < a.p0 + AH; ++q) build_runs<CHAIN, TILE, R>(a, q, g, desc, lane);
     write_phase_info<CHAIN>(a, a.p0, lds, lane);
+    if (lane == 0) abort_flag_set(prior != 0u ? 1 : 0);
     __builtin_amdgcn_s_waitcnt(0);  // copied lists and tables have landed
     wg_barrier();
+    if (prior != 0u) return;  // the streaming waves see the abort flag after this barrier
     const bool pre = CHAIN && a.runimg && a.phinfo;
     for (int32_t p = a.p0; p < a.p1; ++p) {
         const DevPhase ph = phase_of<CHAIN>(a, p);
@@ -1354,7 +1363,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
                         for (int e = 0; e < 4; ++e) ok &= (i + e >= a.G) || ff[e] == flag_val;
                     }
                     if (__all(ok)) break;
-                    if (wall_clock64() - t0 > WAIT_TICKS) {
+                    if (wall_clock64() - t0 > a.wait_ticks) {
                         timed_out = true;
                         break;
                     }
@@ -1375,7 +1384,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
                                 flag_val)
                             seen |= 1u << k;
                     if (__all((seen & need) == need)) break;
-                    if (wall_clock64() - t0 > WAIT_TICKS) {
+                    if (wall_clock64() - t0 > a.wait_ticks) {
                         timed_out = true;
                         break;
                     }
@@ -1395,6 +1404,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
                     wg_barrier();
                 }
                 wg_barrier();
+                __builtin_amdgcn_s_waitcnt(0);  // the gain copies issued before the wait
                 return;
             }
         }
@@ -1412,7 +1422,15 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
         wg_barrier();  // x-hat ready
         // later phases' run list and tables, read while the streaming waves consume
         AheadRegs ahead;
-        if (pre) ahead_load(a, p + AH, p + 1, g, lane, ahead);
+        if (pre) {
+            ahead_load(a, p + AH, p + 1, g, lane, ahead);
+        } else if constexpr (build_in_window(TILE, R)) {
+            // phase p + AH's run list and phase p + 1's tables, built while
+            // the streaming waves consume (phase p's own list and tables are
+            // not touched: its norm is done and the ring has 8 lists)
+            if (p + AH < a.p1) build_runs<CHAIN, TILE, R>(a, p + AH, g, desc, lane);
+            if (p + 1 < a.p1) write_phase_info<CHAIN>(a, p + 1, lds, lane);
+        }
         wg_barrier();  // partials complete
         trace_point(a, p, g, 3, lane);
         if (a.trace && lane < 6) {
@@ -1449,8 +1467,8 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
         if (epi_barrier<TILE, R>() && EPI_BARRIER == 2) wg_barrier();  // flag issued too
         trace_point(a, p, g, 5, lane);
         if (pre) {
-            ahead_store<R>(a, p + AH, p + 1, lds, lane, ahead);
-        } else {
+            ahead_store<TILE, R>(a, p + AH, p + 1, lds, lane, ahead);
+        } else if constexpr (!build_in_window(TILE, R)) {
             if (p + AH < a.p1) build_runs<CHAIN, TILE, R>(a, p + AH, g, desc, lane);
             if (p + 1 < a.p1) write_phase_info<CHAIN>(a, p + 1, lds, lane);
         }

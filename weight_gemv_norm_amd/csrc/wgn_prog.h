@@ -105,10 +105,21 @@ constexpr int MAX_SLOTS = 5;
 constexpr int desc_bufs(int r) { return ring_slots(r) + 2 <= 4 ? 4 : 8; }
 constexpr int desc_ahead(int r) { return ring_slots(r) + 2; }
 constexpr int MAX_DESC_BUFS = 8;
+#ifndef WGN_BUILD_WIN
+#define WGN_BUILD_WIN 0
+#endif
+// Whether the control wave builds run lists (and the next phase's source
+// table) in LDS while the streaming waves consume a phase, instead of right
+// after the phase's completion flag.  Only where lists are built in place
+// (no precomputed images) on the vector path's ring 0; the list of phase
+// p + desc_ahead is then written during phase p, so its buffer must not be
+// phase p's own: the ring has 8 buffers.
+constexpr bool build_in_window(bool tile, int r) { return WGN_BUILD_WIN != 0 && !tile && r == 0; }
+constexpr int desc_bufs_k(bool tile, int r) { return build_in_window(tile, r) ? MAX_DESC_BUFS : desc_bufs(r); }
 static_assert(desc_bufs(0) <= MAX_DESC_BUFS && desc_bufs(1) <= MAX_DESC_BUFS && desc_bufs(2) <= MAX_DESC_BUFS &&
                   ring_slots(0) <= MAX_SLOTS && ring_slots(1) <= MAX_SLOTS && ring_slots(2) <= MAX_SLOTS,
               "ring tables out of range");
-constexpr uint64_t WAIT_TICKS = 200000000ull;  // 2 s at the 100 MHz real-time clock
+constexpr uint64_t WAIT_TICKS = 200000000ull;  // default wait bound: 2 s at the 100 MHz real-time clock
 
 enum { NORM_NONE = 0, NORM_RMS = 1, NORM_LAYER = 2 };
 enum { EPI_NONE = 0, EPI_GELU_TANH = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3,
@@ -201,6 +212,7 @@ struct KArgs {
     int32_t G;
     int32_t n_argmax;
     int32_t nb;            // batch rows
+    uint64_t wait_ticks;   // bound of every in-kernel wait (100 MHz ticks)
     DevPhase iph;
     DevStage ist;
     DevSource isrc;
