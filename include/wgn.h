@@ -147,6 +147,22 @@ wgn_status wgn_lmhead_argmax(const void *h, int64_t h_stride, int32_t batch, int
                              int32_t *idx_out, float *max_out, float *logits_out,
                              void *workspace, size_t ws_bytes, wgn_stream stream);
 
+/* wgn_lmhead_argmax without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): the argmax ticket and per-workgroup keys
+ * live in a fixed device array of the library (33,024 bytes per GPU, held
+ * until the process ends), and the call allocates nothing.  Results are those
+ * of wgn_lmhead_argmax bit for bit.  A launch needing more than the fixed
+ * array (workgroups x batch rows x 8 bytes + 256; more than 256 compute
+ * units at batch 16) returns WGN_E_WORKSPACE; other errors as
+ * wgn_lmhead_argmax.  Every call on one GPU shares that array: calls that
+ * overlap on one GPU (other streams, other threads) race and must not be
+ * issued.  The first call on a GPU also enqueues one small clearing kernel. */
+wgn_status wgn_lmhead_argmax_static(const void *h, int64_t h_stride, int32_t batch, int32_t K,
+                                    const void *gamma, float eps, const void *W_lm, int32_t V,
+                                    int32_t *idx_out, float *max_out, float *logits_out,
+                                    wgn_stream stream);
+
 /* Standalone RMSNorm over `rows` rows of length K, FP16 or BF16 in and out,
  * FP32 statistics, one rounding ("GPU Kernel Optimization" README, section
  * "Architecture": one program per row).  y may not alias x. */

@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
         "wgn_gemv_norm": ([SP, I32, P, SZ, P], I32),
         "wgn_lmhead_argmax_workspace_bytes": ([I32], SZ),
         "wgn_lmhead_argmax": ([P, I64, I32, I32, P, F32, P, I32, P, P, P, P, SZ, P], I32),
+        "wgn_lmhead_argmax_static": ([P, I64, I32, I32, P, F32, P, I32, P, P, P, P], I32),
         "wgn_rmsnorm_rows": ([P, I64, P, F32, P, I64, I32, I32, I32, P], I32),
         "wgn_gemv_int4": ([P, I64, I32, I32, P, P, P, I32, P, I64, P], I32),
         "wgn_stream_read": ([P, SZ, I32, I32, I32, P, P], I32),

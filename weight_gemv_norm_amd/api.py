@@ -120,6 +120,19 @@ def lmhead_argmax(h: torch.Tensor, gamma: Optional[torch.Tensor], eps: float, W_
     L.check(st, "wgn_lmhead_argmax")
 
 
+def lmhead_argmax_static(h: torch.Tensor, gamma: Optional[torch.Tensor], eps: float, W_lm: torch.Tensor,
+                         idx_out: torch.Tensor, max_out: Optional[torch.Tensor] = None,
+                         logits_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """wgn_lmhead_argmax_static: the LM head + argmax with the library's fixed
+    scratch; allocates nothing (no workspace tensor either)."""
+    h2 = h if h.dim() == 2 else h.view(1, -1)
+    B, K = h2.shape
+    V = W_lm.shape[0]
+    st = L.lib().wgn_lmhead_argmax_static(_ptr(h2), _row_stride(h2), B, K, _ptr(gamma), eps, _ptr(W_lm), V,
+                                          _ptr(idx_out), _ptr(max_out), _ptr(logits_out), _stream(stream))
+    L.check(st, "wgn_lmhead_argmax_static")
+
+
 def rmsnorm_rows(x: torch.Tensor, gamma: torch.Tensor, eps: float, y: torch.Tensor, stream=None) -> None:
     assert x.dim() == 2 and x.dtype in (torch.float16, torch.bfloat16) and y.dtype == x.dtype
     dtype = FP16 if x.dtype == torch.float16 else BF16

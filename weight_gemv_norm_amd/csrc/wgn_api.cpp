@@ -28,6 +28,7 @@ size_t gemv_int4_lds_bytes(int32_t batch, int32_t K);
 hipError_t launch_gemv_int4(const uint16_t *x, int64_t xs, int32_t batch, int32_t K, const uint8_t *W4,
                             const uint16_t *sc, const uint16_t *zr, int32_t N, uint16_t *y, int64_t ys,
                             int32_t cus, hipStream_t s);
+hipError_t scratch_address(void **out, hipStream_t s);
 hipError_t launch_stream_read(const void *src, uint64_t n16, int32_t grid, int32_t threads, int32_t depth,
                               uint32_t *sink, hipStream_t s);
 }  // namespace wgn
@@ -959,6 +960,36 @@ wgn_status wgn_lmhead_argmax(const void *h, int64_t h_stride, int32_t batch, int
     s.logits = logits_out;
     s.maxval = max_out;
     return wgn_gemv_norm(&s, batch, workspace, ws_bytes, stream);
+}
+
+wgn_status wgn_lmhead_argmax_static(const void *h, int64_t h_stride, int32_t batch, int32_t K, const void *gamma,
+                                    float eps, const void *W_lm, int32_t V, int32_t *idx_out, float *max_out,
+                                    float *logits_out, wgn_stream stream) {
+    // every argument check of the workspace form, before the scratch is touched
+    wgn_stage s;
+    std::memset(&s, 0, sizeof s);
+    s.N = V;
+    s.K = K;
+    s.W = W_lm;
+    s.norm = gamma ? NORM_RMS : NORM_NONE;
+    s.eps = eps;
+    s.gamma = gamma;
+    s.epi = EPI_ARGMAX;
+    s.x = h;
+    s.x_stride = h_stride;
+    s.y = idx_out;
+    s.logits = logits_out;
+    s.maxval = max_out;
+    wgn_status st = check_stage(s, batch);
+    if (st != WGN_OK) return st;
+    DevInfo d = device_info();
+    if (!d.ok) return WGN_E_DEVICE;
+    SingleLaunch L;
+    if (!single_geometry(s, batch, d.cus, L)) return WGN_E_UNSUPPORTED;
+    if (L.ws > SCRATCH_BYTES) return WGN_E_WORKSPACE;  // more workgroups x batch rows than the fixed scratch holds
+    void *ws = nullptr;
+    if (note(scratch_address(&ws, (hipStream_t)stream), "fixed scratch address") != hipSuccess) return WGN_E_HIP;
+    return wgn_gemv_norm(&s, batch, ws, SCRATCH_BYTES, stream);
 }
 
 wgn_status wgn_rmsnorm_rows(const void *x, int64_t x_stride, const void *gamma, float eps, void *y,

@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "wgn_loader.h"
 
 namespace wgn {
@@ -1681,6 +1683,50 @@ hipError_t launch_rmsnorm_rows(const uint16_t *x, int64_t xs, const uint16_t *g,
     if (f16) hipLaunchKernelGGL(rmsnorm_rows_kernel<true>, grid, block, 0, s, x, xs, g, eps, y, ys, rows, K);
     else hipLaunchKernelGGL(rmsnorm_rows_kernel<false>, grid, block, 0, s, x, xs, g, eps, y, ys, rows, K);
     return hipGetLastError();
+}
+
+}  // namespace wgn
+
+// ------------------------------------------------ fixed scratch (no allocation)
+// Device memory that the allocation-free LM-head entry point uses in place of
+// a caller's workspace: the argmax ticket (offset 0) and the per-workgroup
+// (value, index) keys (offset 256), SCRATCH_BYTES at most -- 256 workgroups x
+// 16 batch rows x 8 bytes plus the ticket area.  Every GPU the library runs on
+// holds its own copy until the process ends; calls on one GPU share it.
+namespace wgn {
+
+static __device__ __align__(256) char scratch[SCRATCH_BYTES];
+
+// Clears the ticket area (the only part that must start at zero; every call
+// leaves it at zero again).  A kernel, not a memset, so that a caller may
+// capture it into a graph.
+__global__ void scratch_clear_kernel(uint32_t *p, int32_t n) {
+    if ((int32_t)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
+
+hipError_t scratch_address(void **out, hipStream_t s) {
+    constexpr int MAX_DEV = 64;
+    static std::mutex mu;
+    static void *ptr[MAX_DEV];
+    *out = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!ptr[dev]) {
+        // the array's name is a host-side stand-in: its device address on
+        // this GPU comes from the runtime, once, with this device current
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(scratch_clear_kernel, dim3(1), dim3(64), 0, s, (uint32_t *)p, 64);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace wgn

@@ -250,6 +250,10 @@ WGN_HD int32_t units_of(int32_t nrows, int32_t parts, int32_t nch, bool tile) {
 constexpr int FLAG_WORDS = WGN_FLAG_WORDS;
 WGN_HD int32_t flag_row(int32_t G) { return FLAG_WORDS == 1 ? (G + 3) & ~3 : G * FLAG_WORDS; }
 constexpr int MAX_GRID = 2048;
+// Fixed device scratch of the allocation-free LM-head call: the ticket area
+// (256 bytes) and one 8-byte key per (workgroup, batch row) for up to 256
+// workgroups and 16 batch rows.
+constexpr size_t SCRATCH_BYTES = 256 + 256 * 16 * 8;
 
 // Meta word of one streamed unit (wave-uniform):
 //   bits  0..13  x-hat byte offset / 16
