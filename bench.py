@@ -58,7 +58,9 @@ def parse():
                     help="decode-attention workload: cache slots (all valid: the new token takes the last; default 32768); "
                          "decode step with attention: cache slots (default 1024, the new token at slot 960)")
     ap.add_argument("--cold", action="store_true",
-                    help="stream a 512 MB scrub buffer between timed steps (evicts the Infinity Cache)")
+                    help="read a 512 MB scrub buffer between timed steps (evicts the Infinity Cache)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the measured streaming-read ceiling (a 2 GiB plain read, a few configurations)")
     return ap.parse_args()
 
 
@@ -189,7 +191,11 @@ def main():
 
     if chain is not None:
         cfg["ring"] = chain.ring
-    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+    # cold runs: a 512 MB plain read between timed steps (read-only, so it
+    # leaves no dirty lines whose write-back would slow the step) evicts the
+    # 256 MB Infinity Cache and the L2s
+    scrub = torch.ones(256 << 20, dtype=torch.int16, device=dev) if args.cold else None
+    scrub_sink = torch.zeros(1, dtype=torch.int32, device=dev) if args.cold else None
 
     if args.prefetch == "tune":
         if chain is None or args.mode != 1:
@@ -232,7 +238,7 @@ def main():
     t_all0.record(stream)
     for i in range(K):
         if scrub is not None:
-            scrub.add_(1)
+            W.stream_read(scrub, 2048, 256, 1, scrub_sink)
         starts[i].record(stream)
         launch()
         ends[i].record(stream)
@@ -243,12 +249,22 @@ def main():
         chain.check()
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e3  # us
     total_ms = t_all0.elapsed_time(t_all1)
+    # one timing basis for value, ms_per_step and the roofline: the events
+    # around each step on the launch stream (the whole-region time, which also
+    # holds the gaps between launches and, with --cold, the scrubs, is reported
+    # beside them as a cross-check)
     us_step = float(np.mean(per))
     us_med = float(np.median(per))
-    ms_per_step = total_ms / K if scrub is None else us_step / 1e3
+    ci = ci95_mean(per)
+    ms_per_step = us_step / 1e3
     gbs = nbytes / (us_step * 1e-6) / 1e9
-    print("[bench] timed %d steps: mean %.2f us, median %.2f us, min %.2f us, wall %.3f s"
-          % (K, us_step, us_med, float(per.min()), wall1 - wall0), file=sys.stderr, flush=True)
+    print("[bench] timed %d steps: mean %.2f us (95%% CI %.2f-%.2f), median %.2f us, min %.2f us, wall %.3f s"
+          % (K, us_step, ci[0], ci[1], us_med, float(per.min()), wall1 - wall0), file=sys.stderr, flush=True)
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = read_ceiling(W, torch, dev)
+        print("[bench] measured streaming-read ceiling %.1f GB/s (%s)" % (ceiling["gbs"], ceiling["config"]),
+              file=sys.stderr, flush=True)
 
     launches = cfg.get("launches_per_step", 1)
     # several launches per step run back to back on one stream: the average
@@ -259,6 +275,9 @@ def main():
                 "unit": "GB/s", "frac": round(l_gbs / HBM_PEAK_GBS, 4),
                 "traffic": recorded_traffic(wl, B, kernel_name), "launch_us_mean": round(l_mean, 3),
                 "launch_us_median": round(l_med, 3), "bytes_per_launch": nbytes // launches}
+    if ceiling is not None:
+        roofline["measured_read_ceiling"] = round(ceiling["gbs"], 1)
+        roofline["frac_of_measured_ceiling"] = round(l_gbs / ceiling["gbs"], 4)
 
     # ----------------------------------------------------------- CPU oracle
     cpu = None
@@ -278,7 +297,12 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(us_step, 3),
+        "us_per_step_median": round(us_med, 3),
+        "us_per_step_ci95": [round(ci[0], 3), round(ci[1], 3)],
+        "region_ms_per_step": round(total_ms / K, 6),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "pct_of_measured_read_ceiling": round(100.0 * gbs / ceiling["gbs"], 2) if ceiling else None,
+        "measured_read_ceiling": ceiling,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -290,6 +314,70 @@ def main():
         "cold": bool(args.cold),
     }
     print(json.dumps(out), flush=True)
+
+def ci95_mean(x):
+    """95 % confidence interval of the mean of the per-step times (Student t)."""
+    from scipy import stats
+    x = np.asarray(x, dtype=np.float64)
+    n = len(x)
+    if n < 2:
+        return (float(x.mean()), float(x.mean()))
+    h = stats.t.ppf(0.975, n - 1) * x.std(ddof=1) / np.sqrt(n)
+    return (float(x.mean() - h), float(x.mean() + h))
+
+
+# Launch shapes of the plain streaming read tried for the ceiling (grid,
+# threads per workgroup, 16-byte loads in flight per lane): the best of each
+# family measured on this GPU.
+CEILING_CONFIGS = ((256, 256, 8), (256, 512, 4), (512, 256, 4), (2048, 256, 1), (1024, 256, 2))
+
+
+def read_ceiling(W, torch, dev, gib=2, reps=5):
+    """The measured streaming-read ceiling of this GPU: the best over a few
+    launch shapes of wgn_stream_read over a 2 GiB buffer (each shape's median
+    over reps reads), in GB/s."""
+    buf = torch.empty(gib << 29, dtype=torch.int16, device=dev)  # gib GiB
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = buf.numel() * 2
+    best, best_cfg, rows = 0.0, None, []
+    for grid, threads, depth in CEILING_CONFIGS:
+        W.stream_read(buf, grid, threads, depth, sink)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            W.stream_read(buf, grid, threads, depth, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        gbs = nbytes / float(np.median(ts)) / 1e9
+        rows.append([grid, threads, depth, round(gbs, 1)])
+        if gbs > best:
+            best, best_cfg = gbs, (grid, threads, depth)
+    del buf
+    torch.cuda.synchronize()
+    return {"gbs": round(best, 1), "bytes": nbytes,
+            "config": "grid %d, %d threads, %d loads in flight per lane" % best_cfg,
+            "tried": rows, "pct_of_peak": round(100.0 * best / HBM_PEAK_GBS, 2)}
+
+
+def host_cpu():
+    """The host's CPU model and core counts (for the oracle's timing)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
 
 # ------------------------------------------------------------ HBM counters
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -400,7 +488,7 @@ def cpu_baseline_decode(inp, bufs, nbytes, budget_s=12.0, max_steps=45):
     print("[bench] cpu baseline: copying weights to host", file=sys.stderr, flush=True)
     layers = [{k: bb(v) for k, v in L.items()} for L in inp["layers"]]
     g_f, W_lm, h0 = bb(inp["g_f"]), bb(inp["W_lm"]), bb(inp["h"])
-    threads = max(1, min(os.cpu_count() or 1, 16))
+    threads = max(1, min(host_cpu()["usable_cpus"] or 1, 16))
     O.set_threads(threads)
     eps = float(np.float32(inp["eps"]))
 
@@ -424,10 +512,20 @@ def cpu_baseline_decode(inp, bufs, nbytes, budget_s=12.0, max_steps=45):
     dt = (time.perf_counter() - t0) / n
     print("[bench] cpu baseline: %d steps, %.3f s per step on %d threads" % (n, dt, threads),
           file=sys.stderr, flush=True)
+    # the same oracle on one thread: one whole step (its result is bit-identical)
+    O.set_threads(1)
+    t1 = time.perf_counter()
+    one_step()
+    dt1 = time.perf_counter() - t1
+    O.set_threads(threads)
+    print("[bench] cpu baseline: one step on 1 thread %.3f s" % dt1, file=sys.stderr, flush=True)
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "seconds_per_step": round(dt, 4), "us_per_step": round(dt * 1e6, 1),
+            "single_thread_seconds_per_step": round(dt1, 3),
+            "single_thread_value": round(nbytes / dt1 / 1e9, 4), "host": host_cpu(),
             "sample": "%d full decode steps (28 blocks + LM head + argmax, batch 1), free-running in the "
-                      "binary64 C oracle with OpenMP over rows; value = algorithmic bytes / mean step time" % n}
+                      "binary64 C oracle with OpenMP over rows on %d threads (cores = threads used), then one "
+                      "step on 1 thread; value = algorithmic bytes / mean step time" % (n, threads)}
 
 
 def cpu_baseline_attention(att, bytes_per_layer, budget_s=10.0, max_reps=200):
@@ -439,7 +537,7 @@ def cpu_baseline_attention(att, bytes_per_layer, budget_s=10.0, max_reps=200):
     t = att[0]
     a = [bb(t[k]) for k in ("q", "k_new", "v_new", "k_cache", "v_cache")]
     pos = t["pos"].cpu().numpy()
-    threads = max(1, min(os.cpu_count() or 1, 16))
+    threads = max(1, min(host_cpu()["usable_cpus"] or 1, 16))
     O.set_threads(threads)
     t0 = time.perf_counter()
     n = 0
@@ -452,7 +550,7 @@ def cpu_baseline_attention(att, bytes_per_layer, budget_s=10.0, max_reps=200):
     print("[bench] cpu baseline: %d layer calls, %.4f s each on %d threads" % (n, dt, threads),
           file=sys.stderr, flush=True)
     return {"value": round(bytes_per_layer / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seconds_per_layer": round(dt, 5),
+            "seconds_per_layer": round(dt, 5), "host": host_cpu(),
             "sample": "%d calls of one layer's attention (same cache length and batch) in the binary64 C "
                       "oracle with OpenMP over query heads; value = algorithmic bytes per layer / mean call "
                       "time" % n}
