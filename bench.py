@@ -91,7 +91,24 @@ def main():
     nbytes = 0
     cfg = {"workload": wl, "batch": B}
     kernel_name = "chain_kernel"
-    if wl in ("decode_step_1536x28", "decoder_block_1536"):
+    if wl in ("decode_step_1536x28", "decoder_block_1536") and B > 16:
+        # batch 17-128: stage by stage on the matrix cores (tiled products,
+        # RMSNorm passes), one HIP graph per step
+        inp = gen.make_stage_tensors(wl, device=dev, batch=B, n_layers=args.layers, vocab=args.vocab)
+        stages, bufs = steps.decoder_stages(inp, dev)
+        bstep = steps.BatchedStep(stages, B, dev)
+        nb = steps.decode_step_bytes(inp)
+        nbytes = nb["total"]
+        flops = 2 * nb["weights"] // 2 * B
+        cfg.update({"hidden": gen.H, "intermediate": gen.I, "layers": len(inp["layers"]),
+                    "vocab": gen.V if "W_lm" in inp else None, "weight_bytes": nb["weights"],
+                    "algorithmic_bytes": nbytes, "flops": flops, "launches_per_step": bstep.n_launches,
+                    "launch": "stage by stage (one HIP graph)", "path": "matrix (tiled products)"})
+        kernel_name = "gemm_kernel+rmsnorm_rows_kernel"
+        bgraph = bstep.capture()
+        launch = bgraph.replay
+        cfg["graph"] = True
+    elif wl in ("decode_step_1536x28", "decoder_block_1536"):
         inp = gen.make_stage_tensors(wl, device=dev, batch=B, n_layers=args.layers, vocab=args.vocab)
         stages, bufs = steps.decoder_stages(inp, dev)
         chain = W.Chain(stages, B, mode=args.mode, path=args.path)

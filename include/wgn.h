@@ -163,6 +163,35 @@ wgn_status wgn_lmhead_argmax_static(const void *h, int64_t h_stride, int32_t bat
                                     int32_t *idx_out, float *max_out, float *logits_out,
                                     wgn_stream stream);
 
+/* ----------------------------------------- larger batches (matrix cores) */
+/* Workspace bytes wgn_gemm_norm needs for this stage at this batch (0 if the
+ * stage or the batch is outside the call). */
+size_t wgn_gemm_norm_workspace_bytes(const wgn_stage *stage, int32_t batch);
+
+/* One norm-fused product for batch in [1, 128] on the matrix cores: the batch
+ * sweep of "One Token, Kernel by Kernel", section "Batching: when does decode
+ * stop being memory-bound?", where every weight read serves all batch rows.
+ * Same stage semantics and numeric contract as wgn_gemv_norm (FP32
+ * accumulation, epilogue on the FP32 sum, one rounding to BF16; argmax over
+ * FP32 logits, lowest index of the maximum).  Differences:
+ *  - the RMSNorm prologue is a pass of its own that writes x-hat (BF16) into
+ *    the workspace, then the product reads it (the unfused order of the same
+ *    page: norm kernel, then the product);
+ *  - a stage with few 64-row tiles is split over K; the last workgroup of a
+ *    tile adds the slices in slice order, so results are reproducible;
+ *  - a LayerNorm prologue and an argmax with a bias return WGN_E_UNSUPPORTED,
+ *    as does a weight matrix of 2^31 bytes or more;
+ *  - outputs (y, logits, maxval) must not overlap x, residual, the weights or
+ *    each other (WGN_E_ARG).
+ * Workspace: wgn_gemm_norm_workspace_bytes(stage, batch) bytes, 256-byte
+ * aligned, any content: it starts with the call's tickets and argmax keys,
+ * which the call clears first (a fill kernel, so the call can be captured in
+ * a HIP graph), followed by x-hat and the partial sums of a K split.
+ * Asynchronous on `stream`: the clear, the norm pass (if any) and the product
+ * kernel; nothing is enqueued on error. */
+wgn_status wgn_gemm_norm(const wgn_stage *stage, int32_t batch, void *workspace, size_t ws_bytes,
+                         wgn_stream stream);
+
 /* Standalone RMSNorm over `rows` rows of length K, FP16 or BF16 in and out,
  * FP32 statistics, one rounding ("GPU Kernel Optimization" README, section
  * "Architecture": one program per row).  y may not alias x. */
@@ -339,7 +368,11 @@ void wgn_chain_destroy(wgn_chain *chain);
  * (from wgn_plan_tune) needs opts->mode == 1 (WGN_E_UNSUPPORTED otherwise) and
  * runs its touch passes on `side` (see wgn_chain_run_plan); side is ignored
  * without one.  The workspace is sized by wgn_chain_workspace_bytes for the
- * same opts (wgn_workspace_bytes covers every mode). */
+ * same opts (wgn_workspace_bytes covers every mode).
+ * batch in [17, 128]: the stages run one after another through the
+ * wgn_gemm_norm path (a plan must not prefetch, opts must not trace or force
+ * the vector path: WGN_E_UNSUPPORTED); the workspace (wgn_workspace_bytes
+ * at that batch) needs no zero fill, the call clears its counters first. */
 wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t batch,
                            const wgn_chain_opts *opts, const struct wgn_plan *plan, void *workspace,
                            size_t ws_bytes, wgn_stream stream, wgn_stream side);
@@ -347,8 +380,11 @@ wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t ba
 /* One workspace size that serves every call of the library on these stages at
  * this batch: a chain over them in either mode with default options, each
  * stage alone through wgn_gemv_norm, and -- when V > 0 -- wgn_lmhead_argmax
- * over V rows.  0 if the stages cannot be planned (a call on them would
- * return its error). */
+ * over V rows.  At batch 17-128: wgn_layer_chain on the stages, each stage
+ * through wgn_gemm_norm, and -- when V > 0 -- an RMSNorm + argmax stage of V
+ * rows over the last stage's output (its N, rounded up to a multiple of 8)
+ * through wgn_gemm_norm.  0 if the
+ * stages cannot be planned (a call on them would return its error). */
 size_t wgn_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch, int32_t V);
 
 /* -------------------------------------------------------- prefetch plans */

@@ -488,7 +488,16 @@ def test_workspace_bytes_serves_every_call():
         for st in stages:
             assert total >= lib.wgn_gemv_norm_workspace_bytes(ctypes.byref(st), B)
         assert total >= lib.wgn_lmhead_argmax_workspace_bytes(B)
-    assert lib.wgn_workspace_bytes(arr, len(stages), 17, 0) == 0   # batch out of range
+    # batch 17-128: the batched matrix-core path, each stage through wgn_gemm_norm
+    for B in (17, 64, 128):
+        stages = fake_decoder(Arena(), B, 2, V=4096)
+        arr = L.stage_array(stages)
+        total = lib.wgn_workspace_bytes(arr, len(stages), B, 151936)
+        assert total > 0
+        for st in stages:
+            need = lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(st), B)
+            assert 0 < need <= total
+    assert lib.wgn_workspace_bytes(arr, len(stages), 129, 0) == 0   # batch out of range
 
 
 def test_layer_chain_and_plan_tune_check_arguments_before_the_device():
@@ -502,3 +511,76 @@ def test_layer_chain_and_plan_tune_check_arguments_before_the_device():
     assert lib.wgn_layer_chain(arr, len(stages), 1, ctypes.byref(o), ctypes.byref(plan), 0x100000, 1 << 30,
                                None, 0x1234) == L.E_UNSUPPORTED
     assert lib.wgn_plan_tune(arr, len(stages), 1, None, 0x100000, 1 << 30, None, 0x1234) == L.E_ARG
+
+
+def call_gemm(st, b, ws=0x100000, ws_bytes=1 << 34):
+    import ctypes
+    return L.lib().wgn_gemm_norm(ctypes.byref(st), b, ws, ws_bytes, None)
+
+
+def test_gemm_norm_workspace_layout():
+    """Workspace of the batched path: tickets (one per 64-row tile + one),
+    argmax keys, x-hat of a norm prologue, and the partial tiles of a K split
+    (4 waves x accumulator sets x 16-row batch groups x 1 KB per slice and
+    tile)."""
+    import ctypes
+    lib = L.lib()
+    ar = Arena()
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    # down projection at batch 128: 24 tiles split into 8 slices of 1120
+    d = fake_stage(ar, 1536, 8960, 128, L.NORM_NONE, residual=ar.take(128 * 1536 * 2))
+    assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(d), 128) == al(25 * 4) + 24 * 8 * 4 * 8 * 1024
+    # gate/up at batch 32: 140 tiles, 2 slices of 768; two accumulator sets; x-hat 32 x 1536
+    gu = fake_stage(ar, 8960, 1536, 32, L.NORM_RMS, L.EPI_SWIGLU)
+    assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(gu), 32) == \
+        al(141 * 4) + al(32 * 1536 * 2) + 140 * 2 * 4 * 2 * 2 * 1024
+    # LM head at batch 17: 2374 tiles (no split), keys, x-hat (gamma null: unit gain)
+    lm = fake_stage(ar, 151936, 1536, 17, L.NORM_RMS, L.EPI_ARGMAX, gamma=False)
+    assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(lm), 17) == al(2375 * 4) + al(17 * 8) + al(17 * 1536 * 2)
+    # LayerNorm prologue at batch 64: 12 tiles split into 2 slices of 384
+    ln = fake_stage(ar, 768, 768, 64, L.NORM_LAYER, beta=True)
+    assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(ln), 64) == \
+        al(13 * 4) + al(64 * 768 * 2) + 12 * 2 * 4 * 4 * 1024
+
+
+def test_gemm_norm_checks_before_the_device():
+    import ctypes
+    lib = L.lib()
+    ar = Arena()
+    good = fake_stage(ar, 256, 512, 64, L.NORM_RMS)
+    need = lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(good), 64)
+    assert need > 0
+    assert call_gemm(good, 0) == L.E_ARG
+    assert call_gemm(good, 129) == L.E_ARG
+    assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(good), 129) == 0
+    am = fake_stage(ar, 256, 512, 64, L.NORM_RMS, L.EPI_ARGMAX, bias=True)
+    assert call_gemm(am, 64) == L.E_UNSUPPORTED                    # argmax with a bias
+    ov = fake_stage(ar, 256, 512, 64, L.NORM_RMS)
+    ov.y = ov.x                                                     # output over the input
+    assert call_gemm(ov, 64) == L.E_ARG
+    assert call_gemm(good, 64, ws=0) == L.E_WORKSPACE
+    assert call_gemm(good, 64, ws=0x100010) == L.E_WORKSPACE       # not 256-aligned
+    assert call_gemm(good, 64, ws_bytes=need - 1) == L.E_WORKSPACE
+    if L.lib().wgn_device_cu_count() == 0:
+        assert call_gemm(good, 64, ws_bytes=need) == L.E_DEVICE    # every host check passed
+
+
+def test_layer_chain_batched_checks_before_the_device():
+    import ctypes
+    lib = L.lib()
+    stages = fake_decoder(Arena(), 32, 1, V=4096)
+    arr = L.stage_array(stages)
+    need = lib.wgn_workspace_bytes(arr, len(stages), 32, 0)
+    assert need > 0
+    plan = L.Plan()
+    plan.prefetch, plan.distance, plan.blocks, plan.frac_pct = 1, 1, 16, 50
+    o = L.ChainOpts()
+    assert lib.wgn_layer_chain(arr, len(stages), 32, None, ctypes.byref(plan), 0x100000, need, None,
+                               None) == L.E_UNSUPPORTED             # no prefetch plans on this path
+    o.trace = 1
+    assert lib.wgn_layer_chain(arr, len(stages), 32, ctypes.byref(o), None, 0x100000, need, None,
+                               None) == L.E_UNSUPPORTED             # no trace
+    assert lib.wgn_layer_chain(arr, len(stages), 32, None, None, 0x100000, need - 1, None,
+                               None) == L.E_WORKSPACE
+    if L.lib().wgn_device_cu_count() == 0:
+        assert lib.wgn_layer_chain(arr, len(stages), 32, None, None, 0x100000, need, None, None) == L.E_DEVICE

@@ -9,4 +9,5 @@ from .api import (Chain, gemv_norm, gemv_norm_workspace_bytes, layer_chain, lmhe
                   partition_selftest, first_wave_of_unit, workspace, device_cu_count, plan_phases,
                   PATH_AUTO, PATH_VECTOR, PATH_MATRIX, Plan, WgnError, decode_attention,
                   decode_attention_workspace_bytes, gemv_int4, stream_read,
-                  workspace_bytes, plan_tune, lmhead_argmax_static)
+                  workspace_bytes, plan_tune, lmhead_argmax_static, gemm_norm,
+                  gemm_norm_workspace_bytes)

@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         "wgn_device_cu_count": ([], I32),
         "wgn_gemv_norm_workspace_bytes": ([SP, I32], SZ),
         "wgn_gemv_norm": ([SP, I32, P, SZ, P], I32),
+        "wgn_gemm_norm_workspace_bytes": ([SP, I32], SZ),
+        "wgn_gemm_norm": ([SP, I32, P, SZ, P], I32),
         "wgn_lmhead_argmax_workspace_bytes": ([I32], SZ),
         "wgn_lmhead_argmax": ([P, I64, I32, I32, P, F32, P, I32, P, P, P, P, SZ, P], I32),
         "wgn_lmhead_argmax_static": ([P, I64, I32, I32, P, F32, P, I32, P, P, P, P], I32),

@@ -101,6 +101,18 @@ def gemv_norm(stage: Stage, batch: int, ws: Optional[torch.Tensor] = None, strea
     L.check(st, "wgn_gemv_norm")
 
 
+def gemm_norm_workspace_bytes(stage: Stage, batch: int) -> int:
+    return int(L.lib().wgn_gemm_norm_workspace_bytes(ctypes.byref(stage), batch))
+
+
+def gemm_norm(stage: Stage, batch: int, ws: Optional[torch.Tensor] = None, stream=None, device="cuda") -> None:
+    """wgn_gemm_norm: one stage at batch 1-128 on the matrix cores (tiled product; RMSNorm as a pass of its own)."""
+    if ws is None:
+        ws = workspace(gemm_norm_workspace_bytes(stage, batch), device)
+    st = L.lib().wgn_gemm_norm(ctypes.byref(stage), batch, _ptr(ws), ws.numel(), _stream(stream))
+    L.check(st, "wgn_gemm_norm")
+
+
 def lmhead_argmax_workspace_bytes(batch: int) -> int:
     return int(L.lib().wgn_lmhead_argmax_workspace_bytes(batch))
 
@@ -325,7 +337,9 @@ def layer_chain(stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 
     arr = L.stage_array(stages)
     o = _opts(mode, grid, path=path)
     if ws is None:
-        ws = workspace(L.lib().wgn_chain_workspace_bytes(arr, len(stages), batch, ctypes.byref(o)), device)
+        nbytes = (L.lib().wgn_workspace_bytes(arr, len(stages), batch, 0) if batch > 16 else
+                  L.lib().wgn_chain_workspace_bytes(arr, len(stages), batch, ctypes.byref(o)))
+        ws = workspace(nbytes, device)
     st = L.lib().wgn_layer_chain(arr, len(stages), batch, ctypes.byref(o),
                                  ctypes.byref(plan) if plan is not None else None, _ptr(ws), ws.numel(),
                                  _stream(stream), _stream(side) if side is not None else None)

@@ -16,6 +16,7 @@
 
 #include "wgn.h"
 #include "wgn_attn.h"
+#include "wgn_gemm.h"
 #include "wgn_loader.h"
 
 namespace wgn {
@@ -82,8 +83,8 @@ inline bool a4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 
 inline bool a2(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
 inline size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
-wgn_status check_stage(const wgn_stage &s, int32_t batch) {
-    if (batch < 1 || batch > MAX_BATCH) return WGN_E_ARG;
+wgn_status check_stage(const wgn_stage &s, int32_t batch, int32_t max_batch = MAX_BATCH) {
+    if (batch < 1 || batch > max_batch) return WGN_E_ARG;
     if (s.N < 1 || s.K < 8 || (s.K & 7)) return WGN_E_ARG;
     if (s.K > (1 << 24)) return WGN_E_UNSUPPORTED;  // 16 rows x K x 2 bytes must fit 32-bit buffer offsets
     if (!s.W || !s.x || !s.y) return WGN_E_ARG;
@@ -935,6 +936,148 @@ wgn_status wgn_gemv_norm(const wgn_stage *stage, int32_t batch, void *workspace,
     return e == hipSuccess ? WGN_OK : WGN_E_HIP;
 }
 
+// ------------------------------------------------ batched product (wgn_gemm.hip)
+namespace wgn {
+
+struct GemmCall {
+    GemmArgs a;
+    bool swiglu = false;
+    bool norm = false;  // x-hat is written into the workspace first
+    size_t lds = 0, ws = 0;
+    size_t counters = 0;  // bytes of tickets and keys at the start of the workspace
+    size_t off_keys = 0, off_xhat = 0, off_part = 0;
+};
+
+// K slices per row tile at most: the last item of a tile adds them one group
+// of loads at a time, so more slices lengthen the tile's tail.
+constexpr int32_t GEMM_MAX_SLICES = 8;
+
+// Work partition and workspace of one stage at batch B on the batched path:
+// row tiles of 64; a stage with fewer tiles than compute units is split over
+// K (whole 32-wide steps per slice) until about one item per compute unit.
+// False if the stage is outside the path (argmax with a bias, a weight
+// matrix past 32-bit byte offsets).
+// base: bytes reserved for counters at the start of the workspace (at least
+// this call's own); stages that share a workspace use the largest, so no
+// stage's data lies where another keeps its tickets.
+bool gemm_plan(const wgn_stage &s, int32_t B, int32_t cus, GemmCall &C, size_t base = 0) {
+    if (s.epi == EPI_ARGMAX && s.bias) return false;
+    if ((int64_t)s.N * s.K * 2 > 0x7FFFFFF0LL) return false;
+    const int32_t nt = (B + 15) / 16;
+    const int32_t kwin = gemm_kwin(nt);
+    const int32_t ntiles = (s.N + GEMM_TILE_ROWS - 1) / GEMM_TILE_ROWS;
+    int32_t S = 1;
+    if (ntiles < cus)
+        S = std::min(std::min((cus + ntiles - 1) / ntiles, GEMM_MAX_SLICES), (s.K + kwin - 1) / kwin);
+    const int32_t kslice = ((s.K + S - 1) / S + 31) / 32 * 32;
+    S = (s.K + kslice - 1) / kslice;
+    std::memset(&C.a, 0, sizeof C.a);
+    C.swiglu = s.epi == EPI_SWIGLU;
+    C.norm = s.norm != NORM_NONE;
+    size_t o = al256((size_t)(ntiles + 1) * sizeof(uint32_t));
+    if (s.epi == EPI_ARGMAX) {
+        C.off_keys = o;
+        o += al256((size_t)B * sizeof(uint64_t));
+    }
+    o = std::max(o, base);
+    C.counters = o;
+    if (C.norm) {
+        C.off_xhat = o;
+        o += al256((size_t)B * s.K * 2);
+    }
+    if (S > 1) {
+        C.off_part = o;
+        o += (size_t)ntiles * S * 4 * (C.swiglu ? 2 : 1) * nt * GEMM_FRAG_BYTES;
+    }
+    C.ws = o;
+    C.lds = gemm_lds_bytes(nt * 16, kwin);
+    GemmArgs &a = C.a;
+    a.W = (const uint16_t *)s.W;
+    a.W_up = (const uint16_t *)s.W_up;
+    a.x = (const uint16_t *)s.x;
+    a.x_stride = B > 1 ? s.x_stride : s.K;
+    a.bias = (const uint16_t *)s.bias;
+    a.residual = (const uint16_t *)s.residual;
+    a.res_stride = s.residual && B > 1 ? s.res_stride : s.N;
+    a.y = s.y;
+    a.y_stride = B > 1 ? s.y_stride : s.N;
+    a.logits = s.logits;
+    a.maxval = s.maxval;
+    a.N = s.N;
+    a.K = s.K;
+    a.B = B;
+    a.epi = s.epi;
+    a.ntiles = ntiles;
+    a.nslices = S;
+    a.kslice = kslice;
+    a.kwin = kwin;
+    return true;
+}
+
+// Enqueue one planned stage: the counter clear (clear = true), the norm pass
+// (if any), then the product.
+hipError_t gemm_run(const wgn_stage &s, int32_t B, const GemmCall &C0, char *ws, hipStream_t st, bool clear) {
+    if (clear) {
+        hipError_t e = launch_zero_words((uint32_t *)ws, (int32_t)(C0.counters / 4), st);
+        if (e != hipSuccess) return e;
+    }
+    GemmArgs a = C0.a;
+    a.tickets = (uint32_t *)ws;
+    a.keys = C0.off_keys ? (uint64_t *)(ws + C0.off_keys) : nullptr;
+    a.part = C0.off_part ? (float *)(ws + C0.off_part) : nullptr;
+    if (C0.norm) {
+        uint16_t *xh = (uint16_t *)(ws + C0.off_xhat);
+        hipError_t e = launch_norm_rows64((const uint16_t *)s.x, B > 1 ? s.x_stride : s.K, (const uint16_t *)s.gamma,
+                                          (const uint16_t *)s.beta, s.eps, s.norm == NORM_LAYER, xh, B, s.K, st);
+        if (e != hipSuccess) return e;
+        a.x = xh;
+        a.x_stride = s.K;
+    }
+    return launch_gemm(a, C0.swiglu, C0.lds, st);
+}
+
+// Checks of a stage on the batched path that need the plan: outputs must not
+// overlap the stage's inputs (x, residual, weights) or each other.
+bool gemm_outputs_disjoint(const wgn_stage &s, int32_t B) {
+    std::vector<Range> reads, writes, consts;
+    stage_ranges(s, B, reads, writes, consts);
+    for (const Range &w : writes) {
+        for (const Range &r : reads)
+            if (overlap(w, r)) return false;
+        for (const Range &c : consts)
+            if (overlap(w, c)) return false;
+    }
+    for (size_t i = 0; i < writes.size(); ++i)
+        for (size_t k = i + 1; k < writes.size(); ++k)
+            if (overlap(writes[i], writes[k])) return false;
+    return true;
+}
+
+}  // namespace wgn
+
+size_t wgn_gemm_norm_workspace_bytes(const wgn_stage *stage, int32_t batch) {
+    if (!stage || check_stage(*stage, batch, GEMM_MAX_BATCH) != WGN_OK) return 0;
+    GemmCall C;
+    DevInfo d = device_info();
+    if (!gemm_plan(*stage, batch, d.cus > 0 ? d.cus : 256, C)) return 0;
+    return C.ws;
+}
+
+wgn_status wgn_gemm_norm(const wgn_stage *stage, int32_t batch, void *workspace, size_t ws_bytes,
+                         wgn_stream stream) {
+    if (!stage) return WGN_E_ARG;
+    wgn_status st = check_stage(*stage, batch, GEMM_MAX_BATCH);
+    if (st != WGN_OK) return st;
+    if (!gemm_outputs_disjoint(*stage, batch)) return WGN_E_ARG;
+    DevInfo d = device_info();
+    GemmCall C;
+    if (!gemm_plan(*stage, batch, d.cus > 0 ? d.cus : 256, C)) return WGN_E_UNSUPPORTED;
+    if (!workspace || ws_bytes < C.ws || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return WGN_E_WORKSPACE;
+    if (!d.ok) return WGN_E_DEVICE;
+    hipError_t e = note(gemm_run(*stage, batch, C, (char *)workspace, (hipStream_t)stream, true), "gemm_norm launch");
+    return e == hipSuccess ? WGN_OK : WGN_E_HIP;
+}
+
 size_t wgn_lmhead_argmax_workspace_bytes(int32_t batch) {
     if (batch < 1 || batch > MAX_BATCH) return 0;
     DevInfo d = device_info();
@@ -1369,9 +1512,47 @@ wgn_status wgn_chain_stage_phases(const wgn_chain *c, int32_t *out) {
 
 void wgn_chain_destroy(wgn_chain *c) { delete c; }
 
+namespace {
+
+// Batch 17-128: the stages one launch (plus a norm pass) each, in list
+// order, on the batched matrix-core path.  The counters at the start of the
+// workspace are cleared first (it may hold a persistent chain's program).
+wgn_status layer_chain_batched(const wgn_stage *stages, int32_t n_stages, int32_t batch, const wgn_chain_opts *opts,
+                               const wgn_plan *plan, void *workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!stages || n_stages < 1) return WGN_E_ARG;
+    if ((plan && plan->prefetch) || (opts && (opts->trace || opts->path == 1))) return WGN_E_UNSUPPORTED;
+    std::vector<GemmCall> calls((size_t)n_stages);
+    size_t need = 0, counters = 0;
+    DevInfo d = device_info();
+    const int32_t cus = d.cus > 0 ? d.cus : 256;
+    for (int32_t i = 0; i < n_stages; ++i) {
+        wgn_status st = check_stage(stages[i], batch, GEMM_MAX_BATCH);
+        if (st != WGN_OK) return st;
+        if (!gemm_outputs_disjoint(stages[i], batch)) return WGN_E_ARG;
+        if (!gemm_plan(stages[i], batch, cus, calls[(size_t)i])) return WGN_E_UNSUPPORTED;
+        counters = std::max(counters, calls[(size_t)i].counters);
+    }
+    // one counter area for all stages, the data of each after it
+    for (int32_t i = 0; i < n_stages; ++i) {
+        gemm_plan(stages[i], batch, cus, calls[(size_t)i], counters);
+        need = std::max(need, calls[(size_t)i].ws);
+    }
+    if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return WGN_E_WORKSPACE;
+    if (!d.ok) return WGN_E_DEVICE;
+    char *ws = (char *)workspace;
+    hipError_t e = note(launch_zero_words((uint32_t *)ws, (int32_t)(counters / 4), stream), "counter clear");
+    for (int32_t i = 0; i < n_stages && e == hipSuccess; ++i)
+        e = note(gemm_run(stages[i], batch, calls[(size_t)i], ws, stream, false), "batched stage launch");
+    return e == hipSuccess ? WGN_OK : WGN_E_HIP;
+}
+
+}  // namespace
+
 wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t batch, const wgn_chain_opts *opts,
                            const wgn_plan *plan, void *workspace, size_t ws_bytes, wgn_stream stream,
                            wgn_stream side) {
+    if (batch > MAX_BATCH && batch <= GEMM_MAX_BATCH)
+        return layer_chain_batched(stages, n_stages, batch, opts, plan, workspace, ws_bytes, (hipStream_t)stream);
     const bool prefetch = plan && plan->prefetch;
     if (prefetch && !(opts && opts->mode == 1)) return WGN_E_UNSUPPORTED;  // plans drive per-phase launches
     wgn_chain *c = nullptr;
@@ -1398,6 +1579,41 @@ wgn_status wgn_plan_tune(const wgn_stage *stages, int32_t n_stages, int32_t batc
 
 size_t wgn_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch, int32_t V) {
     size_t need = 0;
+    if (batch > MAX_BATCH && batch <= GEMM_MAX_BATCH) {
+        // the batched path: each stage's own need; an LM head of V rows over
+        // the hidden state the stages end with (the last stage's output
+        // width, RMSNorm prologue, argmax)
+        if (!stages || n_stages < 1) return 0;
+        std::vector<wgn_stage> all(stages, stages + n_stages);
+        if (V > 0) {
+            alignas(16) static const uint16_t dummy[8] = {};
+            const int32_t kh = (stages[n_stages - 1].N + 7) / 8 * 8;
+            wgn_stage s;
+            std::memset(&s, 0, sizeof s);
+            s.N = V;
+            s.K = kh;
+            s.W = s.x = s.gamma = dummy;
+            s.norm = NORM_RMS;
+            s.epi = EPI_ARGMAX;
+            s.x_stride = kh;
+            s.y = (void *)dummy;
+            all.push_back(s);
+        }
+        DevInfo d = device_info();
+        const int32_t cus = d.cus > 0 ? d.cus : 256;
+        size_t counters = 0;
+        std::vector<GemmCall> calls(all.size());
+        for (size_t i = 0; i < all.size(); ++i) {
+            if (check_stage(all[i], batch, GEMM_MAX_BATCH) != WGN_OK || !gemm_plan(all[i], batch, cus, calls[i]))
+                return 0;
+            counters = std::max(counters, calls[i].counters);
+        }
+        for (size_t i = 0; i < all.size(); ++i) {
+            gemm_plan(all[i], batch, cus, calls[i], counters);
+            need = std::max(need, calls[i].ws);
+        }
+        return need;
+    }
     if (n_stages > 0) {
         wgn_chain_opts o;
         std::memset(&o, 0, sizeof o);

@@ -1,0 +1,405 @@
+// wgn_gemm.hip -- norm-fused weight products for larger batches (up to 128
+// rows) on the matrix cores.
+//
+// "One Token, Kernel by Kernel: A Decode Step on a Laptop GPU", section
+// "Batching: when does decode stop being memory-bound?", runs the same weight
+// products at growing batch: each weight read then serves every batch row, so
+// the arithmetic per byte grows with the batch until the products turn
+// compute-bound.  At 17 to 128 rows the persistent kernel's layout (every
+// workgroup holds the whole normalised input of a phase in LDS) no longer
+// fits: 128 rows of the down projection's 8960 inputs are 2.3 MB.  Here each
+// call is one launch of a tiled product instead:
+//   * an item is a tile of 64 output rows (16 per wave) over one K slice, for
+//     all batch rows at once (padded to a multiple of 16);
+//   * the input slice goes through LDS in windows (at most 72 KB, each batch
+//     row padded by 16 bytes so the 16 rows read by one instruction fall in
+//     different banks), and each wave streams its 16 weight rows straight into
+//     registers as the A operand of v_mfma_f32_16x16x32_bf16 (FP32
+//     accumulation), one 16 x 16 accumulator tile per 16 batch rows;
+//   * a stage with few row tiles is split over K so that the launch fills the
+//     GPU: each item then stores its accumulators (system-scope stores), and
+//     the last item of a tile to take the tile's ticket adds the slices in
+//     slice order -- a fixed FP32 order, so results do not depend on timing --
+//     and applies the epilogue;
+//   * the epilogue is the one of the vector path: bias, GELU (tanh form) or
+//     SwiGLU on the FP32 sum, residual add, one rounding to BF16; or, for the
+//     LM head, packed (value, index) keys merged by an atomic maximum and
+//     turned into indices by the last tile.
+// The normalisation runs before, as its own pass over the batch rows (x-hat
+// written once in BF16, from binary64 statistics and products), which is what
+// the unfused pipeline of the same page does between its RMSNorm kernel and
+// its matrix-vector kernel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wgn_gemm.h"
+#include "wgn_numerics.h"
+#include "wgn_prog.h"
+
+namespace wgn {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int GEMM_COH = 17;                   // sc0|sc1: data exchanged between workgroups
+constexpr int GEMM_WEIGHT_AUX = 2;             // nt: weights are read once
+constexpr uint32_t GEMM_RSRC_W3 = 0x00020000u; // raw buffer descriptor, range-checked
+constexpr uint32_t GEMM_OUT_OF_RANGE = 0xFFFFFFF0u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t grsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, (int)GEMM_RSRC_W3);
+}
+__device__ __forceinline__ f32x4 mfma(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// Slices whose partial tiles are loaded together when a tile's slices are
+// added (one memory round trip per group).
+template <int NT, bool SWI>
+constexpr int sum_group() { return (SWI ? 2 : 1) * NT <= 4 ? 4 : (SWI ? 2 : 1) * NT <= 8 ? 2 : 1; }
+
+template <int NT, bool SWI>
+__global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmArgs a) {
+    extern __shared__ __align__(16) char lds[];
+    constexpr int P = SWI ? 2 : 1;                 // accumulator sets (gate and up)
+    constexpr int MS = gemm_kwin(NT) / 32;         // K steps per window, at most
+    const int32_t w = (int32_t)(threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t q = lane >> 4, j = lane & 15u;
+    const int32_t S = a.nslices;
+    const int32_t tile = (int32_t)blockIdx.x / S;
+    const int32_t slice = (int32_t)blockIdx.x - tile * S;
+    const int32_t n0 = tile * GEMM_TILE_ROWS;
+    const int32_t k0 = slice * a.kslice;
+    const int32_t k1 = min(a.K, k0 + a.kslice);
+    const int32_t arow = n0 + 16 * w + (int32_t)j;  // weight row of this lane's A fragments
+    const uint32_t rstride = (uint32_t)a.kwin * 2u + GEMM_ROW_PAD;
+    const size_t merge_off = (size_t)NT * 16 * rstride;  // argmax merge area, then the last-item flag
+    int32_t *s_last = (int32_t *)(lds + merge_off + 4 * GEMM_MAX_BATCH * 8);
+    const uint32_t wbytes = (uint32_t)((int64_t)a.N * a.K * 2);
+    const __amdgpu_buffer_rsrc_t rw = grsrc(a.W, wbytes);
+    const __amdgpu_buffer_rsrc_t ru = grsrc(SWI ? a.W_up : a.W, wbytes);
+
+    f32x4 acc[P][NT];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) acc[p][ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int32_t kw = k0; kw < k1; kw += a.kwin) {
+        const int32_t kn = min(a.kwin, k1 - kw);  // a multiple of 8
+        const int32_t nst = (kn + 31) >> 5;       // 32-wide K steps of the window
+        const int32_t cpr = nst * 4;              // 16-byte chunks per window row (zero past kn)
+        // the window's weight fragments first, so they are in flight while x-hat is copied
+        u32x4 wa[P][MS];
+#pragma unroll
+        for (int t = 0; t < MS; ++t) {
+            if (t < nst) {
+                const int32_t k = kw + 32 * t + 8 * (int32_t)q;
+                const uint32_t off = (arow < a.N && k < k1) ? (uint32_t)(((int64_t)arow * a.K + k) * 2)
+                                                            : GEMM_OUT_OF_RANGE;  // reads as zero
+                wa[0][t] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, GEMM_WEIGHT_AUX);
+                if constexpr (SWI) wa[P - 1][t] = __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, GEMM_WEIGHT_AUX);
+            }
+        }
+        __syncthreads();  // every wave is done with the previous window
+        const int32_t nchunks = NT * 16 * cpr;
+        for (int32_t i = (int32_t)threadIdx.x; i < nchunks; i += GEMM_THREADS) {
+            const int32_t b = i / cpr, c = i - b * cpr;
+            const int32_t k = kw + 8 * c;
+            u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+            if (b < a.B && k < k1) v = *(const u32x4 *)(a.x + (int64_t)b * a.x_stride + k);
+            *(u32x4 *)(lds + (uint32_t)b * rstride + (uint32_t)c * 16u) = v;
+        }
+        __syncthreads();
+        // B operand: batch row 16 ct + j at K offset 32 t + 8 q of the window
+        const char *xb = lds + j * rstride + q * 16u;
+#pragma unroll
+        for (int t = 0; t < MS; ++t) {
+            if (t < nst) {
+#pragma unroll
+                for (int ct = 0; ct < NT; ++ct) {
+                    const u32x4 xv = *(const u32x4 *)(xb + (uint32_t)ct * 16u * rstride + (uint32_t)t * 64u);
+#pragma unroll
+                    for (int p = 0; p < P; ++p) acc[p][ct] = mfma(wa[p][t], xv, acc[p][ct]);
+                }
+            }
+        }
+    }
+
+    if (S > 1) {
+        // this item's accumulators, then the tile's ticket
+        const __amdgpu_buffer_rsrc_t rp = grsrc(a.part, 0x7FFFFFF0u);
+        auto frag = [&](int32_t s, int p, int ct) -> uint32_t {  // byte offset of this lane's part of a fragment
+            return (uint32_t)(((((size_t)tile * S + s) * 4 + w) * P * NT + (size_t)p * NT + ct) * GEMM_FRAG_BYTES +
+                              lane * 16u);
+        };
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[p][ct]), rp, frag(slice, p, ct), 0,
+                                                       GEMM_COH);
+        __builtin_amdgcn_s_waitcnt(0);  // the stores have completed: visible at the coherent level
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t old = __hip_atomic_fetch_add(&a.tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int32_t last = old == (uint32_t)(S - 1) ? 1 : 0;
+            if (last) __hip_atomic_store(&a.tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *s_last = last;
+        }
+        __syncthreads();
+        if (*s_last == 0) return;
+        // the last item adds the slices in slice order, its own from registers
+        constexpr int GS = sum_group<NT, SWI>();
+        f32x4 sum[P][NT];
+        for (int32_t s0 = 0; s0 < S; s0 += GS) {
+            f32x4 v[GS][P][NT];
+#pragma unroll
+            for (int g = 0; g < GS; ++g) {
+                const int32_t s = s0 + g;
+                if (s < S && s != slice) {
+#pragma unroll
+                    for (int p = 0; p < P; ++p)
+#pragma unroll
+                        for (int ct = 0; ct < NT; ++ct)
+                            v[g][p][ct] = __builtin_bit_cast(
+                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, frag(s, p, ct), 0, GEMM_COH));
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < GS; ++g) {
+                const int32_t s = s0 + g;
+                if (s < S) {
+#pragma unroll
+                    for (int p = 0; p < P; ++p)
+#pragma unroll
+                        for (int ct = 0; ct < NT; ++ct) {
+                            const f32x4 x = s == slice ? acc[p][ct] : v[g][p][ct];
+                            sum[p][ct] = s == 0 ? x : sum[p][ct] + x;
+                        }
+                }
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) acc[p][ct] = sum[p][ct];
+    }
+
+    // ------------------------------------------------------------ epilogue
+    // lane: rows n0 + 16 w + 4 q + r (r = 0..3) of batch rows 16 ct + j
+    if (a.epi != EPI_ARGMAX) {
+        uint16_t *y = (uint16_t *)a.y;
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            const int32_t b = ct * 16 + (int32_t)j;
+            if (b >= a.B) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int32_t n = n0 + 16 * w + 4 * (int32_t)q + r;
+                if (n >= a.N) continue;
+                const float z = acc[0][ct][r] + (a.bias ? bf2f(a.bias[n]) : 0.0f);
+                float e;
+                if (a.epi == EPI_GELU_TANH) e = gelu_tanh(z);
+                else if (a.epi == EPI_SWIGLU) e = silu(z) * acc[P - 1][ct][r];
+                else e = z;
+                if (a.residual) e += bf2f(a.residual[(int64_t)b * a.res_stride + n]);
+                y[(int64_t)b * a.y_stride + n] = f2bf(e);
+            }
+        }
+        return;
+    }
+    // argmax: the tile's best key per batch row, merged over the tiles by an
+    // atomic maximum; the last tile writes the indices and clears the keys
+    uint64_t *mk = (uint64_t *)(lds + merge_off);
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+        const int32_t b = ct * 16 + (int32_t)j;
+        uint64_t best = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int32_t n = n0 + 16 * w + 4 * (int32_t)q + r;
+            if (n < a.N && b < a.B) {
+                const float z = acc[0][ct][r];
+                if (a.logits) a.logits[(int64_t)b * a.N + n] = z;
+                const uint64_t key = ((uint64_t)orderable(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
+                best = key > best ? key : best;
+            }
+        }
+        uint64_t o = __shfl_xor(best, 16);
+        best = o > best ? o : best;
+        o = __shfl_xor(best, 32);
+        best = o > best ? o : best;
+        if (q == 0) mk[w * GEMM_MAX_BATCH + b] = best;
+    }
+    __syncthreads();
+    if ((int32_t)threadIdx.x < a.B) {
+        const int32_t b = (int32_t)threadIdx.x;
+        uint64_t best = mk[b];
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) best = mk[ww * GEMM_MAX_BATCH + b] > best ? mk[ww * GEMM_MAX_BATCH + b] : best;
+        __hip_atomic_fetch_max(&a.keys[b], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this tile's maxima and logits are done
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old =
+            __hip_atomic_fetch_add(&a.tickets[a.ntiles], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int32_t last = old == (uint32_t)(a.ntiles - 1) ? 1 : 0;
+        if (last) __hip_atomic_store(&a.tickets[a.ntiles], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = last;
+    }
+    __syncthreads();
+    if (*s_last != 0 && (int32_t)threadIdx.x < a.B) {
+        const int32_t b = (int32_t)threadIdx.x;
+        const uint64_t key = __hip_atomic_load(&a.keys[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.keys[b], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ((int32_t *)a.y)[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
+        if (a.maxval) a.maxval[b] = unorderable((uint32_t)(key >> 32));
+    }
+}
+
+// FP64 -> BF16, round to nearest even, in two steps that round once: to FP32
+// with round-to-odd (an inexact result keeps an odd last bit, so it can never
+// sit on a BF16 tie), then FP32 -> BF16 to nearest even (v_cvt_pk_bf16_f32).
+// FP32 carries 16 more bits than BF16, so the result equals rounding the FP64
+// value directly (round-to-odd, Boldo and Melquiond).
+__device__ __forceinline__ uint16_t f64_to_bf16(double d) {
+    const float f = (float)d;
+    uint32_t b = __float_as_uint(f);
+    if ((double)f != d && (b & 1u) == 0u) b += fabs((double)f) < fabs(d) ? 1u : 0xFFFFFFFFu;
+    return f2bf(__uint_as_float(b));
+}
+
+// Sum of one value per thread over the workgroup (FP64): waves, then LDS.
+__device__ __forceinline__ double block_sum(double v, double *red) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    const int32_t w = (int32_t)(threadIdx.x >> 6);
+    if ((threadIdx.x & 63u) == 0u) red[w] = v;
+    __syncthreads();
+    const double t = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();  // red is reused by the next sum
+    return t;
+}
+
+// x-hat of one batch row per workgroup, in binary64 as the norms are defined
+// ("GPU Kernel Optimization" README, section "Architecture": mean square,
+// rsqrt, gain multiply; LayerNorm with its mean and biased variance about the
+// mean), rounded once to BF16: RMSNorm x r g with r = (sum x^2 / K + eps)^-1/2;
+// LayerNorm (x - mu) r g + beta with r = (sum (x - mu)^2 / K + eps)^-1/2.
+// The products and sums are kept separate (no fused multiply-add), so each
+// rounds as written.
+template <bool LAYER>
+__global__ __launch_bounds__(256) void norm_rows64_kernel(const uint16_t *x, int64_t x_stride, const uint16_t *gamma,
+                                                          const uint16_t *beta, double eps, uint16_t *y, int32_t K) {
+#pragma clang fp contract(off)
+    __shared__ double red[4];
+    const uint16_t *xr = x + (int64_t)blockIdx.x * x_stride;
+    uint16_t *yr = y + (int64_t)blockIdx.x * K;
+    const int32_t n8 = K >> 3;
+    double mu = 0.0;
+    if constexpr (LAYER) {
+        double s = 0.0;
+        for (int32_t i = (int32_t)threadIdx.x; i < n8; i += 256) {
+            const u32x4 v = *(const u32x4 *)(xr + (int64_t)i * 8);
+            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s += (double)bf2f(vv[e] & 0xFFFFu) + (double)bf2f(vv[e] >> 16);
+        }
+        mu = block_sum(s, red) / (double)K;
+    }
+    double ss = 0.0;
+    for (int32_t i = (int32_t)threadIdx.x; i < n8; i += 256) {
+        const u32x4 v = *(const u32x4 *)(xr + (int64_t)i * 8);
+        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const double lo = (double)bf2f(vv[e] & 0xFFFFu) - mu, hi = (double)bf2f(vv[e] >> 16) - mu;
+            ss += lo * lo;
+            ss += hi * hi;
+        }
+    }
+    const double r = 1.0 / sqrt(block_sum(ss, red) / (double)K + eps);
+    for (int32_t i = (int32_t)threadIdx.x; i < n8; i += 256) {
+        const u32x4 v = *(const u32x4 *)(xr + (int64_t)i * 8);
+        const u32x4 gv = gamma ? *(const u32x4 *)(gamma + (int64_t)i * 8) : (u32x4){0x3F803F80u, 0x3F803F80u,
+                                                                                     0x3F803F80u, 0x3F803F80u};
+        const u32x4 bv = beta ? *(const u32x4 *)(beta + (int64_t)i * 8) : (u32x4){0u, 0u, 0u, 0u};
+        const uint32_t vv[4] = {v.x, v.y, v.z, v.w}, gg[4] = {gv.x, gv.y, gv.z, gv.w}, bb[4] = {bv.x, bv.y, bv.z, bv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            double t[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const double xv = (double)bf2f((vv[e] >> (16 * h)) & 0xFFFFu);
+                const double g = (double)bf2f((gg[e] >> (16 * h)) & 0xFFFFu);
+                t[h] = LAYER ? (xv - mu) * r * g + (double)bf2f((bb[e] >> (16 * h)) & 0xFFFFu) : xv * r * g;
+            }
+            o[e] = (uint32_t)f64_to_bf16(t[0]) | ((uint32_t)f64_to_bf16(t[1]) << 16);
+        }
+        *(u32x4 *)(yr + (int64_t)i * 8) = (u32x4){o[0], o[1], o[2], o[3]};
+    }
+}
+__global__ void zero_words_kernel(uint32_t *p, int32_t n) {
+    const int32_t i = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) p[i] = 0u;
+}
+
+// The window may take more than the default 64 KB of dynamic LDS; the
+// attribute is set once per kernel before its first launch.
+template <int NT, bool SWI>
+hipError_t launch_nt(const GemmArgs &a, size_t lds, hipStream_t s) {
+    static bool done = false;
+    if (!done) {
+        const hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<NT, SWI>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_cap());
+        if (e != hipSuccess) return e;
+        done = true;
+    }
+    hipLaunchKernelGGL((gemm_kernel<NT, SWI>), dim3(a.ntiles * a.nslices), dim3(GEMM_THREADS), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs &a, bool swiglu, size_t lds, hipStream_t s) {
+    const int32_t nt = (a.B + 15) / 16;
+    if (a.ntiles < 1 || a.nslices < 1 || a.B < 1 || a.B > GEMM_MAX_BATCH || lds > lds_cap() || a.kwin < 32 ||
+        a.kwin > gemm_kwin(nt) || (a.kwin & 31) || (a.kslice & 31) || a.kslice < 32)
+        return hipErrorInvalidValue;  // the kernel's window and slice arithmetic assumes these
+    switch (nt * 2 + (swiglu ? 1 : 0)) {
+#define WGN_GEMM_CASE(NT)                                  \
+    case 2 * NT: return launch_nt<NT, false>(a, lds, s);   \
+    case 2 * NT + 1: return launch_nt<NT, true>(a, lds, s);
+        WGN_GEMM_CASE(1) WGN_GEMM_CASE(2) WGN_GEMM_CASE(3) WGN_GEMM_CASE(4)
+        WGN_GEMM_CASE(5) WGN_GEMM_CASE(6) WGN_GEMM_CASE(7) WGN_GEMM_CASE(8)
+#undef WGN_GEMM_CASE
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_zero_words(uint32_t *p, int32_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_rows64(const uint16_t *x, int64_t x_stride, const uint16_t *gamma, const uint16_t *beta,
+                              float eps, bool layer, uint16_t *y, int32_t rows, int32_t K, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (layer)
+        hipLaunchKernelGGL(norm_rows64_kernel<true>, dim3(rows), dim3(256), 0, s, x, x_stride, gamma, beta,
+                           (double)eps, y, K);
+    else
+        hipLaunchKernelGGL(norm_rows64_kernel<false>, dim3(rows), dim3(256), 0, s, x, x_stride, gamma, beta,
+                           (double)eps, y, K);
+    return hipGetLastError();
+}
+
+}  // namespace wgn

@@ -25,6 +25,7 @@
 #include <mutex>
 
 #include "wgn_loader.h"
+#include "wgn_numerics.h"
 
 namespace wgn {
 
@@ -56,7 +57,6 @@ constexpr int POLL_GAP = WGN_POLL_GAP, POLL_DELAY = WGN_POLL_DELAY;
 constexpr uint32_t RSRC_W3 = 0x00020000u; // buffer descriptor word 3 for raw dword loads
 
 // ------------------------------------------------------------------ numerics
-__device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
 
 // FP64 reciprocal and FP32-rounded reciprocal square root: the hardware's
 // FP64 estimates, each refined by two Newton-Raphson steps (every step
@@ -82,9 +82,6 @@ __device__ __forceinline__ float inv_sqrt_mean(double s, int32_t K, float eps) {
     return rsqrt_f64_to_f32(__builtin_fma(s, recip_f64((double)K), (double)eps));
 }
 
-// FP32 -> BF16, round to nearest even (NaN kept quiet).
-// FP32 -> BF16, round to nearest even (gfx950's v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 // Two values packed as BF16 (lo in the low half), one instruction.
 __device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -254,20 +251,6 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
-__device__ __forceinline__ uint32_t orderable(float f) {
-    uint32_t b = __float_as_uint(f);
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float unorderable(uint32_t o) {
-    uint32_t b = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
-    return __uint_as_float(b);
-}
-
-__device__ __forceinline__ float gelu_tanh(float z) {
-    const float c = 0.7978845608028654f;  // sqrt(2/pi)
-    return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
-}
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // ------------------------------------------------------------- sync helpers
 __device__ __forceinline__ void wg_barrier() {

@@ -168,6 +168,37 @@ class DecodeStepWithAttention:
         return g
 
 
+class BatchedStep:
+    """A stage list at batch 17-128: wgn_layer_chain runs it stage by stage on
+    the matrix cores (each stage a tiled product, RMSNorm as a pass of its
+    own), with one workspace; capture() records a call in a HIP graph (the
+    page's replayed step), so replays cost one host call."""
+
+    def __init__(self, stages, batch: int, device):
+        from .api import workspace, workspace_bytes
+        self.stages, self.batch = list(stages), int(batch)
+        self.ws = workspace(workspace_bytes(self.stages, self.batch), device)
+        norms = sum(1 for st in self.stages if st.norm != 0)
+        self.n_launches = 1 + len(self.stages) + norms  # counter clear, products, norm passes
+
+    def run(self, stream=None) -> None:
+        from .api import layer_chain
+        layer_chain(self.stages, self.batch, ws=self.ws, stream=stream)
+
+    def capture(self) -> "torch.cuda.CUDAGraph":
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.run(stream=s)  # first use of every launch path outside capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            self.run(stream=s)
+        torch.cuda.synchronize()
+        return g
+
+
 def ln_gelu_chain_stages(inp: Dict, device):
     """Stages of the LayerNorm -> Linear -> GELU-tanh chain.  Returns (stages, buffers)."""
     B = inp["batch"]
