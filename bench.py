@@ -42,7 +42,8 @@ def parse():
                     help="decode-step workload: LM-head rows (default 151936)")
     ap.add_argument("--mode", type=int, default=0, help="0 persistent kernel, 1 one launch per phase")
     ap.add_argument("--path", type=int, default=0,
-                    help="0 auto (vector path for batch <= 4, matrix cores above), 1 vector, 2 matrix cores")
+                    help="0 auto (vector path for batch <= 4, matrix cores above), 1 vector, 2 matrix cores, "
+                         "3 stage-by-stage tiled products (the only path above batch 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after warm-up, run one plain device copy of this many MiB (the known-size "
@@ -91,9 +92,9 @@ def main():
     nbytes = 0
     cfg = {"workload": wl, "batch": B}
     kernel_name = "chain_kernel"
-    if wl in ("decode_step_1536x28", "decoder_block_1536") and B > 16:
-        # batch 17-128: stage by stage on the matrix cores (tiled products,
-        # RMSNorm passes), one HIP graph per step
+    if wl in ("decode_step_1536x28", "decoder_block_1536") and (B > 16 or args.path == 3):
+        # batch 17-128 (or --path 3): stage by stage on the matrix cores
+        # (tiled products, norm passes), one HIP graph per step
         inp = gen.make_stage_tensors(wl, device=dev, batch=B, n_layers=args.layers, vocab=args.vocab)
         stages, bufs = steps.decoder_stages(inp, dev)
         bstep = steps.BatchedStep(stages, B, dev)

@@ -297,7 +297,9 @@ typedef struct wgn_chain_opts {
                          /* compute units (all resident at once), and at most 2048     */
     int32_t trace;       /* 1: record per-phase, per-workgroup timestamps (see below)  */
     int32_t path;        /* 0: auto (vector path for batch <= 4, matrix cores above);   */
-                         /* 1: vector path (batch <= 4 only); 2: matrix-core path       */
+                         /* 1: vector path (batch <= 4 only); 2: matrix-core path;     */
+                         /* 3: wgn_layer_chain only: the stage-by-stage tiled products */
+                         /* of wgn_gemm_norm at any batch in [1, 128] (always above 16) */
     int32_t no_fuse;     /* 1: keep every stage whole (no hoisting, see below)          */
     int32_t ring;        /* vector path's block-buffer ring: 0 auto; 1: 2 x 20 units,   */
                          /* burst refills; 2: 5 x 8 units, burst refills; 3: 4 x 10     */
@@ -369,10 +371,12 @@ void wgn_chain_destroy(wgn_chain *chain);
  * runs its touch passes on `side` (see wgn_chain_run_plan); side is ignored
  * without one.  The workspace is sized by wgn_chain_workspace_bytes for the
  * same opts (wgn_workspace_bytes covers every mode).
- * batch in [17, 128]: the stages run one after another through the
- * wgn_gemm_norm path (a plan must not prefetch, opts must not trace or force
- * the vector path: WGN_E_UNSUPPORTED); the workspace (wgn_workspace_bytes
- * at that batch) needs no zero fill, the call clears its counters first. */
+ * batch in [17, 128], or opts->path == 3 at any batch: the stages run in list
+ * order through the wgn_gemm_norm path, consecutive independent stages that
+ * read the same input with the same normalisation (Q, K and V) in one launch
+ * after one norm pass (a plan must not prefetch, opts must not trace or force
+ * the vector path: WGN_E_UNSUPPORTED); the workspace (wgn_workspace_bytes at
+ * that batch) needs no zero fill, the call clears its counters first. */
 wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t batch,
                            const wgn_chain_opts *opts, const struct wgn_plan *plan, void *workspace,
                            size_t ws_bytes, wgn_stream stream, wgn_stream side);
@@ -380,7 +384,8 @@ wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t ba
 /* One workspace size that serves every call of the library on these stages at
  * this batch: a chain over them in either mode with default options, each
  * stage alone through wgn_gemv_norm, and -- when V > 0 -- wgn_lmhead_argmax
- * over V rows.  At batch 17-128: wgn_layer_chain on the stages, each stage
+ * over V rows.  At batch 17-128 (and, at any batch, for opts->path == 3 of
+ * wgn_layer_chain): wgn_layer_chain on the stages, each stage
  * through wgn_gemm_norm, and -- when V > 0 -- an RMSNorm + argmax stage of V
  * rows over the last stage's output (its N, rounded up to a multiple of 8)
  * through wgn_gemm_norm.  0 if the

@@ -219,3 +219,16 @@ def test_gemm_norm_calls_share_a_workspace():
     rb = O.stage(bits(x), bits(Wb), norm=O.NORM_RMS, epi=O.EPI_SWIGLU, eps=EPS32, gamma=bits(g), W_up=bits(Wu))
     assert_close_bf16(bits(ya), ra, "first call")
     assert_close_bf16(bits(yb), rb, "second call")
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_tiled_path_at_small_batch(B):
+    """opts.path = 3 runs the batched path at any batch: the two-block decode
+    step at batch 1 and 8, teacher-forced per stage (Q, K and V in one launch)."""
+    from tests.test_gpu_chain import check_decoder
+    say("layer_chain path 3 decode_step 2 layers V=20000 B=%d" % B)
+    inp = gen.make_stage_tensors("decode_step_1536x28", device=DEV, batch=B, n_layers=2, vocab=20000)
+    stages, bufs = steps.decoder_stages(inp, DEV)
+    W.layer_chain(stages, B, path=W.PATH_TILED)
+    torch.cuda.synchronize()
+    check_decoder(inp, bufs, layers_full={0, 1})

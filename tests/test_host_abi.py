@@ -527,20 +527,20 @@ def test_gemm_norm_workspace_layout():
     lib = L.lib()
     ar = Arena()
     al = lambda v: (v + 255) // 256 * 256  # noqa: E731
-    # down projection at batch 128: 24 tiles split into 8 slices of 1120
+    # down projection at batch 128: 24 tiles split into 8 slices of 1152 (the last 896)
     d = fake_stage(ar, 1536, 8960, 128, L.NORM_NONE, residual=ar.take(128 * 1536 * 2))
     assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(d), 128) == al(25 * 4) + 24 * 8 * 4 * 8 * 1024
-    # gate/up at batch 32: 140 tiles, 2 slices of 768; two accumulator sets; x-hat 32 x 1536
+    # gate/up at batch 32: 140 tiles, 4 slices of 384; two accumulator sets; x-hat 32 x 1536
     gu = fake_stage(ar, 8960, 1536, 32, L.NORM_RMS, L.EPI_SWIGLU)
     assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(gu), 32) == \
-        al(141 * 4) + al(32 * 1536 * 2) + 140 * 2 * 4 * 2 * 2 * 1024
+        al(141 * 4) + al(32 * 1536 * 2) + 140 * 4 * 4 * 2 * 2 * 1024
     # LM head at batch 17: 2374 tiles (no split), keys, x-hat (gamma null: unit gain)
     lm = fake_stage(ar, 151936, 1536, 17, L.NORM_RMS, L.EPI_ARGMAX, gamma=False)
     assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(lm), 17) == al(2375 * 4) + al(17 * 8) + al(17 * 1536 * 2)
-    # LayerNorm prologue at batch 64: 12 tiles split into 2 slices of 384
+    # LayerNorm prologue at batch 64: 12 tiles split into 6 slices of 128
     ln = fake_stage(ar, 768, 768, 64, L.NORM_LAYER, beta=True)
     assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(ln), 64) == \
-        al(13 * 4) + al(64 * 768 * 2) + 12 * 2 * 4 * 4 * 1024
+        al(13 * 4) + al(64 * 768 * 2) + 12 * 6 * 4 * 4 * 1024
 
 
 def test_gemm_norm_checks_before_the_device():

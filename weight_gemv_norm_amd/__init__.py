@@ -7,7 +7,7 @@ the first call does, and raises if the library was not built.
 from .api import (Chain, gemv_norm, gemv_norm_workspace_bytes, layer_chain, lmhead_argmax,  # noqa: F401
                   lmhead_argmax_workspace_bytes, make_stage, rmsnorm_rows, chain_workspace_bytes,
                   partition_selftest, first_wave_of_unit, workspace, device_cu_count, plan_phases,
-                  PATH_AUTO, PATH_VECTOR, PATH_MATRIX, Plan, WgnError, decode_attention,
+                  PATH_AUTO, PATH_VECTOR, PATH_MATRIX, PATH_TILED, Plan, WgnError, decode_attention,
                   decode_attention_workspace_bytes, gemv_int4, stream_read,
                   workspace_bytes, plan_tune, lmhead_argmax_static, gemm_norm,
                   gemm_norm_workspace_bytes)

@@ -222,7 +222,7 @@ def decode_attention(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, 
     L.check(st, "wgn_decode_attention")
 
 
-PATH_AUTO, PATH_VECTOR, PATH_MATRIX = 0, 1, 2
+PATH_AUTO, PATH_VECTOR, PATH_MATRIX, PATH_TILED = 0, 1, 2, 3
 
 
 def _opts(mode: int, grid: int, trace: bool = False, path: int = PATH_AUTO, fuse: bool = True,
@@ -337,7 +337,7 @@ def layer_chain(stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 
     arr = L.stage_array(stages)
     o = _opts(mode, grid, path=path)
     if ws is None:
-        nbytes = (L.lib().wgn_workspace_bytes(arr, len(stages), batch, 0) if batch > 16 else
+        nbytes = (L.lib().wgn_workspace_bytes(arr, len(stages), batch, 0) if (batch > 16 or path == PATH_TILED) else
                   L.lib().wgn_chain_workspace_bytes(arr, len(stages), batch, ctypes.byref(o)))
         ws = workspace(nbytes, device)
     st = L.lib().wgn_layer_chain(arr, len(stages), batch, ctypes.byref(o),

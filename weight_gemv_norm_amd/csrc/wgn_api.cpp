@@ -939,101 +939,145 @@ wgn_status wgn_gemv_norm(const wgn_stage *stage, int32_t batch, void *workspace,
 // ------------------------------------------------ batched product (wgn_gemm.hip)
 namespace wgn {
 
-struct GemmCall {
-    GemmArgs a;
+// One launch of the batched path: stages [first, first + n) of a stage list,
+// which read the same input with the same normalisation.
+struct GemmGroup {
+    GemmLaunch L;
+    int32_t first = 0, n = 0;
     bool swiglu = false;
     bool norm = false;  // x-hat is written into the workspace first
     size_t lds = 0, ws = 0;
     size_t counters = 0;  // bytes of tickets and keys at the start of the workspace
-    size_t off_keys = 0, off_xhat = 0, off_part = 0;
+    size_t off_ticket[GEMM_MAX_GROUP] = {}, off_part[GEMM_MAX_GROUP] = {};
+    size_t off_keys = 0, off_xhat = 0;
 };
 
 // K slices per row tile at most: the last item of a tile adds them one group
 // of loads at a time, so more slices lengthen the tile's tail.
 constexpr int32_t GEMM_MAX_SLICES = 8;
 
-// Work partition and workspace of one stage at batch B on the batched path:
-// row tiles of 64; a stage with fewer tiles than compute units is split over
-// K (whole 32-wide steps per slice) until about one item per compute unit.
-// False if the stage is outside the path (argmax with a bias, a weight
-// matrix past 32-bit byte offsets).
-// base: bytes reserved for counters at the start of the workspace (at least
-// this call's own); stages that share a workspace use the largest, so no
-// stage's data lies where another keeps its tickets.
-bool gemm_plan(const wgn_stage &s, int32_t B, int32_t cus, GemmCall &C, size_t base = 0) {
-    if (s.epi == EPI_ARGMAX && s.bias) return false;
-    if ((int64_t)s.N * s.K * 2 > 0x7FFFFFF0LL) return false;
+// Whether stage b may join a launch whose first stage is a: the same input,
+// length and normalisation, the same epilogue family, no argmax.
+bool same_input(const wgn_stage &a, const wgn_stage &b) {
+    return a.x == b.x && a.x_stride == b.x_stride && a.K == b.K && a.norm == b.norm && a.gamma == b.gamma &&
+           a.beta == b.beta && std::memcmp(&a.eps, &b.eps, sizeof a.eps) == 0 &&
+           (a.epi == EPI_SWIGLU) == (b.epi == EPI_SWIGLU) && a.epi != EPI_ARGMAX && b.epi != EPI_ARGMAX;
+}
+
+// Work partition and workspace of stages st[0..n) as one launch at batch B:
+// row tiles of 64 rows; a launch with fewer tiles than two per compute unit is
+// split over K (whole 128-element windows per slice) toward two items per
+// compute unit, while the partial tiles a split stores stay within a third of
+// the launch's weight bytes (at least 8 MB).  base: bytes kept for counters at
+// the start of the workspace (at least the launch's own); launches that share
+// a workspace use the largest, so no launch's data lies where another keeps
+// its tickets.  False if a stage is outside the path (argmax with a bias, a
+// weight matrix past 32-bit byte offsets).
+bool gemm_plan(const wgn_stage *st, int32_t n, int32_t B, int32_t cus, GemmGroup &G, size_t base = 0) {
+    if (n < 1 || n > GEMM_MAX_GROUP) return false;
     const int32_t nt = (B + 15) / 16;
-    const int32_t kwin = gemm_kwin(nt);
-    const int32_t ntiles = (s.N + GEMM_TILE_ROWS - 1) / GEMM_TILE_ROWS;
+    const int32_t P = st[0].epi == EPI_SWIGLU ? 2 : 1;
+    int64_t tiles = 0, wbytes = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const wgn_stage &s = st[i];
+        if (s.epi == EPI_ARGMAX && s.bias) return false;
+        if ((int64_t)s.N * s.K * 2 > 0x7FFFFFF0LL) return false;
+        tiles += (s.N + GEMM_TILE_ROWS - 1) / GEMM_TILE_ROWS;
+        wbytes += (int64_t)s.N * s.K * 2 * P;
+    }
     int32_t S = 1;
-    if (ntiles < cus)
-        S = std::min(std::min((cus + ntiles - 1) / ntiles, GEMM_MAX_SLICES), (s.K + kwin - 1) / kwin);
-    const int32_t kslice = ((s.K + S - 1) / S + 31) / 32 * 32;
-    S = (s.K + kslice - 1) / kslice;
-    std::memset(&C.a, 0, sizeof C.a);
-    C.swiglu = s.epi == EPI_SWIGLU;
-    C.norm = s.norm != NORM_NONE;
-    size_t o = al256((size_t)(ntiles + 1) * sizeof(uint32_t));
-    if (s.epi == EPI_ARGMAX) {
-        C.off_keys = o;
+    if (tiles < 2 * cus) {  // two workgroups fit one compute unit
+        const int64_t per_slice = tiles * 4 * P * nt * GEMM_FRAG_BYTES;
+        const int64_t cap = std::max<int64_t>(1, std::max<int64_t>(wbytes / 3, 8 << 20) / per_slice);
+        S = (int32_t)std::min<int64_t>(std::min<int64_t>((2 * cus + tiles - 1) / tiles, GEMM_MAX_SLICES), cap);
+    }
+    std::memset(&G.L, 0, sizeof G.L);
+    G.n = n;
+    G.L.n = n;
+    G.swiglu = P == 2;
+    G.norm = st[0].norm != NORM_NONE;
+    size_t o = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        G.off_ticket[i] = o;
+        o += al256((size_t)((st[i].N + GEMM_TILE_ROWS - 1) / GEMM_TILE_ROWS + 1) * sizeof(uint32_t));
+    }
+    if (st[0].epi == EPI_ARGMAX) {
+        G.off_keys = o;
         o += al256((size_t)B * sizeof(uint64_t));
     }
     o = std::max(o, base);
-    C.counters = o;
-    if (C.norm) {
-        C.off_xhat = o;
-        o += al256((size_t)B * s.K * 2);
+    G.counters = o;
+    if (G.norm) {
+        G.off_xhat = o;
+        o += al256((size_t)B * st[0].K * 2);
     }
-    if (S > 1) {
-        C.off_part = o;
-        o += (size_t)ntiles * S * 4 * (C.swiglu ? 2 : 1) * nt * GEMM_FRAG_BYTES;
+    int32_t items = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const wgn_stage &s = st[i];
+        const int32_t ntiles = (s.N + GEMM_TILE_ROWS - 1) / GEMM_TILE_ROWS;
+        const int32_t Si = std::min(S, (s.K + GEMM_KWIN - 1) / GEMM_KWIN);
+        const int32_t kslice = ((s.K + Si - 1) / Si + GEMM_KWIN - 1) / GEMM_KWIN * GEMM_KWIN;
+        const int32_t Sn = (s.K + kslice - 1) / kslice;
+        if (Sn > 1) {
+            G.off_part[i] = o;
+            o += (size_t)ntiles * Sn * 4 * P * nt * GEMM_FRAG_BYTES;
+        }
+        GemmArgs &a = G.L.s[i];
+        a.W = (const uint16_t *)s.W;
+        a.W_up = (const uint16_t *)s.W_up;
+        a.x = (const uint16_t *)s.x;
+        a.x_stride = B > 1 ? s.x_stride : s.K;
+        a.bias = (const uint16_t *)s.bias;
+        a.residual = (const uint16_t *)s.residual;
+        a.res_stride = s.residual && B > 1 ? s.res_stride : s.N;
+        a.y = s.y;
+        a.y_stride = B > 1 ? s.y_stride : s.N;
+        a.logits = s.logits;
+        a.maxval = s.maxval;
+        a.N = s.N;
+        a.K = s.K;
+        a.B = B;
+        a.epi = s.epi;
+        a.ntiles = ntiles;
+        a.nslices = Sn;
+        a.kslice = kslice;
+        G.L.start[i] = items;
+        items += ntiles * Sn;
     }
-    C.ws = o;
-    C.lds = gemm_lds_bytes(nt * 16, kwin);
-    GemmArgs &a = C.a;
-    a.W = (const uint16_t *)s.W;
-    a.W_up = (const uint16_t *)s.W_up;
-    a.x = (const uint16_t *)s.x;
-    a.x_stride = B > 1 ? s.x_stride : s.K;
-    a.bias = (const uint16_t *)s.bias;
-    a.residual = (const uint16_t *)s.residual;
-    a.res_stride = s.residual && B > 1 ? s.res_stride : s.N;
-    a.y = s.y;
-    a.y_stride = B > 1 ? s.y_stride : s.N;
-    a.logits = s.logits;
-    a.maxval = s.maxval;
-    a.N = s.N;
-    a.K = s.K;
-    a.B = B;
-    a.epi = s.epi;
-    a.ntiles = ntiles;
-    a.nslices = S;
-    a.kslice = kslice;
-    a.kwin = kwin;
+    G.L.start[n] = items;
+    G.ws = o;
+    G.lds = gemm_lds_bytes(nt * 16);
     return true;
 }
 
-// Enqueue one planned stage: the counter clear (clear = true), the norm pass
-// (if any), then the product.
-hipError_t gemm_run(const wgn_stage &s, int32_t B, const GemmCall &C0, char *ws, hipStream_t st, bool clear) {
+// Enqueue one planned launch: the counter clear (clear = true), the norm pass
+// (if any, once for all its stages), then the product.
+hipError_t gemm_run(const wgn_stage *st, int32_t B, const GemmGroup &G0, char *ws, hipStream_t stream, bool clear) {
     if (clear) {
-        hipError_t e = launch_zero_words((uint32_t *)ws, (int32_t)(C0.counters / 4), st);
+        hipError_t e = launch_zero_words((uint32_t *)ws, (int32_t)(G0.counters / 4), stream);
         if (e != hipSuccess) return e;
     }
-    GemmArgs a = C0.a;
-    a.tickets = (uint32_t *)ws;
-    a.keys = C0.off_keys ? (uint64_t *)(ws + C0.off_keys) : nullptr;
-    a.part = C0.off_part ? (float *)(ws + C0.off_part) : nullptr;
-    if (C0.norm) {
-        uint16_t *xh = (uint16_t *)(ws + C0.off_xhat);
+    GemmLaunch L = G0.L;
+    const uint16_t *x = nullptr;
+    if (G0.norm) {
+        const wgn_stage &s = st[0];
+        uint16_t *xh = (uint16_t *)(ws + G0.off_xhat);
         hipError_t e = launch_norm_rows64((const uint16_t *)s.x, B > 1 ? s.x_stride : s.K, (const uint16_t *)s.gamma,
-                                          (const uint16_t *)s.beta, s.eps, s.norm == NORM_LAYER, xh, B, s.K, st);
+                                          (const uint16_t *)s.beta, s.eps, s.norm == NORM_LAYER, xh, B, s.K, stream);
         if (e != hipSuccess) return e;
-        a.x = xh;
-        a.x_stride = s.K;
+        x = xh;
     }
-    return launch_gemm(a, C0.swiglu, C0.lds, st);
+    for (int32_t i = 0; i < G0.n; ++i) {
+        GemmArgs &a = L.s[i];
+        a.tickets = (uint32_t *)(ws + G0.off_ticket[i]);
+        a.keys = a.epi == EPI_ARGMAX ? (uint64_t *)(ws + G0.off_keys) : nullptr;
+        a.part = G0.off_part[i] ? (float *)(ws + G0.off_part[i]) : nullptr;
+        if (x) {
+            a.x = x;
+            a.x_stride = a.K;
+        }
+    }
+    return launch_gemm(L, G0.swiglu, G0.lds, stream);
 }
 
 // Checks of a stage on the batched path that need the plan: outputs must not
@@ -1053,14 +1097,72 @@ bool gemm_outputs_disjoint(const wgn_stage &s, int32_t B) {
     return true;
 }
 
+// Whether stages a and b may run in one launch: neither writes what the other
+// reads or writes (they run at the same time).
+bool independent(const wgn_stage &a, const wgn_stage &b, int32_t B) {
+    std::vector<Range> ra, wa, ca, rb, wb, cb;
+    stage_ranges(a, B, ra, wa, ca);
+    stage_ranges(b, B, rb, wb, cb);
+    for (const Range &w : wa) {
+        for (const Range &r : rb)
+            if (overlap(w, r)) return false;
+        for (const Range &w2 : wb)
+            if (overlap(w, w2)) return false;
+        for (const Range &c : cb)
+            if (overlap(w, c)) return false;
+    }
+    for (const Range &w : wb) {
+        for (const Range &r : ra)
+            if (overlap(w, r)) return false;
+        for (const Range &c : ca)
+            if (overlap(w, c)) return false;
+    }
+    return true;
+}
+
+// The launches of a stage list on the batched path, in list order: runs of
+// consecutive stages with the same input, normalisation and epilogue family
+// that are independent of each other (at most GEMM_MAX_GROUP) share a launch
+// and one norm pass.  All launches use one counter area (the largest), so the
+// workspace need is the largest launch's with that base.  False if a stage is
+// outside the path.
+bool plan_batched(const wgn_stage *st, int32_t n, int32_t B, int32_t cus, std::vector<GemmGroup> &groups,
+                  size_t &need, size_t &counters) {
+    groups.clear();
+    counters = 0;
+    for (int32_t i = 0; i < n;) {
+        int32_t j = i + 1;
+        while (j < n && j - i < GEMM_MAX_GROUP && same_input(st[i], st[j])) {
+            bool ok = true;
+            for (int32_t k = i; k < j && ok; ++k) ok = independent(st[k], st[j], B);
+            if (!ok) break;
+            ++j;
+        }
+        GemmGroup G;
+        if (!gemm_plan(st + i, j - i, B, cus, G)) return false;
+        G.first = i;
+        counters = std::max(counters, G.counters);
+        groups.push_back(G);
+        i = j;
+    }
+    need = 0;
+    for (GemmGroup &G : groups) {
+        const int32_t first = G.first;
+        gemm_plan(st + first, G.n, B, cus, G, counters);
+        G.first = first;
+        need = std::max(need, G.ws);
+    }
+    return true;
+}
+
 }  // namespace wgn
 
 size_t wgn_gemm_norm_workspace_bytes(const wgn_stage *stage, int32_t batch) {
     if (!stage || check_stage(*stage, batch, GEMM_MAX_BATCH) != WGN_OK) return 0;
-    GemmCall C;
+    GemmGroup G;
     DevInfo d = device_info();
-    if (!gemm_plan(*stage, batch, d.cus > 0 ? d.cus : 256, C)) return 0;
-    return C.ws;
+    if (!gemm_plan(stage, 1, batch, d.cus > 0 ? d.cus : 256, G)) return 0;
+    return G.ws;
 }
 
 wgn_status wgn_gemm_norm(const wgn_stage *stage, int32_t batch, void *workspace, size_t ws_bytes,
@@ -1070,11 +1172,11 @@ wgn_status wgn_gemm_norm(const wgn_stage *stage, int32_t batch, void *workspace,
     if (st != WGN_OK) return st;
     if (!gemm_outputs_disjoint(*stage, batch)) return WGN_E_ARG;
     DevInfo d = device_info();
-    GemmCall C;
-    if (!gemm_plan(*stage, batch, d.cus > 0 ? d.cus : 256, C)) return WGN_E_UNSUPPORTED;
-    if (!workspace || ws_bytes < C.ws || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return WGN_E_WORKSPACE;
+    GemmGroup G;
+    if (!gemm_plan(stage, 1, batch, d.cus > 0 ? d.cus : 256, G)) return WGN_E_UNSUPPORTED;
+    if (!workspace || ws_bytes < G.ws || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return WGN_E_WORKSPACE;
     if (!d.ok) return WGN_E_DEVICE;
-    hipError_t e = note(gemm_run(*stage, batch, C, (char *)workspace, (hipStream_t)stream, true), "gemm_norm launch");
+    hipError_t e = note(gemm_run(stage, batch, G, (char *)workspace, (hipStream_t)stream, true), "gemm_norm launch");
     return e == hipSuccess ? WGN_OK : WGN_E_HIP;
 }
 
@@ -1521,28 +1623,23 @@ wgn_status layer_chain_batched(const wgn_stage *stages, int32_t n_stages, int32_
                                const wgn_plan *plan, void *workspace, size_t ws_bytes, hipStream_t stream) {
     if (!stages || n_stages < 1) return WGN_E_ARG;
     if ((plan && plan->prefetch) || (opts && (opts->trace || opts->path == 1))) return WGN_E_UNSUPPORTED;
-    std::vector<GemmCall> calls((size_t)n_stages);
-    size_t need = 0, counters = 0;
+    if (opts && (opts->path < 0 || opts->path > 3)) return WGN_E_ARG;
     DevInfo d = device_info();
     const int32_t cus = d.cus > 0 ? d.cus : 256;
     for (int32_t i = 0; i < n_stages; ++i) {
         wgn_status st = check_stage(stages[i], batch, GEMM_MAX_BATCH);
         if (st != WGN_OK) return st;
         if (!gemm_outputs_disjoint(stages[i], batch)) return WGN_E_ARG;
-        if (!gemm_plan(stages[i], batch, cus, calls[(size_t)i])) return WGN_E_UNSUPPORTED;
-        counters = std::max(counters, calls[(size_t)i].counters);
     }
-    // one counter area for all stages, the data of each after it
-    for (int32_t i = 0; i < n_stages; ++i) {
-        gemm_plan(stages[i], batch, cus, calls[(size_t)i], counters);
-        need = std::max(need, calls[(size_t)i].ws);
-    }
+    std::vector<GemmGroup> groups;
+    size_t need = 0, counters = 0;
+    if (!plan_batched(stages, n_stages, batch, cus, groups, need, counters)) return WGN_E_UNSUPPORTED;
     if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return WGN_E_WORKSPACE;
     if (!d.ok) return WGN_E_DEVICE;
     char *ws = (char *)workspace;
     hipError_t e = note(launch_zero_words((uint32_t *)ws, (int32_t)(counters / 4), stream), "counter clear");
-    for (int32_t i = 0; i < n_stages && e == hipSuccess; ++i)
-        e = note(gemm_run(stages[i], batch, calls[(size_t)i], ws, stream, false), "batched stage launch");
+    for (size_t g = 0; g < groups.size() && e == hipSuccess; ++g)
+        e = note(gemm_run(stages + groups[g].first, batch, groups[g], ws, stream, false), "batched launch");
     return e == hipSuccess ? WGN_OK : WGN_E_HIP;
 }
 
@@ -1551,7 +1648,7 @@ wgn_status layer_chain_batched(const wgn_stage *stages, int32_t n_stages, int32_
 wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t batch, const wgn_chain_opts *opts,
                            const wgn_plan *plan, void *workspace, size_t ws_bytes, wgn_stream stream,
                            wgn_stream side) {
-    if (batch > MAX_BATCH && batch <= GEMM_MAX_BATCH)
+    if ((batch > MAX_BATCH && batch <= GEMM_MAX_BATCH) || (opts && opts->path == 3 && batch >= 1))
         return layer_chain_batched(stages, n_stages, batch, opts, plan, workspace, ws_bytes, (hipStream_t)stream);
     const bool prefetch = plan && plan->prefetch;
     if (prefetch && !(opts && opts->mode == 1)) return WGN_E_UNSUPPORTED;  // plans drive per-phase launches
@@ -1577,43 +1674,44 @@ wgn_status wgn_plan_tune(const wgn_stage *stages, int32_t n_stages, int32_t batc
     return st;
 }
 
-size_t wgn_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch, int32_t V) {
-    size_t need = 0;
-    if (batch > MAX_BATCH && batch <= GEMM_MAX_BATCH) {
-        // the batched path: each stage's own need; an LM head of V rows over
-        // the hidden state the stages end with (the last stage's output
-        // width, RMSNorm prologue, argmax)
-        if (!stages || n_stages < 1) return 0;
-        std::vector<wgn_stage> all(stages, stages + n_stages);
-        if (V > 0) {
-            alignas(16) static const uint16_t dummy[8] = {};
-            const int32_t kh = (stages[n_stages - 1].N + 7) / 8 * 8;
-            wgn_stage s;
-            std::memset(&s, 0, sizeof s);
-            s.N = V;
-            s.K = kh;
-            s.W = s.x = s.gamma = dummy;
-            s.norm = NORM_RMS;
-            s.epi = EPI_ARGMAX;
-            s.x_stride = kh;
-            s.y = (void *)dummy;
-            all.push_back(s);
-        }
-        DevInfo d = device_info();
-        const int32_t cus = d.cus > 0 ? d.cus : 256;
-        size_t counters = 0;
-        std::vector<GemmCall> calls(all.size());
-        for (size_t i = 0; i < all.size(); ++i) {
-            if (check_stage(all[i], batch, GEMM_MAX_BATCH) != WGN_OK || !gemm_plan(all[i], batch, cus, calls[i]))
-                return 0;
-            counters = std::max(counters, calls[i].counters);
-        }
-        for (size_t i = 0; i < all.size(); ++i) {
-            gemm_plan(all[i], batch, cus, calls[i], counters);
-            need = std::max(need, calls[i].ws);
-        }
-        return need;
+namespace {
+
+// Workspace of the batched path for the stages (and an LM head of V rows over
+// the hidden state the stages end with: the last stage's output width, RMSNorm
+// prologue, argmax); false if a stage is outside the path.
+bool batched_need(const wgn_stage *stages, int32_t n_stages, int32_t batch, int32_t V, size_t &need) {
+    need = 0;
+    if (!stages || n_stages < 1 || batch < 1 || batch > GEMM_MAX_BATCH) return false;
+    std::vector<wgn_stage> all(stages, stages + n_stages);
+    if (V > 0) {
+        alignas(16) static const uint16_t dummy[8] = {};
+        const int32_t kh = (stages[n_stages - 1].N + 7) / 8 * 8;
+        wgn_stage s;
+        std::memset(&s, 0, sizeof s);
+        s.N = V;
+        s.K = kh;
+        s.W = s.x = s.gamma = dummy;
+        s.norm = NORM_RMS;
+        s.epi = EPI_ARGMAX;
+        s.x_stride = kh;
+        s.y = (void *)dummy;
+        all.push_back(s);
     }
+    for (const wgn_stage &s : all)
+        if (check_stage(s, batch, GEMM_MAX_BATCH) != WGN_OK) return false;
+    DevInfo d = device_info();
+    std::vector<GemmGroup> groups;
+    size_t counters = 0;
+    return plan_batched(all.data(), (int32_t)all.size(), batch, d.cus > 0 ? d.cus : 256, groups, need, counters);
+}
+
+}  // namespace
+
+size_t wgn_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch, int32_t V) {
+    size_t batched = 0;
+    const bool batched_ok = batched_need(stages, n_stages, batch, V, batched);
+    if (batch > MAX_BATCH) return batched_ok ? batched : 0;
+    size_t need = 0;
     if (n_stages > 0) {
         wgn_chain_opts o;
         std::memset(&o, 0, sizeof o);
@@ -1626,6 +1724,7 @@ size_t wgn_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t ba
         for (int32_t i = 0; i < n_stages; ++i) need = std::max(need, wgn_gemv_norm_workspace_bytes(&stages[i], batch));
     }
     if (V > 0) need = std::max(need, wgn_lmhead_argmax_workspace_bytes(batch));
+    if (batched_ok) need = std::max(need, batched);  // wgn_layer_chain with opts->path == 3
     return need;
 }
 

@@ -11,11 +11,13 @@
 // call is one launch of a tiled product instead:
 //   * an item is a tile of 64 output rows (16 per wave) over one K slice, for
 //     all batch rows at once (padded to a multiple of 16);
-//   * the input slice goes through LDS in windows (at most 72 KB, each batch
+//   * the input slice goes through LDS in windows of 128 elements (each batch
 //     row padded by 16 bytes so the 16 rows read by one instruction fall in
-//     different banks), and each wave streams its 16 weight rows straight into
-//     registers as the A operand of v_mfma_f32_16x16x32_bf16 (FP32
-//     accumulation), one 16 x 16 accumulator tile per 16 batch rows;
+//     different banks), double-buffered: the next window's copy and weight
+//     loads are in flight while the current one is multiplied.  Each wave
+//     streams its 16 weight rows straight into registers as the A operand of
+//     v_mfma_f32_16x16x32_bf16 (FP32 accumulation), one 16 x 16 accumulator
+//     tile per 16 batch rows;
 //   * a stage with few row tiles is split over K so that the launch fills the
 //     GPU: each item then stores its accumulators (system-scope stores), and
 //     the last item of a tile to take the tile's ticket adds the slices in
@@ -62,26 +64,38 @@ template <int NT, bool SWI>
 constexpr int sum_group() { return (SWI ? 2 : 1) * NT <= 4 ? 4 : (SWI ? 2 : 1) * NT <= 8 ? 2 : 1; }
 
 template <int NT, bool SWI>
-__global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmLaunch G) {
     extern __shared__ __align__(16) char lds[];
-    constexpr int P = SWI ? 2 : 1;                 // accumulator sets (gate and up)
-    constexpr int MS = gemm_kwin(NT) / 32;         // K steps per window, at most
+    // this workgroup's stage and item within it
+    int32_t si = 0;
+#pragma unroll
+    for (int k = 1; k < GEMM_MAX_GROUP; ++k) si += (k < G.n && (int32_t)blockIdx.x >= G.start[k]) ? 1 : 0;
+    const GemmArgs &a = G.s[si];
+    const int32_t item = (int32_t)blockIdx.x - G.start[si];
+    constexpr int P = SWI ? 2 : 1;                           // accumulator sets (gate and up)
+    constexpr int MS = GEMM_KWIN / 32;                       // K steps per window
+    constexpr uint32_t RSTRIDE = GEMM_KWIN * 2 + GEMM_ROW_PAD;  // window row stride (bytes)
+    constexpr uint32_t BUFB = NT * 16 * RSTRIDE;             // one window
     const int32_t w = (int32_t)(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t q = lane >> 4, j = lane & 15u;
     const int32_t S = a.nslices;
-    const int32_t tile = (int32_t)blockIdx.x / S;
-    const int32_t slice = (int32_t)blockIdx.x - tile * S;
+    const int32_t tile = item / S;
+    const int32_t slice = item - tile * S;
     const int32_t n0 = tile * GEMM_TILE_ROWS;
     const int32_t k0 = slice * a.kslice;
     const int32_t k1 = min(a.K, k0 + a.kslice);
+    const int32_t nwin = (k1 - k0 + GEMM_KWIN - 1) / GEMM_KWIN;
     const int32_t arow = n0 + 16 * w + (int32_t)j;  // weight row of this lane's A fragments
-    const uint32_t rstride = (uint32_t)a.kwin * 2u + GEMM_ROW_PAD;
-    const size_t merge_off = (size_t)NT * 16 * rstride;  // argmax merge area, then the last-item flag
+    char *buf0 = lds, *buf1 = lds + BUFB;
+    const size_t merge_off = 2 * (size_t)BUFB;       // argmax merge area, then the last-item flag
     int32_t *s_last = (int32_t *)(lds + merge_off + 4 * GEMM_MAX_BATCH * 8);
     const uint32_t wbytes = (uint32_t)((int64_t)a.N * a.K * 2);
     const __amdgpu_buffer_rsrc_t rw = grsrc(a.W, wbytes);
     const __amdgpu_buffer_rsrc_t ru = grsrc(SWI ? a.W_up : a.W, wbytes);
+    // this thread's share of a window's x-hat copy: 16-byte chunk xc of batch
+    // rows xr0, xr0 + 16, ... (one row per 16 threads)
+    const int32_t xr0 = (int32_t)(threadIdx.x >> 4), xc = (int32_t)(threadIdx.x & 15u);
 
     f32x4 acc[P][NT];
 #pragma unroll
@@ -89,45 +103,75 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) acc[p][ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int32_t kw = k0; kw < k1; kw += a.kwin) {
-        const int32_t kn = min(a.kwin, k1 - kw);  // a multiple of 8
-        const int32_t nst = (kn + 31) >> 5;       // 32-wide K steps of the window
-        const int32_t cpr = nst * 4;              // 16-byte chunks per window row (zero past kn)
-        // the window's weight fragments first, so they are in flight while x-hat is copied
-        u32x4 wa[P][MS];
+    // weight fragments of the window at kw: row arow, K offset kw + 32 t + 8 q
+    auto load_w = [&](int32_t kw, u32x4 (&wa)[P][MS]) {
 #pragma unroll
         for (int t = 0; t < MS; ++t) {
-            if (t < nst) {
-                const int32_t k = kw + 32 * t + 8 * (int32_t)q;
-                const uint32_t off = (arow < a.N && k < k1) ? (uint32_t)(((int64_t)arow * a.K + k) * 2)
-                                                            : GEMM_OUT_OF_RANGE;  // reads as zero
-                wa[0][t] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, GEMM_WEIGHT_AUX);
-                if constexpr (SWI) wa[P - 1][t] = __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, GEMM_WEIGHT_AUX);
+            const int32_t k = kw + 32 * t + 8 * (int32_t)q;
+            const uint32_t off = (arow < a.N && k < k1) ? (uint32_t)(((int64_t)arow * a.K + k) * 2)
+                                                        : GEMM_OUT_OF_RANGE;  // reads as zero
+            wa[0][t] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, GEMM_WEIGHT_AUX);
+            if constexpr (SWI) wa[P - 1][t] = __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, GEMM_WEIGHT_AUX);
+        }
+    };
+    // this thread's x-hat chunks of the window at kw (zero past the slice or the batch)
+    auto load_x = [&](int32_t kw, u32x4 (&xv)[NT]) {
+        const int32_t k = kw + 8 * xc;
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            const int32_t b = xr0 + 16 * c;
+            xv[c] = (b < a.B && k < k1) ? *(const u32x4 *)(a.x + (int64_t)b * a.x_stride + k)
+                                        : (u32x4){0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_x = [&](char *buf, const u32x4 (&xv)[NT]) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+            *(u32x4 *)(buf + (uint32_t)(xr0 + 16 * c) * RSTRIDE + (uint32_t)xc * 16u) = xv[c];
+    };
+    // the window's products: B operand = batch row 16 ct + j at K offset 32 t + 8 q
+    auto compute = [&](const char *buf, const u32x4 (&wa)[P][MS]) {
+        const char *xb = buf + j * RSTRIDE + q * 16u;
+#pragma unroll
+        for (int t = 0; t < MS; ++t)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) {
+                const u32x4 xv = *(const u32x4 *)(xb + (uint32_t)ct * 16u * RSTRIDE + (uint32_t)t * 64u);
+#pragma unroll
+                for (int p = 0; p < P; ++p) acc[p][ct] = mfma(wa[p][t], xv, acc[p][ct]);
             }
+    };
+
+    // Two-stage pipeline over the slice's windows: while window i is
+    // multiplied from one LDS buffer, window i + 1's weights are in flight to
+    // registers and its x-hat to the other buffer.  Windows alternate between
+    // the two register sets and buffers (unrolled by two, so that no register
+    // array is indexed at run time).
+    u32x4 wa0[P][MS], wa1[P][MS], xv[NT];
+    if (nwin > 0) {
+        load_w(k0, wa0);
+        load_x(k0, xv);
+        store_x(buf0, xv);
+    }
+    __syncthreads();
+    for (int32_t i = 0; i < nwin; i += 2) {
+        const bool more1 = i + 1 < nwin;
+        if (more1) {
+            load_w(k0 + (i + 1) * GEMM_KWIN, wa1);
+            load_x(k0 + (i + 1) * GEMM_KWIN, xv);
         }
-        __syncthreads();  // every wave is done with the previous window
-        const int32_t nchunks = NT * 16 * cpr;
-        for (int32_t i = (int32_t)threadIdx.x; i < nchunks; i += GEMM_THREADS) {
-            const int32_t b = i / cpr, c = i - b * cpr;
-            const int32_t k = kw + 8 * c;
-            u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-            if (b < a.B && k < k1) v = *(const u32x4 *)(a.x + (int64_t)b * a.x_stride + k);
-            *(u32x4 *)(lds + (uint32_t)b * rstride + (uint32_t)c * 16u) = v;
+        compute(buf0, wa0);
+        if (more1) store_x(buf1, xv);
+        __syncthreads();  // window i + 1 is in buf1; every wave is done with buf0
+        if (!more1) break;
+        const bool more2 = i + 2 < nwin;
+        if (more2) {
+            load_w(k0 + (i + 2) * GEMM_KWIN, wa0);
+            load_x(k0 + (i + 2) * GEMM_KWIN, xv);
         }
+        compute(buf1, wa1);
+        if (more2) store_x(buf0, xv);
         __syncthreads();
-        // B operand: batch row 16 ct + j at K offset 32 t + 8 q of the window
-        const char *xb = lds + j * rstride + q * 16u;
-#pragma unroll
-        for (int t = 0; t < MS; ++t) {
-            if (t < nst) {
-#pragma unroll
-                for (int ct = 0; ct < NT; ++ct) {
-                    const u32x4 xv = *(const u32x4 *)(xb + (uint32_t)ct * 16u * rstride + (uint32_t)t * 64u);
-#pragma unroll
-                    for (int p = 0; p < P; ++p) acc[p][ct] = mfma(wa[p][t], xv, acc[p][ct]);
-                }
-            }
-        }
     }
 
     if (S > 1) {
@@ -354,7 +398,7 @@ __global__ void zero_words_kernel(uint32_t *p, int32_t n) {
 // The window may take more than the default 64 KB of dynamic LDS; the
 // attribute is set once per kernel before its first launch.
 template <int NT, bool SWI>
-hipError_t launch_nt(const GemmArgs &a, size_t lds, hipStream_t s) {
+hipError_t launch_nt(const GemmLaunch &G, size_t lds, hipStream_t s) {
     static bool done = false;
     if (!done) {
         const hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<NT, SWI>,
@@ -362,21 +406,27 @@ hipError_t launch_nt(const GemmArgs &a, size_t lds, hipStream_t s) {
         if (e != hipSuccess) return e;
         done = true;
     }
-    hipLaunchKernelGGL((gemm_kernel<NT, SWI>), dim3(a.ntiles * a.nslices), dim3(GEMM_THREADS), lds, s, a);
+    hipLaunchKernelGGL((gemm_kernel<NT, SWI>), dim3(G.start[G.n]), dim3(GEMM_THREADS), lds, s, G);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs &a, bool swiglu, size_t lds, hipStream_t s) {
-    const int32_t nt = (a.B + 15) / 16;
-    if (a.ntiles < 1 || a.nslices < 1 || a.B < 1 || a.B > GEMM_MAX_BATCH || lds > lds_cap() || a.kwin < 32 ||
-        a.kwin > gemm_kwin(nt) || (a.kwin & 31) || (a.kslice & 31) || a.kslice < 32)
-        return hipErrorInvalidValue;  // the kernel's window and slice arithmetic assumes these
+hipError_t launch_gemm(const GemmLaunch &G, bool swiglu, size_t lds, hipStream_t s) {
+    if (G.n < 1 || G.n > GEMM_MAX_GROUP || G.start[0] != 0 || lds > lds_cap()) return hipErrorInvalidValue;
+    const int32_t nt = (G.s[0].B + 15) / 16;
+    for (int i = 0; i < G.n; ++i) {
+        const GemmArgs &a = G.s[i];
+        // the kernel's window and slice arithmetic assumes these
+        if (a.ntiles < 1 || a.nslices < 1 || a.B < 1 || a.B > GEMM_MAX_BATCH || (a.B + 15) / 16 != nt ||
+            a.kslice < GEMM_KWIN || (a.kslice % GEMM_KWIN) || (int64_t)a.kslice * (a.nslices - 1) >= a.K ||
+            G.start[i + 1] - G.start[i] != a.ntiles * a.nslices)
+            return hipErrorInvalidValue;
+    }
     switch (nt * 2 + (swiglu ? 1 : 0)) {
 #define WGN_GEMM_CASE(NT)                                  \
-    case 2 * NT: return launch_nt<NT, false>(a, lds, s);   \
-    case 2 * NT + 1: return launch_nt<NT, true>(a, lds, s);
+    case 2 * NT: return launch_nt<NT, false>(G, lds, s);   \
+    case 2 * NT + 1: return launch_nt<NT, true>(G, lds, s);
         WGN_GEMM_CASE(1) WGN_GEMM_CASE(2) WGN_GEMM_CASE(3) WGN_GEMM_CASE(4)
         WGN_GEMM_CASE(5) WGN_GEMM_CASE(6) WGN_GEMM_CASE(7) WGN_GEMM_CASE(8)
 #undef WGN_GEMM_CASE

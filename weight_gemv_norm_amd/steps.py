@@ -169,7 +169,7 @@ class DecodeStepWithAttention:
 
 
 class BatchedStep:
-    """A stage list at batch 17-128: wgn_layer_chain runs it stage by stage on
+    """A stage list at batch 1-128 (path 3; the only one above 16): wgn_layer_chain runs it stage by stage on
     the matrix cores (each stage a tiled product, RMSNorm as a pass of its
     own), with one workspace; capture() records a call in a HIP graph (the
     page's replayed step), so replays cost one host call."""
@@ -182,8 +182,8 @@ class BatchedStep:
         self.n_launches = 1 + len(self.stages) + norms  # counter clear, products, norm passes
 
     def run(self, stream=None) -> None:
-        from .api import layer_chain
-        layer_chain(self.stages, self.batch, ws=self.ws, stream=stream)
+        from .api import layer_chain, PATH_TILED
+        layer_chain(self.stages, self.batch, ws=self.ws, stream=stream, path=PATH_TILED)
 
     def capture(self) -> "torch.cuda.CUDAGraph":
         s = torch.cuda.Stream()
