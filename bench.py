@@ -69,7 +69,7 @@ def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, workload=args.workload, batch=args.batch or 1,
-                      copy_mib=args.calib_copy_mib)
+                      copy_mib=args.calib_copy_mib, path=args.path)
         return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the weight stream runs on a single "
@@ -105,7 +105,7 @@ def main():
                     "vocab": gen.V if "W_lm" in inp else None, "weight_bytes": nb["weights"],
                     "algorithmic_bytes": nbytes, "flops": flops, "launches_per_step": bstep.n_launches,
                     "launch": "stage by stage (one HIP graph)", "path": "matrix (tiled products)"})
-        kernel_name = "gemm_kernel+rmsnorm_rows_kernel"
+        kernel_name = "gemm_kernel"  # with its norm passes and counter clear: one step's launches
         bgraph = bstep.capture()
         launch = bgraph.replay
         cfg["graph"] = True
@@ -284,9 +284,10 @@ def main():
         print("[bench] measured streaming-read ceiling %.1f GB/s (%s)" % (ceiling["gbs"], ceiling["config"]),
               file=sys.stderr, flush=True)
 
-    launches = cfg.get("launches_per_step", 1)
     # several launches per step run back to back on one stream: the average
-    # launch is the step time over the launches
+    # launch is the step time over the launches (the batched path's roofline
+    # unit is the whole step: its traffic is recorded per step)
+    launches = 1 if kernel_name == "gemm_kernel" else cfg.get("launches_per_step", 1)
     l_mean, l_med = us_step / launches, us_med / launches
     l_gbs = nbytes / launches / (l_mean * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": kernel_name, "achieved": round(l_gbs, 1), "peak": HBM_PEAK_GBS,
@@ -404,13 +405,16 @@ CSRC = os.path.join(ROOT, "weight_gemv_norm_amd", "csrc")
 
 # The sources each kernel's recorded traffic depends on (its code and its host planner).
 KERNEL_SOURCES = {
-    "chain_kernel": ("wgn_api.cpp", "wgn_kernels.hip", "wgn_loader.h", "wgn_prog.h"),
+    "chain_kernel": ("wgn_api.cpp", "wgn_kernels.hip", "wgn_loader.h", "wgn_prog.h", "wgn_numerics.h"),
+    "gemm_kernel": ("wgn_api.cpp", "wgn_gemm.hip", "wgn_gemm.h", "wgn_numerics.h", "wgn_prog.h"),
     "decode_attention_kernel": ("wgn_attn.h", "wgn_attn.hip"),
     "gemv_int4_kernel": ("wgn_int4.hip",),
 }
 
 
-def kernel_of(workload: str) -> str:
+def kernel_of(workload: str, batch: int = 1, path: int = 0) -> str:
+    if workload in ("decode_step_1536x28", "decoder_block_1536") and (batch > 16 or path == 3):
+        return "gemm_kernel"
     return {"decode_attention_12q2kv128": "decode_attention_kernel",
             "gemv_int4_lmhead_151936": "gemv_int4_kernel"}.get(workload, "chain_kernel")
 
@@ -453,35 +457,48 @@ def _pmc_rows(path, counter):
     return rows
 
 
-def summarize_pmc(fetch_csv, write_csv, out_txt, workload, batch, copy_mib):
+def summarize_pmc(fetch_csv, write_csv, out_txt, workload, batch, copy_mib, path=0):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the workload's kernel, scaled
-    by what the same counters read for a plain copy of copy_mib MiB."""
+    by what the same counters read for a plain copy of copy_mib MiB.  The
+    batched path runs several launches per step (one counter clear, norm
+    passes, products): its figure is per step, the sum over the run's launches
+    divided by its counter clears."""
     assert copy_mib > 0, "--calib-copy-mib of the profiled run is needed"
-    kernel = kernel_of(workload)
+    kernel = kernel_of(workload, batch, path)
     out = {}
-    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
-        rows = _pmc_rows(path, counter)
+    for counter, csv_path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _pmc_rows(csv_path, counter)
         # per dispatch, the counter summed over its instances
         per = {}
         for name, d, v in rows:
             per.setdefault((name, d), 0.0)
             per[(name, d)] += v
-        kern = [v for (n, d), v in per.items() if kernel in n]
         copies = [v for (n, d), v in per.items() if "copyBuffer" in n or "copy_kernel" in n]
+        if kernel == "gemm_kernel":
+            steps = sum(1 for (n, d) in per if "zero_words_kernel" in n)
+            tot = sum(v for (n, d), v in per.items()
+                      if "gemm_kernel" in n or "norm_rows64_kernel" in n or "zero_words_kernel" in n)
+            kern = [tot / max(steps, 1)] if steps else []
+            nk = steps
+        else:
+            kern = [v for (n, d), v in per.items() if kernel in n]
+            nk = len(kern)
         assert kern and copies, (counter, len(kern), len(copies))
         copy_kib = max(copies)  # the calibration copy is the largest copy of the run
         scale = (copy_mib * 1024.0) / copy_kib
-        out[counter] = (float(np.median(kern)), copy_kib, scale, len(kern))
+        out[counter] = (float(np.median(kern)), copy_kib, scale, nk)
     fetch = out["FETCH_SIZE"][0] * out["FETCH_SIZE"][2] * 1024
     write = out["WRITE_SIZE"][0] * out["WRITE_SIZE"][2] * 1024
+    unit = "step (all launches)" if kernel == "gemm_kernel" else "dispatch"
     with open(out_txt, "w") as f:
-        f.write("# HBM traffic of %s, %s, batch %d (rocprofv3 --pmc, one counter per run)\n"
-                % (kernel, workload, batch))
+        f.write("# HBM traffic of %s, %s, batch %d (rocprofv3 --pmc, one counter per run), per %s\n"
+                % (kernel, workload, batch, unit))
         f.write("# commands (from the repository root):\n")
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             f.write("#   rocprofv3 --pmc %s --output-format csv -d gpurun_out/pmc_%s -o run -- python bench.py "
-                    "--workload %s --batch %d --steps 10 --warmup 3 --no-cpu-baseline --calib-copy-mib %d\n"
-                    % (c, c.lower(), workload, batch, copy_mib))
+                    "--workload %s --batch %d%s --steps 10 --warmup 3 --no-cpu-baseline --no-ceiling "
+                    "--calib-copy-mib %d\n"
+                    % (c, c.lower(), workload, batch, " --path 3" if path == 3 else "", copy_mib))
         f.write("# calibration: a plain device copy of %d MiB reads and writes %d KiB\n"
                 % (copy_mib, copy_mib * 1024))
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
