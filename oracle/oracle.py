@@ -10,9 +10,10 @@ BF16 and FP16 tensors are passed as ``uint16`` bit patterns.
 
 Every function below follows the definition stated in ``wgn_oracle.c``'s header,
 which cites the page passage each step comes from.  Parity status: the norm,
-product, epilogue, argmax, decode-attention and 4-bit product definitions are pinned by the ``-m "not gpu"``
-tests in ``tests/test_oracle_pins.py``, ``tests/test_oracle_attention.py`` and ``tests/test_oracle_int4.py`` (closed forms, invariants and exact
-rational brute force); the values for random inputs are "parity unpinned"
+product, epilogue, argmax, decode-attention, 4-bit product and block-backward definitions are pinned by the ``-m "not gpu"``
+tests in ``tests/test_oracle_pins.py``, ``tests/test_oracle_attention.py``, ``tests/test_oracle_int4.py`` and
+``tests/test_oracle_backward.py`` (closed forms, invariants, exact rational brute force, FP64 autograd
+and finite differences); the values for random inputs are "parity unpinned"
 beyond the oracle itself, because the pages print no worked numeric example.
 """
 from __future__ import annotations
@@ -93,6 +94,13 @@ def _load():
         lib.wgo_decode_attention.restype = None
         lib.wgo_matvec_int4.argtypes = [P, P, P, I64, I64, P, I64, I64, P, P]
         lib.wgo_matvec_int4.restype = None
+        lib.wgo_gelu_tanh_grad.argtypes = [D]
+        lib.wgo_gelu_tanh_grad.restype = D
+        lib.wgo_mean_square_grad.argtypes = [P, I64, I64, I64, P, I64]
+        lib.wgo_mean_square_grad.restype = None
+        lib.wgo_block_backward.argtypes = [I64, I64, I64, P, I64, P, P, D, P, P, P, I64, I,
+                                           P, P, P, P, P, P]
+        lib.wgo_block_backward.restype = None
         _lib = lib
         return lib
 
@@ -286,3 +294,75 @@ def matvec_int4(W4, scales, zeros, x, want_acc=False):
     acc = np.empty((B, N), dtype=np.float64) if want_acc else None
     _load().wgo_matvec_int4(_ptr(W4), _ptr(sc), _ptr(zr), N, K, _ptr(x), K, B, _ptr(y), _ptr(acc))
     return (y, acc) if want_acc else y
+
+
+# ------------------------------------------------------------------ backward
+def gelu_tanh_grad(z: float) -> float:
+    return _load().wgo_gelu_tanh_grad(float(z))
+
+
+def mean_square_grad(y):
+    """Gradient of mean(y^2) over a [B][N] BF16 output: R(2 y / (B N)), uint16 bits."""
+    y = _u16(np.atleast_2d(y))
+    B, N = y.shape
+    g = np.empty((B, N), dtype=np.uint16)
+    _load().wgo_mean_square_grad(_ptr(y), N, N, B, _ptr(g), N)
+    return g
+
+
+def block_backward(x, W, gy, *, gamma=None, beta=None, eps=1e-5, bias=None, rnd=True):
+    """Backward of one LayerNorm -> Linear(+bias) -> GELU-tanh block.
+
+    x [B][K], W [N][K]: uint16 BF16; gy [B][N]: uint16 BF16 or float64 values.
+    Returns a dict of binary64
+    arrays: gx [B][K], gW [N][K], gb [N] (bias given), ggamma and gbeta [K]
+    (gamma / beta given), gz [B][N].  With rnd=True every one of them holds
+    BF16 values (convert with ``to_bf16_bits``)."""
+    x = _u16(np.atleast_2d(x))
+    W = _u16(W)
+    gy = np.atleast_2d(gy)
+    gy = bf16_array_to_f64(gy) if gy.dtype == np.uint16 else np.ascontiguousarray(gy, dtype=np.float64)
+    B, K = x.shape
+    N, K2 = W.shape
+    assert K == K2 and gy.shape == (B, N)
+    out = {"gx": np.empty((B, K)), "gW": np.empty((N, K)), "gz": np.empty((B, N))}
+    out["gb"] = np.empty(N) if bias is not None else None
+    out["ggamma"] = np.empty(K) if gamma is not None else None
+    out["gbeta"] = np.empty(K) if beta is not None else None
+    _load().wgo_block_backward(N, K, B, _ptr(x), K,
+                               _ptr(None if gamma is None else _u16(gamma)),
+                               _ptr(None if beta is None else _u16(beta)), float(eps),
+                               _ptr(W), _ptr(None if bias is None else _u16(bias)),
+                               _ptr(gy), N, 1 if rnd else 0,
+                               _ptr(out["gx"]), _ptr(out["gW"]), _ptr(out["gb"]),
+                               _ptr(out["ggamma"]), _ptr(out["gbeta"]), _ptr(out["gz"]))
+    return {k: v for k, v in out.items() if v is not None}
+
+
+def to_bf16_bits(a) -> np.ndarray:
+    """BF16 bit patterns of binary64 values that are BF16 values (exact)."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    f = a.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), a, equal_nan=True), "not BF16 values"
+    u = f.view(np.uint32)
+    assert not np.any(u & 0xFFFF), "not BF16 values"
+    return (u >> 16).astype(np.uint16)
+
+
+def chain_backward(xs, layers, gy_last=None, *, eps=1e-5, rnd=True):
+    """Backward of a chain of LayerNorm -> Linear -> GELU-tanh blocks, last block first.
+
+    xs[i]: [B][K_i] uint16 input of block i (the forward's saved activations);
+    xs[len(layers)]: the chain output, used for the mean-square loss when
+    gy_last is None.  layers[i]: dict with W, and optionally bias, gamma, beta
+    (uint16).  Returns (per-block list of block_backward dicts, gx of the chain
+    input).  Between blocks the input gradient is BF16 (rnd=True) or binary64."""
+    gy = mean_square_grad(xs[-1]) if gy_last is None else gy_last
+    out = [None] * len(layers)
+    for i in range(len(layers) - 1, -1, -1):
+        L = layers[i]
+        r = block_backward(xs[i], L["W"], gy, gamma=L.get("gamma"), beta=L.get("beta"), eps=eps,
+                           bias=L.get("bias"), rnd=rnd)
+        out[i] = r
+        gy = to_bf16_bits(r["gx"]) if rnd else r["gx"]
+    return out, out[0]["gx"]

@@ -37,6 +37,22 @@
  *                by Kernel", section "The fix: Part 10's split-KV kernel".
  *   4-bit     y = R( sum_k (s_g q_k + z_g) x_k ), 4-bit codes q in groups of 128
  *             -- "One Token, Kernel by Kernel", section "4-bit weights".
+ *   backward  of one block y = R(GELU(z)), z = xh W^T + bias, xh = R(LayerNorm(x)),
+ *             given the output gradient gy (BF16), in this order:
+ *               gz  = R( gy * GELU'(z) )
+ *               gb  = R( sum_b gz ),  gW[n][k] = R( sum_b gz[b][n] xh[b][k] )
+ *               gxh = sum_n gz[b][n] W[n][k]                (not rounded)
+ *               u = (x - mu) / sigma,  gu = gamma * gxh
+ *               gx  = R( (gu - mean_k gu - u * mean_k(gu u)) / sigma )
+ *               ggamma = R( sum_b gxh u ),  gbeta = R( sum_b gxh )
+ *             and the mean-square loss of the last output, g = R( 2 y / (batch N) )
+ *             -- "Making small PyTorch ops faster on a laptop GPU", sections "It
+ *                works in training too" (the example step's loss is the mean of
+ *                the squared FP32 output; the backward visits the layers in
+ *                reverse) and "Beyond language models" (the LayerNorm -> Linear
+ *                -> GELU block).  The rounding points are a reading: BF16 at
+ *                every tensor the unfused pipeline would store (gz, the
+ *                parameter gradients, gx), wide arithmetic inside.
  *
  * R() is round-to-nearest-even to BF16 (FP16 for the standalone FP16 norm rows),
  * taken directly from the binary64 value (one rounding).  x-hat is rounded to
@@ -453,4 +469,133 @@ void wgo_matvec_int4(const uint8_t *W4, const uint16_t *scales, const uint16_t *
             if (acc_out) acc_out[b * N + n] = acc;
         }
     }
+}
+
+/* ---------------------------------------------------------------- backward */
+
+/* Derivative of the GELU-tanh form above: with a = c (z + 0.044715 z^3) and
+ * t = tanh(a), d/dz = 0.5 (1 + t) + 0.5 z (1 - t^2) c (1 + 3 * 0.044715 z^2). */
+double wgo_gelu_tanh_grad(double z)
+{
+    const double c = sqrt(2.0 / M_PI);
+    const double t = tanh(c * (z + 0.044715 * z * z * z));
+    return 0.5 * (1.0 + t) + 0.5 * z * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * z * z);
+}
+
+/* Gradient of loss = mean over [batch][N] of y^2 (y read as BF16, squared and
+ * averaged in wide precision): g = R(2 y / (batch N)). */
+void wgo_mean_square_grad(const uint16_t *y, int64_t y_stride, int64_t N, int64_t batch,
+                          uint16_t *g, int64_t g_stride)
+{
+    const double s = 2.0 / ((double)batch * (double)N);
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t n = 0; n < N; ++n)
+            g[b * g_stride + n] = wgo_f64_to_bf16(wgo_bf16_to_f64(y[b * y_stride + n]) * s);
+}
+
+static double rnd_bf16(int rnd, double v) { return rnd ? wgo_bf16_to_f64(wgo_f64_to_bf16(v)) : v; }
+
+/*
+ * Backward of one LayerNorm -> Linear(+bias) -> GELU-tanh block (definition in
+ * the header).  x [batch][x_stride] BF16 block input; W [N][K]; bias [N] or
+ * NULL; gamma, beta [K] or NULL (1, 0); gy [batch][gy_stride] gradient of the
+ * block output (binary64 values; BF16 values between rounded blocks).  rnd = 1 rounds at the stated points; rnd = 0 keeps every
+ * value in binary64 (also xh, so that the result is the exact derivative of the
+ * unrounded block).  Outputs (binary64; BF16 values when rnd = 1):
+ * gx [batch][K], gW [N][K], gb [N] (NULL skips), ggamma and gbeta [K] (NULL
+ * skips), gz [batch][N] (NULL skips).  Sums run in ascending index order.
+ */
+void wgo_block_backward(int64_t N, int64_t K, int64_t batch,
+                        const uint16_t *x, int64_t x_stride,
+                        const uint16_t *gamma, const uint16_t *beta, double eps,
+                        const uint16_t *W, const uint16_t *bias,
+                        const double *gy, int64_t gy_stride, int rnd,
+                        double *gx, double *gW, double *gb, double *ggamma, double *gbeta,
+                        double *gz_out)
+{
+    double *u = (double *)malloc((size_t)(batch * K) * sizeof(double));
+    double *xh = (double *)malloc((size_t)(batch * K) * sizeof(double));
+    double *sig = (double *)malloc((size_t)batch * sizeof(double));
+    double *gz = (double *)malloc((size_t)(batch * N) * sizeof(double));
+    double *gxh = (double *)malloc((size_t)(batch * K) * sizeof(double));
+    /* forward again: LayerNorm statistics, u, xh */
+    for (int64_t b = 0; b < batch; ++b) {
+        const uint16_t *xb = x + b * x_stride;
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k) s += wgo_bf16_to_f64(xb[k]);
+        const double mu = s / (double)K;
+        double sv = 0.0;
+        for (int64_t k = 0; k < K; ++k) { double d = wgo_bf16_to_f64(xb[k]) - mu; sv += d * d; }
+        sig[b] = sqrt(sv / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k) {
+            u[b * K + k] = (wgo_bf16_to_f64(xb[k]) - mu) / sig[b];
+            const double v = u[b * K + k] * (gamma ? wgo_bf16_to_f64(gamma[k]) : 1.0)
+                             + (beta ? wgo_bf16_to_f64(beta[k]) : 0.0);
+            xh[b * K + k] = rnd_bf16(rnd, v);
+        }
+    }
+    /* pre-activation, then gz = gy * GELU'(z) */
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+#endif
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < batch; ++b) {
+            double z = 0.0;
+            for (int64_t k = 0; k < K; ++k) z += wgo_bf16_to_f64(W[n * K + k]) * xh[b * K + k];
+            if (bias) z += wgo_bf16_to_f64(bias[n]);
+            gz[b * N + n] = rnd_bf16(rnd, gy[b * gy_stride + n] * wgo_gelu_tanh_grad(z));
+        }
+    }
+    if (gz_out) memcpy(gz_out, gz, (size_t)(batch * N) * sizeof(double));
+    /* bias and weight gradients: sums over the batch */
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+#endif
+    for (int64_t n = 0; n < N; ++n) {
+        if (gb) {
+            double s = 0.0;
+            for (int64_t b = 0; b < batch; ++b) s += gz[b * N + n];
+            gb[n] = rnd_bf16(rnd, s);
+        }
+        for (int64_t k = 0; k < K; ++k) {
+            double s = 0.0;
+            for (int64_t b = 0; b < batch; ++b) s += gz[b * N + n] * xh[b * K + k];
+            gW[n * K + k] = rnd_bf16(rnd, s);
+        }
+    }
+    /* gradient of the normalised input: gxh = gz W (sum over the output rows) */
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+#endif
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t b = 0; b < batch; ++b) {
+            double s = 0.0;
+            for (int64_t n = 0; n < N; ++n) s += gz[b * N + n] * wgo_bf16_to_f64(W[n * K + k]);
+            gxh[b * K + k] = s;
+        }
+    /* LayerNorm backward */
+    for (int64_t b = 0; b < batch; ++b) {
+        double m1 = 0.0, m2 = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double gu = (gamma ? wgo_bf16_to_f64(gamma[k]) : 1.0) * gxh[b * K + k];
+            m1 += gu;
+            m2 += gu * u[b * K + k];
+        }
+        m1 /= (double)K;
+        m2 /= (double)K;
+        for (int64_t k = 0; k < K; ++k) {
+            const double gu = (gamma ? wgo_bf16_to_f64(gamma[k]) : 1.0) * gxh[b * K + k];
+            gx[b * K + k] = rnd_bf16(rnd, (gu - m1 - u[b * K + k] * m2) / sig[b]);
+        }
+    }
+    for (int64_t k = 0; k < K; ++k) {
+        double sg = 0.0, sb = 0.0;
+        for (int64_t b = 0; b < batch; ++b) {
+            sg += gxh[b * K + k] * u[b * K + k];
+            sb += gxh[b * K + k];
+        }
+        if (ggamma) ggamma[k] = rnd_bf16(rnd, sg);
+        if (gbeta) gbeta[k] = rnd_bf16(rnd, sb);
+    }
+    free(u); free(xh); free(sig); free(gz); free(gxh);
 }
