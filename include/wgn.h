@@ -101,7 +101,9 @@ typedef struct wgn_stage {
     int64_t res_stride;
     void *y;              /* [batch][y_stride] BF16 output; ARGMAX: int32 [batch]     */
     int64_t y_stride;     /* elements between batch rows of y (ignored for ARGMAX)    */
-    float *logits;        /* ARGMAX only: optional FP32 [batch][N] logits, or NULL    */
+    float *logits;        /* ARGMAX: optional FP32 [batch][N] logits; GELU_TANH:      */
+                          /* optional FP32 [batch][N] pre-activation (accumulator +   */
+                          /* bias, before GELU) for the backward pass; else NULL      */
     float *maxval;        /* ARGMAX only: optional FP32 [batch] maxima, or NULL       */
 } wgn_stage;
 
@@ -391,6 +393,81 @@ wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t ba
  * through wgn_gemm_norm.  0 if the
  * stages cannot be planned (a call on them would return its error). */
 size_t wgn_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch, int32_t V);
+
+/* --------------------------------------------------------- backward pass */
+/* Backward pass of a chain of LayerNorm -> Linear(+bias) -> GELU-tanh blocks
+ * for small-batch training ("Making small PyTorch ops faster on a laptop GPU",
+ * section "It works in training too": the backward visits the layers in
+ * reverse, so the weights to fetch ahead while block i's gradient is computed
+ * are those of block i-1; section "Beyond language models" for the block).
+ *
+ * stages: the forward stages as given to wgn_layer_chain (same order), each
+ * norm = LAYER, epi = GELU_TANH, no residual, stage i's K equal to stage i-1's
+ * N, and `logits` pointing at the FP32 [batch][N] pre-activation that the
+ * forward wrote there (a GELU stage with logits set keeps it); stage x is the
+ * block input and the last stage's y the chain output.  All forward tensors
+ * are read only and must hold the forward's values.  batch in [1, 16].
+ * Definition, per block, from the output gradient gy (BF16):
+ *   gz = R(gy GELU'(z)), gb = R(sum_b gz), gW = R(sum_b gz xh),
+ *   gxh = gz W, gx = R(LayerNorm backward of gxh), ggamma = R(sum_b gxh u),
+ *   gbeta = R(sum_b gxh), with xh = R(LayerNorm(x)), u = (x - mean) / sigma;
+ * gx of block i is gy of block i-1.  The last block's gy is g_out (BF16
+ * [batch][g_stride]) or, when g_out is NULL, the gradient of the mean of the
+ * squared chain output, R(2 y / (batch N)).  R() rounds to BF16. */
+typedef struct wgn_grad {
+    void *gW;      /* [N][K] BF16, required, 16-byte aligned                          */
+    void *gbias;   /* [N] BF16: required when the stage has a bias, else NULL          */
+    void *ggamma;  /* [K] BF16 or NULL; NULL when the stage has no gamma               */
+    void *gbeta;   /* [K] BF16 or NULL; NULL when the stage has no beta                */
+    void *gy;      /* [batch][N] BF16 or NULL: the gradient reaching the block output  */
+    void *gz;      /* [batch][N] BF16 or NULL: the gradient of the pre-activation      */
+} wgn_grad;
+typedef struct wgn_backward wgn_backward;
+
+/* Workspace bytes of a backward pass over these stages (0 if they do not
+ * qualify: a create call would return its error). */
+size_t wgn_backward_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch);
+
+/* Validate, lay the block table out in the workspace (one host->device copy
+ * on `stream`, then a stream synchronisation) and return a host handle.
+ * grads[n_stages]: the outputs of each block.  g_in: NULL or BF16
+ * [batch][gin_stride] for the gradient of the chain input.  Outputs may
+ * overlap neither each other, nor any tensor read, nor the workspace
+ * (WGN_E_ARG).  The buffers must stay valid while the handle is used.
+ * WGN_E_UNSUPPORTED for a stage that is not a LayerNorm + GELU block (or
+ * whose N x K reaches 2^30).  Not for the hot loop. */
+wgn_status wgn_backward_create(const wgn_stage *stages, int32_t n_stages, int32_t batch,
+                               const wgn_grad *grads, const void *g_out, int64_t g_stride,
+                               void *g_in, int64_t gin_stride, void *workspace, size_t ws_bytes,
+                               wgn_stream stream, wgn_backward **out);
+
+/* Enqueue one backward pass on `stream`: a prep launch (LayerNorm statistics
+ * and x-hat of every block input; it also clears the run's counters) and one
+ * persistent launch that walks the blocks from the last to the first, then
+ * writes g_in.  prefetch = 1: each workgroup requests its weight tile of the
+ * next block in backward order (block i-1 while block i runs) before it waits
+ * for block i to finish; 0: only after the wait.  Results are bit-identical
+ * either way and between runs.  No host synchronisation; graph-capturable. */
+wgn_status wgn_backward_run(const wgn_backward *bw, int32_t prefetch, wgn_stream stream);
+
+/* Synchronise `stream`; WGN_E_TIMEOUT if an in-kernel wait of the last run
+ * hit its bound (its outputs are then incomplete), else WGN_OK.  Each run
+ * starts from cleared counters. */
+wgn_status wgn_backward_check(const wgn_backward *bw, wgn_stream stream);
+
+/* Bound of the in-kernel waits of later runs in microseconds (negative: the
+ * default of 2 s; 0: a wait gives up at its first unsuccessful poll, so tests
+ * can force the time-out path from the host).  WGN_E_ARG above the default. */
+wgn_status wgn_backward_set_wait_us(wgn_backward *bw, int64_t us);
+/* Workgroups of the persistent launch (all resident at once); -1 for NULL. */
+int32_t wgn_backward_grid(const wgn_backward *bw);
+void wgn_backward_destroy(wgn_backward *bw);
+
+/* create + run + destroy in one call (the create step synchronises `stream`). */
+wgn_status wgn_chain_backward(const wgn_stage *stages, int32_t n_stages, int32_t batch,
+                              const wgn_grad *grads, const void *g_out, int64_t g_stride,
+                              void *g_in, int64_t gin_stride, int32_t prefetch, void *workspace,
+                              size_t ws_bytes, wgn_stream stream);
 
 /* -------------------------------------------------------- prefetch plans */
 /* Optional prefetch of later launches' weights into the GPU's memory-side

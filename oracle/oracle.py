@@ -98,7 +98,7 @@ def _load():
         lib.wgo_gelu_tanh_grad.restype = D
         lib.wgo_mean_square_grad.argtypes = [P, I64, I64, I64, P, I64]
         lib.wgo_mean_square_grad.restype = None
-        lib.wgo_block_backward.argtypes = [I64, I64, I64, P, I64, P, P, D, P, P, P, I64, I,
+        lib.wgo_block_backward.argtypes = [I64, I64, I64, P, I64, P, P, D, P, P, P, I64, P, I,
                                            P, P, P, P, P, P]
         lib.wgo_block_backward.restype = None
         _lib = lib
@@ -310,14 +310,16 @@ def mean_square_grad(y):
     return g
 
 
-def block_backward(x, W, gy, *, gamma=None, beta=None, eps=1e-5, bias=None, rnd=True):
+def block_backward(x, W, gy, *, gamma=None, beta=None, eps=1e-5, bias=None, rnd=True, gz_in=None):
     """Backward of one LayerNorm -> Linear(+bias) -> GELU-tanh block.
 
     x [B][K], W [N][K]: uint16 BF16; gy [B][N]: uint16 BF16 or float64 values.
     Returns a dict of binary64
     arrays: gx [B][K], gW [N][K], gb [N] (bias given), ggamma and gbeta [K]
     (gamma / beta given), gz [B][N].  With rnd=True every one of them holds
-    BF16 values (convert with ``to_bf16_bits``)."""
+    BF16 values (convert with ``to_bf16_bits``).  gz_in ([B][N], uint16 BF16
+    or float64): a rounding decision taken elsewhere; the products and the
+    norm backward then start from it (the returned gz is still the oracle's)."""
     x = _u16(np.atleast_2d(x))
     W = _u16(W)
     gy = np.atleast_2d(gy)
@@ -329,11 +331,15 @@ def block_backward(x, W, gy, *, gamma=None, beta=None, eps=1e-5, bias=None, rnd=
     out["gb"] = np.empty(N) if bias is not None else None
     out["ggamma"] = np.empty(K) if gamma is not None else None
     out["gbeta"] = np.empty(K) if beta is not None else None
+    if gz_in is not None:
+        gz_in = np.atleast_2d(gz_in)
+        gz_in = bf16_array_to_f64(gz_in) if gz_in.dtype == np.uint16 else np.ascontiguousarray(gz_in, np.float64)
+        assert gz_in.shape == (B, N)
     _load().wgo_block_backward(N, K, B, _ptr(x), K,
                                _ptr(None if gamma is None else _u16(gamma)),
                                _ptr(None if beta is None else _u16(beta)), float(eps),
                                _ptr(W), _ptr(None if bias is None else _u16(bias)),
-                               _ptr(gy), N, 1 if rnd else 0,
+                               _ptr(gy), N, _ptr(gz_in), 1 if rnd else 0,
                                _ptr(out["gx"]), _ptr(out["gW"]), _ptr(out["gb"]),
                                _ptr(out["ggamma"]), _ptr(out["gbeta"]), _ptr(out["gz"]))
     return {k: v for k, v in out.items() if v is not None}

@@ -503,13 +503,16 @@ static double rnd_bf16(int rnd, double v) { return rnd ? wgo_bf16_to_f64(wgo_f64
  * value in binary64 (also xh, so that the result is the exact derivative of the
  * unrounded block).  Outputs (binary64; BF16 values when rnd = 1):
  * gx [batch][K], gW [N][K], gb [N] (NULL skips), ggamma and gbeta [K] (NULL
- * skips), gz [batch][N] (NULL skips).  Sums run in ascending index order.
+ * skips), gz [batch][N] (NULL skips).  gz_in [batch][N] (or NULL): when given,
+ * the products and the norm backward use it in place of the computed gz (gz
+ * itself is still computed and returned in gz_out).  Sums run in ascending
+ * index order.
  */
 void wgo_block_backward(int64_t N, int64_t K, int64_t batch,
                         const uint16_t *x, int64_t x_stride,
                         const uint16_t *gamma, const uint16_t *beta, double eps,
                         const uint16_t *W, const uint16_t *bias,
-                        const double *gy, int64_t gy_stride, int rnd,
+                        const double *gy, int64_t gy_stride, const double *gz_in, int rnd,
                         double *gx, double *gW, double *gb, double *ggamma, double *gbeta,
                         double *gz_out)
 {
@@ -547,6 +550,9 @@ void wgo_block_backward(int64_t N, int64_t K, int64_t batch,
         }
     }
     if (gz_out) memcpy(gz_out, gz, (size_t)(batch * N) * sizeof(double));
+    /* a caller that compares against a computation which rounded gz itself
+     * hands that rounding decision in: the steps below then start from it */
+    if (gz_in) memcpy(gz, gz_in, (size_t)(batch * N) * sizeof(double));
     /* bias and weight gradients: sums over the batch */
 #ifdef _OPENMP
 #pragma omp parallel for schedule(static) num_threads(g_threads)

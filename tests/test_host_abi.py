@@ -584,3 +584,103 @@ def test_layer_chain_batched_checks_before_the_device():
                                None) == L.E_WORKSPACE
     if L.lib().wgn_device_cu_count() == 0:
         assert lib.wgn_layer_chain(arr, len(stages), 32, None, None, 0x100000, need, None, None) == L.E_DEVICE
+
+
+# ----------------------------------------------------------- backward pass
+def fake_train_chain(ar, B, n, D=768, K0=None):
+    """n LayerNorm -> Linear -> GELU blocks with kept pre-activations, plus
+    their gradient outputs (fake addresses)."""
+    stages, grads = [], []
+    x = None
+    for i in range(n):
+        K = K0 if (i == 0 and K0) else D
+        s = fake_stage(ar, D, K, B, L.NORM_LAYER, L.EPI_GELU_TANH, x=x, bias=True, beta=True)
+        s.eps = 1e-5
+        s.logits = ar.take(B * D * 4)
+        x = s.y
+        stages.append(s)
+        g = L.Grad()
+        g.gW, g.gbias, g.ggamma, g.gbeta = ar.take(D * K * 2), ar.take(D * 2), ar.take(K * 2), ar.take(K * 2)
+        g.gy, g.gz = ar.take(B * D * 2), ar.take(B * D * 2)
+        grads.append(g)
+    return stages, grads
+
+
+def call_backward(stages, grads, B, ws=None, ws_bytes=None, g_in=None, gin_stride=0, g_out=None, g_stride=0):
+    import ctypes
+    arr = L.stage_array(stages)
+    gr = (L.Grad * len(grads))(*grads)
+    need = L.lib().wgn_backward_workspace_bytes(arr, len(stages), B)
+    if ws is None:
+        ws = 1 << 44
+    h = ctypes.c_void_p()
+    return L.lib().wgn_backward_create(arr, len(stages), B, gr, g_out, g_stride, g_in, gin_stride, ws,
+                                       need if ws_bytes is None else ws_bytes, None, ctypes.byref(h))
+
+
+def test_backward_workspace_layout():
+    """Per block: statistics, x-hat, gxh and column sums; one partial buffer of
+    the largest block; counters.  72 x 768 at batch 16 stays near 10 MB."""
+    for B in (1, 4, 16):
+        ar = Arena()
+        st, _ = fake_train_chain(ar, B, 72)
+        need = L.lib().wgn_backward_workspace_bytes(L.stage_array(st), 72, B)
+        per_layer = B * 768 * (2 + 4)
+        part = 24 * B * 768 * 4
+        assert per_layer * 72 + part < need < per_layer * 72 + part + 72 * 2048 + 72 * 128 + 65536, (B, need)
+    ar = Arena()
+    st, _ = fake_train_chain(ar, 17, 2)
+    assert L.lib().wgn_backward_workspace_bytes(L.stage_array(st), 2, 17) == 0  # batch above 16
+    st, _ = fake_train_chain(ar, 4, 2)
+    st[1].epi = L.EPI_NONE
+    st[1].logits = None
+    assert L.lib().wgn_backward_workspace_bytes(L.stage_array(st), 2, 4) == 0  # not a GELU block
+
+
+def test_backward_checks_before_the_device():
+    """Every argument error is reported before the device is looked at (this
+    host has none: a valid call ends in WGN_E_DEVICE)."""
+    B = 4
+    ar = Arena()
+    st, gr = fake_train_chain(ar, B, 3)
+    assert call_backward(st, gr, B) == L.E_DEVICE
+    cases = []
+    s2, g2 = fake_train_chain(ar, B, 3); s2[1].norm = L.NORM_RMS; s2[1].beta = None; g2[1].gbeta = None
+    cases.append((s2, g2, L.E_UNSUPPORTED, "RMSNorm block"))
+    s2, g2 = fake_train_chain(ar, B, 3); s2[2].logits = None
+    cases.append((s2, g2, L.E_ARG, "no pre-activation"))
+    s2, g2 = fake_train_chain(ar, B, 3); s2[0].residual = ar.take(B * 768 * 2); s2[0].res_stride = 768
+    cases.append((s2, g2, L.E_UNSUPPORTED, "residual"))
+    s2, g2 = fake_train_chain(ar, B, 3, K0=512); s2[1].K = 512
+    cases.append((s2, g2, L.E_ARG, "shapes do not chain"))
+    s2, g2 = fake_train_chain(ar, B, 3); g2[1].gbias = None
+    cases.append((s2, g2, L.E_ARG, "bias without its gradient"))
+    s2, g2 = fake_train_chain(ar, B, 3); s2[0].gamma = None
+    cases.append((s2, g2, L.E_ARG, "gain gradient without a gain"))
+    s2, g2 = fake_train_chain(ar, B, 3); g2[2].gW = None
+    cases.append((s2, g2, L.E_ARG, "no weight gradient"))
+    s2, g2 = fake_train_chain(ar, B, 3); g2[2].gW += 8
+    cases.append((s2, g2, L.E_ALIGN, "weight gradient misaligned"))
+    s2, g2 = fake_train_chain(ar, B, 3); g2[1].gz = g2[0].gW + 64
+    cases.append((s2, g2, L.E_ARG, "two outputs overlap"))
+    s2, g2 = fake_train_chain(ar, B, 3); g2[2].gW = s2[1].W
+    cases.append((s2, g2, L.E_ARG, "an output overwrites a weight"))
+    s2, g2 = fake_train_chain(ar, B, 3); g2[0].gy = s2[1].logits
+    cases.append((s2, g2, L.E_ARG, "an output overwrites a pre-activation"))
+    for s, g, want, what in cases:
+        assert call_backward(s, g, B) == want, what
+    assert call_backward(st, gr, 17) == L.E_ARG
+    assert call_backward(st, gr, B, ws_bytes=1024) == L.E_WORKSPACE
+    assert call_backward(st, gr, B, ws=(1 << 44) + 64) == L.E_WORKSPACE  # 256-byte alignment
+    assert call_backward(st, gr, B, ws=st[0].W) == L.E_ARG  # workspace over a weight
+    assert call_backward(st, gr, B, g_in=st[0].x, gin_stride=768) == L.E_ARG  # g_in over the input
+    assert call_backward(st, gr, B, g_in=ar.take(B * 768 * 2), gin_stride=700) == L.E_ARG
+    assert call_backward(st, gr, B, g_in=ar.take(B * 768 * 2) + 1, gin_stride=768) == L.E_ALIGN
+    assert call_backward(st, gr, B, g_out=ar.take(B * 768 * 2), g_stride=768) == L.E_DEVICE
+    import ctypes
+    arr = L.stage_array(st)
+    gra = (L.Grad * 3)(*gr)
+    assert L.lib().wgn_chain_backward(arr, 3, B, gra, None, 0, None, 0, 2, 1 << 44, 1 << 30, None) == L.E_ARG
+    assert L.lib().wgn_backward_run(None, 1, None) == L.E_ARG
+    assert L.lib().wgn_backward_check(None, None) == L.E_ARG
+    assert L.lib().wgn_backward_grid(None) == -1

@@ -231,3 +231,28 @@ def test_chain_backward_matches_autograd_with_rounded_activations():
     for i in range(L):
         for k, kk in (("W", "gW"), ("bias", "gb"), ("gamma", "ggamma"), ("beta", "gbeta")):
             assert rel_err(per[i][kk], params[i][k].grad.numpy()) < 1e-11, (i, k)
+
+
+def test_given_gz_replaces_only_the_rounding_decision():
+    """gz_in = the oracle's own gz reproduces every output bit for bit; a
+    different gz_in changes the products (gW, gb, gx) as the definition says:
+    gb becomes R(sum_b gz_in) exactly."""
+    from test_oracle_pins import rne_bf16_bits, bf16_val
+
+    B, N, K = 4, 24, 32
+    eps = float(np.float32(1e-5))
+    x = rand_bf16((B, K))
+    p = block_params(N, K)
+    gy = rand_bf16((B, N), std=0.1)
+    r = O.block_backward(x, p["W"], gy, gamma=p["gamma"], beta=p["beta"], eps=eps, bias=p["bias"])
+    r2 = O.block_backward(x, p["W"], gy, gamma=p["gamma"], beta=p["beta"], eps=eps, bias=p["bias"],
+                          gz_in=O.to_bf16_bits(r["gz"]))
+    for k in r:
+        assert np.array_equal(r[k], r2[k]), k
+    alt = rand_bf16((B, N), std=0.05)
+    r3 = O.block_backward(x, p["W"], gy, gamma=p["gamma"], beta=p["beta"], eps=eps, bias=p["bias"],
+                          gz_in=alt)
+    assert np.array_equal(r3["gz"], r["gz"])
+    for n in range(N):
+        s = sum((bf16_val(int(alt[b, n])) for b in range(B)), Fraction(0))
+        assert O.to_bf16_bits(r3["gb"][n:n + 1])[0] == rne_bf16_bits(s)

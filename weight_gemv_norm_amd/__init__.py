@@ -10,4 +10,5 @@ from .api import (Chain, gemv_norm, gemv_norm_workspace_bytes, layer_chain, lmhe
                   PATH_AUTO, PATH_VECTOR, PATH_MATRIX, PATH_TILED, Plan, WgnError, decode_attention,
                   decode_attention_workspace_bytes, gemv_int4, stream_read,
                   workspace_bytes, plan_tune, lmhead_argmax_static, gemm_norm,
-                  gemm_norm_workspace_bytes)
+                  gemm_norm_workspace_bytes, make_grad, backward_workspace_bytes, Backward,
+                  chain_backward)

@@ -48,6 +48,11 @@ class Plan(ctypes.Structure):
                 ("plain_us", F32), ("best_us", F32), ("speedup_lo", F32), ("candidates", I32)]
 
 
+class Grad(ctypes.Structure):
+    """Mirror of wgn_grad."""
+    _fields_ = [("gW", P), ("gbias", P), ("ggamma", P), ("gbeta", P), ("gy", P), ("gz", P)]
+
+
 class WgnError(RuntimeError):
     def __init__(self, status: int, what: str):
         msg = "%s failed: %s (%d)" % (what, status_string(status), status)
@@ -107,6 +112,15 @@ def lib() -> ctypes.CDLL:
         "wgn_first_wave_of_unit": ([I32, I32, I32], I32),
         "wgn_partition_selftest": ([SP, I32, I32, OP], I32),
         "wgn_plan_phases": ([SP, I32, I32, OP, ctypes.POINTER(I32)], I32),
+        "wgn_backward_workspace_bytes": ([SP, I32, I32], SZ),
+        "wgn_backward_create": ([SP, I32, I32, ctypes.POINTER(Grad), P, I64, P, I64, P, SZ, P,
+                                 ctypes.POINTER(P)], I32),
+        "wgn_backward_run": ([P, I32, P], I32),
+        "wgn_backward_check": ([P, P], I32),
+        "wgn_backward_set_wait_us": ([P, I64], I32),
+        "wgn_backward_grid": ([P], I32),
+        "wgn_backward_destroy": ([P], None),
+        "wgn_chain_backward": ([SP, I32, I32, ctypes.POINTER(Grad), P, I64, P, I64, I32, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)

@@ -13,7 +13,7 @@ import torch
 
 from . import _lib as L
 from ._lib import (EPI_ARGMAX, EPI_GELU_TANH, EPI_NONE, EPI_SWIGLU, NORM_LAYER,  # noqa: F401
-                   NORM_NONE, NORM_RMS, BF16, FP16, ChainOpts, Plan, Stage, WgnError)
+                   NORM_NONE, NORM_RMS, BF16, FP16, ChainOpts, Grad, Plan, Stage, WgnError)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -55,8 +55,14 @@ def make_stage(W: torch.Tensor, x: torch.Tensor, y: torch.Tensor, *, norm: int =
                beta: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
                epi: int = EPI_NONE, W_up: Optional[torch.Tensor] = None,
                residual: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
-               maxval: Optional[torch.Tensor] = None) -> Stage:
-    """Describe y = R(residual + epi(W . norm(x) + bias)) over device tensors."""
+               maxval: Optional[torch.Tensor] = None, pre: Optional[torch.Tensor] = None) -> Stage:
+    """Describe y = R(residual + epi(W . norm(x) + bias)) over device tensors.
+
+    pre: FP32 [batch][N] that a GELU stage fills with its pre-activation (the
+    wgn_stage `logits` field of a GELU stage), for the backward pass."""
+    assert logits is None or pre is None, "logits (argmax) and pre (GELU) are one field"
+    if pre is not None:
+        logits = pre
     assert W.dim() == 2 and W.is_contiguous()
     N, K = W.shape
     s = Stage()
@@ -385,3 +391,77 @@ def plan_phases(stages: Sequence[Stage], batch: int, grid: int = 0, path: int = 
 
 def first_wave_of_unit(u: int, units: int, waves: int) -> int:
     return int(L.lib().wgn_first_wave_of_unit(u, units, waves))
+
+
+# ------------------------------------------------------------------ backward
+def make_grad(gW: torch.Tensor, gbias: Optional[torch.Tensor] = None, ggamma: Optional[torch.Tensor] = None,
+              gbeta: Optional[torch.Tensor] = None, gy: Optional[torch.Tensor] = None,
+              gz: Optional[torch.Tensor] = None) -> Grad:
+    """Describe one block's gradient outputs (wgn_grad)."""
+    g = Grad()
+    g.gW, g.gbias, g.ggamma, g.gbeta, g.gy, g.gz = (_ptr(gW), _ptr(gbias), _ptr(ggamma), _ptr(gbeta), _ptr(gy),
+                                                    _ptr(gz))
+    return g
+
+
+def backward_workspace_bytes(stages: Sequence[Stage], batch: int) -> int:
+    return int(L.lib().wgn_backward_workspace_bytes(L.stage_array(stages), len(stages), batch))
+
+
+class Backward:
+    """A planned backward pass (wgn_backward_create); run() enqueues one pass."""
+
+    def __init__(self, stages: Sequence[Stage], batch: int, grads: Sequence[Grad],
+                 g_out: Optional[torch.Tensor] = None, g_in: Optional[torch.Tensor] = None,
+                 ws: Optional[torch.Tensor] = None, stream=None, device="cuda"):
+        assert len(grads) == len(stages)
+        self._arr = L.stage_array(stages)
+        self._grads = (Grad * len(grads))(*grads)
+        need = L.lib().wgn_backward_workspace_bytes(self._arr, len(stages), batch)
+        self.ws = ws if ws is not None else workspace(max(int(need), 256), device)
+        h = ctypes.c_void_p()
+        st = L.lib().wgn_backward_create(self._arr, len(stages), batch, self._grads, _ptr(g_out),
+                                         _row_stride(g_out) if g_out is not None else 0, _ptr(g_in),
+                                         _row_stride(g_in) if g_in is not None else 0, _ptr(self.ws),
+                                         self.ws.numel(), _stream(stream), ctypes.byref(h))
+        L.check(st, "wgn_backward_create")
+        self._h = h
+
+    def run(self, prefetch: bool = True, stream=None) -> None:
+        L.check(L.lib().wgn_backward_run(self._h, 1 if prefetch else 0, _stream(stream)), "wgn_backward_run")
+
+    def check(self, stream=None) -> None:
+        L.check(L.lib().wgn_backward_check(self._h, _stream(stream)), "wgn_backward_check")
+
+    def set_wait_us(self, us: int) -> None:
+        L.check(L.lib().wgn_backward_set_wait_us(self._h, int(us)), "wgn_backward_set_wait_us")
+
+    @property
+    def grid(self) -> int:
+        return int(L.lib().wgn_backward_grid(self._h))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            L.lib().wgn_backward_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def chain_backward(stages: Sequence[Stage], batch: int, grads: Sequence[Grad], g_out: Optional[torch.Tensor] = None,
+                   g_in: Optional[torch.Tensor] = None, prefetch: bool = True, ws: Optional[torch.Tensor] = None,
+                   stream=None, device="cuda") -> None:
+    """wgn_chain_backward: create, run and release a backward pass in one call."""
+    arr = L.stage_array(stages)
+    gr = (Grad * len(grads))(*grads)
+    if ws is None:
+        ws = workspace(max(int(L.lib().wgn_backward_workspace_bytes(arr, len(stages), batch)), 256), device)
+    st = L.lib().wgn_chain_backward(arr, len(stages), batch, gr, _ptr(g_out),
+                                    _row_stride(g_out) if g_out is not None else 0, _ptr(g_in),
+                                    _row_stride(g_in) if g_in is not None else 0, 1 if prefetch else 0,
+                                    _ptr(ws), ws.numel(), _stream(stream))
+    L.check(st, "wgn_chain_backward")

@@ -10,8 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libwgn.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("wgn_kernels.hip", "wgn_attn.hip", "wgn_int4.hip", "wgn_read.hip", "wgn_gemm.hip", "wgn_api.cpp")]
-HEADERS = [os.path.join(CSRC, f) for f in ("wgn_prog.h", "wgn_loader.h", "wgn_attn.h", "wgn_numerics.h", "wgn_gemm.h")] + [os.path.join(INCLUDE, "wgn.h")]
+SOURCES = [os.path.join(CSRC, f) for f in ("wgn_kernels.hip", "wgn_attn.hip", "wgn_int4.hip", "wgn_read.hip", "wgn_gemm.hip", "wgn_bwd.hip", "wgn_api.cpp")]
+HEADERS = [os.path.join(CSRC, f) for f in ("wgn_prog.h", "wgn_loader.h", "wgn_attn.h", "wgn_numerics.h", "wgn_gemm.h", "wgn_bwd.h")] + [os.path.join(INCLUDE, "wgn.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -16,6 +16,7 @@
 
 #include "wgn.h"
 #include "wgn_attn.h"
+#include "wgn_bwd.h"
 #include "wgn_gemm.h"
 #include "wgn_loader.h"
 
@@ -94,7 +95,8 @@ wgn_status check_stage(const wgn_stage &s, int32_t batch, int32_t max_batch = MA
     if (s.epi != EPI_SWIGLU && s.W_up) return WGN_E_ARG;
     if (s.epi == EPI_SWIGLU && s.bias) return WGN_E_UNSUPPORTED;
     if (s.epi == EPI_ARGMAX && s.residual) return WGN_E_ARG;
-    if (s.epi != EPI_ARGMAX && (s.logits || s.maxval)) return WGN_E_ARG;
+    if (s.maxval && s.epi != EPI_ARGMAX) return WGN_E_ARG;
+    if (s.logits && s.epi != EPI_ARGMAX && s.epi != EPI_GELU_TANH) return WGN_E_ARG;
     if (s.norm != NORM_LAYER && s.beta) return WGN_E_ARG;
     if (s.norm == NORM_NONE && s.gamma) return WGN_E_ARG;
     if (s.norm != NORM_NONE && !(s.eps >= 0.0f)) return WGN_E_ARG;
@@ -107,7 +109,7 @@ wgn_status check_stage(const wgn_stage &s, int32_t batch, int32_t max_batch = MA
     if ((s.bias && !a2(s.bias)) || (s.residual && !a2(s.residual))) return WGN_E_ALIGN;
     if (s.epi == EPI_ARGMAX) {
         if (!a4(s.y) || (s.logits && !a4(s.logits)) || (s.maxval && !a4(s.maxval))) return WGN_E_ALIGN;
-    } else if (!a2(s.y)) {
+    } else if (!a2(s.y) || (s.logits && !a4(s.logits))) {
         return WGN_E_ALIGN;
     }
     return WGN_OK;
@@ -136,6 +138,7 @@ void stage_ranges(const wgn_stage &s, int32_t B, std::vector<Range> &reads, std:
         if (s.maxval) writes.push_back(rng(s.maxval, (size_t)B * 4));
     } else {
         writes.push_back(rng(s.y, ((size_t)(B - 1) * s.y_stride + s.N) * 2));
+        if (s.logits) writes.push_back(rng(s.logits, (size_t)B * s.N * 4));
     }
     consts.push_back(rng(s.W, (size_t)s.N * s.K * 2));
     if (s.W_up) consts.push_back(rng(s.W_up, (size_t)s.N * s.K * 2));
@@ -2012,6 +2015,264 @@ wgn_status wgn_stream_read(const void *src, size_t bytes, int32_t grid, int32_t 
     hipError_t e = note(launch_stream_read(src, (uint64_t)(bytes >> 4), grid, threads, depth, sink, (hipStream_t)stream),
                         "stream_read launch");
     return e == hipSuccess ? WGN_OK : WGN_E_HIP;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ backward pass
+struct wgn_backward {
+    int32_t n = 0, B = 0, G = 0;
+    void *ws = nullptr;
+    size_t err_off = 0, ctr_off = 0;
+    int32_t nctr = 0;
+    wgn::BwdArgs a;
+};
+
+namespace {
+
+using wgn::BwdLayer;
+
+// Offsets of one backward run's workspace: the layer table, per-layer
+// statistics, x-hat, gxh and column sums, the shared partial buffer, then
+// the counters (done per layer, tickets, error word).
+struct BwdLayout {
+    std::vector<size_t> stats, xh, gxh, s12;
+    size_t descs = 0, part = 0, ctr = 0, total = 0;
+    int32_t max_ncb = 0, nctr = 0;
+};
+
+inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+wgn_status bwd_check_stages(const wgn_stage *stages, int32_t n, int32_t batch) {
+    if (!stages || n < 1 || n > wgn::BWD_MAX_LAYERS) return WGN_E_ARG;
+    if (batch < 1 || batch > wgn::BWD_MAX_BATCH) return WGN_E_ARG;
+    for (int32_t i = 0; i < n; ++i) {
+        const wgn_stage &s = stages[i];
+        const wgn_status st = check_stage(s, batch, wgn::BWD_MAX_BATCH);
+        if (st != WGN_OK) return st;
+        if (s.norm != NORM_LAYER || s.epi != EPI_GELU_TANH || s.residual) return WGN_E_UNSUPPORTED;
+        if (!s.logits) return WGN_E_ARG;  // the pre-activations the forward kept
+        if ((int64_t)s.N * s.K >= ((int64_t)1 << 30)) return WGN_E_UNSUPPORTED;  // 32-bit byte offsets
+        if (i > 0 && s.K != stages[i - 1].N) return WGN_E_ARG;
+    }
+    return WGN_OK;
+}
+
+BwdLayout bwd_layout(const wgn_stage *stages, int32_t n, int32_t B) {
+    BwdLayout L;
+    size_t o = 0;
+    L.descs = o;
+    o = up256(o + (size_t)n * sizeof(BwdLayer));
+    size_t part = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t N = stages[i].N, K = stages[i].K;
+        const int32_t nrb = (N + wgn::BWD_TILE_ROWS - 1) / wgn::BWD_TILE_ROWS;
+        const int32_t ncb = (K + wgn::BWD_TILE_COLS - 1) / wgn::BWD_TILE_COLS;
+        L.max_ncb = std::max(L.max_ncb, ncb);
+        part = std::max(part, (size_t)nrb * B * K * 4);
+        L.stats.push_back(o);
+        o = up256(o + (size_t)B * 2 * 4);
+        L.xh.push_back(o);
+        o = up256(o + (size_t)B * K * 2);
+        L.gxh.push_back(o);
+        o = up256(o + (size_t)B * K * 4);
+        L.s12.push_back(o);
+        o = up256(o + (size_t)ncb * B * 2 * 4);
+    }
+    L.part = o;
+    o = up256(o + part);
+    L.ctr = o;
+    L.nctr = n + L.max_ncb + 1;
+    o = up256(o + (size_t)L.nctr * 4);
+    L.total = o;
+    return L;
+}
+
+// Byte ranges the backward pass writes (outputs) and reads (forward tensors);
+// outputs may overlap neither each other nor anything read.
+wgn_status bwd_check_ranges(const wgn_stage *st, int32_t n, int32_t B, const wgn_grad *gr, const void *g_out,
+                            int64_t g_stride, const void *g_in, int64_t gin_stride, const void *ws, size_t ws_bytes) {
+    std::vector<Range> w, r;
+    auto rows = [&](const void *p, int64_t stride, int32_t len) {
+        return rng(p, ((size_t)(B - 1) * (size_t)stride + (size_t)len) * 2);
+    };
+    for (int32_t i = 0; i < n; ++i) {
+        const wgn_stage &s = st[i];
+        const wgn_grad &g = gr[i];
+        w.push_back(rng(g.gW, (size_t)s.N * s.K * 2));
+        if (g.gbias) w.push_back(rng(g.gbias, (size_t)s.N * 2));
+        if (g.ggamma) w.push_back(rng(g.ggamma, (size_t)s.K * 2));
+        if (g.gbeta) w.push_back(rng(g.gbeta, (size_t)s.K * 2));
+        if (g.gy) w.push_back(rng(g.gy, (size_t)B * s.N * 2));
+        if (g.gz) w.push_back(rng(g.gz, (size_t)B * s.N * 2));
+        r.push_back(rng(s.W, (size_t)s.N * s.K * 2));
+        r.push_back(rows(s.x, s.x_stride, s.K));
+        r.push_back(rng(s.logits, (size_t)B * s.N * 4));
+        if (s.gamma) r.push_back(rng(s.gamma, (size_t)s.K * 2));
+        if (s.beta) r.push_back(rng(s.beta, (size_t)s.K * 2));
+    }
+    const wgn_stage &last = st[n - 1];
+    if (g_out) r.push_back(rows(g_out, g_stride, last.N));
+    else r.push_back(rows(last.y, last.y_stride, last.N));
+    if (g_in) w.push_back(rows(g_in, gin_stride, st[0].K));
+    w.push_back(rng(ws, ws_bytes));
+    std::sort(w.begin(), w.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < w.size(); ++i)
+        if (w[i].lo < w[i - 1].hi) return WGN_E_ARG;
+    for (const Range &q : r) {
+        auto it = std::lower_bound(w.begin(), w.end(), q.hi, [](const Range &a, uintptr_t v) { return a.lo < v; });
+        if (it != w.begin() && overlap(*(it - 1), q)) return WGN_E_ARG;
+    }
+    return WGN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wgn_backward_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch) {
+    if (bwd_check_stages(stages, n_stages, batch) != WGN_OK) return 0;
+    return bwd_layout(stages, n_stages, batch).total;
+}
+
+wgn_status wgn_backward_create(const wgn_stage *stages, int32_t n, int32_t batch, const wgn_grad *grads,
+                               const void *g_out, int64_t g_stride, void *g_in, int64_t gin_stride,
+                               void *workspace, size_t ws_bytes, wgn_stream stream, wgn_backward **out) {
+    if (!out) return WGN_E_ARG;
+    *out = nullptr;
+    wgn_status st = bwd_check_stages(stages, n, batch);
+    if (st != WGN_OK) return st;
+    if (!grads) return WGN_E_ARG;
+    for (int32_t i = 0; i < n; ++i) {
+        const wgn_stage &s = stages[i];
+        const wgn_grad &g = grads[i];
+        if (!g.gW) return WGN_E_ARG;
+        if (!g.gbias != !s.bias) return WGN_E_ARG;
+        if ((g.ggamma && !s.gamma) || (g.gbeta && !s.beta)) return WGN_E_ARG;
+        if (!a16(g.gW)) return WGN_E_ALIGN;
+        if (!a2(g.gbias) || !a2(g.ggamma) || !a2(g.gbeta) || !a2(g.gy) || !a2(g.gz)) return WGN_E_ALIGN;
+    }
+    const wgn_stage &last = stages[n - 1];
+    if (g_out && batch > 1 && g_stride < last.N) return WGN_E_ARG;
+    if (g_in && batch > 1 && gin_stride < stages[0].K) return WGN_E_ARG;
+    if (!a2(g_out) || !a2(g_in)) return WGN_E_ALIGN;
+    const BwdLayout L = bwd_layout(stages, n, batch);
+    if (!workspace || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return WGN_E_WORKSPACE;
+    st = bwd_check_ranges(stages, n, batch, grads, g_out, g_stride, g_in, gin_stride, workspace, ws_bytes);
+    if (st != WGN_OK) return st;
+    DevInfo d = device_info();
+    if (!d.ok) return WGN_E_DEVICE;
+
+    char *ws = (char *)workspace;
+    std::vector<BwdLayer> img((size_t)n);
+    int32_t max_items = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const wgn_stage &s = stages[i];
+        const wgn_grad &g = grads[i];
+        BwdLayer &b = img[(size_t)i];
+        std::memset(&b, 0, sizeof b);
+        b.W = (const uint16_t *)s.W;
+        b.x = (const uint16_t *)s.x;
+        b.gamma = (const uint16_t *)s.gamma;
+        b.beta = (const uint16_t *)s.beta;
+        b.pre = s.logits;
+        b.gW = (uint16_t *)g.gW;
+        b.gb = (uint16_t *)g.gbias;
+        b.ggamma = (uint16_t *)g.ggamma;
+        b.gbeta = (uint16_t *)g.gbeta;
+        b.gy = (uint16_t *)g.gy;
+        b.gz = (uint16_t *)g.gz;
+        b.stats = (float *)(ws + L.stats[(size_t)i]);
+        b.xh = (uint16_t *)(ws + L.xh[(size_t)i]);
+        b.gxh = (float *)(ws + L.gxh[(size_t)i]);
+        b.s12 = (float *)(ws + L.s12[(size_t)i]);
+        b.x_stride = batch > 1 ? s.x_stride : s.K;
+        b.eps = s.eps;
+        b.N = s.N;
+        b.K = s.K;
+        b.nrb = (s.N + wgn::BWD_TILE_ROWS - 1) / wgn::BWD_TILE_ROWS;
+        b.ncb = (s.K + wgn::BWD_TILE_COLS - 1) / wgn::BWD_TILE_COLS;
+        max_items = std::max(max_items, b.nrb * b.ncb);
+    }
+    const int32_t resident = wgn::bwd_resident_grid();
+    if (resident < 1) return WGN_E_HIP;
+    hipStream_t s = (hipStream_t)stream;
+    if (note(hipMemcpyAsync(ws + L.descs, img.data(), img.size() * sizeof(BwdLayer), hipMemcpyHostToDevice, s),
+             "backward upload") != hipSuccess ||
+        note(hipStreamSynchronize(s), "backward create sync") != hipSuccess)
+        return WGN_E_HIP;
+    wgn_backward *h = new (std::nothrow) wgn_backward;
+    if (!h) return WGN_E_HIP;
+    h->n = n;
+    h->B = batch;
+    h->G = std::min(max_items, resident);
+    h->ws = workspace;
+    h->ctr_off = L.ctr;
+    h->nctr = L.nctr;
+    h->err_off = L.ctr + (size_t)(n + L.max_ncb) * 4;
+    wgn::BwdArgs &a = h->a;
+    std::memset(&a, 0, sizeof a);
+    a.layers = (const BwdLayer *)(ws + L.descs);
+    a.n = n;
+    a.B = batch;
+    a.y = (const uint16_t *)last.y;
+    a.y_stride = batch > 1 ? last.y_stride : last.N;
+    a.g_out = (const uint16_t *)g_out;
+    a.g_stride = batch > 1 ? g_stride : last.N;
+    a.g_in = (uint16_t *)g_in;
+    a.gin_stride = batch > 1 ? gin_stride : stages[0].K;
+    a.part = (float *)(ws + L.part);
+    a.done = (uint32_t *)(ws + L.ctr);
+    a.tickets = a.done + n;
+    a.err = a.tickets + L.max_ncb;
+    a.wait_ticks = WAIT_TICKS;
+    *out = h;
+    return WGN_OK;
+}
+
+wgn_status wgn_backward_run(const wgn_backward *h, int32_t prefetch, wgn_stream stream) {
+    if (!h || (prefetch != 0 && prefetch != 1)) return WGN_E_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    wgn::BwdArgs a = h->a;
+    a.prefetch = prefetch;
+    if (note(wgn::launch_bwd_prep(a.layers, h->n, h->B, a.done, h->nctr, s), "backward prep launch") != hipSuccess ||
+        note(wgn::launch_bwd(a, h->G, s), "backward launch") != hipSuccess)
+        return WGN_E_HIP;
+    return WGN_OK;
+}
+
+wgn_status wgn_backward_check(const wgn_backward *h, wgn_stream stream) {
+    if (!h) return WGN_E_ARG;
+    if (note(hipStreamSynchronize((hipStream_t)stream), "backward check sync") != hipSuccess) return WGN_E_HIP;
+    uint32_t err = 0;
+    if (note(hipMemcpy(&err, (const char *)h->ws + h->err_off, 4, hipMemcpyDeviceToHost), "backward check read") !=
+        hipSuccess)
+        return WGN_E_HIP;
+    return err ? WGN_E_TIMEOUT : WGN_OK;
+}
+
+wgn_status wgn_backward_set_wait_us(wgn_backward *h, int64_t us) {
+    if (!h) return WGN_E_ARG;
+    if (us > (int64_t)(WAIT_TICKS / 100) * 1000) return WGN_E_ARG;
+    h->a.wait_ticks = us < 0 ? WAIT_TICKS : (uint64_t)us * 100u;  // the real-time clock runs at 100 MHz
+    return WGN_OK;
+}
+
+int32_t wgn_backward_grid(const wgn_backward *h) { return h ? h->G : -1; }
+
+void wgn_backward_destroy(wgn_backward *h) { delete h; }
+
+wgn_status wgn_chain_backward(const wgn_stage *stages, int32_t n, int32_t batch, const wgn_grad *grads,
+                              const void *g_out, int64_t g_stride, void *g_in, int64_t gin_stride, int32_t prefetch,
+                              void *workspace, size_t ws_bytes, wgn_stream stream) {
+    if (prefetch != 0 && prefetch != 1) return WGN_E_ARG;
+    wgn_backward *h = nullptr;
+    wgn_status st = wgn_backward_create(stages, n, batch, grads, g_out, g_stride, g_in, gin_stride, workspace,
+                                        ws_bytes, stream, &h);
+    if (st != WGN_OK) return st;
+    st = wgn_backward_run(h, prefetch, stream);
+    wgn_backward_destroy(h);
+    return st;
 }
 
 }  // extern "C"

@@ -248,8 +248,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmLaunch G) {
                 if (n >= a.N) continue;
                 const float z = acc[0][ct][r] + (a.bias ? bf2f(a.bias[n]) : 0.0f);
                 float e;
-                if (a.epi == EPI_GELU_TANH) e = gelu_tanh(z);
-                else if (a.epi == EPI_SWIGLU) e = silu(z) * acc[P - 1][ct][r];
+                if (a.epi == EPI_GELU_TANH) {
+                    e = gelu_tanh(z);
+                    if (a.logits) a.logits[(int64_t)b * a.N + n] = z;  // pre-activation for the backward pass
+                } else if (a.epi == EPI_SWIGLU) e = silu(z) * acc[P - 1][ct][r];
                 else e = z;
                 if (a.residual) e += bf2f(a.residual[(int64_t)b * a.res_stride + n]);
                 y[(int64_t)b * a.y_stride + n] = f2bf(e);
@@ -305,18 +307,6 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmLaunch G) {
         ((int32_t *)a.y)[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
         if (a.maxval) a.maxval[b] = unorderable((uint32_t)(key >> 32));
     }
-}
-
-// FP64 -> BF16, round to nearest even, in two steps that round once: to FP32
-// with round-to-odd (an inexact result keeps an odd last bit, so it can never
-// sit on a BF16 tie), then FP32 -> BF16 to nearest even (v_cvt_pk_bf16_f32).
-// FP32 carries 16 more bits than BF16, so the result equals rounding the FP64
-// value directly (round-to-odd, Boldo and Melquiond).
-__device__ __forceinline__ uint16_t f64_to_bf16(double d) {
-    const float f = (float)d;
-    uint32_t b = __float_as_uint(f);
-    if ((double)f != d && (b & 1u) == 0u) b += fabs((double)f) < fabs(d) ? 1u : 0xFFFFFFFFu;
-    return f2bf(__uint_as_float(b));
 }
 
 // Sum of one value per thread over the workgroup (FP64): waves, then LDS.

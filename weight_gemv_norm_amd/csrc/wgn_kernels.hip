@@ -1109,7 +1109,13 @@ __device__ __forceinline__ void epilogue(const KArgs &a, const RunHdr &h, const 
         const float *ep = epi + (size_t)(r.rp_base + i * r.parts) * epi_rec(nb);
         const float z = acc[0] + (r.bias ? ep[0] : 0.0f);
         float e;
-        if (epi_kind == EPI_GELU_TANH) e = gelu_tanh(z);
+        if (epi_kind == EPI_GELU_TANH) {
+            e = gelu_tanh(z);
+            // the pre-activation, kept for the backward pass of the GELU
+            if (r.logits)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z), rsrc_of(r.logits),
+                                                      (int)(((int64_t)b * r.N + n) * 4), 0, COH);
+        }
         else if (epi_kind == EPI_SWIGLU) e = silu(z) * acc[1];
         else e = z;
         if (r.residual) e += ep[1 + b];

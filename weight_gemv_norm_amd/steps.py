@@ -199,20 +199,107 @@ class BatchedStep:
         return g
 
 
-def ln_gelu_chain_stages(inp: Dict, device):
-    """Stages of the LayerNorm -> Linear -> GELU-tanh chain.  Returns (stages, buffers)."""
+def ln_gelu_chain_stages(inp: Dict, device, keep_pre: bool = False):
+    """Stages of the LayerNorm -> Linear -> GELU-tanh chain.  Returns (stages,
+    buffers); keep_pre: each stage also keeps its FP32 pre-activation (for
+    the backward pass) in buffers["pre"]."""
     B = inp["batch"]
     eps = inp["eps"]
     x = inp["x"]
     outs = [x]
+    pres = []
     stages = []
     for L in inp["layers"]:
-        y = alloc(B, L["W"].shape[0], device)
-        stages.append(make_stage(L["W"], x, y, norm=NORM_LAYER, eps=eps, gamma=L["gamma"], beta=L["beta"],
-                                 bias=L["bias"], epi=EPI_GELU_TANH))
+        N = L["W"].shape[0]
+        y = alloc(B, N, device)
+        pre = alloc(B, N, device, torch.float32) if keep_pre else None
+        stages.append(make_stage(L["W"], x, y, norm=NORM_LAYER, eps=eps, gamma=L.get("gamma"), beta=L.get("beta"),
+                                 bias=L.get("bias"), epi=EPI_GELU_TANH, pre=pre))
         outs.append(y)
+        pres.append(pre)
         x = y
-    return stages, {"x": outs}
+    return stages, {"x": outs, "pre": pres}
+
+
+class TrainStep:
+    """One small-batch training step of the LayerNorm -> Linear -> GELU chain:
+    the forward chain (keeping each block's pre-activation), then the backward
+    pass from the gradient of the mean of the squared output, last block first
+    ("Making small PyTorch ops faster on a laptop GPU", section "It works in
+    training too": the example step's loss is the mean of the squared output,
+    and the backward fetches the weights of block i-1 while block i runs).
+    The parameter gradients land in self.grads[i] (gW, gb, ggamma, gbeta);
+    keep=True also keeps each block's output gradient gy and pre-activation
+    gradient gz, and the chain-input gradient g_in."""
+
+    def __init__(self, inp: Dict, device, prefetch: bool = True, keep: bool = True, g_out=None):
+        from .api import Backward, Chain, make_grad
+        self.inp, self.B, self.prefetch = inp, inp["batch"], prefetch
+        self.stages, self.bufs = ln_gelu_chain_stages(inp, device, keep_pre=True)
+        self.fwd = Chain(self.stages, self.B)
+        self.grads = []
+        gstructs = []
+        for L in inp["layers"]:
+            N, K = L["W"].shape
+            g = {"gW": torch.empty((N, K), dtype=torch.bfloat16, device=device)}
+            if L.get("bias") is not None:
+                g["gb"] = torch.empty(N, dtype=torch.bfloat16, device=device)
+            if L.get("gamma") is not None:
+                g["ggamma"] = torch.empty(K, dtype=torch.bfloat16, device=device)
+            if L.get("beta") is not None:
+                g["gbeta"] = torch.empty(K, dtype=torch.bfloat16, device=device)
+            if keep:
+                g["gy"] = alloc(self.B, N, device)
+                g["gz"] = alloc(self.B, N, device)
+            self.grads.append(g)
+            gstructs.append(make_grad(g["gW"], g.get("gb"), g.get("ggamma"), g.get("gbeta"), g.get("gy"),
+                                      g.get("gz")))
+        K0 = inp["layers"][0]["W"].shape[1]
+        self.g_in = alloc(self.B, K0, device) if keep else None
+        self.bwd = Backward(self.stages, self.B, gstructs, g_out=g_out, g_in=self.g_in, device=device)
+
+    def forward(self, stream=None) -> None:
+        self.fwd.run(stream)
+
+    def backward(self, stream=None) -> None:
+        self.bwd.run(self.prefetch, stream)
+
+    def run(self, stream=None) -> None:
+        self.forward(stream)
+        self.backward(stream)
+
+    def check(self) -> None:
+        self.fwd.check()
+        self.bwd.check()
+
+    def capture(self) -> "torch.cuda.CUDAGraph":
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.run(stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            self.run(stream=s)
+        torch.cuda.synchronize()
+        return g
+
+
+def train_step_bytes(inp: Dict) -> Dict[str, int]:
+    """Algorithmic bytes of one training step (forward + backward): every
+    weight read twice (forward product, backward product) and every weight
+    gradient written once dominate; activations, pre-activations and the
+    small parameter tensors are counted once per pass that moves them."""
+    B = inp["batch"]
+    w = sum(L["W"].numel() * 2 for L in inp["layers"])
+    small = act = 0
+    for L in inp["layers"]:
+        N, K = L["W"].shape
+        small += 2 * (2 * K + N) * 2                  # gamma, beta, bias read; their gradients written
+        act += B * (K * 2 + N * 2 + N * 4) * 2        # x and y (BF16) and z (FP32): forward writes, backward reads
+    return {"weights_fwd": w, "weights_bwd": w, "weight_grads": w, "small": small, "activations": act,
+            "total": 3 * w + small + act}
 
 
 def decode_step_bytes(inp: Dict) -> Dict[str, int]:
