@@ -34,7 +34,7 @@ def parse():
                     choices=["decode_step_1536x28", "decoder_block_1536", "ln_gelu_chain_768x72",
                              "rmsnorm_gemv_256", "rmsnorm_rows_960x1536_f16", "lmhead_151936",
                              "decode_attention_12q2kv128", "decode_step_attn_1536x28",
-                             "gemv_int4_lmhead_151936"])
+                             "gemv_int4_lmhead_151936", "ln_gelu_train_768x72"])
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None,
                     help="decode-step workload: number of decoder blocks (default 28)")
@@ -60,6 +60,11 @@ def parse():
                          "decode step with attention: cache slots (default 1024, the new token at slot 960)")
     ap.add_argument("--cold", action="store_true",
                     help="read a 512 MB scrub buffer between timed steps (evicts the Infinity Cache)")
+    ap.add_argument("--bwd-prefetch", default="off", choices=["on", "off"],
+                    help="training-step workload: the prefetch setting of the timed steps (both are "
+                         "compared in an interleaved A/B pass after the timing)")
+    ap.add_argument("--ab-rounds", type=int, default=20,
+                    help="training-step workload: rounds of the prefetch on/off comparison")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the measured streaming-read ceiling (a 2 GiB plain read, a few configurations)")
     return ap.parse_args()
@@ -83,7 +88,7 @@ def main():
     dev = "cuda"
     torch.cuda.set_device(0)
     wl = args.workload
-    B = args.batch if args.batch is not None else (4 if wl == "ln_gelu_chain_768x72" else 1)
+    B = args.batch if args.batch is not None else (4 if wl in ("ln_gelu_chain_768x72", "ln_gelu_train_768x72") else 1)
     print("[bench] workload %s batch %d mode %d" % (wl, B, args.mode), file=sys.stderr, flush=True)
 
     # ----------------------------------------------------------- build work
@@ -161,6 +166,29 @@ def main():
         cfg.update({"width": 768, "blocks": 72, "algorithmic_bytes": nbytes, "phases": chain.num_phases,
                     "launch": "persistent" if args.mode == 0 else "per-phase"})
         launch = chain.run
+    elif wl == "ln_gelu_train_768x72":
+        # one small-batch training step of the LayerNorm chain: forward (keeping
+        # pre-activations), gradient of the mean-square loss, backward pass
+        inp = gen.make_stage_tensors("ln_gelu_chain_768x72", device=dev, batch=B, n_layers=args.layers,
+                                     seeded_ln_params=True)
+        tstep = steps.TrainStep(inp, dev, prefetch=args.bwd_prefetch == "on", keep=False)  # noqa: E501
+        tb = steps.train_step_bytes(inp)
+        nbytes = tb["total"]
+        bwd_bytes = tb["weights_bwd"] + tb["weight_grads"] + tb["small"] // 2 + tb["activations"] // 2
+        n_blocks = len(inp["layers"])
+        cfg.update({"width": 768, "blocks": n_blocks, "algorithmic_bytes": nbytes, "bytes": tb,
+                    "backward_bytes": bwd_bytes, "loss": "mean of the squared chain output",
+                    "launch": "forward chain + backward prep + backward, one HIP graph",
+                    "launches_per_step": 3, "prefetch": args.bwd_prefetch,
+                    "backward_grid": tstep.bwd.grid, "forward_phases": tstep.fwd.num_phases})
+        kernel_name = "bwd_kernel"
+        tstep.prefetch = True
+        g_on = tstep.capture()
+        tstep.prefetch = False
+        g_off = tstep.capture()
+        tstep.prefetch = args.bwd_prefetch == "on"
+        launch = g_on.replay if tstep.prefetch else g_off.replay
+        cfg["graph"] = True
     elif wl == "rmsnorm_gemv_256":
         t = gen.make_stage_tensors(wl, device=dev, batch=B)
         y = torch.empty((B, 256), dtype=torch.bfloat16, device=dev)
@@ -265,6 +293,8 @@ def main():
     wall1 = time.perf_counter()
     if chain is not None:
         chain.check()
+    if wl == "ln_gelu_train_768x72":
+        tstep.check()
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e3  # us
     total_ms = t_all0.elapsed_time(t_all1)
     # one timing basis for value, ms_per_step and the roofline: the events
@@ -289,11 +319,23 @@ def main():
     # unit is the whole step: its traffic is recorded per step)
     launches = 1 if kernel_name == "gemm_kernel" else cfg.get("launches_per_step", 1)
     l_mean, l_med = us_step / launches, us_med / launches
-    l_gbs = nbytes / launches / (l_mean * 1e-6) / 1e9
+    l_bytes = nbytes // launches
+    if wl == "ln_gelu_train_768x72":
+        # the dominant kernel is the backward launch: timed on its own stream
+        # (prep + backward, eager) with events around each call
+        train_ab = train_prefetch_ab(tstep, g_on, g_off, torch, args.ab_rounds, scrub, scrub_sink, W)
+        cfg["prefetch_ab"] = train_ab
+        l_mean, l_med = train_ab["backward_us_mean"], train_ab["backward_us_median"]
+        l_bytes = bwd_bytes
+    l_gbs = l_bytes / (l_mean * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": kernel_name, "achieved": round(l_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(l_gbs / HBM_PEAK_GBS, 4),
                 "traffic": recorded_traffic(wl, B, kernel_name), "launch_us_mean": round(l_mean, 3),
-                "launch_us_median": round(l_med, 3), "bytes_per_launch": nbytes // launches}
+                "launch_us_median": round(l_med, 3), "bytes_per_launch": l_bytes}
+    if wl == "ln_gelu_train_768x72":
+        roofline["timed"] = "bwd_prep_kernel + bwd_kernel, back to back on one stream"
+        roofline["bytes_per_launch_basis"] = ("backward: every weight read once, every weight gradient written "
+                                              "once, block inputs and pre-activations read, small parameters")
     if ceiling is not None:
         roofline["measured_read_ceiling"] = round(ceiling["gbs"], 1)
         roofline["frac_of_measured_ceiling"] = round(l_gbs / ceiling["gbs"], 4)
@@ -304,11 +346,16 @@ def main():
         cpu = cpu_baseline_decode(inp, bufs, nbytes)
     elif not args.no_cpu_baseline and wl == "decode_attention_12q2kv128":
         cpu = cpu_baseline_attention(att, cfg["bytes_per_launch"])
+    elif not args.no_cpu_baseline and wl == "ln_gelu_train_768x72":
+        cpu = cpu_baseline_train(inp, tstep, nbytes)
 
     out = {
         "metric": METRIC if wl == "decode_step_1536x28" and B == 1 else METRIC.replace("batch 1", "batch %d" % B)
         if wl == "decode_step_1536x28" else ("decode attention GB/s (keys and values read once per step)"
-                                             if wl == "decode_attention_12q2kv128" else "%s weight-stream GB/s" % wl),
+                                             if wl == "decode_attention_12q2kv128" else
+                                             ("training step (forward + backward) GB/s of algorithmic bytes, "
+                                              "batch %d" % B if wl == "ln_gelu_train_768x72" else
+                                              "%s weight-stream GB/s" % wl)),
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -409,6 +456,7 @@ KERNEL_SOURCES = {
     "gemm_kernel": ("wgn_api.cpp", "wgn_gemm.hip", "wgn_gemm.h", "wgn_numerics.h", "wgn_prog.h"),
     "decode_attention_kernel": ("wgn_attn.h", "wgn_attn.hip"),
     "gemv_int4_kernel": ("wgn_int4.hip",),
+    "bwd_kernel": ("wgn_api.cpp", "wgn_bwd.hip", "wgn_bwd.h", "wgn_numerics.h"),
 }
 
 
@@ -416,7 +464,8 @@ def kernel_of(workload: str, batch: int = 1, path: int = 0) -> str:
     if workload in ("decode_step_1536x28", "decoder_block_1536") and (batch > 16 or path == 3):
         return "gemm_kernel"
     return {"decode_attention_12q2kv128": "decode_attention_kernel",
-            "gemv_int4_lmhead_151936": "gemv_int4_kernel"}.get(workload, "chain_kernel")
+            "gemv_int4_lmhead_151936": "gemv_int4_kernel",
+            "ln_gelu_train_768x72": "bwd_kernel"}.get(workload, "chain_kernel")
 
 
 def kernel_sources_digest(kernel: str = "chain_kernel") -> str:
@@ -561,6 +610,98 @@ def cpu_baseline_decode(inp, bufs, nbytes, budget_s=12.0, max_steps=45):
             "sample": "%d full decode steps (28 blocks + LM head + argmax, batch 1), free-running in the "
                       "binary64 C oracle with OpenMP over rows on %d threads (cores = threads used), then one "
                       "step on 1 thread; value = algorithmic bytes / mean step time" % (n, threads)}
+
+
+def train_prefetch_ab(ts, g_on, g_off, torch, rounds, scrub=None, scrub_sink=None, W=None, reps=10):
+    """Interleaved A/B of the training step with the backward prefetch on and
+    off (one HIP graph each), `rounds` rounds of `reps` replays per setting in
+    alternating order; then the backward alone (prep + backward launches,
+    eager) with events around each call, prefetch on.  Saving = 1 - on / off,
+    paired by round, with a 95 % confidence interval."""
+    on, off = [], []
+    for r in range(rounds):
+        order = ((g_on, on), (g_off, off)) if r % 2 == 0 else ((g_off, off), (g_on, on))
+        for g, acc in order:
+            ev = []
+            for _ in range(reps):
+                if scrub is not None:
+                    W.stream_read(scrub, 2048, 256, 1, scrub_sink)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+                ev.append((a, b))
+            torch.cuda.synchronize()
+            acc.append(float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3)
+    ts.check()
+    on, off = np.array(on), np.array(off)
+    sav = 1.0 - on / off
+    ci = ci95_mean(sav)
+    # the backward launches alone, on the stream they are launched on
+    st = torch.cuda.current_stream()
+    saved = ts.prefetch
+    res = {}
+    for pf in (True, False):
+        ts.prefetch = pf
+        per = []
+        for _ in range(rounds * 2):
+            ts.forward()
+            if scrub is not None:
+                W.stream_read(scrub, 2048, 256, 1, scrub_sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            ts.backward()
+            b.record(st)
+            torch.cuda.synchronize()
+            per.append(a.elapsed_time(b) * 1e3)
+        res[pf] = np.array(per)
+    ts.prefetch = saved
+    ts.check()
+    out = {"rounds": rounds, "replays_per_round": reps,
+           "step_us_prefetch_on": round(float(on.mean()), 3), "step_us_prefetch_off": round(float(off.mean()), 3),
+           "saving_pct": round(100.0 * float(sav.mean()), 3),
+           "saving_pct_ci95": [round(100.0 * ci[0], 3), round(100.0 * ci[1], 3)],
+           # the prefetch rule of the forward plans: kept only if the 95 % CI of
+           # the saving clears +1 %
+           "prefetch_kept": bool(100.0 * ci[0] > 1.0),
+           "backward_us_mean": round(float(res[True].mean()), 3),
+           "backward_us_median": round(float(np.median(res[True])), 3),
+           "backward_us_mean_prefetch_off": round(float(res[False].mean()), 3)}
+    print("[bench] prefetch A/B: %s" % out, file=sys.stderr, flush=True)
+    return out
+
+
+def cpu_baseline_train(inp, ts, nbytes, budget_s=12.0):
+    """The CPU oracle (as it stands) on a bounded sample of the training step:
+    the forward stage and the block backward of a few blocks (from the last
+    one down, on the GPU step's own activations), scaled to all blocks."""
+    from oracle import oracle as O
+    from synth.gen import bf16_bits_to_numpy as bb
+    threads = max(1, min(host_cpu()["usable_cpus"] or 1, 16))
+    O.set_threads(threads)
+    eps = float(np.float32(inp["eps"]))
+    layers = inp["layers"]
+    xs = [bb(x) for x in ts.bufs["x"]]
+    n = len(layers)
+    gy = O.mean_square_grad(xs[n])
+    t0 = time.perf_counter()
+    done = 0
+    for i in range(n - 1, -1, -1):
+        L = {k: bb(v) for k, v in layers[i].items()}
+        O.stage(xs[i], L["W"], norm=O.NORM_LAYER, eps=eps, gamma=L["gamma"], beta=L["beta"], bias=L["bias"],
+                epi=O.EPI_GELU_TANH)
+        r = O.block_backward(xs[i], L["W"], gy, gamma=L["gamma"], beta=L["beta"], eps=eps, bias=L["bias"])
+        gy = O.to_bf16_bits(r["gx"])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / done * n
+    print("[bench] cpu baseline: %d of %d blocks, %.3f s per step on %d threads" % (done, n, dt, threads),
+          file=sys.stderr, flush=True)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds_per_step": round(dt, 4), "host": host_cpu(),
+            "sample": "forward stage + block backward of %d of the %d blocks (last first), binary64 C oracle "
+                      "with OpenMP over rows on %d threads, scaled to the whole step" % (done, n, threads)}
 
 
 def cpu_baseline_attention(att, bytes_per_layer, budget_s=10.0, max_reps=200):

@@ -456,11 +456,21 @@ wgn_status wgn_backward_run(const wgn_backward *bw, int32_t prefetch, wgn_stream
 wgn_status wgn_backward_check(const wgn_backward *bw, wgn_stream stream);
 
 /* Bound of the in-kernel waits of later runs in microseconds (negative: the
- * default of 2 s; 0: a wait gives up at its first unsuccessful poll, so tests
- * can force the time-out path from the host).  WGN_E_ARG above the default. */
+ * default of 2 s; 0: every wait gives up at once, so tests can force the
+ * time-out path from the host).  WGN_E_ARG above the default. */
 wgn_status wgn_backward_set_wait_us(wgn_backward *bw, int64_t us);
 /* Workgroups of the persistent launch (all resident at once); -1 for NULL. */
 int32_t wgn_backward_grid(const wgn_backward *bw);
+/* Later runs record timestamps of the device's 100 MHz real-time clock into
+ * the device buffer (NULL stops): for block i and workgroup g, at
+ * buf[(i * grid + g) * WGN_BWD_TRACE_POINTS + p], of the workgroup's first
+ * tile of the block: p = 0 before the wait for block i+1, 1 wait over, 2 the
+ * tile's gz ready, 3 the tile's partial and row-sum shares stored, 4 the
+ * workgroup's flag for block i set, 5 its next tile's loads issued, 6 the
+ * tile's weight-gradient work done.  n_slots must cover n_stages x grid x
+ * WGN_BWD_TRACE_POINTS (WGN_E_ARG). */
+#define WGN_BWD_TRACE_POINTS 7
+wgn_status wgn_backward_set_trace(wgn_backward *bw, uint64_t *device_buf, size_t n_slots);
 void wgn_backward_destroy(wgn_backward *bw);
 
 /* create + run + destroy in one call (the create step synchronises `stream`). */

@@ -619,15 +619,19 @@ def call_backward(stages, grads, B, ws=None, ws_bytes=None, g_in=None, gin_strid
 
 
 def test_backward_workspace_layout():
-    """Per block: statistics, x-hat, gxh and column sums; one partial buffer of
-    the largest block; counters.  72 x 768 at batch 16 stays near 10 MB."""
+    """The block table (136 bytes a block), then per block: statistics and
+    x-hat; two partial buffers of the largest
+    block (64-row blocks) and two buffers of per-tile shares (by block
+    parity); one flag per tile of the largest block and the error word."""
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
     for B in (1, 4, 16):
         ar = Arena()
         st, _ = fake_train_chain(ar, B, 72)
         need = L.lib().wgn_backward_workspace_bytes(L.stage_array(st), 72, B)
-        per_layer = B * 768 * (2 + 4)
-        part = 24 * B * 768 * 4
-        assert per_layer * 72 + part < need < per_layer * 72 + part + 72 * 2048 + 72 * 128 + 65536, (B, need)
+        tiles = 12 * 12
+        want = (up(72 * 136) + 72 * (up(B * 8) + up(B * 768 * 2)) + 2 * (up(12 * B * 768 * 4) + up(tiles * B * 8))
+                + up((tiles + 4) * 4))
+        assert need == want, (B, need, want)
     ar = Arena()
     st, _ = fake_train_chain(ar, 17, 2)
     assert L.lib().wgn_backward_workspace_bytes(L.stage_array(st), 2, 17) == 0  # batch above 16

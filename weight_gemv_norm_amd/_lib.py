@@ -119,6 +119,7 @@ def lib() -> ctypes.CDLL:
         "wgn_backward_check": ([P, P], I32),
         "wgn_backward_set_wait_us": ([P, I64], I32),
         "wgn_backward_grid": ([P], I32),
+        "wgn_backward_set_trace": ([P, P, SZ], I32),
         "wgn_backward_destroy": ([P], None),
         "wgn_chain_backward": ([SP, I32, I32, ctypes.POINTER(Grad), P, I64, P, I64, I32, P, SZ, P], I32),
     }

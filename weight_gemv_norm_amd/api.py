@@ -440,6 +440,12 @@ class Backward:
     def grid(self) -> int:
         return int(L.lib().wgn_backward_grid(self._h))
 
+    def set_trace(self, buf: Optional[torch.Tensor]) -> None:
+        """Record per-block timestamps of later runs into buf (int64 device
+        tensor of n_stages x grid x 5 slots); None stops."""
+        L.check(L.lib().wgn_backward_set_trace(self._h, _ptr(buf), 0 if buf is None else buf.numel()),
+                "wgn_backward_set_trace")
+
     def close(self) -> None:
         if getattr(self, "_h", None):
             L.lib().wgn_backward_destroy(self._h)

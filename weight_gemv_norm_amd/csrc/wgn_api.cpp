@@ -2033,12 +2033,14 @@ namespace {
 using wgn::BwdLayer;
 
 // Offsets of one backward run's workspace: the layer table, per-layer
-// statistics, x-hat, gxh and column sums, the shared partial buffer, then
-// the counters (done per layer, tickets, error word).
+// statistics and x-hat, two partial buffers and two share buffers (by block
+// parity), then the counters: one flag per workgroup of the largest grid
+// (the device's resident workgroups, at most the largest block's tiles)
+// and the error word.
 struct BwdLayout {
-    std::vector<size_t> stats, xh, gxh, s12;
-    size_t descs = 0, part = 0, ctr = 0, total = 0;
-    int32_t max_ncb = 0, nctr = 0;
+    std::vector<size_t> stats, xh;
+    size_t descs = 0, part[2] = {0, 0}, q[2] = {0, 0}, ctr = 0, total = 0;
+    int32_t max_items = 0, nctr = 0;
 };
 
 inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -2068,21 +2070,22 @@ BwdLayout bwd_layout(const wgn_stage *stages, int32_t n, int32_t B) {
         const int32_t N = stages[i].N, K = stages[i].K;
         const int32_t nrb = (N + wgn::BWD_TILE_ROWS - 1) / wgn::BWD_TILE_ROWS;
         const int32_t ncb = (K + wgn::BWD_TILE_COLS - 1) / wgn::BWD_TILE_COLS;
-        L.max_ncb = std::max(L.max_ncb, ncb);
+        L.max_items = std::max(L.max_items, nrb * ncb);
         part = std::max(part, (size_t)nrb * B * K * 4);
         L.stats.push_back(o);
         o = up256(o + (size_t)B * 2 * 4);
         L.xh.push_back(o);
         o = up256(o + (size_t)B * K * 2);
-        L.gxh.push_back(o);
-        o = up256(o + (size_t)B * K * 4);
-        L.s12.push_back(o);
-        o = up256(o + (size_t)ncb * B * 2 * 4);
     }
-    L.part = o;
-    o = up256(o + part);
+    for (int p = 0; p < 2; ++p) {
+        L.part[p] = o;
+        o = up256(o + part);
+        L.q[p] = o;
+        o = up256(o + (size_t)L.max_items * B * 2 * 4);
+    }
     L.ctr = o;
-    L.nctr = n + L.max_ncb + 1;
+    // flags of every workgroup (rounded up to 4: the polls read 16 bytes), the error word
+    L.nctr = (L.max_items + 3) / 4 * 4 + 4;
     o = up256(o + (size_t)L.nctr * 4);
     L.total = o;
     return L;
@@ -2165,7 +2168,6 @@ wgn_status wgn_backward_create(const wgn_stage *stages, int32_t n, int32_t batch
 
     char *ws = (char *)workspace;
     std::vector<BwdLayer> img((size_t)n);
-    int32_t max_items = 0;
     for (int32_t i = 0; i < n; ++i) {
         const wgn_stage &s = stages[i];
         const wgn_grad &g = grads[i];
@@ -2184,15 +2186,12 @@ wgn_status wgn_backward_create(const wgn_stage *stages, int32_t n, int32_t batch
         b.gz = (uint16_t *)g.gz;
         b.stats = (float *)(ws + L.stats[(size_t)i]);
         b.xh = (uint16_t *)(ws + L.xh[(size_t)i]);
-        b.gxh = (float *)(ws + L.gxh[(size_t)i]);
-        b.s12 = (float *)(ws + L.s12[(size_t)i]);
         b.x_stride = batch > 1 ? s.x_stride : s.K;
         b.eps = s.eps;
         b.N = s.N;
         b.K = s.K;
         b.nrb = (s.N + wgn::BWD_TILE_ROWS - 1) / wgn::BWD_TILE_ROWS;
         b.ncb = (s.K + wgn::BWD_TILE_COLS - 1) / wgn::BWD_TILE_COLS;
-        max_items = std::max(max_items, b.nrb * b.ncb);
     }
     const int32_t resident = wgn::bwd_resident_grid();
     if (resident < 1) return WGN_E_HIP;
@@ -2205,11 +2204,11 @@ wgn_status wgn_backward_create(const wgn_stage *stages, int32_t n, int32_t batch
     if (!h) return WGN_E_HIP;
     h->n = n;
     h->B = batch;
-    h->G = std::min(max_items, resident);
+    h->G = std::min(L.max_items, resident);  // every workgroup resident at once
     h->ws = workspace;
     h->ctr_off = L.ctr;
     h->nctr = L.nctr;
-    h->err_off = L.ctr + (size_t)(n + L.max_ncb) * 4;
+    h->err_off = L.ctr + (size_t)(L.nctr - 4) * 4;
     wgn::BwdArgs &a = h->a;
     std::memset(&a, 0, sizeof a);
     a.layers = (const BwdLayer *)(ws + L.descs);
@@ -2221,10 +2220,13 @@ wgn_status wgn_backward_create(const wgn_stage *stages, int32_t n, int32_t batch
     a.g_stride = batch > 1 ? g_stride : last.N;
     a.g_in = (uint16_t *)g_in;
     a.gin_stride = batch > 1 ? gin_stride : stages[0].K;
-    a.part = (float *)(ws + L.part);
-    a.done = (uint32_t *)(ws + L.ctr);
-    a.tickets = a.done + n;
-    a.err = a.tickets + L.max_ncb;
+    for (int p = 0; p < 2; ++p) {
+        a.part[p] = (float *)(ws + L.part[p]);
+        a.q[p] = (float *)(ws + L.q[p]);
+    }
+    a.flags = (uint32_t *)(ws + L.ctr);
+    a.err = (uint32_t *)(ws + h->err_off);
+    a.tile_wgs = h->G;
     a.wait_ticks = WAIT_TICKS;
     *out = h;
     return WGN_OK;
@@ -2235,7 +2237,7 @@ wgn_status wgn_backward_run(const wgn_backward *h, int32_t prefetch, wgn_stream 
     hipStream_t s = (hipStream_t)stream;
     wgn::BwdArgs a = h->a;
     a.prefetch = prefetch;
-    if (note(wgn::launch_bwd_prep(a.layers, h->n, h->B, a.done, h->nctr, s), "backward prep launch") != hipSuccess ||
+    if (note(wgn::launch_bwd_prep(a.layers, h->n, h->B, a.flags, h->nctr, s), "backward prep launch") != hipSuccess ||
         note(wgn::launch_bwd(a, h->G, s), "backward launch") != hipSuccess)
         return WGN_E_HIP;
     return WGN_OK;
@@ -2259,6 +2261,14 @@ wgn_status wgn_backward_set_wait_us(wgn_backward *h, int64_t us) {
 }
 
 int32_t wgn_backward_grid(const wgn_backward *h) { return h ? h->G : -1; }
+
+wgn_status wgn_backward_set_trace(wgn_backward *h, uint64_t *device_buf, size_t n_slots) {
+    if (!h) return WGN_E_ARG;
+    if (device_buf && n_slots < (size_t)h->n * h->G * wgn::BWD_TRACE_POINTS) return WGN_E_ARG;
+    if (device_buf && (reinterpret_cast<uintptr_t>(device_buf) & 7u)) return WGN_E_ALIGN;
+    h->a.trace = device_buf;
+    return WGN_OK;
+}
 
 void wgn_backward_destroy(wgn_backward *h) { delete h; }
 

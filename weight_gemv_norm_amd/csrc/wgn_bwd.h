@@ -8,7 +8,7 @@
 namespace wgn {
 
 constexpr int BWD_MAX_BATCH = 16;
-constexpr int BWD_TILE_ROWS = 32;     // weight rows of one item (8 per wave)
+constexpr int BWD_TILE_ROWS = 64;     // weight rows of one item (16 per wave)
 constexpr int BWD_TILE_COLS = 64;     // weight columns of one item (16 bytes per thread)
 constexpr int BWD_THREADS = 256;
 constexpr int BWD_MAX_LAYERS = 4096;
@@ -30,8 +30,6 @@ struct BwdLayer {
     // workspace
     float *stats;            // [B][2]: mean and 1 / sigma of the input rows
     uint16_t *xh;            // [B][K] BF16 x-hat
-    float *gxh;              // [B][K] FP32 gradient of x-hat (final, column-block finishers)
-    float *s12;              // [ncb][B][2] column-block sums of gamma gxh and gamma gxh u
     int64_t x_stride;
     float eps;
     int32_t N, K, nrb, ncb;  // row blocks of BWD_TILE_ROWS, column blocks of BWD_TILE_COLS
@@ -46,13 +44,20 @@ struct BwdArgs {
     int64_t g_stride;
     uint16_t *g_in;          // [B][gin_stride] gradient of the chain input, or null
     int64_t gin_stride;
-    float *part;             // [max nrb][B][max K] row-block partials of gxh (shared by the layers)
-    uint32_t *tickets;       // [max ncb] (zero at launch; the last arrival resets its own)
-    uint32_t *done;          // [n] finished column blocks per layer (zero at launch)
+    float *part[2];          // [max nrb][B][max K] row-block partials of gxh, by block parity
+    float *q[2];             // [max tiles][B][2] per-tile shares of the LayerNorm row sums, by block parity
+    uint32_t *flags;         // [tile_wgs]: blocks each workgroup is done with (zero at launch)
     uint32_t *err;           // set to 1 when a bounded wait gives up
     uint64_t wait_ticks;
+    uint64_t *trace;         // null, or [n][grid][BWD_TRACE_POINTS] real-time clock stamps
+    int32_t tile_wgs;        // the grid
     int32_t prefetch;        // 1: issue the next layer's weight loads before waiting for it
 };
+// Trace points of a workgroup's first tile of each block: 0 before the wait
+// for the following block, 1 wait over, 2 gz of the tile ready, 3 the tile's
+// partial and shares stored, 4 the workgroup's flag for the block set, 5 the
+// next tile's loads issued, 6 the tile's weight-gradient work done.
+constexpr int BWD_TRACE_POINTS = 7;
 
 // Statistics and x-hat of every block input; also clears nzero counter words.
 hipError_t launch_bwd_prep(const BwdLayer *layers, int32_t n, int32_t B, uint32_t *zero, int32_t nzero,

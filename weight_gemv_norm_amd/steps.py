@@ -230,9 +230,12 @@ class TrainStep:
     and the backward fetches the weights of block i-1 while block i runs).
     The parameter gradients land in self.grads[i] (gW, gb, ggamma, gbeta);
     keep=True also keeps each block's output gradient gy and pre-activation
-    gradient gz, and the chain-input gradient g_in."""
+    gradient gz, and the chain-input gradient g_in.  prefetch: the backward
+    requests each block's weight tiles before waiting for the block after it
+    (off by default: on this GPU it did not clear +1 % when measured; the
+    bench's A/B pass measures it on every run)."""
 
-    def __init__(self, inp: Dict, device, prefetch: bool = True, keep: bool = True, g_out=None):
+    def __init__(self, inp: Dict, device, prefetch: bool = False, keep: bool = True, g_out=None):
         from .api import Backward, Chain, make_grad
         self.inp, self.B, self.prefetch = inp, inp["batch"], prefetch
         self.stages, self.bufs = ln_gelu_chain_stages(inp, device, keep_pre=True)
