@@ -547,7 +547,9 @@ def summarize_pmc(fetch_csv, write_csv, out_txt, workload, batch, copy_mib, path
             f.write("#   rocprofv3 --pmc %s --output-format csv -d gpurun_out/pmc_%s -o run -- python bench.py "
                     "--workload %s --batch %d%s --steps 10 --warmup 3 --no-cpu-baseline --no-ceiling "
                     "--calib-copy-mib %d\n"
-                    % (c, c.lower(), workload, batch, " --path 3" if path == 3 else "", copy_mib))
+                    % (c, c.lower(), workload, batch,
+                       " --path 3" if path == 3 else (" --ab-rounds 2" if workload == "ln_gelu_train_768x72" else ""),
+                       copy_mib))
         f.write("# calibration: a plain device copy of %d MiB reads and writes %d KiB\n"
                 % (copy_mib, copy_mib * 1024))
         for c in ("FETCH_SIZE", "WRITE_SIZE"):

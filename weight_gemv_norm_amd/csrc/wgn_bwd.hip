@@ -54,7 +54,6 @@ constexpr int WROW = TC + 8;                  // LDS row of the weight tile: 16 
 
 static_assert(BWD_THREADS == 256 && TR == 64 && TC == 64 && NBM * 16 == BWD_THREADS,
               "thread layout of an item");
-constexpr int BWD_BLOCK = BWD_THREADS;
 
 // The block table is written by the host before the launch and only read
 // here: read through the constant address space, its fields come in with
@@ -99,13 +98,6 @@ __device__ __forceinline__ ItemData load_item(CLayer &L, int32_t B, int32_t item
     const int32_t r = item / L.ncb, c = item - r * L.ncb;
     const int32_t n0 = r * TR, k0 = c * TC;
     ItemData d;
-    if (t >= BWD_THREADS) {
-        d.w[0] = d.w[1] = (u32x4){0u, 0u, 0u, 0u};
-        d.z[0] = d.z[1] = d.z[2] = d.z[3] = 0.0f;
-        d.xh = d.xin = d.gam = (u32x2){0u, 0u};
-        d.mu = d.rs = 0.0f;
-        return d;
-    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int32_t n = n0 + (t >> 3) + 32 * h, k = k0 + 8 * (t & 7);
@@ -156,7 +148,7 @@ struct LnPre {
 __device__ LnPre gather_following(const BwdArgs &a, CLayer &U, int32_t ui, int32_t n0, Smem &sm) {
     const int32_t t = (int32_t)threadIdx.x, B = a.B;
     LnPre lp;
-    if (t < BWD_THREADS) {
+    {
         const int32_t n = n0 + (t & 63);
         lp.gam = (U.gamma && n < U.K) ? bf2f(U.gamma[n]) : 1.0f;
 #pragma unroll
@@ -170,7 +162,7 @@ __device__ LnPre gather_following(const BwdArgs &a, CLayer &U, int32_t ui, int32
     }
     const float *part = a.part[ui & 1];
     const float *q = a.q[ui & 1];
-    if (t < BWD_THREADS) {
+    {
         const int32_t b = t >> 4, kq = 4 * (t & 15), k = n0 + kq;
         f32x4 g = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
         if (b < B && k < U.K) {
@@ -186,7 +178,7 @@ __device__ LnPre gather_following(const BwdArgs &a, CLayer &U, int32_t ui, int32
         }
         *(f32x4 *)&sm.gx[b][kq] = g;
     }
-    if (t < BWD_THREADS) {
+    {
         const int32_t b = t & 15, grp = t >> 4, items = U.nrb * U.ncb;
         f32x2 s = (f32x2){0.0f, 0.0f};
         if (b < B) {
@@ -280,13 +272,10 @@ __device__ void run_a(const BwdArgs &a, CLayer &L, CLayer &U, bool last, int32_t
     const int32_t B = a.B, N = L.N, K = L.K;
     const int32_t r = item / L.ncb, c = item - r * L.ncb;
     const int32_t n0 = r * TR, k0 = c * TC;
-    const bool dt = t < BWD_THREADS;  // a data thread (not the control wave)
     __syncthreads();  // the previous item is done with the LDS
-    if (dt) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) *(u32x4 *)&sm.w[(t >> 3) + 32 * h][8 * (t & 7)] = d.w[h];
-        *(u32x2 *)&sm.xh[t >> 4][4 * (t & 15)] = d.xh;
-    }
+    for (int h = 0; h < 2; ++h) *(u32x4 *)&sm.w[(t >> 3) + 32 * h][8 * (t & 7)] = d.w[h];
+    *(u32x2 *)&sm.xh[t >> 4][4 * (t & 15)] = d.xh;
     LnPre lp;
     if (!last) lp = gather_following(a, U, li + 1, n0, sm);
     __syncthreads();
@@ -295,7 +284,7 @@ __device__ void run_a(const BwdArgs &a, CLayer &L, CLayer &U, bool last, int32_t
     // gradient also gxh u at these elements
     const int32_t rho = t & 63, n = n0 + rho;
 #pragma unroll
-    for (int h = 0; h < 4 && dt; ++h) {
+    for (int h = 0; h < 4; ++h) {
         const int32_t b = (t >> 6) + 4 * h;
         float gzv = 0.0f;
         if (b < B && n < N) {
@@ -327,9 +316,9 @@ __device__ void run_a(const BwdArgs &a, CLayer &L, CLayer &U, bool last, int32_t
     {
         const int32_t Bp = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : 16;
         const int32_t RG = 16 / Bp, RPG = TR / RG;
-        const int32_t kq = 4 * (t & 15), b = (t >> 4) & (Bp - 1), rg = dt ? (t >> 4) / Bp : -1;
+        const int32_t kq = 4 * (t & 15), b = (t >> 4) & (Bp - 1), rg = (t >> 4) / Bp;
         f32x4 p = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-        if (dt && b < B && k0 + kq < K) {
+        if (b < B && k0 + kq < K) {
             for (int32_t rr0 = rg * RPG; rr0 < (rg + 1) * RPG; rr0 += 4) {
                 const f32x4 g4 = *(const f32x4 *)&sm.gz[b][rr0];
                 u32x2 wv[4];
@@ -345,7 +334,7 @@ __device__ void run_a(const BwdArgs &a, CLayer &L, CLayer &U, bool last, int32_t
                 }
             }
         }
-        if (dt) *(f32x4 *)&sm.pr[t >> 4][kq] = p;
+        *(f32x4 *)&sm.pr[t >> 4][kq] = p;
         __syncthreads();
         if (rg == 0) {
             for (int32_t g2 = 1; g2 < RG; ++g2) p += *(const f32x4 *)&sm.pr[g2 * Bp + b][kq];
@@ -380,7 +369,6 @@ __device__ void run_a(const BwdArgs &a, CLayer &L, CLayer &U, bool last, int32_t
 // more of this than another.
 __device__ void run_b(const BwdArgs &a, CLayer &L, CLayer &U, bool last, int32_t item, Smem &sm) {
     const int32_t t = (int32_t)threadIdx.x;
-    if (t >= BWD_THREADS) return;  // no barrier below
     const int32_t B = a.B, N = L.N, K = L.K;
     const int32_t r = item / L.ncb, c = item - r * L.ncb;
     const int32_t n0 = r * TR, k0 = c * TC;
@@ -448,7 +436,7 @@ __device__ void run_b(const BwdArgs &a, CLayer &L, CLayer &U, bool last, int32_t
     }
 }
 
-__global__ __launch_bounds__(BWD_BLOCK) void bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdArgs a) {
     __shared__ __align__(16) Smem sm;
     const int32_t g = (int32_t)blockIdx.x, T = a.tile_wgs;
     ItemData cur;
@@ -513,7 +501,7 @@ __global__ __launch_bounds__(BWD_BLOCK) void bwd_kernel(BwdArgs a) {
         const LnPre lp = gather_following(a, L, 0, n0, sm);
         __syncthreads();
         const int32_t rho = t & 63, n = n0 + rho;
-        if (a.g_in && n < L.K && t < BWD_THREADS)
+        if (a.g_in && n < L.K)
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
                 const int32_t b = (t >> 6) + 4 * h;
@@ -621,7 +609,7 @@ hipError_t launch_bwd_prep(const BwdLayer *layers, int32_t n, int32_t B, uint32_
 
 hipError_t launch_bwd(const BwdArgs &a, int32_t grid, hipStream_t s) {
     if (grid < 1 || a.n < 1 || a.B < 1 || a.B > BWD_MAX_BATCH) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(bwd_kernel, dim3((unsigned)grid), dim3(BWD_BLOCK), 0, s, a);
+    hipLaunchKernelGGL(bwd_kernel, dim3((unsigned)grid), dim3(BWD_THREADS), 0, s, a);
     return hipGetLastError();
 }
 
@@ -629,7 +617,7 @@ int32_t bwd_resident_grid() {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_kernel, BWD_BLOCK, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_kernel, BWD_THREADS, 0) != hipSuccess) return 0;
     return cus * per;
 }
 
