@@ -985,6 +985,9 @@ bool gemm_plan(const wgn_stage *st, int32_t n, int32_t B, int32_t cus, GemmGroup
         const wgn_stage &s = st[i];
         if (s.epi == EPI_ARGMAX && s.bias) return false;
         if ((int64_t)s.N * s.K * 2 > 0x7FFFFFF0LL) return false;
+        // the input rows are read through a 32-bit buffer range too
+        const int64_t xs = s.norm != NORM_NONE ? s.K : (B > 1 ? s.x_stride : s.K);
+        if (((int64_t)(B - 1) * xs + s.K) * 2 > 0x7FFFFFF0LL) return false;
         tiles += (s.N + GEMM_TILE_ROWS - 1) / GEMM_TILE_ROWS;
         wbytes += (int64_t)s.N * s.K * 2 * P;
     }

@@ -9,14 +9,14 @@ namespace wgn {
 constexpr int GEMM_MAX_BATCH = 128;                      // batch rows of one call
 constexpr int GEMM_TILE_ROWS = 64;                       // output rows per item (16 per wave)
 constexpr int GEMM_THREADS = 256;                        // four waves
-constexpr int GEMM_KWIN = 128;                          // K elements per LDS window (4 steps of 32)
-constexpr int GEMM_ROW_PAD = 16;                         // bytes after each batch row of the window
+constexpr int GEMM_KWIN = 64;                            // K elements per window (2 steps of 32)
+constexpr int GEMM_RING = 4;                             // windows in the LDS ring (3 in flight)
 constexpr int GEMM_FRAG_BYTES = 64 * 16;                 // one wave's 16 x 16 FP32 accumulator tile
 
 // One call's work: items = ntiles x nslices; item i is row tile i / nslices
 // (rows 64 t ..) over K slice i % nslices (elements [s kslice, (s+1) kslice),
-// kslice a multiple of GEMM_KWIN), streamed through LDS windows of GEMM_KWIN
-// elements.  With nslices > 1 each item
+// kslice a multiple of GEMM_KWIN), streamed through a ring of LDS windows of
+// GEMM_KWIN elements.  With nslices > 1 each item
 // leaves its accumulators in part[] and the last item of a tile to finish
 // (tickets[tile]) adds the slices in slice order and applies the epilogue.
 struct GemmArgs {
@@ -46,11 +46,18 @@ struct GemmLaunch {
     int32_t n;
 };
 
-// LDS bytes of a call: two x-hat windows (the one being multiplied and the
-// next one being copied), the argmax merge area and a flag; at most
-// lds_cap(), so that two workgroups fit one compute unit's 160 KB.
+// A window of bpad = 16 nt batch rows is nt * 2 copies of 1 KB (8 rows of
+// GEMM_KWIN elements each), spread over the four waves; a ring slot holds
+// every wave's copies (the ones past the batch are never read).
+constexpr int gemm_copies_per_wave(int nt) { return (nt * 2 + 3) / 4; }
+constexpr uint32_t gemm_slot_bytes(int nt) { return (uint32_t)gemm_copies_per_wave(nt) * 4u * 1024u; }
+static_assert(GEMM_KWIN * 2 * 8 == 1024, "one copy is 8 batch rows of a window");
+
+// LDS bytes of a call: the ring of input windows (also the epilogue's
+// staging area), the argmax merge area and a flag; at most lds_cap(), so
+// that two workgroups fit one compute unit's 160 KB.
 inline size_t gemm_lds_bytes(int32_t bpad) {
-    return 2 * (size_t)bpad * ((size_t)GEMM_KWIN * 2 + GEMM_ROW_PAD) + (size_t)4 * GEMM_MAX_BATCH * 8 + 16;
+    return (size_t)GEMM_RING * gemm_slot_bytes((bpad + 15) / 16) + (size_t)4 * GEMM_MAX_BATCH * 8 + 16;
 }
 inline constexpr size_t lds_cap() { return 80 * 1024; }
 

@@ -58,6 +58,30 @@ __device__ __forceinline__ f32x4 mfma(const u32x4 &a, const u32x4 &b, const f32x
                                                    0, 0, 0);
 }
 
+#define GEMM_LAS __attribute__((address_space(3)))
+
+// Wait until at most N loads of this wave are in flight and its LDS accesses
+// are done (s_waitcnt: vmcnt in bits 3:0 and 15:14, lgkmcnt 0, expcnt left).
+template <int N>
+__device__ __forceinline__ void wait_vm_lds0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
+}
+// A buffer offset, or one past every buffer's range (reads as zero) when ok
+// is false: an OR with a mask rather than a choice between two offsets,
+// which the compiler would turn into two loads under complementary masks.
+__device__ __forceinline__ uint32_t oor_unless(bool ok, uint32_t off) {
+    return off | (((uint32_t)ok - 1u) & GEMM_OUT_OF_RANGE);
+}
+// Workgroup barrier without the memory fences of __syncthreads, whose
+// release would wait for every load in flight, LDS copies included; the
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Slices whose partial tiles are loaded together when a tile's slices are
 // added (one memory round trip per group).
 template <int NT, bool SWI>
@@ -74,8 +98,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmLaunch G) {
     const int32_t item = (int32_t)blockIdx.x - G.start[si];
     constexpr int P = SWI ? 2 : 1;                           // accumulator sets (gate and up)
     constexpr int MS = GEMM_KWIN / 32;                       // K steps per window
-    constexpr uint32_t RSTRIDE = GEMM_KWIN * 2 + GEMM_ROW_PAD;  // window row stride (bytes)
-    constexpr uint32_t BUFB = NT * 16 * RSTRIDE;             // one window
+    constexpr int D = GEMM_RING;                             // windows in flight
+    constexpr int XI = gemm_copies_per_wave(NT);             // 1 KB input copies per wave and window
+    constexpr uint32_t XB = gemm_slot_bytes(NT);             // one ring slot
+    constexpr int LPW = P * MS + XI;                         // loads per wave and window
+    constexpr uint32_t TSTRIDE = GEMM_TILE_ROWS * 4 + 16;    // epilogue staging: bytes per batch row
+    static_assert(NT * 16 * TSTRIDE <= D * XB, "the epilogue's staging fits the ring");
     const int32_t w = (int32_t)(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t q = lane >> 4, j = lane & 15u;
@@ -87,16 +115,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmLaunch G) {
     const int32_t k1 = min(a.K, k0 + a.kslice);
     const int32_t nwin = (k1 - k0 + GEMM_KWIN - 1) / GEMM_KWIN;
     const int32_t arow = n0 + 16 * w + (int32_t)j;  // weight row of this lane's A fragments
-    char *buf0 = lds, *buf1 = lds + BUFB;
-    const size_t merge_off = 2 * (size_t)BUFB;       // argmax merge area, then the last-item flag
+    const size_t merge_off = (size_t)D * XB;          // argmax merge area, then the last-item flag
     int32_t *s_last = (int32_t *)(lds + merge_off + 4 * GEMM_MAX_BATCH * 8);
     const uint32_t wbytes = (uint32_t)((int64_t)a.N * a.K * 2);
     const __amdgpu_buffer_rsrc_t rw = grsrc(a.W, wbytes);
     const __amdgpu_buffer_rsrc_t ru = grsrc(SWI ? a.W_up : a.W, wbytes);
-    // this thread's share of a window's x-hat copy: 16-byte chunk xc of batch
-    // rows xr0, xr0 + 16, ... (one row per 16 threads)
-    const int32_t xr0 = (int32_t)(threadIdx.x >> 4), xc = (int32_t)(threadIdx.x & 15u);
-
+    const __amdgpu_buffer_rsrc_t rx = grsrc(a.x, (uint32_t)(((int64_t)(a.B - 1) * a.x_stride + a.K) * 2));
     f32x4 acc[P][NT];
 #pragma unroll
     for (int p = 0; p < P; ++p)
@@ -104,75 +128,74 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmLaunch G) {
         for (int ct = 0; ct < NT; ++ct) acc[p][ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
     // weight fragments of the window at kw: row arow, K offset kw + 32 t + 8 q
+    // (past the slice, or for a window after the last, the loads read zero)
     auto load_w = [&](int32_t kw, u32x4 (&wa)[P][MS]) {
 #pragma unroll
         for (int t = 0; t < MS; ++t) {
             const int32_t k = kw + 32 * t + 8 * (int32_t)q;
-            const uint32_t off = (arow < a.N && k < k1) ? (uint32_t)(((int64_t)arow * a.K + k) * 2)
-                                                        : GEMM_OUT_OF_RANGE;  // reads as zero
+            const uint32_t off = oor_unless(arow < a.N && k < k1, (uint32_t)(((int64_t)arow * a.K + k) * 2));
             wa[0][t] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, GEMM_WEIGHT_AUX);
             if constexpr (SWI) wa[P - 1][t] = __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, GEMM_WEIGHT_AUX);
         }
     };
-    // this thread's x-hat chunks of the window at kw (zero past the slice or the batch)
-    auto load_x = [&](int32_t kw, u32x4 (&xv)[NT]) {
-        const int32_t k = kw + 8 * xc;
+    // The input window at kw, copied into a ring slot by LDS-DMA loads: 1 KB
+    // copies m = w, w + 4, ... of 8 batch rows each.  Batch row r sits at
+    // r * 128 bytes with its 16-byte chunk c in place c ^ ((r >> 1) & 7), so
+    // that the 16 rows one read instruction touches fall in different banks.
+    // A chunk past the slice takes the slice's first chunk instead (finite
+    // input against a zero weight); rows past the batch and windows after the
+    // last are left out of range (no memory traffic; those columns and
+    // windows are never used).
+    auto issue_x = [&](int32_t kw, char *slot) {
 #pragma unroll
-        for (int c = 0; c < NT; ++c) {
-            const int32_t b = xr0 + 16 * c;
-            xv[c] = (b < a.B && k < k1) ? *(const u32x4 *)(a.x + (int64_t)b * a.x_stride + k)
-                                        : (u32x4){0u, 0u, 0u, 0u};
+        for (int e = 0; e < XI; ++e) {
+            const int32_t m = w + 4 * e;
+            const int32_t row = 8 * m + (int32_t)(lane >> 3);
+            const int32_t k = kw + 8 * ((int32_t)(lane & 7u) ^ ((4 * m + (int32_t)(lane >> 4)) & 7));
+            const uint32_t off = oor_unless(row < a.B, (uint32_t)(((int64_t)row * a.x_stride + (k < k1 ? k : k0)) * 2));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (GEMM_LAS void *)(slot + m * 1024), 16, off, 0, 0, 0);
         }
     };
-    auto store_x = [&](char *buf, const u32x4 (&xv)[NT]) {
-#pragma unroll
-        for (int c = 0; c < NT; ++c)
-            *(u32x4 *)(buf + (uint32_t)(xr0 + 16 * c) * RSTRIDE + (uint32_t)xc * 16u) = xv[c];
-    };
-    // the window's products: B operand = batch row 16 ct + j at K offset 32 t + 8 q
-    auto compute = [&](const char *buf, const u32x4 (&wa)[P][MS]) {
-        const char *xb = buf + j * RSTRIDE + q * 16u;
+    // the window's products: B operand = batch row 16 ct + j, chunk 4 t + q
+    auto compute = [&](const char *slot, const u32x4 (&wa)[P][MS]) {
 #pragma unroll
         for (int t = 0; t < MS; ++t)
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) {
-                const u32x4 xv = *(const u32x4 *)(xb + (uint32_t)ct * 16u * RSTRIDE + (uint32_t)t * 64u);
+                const u32x4 xv = *(const u32x4 *)(slot + (uint32_t)ct * 2048u + j * 128u +
+                                                  ((((uint32_t)(4 * t) + q) ^ (j >> 1)) << 4));
 #pragma unroll
                 for (int p = 0; p < P; ++p) acc[p][ct] = mfma(wa[p][t], xv, acc[p][ct]);
             }
     };
 
-    // Two-stage pipeline over the slice's windows: while window i is
-    // multiplied from one LDS buffer, window i + 1's weights are in flight to
-    // registers and its x-hat to the other buffer.  Windows alternate between
-    // the two register sets and buffers (unrolled by two, so that no register
-    // array is indexed at run time).
-    u32x4 wa0[P][MS], wa1[P][MS], xv[NT];
-    if (nwin > 0) {
-        load_w(k0, wa0);
-        load_x(k0, xv);
-        store_x(buf0, xv);
+    // Ring of GEMM_RING windows: window i is multiplied from slot i % RING
+    // and register set i % RING while windows i + 1 .. i + RING - 1 are in
+    // flight.  Every step issues the same loads (out of range past the
+    // slice), so a fixed count of outstanding loads marks window i as landed;
+    // each wave waits for its own copies, then the barrier makes every wave's
+    // copies visible and frees the slot of window i - 1 for window
+    // i + RING - 1.  Unrolled by RING, so that no register array is indexed
+    // at run time.
+    u32x4 wa[D][P][MS];
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) {
+        load_w(k0 + d * GEMM_KWIN, wa[d]);
+        issue_x(k0 + d * GEMM_KWIN, lds + d * XB);
+        asm volatile("" ::: "memory");  // windows issued in order: the count above relies on it
     }
-    __syncthreads();
-    for (int32_t i = 0; i < nwin; i += 2) {
-        const bool more1 = i + 1 < nwin;
-        if (more1) {
-            load_w(k0 + (i + 1) * GEMM_KWIN, wa1);
-            load_x(k0 + (i + 1) * GEMM_KWIN, xv);
+    for (int32_t i = 0; i < nwin; i += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            wait_vm_lds0<(D - 2) * LPW>();
+            ring_barrier();
+            const int32_t kn = k0 + (i + d + D - 1) * GEMM_KWIN;
+            load_w(kn, wa[(d + D - 1) % D]);
+            issue_x(kn, lds + ((d + D - 1) % D) * XB);
+            compute(lds + d * XB, wa[d]);
         }
-        compute(buf0, wa0);
-        if (more1) store_x(buf1, xv);
-        __syncthreads();  // window i + 1 is in buf1; every wave is done with buf0
-        if (!more1) break;
-        const bool more2 = i + 2 < nwin;
-        if (more2) {
-            load_w(k0 + (i + 2) * GEMM_KWIN, wa0);
-            load_x(k0 + (i + 2) * GEMM_KWIN, xv);
-        }
-        compute(buf1, wa1);
-        if (more2) store_x(buf0, xv);
-        __syncthreads();
     }
+    __builtin_amdgcn_s_waitcnt(0);  // the ring's copies past the last window have landed: LDS is free after a barrier
 
     if (S > 1) {
         // this item's accumulators, then the tile's ticket
@@ -235,26 +258,66 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmLaunch G) {
     }
 
     // ------------------------------------------------------------ epilogue
-    // lane: rows n0 + 16 w + 4 q + r (r = 0..3) of batch rows 16 ct + j
+    // lane: rows n0 + 16 w + 4 q + r (r = 0..3) of batch rows 16 ct + j.
+    // The activated tile goes through LDS (a window buffer, free now) so
+    // that the residual is read and the output written in 16-byte chunks of
+    // 8 consecutive rows of one batch row: the fragment layout would make
+    // every store instruction touch 16 batch rows with 2-byte writes.
     if (a.epi != EPI_ARGMAX) {
-        uint16_t *y = (uint16_t *)a.y;
+        __syncthreads();  // every wave is done with the window buffers
+        float *tb = (float *)lds;  // [16 NT batch rows][64 rows], row stride TSTRIDE bytes
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
-            const int32_t b = ct * 16 + (int32_t)j;
-            if (b >= a.B) continue;
+            f32x4 e4;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int32_t n = n0 + 16 * w + 4 * (int32_t)q + r;
-                if (n >= a.N) continue;
-                const float z = acc[0][ct][r] + (a.bias ? bf2f(a.bias[n]) : 0.0f);
+                const float z = acc[0][ct][r] + ((a.bias && n < a.N) ? bf2f(a.bias[n]) : 0.0f);
                 float e;
                 if (a.epi == EPI_GELU_TANH) {
                     e = gelu_tanh(z);
-                    if (a.logits) a.logits[(int64_t)b * a.N + n] = z;  // pre-activation for the backward pass
+                    const int32_t b = ct * 16 + (int32_t)j;
+                    if (a.logits && n < a.N && b < a.B)
+                        a.logits[(int64_t)b * a.N + n] = z;  // pre-activation for the backward pass
                 } else if (a.epi == EPI_SWIGLU) e = silu(z) * acc[P - 1][ct][r];
                 else e = z;
-                if (a.residual) e += bf2f(a.residual[(int64_t)b * a.res_stride + n]);
-                y[(int64_t)b * a.y_stride + n] = f2bf(e);
+                e4[r] = e;
+            }
+            *(f32x4 *)((char *)tb + (uint32_t)(ct * 16 + (int32_t)j) * TSTRIDE + (uint32_t)(16 * w + 4 * (int32_t)q) * 4u) = e4;
+        }
+        __syncthreads();
+        uint16_t *y = (uint16_t *)a.y;
+        // 16-byte accesses need 16-byte aligned rows of y (and of the residual)
+        const bool vy = ((uintptr_t)y & 15u) == 0 && (a.y_stride & 7) == 0 &&
+                        (!a.residual || (((uintptr_t)a.residual & 15u) == 0 && (a.res_stride & 7) == 0));
+        for (int32_t idx = (int32_t)threadIdx.x; idx < NT * 16 * 8; idx += GEMM_THREADS) {
+            const int32_t b = idx >> 3, c8 = idx & 7, n = n0 + 8 * c8;
+            if (b >= a.B || n >= a.N) continue;
+            const float *src = (const float *)((const char *)tb + (uint32_t)b * TSTRIDE + (uint32_t)c8 * 32u);
+            const f32x4 lo = *(const f32x4 *)src, hi = *(const f32x4 *)(src + 4);
+            float e[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if (vy && n + 8 <= a.N) {
+                if (a.residual) {
+                    const u32x4 rv = *(const u32x4 *)(a.residual + (int64_t)b * a.res_stride + n);
+                    const uint32_t rr[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        e[2 * k] += bf2f(rr[k] & 0xFFFFu);
+                        e[2 * k + 1] += bf2f(rr[k] >> 16);
+                    }
+                }
+                u32x4 o;
+                o.x = (uint32_t)f2bf(e[0]) | ((uint32_t)f2bf(e[1]) << 16);
+                o.y = (uint32_t)f2bf(e[2]) | ((uint32_t)f2bf(e[3]) << 16);
+                o.z = (uint32_t)f2bf(e[4]) | ((uint32_t)f2bf(e[5]) << 16);
+                o.w = (uint32_t)f2bf(e[6]) | ((uint32_t)f2bf(e[7]) << 16);
+                *(u32x4 *)(y + (int64_t)b * a.y_stride + n) = o;
+            } else {
+                for (int k = 0; k < 8 && n + k < a.N; ++k) {
+                    float v = e[k];
+                    if (a.residual) v += bf2f(a.residual[(int64_t)b * a.res_stride + n + k]);
+                    y[(int64_t)b * a.y_stride + n + k] = f2bf(v);
+                }
             }
         }
         return;
