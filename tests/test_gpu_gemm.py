@@ -1,7 +1,8 @@
 """GPU parity of the batched matrix-core path (wgn_gemm_norm, and wgn_layer_chain
 at batch 17-128) against the CPU oracle, teacher-forced per stage, on seeded
-synthetic inputs: ragged batches, row tiles and K tails, every epilogue, the
-K split and its fixed-order sum, the argmax merge and the decode step."""
+synthetic inputs: ragged batches, row tiles and K tails, every epilogue, tiles
+shared between workgroups and their fixed-order sum, the argmax merge and the
+decode step."""
 import numpy as np
 import pytest
 import torch
@@ -39,8 +40,8 @@ CASES = [
     (1, 8, 17, O.NORM_RMS, O.EPI_NONE, False, False, True),          # one row, one 8-wide K step
     (37, 264, 32, O.NORM_NONE, O.EPI_GELU_TANH, True, False, False),  # ragged rows, K tail inside a step
     (1000, 520, 33, O.NORM_NONE, O.EPI_NONE, False, True, False),    # batch 33: three 16-row groups
-    (300, 1536, 64, O.NORM_RMS, O.EPI_SWIGLU, False, True, True),    # K split in 3, two accumulator sets
-    (1536, 8960, 128, O.NORM_NONE, O.EPI_NONE, False, True, False),  # the down projection: 8 slices
+    (300, 1536, 64, O.NORM_RMS, O.EPI_SWIGLU, False, True, True),    # tiles shared by 6 workgroups, two accumulator sets
+    (1536, 8960, 128, O.NORM_NONE, O.EPI_NONE, False, True, False),  # the down projection: 24 tiles over 256 workgroups
     (8960, 1536, 128, O.NORM_RMS, O.EPI_SWIGLU, False, False, True),  # gate/up at batch 128
     (2048, 1536, 100, O.NORM_RMS, O.EPI_NONE, False, False, True),   # Q/K/V-sized, batch 100
     (17, 4096, 48, O.NORM_RMS, O.EPI_NONE, True, True, False),       # RMSNorm with a unit gain
@@ -48,6 +49,11 @@ CASES = [
     (37, 264, 32, O.NORM_LAYER, O.EPI_GELU_TANH, True, False, True),  # LayerNorm (gain and shift)
     (768, 768, 64, O.NORM_LAYER, O.EPI_GELU_TANH, True, False, True),  # the LayerNorm chain's shape
     (513, 1024, 20, O.NORM_LAYER, O.EPI_NONE, True, True, False),     # LayerNorm, unit gain, zero shift
+    # 7 tiles x 150 windows over 256 workgroups of 4 or 5 windows: ranges that
+    # start and end inside tiles, workgroups whose range crosses a tile boundary
+    (448, 9600, 24, O.NORM_RMS, O.EPI_NONE, False, True, True),
+    # 1028 tiles, 4 or more per workgroup: one workgroup per tile, a ragged last tile
+    (65760, 128, 17, O.NORM_NONE, O.EPI_GELU_TANH, True, False, False),
 ]
 
 
@@ -78,7 +84,7 @@ def test_gemm_norm_shapes(case):
                   W_up=None if Wu is None else bits(Wu),
                   bias=None if bias is None else bits(bias), residual=None if res is None else bits(res))
     assert_close_bf16(bits(y), ref, "gemm_norm %r" % (case,))
-    # reruns give the same bits (the K split is added in slice order) and leave
+    # reruns give the same bits (shared tiles are added in contributor order) and leave
     # the workspace's tickets at zero
     first = y.clone()
     for _ in range(2):

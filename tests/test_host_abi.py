@@ -520,27 +520,35 @@ def call_gemm(st, b, ws=0x100000, ws_bytes=1 << 34):
 
 def test_gemm_norm_workspace_layout():
     """Workspace of the batched path: tickets (one per 64-row tile + one),
-    argmax keys, x-hat of a norm prologue, and the partial tiles of a K split
-    (4 waves x accumulator sets x 16-row batch groups x 1 KB per slice and
-    tile)."""
+    argmax keys, x-hat of a norm prologue, and the contributor slots of the
+    tiles shared between workgroups (workgroups + tiles slots of 4 waves x
+    accumulator sets x 16-row batch groups x 1 KB).  The launch's 256
+    workgroups (one per compute unit; 256 when no device is visible) are
+    spread evenly over the stage's 64-element windows, with at least 4
+    windows each; a stage with 4 or more tiles per workgroup gives every tile
+    its own workgroup."""
     import ctypes
     lib = L.lib()
     ar = Arena()
     al = lambda v: (v + 255) // 256 * 256  # noqa: E731
-    # down projection at batch 128: 24 tiles split into 8 slices of 1152 (the last 896)
+    # down projection at batch 128: 24 tiles x 140 windows over 256 workgroups
     d = fake_stage(ar, 1536, 8960, 128, L.NORM_NONE, residual=ar.take(128 * 1536 * 2))
-    assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(d), 128) == al(25 * 4) + 24 * 8 * 4 * 8 * 1024
-    # gate/up at batch 32: 140 tiles, 4 slices of 384; two accumulator sets; x-hat 32 x 1536
+    assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(d), 128) == al(25 * 4) + (256 + 24) * 4 * 8 * 1024
+    # gate/up at batch 32: 140 tiles x 24 windows; two accumulator sets; x-hat 32 x 1536
     gu = fake_stage(ar, 8960, 1536, 32, L.NORM_RMS, L.EPI_SWIGLU)
     assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(gu), 32) == \
-        al(141 * 4) + al(32 * 1536 * 2) + 140 * 4 * 4 * 2 * 2 * 1024
-    # LM head at batch 17: 2374 tiles (no split), keys, x-hat (gamma null: unit gain)
+        al(141 * 4) + al(32 * 1536 * 2) + (256 + 140) * 4 * 2 * 2 * 1024
+    # LM head at batch 17: 2374 tiles, one workgroup each (no slots), keys,
+    # x-hat (gamma null: unit gain)
     lm = fake_stage(ar, 151936, 1536, 17, L.NORM_RMS, L.EPI_ARGMAX, gamma=False)
     assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(lm), 17) == al(2375 * 4) + al(17 * 8) + al(17 * 1536 * 2)
-    # LayerNorm prologue at batch 64: 12 tiles split into 6 slices of 128
+    # LayerNorm prologue at batch 64: 12 tiles x 12 windows, 36 workgroups of 4 windows
     ln = fake_stage(ar, 768, 768, 64, L.NORM_LAYER, beta=True)
     assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(ln), 64) == \
-        al(13 * 4) + al(64 * 768 * 2) + 12 * 6 * 4 * 4 * 1024
+        al(13 * 4) + al(64 * 768 * 2) + (36 + 12) * 4 * 4 * 1024
+    # one window per tile (K = 64): no tile is shared, no slots
+    one = fake_stage(ar, 640, 64, 32, L.NORM_NONE)
+    assert lib.wgn_gemm_norm_workspace_bytes(ctypes.byref(one), 32) == al(11 * 4)
 
 
 def test_gemm_norm_checks_before_the_device():

@@ -949,38 +949,67 @@ struct GemmGroup {
     int32_t first = 0, n = 0;
     bool swiglu = false;
     bool norm = false;  // x-hat is written into the workspace first
+    int32_t norm_stage = -1;  // the first normalised stage: its input and norm make the x-hat
     size_t lds = 0, ws = 0;
     size_t counters = 0;  // bytes of tickets and keys at the start of the workspace
     size_t off_ticket[GEMM_MAX_GROUP] = {}, off_part[GEMM_MAX_GROUP] = {};
     size_t off_keys = 0, off_xhat = 0;
 };
 
-// K slices per row tile at most: the last item of a tile adds them one group
-// of loads at a time, so more slices lengthen the tile's tail.
-constexpr int32_t GEMM_MAX_SLICES = 8;
+// Workgroups of a batched launch per compute unit, and the fewest windows a
+// workgroup streams (fewer would mostly add contributions to be summed).
+#ifndef WGN_GEMM_WG_PER_CU
+#define WGN_GEMM_WG_PER_CU 1
+#endif
+constexpr int32_t GEMM_MIN_UNITS = 4;
+// Tiles per workgroup of the launch from which a stage's tiles become whole
+// workgroups of their own.
+constexpr int32_t GEMM_TILES_WHOLE = 4;
 
-// Whether stage b may join a launch whose first stage is a: the same input,
-// length and normalisation, the same epilogue family, no argmax.
-bool same_input(const wgn_stage &a, const wgn_stage &b) {
+// Whether two normalised stages read the same x-hat: the same input, length
+// and normalisation.
+bool same_norm_input(const wgn_stage &a, const wgn_stage &b) {
     return a.x == b.x && a.x_stride == b.x_stride && a.K == b.K && a.norm == b.norm && a.gamma == b.gamma &&
-           a.beta == b.beta && std::memcmp(&a.eps, &b.eps, sizeof a.eps) == 0 &&
-           (a.epi == EPI_SWIGLU) == (b.epi == EPI_SWIGLU) && a.epi != EPI_ARGMAX && b.epi != EPI_ARGMAX;
+           a.beta == b.beta && std::memcmp(&a.eps, &b.eps, sizeof a.eps) == 0;
+}
+
+// Whether stage st[j] may join the launch of stages st[i..j): the same
+// epilogue family (one kernel instance), no argmax, and if it is normalised,
+// the same x-hat as the launch's other normalised stages (one norm pass per
+// launch).  Stages without normalisation read their own inputs.
+bool may_join(const wgn_stage *st, int32_t i, int32_t j) {
+    const wgn_stage &b = st[j];
+    if ((st[i].epi == EPI_SWIGLU) != (b.epi == EPI_SWIGLU) || st[i].epi == EPI_ARGMAX || b.epi == EPI_ARGMAX)
+        return false;
+    if (b.norm == NORM_NONE) return true;
+    for (int32_t k = i; k < j; ++k)
+        if (st[k].norm != NORM_NONE) return same_norm_input(st[k], b);
+    return true;
+}
+
+// The first normalised stage of st[0..n), or -1.
+int32_t first_normalised(const wgn_stage *st, int32_t n) {
+    for (int32_t i = 0; i < n; ++i)
+        if (st[i].norm != NORM_NONE) return i;
+    return -1;
 }
 
 // Work partition and workspace of stages st[0..n) as one launch at batch B:
-// row tiles of 64 rows; a launch with fewer tiles than two per compute unit is
-// split over K (whole 128-element windows per slice) toward two items per
-// compute unit, while the partial tiles a split stores stay within a third of
-// the launch's weight bytes (at least 8 MB).  base: bytes kept for counters at
-// the start of the workspace (at least the launch's own); launches that share
-// a workspace use the largest, so no launch's data lies where another keeps
-// its tickets.  False if a stage is outside the path (argmax with a bias, a
-// weight matrix past 32-bit byte offsets).
+// a stage's units are the 64-element windows of its 64-row tiles; the
+// launch's cus x WGN_GEMM_WG_PER_CU workgroups are shared among the stages in
+// proportion to their units (each workgroup then streams the same number of
+// windows), with at least GEMM_MIN_UNITS windows per workgroup; a stage with
+// GEMM_TILES_WHOLE or more tiles per workgroup gives each tile a workgroup.  base: bytes
+// kept for counters at the start of the workspace (at least the launch's
+// own); launches that share a workspace use the largest, so no launch's data
+// lies where another keeps its tickets.  False if a stage is outside the path
+// (argmax with a bias, a weight matrix or input rows past 32-bit byte
+// offsets).
 bool gemm_plan(const wgn_stage *st, int32_t n, int32_t B, int32_t cus, GemmGroup &G, size_t base = 0) {
     if (n < 1 || n > GEMM_MAX_GROUP) return false;
     const int32_t nt = (B + 15) / 16;
     const int32_t P = st[0].epi == EPI_SWIGLU ? 2 : 1;
-    int64_t tiles = 0, wbytes = 0;
+    int64_t units = 0;
     for (int32_t i = 0; i < n; ++i) {
         const wgn_stage &s = st[i];
         if (s.epi == EPI_ARGMAX && s.bias) return false;
@@ -988,20 +1017,15 @@ bool gemm_plan(const wgn_stage *st, int32_t n, int32_t B, int32_t cus, GemmGroup
         // the input rows are read through a 32-bit buffer range too
         const int64_t xs = s.norm != NORM_NONE ? s.K : (B > 1 ? s.x_stride : s.K);
         if (((int64_t)(B - 1) * xs + s.K) * 2 > 0x7FFFFFF0LL) return false;
-        tiles += (s.N + GEMM_TILE_ROWS - 1) / GEMM_TILE_ROWS;
-        wbytes += (int64_t)s.N * s.K * 2 * P;
+        units += (int64_t)((s.N + GEMM_TILE_ROWS - 1) / GEMM_TILE_ROWS) * ((s.K + GEMM_KWIN - 1) / GEMM_KWIN);
     }
-    int32_t S = 1;
-    if (tiles < 2 * cus) {  // two workgroups fit one compute unit
-        const int64_t per_slice = tiles * 4 * P * nt * GEMM_FRAG_BYTES;
-        const int64_t cap = std::max<int64_t>(1, std::max<int64_t>(wbytes / 3, 8 << 20) / per_slice);
-        S = (int32_t)std::min<int64_t>(std::min<int64_t>((2 * cus + tiles - 1) / tiles, GEMM_MAX_SLICES), cap);
-    }
+    const int64_t target = (int64_t)std::max(cus, 1) * WGN_GEMM_WG_PER_CU;
     std::memset(&G.L, 0, sizeof G.L);
     G.n = n;
     G.L.n = n;
     G.swiglu = P == 2;
-    G.norm = st[0].norm != NORM_NONE;
+    G.norm_stage = first_normalised(st, n);
+    G.norm = G.norm_stage >= 0;
     size_t o = 0;
     for (int32_t i = 0; i < n; ++i) {
         G.off_ticket[i] = o;
@@ -1015,18 +1039,29 @@ bool gemm_plan(const wgn_stage *st, int32_t n, int32_t B, int32_t cus, GemmGroup
     G.counters = o;
     if (G.norm) {
         G.off_xhat = o;
-        o += al256((size_t)B * st[0].K * 2);
+        o += al256((size_t)B * st[G.norm_stage].K * 2);
     }
-    int32_t items = 0;
+    int32_t wgs_total = 0;
     for (int32_t i = 0; i < n; ++i) {
         const wgn_stage &s = st[i];
         const int32_t ntiles = (s.N + GEMM_TILE_ROWS - 1) / GEMM_TILE_ROWS;
-        const int32_t Si = std::min(S, (s.K + GEMM_KWIN - 1) / GEMM_KWIN);
-        const int32_t kslice = ((s.K + Si - 1) / Si + GEMM_KWIN - 1) / GEMM_KWIN * GEMM_KWIN;
-        const int32_t Sn = (s.K + kslice - 1) / kslice;
-        if (Sn > 1) {
+        const int32_t nwin = (s.K + GEMM_KWIN - 1) / GEMM_KWIN;
+        const int64_t U = (int64_t)ntiles * nwin;
+        const int64_t share = (target * U + units / 2) / units;
+        // A stage with many more tiles than workgroups (an LM head) keeps one
+        // tile per workgroup: the hardware then runs two at a time on each
+        // compute unit, one's epilogue under the other's stream, which beats
+        // refilling one workgroup's pipeline for every tile.
+        const int32_t wgs = ntiles >= GEMM_TILES_WHOLE * target
+                                ? ntiles
+                                : (int32_t)std::max<int64_t>(1, std::min(share, U / GEMM_MIN_UNITS));
+        if (gemm_tiles_shared(ntiles, nwin, wgs)) {
+            // contributor slots of the shared tiles: at most wgs + ntiles - 1
+            // (consecutive tiles' slots never overlap), addressed with 32-bit offsets
+            const size_t part = (size_t)(wgs + ntiles) * 4 * P * nt * GEMM_FRAG_BYTES;
+            if (part > 0x7FFFFFF0u) return false;
             G.off_part[i] = o;
-            o += (size_t)ntiles * Sn * 4 * P * nt * GEMM_FRAG_BYTES;
+            o += part;
         }
         GemmArgs &a = G.L.s[i];
         a.W = (const uint16_t *)s.W;
@@ -1045,12 +1080,12 @@ bool gemm_plan(const wgn_stage *st, int32_t n, int32_t B, int32_t cus, GemmGroup
         a.B = B;
         a.epi = s.epi;
         a.ntiles = ntiles;
-        a.nslices = Sn;
-        a.kslice = kslice;
-        G.L.start[i] = items;
-        items += ntiles * Sn;
+        a.nwin = nwin;
+        a.wgs = wgs;
+        G.L.start[i] = wgs_total;
+        wgs_total += wgs;
     }
-    G.L.start[n] = items;
+    G.L.start[n] = wgs_total;
     G.ws = o;
     G.lds = gemm_lds_bytes(nt * 16);
     return true;
@@ -1066,7 +1101,7 @@ hipError_t gemm_run(const wgn_stage *st, int32_t B, const GemmGroup &G0, char *w
     GemmLaunch L = G0.L;
     const uint16_t *x = nullptr;
     if (G0.norm) {
-        const wgn_stage &s = st[0];
+        const wgn_stage &s = st[G0.norm_stage];
         uint16_t *xh = (uint16_t *)(ws + G0.off_xhat);
         hipError_t e = launch_norm_rows64((const uint16_t *)s.x, B > 1 ? s.x_stride : s.K, (const uint16_t *)s.gamma,
                                           (const uint16_t *)s.beta, s.eps, s.norm == NORM_LAYER, xh, B, s.K, stream);
@@ -1078,7 +1113,7 @@ hipError_t gemm_run(const wgn_stage *st, int32_t B, const GemmGroup &G0, char *w
         a.tickets = (uint32_t *)(ws + G0.off_ticket[i]);
         a.keys = a.epi == EPI_ARGMAX ? (uint64_t *)(ws + G0.off_keys) : nullptr;
         a.part = G0.off_part[i] ? (float *)(ws + G0.off_part[i]) : nullptr;
-        if (x) {
+        if (x && st[i].norm != NORM_NONE) {
             a.x = x;
             a.x_stride = a.K;
         }
@@ -1127,9 +1162,10 @@ bool independent(const wgn_stage &a, const wgn_stage &b, int32_t B) {
 }
 
 // The launches of a stage list on the batched path, in list order: runs of
-// consecutive stages with the same input, normalisation and epilogue family
-// that are independent of each other (at most GEMM_MAX_GROUP) share a launch
-// and one norm pass.  All launches use one counter area (the largest), so the
+// consecutive stages of one epilogue family that are independent of each
+// other (at most GEMM_MAX_GROUP) share a launch, provided the normalised ones
+// among them read the same x-hat (one norm pass per launch); stages without
+// normalisation may read any input.  All launches use one counter area (the largest), so the
 // workspace need is the largest launch's with that base.  False if a stage is
 // outside the path.
 bool plan_batched(const wgn_stage *st, int32_t n, int32_t B, int32_t cus, std::vector<GemmGroup> &groups,
@@ -1138,7 +1174,7 @@ bool plan_batched(const wgn_stage *st, int32_t n, int32_t B, int32_t cus, std::v
     counters = 0;
     for (int32_t i = 0; i < n;) {
         int32_t j = i + 1;
-        while (j < n && j - i < GEMM_MAX_GROUP && same_input(st[i], st[j])) {
+        while (j < n && j - i < GEMM_MAX_GROUP && may_join(st, i, j)) {
             bool ok = true;
             for (int32_t k = i; k < j && ok; ++k) ok = independent(st[k], st[j], B);
             if (!ok) break;

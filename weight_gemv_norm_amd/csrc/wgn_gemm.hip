@@ -88,14 +88,14 @@ template <int NT, bool SWI>
 constexpr int sum_group() { return (SWI ? 2 : 1) * NT <= 4 ? 4 : (SWI ? 2 : 1) * NT <= 8 ? 2 : 1; }
 
 template <int NT, bool SWI>
-__global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmLaunch G) {
+__global__ __launch_bounds__(GEMM_THREADS, WGN_GEMM_OCC) void gemm_kernel(GemmLaunch G) {
     extern __shared__ __align__(16) char lds[];
-    // this workgroup's stage and item within it
+    // this workgroup's stage and place among the stage's workgroups
     int32_t si = 0;
 #pragma unroll
     for (int k = 1; k < GEMM_MAX_GROUP; ++k) si += (k < G.n && (int32_t)blockIdx.x >= G.start[k]) ? 1 : 0;
     const GemmArgs &a = G.s[si];
-    const int32_t item = (int32_t)blockIdx.x - G.start[si];
+    const int32_t g = (int32_t)blockIdx.x - G.start[si];
     constexpr int P = SWI ? 2 : 1;                           // accumulator sets (gate and up)
     constexpr int MS = GEMM_KWIN / 32;                       // K steps per window
     constexpr int D = GEMM_RING;                             // windows in flight
@@ -104,271 +104,334 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmLaunch G) {
     constexpr int LPW = P * MS + XI;                         // loads per wave and window
     constexpr uint32_t TSTRIDE = GEMM_TILE_ROWS * 4 + 16;    // epilogue staging: bytes per batch row
     static_assert(NT * 16 * TSTRIDE <= D * XB, "the epilogue's staging fits the ring");
+    constexpr int RI = (NT * 16 * 8 + GEMM_THREADS - 1) / GEMM_THREADS;  // output chunks per thread
     const int32_t w = (int32_t)(threadIdx.x >> 6);
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t q = lane >> 4, j = lane & 15u;
-    const int32_t S = a.nslices;
-    const int32_t tile = item / S;
-    const int32_t slice = item - tile * S;
-    const int32_t n0 = tile * GEMM_TILE_ROWS;
-    const int32_t k0 = slice * a.kslice;
-    const int32_t k1 = min(a.K, k0 + a.kslice);
-    const int32_t nwin = (k1 - k0 + GEMM_KWIN - 1) / GEMM_KWIN;
-    const int32_t arow = n0 + 16 * w + (int32_t)j;  // weight row of this lane's A fragments
-    const size_t merge_off = (size_t)D * XB;          // argmax merge area, then the last-item flag
+    const size_t merge_off = (size_t)D * XB;          // argmax merge area, then the last-contributor flag
     int32_t *s_last = (int32_t *)(lds + merge_off + 4 * GEMM_MAX_BATCH * 8);
     const uint32_t wbytes = (uint32_t)((int64_t)a.N * a.K * 2);
     const __amdgpu_buffer_rsrc_t rw = grsrc(a.W, wbytes);
     const __amdgpu_buffer_rsrc_t ru = grsrc(SWI ? a.W_up : a.W, wbytes);
     const __amdgpu_buffer_rsrc_t rx = grsrc(a.x, (uint32_t)(((int64_t)(a.B - 1) * a.x_stride + a.K) * 2));
-    f32x4 acc[P][NT];
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct) acc[p][ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    const __amdgpu_buffer_rsrc_t rp = grsrc(a.part, 0x7FFFFFF0u);
+    uint16_t *y = (uint16_t *)a.y;
+    // 16-byte output accesses need 16-byte aligned rows of y (and of the residual)
+    const bool vy = ((uintptr_t)y & 15u) == 0 && (a.y_stride & 7) == 0 &&
+                    (!a.residual || (((uintptr_t)a.residual & 15u) == 0 && (a.res_stride & 7) == 0));
 
-    // weight fragments of the window at kw: row arow, K offset kw + 32 t + 8 q
-    // (past the slice, or for a window after the last, the loads read zero)
-    auto load_w = [&](int32_t kw, u32x4 (&wa)[P][MS]) {
+    // The stage's units are the windows of its row tiles, tile by tile
+    // (nwin per tile); workgroup g takes units [g U / wgs, (g + 1) U / wgs),
+    // so every workgroup streams the same number of windows.  A tile whose
+    // units fall to several workgroups (its contributors, consecutive) is
+    // added up by the last of them to finish, in contributor order.
+    const int64_t U = (int64_t)a.ntiles * a.nwin;
+    const int32_t u0 = (int32_t)((int64_t)g * U / a.wgs), u1 = (int32_t)((int64_t)(g + 1) * U / a.wgs);
+    auto owner = [&](int64_t u) -> int32_t { return (int32_t)(((u + 1) * a.wgs - 1) / U); };
+
+    for (int32_t u = u0; u < u1;) {
+        // one segment: windows [wb0, we0) of row tile `tile`
+        const int32_t tile = u / a.nwin;
+        const int32_t wb0 = u - tile * a.nwin;
+        const int32_t we0 = min(a.nwin, wb0 + (u1 - u));
+        u += we0 - wb0;
+        const int32_t n0 = tile * GEMM_TILE_ROWS;
+        const int32_t k0 = wb0 * GEMM_KWIN, k1 = min(a.K, we0 * GEMM_KWIN);
+        const int32_t nwin = we0 - wb0;
+        // The thread's index is taken afresh in every segment (an empty asm
+        // statement hides its value), so that the compiler derives the
+        // thread's addresses here rather than keeping all of them live
+        // across the whole loop, epilogue included.
+        uint32_t tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const uint32_t lane = tid & 63u;
+        const uint32_t q = lane >> 4, j = lane & 15u;
+        const int32_t arow = n0 + 16 * w + (int32_t)j;  // weight row of this lane's A fragments
+
+        f32x4 acc[P][NT];
 #pragma unroll
-        for (int t = 0; t < MS; ++t) {
-            const int32_t k = kw + 32 * t + 8 * (int32_t)q;
-            const uint32_t off = oor_unless(arow < a.N && k < k1, (uint32_t)(((int64_t)arow * a.K + k) * 2));
-            wa[0][t] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, GEMM_WEIGHT_AUX);
-            if constexpr (SWI) wa[P - 1][t] = __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, GEMM_WEIGHT_AUX);
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) acc[p][ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+        // weight fragments of the window at kw: row arow, K offset kw + 32 t + 8 q
+        // (past the segment, or for a window after the last, the loads read zero)
+        auto load_w = [&](int32_t kw, u32x4 (&wa)[P][MS]) {
+#pragma unroll
+            for (int t = 0; t < MS; ++t) {
+                const int32_t k = kw + 32 * t + 8 * (int32_t)q;
+                const uint32_t off = oor_unless(arow < a.N && k < k1, (uint32_t)(((int64_t)arow * a.K + k) * 2));
+                wa[0][t] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, GEMM_WEIGHT_AUX);
+                if constexpr (SWI) wa[P - 1][t] = __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, GEMM_WEIGHT_AUX);
+            }
+        };
+        // The input window at kw, copied into a ring slot by LDS-DMA loads:
+        // 1 KB copies m = w, w + 4, ... of 8 batch rows each.  Batch row r
+        // sits at r * 128 bytes with its 16-byte chunk c in place
+        // c ^ ((r >> 1) & 7), so that the 16 rows one read instruction
+        // touches fall in different banks.  A chunk past the segment takes
+        // the segment's first chunk instead (finite input against a zero
+        // weight); rows past the batch are left out of range (no memory
+        // traffic; those columns are never used).
+        auto issue_x = [&](int32_t kw, char *slot) {
+#pragma unroll
+            for (int e = 0; e < XI; ++e) {
+                const int32_t m = w + 4 * e;
+                const int32_t row = 8 * m + (int32_t)(lane >> 3);
+                const int32_t k = kw + 8 * ((int32_t)(lane & 7u) ^ ((4 * m + (int32_t)(lane >> 4)) & 7));
+                const uint32_t off =
+                    oor_unless(row < a.B, (uint32_t)(((int64_t)row * a.x_stride + (k < k1 ? k : k0)) * 2));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (GEMM_LAS void *)(slot + m * 1024), 16, off, 0, 0, 0);
+            }
+        };
+        // the window's products: B operand = batch row 16 ct + j, chunk 4 t + q
+        auto compute = [&](const char *slot, const u32x4 (&wa)[P][MS]) {
+#pragma unroll
+            for (int t = 0; t < MS; ++t)
+#pragma unroll
+                for (int ct = 0; ct < NT; ++ct) {
+                    const u32x4 xv = *(const u32x4 *)(slot + (uint32_t)ct * 2048u + j * 128u +
+                                                      ((((uint32_t)(4 * t) + q) ^ (j >> 1)) << 4));
+#pragma unroll
+                    for (int p = 0; p < P; ++p) acc[p][ct] = mfma(wa[p][t], xv, acc[p][ct]);
+                }
+        };
+
+        // Ring of GEMM_RING windows: window i is multiplied from slot i % RING
+        // and register set i % RING while windows i + 1 .. i + RING - 1 are in
+        // flight.  Every step issues the same loads (zero weights past the
+        // segment), so a fixed count of outstanding loads marks window i as
+        // landed; each wave waits for its own copies, then the barrier makes
+        // every wave's copies visible and frees the slot of window i - 1 for
+        // window i + RING - 1.  Unrolled by RING, so that no register array
+        // is indexed at run time; the windows that pad the segment to a
+        // multiple of RING add zero products.
+        __syncthreads();  // the previous segment's epilogue is done with the ring
+        u32x4 wa[D][P][MS];
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d) {
+            load_w(k0 + d * GEMM_KWIN, wa[d]);
+            issue_x(k0 + d * GEMM_KWIN, lds + d * XB);
+            asm volatile("" ::: "memory");  // windows issued in order: the count below relies on it
         }
-    };
-    // The input window at kw, copied into a ring slot by LDS-DMA loads: 1 KB
-    // copies m = w, w + 4, ... of 8 batch rows each.  Batch row r sits at
-    // r * 128 bytes with its 16-byte chunk c in place c ^ ((r >> 1) & 7), so
-    // that the 16 rows one read instruction touches fall in different banks.
-    // A chunk past the slice takes the slice's first chunk instead (finite
-    // input against a zero weight); rows past the batch and windows after the
-    // last are left out of range (no memory traffic; those columns and
-    // windows are never used).
-    auto issue_x = [&](int32_t kw, char *slot) {
+        for (int32_t i = 0; i < nwin; i += D) {
 #pragma unroll
-        for (int e = 0; e < XI; ++e) {
-            const int32_t m = w + 4 * e;
-            const int32_t row = 8 * m + (int32_t)(lane >> 3);
-            const int32_t k = kw + 8 * ((int32_t)(lane & 7u) ^ ((4 * m + (int32_t)(lane >> 4)) & 7));
-            const uint32_t off = oor_unless(row < a.B, (uint32_t)(((int64_t)row * a.x_stride + (k < k1 ? k : k0)) * 2));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (GEMM_LAS void *)(slot + m * 1024), 16, off, 0, 0, 0);
+            for (int d = 0; d < D; ++d) {
+                wait_vm_lds0<(D - 2) * LPW>();
+                ring_barrier();
+                const int32_t kn = k0 + (i + d + D - 1) * GEMM_KWIN;
+                load_w(kn, wa[(d + D - 1) % D]);
+                issue_x(kn, lds + ((d + D - 1) % D) * XB);
+                compute(lds + d * XB, wa[d]);
+            }
         }
-    };
-    // the window's products: B operand = batch row 16 ct + j, chunk 4 t + q
-    auto compute = [&](const char *slot, const u32x4 (&wa)[P][MS]) {
+        __builtin_amdgcn_s_waitcnt(0);  // the ring's copies past the last window have landed
+
+        // The epilogue's own inputs, requested as soon as this workgroup
+        // knows it applies the epilogue (before the contributions are added,
+        // whose loads then overlap them): the bias of this lane's 4 rows and,
+        // where 16-byte accesses are allowed, the residual chunks of this
+        // thread's outputs (8 rows of one batch row, as the output loop takes
+        // them).
+        float bz[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        u32x4 rv[RI];
+        auto fetch_epilogue_inputs = [&]() {
+            if (a.epi == EPI_ARGMAX) return;
+            if (a.bias) {
 #pragma unroll
-        for (int t = 0; t < MS; ++t)
+                for (int r = 0; r < 4; ++r) {
+                    const int32_t n = n0 + 16 * w + 4 * (int32_t)q + r;
+                    if (n < a.N) bz[r] = bf2f(a.bias[n]);
+                }
+            }
+            if (a.residual && vy) {
+#pragma unroll
+                for (int it = 0; it < RI; ++it) {
+                    const int32_t idx = (int32_t)tid + it * GEMM_THREADS;
+                    const int32_t b = idx >> 3, n = n0 + 8 * (idx & 7);
+                    if (idx < NT * 16 * 8 && b < a.B && n + 8 <= a.N)
+                        rv[it] = *(const u32x4 *)(a.residual + (int64_t)b * a.res_stride + n);
+                }
+            }
+        };
+
+        bool epi = true;
+        if (wb0 > 0 || we0 < a.nwin) {
+            // a shared tile: this workgroup's accumulators go to its
+            // contributor slot, then the tile's ticket
+            const int32_t first = owner((int64_t)tile * a.nwin);
+            const int32_t nc = owner((int64_t)tile * a.nwin + a.nwin - 1) - first + 1;  // contributors
+            const int32_t kc = g - first;                                               // this one
+            const int32_t base = first + tile;  // slot of contributor 0: slots of successive tiles never overlap
+            auto frag = [&](int32_t c, int p, int ct) -> uint32_t {  // byte offset of this lane's part of a fragment
+                return (uint32_t)(((((size_t)(base + c)) * 4 + w) * P * NT + (size_t)p * NT + ct) * GEMM_FRAG_BYTES +
+                                  lane * 16u);
+            };
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+#pragma unroll
+                for (int ct = 0; ct < NT; ++ct)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[p][ct]), rp, frag(kc, p, ct), 0,
+                                                           GEMM_COH);
+            __builtin_amdgcn_s_waitcnt(0);  // the stores have completed: visible at the coherent level
+            __syncthreads();
+            if (tid == 0u) {
+                const uint32_t old =
+                    __hip_atomic_fetch_add(&a.tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int32_t last = old == (uint32_t)(nc - 1) ? 1 : 0;
+                if (last) __hip_atomic_store(&a.tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *s_last = last;
+            }
+            __syncthreads();
+            epi = *s_last != 0;
+            if (epi) {
+                fetch_epilogue_inputs();
+                // the last contributor adds the contributions in contributor
+                // order, its own too (stored like the others), into acc
+                constexpr int GS = sum_group<NT, SWI>();
+                for (int32_t c0 = 0; c0 < nc; c0 += GS) {
+                    f32x4 v[GS][P][NT];
+#pragma unroll
+                    for (int gg = 0; gg < GS; ++gg) {
+                        if (c0 + gg < nc) {
+#pragma unroll
+                            for (int p = 0; p < P; ++p)
+#pragma unroll
+                                for (int ct = 0; ct < NT; ++ct)
+                                    v[gg][p][ct] = __builtin_bit_cast(
+                                        f32x4,
+                                        __builtin_amdgcn_raw_buffer_load_b128(rp, frag(c0 + gg, p, ct), 0, GEMM_COH));
+                        }
+                    }
+#pragma unroll
+                    for (int gg = 0; gg < GS; ++gg) {
+                        if (c0 + gg < nc) {
+#pragma unroll
+                            for (int p = 0; p < P; ++p)
+#pragma unroll
+                                for (int ct = 0; ct < NT; ++ct)
+                                    acc[p][ct] = c0 + gg == 0 ? v[gg][p][ct] : acc[p][ct] + v[gg][p][ct];
+                        }
+                    }
+                }
+            }
+        } else {
+            fetch_epilogue_inputs();
+        }
+        if (!epi) continue;
+
+        // ------------------------------------------------------------ epilogue
+        // lane: rows n0 + 16 w + 4 q + r (r = 0..3) of batch rows 16 ct + j.
+        if (a.epi != EPI_ARGMAX) {
+            // The activated tile goes through LDS (the ring, free now) so
+            // that the residual is read and the output written in 16-byte
+            // chunks of 8 consecutive rows of one batch row: the fragment
+            // layout would make every store instruction touch 16 batch rows
+            // with 2-byte writes.
+            __syncthreads();  // every wave is done with the ring
+            float *tb = (float *)lds;  // [16 NT batch rows][64 rows], row stride TSTRIDE bytes
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) {
-                const u32x4 xv = *(const u32x4 *)(slot + (uint32_t)ct * 2048u + j * 128u +
-                                                  ((((uint32_t)(4 * t) + q) ^ (j >> 1)) << 4));
+                f32x4 e4;
 #pragma unroll
-                for (int p = 0; p < P; ++p) acc[p][ct] = mfma(wa[p][t], xv, acc[p][ct]);
-            }
-    };
-
-    // Ring of GEMM_RING windows: window i is multiplied from slot i % RING
-    // and register set i % RING while windows i + 1 .. i + RING - 1 are in
-    // flight.  Every step issues the same loads (out of range past the
-    // slice), so a fixed count of outstanding loads marks window i as landed;
-    // each wave waits for its own copies, then the barrier makes every wave's
-    // copies visible and frees the slot of window i - 1 for window
-    // i + RING - 1.  Unrolled by RING, so that no register array is indexed
-    // at run time.
-    u32x4 wa[D][P][MS];
-#pragma unroll
-    for (int d = 0; d < D - 1; ++d) {
-        load_w(k0 + d * GEMM_KWIN, wa[d]);
-        issue_x(k0 + d * GEMM_KWIN, lds + d * XB);
-        asm volatile("" ::: "memory");  // windows issued in order: the count above relies on it
-    }
-    for (int32_t i = 0; i < nwin; i += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            wait_vm_lds0<(D - 2) * LPW>();
-            ring_barrier();
-            const int32_t kn = k0 + (i + d + D - 1) * GEMM_KWIN;
-            load_w(kn, wa[(d + D - 1) % D]);
-            issue_x(kn, lds + ((d + D - 1) % D) * XB);
-            compute(lds + d * XB, wa[d]);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // the ring's copies past the last window have landed: LDS is free after a barrier
-
-    if (S > 1) {
-        // this item's accumulators, then the tile's ticket
-        const __amdgpu_buffer_rsrc_t rp = grsrc(a.part, 0x7FFFFFF0u);
-        auto frag = [&](int32_t s, int p, int ct) -> uint32_t {  // byte offset of this lane's part of a fragment
-            return (uint32_t)(((((size_t)tile * S + s) * 4 + w) * P * NT + (size_t)p * NT + ct) * GEMM_FRAG_BYTES +
-                              lane * 16u);
-        };
-#pragma unroll
-        for (int p = 0; p < P; ++p)
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[p][ct]), rp, frag(slice, p, ct), 0,
-                                                       GEMM_COH);
-        __builtin_amdgcn_s_waitcnt(0);  // the stores have completed: visible at the coherent level
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t old = __hip_atomic_fetch_add(&a.tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const int32_t last = old == (uint32_t)(S - 1) ? 1 : 0;
-            if (last) __hip_atomic_store(&a.tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            *s_last = last;
-        }
-        __syncthreads();
-        if (*s_last == 0) return;
-        // the last item adds the slices in slice order, its own from registers
-        constexpr int GS = sum_group<NT, SWI>();
-        f32x4 sum[P][NT];
-        for (int32_t s0 = 0; s0 < S; s0 += GS) {
-            f32x4 v[GS][P][NT];
-#pragma unroll
-            for (int g = 0; g < GS; ++g) {
-                const int32_t s = s0 + g;
-                if (s < S && s != slice) {
-#pragma unroll
-                    for (int p = 0; p < P; ++p)
-#pragma unroll
-                        for (int ct = 0; ct < NT; ++ct)
-                            v[g][p][ct] = __builtin_bit_cast(
-                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, frag(s, p, ct), 0, GEMM_COH));
+                for (int r = 0; r < 4; ++r) {
+                    const int32_t n = n0 + 16 * w + 4 * (int32_t)q + r;
+                    const float z = acc[0][ct][r] + bz[r];
+                    float e;
+                    if (a.epi == EPI_GELU_TANH) {
+                        e = gelu_tanh(z);
+                        const int32_t b = ct * 16 + (int32_t)j;
+                        if (a.logits && n < a.N && b < a.B)
+                            a.logits[(int64_t)b * a.N + n] = z;  // pre-activation for the backward pass
+                    } else if (a.epi == EPI_SWIGLU) e = silu(z) * acc[P - 1][ct][r];
+                    else e = z;
+                    e4[r] = e;
                 }
+                *(f32x4 *)((char *)tb + (uint32_t)(ct * 16 + (int32_t)j) * TSTRIDE +
+                           (uint32_t)(16 * w + 4 * (int32_t)q) * 4u) = e4;
             }
+            __syncthreads();
 #pragma unroll
-            for (int g = 0; g < GS; ++g) {
-                const int32_t s = s0 + g;
-                if (s < S) {
+            for (int it = 0; it < RI; ++it) {
+                const int32_t idx = (int32_t)tid + it * GEMM_THREADS;
+                const int32_t b = idx >> 3, c8 = idx & 7, n = n0 + 8 * c8;
+                if (idx >= NT * 16 * 8 || b >= a.B || n >= a.N) continue;
+                const float *src = (const float *)((const char *)tb + (uint32_t)b * TSTRIDE + (uint32_t)c8 * 32u);
+                const f32x4 lo = *(const f32x4 *)src, hi = *(const f32x4 *)(src + 4);
+                float e[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                if (vy && n + 8 <= a.N) {
+                    if (a.residual) {
+                        const uint32_t rr[4] = {rv[it].x, rv[it].y, rv[it].z, rv[it].w};
 #pragma unroll
-                    for (int p = 0; p < P; ++p)
-#pragma unroll
-                        for (int ct = 0; ct < NT; ++ct) {
-                            const f32x4 x = s == slice ? acc[p][ct] : v[g][p][ct];
-                            sum[p][ct] = s == 0 ? x : sum[p][ct] + x;
+                        for (int k = 0; k < 4; ++k) {
+                            e[2 * k] += bf2f(rr[k] & 0xFFFFu);
+                            e[2 * k + 1] += bf2f(rr[k] >> 16);
                         }
+                    }
+                    u32x4 o;
+                    o.x = (uint32_t)f2bf(e[0]) | ((uint32_t)f2bf(e[1]) << 16);
+                    o.y = (uint32_t)f2bf(e[2]) | ((uint32_t)f2bf(e[3]) << 16);
+                    o.z = (uint32_t)f2bf(e[4]) | ((uint32_t)f2bf(e[5]) << 16);
+                    o.w = (uint32_t)f2bf(e[6]) | ((uint32_t)f2bf(e[7]) << 16);
+                    *(u32x4 *)(y + (int64_t)b * a.y_stride + n) = o;
+                } else {
+                    for (int k = 0; k < 8 && n + k < a.N; ++k) {
+                        float v = e[k];
+                        if (a.residual) v += bf2f(a.residual[(int64_t)b * a.res_stride + n + k]);
+                        y[(int64_t)b * a.y_stride + n + k] = f2bf(v);
+                    }
                 }
             }
+            continue;
         }
-#pragma unroll
-        for (int p = 0; p < P; ++p)
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct) acc[p][ct] = sum[p][ct];
-    }
-
-    // ------------------------------------------------------------ epilogue
-    // lane: rows n0 + 16 w + 4 q + r (r = 0..3) of batch rows 16 ct + j.
-    // The activated tile goes through LDS (a window buffer, free now) so
-    // that the residual is read and the output written in 16-byte chunks of
-    // 8 consecutive rows of one batch row: the fragment layout would make
-    // every store instruction touch 16 batch rows with 2-byte writes.
-    if (a.epi != EPI_ARGMAX) {
-        __syncthreads();  // every wave is done with the window buffers
-        float *tb = (float *)lds;  // [16 NT batch rows][64 rows], row stride TSTRIDE bytes
+        // argmax: the tile's best key per batch row, merged over the tiles by
+        // an atomic maximum; the last tile writes the indices and clears the
+        // keys
+        uint64_t *mk = (uint64_t *)(lds + merge_off);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
-            f32x4 e4;
+            const int32_t b = ct * 16 + (int32_t)j;
+            uint64_t best = 0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int32_t n = n0 + 16 * w + 4 * (int32_t)q + r;
-                const float z = acc[0][ct][r] + ((a.bias && n < a.N) ? bf2f(a.bias[n]) : 0.0f);
-                float e;
-                if (a.epi == EPI_GELU_TANH) {
-                    e = gelu_tanh(z);
-                    const int32_t b = ct * 16 + (int32_t)j;
-                    if (a.logits && n < a.N && b < a.B)
-                        a.logits[(int64_t)b * a.N + n] = z;  // pre-activation for the backward pass
-                } else if (a.epi == EPI_SWIGLU) e = silu(z) * acc[P - 1][ct][r];
-                else e = z;
-                e4[r] = e;
+                if (n < a.N && b < a.B) {
+                    const float z = acc[0][ct][r];
+                    if (a.logits) a.logits[(int64_t)b * a.N + n] = z;
+                    const uint64_t key = ((uint64_t)orderable(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
+                    best = key > best ? key : best;
+                }
             }
-            *(f32x4 *)((char *)tb + (uint32_t)(ct * 16 + (int32_t)j) * TSTRIDE + (uint32_t)(16 * w + 4 * (int32_t)q) * 4u) = e4;
+            uint64_t o = __shfl_xor(best, 16);
+            best = o > best ? o : best;
+            o = __shfl_xor(best, 32);
+            best = o > best ? o : best;
+            if (q == 0) mk[w * GEMM_MAX_BATCH + b] = best;
         }
         __syncthreads();
-        uint16_t *y = (uint16_t *)a.y;
-        // 16-byte accesses need 16-byte aligned rows of y (and of the residual)
-        const bool vy = ((uintptr_t)y & 15u) == 0 && (a.y_stride & 7) == 0 &&
-                        (!a.residual || (((uintptr_t)a.residual & 15u) == 0 && (a.res_stride & 7) == 0));
-        for (int32_t idx = (int32_t)threadIdx.x; idx < NT * 16 * 8; idx += GEMM_THREADS) {
-            const int32_t b = idx >> 3, c8 = idx & 7, n = n0 + 8 * c8;
-            if (b >= a.B || n >= a.N) continue;
-            const float *src = (const float *)((const char *)tb + (uint32_t)b * TSTRIDE + (uint32_t)c8 * 32u);
-            const f32x4 lo = *(const f32x4 *)src, hi = *(const f32x4 *)(src + 4);
-            float e[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            if (vy && n + 8 <= a.N) {
-                if (a.residual) {
-                    const u32x4 rv = *(const u32x4 *)(a.residual + (int64_t)b * a.res_stride + n);
-                    const uint32_t rr[4] = {rv.x, rv.y, rv.z, rv.w};
+        if ((int32_t)tid < a.B) {
+            const int32_t b = (int32_t)tid;
+            uint64_t best = mk[b];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        e[2 * k] += bf2f(rr[k] & 0xFFFFu);
-                        e[2 * k + 1] += bf2f(rr[k] >> 16);
-                    }
-                }
-                u32x4 o;
-                o.x = (uint32_t)f2bf(e[0]) | ((uint32_t)f2bf(e[1]) << 16);
-                o.y = (uint32_t)f2bf(e[2]) | ((uint32_t)f2bf(e[3]) << 16);
-                o.z = (uint32_t)f2bf(e[4]) | ((uint32_t)f2bf(e[5]) << 16);
-                o.w = (uint32_t)f2bf(e[6]) | ((uint32_t)f2bf(e[7]) << 16);
-                *(u32x4 *)(y + (int64_t)b * a.y_stride + n) = o;
-            } else {
-                for (int k = 0; k < 8 && n + k < a.N; ++k) {
-                    float v = e[k];
-                    if (a.residual) v += bf2f(a.residual[(int64_t)b * a.res_stride + n + k]);
-                    y[(int64_t)b * a.y_stride + n + k] = f2bf(v);
-                }
-            }
+            for (int ww = 1; ww < 4; ++ww)
+                best = mk[ww * GEMM_MAX_BATCH + b] > best ? mk[ww * GEMM_MAX_BATCH + b] : best;
+            __hip_atomic_fetch_max(&a.keys[b], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        return;
-    }
-    // argmax: the tile's best key per batch row, merged over the tiles by an
-    // atomic maximum; the last tile writes the indices and clears the keys
-    uint64_t *mk = (uint64_t *)(lds + merge_off);
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-        const int32_t b = ct * 16 + (int32_t)j;
-        uint64_t best = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int32_t n = n0 + 16 * w + 4 * (int32_t)q + r;
-            if (n < a.N && b < a.B) {
-                const float z = acc[0][ct][r];
-                if (a.logits) a.logits[(int64_t)b * a.N + n] = z;
-                const uint64_t key = ((uint64_t)orderable(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
-                best = key > best ? key : best;
-            }
+        __builtin_amdgcn_s_waitcnt(0);  // this tile's maxima and logits are done
+        __syncthreads();
+        if (tid == 0u) {
+            const uint32_t old =
+                __hip_atomic_fetch_add(&a.tickets[a.ntiles], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int32_t last = old == (uint32_t)(a.ntiles - 1) ? 1 : 0;
+            if (last) __hip_atomic_store(&a.tickets[a.ntiles], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *s_last = last;
         }
-        uint64_t o = __shfl_xor(best, 16);
-        best = o > best ? o : best;
-        o = __shfl_xor(best, 32);
-        best = o > best ? o : best;
-        if (q == 0) mk[w * GEMM_MAX_BATCH + b] = best;
-    }
-    __syncthreads();
-    if ((int32_t)threadIdx.x < a.B) {
-        const int32_t b = (int32_t)threadIdx.x;
-        uint64_t best = mk[b];
-#pragma unroll
-        for (int ww = 1; ww < 4; ++ww) best = mk[ww * GEMM_MAX_BATCH + b] > best ? mk[ww * GEMM_MAX_BATCH + b] : best;
-        __hip_atomic_fetch_max(&a.keys[b], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this tile's maxima and logits are done
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t old =
-            __hip_atomic_fetch_add(&a.tickets[a.ntiles], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int32_t last = old == (uint32_t)(a.ntiles - 1) ? 1 : 0;
-        if (last) __hip_atomic_store(&a.tickets[a.ntiles], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_last = last;
-    }
-    __syncthreads();
-    if (*s_last != 0 && (int32_t)threadIdx.x < a.B) {
-        const int32_t b = (int32_t)threadIdx.x;
-        const uint64_t key = __hip_atomic_load(&a.keys[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.keys[b], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ((int32_t *)a.y)[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
-        if (a.maxval) a.maxval[b] = unorderable((uint32_t)(key >> 32));
+        __syncthreads();
+        if (*s_last != 0 && (int32_t)tid < a.B) {
+            const int32_t b = (int32_t)tid;
+            const uint64_t key = __hip_atomic_load(&a.keys[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.keys[b], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ((int32_t *)a.y)[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
+            if (a.maxval) a.maxval[b] = unorderable((uint32_t)(key >> 32));
+        }
     }
 }
 
@@ -471,9 +534,11 @@ hipError_t launch_gemm(const GemmLaunch &G, bool swiglu, size_t lds, hipStream_t
     for (int i = 0; i < G.n; ++i) {
         const GemmArgs &a = G.s[i];
         // the kernel's window and slice arithmetic assumes these
-        if (a.ntiles < 1 || a.nslices < 1 || a.B < 1 || a.B > GEMM_MAX_BATCH || (a.B + 15) / 16 != nt ||
-            a.kslice < GEMM_KWIN || (a.kslice % GEMM_KWIN) || (int64_t)a.kslice * (a.nslices - 1) >= a.K ||
-            G.start[i + 1] - G.start[i] != a.ntiles * a.nslices)
+        // (every workgroup of a stage has at least one unit: contributor
+        // counts rely on it)
+        if (a.ntiles < 1 || a.B < 1 || a.B > GEMM_MAX_BATCH || (a.B + 15) / 16 != nt || a.K < 1 ||
+            a.nwin != (a.K + GEMM_KWIN - 1) / GEMM_KWIN || a.wgs < 1 || (int64_t)a.wgs > (int64_t)a.ntiles * a.nwin ||
+            G.start[i + 1] - G.start[i] != a.wgs || (gemm_tiles_shared(a.ntiles, a.nwin, a.wgs) && !a.part))
             return hipErrorInvalidValue;
     }
     switch (nt * 2 + (swiglu ? 1 : 0)) {
