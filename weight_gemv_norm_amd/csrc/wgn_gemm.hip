@@ -506,6 +506,76 @@ __global__ __launch_bounds__(256) void norm_rows64_kernel(const uint16_t *x, int
         *(u32x4 *)(yr + (int64_t)i * 8) = (u32x4){o[0], o[1], o[2], o[3]};
     }
 }
+// The same norm with the row held in registers (at most C 16-byte chunks per
+// thread, K <= 2048 C): the row, its gain and its shift are loaded once, at
+// the start, instead of once per pass.  Each thread takes the same chunks in
+// the same order and the sums are the same, so x-hat has the same bits.
+template <bool LAYER, int C>
+__global__ __launch_bounds__(256) void norm_rows64_reg_kernel(const uint16_t *x, int64_t x_stride,
+                                                              const uint16_t *gamma, const uint16_t *beta, double eps,
+                                                              uint16_t *y, int32_t K) {
+#pragma clang fp contract(off)
+    __shared__ double red[4];
+    const uint16_t *xr = x + (int64_t)blockIdx.x * x_stride;
+    uint16_t *yr = y + (int64_t)blockIdx.x * K;
+    const int32_t n8 = K >> 3;
+    u32x4 v[C], gv[C], bv[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int32_t i = (int32_t)threadIdx.x + 256 * c;
+        const bool in = i < n8;
+        v[c] = in ? *(const u32x4 *)(xr + (int64_t)i * 8) : (u32x4){0u, 0u, 0u, 0u};
+        gv[c] = (in && gamma) ? *(const u32x4 *)(gamma + (int64_t)i * 8)
+                              : (u32x4){0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+        bv[c] = (in && beta) ? *(const u32x4 *)(beta + (int64_t)i * 8) : (u32x4){0u, 0u, 0u, 0u};
+    }
+    double mu = 0.0;
+    if constexpr (LAYER) {
+        double s = 0.0;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            if ((int32_t)threadIdx.x + 256 * c >= n8) break;
+            const uint32_t vv[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s += (double)bf2f(vv[e] & 0xFFFFu) + (double)bf2f(vv[e] >> 16);
+        }
+        mu = block_sum(s, red) / (double)K;
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        if ((int32_t)threadIdx.x + 256 * c >= n8) break;
+        const uint32_t vv[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const double lo = (double)bf2f(vv[e] & 0xFFFFu) - mu, hi = (double)bf2f(vv[e] >> 16) - mu;
+            ss += lo * lo;
+            ss += hi * hi;
+        }
+    }
+    const double r = 1.0 / sqrt(block_sum(ss, red) / (double)K + eps);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int32_t i = (int32_t)threadIdx.x + 256 * c;
+        if (i >= n8) break;
+        const uint32_t vv[4] = {v[c].x, v[c].y, v[c].z, v[c].w}, gg[4] = {gv[c].x, gv[c].y, gv[c].z, gv[c].w},
+                       bb[4] = {bv[c].x, bv[c].y, bv[c].z, bv[c].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            double t[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const double xv = (double)bf2f((vv[e] >> (16 * h)) & 0xFFFFu);
+                const double g = (double)bf2f((gg[e] >> (16 * h)) & 0xFFFFu);
+                t[h] = LAYER ? (xv - mu) * r * g + (double)bf2f((bb[e] >> (16 * h)) & 0xFFFFu) : xv * r * g;
+            }
+            o[e] = (uint32_t)f64_to_bf16(t[0]) | ((uint32_t)f64_to_bf16(t[1]) << 16);
+        }
+        *(u32x4 *)(yr + (int64_t)i * 8) = (u32x4){o[0], o[1], o[2], o[3]};
+    }
+}
+
 __global__ void zero_words_kernel(uint32_t *p, int32_t n) {
     const int32_t i = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
     if (i < n) p[i] = 0u;
@@ -561,12 +631,24 @@ hipError_t launch_zero_words(uint32_t *p, int32_t n, hipStream_t s) {
 hipError_t launch_norm_rows64(const uint16_t *x, int64_t x_stride, const uint16_t *gamma, const uint16_t *beta,
                               float eps, bool layer, uint16_t *y, int32_t rows, int32_t K, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    if (layer)
-        hipLaunchKernelGGL(norm_rows64_kernel<true>, dim3(rows), dim3(256), 0, s, x, x_stride, gamma, beta,
-                           (double)eps, y, K);
+    const int32_t c = ((K >> 3) + 255) / 256;  // 16-byte chunks per thread
+    const double e = (double)eps;
+#define WGN_NORM_REG(L, C) hipLaunchKernelGGL((norm_rows64_reg_kernel<L, C>), dim3(rows), dim3(256), 0, s, x, \
+                                              x_stride, gamma, beta, e, y, K)
+    if (c <= 1) {
+        if (layer) WGN_NORM_REG(true, 1);
+        else WGN_NORM_REG(false, 1);
+    } else if (c == 2) {
+        if (layer) WGN_NORM_REG(true, 2);
+        else WGN_NORM_REG(false, 2);
+    } else if (c <= 4) {
+        if (layer) WGN_NORM_REG(true, 4);
+        else WGN_NORM_REG(false, 4);
+    } else if (layer)
+        hipLaunchKernelGGL(norm_rows64_kernel<true>, dim3(rows), dim3(256), 0, s, x, x_stride, gamma, beta, e, y, K);
     else
-        hipLaunchKernelGGL(norm_rows64_kernel<false>, dim3(rows), dim3(256), 0, s, x, x_stride, gamma, beta,
-                           (double)eps, y, K);
+        hipLaunchKernelGGL(norm_rows64_kernel<false>, dim3(rows), dim3(256), 0, s, x, x_stride, gamma, beta, e, y, K);
+#undef WGN_NORM_REG
     return hipGetLastError();
 }
 
