@@ -4,7 +4,8 @@
 // of (row n, group k/128).
 //
 // Each lane owns 16 bytes (32 codes, a quarter of a group) of a row per 1 KB
-// slice; a wave takes 4 rows at a time, all their loads issued before use.
+// slice; a wave takes 4 rows at a time, the loads of several such items
+// issued together before use.
 // Codes become BF16 pairs without conversion instructions: the byte permute
 // v_perm_b32 places one code in the mantissa of each half and an OR with
 // 0x4300 gives the BF16 values 128 + q, exact; v_dot2_f32_bf16 then forms
@@ -34,6 +35,13 @@ constexpr int I4_ROWS = WGN_I4_ROWS;         // rows per wave at a time
 #endif
 constexpr int I4_WAVES = WGN_I4_WAVES;
 constexpr int I4_BLOCKS_PER_CU = WGN_I4_BLOCKS_PER_CU;  // cap of the grid (workgroups stride over row groups)
+#ifndef WGN_I4_BATCH
+#define WGN_I4_BATCH 2
+#endif
+// items whose loads are issued together, at batch 1 and 2 (one at larger
+// batches, whose registers go to x; measured: 2 is 5 % faster than 1 at batch
+// 1, 4 slower than 2, and 2 slower than 1 at batch 8)
+constexpr int I4_BATCH = WGN_I4_BATCH;
 constexpr uint32_t I4_MAGIC = 0x43004300u;   // BF16 128.0 in both halves
 constexpr int I4_MAX_LDS = 160 * 1024;       // dynamic LDS of one workgroup on gfx950
 
@@ -83,77 +91,119 @@ __global__ __launch_bounds__(64 * I4_WAVES) void gemv_int4_kernel(const uint16_t
 
     const int32_t slices = (half + 1023) / 1024;
     const int32_t groups = (N + I4_ROWS * I4_WAVES - 1) / (I4_ROWS * I4_WAVES);
-    for (int32_t rg = blockIdx.x; rg < groups; rg += gridDim.x) {
+    // One item is a slice c of the wave's 4 rows of row group rg; a
+    // workgroup's items are (rg, c) for rg = blockIdx.x, + gridDim.x, ... in
+    // order.  Items are taken IB at a time: all their codes, scales and
+    // zeros are requested before the first is used, so one memory round trip
+    // serves IB items.  Loads past the last item re-read the last
+    // row group (in range, never used), so every pass issues the same loads.
+    struct Item {
+        u32x4 code[I4_ROWS];
+        float s[I4_ROWS], z[I4_ROWS];
+    };
+    // Buffer loads with 32-bit offsets (the host keeps the codes below 2 GB):
+    // one offset register per load, so that computing the next item's
+    // addresses needs no registers a load in flight still owns.
+    const __amdgpu_buffer_rsrc_t rcode = __builtin_amdgcn_make_buffer_rsrc((void *)W4, (short)0,
+                                                                           (int)((int64_t)N * half), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc((void *)sc, (short)0,
+                                                                         (int)((int64_t)N * ng * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rzr = __builtin_amdgcn_make_buffer_rsrc((void *)zr, (short)0,
+                                                                         (int)((int64_t)N * ng * 2), 0x00020000);
+    auto load = [&](int32_t rg, int32_t c, Item &it) {
+        rg = min(rg, groups - 1);
         const int32_t n0 = (rg * I4_WAVES + w) * I4_ROWS;
-        float acc[I4_ROWS][B];
-#pragma unroll
-        for (int r = 0; r < I4_ROWS; ++r)
-#pragma unroll
-            for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
-        for (int32_t c = 0; c < slices; ++c) {
-            const int32_t byte0 = (c * 64 + lane) * 16;    // this lane's bytes within a row
-            const bool act = byte0 < half;
-            const int32_t kb = act ? byte0 * 2 : 0;        // first k of those bytes
-            const int32_t g = kb / 128;
-            u32x4 code[I4_ROWS];
-            float s[I4_ROWS], z[I4_ROWS];
-#pragma unroll
-            for (int r = 0; r < I4_ROWS; ++r) {
-                const int32_t n = min(n0 + r, N - 1);      // in range; rows past N are not stored
-                code[r] = *(const u32x4 *)(W4 + (size_t)n * half + (act ? byte0 : 0));
-                s[r] = bf2f(sc[(size_t)n * ng + g]);
-                z[r] = bf2f(zr[(size_t)n * ng + g]);
-            }
-            if (act) {
-                // x of every batch row for this lane's 32 inputs, and their sums
-                uint32_t xw[B][16];
-                float S[B];
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    const u32x4 *xp = (const u32x4 *)(sx + (size_t)b * K + kb);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const u32x4 v = xp[u];
-                        xw[b][4 * u] = v.x; xw[b][4 * u + 1] = v.y; xw[b][4 * u + 2] = v.z; xw[b][4 * u + 3] = v.w;
-                    }
-                    S[b] = ssum[b * K32 + kb / 32];
-                }
-#pragma unroll
-                for (int r = 0; r < I4_ROWS; ++r) {
-                    // the row's 16 code pairs as BF16 (128 + q) pairs, decoded once for all batch rows
-                    const uint32_t cw[4] = {code[r].x, code[r].y, code[r].z, code[r].w};
-                    uint32_t pr[16];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const uint32_t lo = cw[u] & 0x0F0F0F0Fu, hi = (cw[u] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            // bytes [lo_j, 0, hi_j, 0]: codes of k = 2j (low half) and 2j+1 (high half)
-                            const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
-                            pr[4 * u + j] = __builtin_amdgcn_perm(hi, lo, sel) | I4_MAGIC;
-                        }
-                    }
-#pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        float dot = 0.0f;
-#pragma unroll
-                        for (int m = 0; m < 16; ++m)
-                            dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr[m]),
-                                                                  __builtin_bit_cast(bf16x2, xw[b][m]), dot, false);
-                        acc[r][b] += s[r] * dot + (z[r] - 128.0f * s[r]) * S[b];
-                    }
-                }
-            }
-        }
+        const int32_t byte0 = (c * 64 + lane) * 16;  // this lane's bytes within a row
+        const bool act = byte0 < half;
+        const uint32_t g = (uint32_t)(act ? byte0 * 2 : 0) / 128u;
 #pragma unroll
         for (int r = 0; r < I4_ROWS; ++r) {
+            const uint32_t n = (uint32_t)min(n0 + r, N - 1);  // in range; rows past N are not stored
+            it.code[r] = __builtin_amdgcn_raw_buffer_load_b128(rcode, n * (uint32_t)half + (act ? byte0 : 0), 0, 0);
+            it.s[r] = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rsc, (n * (uint32_t)ng + g) * 2u, 0, 0));
+            it.z[r] = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rzr, (n * (uint32_t)ng + g) * 2u, 0, 0));
+        }
+    };
+    float acc[I4_ROWS][B];
+#pragma unroll
+    for (int r = 0; r < I4_ROWS; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+    auto use = [&](int32_t rg, int32_t c, const Item &it) {
+        const int32_t byte0 = (c * 64 + lane) * 16;
+        if (byte0 < half) {
+            const int32_t kb = byte0 * 2;  // first k of this lane's bytes
+            // x of every batch row for this lane's 32 inputs, and their sums
+            uint32_t xw[B][16];
+            float S[B];
 #pragma unroll
             for (int b = 0; b < B; ++b) {
-                const float t = wave_sum_last(acc[r][b]);
-                if (lane == 63 && n0 + r < N)
-                    y[(size_t)b * ys + n0 + r] = __builtin_bit_cast(uint16_t, (__bf16)t);
+                const u32x4 *xp = (const u32x4 *)(sx + (size_t)b * K + kb);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const u32x4 v = xp[u];
+                    xw[b][4 * u] = v.x; xw[b][4 * u + 1] = v.y; xw[b][4 * u + 2] = v.z; xw[b][4 * u + 3] = v.w;
+                }
+                S[b] = ssum[b * K32 + kb / 32];
+            }
+#pragma unroll
+            for (int r = 0; r < I4_ROWS; ++r) {
+                // the row's 16 code pairs as BF16 (128 + q) pairs, decoded once for all batch rows
+                const uint32_t cw[4] = {it.code[r].x, it.code[r].y, it.code[r].z, it.code[r].w};
+                uint32_t pr[16];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t lo = cw[u] & 0x0F0F0F0Fu, hi = (cw[u] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        // bytes [lo_q, 0, hi_q, 0]: codes of k = 2q (low half) and 2q+1 (high half)
+                        const uint32_t sel = (uint32_t)q | (0x0Cu << 8) | ((uint32_t)(4 + q) << 16) | (0x0Cu << 24);
+                        pr[4 * u + q] = __builtin_amdgcn_perm(hi, lo, sel) | I4_MAGIC;
+                    }
+                }
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    float dot = 0.0f;
+#pragma unroll
+                    for (int m = 0; m < 16; ++m)
+                        dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr[m]),
+                                                              __builtin_bit_cast(bf16x2, xw[b][m]), dot, false);
+                    acc[r][b] += it.s[r] * dot + (it.z[r] - 128.0f * it.s[r]) * S[b];
+                }
             }
         }
+        if (c == slices - 1) {
+            const int32_t n0 = (rg * I4_WAVES + w) * I4_ROWS;
+#pragma unroll
+            for (int r = 0; r < I4_ROWS; ++r) {
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const float t = wave_sum_last(acc[r][b]);
+                    if (lane == 63 && n0 + r < N)
+                        y[(size_t)b * ys + n0 + r] = __builtin_bit_cast(uint16_t, (__bf16)t);
+                    acc[r][b] = 0.0f;
+                }
+            }
+        }
+    };
+    constexpr int IB = B <= 2 ? I4_BATCH : 1;
+    int32_t rg = blockIdx.x, c = 0;
+    while (rg < groups) {
+        Item it[IB];
+        int32_t rgs[IB], cs[IB];
+#pragma unroll
+        for (int u = 0; u < IB; ++u) {
+            rgs[u] = rg;
+            cs[u] = c;
+            load(rg, c, it[u]);
+            if (++c == slices) {
+                c = 0;
+                rg += gridDim.x;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < IB; ++u)
+            if (rgs[u] < groups) use(rgs[u], cs[u], it[u]);
     }
 }
 
