@@ -374,9 +374,10 @@ void wgn_chain_destroy(wgn_chain *chain);
  * without one.  The workspace is sized by wgn_chain_workspace_bytes for the
  * same opts (wgn_workspace_bytes covers every mode).
  * batch in [17, 128], or opts->path == 3 at any batch: the stages run in list
- * order through the wgn_gemm_norm path, consecutive independent stages that
- * read the same input with the same normalisation (Q, K and V) in one launch
- * after one norm pass (a plan must not prefetch, opts must not trace or force
+ * order through the wgn_gemm_norm path, up to 4 consecutive independent
+ * stages of one epilogue family in one launch (Q, K, V and an O product that
+ * reads its own input), the normalised ones among them reading one x-hat made
+ * by one norm pass (a plan must not prefetch, opts must not trace or force
  * the vector path: WGN_E_UNSUPPORTED); the workspace (wgn_workspace_bytes at
  * that batch) needs no zero fill, the call clears its counters first. */
 wgn_status wgn_layer_chain(const wgn_stage *stages, int32_t n_stages, int32_t batch,

@@ -1806,13 +1806,15 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
     a.nb = nb;
     int32_t bad = 0;
     if (P.lds_total() > LDS_BUDGET) ++bad;
-    // the all-wave normalisation split covers every (item, lane-in-item)
-    // once for every item count the kernel uses (items = (source, batch
-    // row) pairs, padded to a power of two, at most MAX_SRC x MAX_BATCH), and
-    // each item's statistics sit in the waves and slots the combine step reads
-    {
-        const int32_t nw = WAVES;
+    // both normalisation splits cover every (item, lane-in-item) once for
+    // every item count the kernel uses (items = (source, batch row) pairs,
+    // padded to a power of two, at most MAX_SRC x MAX_BATCH): the one-wave
+    // split over min(items, WAVES) waves, no item spanning more than one
+    // wave, and the spread split over WAVES waves, each item's statistics in
+    // the waves and slots its combine step reads
+    for (int32_t spread = 0; spread <= 1; ++spread) {
         for (int32_t nq = 1; nq <= MAX_SRC * MAX_BATCH; nq *= 2) {
+            const int32_t nw = spread ? WAVES : std::min<int32_t>(nq, WAVES);
             std::vector<std::vector<int32_t>> cover(nq);
             for (int32_t w = 0; w < nw; ++w)
                 for (uint32_t lane = 0; lane < 64; ++lane) {
@@ -1821,6 +1823,7 @@ int32_t wgn_partition_selftest(const wgn_stage *stages, int32_t n_stages, int32_
                     if (!S.active) continue;
                     if (w < S.w0 || w >= S.w1 || S.sub < 0 || S.sub >= S.lanes) ++bad;
                     if (S.w1 - S.w0 == 1 && S.slot != S.rslot) ++bad;
+                    if (!spread && (S.w1 != S.w0 + 1 || S.lanes > 64)) ++bad;
                     cover[S.row].push_back(S.sub);
                 }
             for (int32_t r = 0; r < nq; ++r) {

@@ -279,28 +279,113 @@ __device__ __forceinline__ void trace_point(const KArgs &a, int32_t p, int32_t g
 }
 
 // ------------------------------------------------------ normalisation (all waves)
-// The inputs of a phase are normalised by all WAVES waves of the workgroup
+// The inputs of a phase are normalised by the waves of the workgroup
 // together.  The work items are the (job, batch row) pairs -- item
 // q = j * Pb + b, Pb = batch rounded up to a power of two, the number of items
-// padded to a power of two -- and they are spread over the waves like rows by
-// norm_split: an item over one or more whole waves when there are at most
-// WAVES items, several items in one wave otherwise.  Each lane serves one
-// item and walks a strided share of its 16-byte chunks, so a wave carries one
-// job's latency chain, not one per job.  Sums are formed per chunk in FP32
-// (chunk_stat) and accumulated in FP64, reduced inside the wave, posted per
-// wave in LDS and combined in wave order after a barrier: the statistics are
-// as good as exact and their order is fixed.
-__device__ __forceinline__ double2 *norm_stats(char *lds, int32_t w, int32_t slot) {
-    return (double2 *)(lds + LDS_STATS_OFF) + (w * STATS_ROWS + slot);
+// P padded to a power of two -- and they are spread over the waves like rows
+// by norm_split.  Each lane serves one item and walks a strided share of its
+// 16-byte chunks.  Sums are formed per chunk in FP32 (chunk_stat),
+// accumulated in FP64 and reduced inside the wave, so the statistics are as
+// good as exact and their order is fixed.  Two splits:
+//   * batch 3 and above (at least 4 items): never more than one wave per
+//     item (the extra waves idle, or a wave holds several items); every lane
+//     of an item then holds its statistics after the wave's reduction, and
+//     no barrier or LDS round trip lies between the statistics and the
+//     normalisation;
+//   * batch 1 and 2 (a few items): an item spreads over several whole waves,
+//     whose partial statistics are posted in LDS and combined in wave order
+//     after a barrier -- shorter per-lane loops, which beat the saved barrier
+//     there (measured: batch-1 decode step 740 against 742 us; LayerNorm
+//     chain at batch 4 and 16 530 and 685 against 544 and 725 us).
+// The split is fixed per kernel instance (one code path each: the batch-1
+// kernel spills to scratch with both).
+template <int B>
+constexpr bool norm_one_wave() { return B >= 3; }
+
+// log2 of the padded item count of the phase's jobs
+__device__ __forceinline__ int32_t norm_items_log2(const NormHdr &J) {
+    const int32_t lb = J.nb <= 1 ? 0 : 32 - wgn_clz((uint32_t)(J.nb - 1));
+    const int32_t lj = J.njobs <= 1 ? 0 : 32 - wgn_clz((uint32_t)(J.njobs - 1));
+    return lb + lj;
 }
 
 struct NormItem {
     NormSplit S;
-    int32_t j, b;  // job and batch row of this lane's item
-    bool active;
+    int32_t j, b;        // job and batch row of this lane's item
+    bool active;         // this lane serves a real item
+    bool wave_active;    // this wave serves items at all
 };
 __device__ __forceinline__ NormItem norm_item(const NormHdr &J, int32_t w, uint32_t lane, int32_t nw) {
     NormItem it;
+    const int32_t lb = J.nb <= 1 ? 0 : 32 - wgn_clz((uint32_t)(J.nb - 1));
+    const int32_t P = 1 << norm_items_log2(J);
+    const int32_t nwe = P < nw ? P : nw;  // waves that serve items: one wave per item at most
+    it.wave_active = w < nwe;
+    it.S = norm_split(P, it.wave_active ? w : 0, lane, nwe);
+    it.j = it.S.row >> lb;
+    it.b = it.S.row & ((1 << lb) - 1);
+    it.active = it.wave_active && it.S.active && it.j < J.njobs && it.b < J.nb;
+    return it;
+}
+
+// One-wave split: statistics of this lane's item, then its share of the item
+// normalised and rounded to BF16 in place.
+__device__ void norm_item_apply(char *lds, int32_t w, uint32_t lane, int32_t nw) {
+    const NormHdr &J = *(const NormHdr *)(lds + LDS_NORM_OFF);
+    const NormItem it = norm_item(J, w, lane, nw);
+    if (!it.wave_active) return;
+    const NormSplit &S = it.S;
+    const NormJob &jb = J.job[it.active ? it.j : 0];
+    const bool layer = jb.norm == NORM_LAYER;
+    const int32_t K = jb.K, n8 = it.active ? K >> 3 : 0;
+    uint16_t *dst = (uint16_t *)(lds + J.x_off + ((size_t)(it.active ? it.b : 0) * J.xb + jb.xoff) * 2);
+    double s1 = 0.0, s2 = 0.0;
+    for (int32_t i = S.sub; i < n8; i += S.lanes) {
+        const u32x4 v = *(const u32x4 *)(dst + i * 8);
+        s2 += chunk_stat(v, false);
+        if (layer) s1 += chunk_stat(v, true);
+    }
+    if (S.lpr == 64) {
+        s1 = wave_sum_f64(s1);
+        s2 = wave_sum_f64(s2);
+    } else {
+        s1 = group_sum_f64(s1, S.lpr);
+        s2 = group_sum_f64(s2, S.lpr);
+    }
+    if (!it.active) return;
+    float mean = 0.0f, rstd;
+    if (!layer) {
+        rstd = inv_sqrt_mean(s2, K, jb.eps);
+    } else {
+        const double rk = recip_f64((double)K);
+        const double m = s1 * rk;
+        const double var = __builtin_fma(s2, rk, -m * m);  // biased; FP64 sums, see above
+        mean = (float)m;
+        rstd = rsqrt_f64_to_f32((var > 0.0 ? var : 0.0) + (double)jb.eps);
+    }
+    const char *gp = lds + jb.prm;
+    const char *bp = lds + jb.prm + jb.prm_half;
+    for (int32_t i = S.sub; i < n8; i += S.lanes) {
+        const u32x4 v = *(const u32x4 *)(dst + i * 8);
+        const u32x4 gv = jb.has_gamma ? *(const u32x4 *)(gp + i * 16)
+                                      : (u32x4){0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+        const u32x4 bv = jb.has_beta ? *(const u32x4 *)(bp + i * 16) : (u32x4){0u, 0u, 0u, 0u};
+        *(u32x4 *)(dst + i * 8) = chunk_apply(v, gv, bv, mean, rstd, layer);
+    }
+}
+
+// Spread split: statistics over several waves, posted per wave in LDS.
+__device__ __forceinline__ double2 *norm_stats(char *lds, int32_t w, int32_t slot) {
+    return (double2 *)(lds + LDS_STATS_OFF) + (w * STATS_ROWS + slot);
+}
+
+struct NormItemW {
+    NormSplit S;
+    int32_t j, b;  // job and batch row of this lane's item
+    bool active;
+};
+__device__ __forceinline__ NormItemW norm_item_w(const NormHdr &J, int32_t w, uint32_t lane, int32_t nw) {
+    NormItemW it;
     const int32_t lb = J.nb <= 1 ? 0 : 32 - wgn_clz((uint32_t)(J.nb - 1));
     const int32_t lj = J.njobs <= 1 ? 0 : 32 - wgn_clz((uint32_t)(J.njobs - 1));
     it.S = norm_split(1 << (lj + lb), w, lane, nw);
@@ -313,7 +398,7 @@ __device__ __forceinline__ NormItem norm_item(const NormHdr &J, int32_t w, uint3
 // Step 1 (after the inputs have landed in LDS): partial statistics.
 __device__ void norm_all_stats(char *lds, int32_t w, uint32_t lane, int32_t nw) {
     const NormHdr &J = *(const NormHdr *)(lds + LDS_NORM_OFF);
-    const NormItem it = norm_item(J, w, lane, nw);
+    const NormItemW it = norm_item_w(J, w, lane, nw);
     const NormSplit &S = it.S;
     const NormJob &jb = J.job[it.active ? it.j : 0];
     const bool layer = jb.norm == NORM_LAYER;
@@ -344,7 +429,7 @@ __device__ void norm_all_stats(char *lds, int32_t w, uint32_t lane, int32_t nw) 
 // share and round to BF16 in place.
 __device__ void norm_all_apply(char *lds, int32_t w, uint32_t lane, int32_t nw) {
     const NormHdr &J = *(const NormHdr *)(lds + LDS_NORM_OFF);
-    const NormItem it = norm_item(J, w, lane, nw);
+    const NormItemW it = norm_item_w(J, w, lane, nw);
     if (!it.active) return;
     const NormSplit &S = it.S;
     const NormJob &jb = J.job[it.j];
@@ -378,13 +463,20 @@ __device__ void norm_all_apply(char *lds, int32_t w, uint32_t lane, int32_t nw) 
     }
 }
 
-// Both steps with their barriers; every wave calls this for a phase whose
-// run header says it has a normalised input, right before the x-hat barrier.
+// Every wave calls this for a phase whose run header says it has a
+// normalised input, right before the x-hat barrier.  Barriers: one (inputs
+// in LDS, jobs posted), and with the spread split one more (statistics of
+// every wave posted).
+template <int B>
 __device__ __forceinline__ void norm_all(char *lds, int32_t w, uint32_t lane) {
     wg_barrier();  // inputs in LDS, jobs posted
-    norm_all_stats(lds, w, lane, WAVES);
-    wg_barrier();  // statistics of every wave posted
-    norm_all_apply(lds, w, lane, WAVES);
+    if constexpr (norm_one_wave<B>()) {
+        norm_item_apply(lds, w, lane, WAVES);
+    } else {
+        norm_all_stats(lds, w, lane, WAVES);
+        wg_barrier();  // statistics of every wave posted
+        norm_all_apply(lds, w, lane, WAVES);
+    }
 }
 
 
@@ -727,7 +819,7 @@ __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_
     for (int k = 0; k < NS - 1; ++k) load_block<B, D>(a, S, d[k], m[k], lane);
     PendLoads pq = prepare_block<B, D>(a, S, m[NS - 1], lane);
     if constexpr (in_share<false, R>()) share_inputs<B, CHAIN>(a, S, a.p0, lds, lane, w);
-    if (((const RunHdr *)run_buf_s(S, a.p0))->has_norm) norm_all(lds, w, lane);
+    if (((const RunHdr *)run_buf_s(S, a.p0))->has_norm) norm_all<B>(lds, w, lane);
     wg_barrier();  // x-hat of the first phase is ready
     bool ok = abort_flag_get() == 0;
     int32_t p = a.p0;
@@ -763,7 +855,7 @@ __device__ __forceinline__ void stream_wave_il(const KArgs &a, int32_t g, int32_
             if (end && ++p < a.p1) {
                 if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
                 if constexpr (in_share<false, R>()) share_inputs<B, CHAIN>(a, S, p, lds, lane, w);
-                if (((const RunHdr *)run_buf_s(S, p))->has_norm) norm_all(lds, w, lane);
+                if (((const RunHdr *)run_buf_s(S, p))->has_norm) norm_all<B>(lds, w, lane);
                 wg_barrier();  // x-hat of phase p is ready
                 ok = abort_flag_get() == 0;
                 if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
@@ -806,7 +898,7 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
 #pragma unroll
     for (int k = 0; k < NS; ++k) load_any<B, TILE, R>(a, S, d[k], m[k], lane);
     if constexpr (in_share<TILE, R>()) share_inputs<B, CHAIN>(a, S, a.p0, lds, lane, w);
-    if (((const RunHdr *)run_buf_s(S, a.p0))->has_norm) norm_all(lds, w, lane);
+    if (((const RunHdr *)run_buf_s(S, a.p0))->has_norm) norm_all<B>(lds, w, lane);
     wg_barrier();  // x-hat of the first phase is ready
     bool ok = abort_flag_get() == 0;
     int32_t p = a.p0;
@@ -849,7 +941,7 @@ __device__ __forceinline__ void stream_wave(const KArgs &a, int32_t g, int32_t w
             if (end && ++p < a.p1) {
                 if (tw) tl[(p & 1) * 6 + 1] = wall_clock64();
                 if constexpr (in_share<TILE, R>()) share_inputs<B, CHAIN>(a, S, p, lds, lane, w);
-                if (((const RunHdr *)run_buf_s(S, p))->has_norm) norm_all(lds, w, lane);
+                if (((const RunHdr *)run_buf_s(S, p))->has_norm) norm_all<B>(lds, w, lane);
                 wg_barrier();  // x-hat of phase p is ready
                 ok = abort_flag_get() == 0;
                 if (tw) tl[(p & 1) * 6 + 0] = wall_clock64();
@@ -1391,8 +1483,9 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
                 // exit
                 if (in_share<TILE, R>() && h.share_in) wg_barrier();
                 if (h.has_norm) {
+                    // the barriers of norm_all
                     wg_barrier();
-                    wg_barrier();
+                    if constexpr (!norm_one_wave<B>()) wg_barrier();
                 }
                 wg_barrier();
                 __builtin_amdgcn_s_waitcnt(0);  // the gain copies issued before the wait
@@ -1408,7 +1501,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
         }
         stage_epilogue_inputs<B, CHAIN>(a, h, runs, epi, lane);
         __builtin_amdgcn_s_waitcnt(0);  // inputs, gains and epilogue values have landed
-        if (h.has_norm) norm_all(lds, STREAM_WAVES, lane);
+        if (h.has_norm) norm_all<B>(lds, STREAM_WAVES, lane);
         trace_point(a, p, g, 2, lane);
         wg_barrier();  // x-hat ready
         // later phases' run list and tables, read while the streaming waves consume
