@@ -77,10 +77,7 @@ constexpr int EPI_SHARE = WGN_EPI_SHARE;
 // (batch 2-4); the burst rings keep one large block in flight at a phase
 // start and copy on the control wave alone.
 constexpr int IN_SHARE = WGN_IN_SHARE;
-#ifndef WGN_SHARE_IN_MIN_KB
-#define WGN_SHARE_IN_MIN_KB 32
-#endif
-constexpr int SHARE_IN_MIN_BYTES = WGN_SHARE_IN_MIN_KB * 1024;
+constexpr int SHARE_IN_MIN_BYTES = 32 * 1024;
 // Block-buffer rings of the vector path's streaming waves (the matrix-core
 // path always uses ring 0's two buffers).  A wave keeps slots - 1 blocks of
 // `depth` units in flight beyond the one it consumes:
