@@ -55,6 +55,9 @@ def parse():
                     help="with --mode 1: tune an Infinity-Cache prefetch plan (touch passes on a second "
                          "stream, wgn_plan_tune) before timing, and time the plan it keeps")
     ap.add_argument("--tune-reps", type=int, default=15, help="rounds of the prefetch tuner")
+    ap.add_argument("--attn", default="fused", choices=["fused", "launches"],
+                    help="decode_step_attn: attention as phases of the one chain launch, or launches of its own")
+    ap.add_argument("--ring", type=int, default=0, help="decode_step_attn: streaming ring (0 auto, 1..3)")
     ap.add_argument("--slots", type=int, default=None,
                     help="decode-attention workload: cache slots (all valid: the new token takes the last; default 32768); "
                          "decode step with attention: cache slots (default 1024, the new token at slot 960)")
@@ -135,15 +138,17 @@ def main():
                                      vocab=args.vocab)
         n_layers = len(inp["layers"])
         caches = gen.make_kv_caches(B, S, [pos] * B, n_layers=n_layers, nan_tail=False, device=dev)
-        dstep = steps.DecodeStepWithAttention(inp, caches, dev, mode=args.mode)
+        dstep = steps.DecodeStepWithAttention(inp, caches, dev, mode=args.mode, fused=args.attn == "fused",
+                                              ring=args.ring)
         nb = steps.decode_step_bytes(inp)
         kv = n_layers * (2 * B * gen.NKV * (pos + 1) * gen.HEAD_DIM * 2 + 2 * 2 * B * gen.NKV * gen.HEAD_DIM * 2)
         nbytes = nb["total"] + kv
         cfg.update({"hidden": gen.H, "intermediate": gen.I, "layers": n_layers, "vocab": gen.V if "W_lm" in inp
                     else None, "weight_bytes": nb["weights"], "kv_bytes": kv, "slots": S, "position": pos,
                     "algorithmic_bytes": nbytes, "launches_per_step": dstep.n_launches,
-                    "launch": "persistent chains between attention launches"})
-        kernel_name = "chain_kernel+decode_attention_kernel"
+                    "launch": ("one persistent launch, attention as phases" if dstep.fused
+                               else "persistent chains between attention launches")})
+        kernel_name = "chain_kernel" if dstep.fused else "chain_kernel+decode_attention_kernel"
         # one HIP graph per step: 57 launches from Python would leave the GPU idle
         dgraph = dstep.capture()
         launch = dgraph.replay

@@ -321,6 +321,56 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
                             const wgn_chain_opts *opts, void *workspace, size_t ws_bytes,
                             wgn_stream stream, wgn_chain **out);
 
+/* Decode attention as part of a chain: the operation of wgn_decode_attention
+ * (same passages, same cache layout, append and outputs) run inside the
+ * chain's launch, between the stages that write q, k_new and v_new and the
+ * stage that reads out ("Making small PyTorch ops faster on a laptop GPU",
+ * section "A full decode step is a different story"; "One Token, Kernel by
+ * Kernel", sections "The fix: Part 10's split-KV kernel" and "Step 3: where
+ * the 14.8 ms go": attention as a part of the one decode step).
+ *   q       [batch][q_stride]   BF16, q_heads x head_dim per row (read)
+ *   k_new   [batch][k_stride]   BF16, kv_heads x head_dim per row (read; v_new likewise)
+ *   k_cache [batch][kv_heads][slots][head_dim] BF16: slot pos[b] of row b
+ *           is overwritten with k_new (v_cache with v_new)
+ *   pos     [batch] int32 in device memory (out of [0, slots): no append, zero output)
+ *   out     [batch][out_stride] BF16, q_heads x head_dim per row (written)
+ *   scale   the score scale (finite; 1/sqrt(head_dim) in the pages' model)
+ * head_dim must be 128 and q_heads / kv_heads at most 8 (WGN_E_UNSUPPORTED
+ * otherwise).  Pointers 16-byte aligned (pos 4-byte), strides multiples of 8
+ * elements and at least the row length when batch > 1; out, the caches and
+ * the inputs may not overlap.  The item runs as two phases without weights:
+ * partial results per chunk of the cache, then their merge; the product phases
+ * around them keep streaming weights ahead. */
+typedef struct wgn_attn_stage {
+    const void *q;
+    int64_t q_stride;
+    const void *k_new;
+    int64_t k_stride;
+    const void *v_new;
+    int64_t v_stride;
+    void *k_cache;
+    void *v_cache;
+    const int32_t *pos;
+    void *out;
+    int64_t out_stride;
+    int32_t q_heads, kv_heads, slots, head_dim;
+    float scale;
+} wgn_attn_stage;
+
+/* A chain of `stages` with attention items: item i runs after stages
+ * [0, attn_before[i]) and before stage attn_before[i] (non-decreasing, in
+ * [0, n_stages]).  Hoisting (opts.no_fuse = 0) is not applied to such a chain.
+ * Otherwise as wgn_chain_workspace_bytes / wgn_chain_create; the workspace
+ * also holds the attention partials.  A chain created here runs with
+ * wgn_chain_run, wgn_chain_check and the other chain calls. */
+size_t wgn_chain_attn_workspace_bytes(const wgn_stage *stages, int32_t n_stages, const wgn_attn_stage *attn,
+                                      const int32_t *attn_before, int32_t n_attn, int32_t batch,
+                                      const wgn_chain_opts *opts);
+wgn_status wgn_chain_create_attn(const wgn_stage *stages, int32_t n_stages, const wgn_attn_stage *attn,
+                                 const int32_t *attn_before, int32_t n_attn, int32_t batch,
+                                 const wgn_chain_opts *opts, void *workspace, size_t ws_bytes,
+                                 wgn_stream stream, wgn_chain **out);
+
 /* Enqueue one run of the chain on `stream` (no host synchronisation). */
 wgn_status wgn_chain_run(const wgn_chain *chain, wgn_stream stream);
 

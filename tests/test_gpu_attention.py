@@ -142,20 +142,34 @@ def test_decode_attention_graph_replays():
         t["k_new"].mul_(0.5)
 
 
-@pytest.mark.parametrize("batch,pos", [(1, [960]), (2, [960, 37])])
-def test_decode_step_with_attention_teacher_forced(batch, pos):
+@pytest.mark.parametrize("fused,batch,pos,slots,mode,ring", [
+    (False, 1, [960], 1024, 0, 0), (False, 2, [960, 37], 1024, 0, 0),
+    (True, 1, [960], 1024, 0, 0),                 # the pages' step: one launch, attention inside
+    (True, 2, [960, 37], 1024, 0, 0),
+    (True, 4, [1023, 0, 500, -1], 1024, 0, 0),    # full cache, first slot, a row with no valid slot
+    (True, 1, [4223], 4224, 0, 0),                # several passes per chunk, ragged last chunk
+    (True, 3, [4000, 17, 2047], 4224, 0, 0),
+    (True, 2, [960, 37], 1024, 0, 2),             # the 5 x 8-unit ring
+    (True, 5, [960, 37, 1023, 0, 640], 1024, 0, 0),  # matrix-core path
+    (True, 2, [960, 37], 1024, 1, 0),             # one launch per phase
+])
+def test_decode_step_with_attention_teacher_forced(fused, batch, pos, slots, mode, ring):
     """Two decoder blocks whose attention is computed (Q/K/V -> decode
-    attention over a 1,024-slot cache -> O -> MLP), then the LM head: every
-    stage is checked against the oracle on the GPU's own inputs to it, the
-    caches bit for bit, and the argmax."""
+    attention over the cache -> O -> MLP), then the LM head: every stage is
+    checked against the oracle on the GPU's own inputs to it, the caches bit
+    for bit, and the argmax.  fused: attention as phases of the chain's one
+    launch; else its own launches between chains."""
     from weight_gemv_norm_amd import steps
     from tests.gpu_util import check_argmax
-    say("decode step with attention batch %d pos %s" % (batch, pos))
+    say("decode step with attention fused %s batch %d pos %s slots %d mode %d ring %d"
+        % (fused, batch, pos, slots, mode, ring))
     dev = "cuda"
     inp = gen.make_stage_tensors("decode_step_1536x28", device=dev, batch=batch, n_layers=2, vocab=4096)
-    caches = gen.make_kv_caches(batch, 1024, pos, n_layers=2, device=dev)
+    caches = gen.make_kv_caches(batch, slots, pos, n_layers=2, device=dev)
     before = [(bits(c["k_cache"]), bits(c["v_cache"])) for c in caches]
-    step = steps.DecodeStepWithAttention(inp, caches, dev)
+    step = steps.DecodeStepWithAttention(inp, caches, dev, fused=fused, mode=mode, ring=ring)
+    if fused and mode == 0:
+        assert step.n_launches == 1
     step.run()
     torch.cuda.synchronize()
     step.check()
@@ -186,16 +200,17 @@ def test_decode_step_with_attention_teacher_forced(batch, pos):
         check_argmax(int(b["idx"][r]), lg[r], "argmax row %d" % r)
 
 
-def test_decode_step_with_attention_graph_replays_match_eager():
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_step_with_attention_graph_replays_match_eager(fused):
     """The composed step captured in one HIP graph: three replays, with eager
     work between them, each bit-identical to an eager run (every replay
     appends the same key/value at the same slot, so the outputs repeat)."""
     from weight_gemv_norm_amd import steps
-    say("decode step with attention: graph replays")
+    say("decode step with attention: graph replays, fused %s" % fused)
     dev = "cuda"
     inp = gen.make_stage_tensors("decode_step_1536x28", device=dev, batch=2, n_layers=2, vocab=4096)
     caches = gen.make_kv_caches(2, 1024, [960, 500], n_layers=2, device=dev)
-    step = steps.DecodeStepWithAttention(inp, caches, dev)
+    step = steps.DecodeStepWithAttention(inp, caches, dev, fused=fused)
     step.run()
     torch.cuda.synchronize()
     eager = {k: [t.clone() for t in step.bufs[k]] for k in ("a", "h")}

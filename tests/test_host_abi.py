@@ -696,3 +696,98 @@ def test_backward_checks_before_the_device():
     assert L.lib().wgn_backward_run(None, 1, None) == L.E_ARG
     assert L.lib().wgn_backward_check(None, None) == L.E_ARG
     assert L.lib().wgn_backward_grid(None) == -1
+
+
+# ------------------------------------------------- attention inside a chain
+def fake_attn(ar, B, q_y, k_y, v_y, out, slots=1024, hq=12, hkv=2):
+    a = L.AttnStage()
+    a.q, a.q_stride = q_y, hq * 128
+    a.k_new, a.k_stride = k_y, hkv * 128
+    a.v_new, a.v_stride = v_y, hkv * 128
+    a.k_cache = ar.take(B * hkv * slots * 256)
+    a.v_cache = ar.take(B * hkv * slots * 256)
+    a.pos = ar.take(B * 4)
+    a.out, a.out_stride = out, hq * 128
+    a.q_heads, a.kv_heads, a.slots, a.head_dim = hq, hkv, slots, 128
+    a.scale = 128 ** -0.5
+    return a
+
+
+def attn_chain(ar, B, n_layers=2, slots=1024):
+    """Stages and attention items of a decode step with computed attention:
+    {Q, K, V} -> attention -> O -> gate/up -> down per layer."""
+    stages, att = [], []
+    h = ar.take(B * 1536 * 2)
+    for _ in range(n_layers):
+        q = fake_stage(ar, 1536, 1536, B, L.NORM_RMS, x=h)
+        k = fake_stage(ar, 256, 1536, B, L.NORM_RMS, x=h)
+        v = fake_stage(ar, 256, 1536, B, L.NORM_RMS, x=h)
+        k.gamma = v.gamma = q.gamma  # one x-hat for the three
+        a_out = ar.take(B * 1536 * 2)
+        stages += [q, k, v]
+        att.append((len(stages), fake_attn(ar, B, q.y, k.y, v.y, a_out, slots)))
+        o = fake_stage(ar, 1536, 1536, B, L.NORM_NONE, x=a_out, residual=h)
+        gu = fake_stage(ar, 8960, 1536, B, L.NORM_RMS, L.EPI_SWIGLU, x=o.y)
+        d = fake_stage(ar, 1536, 8960, B, L.NORM_NONE, x=gu.y, residual=o.y)
+        stages += [o, gu, d]
+        h = d.y
+    return stages, att
+
+
+def attn_ws(stages, att, B, grid=256):
+    arr = L.stage_array(stages)
+    A = (L.AttnStage * max(1, len(att)))()
+    before = (L.I32 * max(1, len(att)))()
+    for i, (b, a) in enumerate(att):
+        A[i], before[i] = a, b
+    o = L.ChainOpts()
+    o.grid = grid
+    return L.lib().wgn_chain_attn_workspace_bytes(arr, len(stages), A, before, len(att), B, o)
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 5, 16])
+def test_attention_chain_plans(B):
+    """A chain with attention items plans (workspace > 0) at every batch of
+    both paths, and its workspace holds the partials: per (batch row,
+    key/value head) one partial of 12/2 x 130 floats per chunk, chunks of a
+    multiple of 16 slots with about one per workgroup."""
+    ar = Arena()
+    stages, att = attn_chain(ar, B)
+    ws = attn_ws(stages, att, B)
+    assert ws > 0
+    # the same stages without attention (the attention output then an input
+    # nobody writes) need less: no attention descriptors and no partials
+    arr = L.stage_array(stages)
+    o = L.ChainOpts()
+    o.grid, o.no_fuse = 256, 1
+    plain = L.lib().wgn_chain_workspace_bytes(arr, len(stages), B, o)
+    assert 0 < plain < ws
+    per = max(1, 256 // (B * 2))
+    chunk = -(-(-(-1024 // per)) // 16) * 16
+    nchunk = -(-1024 // chunk)
+    part = B * 2 * nchunk * ((6 * 130 + 3) & ~3) * 4
+    assert ws - plain >= part
+
+
+def test_attention_chain_argument_checks():
+    ar = Arena()
+    stages, att = attn_chain(ar, 1)
+    assert attn_ws(stages, att, 1) > 0
+    bad = []
+    for field, value in (("head_dim", 64), ("q_heads", 13), ("kv_heads", 0), ("slots", 0), ("scale", float("inf")),
+                         ("pos", 0), ("q", None)):
+        _, a0 = att[0]
+        a = L.AttnStage.from_buffer_copy(a0)
+        setattr(a, field, value)
+        bad.append((field, [(att[0][0], a)] + att[1:]))
+    _, a0 = att[0]
+    a = L.AttnStage.from_buffer_copy(a0)
+    a.q = a.q + 8  # not 16-byte aligned
+    bad.append(("alignment", [(att[0][0], a)] + att[1:]))
+    a = L.AttnStage.from_buffer_copy(a0)
+    a.out = a.k_cache  # writes into its own cache
+    bad.append(("overlap", [(att[0][0], a)] + att[1:]))
+    bad.append(("order", [(att[1][0], att[0][1]), (att[0][0], att[1][1])]))
+    bad.append(("position", [(len(stages) + 1, att[0][1])]))
+    for what, items in bad:
+        assert attn_ws(stages, items, 1) == 0, what

@@ -11,4 +11,4 @@ from .api import (Chain, gemv_norm, gemv_norm_workspace_bytes, layer_chain, lmhe
                   decode_attention_workspace_bytes, gemv_int4, stream_read,
                   workspace_bytes, plan_tune, lmhead_argmax_static, gemm_norm,
                   gemm_norm_workspace_bytes, make_grad, backward_workspace_bytes, Backward,
-                  chain_backward)
+                  chain_backward, make_attn_stage)

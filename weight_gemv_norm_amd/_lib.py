@@ -36,6 +36,19 @@ class Stage(ctypes.Structure):
     ]
 
 
+class AttnStage(ctypes.Structure):
+    """Mirror of wgn_attn_stage."""
+    _fields_ = [
+        ("q", P), ("q_stride", I64),
+        ("k_new", P), ("k_stride", I64),
+        ("v_new", P), ("v_stride", I64),
+        ("k_cache", P), ("v_cache", P), ("pos", P),
+        ("out", P), ("out_stride", I64),
+        ("q_heads", I32), ("kv_heads", I32), ("slots", I32), ("head_dim", I32),
+        ("scale", F32),
+    ]
+
+
 class ChainOpts(ctypes.Structure):
     """Mirror of wgn_chain_opts."""
     _fields_ = [("mode", I32), ("grid", I32), ("trace", I32), ("path", I32), ("no_fuse", I32),
@@ -95,6 +108,10 @@ def lib() -> ctypes.CDLL:
         "wgn_decode_attention": ([P, P, P, P, P, P, I32, I32, I32, I32, I32, F32, P, P, ctypes.c_size_t, P], I32),
         "wgn_chain_workspace_bytes": ([SP, I32, I32, OP], SZ),
         "wgn_chain_create": ([SP, I32, I32, OP, P, SZ, P, ctypes.POINTER(P)], I32),
+        "wgn_chain_attn_workspace_bytes": ([SP, I32, ctypes.POINTER(AttnStage), ctypes.POINTER(I32), I32, I32, OP],
+                                           SZ),
+        "wgn_chain_create_attn": ([SP, I32, ctypes.POINTER(AttnStage), ctypes.POINTER(I32), I32, I32, OP, P, SZ, P,
+                                   ctypes.POINTER(P)], I32),
         "wgn_chain_run": ([P, P], I32),
         "wgn_chain_check": ([P, P], I32),
         "wgn_chain_set_wait_us": ([P, I64], I32),

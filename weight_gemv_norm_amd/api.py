@@ -13,7 +13,7 @@ import torch
 
 from . import _lib as L
 from ._lib import (EPI_ARGMAX, EPI_GELU_TANH, EPI_NONE, EPI_SWIGLU, NORM_LAYER,  # noqa: F401
-                   NORM_NONE, NORM_RMS, BF16, FP16, ChainOpts, Grad, Plan, Stage, WgnError)
+                   NORM_NONE, NORM_RMS, BF16, FP16, AttnStage, ChainOpts, Grad, Plan, Stage, WgnError)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -228,6 +228,39 @@ def decode_attention(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, 
     L.check(st, "wgn_decode_attention")
 
 
+def make_attn_stage(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                    v_cache: torch.Tensor, pos: torch.Tensor, out: torch.Tensor,
+                    scale: Optional[float] = None) -> AttnStage:
+    """A wgn_attn_stage (attention inside a chain) over device tensors: q/out
+    [B][Hq*D] (or [B][Hq][D]), k_new/v_new [B][Hkv*D], caches [B][Hkv][S][D]
+    (all BF16, rows may be strided), pos int32 [B]."""
+    _need(k_cache.dim() == 4, "k_cache must be [B][Hkv][S][D]")
+    B, Hkv, S, D = k_cache.shape
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "v_cache must have k_cache's shape")
+    q2, o2, k2, v2 = (t.reshape(t.shape[0], -1) if t.dim() == 3 else t for t in (q, out, k_new, v_new))
+    _need(q2.shape[0] == B and q2.shape[1] % D == 0, "q must be [%d][Hq*%d]" % (B, D))
+    _need(tuple(o2.shape) == tuple(q2.shape), "out must have q's shape")
+    for name, t in (("k_new", k2), ("v_new", v2)):
+        _need(tuple(t.shape) == (B, Hkv * D), "%s must be [%d][%d]" % (name, B, Hkv * D))
+    _need(tuple(pos.shape) == (B,) and pos.dtype == torch.int32, "pos must be int32 [batch]")
+    for name, t in (("q", q2), ("k_new", k2), ("v_new", v2), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("out", o2)):
+        _need(t.dtype == torch.bfloat16, "%s must be BF16" % name)
+        _need(t.stride(-1) == 1, "%s must have unit stride along its rows" % name)
+    for t in (k_cache, v_cache, pos):
+        _need(t.is_contiguous(), "caches and pos must be contiguous")
+    _same_device(q2, k2, v2, k_cache, v_cache, pos, o2)
+    a = AttnStage()
+    a.q, a.q_stride = _ptr(q2), _row_stride(q2)
+    a.k_new, a.k_stride = _ptr(k2), _row_stride(k2)
+    a.v_new, a.v_stride = _ptr(v2), _row_stride(v2)
+    a.k_cache, a.v_cache, a.pos = _ptr(k_cache), _ptr(v_cache), _ptr(pos)
+    a.out, a.out_stride = _ptr(o2), _row_stride(o2)
+    a.q_heads, a.kv_heads, a.slots, a.head_dim = q2.shape[1] // D, Hkv, S, D
+    a.scale = D ** -0.5 if scale is None else scale
+    return a
+
+
 PATH_AUTO, PATH_VECTOR, PATH_MATRIX, PATH_TILED = 0, 1, 2, 3
 
 
@@ -255,22 +288,34 @@ class Chain:
 
     def __init__(self, stages: Sequence[Stage], batch: int, mode: int = 0, grid: int = 0,
                  ws: Optional[torch.Tensor] = None, stream=None, device="cuda", trace: bool = False,
-                 path: int = PATH_AUTO, fuse: bool = True, ring: int = 0):
+                 path: int = PATH_AUTO, fuse: bool = True, ring: int = 0,
+                 attn: Optional[Sequence] = None):
         """ring: 0 chooses the streaming waves' block-buffer ring by the chain's
-        shape; 1..3 force ring 0..2 (wgn_chain_opts.ring)."""
+        shape; 1..3 force ring 0..2 (wgn_chain_opts.ring).  attn: (before,
+        AttnStage) pairs, attention items run before stage `before`
+        (wgn_chain_create_attn)."""
         self._arr = L.stage_array(stages)
         self.n_stages = len(stages)
         self.batch = batch
         o = _opts(mode, grid, trace, path, fuse, ring)
-        need = L.lib().wgn_chain_workspace_bytes(self._arr, len(stages), batch, ctypes.byref(o))
+        attn = list(attn or [])
+        self._att = (L.AttnStage * max(1, len(attn)))()
+        self._before = (ctypes.c_int32 * max(1, len(attn)))()
+        for i, (before, a) in enumerate(attn):
+            self._before[i] = before
+            self._att[i] = a
+        na = len(attn)
+        need = L.lib().wgn_chain_attn_workspace_bytes(self._arr, len(stages), self._att, self._before, na, batch,
+                                                      ctypes.byref(o))
         if need == 0:
             # planning failed: let create report the precise status
             need = 256
         self.ws = ws if ws is not None else workspace(need, device)
         h = ctypes.c_void_p()
-        st = L.lib().wgn_chain_create(self._arr, len(stages), batch, ctypes.byref(o), _ptr(self.ws),
-                                      self.ws.numel(), _stream(stream), ctypes.byref(h))
-        L.check(st, "wgn_chain_create")
+        st = L.lib().wgn_chain_create_attn(self._arr, len(stages), self._att, self._before, na, batch,
+                                           ctypes.byref(o), _ptr(self.ws), self.ws.numel(), _stream(stream),
+                                           ctypes.byref(h))
+        L.check(st, "wgn_chain_create_attn" if na else "wgn_chain_create")
         self._h = h
 
     def run(self, stream=None, plan: Optional[Plan] = None, side=None) -> None:

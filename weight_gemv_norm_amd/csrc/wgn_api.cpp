@@ -182,6 +182,8 @@ struct Program {
     std::vector<FFix> f_fix;             // pointers into the FP32 row-sum area, set at creation
     size_t f_bytes = 0;                  // bytes of that workspace area
     int32_t n_argmax = 0;
+    std::vector<DevAttn> attn;           // attention items (part set at creation)
+    size_t attn_part_bytes = 0;          // workspace bytes of the partials (shared by all items)
     size_t lds_end = 0;                  // dynamic LDS bytes of the largest phase (set with tile)
     size_t lds_total() const { return lds_end; }
     static size_t al16(size_t v) { return (v + 15) & ~size_t(15); }
@@ -396,8 +398,82 @@ void find_hoists(const wgn_stage *st, int32_t n, int32_t B, std::vector<int32_t>
     }
 }
 
-wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_t path, bool fuse, Program &P) {
+// Checks of one attention item of a chain, and the byte ranges it reads and
+// writes (caches included).
+wgn_status check_attn(const wgn_attn_stage &s, int32_t B, std::vector<Range> &reads, std::vector<Range> &writes) {
+    reads.clear();
+    writes.clear();
+    if (!s.q || !s.k_new || !s.v_new || !s.k_cache || !s.v_cache || !s.pos || !s.out) return WGN_E_ARG;
+    if (s.q_heads < 1 || s.kv_heads < 1 || s.slots < 1 || s.q_heads % s.kv_heads) return WGN_E_ARG;
+    if (!std::isfinite(s.scale)) return WGN_E_ARG;
+    if (s.head_dim != ATTN_D || s.q_heads / s.kv_heads > ATTN_MAX_GROUP) return WGN_E_UNSUPPORTED;
+    // 32-bit buffer offsets: one (batch row, head) cache row set, and the partials
+    if ((int64_t)s.slots * ATTN_D * 2 >= (1ll << 31)) return WGN_E_UNSUPPORTED;
+    const int64_t qn = (int64_t)s.q_heads * ATTN_D, kn = (int64_t)s.kv_heads * ATTN_D;
+    if (B > 1 && (s.q_stride < qn || s.k_stride < kn || s.v_stride < kn || s.out_stride < qn)) return WGN_E_ARG;
+    if (!a16(s.q) || !a16(s.k_new) || !a16(s.v_new) || !a16(s.k_cache) || !a16(s.v_cache) || !a16(s.out) ||
+        !a4(s.pos))
+        return WGN_E_ALIGN;
+    if ((s.q_stride & 7) || (s.k_stride & 7) || (s.v_stride & 7) || (s.out_stride & 7)) return WGN_E_ALIGN;
+    const size_t cache = (size_t)B * s.kv_heads * s.slots * ATTN_D * 2;
+    const Range rk = rng(s.k_cache, cache), rv = rng(s.v_cache, cache);
+    const Range ro = rng(s.out, ((size_t)(B - 1) * s.out_stride + qn) * 2);
+    const Range rin[4] = {rng(s.q, ((size_t)(B - 1) * s.q_stride + qn) * 2),
+                          rng(s.k_new, ((size_t)(B - 1) * s.k_stride + kn) * 2),
+                          rng(s.v_new, ((size_t)(B - 1) * s.v_stride + kn) * 2), rng(s.pos, (size_t)B * 4)};
+    if (overlap(rk, rv) || overlap(ro, rk) || overlap(ro, rv)) return WGN_E_ARG;
+    for (const Range &x : rin)
+        if (overlap(x, rk) || overlap(x, rv) || overlap(x, ro)) return WGN_E_ARG;
+    for (const Range &x : rin) reads.push_back(x);
+    reads.push_back(rk);
+    reads.push_back(rv);
+    writes.push_back(ro);
+    writes.push_back(rk);
+    writes.push_back(rv);
+    return WGN_OK;
+}
+
+// Device descriptor of an attention item over G workgroups: chunks of a
+// multiple of ATTN_PASS slots, about one scores item per workgroup.
+DevAttn make_dev_attn(const wgn_attn_stage &s, int32_t B, int32_t G) {
+    DevAttn d;
+    std::memset(&d, 0, sizeof d);
+    d.q = (const uint16_t *)s.q;
+    d.k_new = (const uint16_t *)s.k_new;
+    d.v_new = (const uint16_t *)s.v_new;
+    d.k_cache = (uint16_t *)s.k_cache;
+    d.v_cache = (uint16_t *)s.v_cache;
+    d.pos = s.pos;
+    d.out = (uint16_t *)s.out;
+    d.q_stride = s.q_stride;
+    d.k_stride = s.k_stride;
+    d.v_stride = s.v_stride;
+    d.out_stride = s.out_stride;
+    d.hq = s.q_heads;
+    d.hkv = s.kv_heads;
+    d.slots = s.slots;
+    const int32_t pairs = B * s.kv_heads;
+    const int32_t per = std::max(1, G / pairs);
+    int32_t chunk = (s.slots + per - 1) / per;
+    chunk = (chunk + ATTN_PASS - 1) / ATTN_PASS * ATTN_PASS;
+    d.chunk = chunk;
+    d.nchunk = (s.slots + chunk - 1) / chunk;
+    d.scale_log2 = (float)((double)s.scale * 1.4426950408889634);  // log2(e)
+    return d;
+}
+
+size_t attn_part_bytes_of(const DevAttn &d, int32_t B) {
+    return (size_t)B * d.hkv * d.nchunk * attn_part_floats(d.hq / d.hkv) * sizeof(float);
+}
+
+wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_t path, bool fuse, Program &P,
+                const wgn_attn_stage *att = nullptr, const int32_t *att_before = nullptr, int32_t n_att = 0) {
     if (!stages || n < 1 || G < 1) return WGN_E_ARG;
+    if (n_att < 0 || (n_att > 0 && (!att || !att_before))) return WGN_E_ARG;
+    for (int32_t k = 0; k < n_att; ++k)
+        if (att_before[k] < 0 || att_before[k] > n || (k > 0 && att_before[k] < att_before[k - 1])) return WGN_E_ARG;
+    // the hoists assume an attention output that no stage writes
+    if (n_att > 0) fuse = false;
     for (int32_t i = 0; i < n; ++i) {
         wgn_status st = check_stage(stages[i], B);
         if (st != WGN_OK) return st;
@@ -409,6 +485,11 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
     std::vector<Range> r, w, c, allw;
     for (int32_t i = 0; i < n; ++i) {
         stage_ranges(stages[i], B, r, w, c);
+        allw.insert(allw.end(), w.begin(), w.end());
+    }
+    for (int32_t k = 0; k < n_att; ++k) {
+        const wgn_status st = check_attn(att[k], B, r, w);
+        if (st != WGN_OK) return st;
         allw.insert(allw.end(), w.begin(), w.end());
     }
     for (int32_t i = 0; i < n; ++i) {
@@ -425,13 +506,23 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
   replan:
     std::vector<PStage> ps;
     std::vector<std::vector<int32_t>> lists;
+    std::vector<int32_t> list_att;  // per list: -1, or the attention item it stands for
     for (;;) {
         ps.clear();
         lists.clear();
+        list_att.clear();
         std::vector<int32_t> phase_of_ps;
         std::vector<Range> ph_reads, ph_writes;
         std::vector<int32_t> pos(n, -1);
+        int32_t next_att = 0;
+        auto place_attn = [&](int32_t before) {
+            for (; next_att < n_att && att_before[next_att] == before; ++next_att) {
+                lists.emplace_back();
+                list_att.push_back(next_att);
+            }
+        };
         for (int32_t i = 0; i < n; ++i) {
+            place_attn(i);
             if (into[i] >= 0) continue;
             PStage p;
             p.s = stages[i];
@@ -442,8 +533,8 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
                 const wgn_stage &S = stages[p.post];
                 w.push_back(rng(S.y, ((size_t)(B - 1) * S.y_stride + S.N) * 2));
             }
-            bool conflict = lists.empty() || any_overlap(r, ph_writes) || any_overlap(w, ph_reads) ||
-                            any_overlap(w, ph_writes);
+            bool conflict = lists.empty() || list_att.back() >= 0 || any_overlap(r, ph_writes) ||
+                            any_overlap(w, ph_reads) || any_overlap(w, ph_writes);
             if (!conflict) {
                 std::vector<DevSource> srcs;
                 for (int32_t q : lists.back()) {
@@ -458,6 +549,7 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
             }
             if (conflict) {
                 lists.emplace_back();
+                list_att.push_back(-1);
                 ph_reads.clear();
                 ph_writes.clear();
             }
@@ -468,6 +560,7 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
             ph_reads.insert(ph_reads.end(), r.begin(), r.end());
             ph_writes.insert(ph_writes.end(), w.begin(), w.end());
         }
+        place_attn(n);
         bool undone = false;
         for (int32_t s = 0; s < n; ++s) {
             if (into[s] < 0) continue;
@@ -531,7 +624,30 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
         P.part_bytes.push_back(pb);
         return true;
     };
-    for (const std::vector<int32_t> &lst : lists) {
+    for (int32_t k = 0; k < n_att; ++k) {
+        P.attn.push_back(make_dev_attn(att[k], B, G));
+        P.attn_part_bytes = std::max(P.attn_part_bytes, attn_part_bytes_of(P.attn.back(), B));
+    }
+    for (size_t li = 0; li < lists.size(); ++li) {
+        const std::vector<int32_t> &lst = lists[li];
+        if (list_att[li] >= 0) {
+            // attention: a scores phase and a merge phase, no weights
+            for (int32_t kind = 0; kind < 2 && fail == WGN_OK; ++kind) {
+                DevPhase ph;
+                std::memset(&ph, 0, sizeof ph);
+                ph.stage0 = (int32_t)P.stages.size();
+                ph.src0 = (int32_t)P.sources.size();
+                ph.rb_off = -1;
+                ph.xb = xb_of(P, ph);
+                ph.wait = P.phases.empty() ? 0 : 1;
+                ph.att = 2 * list_att[li] + 1 + kind;
+                const int32_t first = (int32_t)P.phases.size();
+                if (!push_phase(ph, phase_stats(P.stages, P.rowb, ph, G, tile), false)) fail = WGN_E_UNSUPPORTED;
+                else P.group_end.push_back(first + 1);
+            }
+            if (fail != WGN_OK) break;
+            continue;
+        }
         DevPhase cur;
         std::memset(&cur, 0, sizeof cur);
         cur.stage0 = (int32_t)P.stages.size();
@@ -688,7 +804,8 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
 
 struct WsLayout {
     // ctr..am_part is the synchronisation area (flags, run counter, tickets, error word)
-    size_t phases, stages, sources, rowb, runimg, phinfo, touch, ctr, run, tickets, err, am_part, fsum, trace, total;
+    size_t phases, stages, sources, rowb, runimg, phinfo, att, touch, ctr, run, tickets, err, am_part, fsum, attp,
+        trace, total;
 };
 
 WsLayout ws_layout(const Program &P, bool trace) {
@@ -706,6 +823,8 @@ WsLayout ws_layout(const Program &P, bool trace) {
     o += al256(P.phases.size() * (size_t)P.G * RUN_BUF_STRIDE);
     L.phinfo = o;  // every phase's source table and normalisation jobs
     o += al256(P.phases.size() * (size_t)PHASE_INFO_BYTES);
+    L.att = o;     // attention items
+    o += al256(P.attn.size() * sizeof(DevAttn));
     L.touch = o;   // weight ranges of every launch group, for a prefetch plan's touch pass
     o += al256(P.phases.size() * (size_t)MAX_TOUCH * sizeof(TouchRange));
     L.ctr = o;
@@ -720,6 +839,8 @@ WsLayout ws_layout(const Program &P, bool trace) {
     o += al256((size_t)P.n_argmax * P.G * P.B * sizeof(uint64_t));
     L.fsum = o;
     o += P.f_bytes;
+    L.attp = o;    // attention partials
+    o += al256(P.attn_part_bytes);
     L.trace = o;
     if (trace) o += al256(P.phases.size() * (size_t)P.G * TRACE_POINTS * sizeof(uint64_t));
     L.total = o;
@@ -1302,13 +1423,29 @@ wgn_status wgn_rmsnorm_rows(const void *x, int64_t x_stride, const void *gamma, 
 
 size_t wgn_chain_workspace_bytes(const wgn_stage *stages, int32_t n_stages, int32_t batch,
                                  const wgn_chain_opts *opts) {
+    return wgn_chain_attn_workspace_bytes(stages, n_stages, nullptr, nullptr, 0, batch, opts);
+}
+
+size_t wgn_chain_attn_workspace_bytes(const wgn_stage *stages, int32_t n_stages, const wgn_attn_stage *attn,
+                                      const int32_t *attn_before, int32_t n_attn, int32_t batch,
+                                      const wgn_chain_opts *opts) {
     Program P;
-    if (plan(stages, n_stages, batch, resolve_grid(opts), opts_path(opts), opts_fuse(opts), P) != WGN_OK) return 0;
+    if (plan(stages, n_stages, batch, resolve_grid(opts), opts_path(opts), opts_fuse(opts), P, attn, attn_before,
+             n_attn) != WGN_OK)
+        return 0;
     return ws_layout(P, opts && opts->trace).total;
 }
 
 wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t batch, const wgn_chain_opts *opts,
                             void *workspace, size_t ws_bytes, wgn_stream stream, wgn_chain **out) {
+    return wgn_chain_create_attn(stages, n_stages, nullptr, nullptr, 0, batch, opts, workspace, ws_bytes, stream,
+                                 out);
+}
+
+wgn_status wgn_chain_create_attn(const wgn_stage *stages, int32_t n_stages, const wgn_attn_stage *attn,
+                                 const int32_t *attn_before, int32_t n_attn, int32_t batch,
+                                 const wgn_chain_opts *opts, void *workspace, size_t ws_bytes, wgn_stream stream,
+                                 wgn_chain **out) {
     if (!out) return WGN_E_ARG;
     *out = nullptr;
     if (opts) {
@@ -1322,7 +1459,8 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     }
     wgn_chain *c = new (std::nothrow) wgn_chain();
     if (!c) return WGN_E_ARG;
-    wgn_status st = plan(stages, n_stages, batch, resolve_grid(opts), opts_path(opts), opts_fuse(opts), c->P);
+    wgn_status st = plan(stages, n_stages, batch, resolve_grid(opts), opts_path(opts), opts_fuse(opts), c->P, attn,
+                         attn_before, n_attn);
     if (st != WGN_OK) {
         delete c;
         return st;
@@ -1356,6 +1494,9 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     std::memcpy(img.data() + c->L.stages, c->P.stages.data(), c->P.stages.size() * sizeof(DevStage));
     std::memcpy(img.data() + c->L.sources, c->P.sources.data(), c->P.sources.size() * sizeof(DevSource));
     std::memcpy(img.data() + c->L.rowb, c->P.rowb.data(), c->P.rowb.size() * sizeof(int32_t));
+    for (DevAttn &d : c->P.attn) d.part = (float *)((char *)workspace + c->L.attp);
+    if (!c->P.attn.empty())
+        std::memcpy(img.data() + c->L.att, c->P.attn.data(), c->P.attn.size() * sizeof(DevAttn));
     {
         // Run lists and phase tables are functions of (phase, workgroup)
         // alone: build them here, with the kernel's own code over the host
@@ -1432,6 +1573,7 @@ wgn_status wgn_chain_create(const wgn_stage *stages, int32_t n_stages, int32_t b
     a.err = (uint32_t *)(ws + c->L.err);
     a.am_part = (uint64_t *)(ws + c->L.am_part);
     a.trace = c->trace ? (uint64_t *)(ws + c->L.trace) : nullptr;
+    a.att = c->P.attn.empty() ? nullptr : (const DevAttn *)(ws + c->L.att);
     a.p0 = 0;
     a.p1 = (int32_t)c->P.phases.size();
     a.persistent = c->mode == 0 ? 1 : 0;

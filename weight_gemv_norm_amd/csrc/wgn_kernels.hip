@@ -1383,7 +1383,211 @@ __device__ __forceinline__ void ahead_store(const KArgs &a, int32_t q_rl, int32_
     }
 }
 
-template <int B, bool CHAIN, bool TILE, int R>
+// ------------------------------------------------------- attention phases
+// Run by the control wave in place of a product phase's input copies and
+// normalisation; the phase streams no weights, so the streaming waves only
+// meet its barriers (its weights-ahead walk continues past it).  q, k_new and
+// v_new were written earlier in the same launch: read at the coherent level.
+
+// Maximum over the 64 lanes; every lane gets the same value.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) v = fmaxf(v, __shfl_xor(v, s));
+    return v;
+}
+
+// Scores phase: this workgroup's (batch row, key/value head, chunk) item.  A
+// wave pass covers 16 slots: row r of 16 lanes takes slots t + 4 i + r
+// (i < 4), lane col of a row holds dimensions 8 col .. 8 col + 7.  Slots past
+// the chunk or the last valid slot re-read the last valid one (never beyond
+// it) and get weight 0.
+__device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_t g, int32_t G, uint32_t lane) {
+    const int32_t grp = A.hq / A.hkv, E = attn_part_floats(grp);
+    const int32_t r = (int32_t)(lane >> 4), col = (int32_t)(lane & 15);
+    const int32_t items = nb * A.hkv * A.nchunk;
+    const uint32_t lo = (uint32_t)col * 16u;  // this lane's byte offset inside a 256-byte row
+    for (int32_t it = g; it < items; it += G) {
+        const int32_t pair = it / A.nchunk, c = it - pair * A.nchunk;
+        const int32_t b = pair / A.hkv, kh = pair - b * A.hkv;
+        const int32_t p0 = uniform_i32(A.pos[b]);
+        const int32_t last = (p0 >= 0 && p0 < A.slots) ? p0 : -1;
+        const int32_t t0 = c * A.chunk;
+        if (t0 > last) continue;  // no valid slot: the merge skips this chunk
+        const int32_t t1 = min(t0 + A.chunk, last + 1);
+        const __amdgpu_buffer_rsrc_t rkc = rsrc_of(A.k_cache + (size_t)pair * A.slots * ATTN_D);
+        const __amdgpu_buffer_rsrc_t rvc = rsrc_of(A.v_cache + (size_t)pair * A.slots * ATTN_D);
+        const __amdgpu_buffer_rsrc_t rq = rsrc_of(A.q + (size_t)b * A.q_stride + (size_t)kh * grp * ATTN_D);
+        const __amdgpu_buffer_rsrc_t rkn = rsrc_of(A.k_new + (size_t)b * A.k_stride + (size_t)kh * ATTN_D);
+        const __amdgpu_buffer_rsrc_t rvn = rsrc_of(A.v_new + (size_t)b * A.v_stride + (size_t)kh * ATTN_D);
+        u32x4 qv[ATTN_MAX_GROUP];
+        float m[ATTN_MAX_GROUP], l[ATTN_MAX_GROUP], acc[ATTN_MAX_GROUP][8];
+#pragma unroll
+        for (int h = 0; h < ATTN_MAX_GROUP; ++h) {
+            const int32_t hh = h < grp ? h : 0;  // in range; heads past the group are never used
+            qv[h] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)((uint32_t)hh * ATTN_D * 2u + lo), 0, COH);
+            m[h] = -INFINITY;
+            l[h] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
+        }
+        for (int32_t t = t0; t < t1; t += ATTN_PASS) {
+            u32x4 kd[4], vd[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int32_t sl = min(t + 4 * i + r, last);
+                if (sl == last) {  // the new token: from k_new / v_new
+                    kd[i] = __builtin_amdgcn_raw_buffer_load_b128(rkn, (int)lo, 0, COH);
+                    vd[i] = __builtin_amdgcn_raw_buffer_load_b128(rvn, (int)lo, 0, COH);
+                } else {
+                    kd[i] = __builtin_amdgcn_raw_buffer_load_b128(rkc, (int)((uint32_t)sl * ATTN_D * 2u + lo), 0, 0);
+                    vd[i] = __builtin_amdgcn_raw_buffer_load_b128(rvc, (int)((uint32_t)sl * ATTN_D * 2u + lo), 0, 0);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < ATTN_MAX_GROUP; ++h) {
+                if (h >= grp) break;
+                float sc[4], mx = m[h];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float sv = group_sum(dot8(kd[i], qv[h], 0.0f), 16) * A.scale_log2;
+                    sc[i] = t + 4 * i + r < t1 ? sv : -INFINITY;
+                    mx = fmaxf(mx, sc[i]);
+                }
+                if (mx != -INFINITY) {  // this row has seen a valid slot
+                    const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);
+                    float pw[4], lw = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pw[i] = __builtin_amdgcn_exp2f(sc[i] - mx);
+                        lw += pw[i];
+                    }
+                    l[h] = l[h] * alpha + lw;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float e0 = acc[h][2 * j] * alpha, e1 = acc[h][2 * j + 1] * alpha;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t vw = j == 0 ? vd[i].x : j == 1 ? vd[i].y : j == 2 ? vd[i].z : vd[i].w;
+                            e0 += pw[i] * bf2f(vw & 0xFFFFu);
+                            e1 += pw[i] * bf2f(vw >> 16);
+                        }
+                        acc[h][2 * j] = e0;
+                        acc[h][2 * j + 1] = e1;
+                    }
+                    m[h] = mx;
+                }
+            }
+            // the append: the row holding the new token's slot stores it (no
+            // workgroup reads that slot from the cache in this launch)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (t + 4 * i + r == last) {
+                    __builtin_amdgcn_raw_buffer_store_b128(kd[i], rkc, (int)((uint32_t)last * ATTN_D * 2u + lo), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(vd[i], rvc, (int)((uint32_t)last * ATTN_D * 2u + lo), 0, 0);
+                }
+            }
+        }
+        // the four rows of the wave combined (every row ends with the same
+        // bits), then one partial: acc[G][D], m[G], l[G]
+        const __amdgpu_buffer_rsrc_t rp = rsrc_of(A.part + ((size_t)pair * A.nchunk + c) * E);
+#pragma unroll
+        for (int h = 0; h < ATTN_MAX_GROUP; ++h) {
+            if (h >= grp) break;
+            float M = fmaxf(m[h], __shfl_xor(m[h], 16));
+            M = fmaxf(M, __shfl_xor(M, 32));  // finite: row 0 holds slot t0 <= last
+            const float f = __builtin_amdgcn_exp2f(m[h] - M);
+            float L = l[h] * f;
+            L += __shfl_xor(L, 16);
+            L += __shfl_xor(L, 32);
+            float o[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float v = acc[h][j] * f;
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                o[j] = v;
+            }
+            if ((h & 3) == r) {
+                const int off = (h * ATTN_D + col * 8) * 4;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (f32x4){o[0], o[1], o[2], o[3]}), rp,
+                                                       off, 0, COH);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (f32x4){o[4], o[5], o[6], o[7]}), rp,
+                                                       off + 16, 0, COH);
+            }
+            if (lane == 0) {
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(M), rp, (grp * ATTN_D + h) * 4, 0, COH);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(L), rp, (grp * ATTN_D + grp + h) * 4, 0, COH);
+            }
+        }
+    }
+}
+
+// Merge phase: items (batch row, query head, 16-dimension slice) spread over
+// the workgroups.  Lane i folds the partials of chunks i, i + 64, ... in that
+// order (running maximum), then the wave combines its lanes in a fixed order;
+// lanes 0-7 store the 16 BF16 outputs.  A row with no valid slot gets 0.
+__device__ __forceinline__ void attn_merge(const DevAttn &A, int32_t nb, int32_t g, int32_t G, uint32_t lane) {
+    constexpr int NSL = ATTN_D / ATTN_SLICE;
+    const int32_t grp = A.hq / A.hkv, E = attn_part_floats(grp);
+    const int32_t items = nb * A.hq * NSL;
+    for (int32_t it = g; it < items; it += G) {
+        const int32_t b = it / (A.hq * NSL), rem = it - b * A.hq * NSL;
+        const int32_t hq = rem / NSL, ds = rem - hq * NSL;
+        const int32_t kh = hq / grp, hi = hq - kh * grp, pair = b * A.hkv + kh;
+        const int32_t p0 = uniform_i32(A.pos[b]);
+        const int32_t last = (p0 >= 0 && p0 < A.slots) ? p0 : -1;
+        const int32_t nvalid = last < 0 ? 0 : last / A.chunk + 1;  // chunks holding a valid slot
+        const __amdgpu_buffer_rsrc_t rp = rsrc_of(A.part + (size_t)pair * A.nchunk * E);
+        float mm = -INFINITY, ll = 0.0f, aa[ATTN_SLICE];
+#pragma unroll
+        for (int j = 0; j < ATTN_SLICE; ++j) aa[j] = 0.0f;
+        for (int32_t i = (int32_t)lane; i < nvalid; i += 64) {
+            const int32_t base = i * E;
+            const float mi = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (base + grp * ATTN_D + hi) * 4, 0, COH));
+            const float li =
+                __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (base + grp * ATTN_D + grp + hi) * 4, 0, COH));
+            u32x4 av[ATTN_SLICE / 4];
+#pragma unroll
+            for (int k = 0; k < ATTN_SLICE / 4; ++k)
+                av[k] = __builtin_amdgcn_raw_buffer_load_b128(rp, (base + hi * ATTN_D + ds * ATTN_SLICE + 4 * k) * 4, 0,
+                                                              COH);
+            const float M = fmaxf(mm, mi);
+            const float f0 = __builtin_amdgcn_exp2f(mm - M), f1 = __builtin_amdgcn_exp2f(mi - M);
+            ll = ll * f0 + li * f1;
+#pragma unroll
+            for (int k = 0; k < ATTN_SLICE / 4; ++k) {
+                const f32x4 v = __builtin_bit_cast(f32x4, av[k]);
+                aa[4 * k] = aa[4 * k] * f0 + v.x * f1;
+                aa[4 * k + 1] = aa[4 * k + 1] * f0 + v.y * f1;
+                aa[4 * k + 2] = aa[4 * k + 2] * f0 + v.z * f1;
+                aa[4 * k + 3] = aa[4 * k + 3] * f0 + v.w * f1;
+            }
+            mm = M;
+        }
+        const float M = wave_max(mm);
+        const float f = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mm - M);
+        const float L = wave_sum(ll * f);
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < ATTN_SLICE / 2; ++j) {
+            const float o0 = wave_sum(aa[2 * j] * f), o1 = wave_sum(aa[2 * j + 1] * f);
+            const uint32_t w2 = L > 0.0f ? f2bf2(o0 / L, o1 / L) : 0u;
+            word = lane == (uint32_t)j ? w2 : word;
+        }
+        if (lane < (uint32_t)(ATTN_SLICE / 2))
+            __builtin_amdgcn_raw_buffer_store_b32(
+                word, rsrc_of(A.out + (size_t)b * A.out_stride + (size_t)hq * ATTN_D + ds * ATTN_SLICE),
+                (int)(lane * 4u), 0, COH);
+    }
+}
+
+__device__ __forceinline__ void attention_phase(const KArgs &a, int32_t att, int32_t g, uint32_t lane) {
+    const DevAttn A = WGN_CONST_PTR(DevAttn, a.att)[(att - 1) >> 1];
+    if ((att - 1) & 1) attn_merge(A, a.nb, g, a.G, lane);
+    else attn_scores(A, a.nb, g, a.G, lane);
+}
+
+template <int B, bool CHAIN, bool TILE, int R, bool ATT>
 __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *lds) {
     const uint32_t lane = lane_id();
     char *desc = lds + LDS_DESC_OFF;
@@ -1499,6 +1703,9 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
         } else {
             issue_source_loads<B, CHAIN>(a, ph.nsrc, ph.xb, lds, xh, lane, 0, 1, true);
         }
+        if constexpr (ATT) {
+            if (ph.att) attention_phase(a, ph.att, g, lane);
+        }
         stage_epilogue_inputs<B, CHAIN>(a, h, runs, epi, lane);
         __builtin_amdgcn_s_waitcnt(0);  // inputs, gains and epilogue values have landed
         if (h.has_norm) norm_all<B>(lds, STREAM_WAVES, lane);
@@ -1573,7 +1780,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
     }
 }
 
-template <int B, bool CHAIN, bool TILE, int R>
+template <int B, bool CHAIN, bool TILE, int R, bool ATT>
 __global__ __launch_bounds__(THREADS, 1) void chain_kernel(KArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int32_t g = blockIdx.x;
@@ -1582,7 +1789,7 @@ __global__ __launch_bounds__(THREADS, 1) void chain_kernel(KArgs a) {
         if constexpr (!TILE && ring_interleaved(R)) stream_wave_il<B, CHAIN, R>(a, g, w, lds);
         else stream_wave<B, CHAIN, TILE, R>(a, g, w, lds);
     }
-    else control_wave<B, CHAIN, TILE, R>(a, g, lds);
+    else control_wave<B, CHAIN, TILE, R, ATT>(a, g, lds);
 }
 
 // ------------------------------------------------------------- touch pass
@@ -1703,26 +1910,28 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t *x, in
 // ------------------------------------------------------------ host launchers
 namespace wgn {
 
-template <int B, bool CHAIN, bool TILE, int R>
+template <int B, bool CHAIN, bool TILE, int R, bool ATT = false>
 static hipError_t launch_chain_b(const KArgs &a, int32_t grid, size_t lds, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
         // 160 KB of LDS per workgroup on gfx950, minus the kernel's static LDS
-        hipError_t e = hipFuncSetAttribute((const void *)chain_kernel<B, CHAIN, TILE, R>,
+        hipError_t e = hipFuncSetAttribute((const void *)chain_kernel<B, CHAIN, TILE, R, ATT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((chain_kernel<B, CHAIN, TILE, R>), dim3(grid), dim3(THREADS), lds, s, a);
+    hipLaunchKernelGGL((chain_kernel<B, CHAIN, TILE, R, ATT>), dim3(grid), dim3(THREADS), lds, s, a);
     return hipGetLastError();
 }
 
-template <int B>
+// Chains with attention phases run kernels of their own (ATT), so that the
+// kernels of chains without them stay as they are.
+template <int B, bool ATT>
 static hipError_t launch_chain_ring(int32_t ring, const KArgs &a, int32_t grid, size_t lds, hipStream_t s) {
     switch (ring) {
-    case 0: return launch_chain_b<B, true, false, 0>(a, grid, lds, s);
-    case 1: return launch_chain_b<B, true, false, 1>(a, grid, lds, s);
-    case 2: return launch_chain_b<B, true, false, 2>(a, grid, lds, s);
+    case 0: return launch_chain_b<B, true, false, 0, ATT>(a, grid, lds, s);
+    case 1: return launch_chain_b<B, true, false, 1, ATT>(a, grid, lds, s);
+    case 2: return launch_chain_b<B, true, false, 2, ATT>(a, grid, lds, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1731,8 +1940,10 @@ static hipError_t launch_chain_ring(int32_t ring, const KArgs &a, int32_t grid, 
 // memory) and the matrix-core path use ring 0.
 hipError_t launch_chain(int32_t batch, bool tile, int32_t ring, const KArgs &a, int32_t grid, size_t lds,
                         hipStream_t s) {
+    const bool att = a.att != nullptr;
     if (tile) {
         if (batch > MAX_BATCH) return hipErrorInvalidValue;
+        if (att) return launch_chain_b<MAX_BATCH, true, true, 0, true>(a, grid, lds, s);
         return a.phases ? launch_chain_b<MAX_BATCH, true, true, 0>(a, grid, lds, s)
                         : launch_chain_b<MAX_BATCH, false, true, 0>(a, grid, lds, s);
     }
@@ -1745,11 +1956,20 @@ hipError_t launch_chain(int32_t batch, bool tile, int32_t ring, const KArgs &a, 
         default: return hipErrorInvalidValue;
         }
     }
+    if (att) {
+        switch (batch) {
+        case 1: return launch_chain_ring<1, true>(ring, a, grid, lds, s);
+        case 2: return launch_chain_ring<2, true>(ring, a, grid, lds, s);
+        case 3: return launch_chain_ring<3, true>(ring, a, grid, lds, s);
+        case 4: return launch_chain_ring<4, true>(ring, a, grid, lds, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (batch) {
-    case 1: return launch_chain_ring<1>(ring, a, grid, lds, s);
-    case 2: return launch_chain_ring<2>(ring, a, grid, lds, s);
-    case 3: return launch_chain_ring<3>(ring, a, grid, lds, s);
-    case 4: return launch_chain_ring<4>(ring, a, grid, lds, s);
+    case 1: return launch_chain_ring<1, false>(ring, a, grid, lds, s);
+    case 2: return launch_chain_ring<2, false>(ring, a, grid, lds, s);
+    case 3: return launch_chain_ring<3, false>(ring, a, grid, lds, s);
+    case 4: return launch_chain_ring<4, false>(ring, a, grid, lds, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -181,7 +181,49 @@ struct DevPhase {
     int32_t prm_off;       // LDS byte offset of the norm gains/shifts
     int32_t epi_off;       // LDS byte offset of the staged bias/residual values
     int32_t carry_off;     // LDS byte offset of the K-window carry (row-parts x batch FP32)
-    int32_t pad;
+    int32_t att;           // 0: a product phase; 2k+1 / 2k+2: the scores / merge phase of attention k
+};
+
+// Attention of each batch row's new token over its key/value cache, as two
+// phases of a chain that stream no weights ("Making small PyTorch ops faster
+// on a laptop GPU", section "A full decode step is a different story": the
+// new key and value appended, FP32 softmax, the cache split across blocks and
+// the splits merged; "One Token, Kernel by Kernel", section "The fix: Part
+// 10's split-KV kernel": (batch, head, slot, dimension) cache layout, the
+// valid length read on the device, each key/value head read once for its
+// group of query heads).
+//  * scores phase: item (batch row, key/value head, chunk of `chunk` slots),
+//    one per workgroup; the control wave scores its slots for every query
+//    head of the group, keeps a running maximum and weight sum per head
+//    (online softmax) and writes one partial: the weighted value sums, the
+//    maxima and the weight sums.  The chunk holding the new token's slot
+//    takes that key and value from k_new / v_new and appends them.
+//  * merge phase: item (batch row, query head, 16 dimensions), spread over
+//    the workgroups; the control wave merges the valid chunks' partials of
+//    its head (lane i takes chunks i, i + 64, ...; then a wave reduction in a
+//    fixed order) and stores 16 BF16 outputs.
+// Both phases end with the usual completion flags, so the product that reads
+// `out` waits for the merge like for any earlier phase.
+constexpr int ATTN_D = 128;          // head dimension
+constexpr int ATTN_MAX_GROUP = 8;    // query heads per key/value head
+constexpr int ATTN_PASS = 16;        // slots one wave scores per pass (4 rows of 16 lanes x 4 loads)
+constexpr int ATTN_SLICE = 16;       // output dimensions per merge item
+// Floats of one partial: acc[G][D], then m[G], then l[G]; padded to 16 bytes.
+WGN_HD int32_t attn_part_floats(int32_t G) { return (G * (ATTN_D + 2) + 3) & ~3; }
+struct DevAttn {
+    const uint16_t *q;       // [B][q_stride]: q_heads x ATTN_D (written earlier in the launch)
+    const uint16_t *k_new;   // [B][k_stride]: kv_heads x ATTN_D
+    const uint16_t *v_new;   // [B][v_stride]
+    uint16_t *k_cache;       // [B][kv_heads][slots][ATTN_D]
+    uint16_t *v_cache;
+    const int32_t *pos;      // [B]: slot of the new token (out of range: no valid slot, output 0)
+    uint16_t *out;           // [B][out_stride]: q_heads x ATTN_D
+    float *part;             // [B * kv_heads][nchunk][attn_part_floats(G)] partials
+    int64_t q_stride, k_stride, v_stride, out_stride;
+    int32_t hq, hkv, slots;
+    int32_t chunk;           // slots per scores item (a multiple of ATTN_PASS)
+    int32_t nchunk;          // chunks per (batch row, key/value head)
+    float scale_log2;        // score scale times log2(e): weights are 2^(s - m)
 };
 
 // One contiguous byte range of weights read by the optional touch pass (the
@@ -207,6 +249,7 @@ struct KArgs {
     uint64_t *trace;       // [nphases][G][TRACE_POINTS] timestamps, or null
     const char *runimg;    // chains: [nphases][G] run lists, RUN_BUF_STRIDE bytes each (built on the host)
     const char *phinfo;    // chains: [nphases] phase infos, PHASE_INFO_BYTES each (built on the host)
+    const DevAttn *att;    // chains with attention phases: [attention items], else null
     int32_t p0, p1;        // phases of this launch
     int32_t persistent;
     int32_t G;

@@ -78,14 +78,18 @@ class DecodeStepWithAttention:
     and down ("One Token, Kernel by Kernel", sections "What one block
     launches" and "The fix: Part 10's split-KV kernel").
 
-    Launches: one chain {Q, K, V of layer 0}; then per layer one attention
-    launch and one chain {O, gate/up, down, and the next layer's Q, K, V} (the
-    last chain ends with the final norm, LM head and argmax).  Every chain is
-    a persistent kernel of its own; attention is not yet a phase inside it.
+    fused=True (default): one chain, one persistent launch per step; each
+    layer's attention runs inside it as two phases without weights
+    (wgn_chain_create_attn), between {Q, K, V} and {O}.
+    fused=False: one chain {Q, K, V of layer 0}; then per layer one
+    wgn_decode_attention launch and one chain {O, gate/up, down, and the next
+    layer's Q, K, V} (the last chain ends with the final norm, LM head and
+    argmax), every chain a persistent kernel of its own.
     Buffers: q/k/v/a/h1/s/h per layer as in decoder_stages, with a [B][Hq*D]
     the attention output that feeds O."""
 
-    def __init__(self, inp: Dict, caches: List[Dict], device, mode: int = 0):
+    def __init__(self, inp: Dict, caches: List[Dict], device, mode: int = 0, fused: bool = True,
+                 ring: int = 0):
         from . import api as W
         B = inp["batch"]
         eps = inp["eps"]
@@ -118,17 +122,34 @@ class DecodeStepWithAttention:
                                maxval=mx)]
             bufs["idx"], bufs["maxval"] = idx, mx
         self.bufs = bufs
-        self.chains = [W.Chain(qkv[0], B, mode=mode)]
-        self.attn = []
+        self.fused = fused
         hd = 128  # head dimension of the attention kernel
         NQ, NKV = layers[0]["wq"].shape[0] // hd, layers[0]["wk"].shape[0] // hd
+        if fused:
+            stages, att = list(qkv[0]), []
+            for l, L in enumerate(layers):
+                h_in, h1, s, hn = bufs["h"][l], bufs["h1"][l], bufs["s"][l], bufs["h"][l + 1]
+                c = caches[l]
+                att.append((len(stages), W.make_attn_stage(bufs["q"][l], bufs["k"][l], bufs["v"][l], c["k_cache"],
+                                                           c["v_cache"], c["pos"], bufs["a"][l])))
+                stages += [make_stage(L["wo"], bufs["a"][l], h1, norm=NORM_NONE, residual=h_in),
+                           make_stage(L["wg"], h1, s, norm=NORM_RMS, eps=eps, gamma=L["g2"], epi=EPI_SWIGLU,
+                                      W_up=L["wu"]),
+                           make_stage(L["wd"], s, hn, norm=NORM_NONE, residual=h1)]
+                stages += qkv[l + 1] if l + 1 < len(layers) else tail
+            self.chains = [W.Chain(stages, B, mode=mode, attn=att, ring=ring)]
+            self.attn = []
+            self.n_launches = 1 if mode == 0 else self.chains[0].num_phases
+            return
+        self.chains = [W.Chain(qkv[0], B, mode=mode, ring=ring)]
+        self.attn = []
         for l, L in enumerate(layers):
             h_in, h1, s, hn = bufs["h"][l], bufs["h1"][l], bufs["s"][l], bufs["h"][l + 1]
             st = [make_stage(L["wo"], bufs["a"][l], h1, norm=NORM_NONE, residual=h_in),
                   make_stage(L["wg"], h1, s, norm=NORM_RMS, eps=eps, gamma=L["g2"], epi=EPI_SWIGLU, W_up=L["wu"]),
                   make_stage(L["wd"], s, hn, norm=NORM_NONE, residual=h1)]
             st += qkv[l + 1] if l + 1 < len(layers) else tail
-            self.chains.append(W.Chain(st, B, mode=mode))
+            self.chains.append(W.Chain(st, B, mode=mode, ring=ring))
             c = caches[l]
             S = c["k_cache"].shape[2]
             self.attn.append(dict(
