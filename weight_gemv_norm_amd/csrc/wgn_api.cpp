@@ -310,7 +310,7 @@ bool layout_phase(const Program &P, DevPhase &ph, const PhaseStats &S, bool carr
         if ((d.bias || d.residual || d.post_y) && !(d.carry & CARRY_OUT)) epi_in = true;
     }
     const size_t x = al256(nb * (size_t)ph.xb * 2);
-    const size_t part = Program::al16((size_t)S.max_rp * S.jmax * nb * 4);
+    const size_t part = ph.att ? (size_t)ATTN_CMB_BYTES : Program::al16((size_t)S.max_rp * S.jmax * nb * 4);
     const size_t epi = epi_in ? Program::al16((size_t)S.max_rp * epi_rec((int32_t)nb) * 4) : 0;
     const size_t cy = carry ? Program::al16((size_t)S.max_rp * nb * 4) : 0;
     size_t o = lds_dyn_off(path_desc_bufs(P.tile));
@@ -638,7 +638,9 @@ wgn_status plan(const wgn_stage *stages, int32_t n, int32_t B, int32_t G, int32_
                 ph.stage0 = (int32_t)P.stages.size();
                 ph.src0 = (int32_t)P.sources.size();
                 ph.rb_off = -1;
-                ph.xb = xb_of(P, ph);
+                // one unit of x-hat per batch row, zeroed by the kernel: the
+                // phase's empty blocks read it against zero weights
+                ph.xb = P.tile ? UNIT + 8 : UNIT;
                 ph.wait = P.phases.empty() ? 0 : 1;
                 ph.att = 2 * list_att[li] + 1 + kind;
                 const int32_t first = (int32_t)P.phases.size();
@@ -1563,7 +1565,7 @@ wgn_status wgn_chain_create_attn(const wgn_stage *stages, int32_t n_stages, cons
     a.rowb = (const int32_t *)(ws + c->L.rowb);
     // precomputed lists from batch 2 up (at batch 1 the kernel builds them
     // while it waits for flags that arrive later anyway)
-    if (c->P.B > 1 || c->P.tile || WGN_PRE_B1) {
+    if (c->P.B > 1 || c->P.tile || WGN_PRE_B1 || !c->P.attn.empty()) {
         a.runimg = ws + c->L.runimg;
         a.phinfo = ws + c->L.phinfo;
     }

@@ -1389,19 +1389,66 @@ __device__ __forceinline__ void ahead_store(const KArgs &a, int32_t q_rl, int32_
 // meet its barriers (its weights-ahead walk continues past it).  q, k_new and
 // v_new were written earlier in the same launch: read at the coherent level.
 
-// Maximum over the 64 lanes; every lane gets the same value.
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) v = fmaxf(v, __shfl_xor(v, s));
-    return v;
+// Maximum / sum over the 64 lanes by DPP (rows, then the row broadcasts into
+// lane 63), read back from lane 63 into a scalar register: every lane gets
+// the same value, with no LDS permute on the path.
+__device__ __forceinline__ float wave_max_bcast(float v) {
+    const int ninf = (int)0xFF800000u;
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x142, 0xA, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x143, 0xC, 0xF, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_sum_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_last(v)), 63));
 }
 
-// Scores phase: this workgroup's (batch row, key/value head, chunk) item.  A
-// wave pass covers 16 slots: row r of 16 lanes takes slots t + 4 i + r
-// (i < 4), lane col of a row holds dimensions 8 col .. 8 col + 7.  Slots past
-// the chunk or the last valid slot re-read the last valid one (never beyond
-// it) and get weight 0.
-__device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_t g, int32_t G, uint32_t lane) {
+// Position of batch row b's new token, read through the scalar cache (a
+// value written before the launch): no vector-memory round trip.
+__device__ __forceinline__ int32_t attn_last(const DevAttn &A, int32_t b) {
+    const int32_t p0 = WGN_CONST_PTR(int32_t, A.pos)[b];
+    return (p0 >= 0 && p0 < A.slots) ? p0 : -1;
+}
+
+// The scores item of this workgroup and the first pass of its cache rows,
+// copied into LDS (stage: 4 key then 4 value copies of 1 KB, lane l's 16
+// bytes at l * 16) before the wait for the previous phase: the cache does not
+// depend on it, and the copies hold no registers across the wait.  Row r of
+// 16 lanes takes slots t + 4 i + r (i < 4), lane col of a row holds
+// dimensions 8 col .. 8 col + 7; slots past the chunk or the last valid slot
+// re-read the last valid one (never beyond it) and get weight 0.  The new
+// token's slot is read here too and replaced after the wait.
+__device__ __forceinline__ void attn_prefetch(const DevAttn &A, int32_t nb, int32_t g, uint32_t lane, char *stage) {
+    const int32_t r = (int32_t)(lane >> 4);
+    const uint32_t lo = (lane & 15u) * 16u;
+    const int32_t items = nb * A.hkv * A.nchunk;
+    if (g >= items) return;
+    const int32_t pair = g / A.nchunk, c = g - pair * A.nchunk;
+    const int32_t last = attn_last(A, pair / A.hkv);
+    const int32_t t0 = c * A.chunk;
+    if (t0 > last) return;  // no valid slot: nothing is scored
+    const char *kc = (const char *)(A.k_cache + (size_t)pair * A.slots * ATTN_D);
+    const char *vc = (const char *)(A.v_cache + (size_t)pair * A.slots * ATTN_D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const size_t off = (size_t)min(t0 + 4 * i + r, last) * ATTN_D * 2 + lo;
+        __builtin_amdgcn_global_load_lds((const WGN_GAS void *)(kc + off), (WGN_LAS void *)(stage + i * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const WGN_GAS void *)(vc + off), (WGN_LAS void *)(stage + (4 + i) * 1024), 16, 0,
+                                         0);
+    }
+}
+
+// Scores phase: this workgroup's (batch row, key/value head, chunk) item
+// (one per workgroup as planned; further items, if any, load their rows
+// here).  Online softmax per query head over the passes; the four rows of
+// the wave are combined through LDS (cmb: [row][head][D] FP32, then m and l
+// per (row, head)) in row order, and one partial is written: acc[G][D],
+// m[G], l[G].
+__device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_t g, int32_t G, uint32_t lane,
+                                            float *cmb, const char *stage) {
     const int32_t grp = A.hq / A.hkv, E = attn_part_floats(grp);
     const int32_t r = (int32_t)(lane >> 4), col = (int32_t)(lane & 15);
     const int32_t items = nb * A.hkv * A.nchunk;
@@ -1409,8 +1456,7 @@ __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_
     for (int32_t it = g; it < items; it += G) {
         const int32_t pair = it / A.nchunk, c = it - pair * A.nchunk;
         const int32_t b = pair / A.hkv, kh = pair - b * A.hkv;
-        const int32_t p0 = uniform_i32(A.pos[b]);
-        const int32_t last = (p0 >= 0 && p0 < A.slots) ? p0 : -1;
+        const int32_t last = attn_last(A, b);
         const int32_t t0 = c * A.chunk;
         if (t0 > last) continue;  // no valid slot: the merge skips this chunk
         const int32_t t1 = min(t0 + A.chunk, last + 1);
@@ -1419,106 +1465,138 @@ __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_
         const __amdgpu_buffer_rsrc_t rq = rsrc_of(A.q + (size_t)b * A.q_stride + (size_t)kh * grp * ATTN_D);
         const __amdgpu_buffer_rsrc_t rkn = rsrc_of(A.k_new + (size_t)b * A.k_stride + (size_t)kh * ATTN_D);
         const __amdgpu_buffer_rsrc_t rvn = rsrc_of(A.v_new + (size_t)b * A.v_stride + (size_t)kh * ATTN_D);
-        u32x4 qv[ATTN_MAX_GROUP];
-        float m[ATTN_MAX_GROUP], l[ATTN_MAX_GROUP], acc[ATTN_MAX_GROUP][8];
+        const u32x4 kn = __builtin_amdgcn_raw_buffer_load_b128(rkn, (int)lo, 0, COH);
+        const u32x4 vn = __builtin_amdgcn_raw_buffer_load_b128(rvn, (int)lo, 0, COH);
+        // the group's query heads HS at a time (registers), each sweep over
+        // every pass of the chunk; the first pass comes from the staged copies
+        constexpr int HS = 4;
+        for (int32_t h0 = 0; h0 < grp; h0 += HS) {
+            u32x4 qv[HS];
+            float m[HS], l[HS], acc[HS][8];
 #pragma unroll
-        for (int h = 0; h < ATTN_MAX_GROUP; ++h) {
-            const int32_t hh = h < grp ? h : 0;  // in range; heads past the group are never used
-            qv[h] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)((uint32_t)hh * ATTN_D * 2u + lo), 0, COH);
-            m[h] = -INFINITY;
-            l[h] = 0.0f;
+            for (int h = 0; h < HS; ++h) {
+                const int32_t hh = h0 + h < grp ? h0 + h : 0;  // in range; heads past the group are never used
+                qv[h] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)((uint32_t)hh * ATTN_D * 2u + lo), 0, COH);
+                m[h] = -INFINITY;
+                l[h] = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
-        }
-        for (int32_t t = t0; t < t1; t += ATTN_PASS) {
-            u32x4 kd[4], vd[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int32_t sl = min(t + 4 * i + r, last);
-                if (sl == last) {  // the new token: from k_new / v_new
-                    kd[i] = __builtin_amdgcn_raw_buffer_load_b128(rkn, (int)lo, 0, COH);
-                    vd[i] = __builtin_amdgcn_raw_buffer_load_b128(rvn, (int)lo, 0, COH);
-                } else {
-                    kd[i] = __builtin_amdgcn_raw_buffer_load_b128(rkc, (int)((uint32_t)sl * ATTN_D * 2u + lo), 0, 0);
-                    vd[i] = __builtin_amdgcn_raw_buffer_load_b128(rvc, (int)((uint32_t)sl * ATTN_D * 2u + lo), 0, 0);
-                }
+                for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
             }
-#pragma unroll
-            for (int h = 0; h < ATTN_MAX_GROUP; ++h) {
-                if (h >= grp) break;
-                float sc[4], mx = m[h];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float sv = group_sum(dot8(kd[i], qv[h], 0.0f), 16) * A.scale_log2;
-                    sc[i] = t + 4 * i + r < t1 ? sv : -INFINITY;
-                    mx = fmaxf(mx, sc[i]);
-                }
-                if (mx != -INFINITY) {  // this row has seen a valid slot
-                    const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);
-                    float pw[4], lw = 0.0f;
+            for (int32_t t = t0; t < t1; t += ATTN_PASS) {
+                u32x4 kd[4], vd[4];
+                if (it == g && t == t0) {
+                    __builtin_amdgcn_s_waitcnt(0);  // the copies into stage have landed
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        pw[i] = __builtin_amdgcn_exp2f(sc[i] - mx);
-                        lw += pw[i];
+                        kd[i] = *(const u32x4 *)(stage + i * 1024 + lane * 16);
+                        vd[i] = *(const u32x4 *)(stage + (4 + i) * 1024 + lane * 16);
                     }
-                    l[h] = l[h] * alpha + lw;
+                } else {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float e0 = acc[h][2 * j] * alpha, e1 = acc[h][2 * j + 1] * alpha;
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t sl = (uint32_t)min(t + 4 * i + r, last);
+                        kd[i] = __builtin_amdgcn_raw_buffer_load_b128(rkc, (int)(sl * ATTN_D * 2u + lo), 0, 0);
+                        vd[i] = __builtin_amdgcn_raw_buffer_load_b128(rvc, (int)(sl * ATTN_D * 2u + lo), 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (min(t + 4 * i + r, last) == last) {  // the new token: from k_new / v_new
+                        kd[i] = kn;
+                        vd[i] = vn;
+                    }
+                }
+#pragma unroll
+                for (int h = 0; h < HS; ++h) {
+                    if (h0 + h >= grp) break;
+                    float sc[4], mx = m[h];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float sv = group_sum(dot8(kd[i], qv[h], 0.0f), 16) * A.scale_log2;
+                        sc[i] = t + 4 * i + r < t1 ? sv : -INFINITY;
+                        mx = fmaxf(mx, sc[i]);
+                    }
+                    if (mx != -INFINITY) {  // this row has seen a valid slot
+                        const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);
+                        float pw[4], lw = 0.0f;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const uint32_t vw = j == 0 ? vd[i].x : j == 1 ? vd[i].y : j == 2 ? vd[i].z : vd[i].w;
-                            e0 += pw[i] * bf2f(vw & 0xFFFFu);
-                            e1 += pw[i] * bf2f(vw >> 16);
+                            pw[i] = __builtin_amdgcn_exp2f(sc[i] - mx);
+                            lw += pw[i];
                         }
-                        acc[h][2 * j] = e0;
-                        acc[h][2 * j + 1] = e1;
+                        l[h] = l[h] * alpha + lw;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            float e0 = acc[h][2 * j] * alpha, e1 = acc[h][2 * j + 1] * alpha;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const uint32_t vw = j == 0 ? vd[i].x : j == 1 ? vd[i].y : j == 2 ? vd[i].z : vd[i].w;
+                                e0 += pw[i] * bf2f(vw & 0xFFFFu);
+                                e1 += pw[i] * bf2f(vw >> 16);
+                            }
+                            acc[h][2 * j] = e0;
+                            acc[h][2 * j + 1] = e1;
+                        }
+                        m[h] = mx;
                     }
-                    m[h] = mx;
+                }
+                // the append (first sweep): the row holding the new token's
+                // slot stores it (no workgroup reads that slot from the cache
+                // in this launch)
+                if (h0 == 0) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (t + 4 * i + r == last) {
+                            __builtin_amdgcn_raw_buffer_store_b128(kd[i], rkc, (int)((uint32_t)last * ATTN_D * 2u + lo),
+                                                                   0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b128(vd[i], rvc, (int)((uint32_t)last * ATTN_D * 2u + lo),
+                                                                   0, 0);
+                        }
+                    }
                 }
             }
-            // the append: the row holding the new token's slot stores it (no
-            // workgroup reads that slot from the cache in this launch)
+            // this sweep's rows into LDS, to be combined in row order below
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (t + 4 * i + r == last) {
-                    __builtin_amdgcn_raw_buffer_store_b128(kd[i], rkc, (int)((uint32_t)last * ATTN_D * 2u + lo), 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b128(vd[i], rvc, (int)((uint32_t)last * ATTN_D * 2u + lo), 0, 0);
+            for (int h = 0; h < HS; ++h) {
+                if (h0 + h >= grp) break;
+                const int32_t hh = h0 + h;
+                float *dst = cmb + ((r * ATTN_MAX_GROUP + hh) * ATTN_D + col * 8);
+                *(f32x4 *)dst = (f32x4){acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+                *(f32x4 *)(dst + 4) = (f32x4){acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+                if (col == 0) {
+                    cmb[4 * ATTN_MAX_GROUP * ATTN_D + r * ATTN_MAX_GROUP + hh] = m[h];
+                    cmb[4 * ATTN_MAX_GROUP * ATTN_D + 4 * ATTN_MAX_GROUP + r * ATTN_MAX_GROUP + hh] = l[h];
                 }
             }
         }
-        // the four rows of the wave combined (every row ends with the same
-        // bits), then one partial: acc[G][D], m[G], l[G]
         const __amdgpu_buffer_rsrc_t rp = rsrc_of(A.part + ((size_t)pair * A.nchunk + c) * E);
 #pragma unroll
-        for (int h = 0; h < ATTN_MAX_GROUP; ++h) {
-            if (h >= grp) break;
-            float M = fmaxf(m[h], __shfl_xor(m[h], 16));
-            M = fmaxf(M, __shfl_xor(M, 32));  // finite: row 0 holds slot t0 <= last
-            const float f = __builtin_amdgcn_exp2f(m[h] - M);
-            float L = l[h] * f;
-            L += __shfl_xor(L, 16);
-            L += __shfl_xor(L, 32);
-            float o[8];
+        for (int k = 0; k < ATTN_MAX_GROUP / 2; ++k) {
+            const int32_t q4 = (int32_t)lane + 64 * k;  // float4 group: head q4 / 32, dimensions 4 (q4 % 32) ..
+            if (q4 >= grp * (ATTN_D / 4)) break;
+            const int32_t h = q4 >> 5, d0 = (q4 & 31) * 4;
+            float mr[4], lr[4], M = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float v = acc[h][j] * f;
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
-                o[j] = v;
+            for (int rr = 0; rr < 4; ++rr) {
+                mr[rr] = cmb[4 * ATTN_MAX_GROUP * ATTN_D + rr * ATTN_MAX_GROUP + h];
+                lr[rr] = cmb[4 * ATTN_MAX_GROUP * ATTN_D + 4 * ATTN_MAX_GROUP + rr * ATTN_MAX_GROUP + h];
+                M = fmaxf(M, mr[rr]);  // finite: row 0 holds slot t0 <= last
             }
-            if ((h & 3) == r) {
-                const int off = (h * ATTN_D + col * 8) * 4;
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (f32x4){o[0], o[1], o[2], o[3]}), rp,
-                                                       off, 0, COH);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (f32x4){o[4], o[5], o[6], o[7]}), rp,
-                                                       off + 16, 0, COH);
+            f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+            float L = 0.0f;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const float f = __builtin_amdgcn_exp2f(mr[rr] - M);
+                o += f * *(const f32x4 *)(cmb + ((rr * ATTN_MAX_GROUP + h) * ATTN_D + d0));
+                L += f * lr[rr];
             }
-            if (lane == 0) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rp, (h * ATTN_D + d0) * 4, 0, COH);
+            if (d0 == 0) {
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(M), rp, (grp * ATTN_D + h) * 4, 0, COH);
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(L), rp, (grp * ATTN_D + grp + h) * 4, 0, COH);
             }
         }
+
     }
 }
 
@@ -1534,8 +1612,7 @@ __device__ __forceinline__ void attn_merge(const DevAttn &A, int32_t nb, int32_t
         const int32_t b = it / (A.hq * NSL), rem = it - b * A.hq * NSL;
         const int32_t hq = rem / NSL, ds = rem - hq * NSL;
         const int32_t kh = hq / grp, hi = hq - kh * grp, pair = b * A.hkv + kh;
-        const int32_t p0 = uniform_i32(A.pos[b]);
-        const int32_t last = (p0 >= 0 && p0 < A.slots) ? p0 : -1;
+        const int32_t last = attn_last(A, b);
         const int32_t nvalid = last < 0 ? 0 : last / A.chunk + 1;  // chunks holding a valid slot
         const __amdgpu_buffer_rsrc_t rp = rsrc_of(A.part + (size_t)pair * A.nchunk * E);
         float mm = -INFINITY, ll = 0.0f, aa[ATTN_SLICE];
@@ -1564,13 +1641,13 @@ __device__ __forceinline__ void attn_merge(const DevAttn &A, int32_t nb, int32_t
             }
             mm = M;
         }
-        const float M = wave_max(mm);
+        const float M = wave_max_bcast(mm);
         const float f = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mm - M);
-        const float L = wave_sum(ll * f);
+        const float L = wave_sum_bcast(ll * f);
         uint32_t word = 0;
 #pragma unroll
         for (int j = 0; j < ATTN_SLICE / 2; ++j) {
-            const float o0 = wave_sum(aa[2 * j] * f), o1 = wave_sum(aa[2 * j + 1] * f);
+            const float o0 = wave_sum_bcast(aa[2 * j] * f), o1 = wave_sum_bcast(aa[2 * j + 1] * f);
             const uint32_t w2 = L > 0.0f ? f2bf2(o0 / L, o1 / L) : 0u;
             word = lane == (uint32_t)j ? w2 : word;
         }
@@ -1581,11 +1658,10 @@ __device__ __forceinline__ void attn_merge(const DevAttn &A, int32_t nb, int32_t
     }
 }
 
-__device__ __forceinline__ void attention_phase(const KArgs &a, int32_t att, int32_t g, uint32_t lane) {
-    const DevAttn A = WGN_CONST_PTR(DevAttn, a.att)[(att - 1) >> 1];
-    if ((att - 1) & 1) attn_merge(A, a.nb, g, a.G, lane);
-    else attn_scores(A, a.nb, g, a.G, lane);
+__device__ __forceinline__ const DevAttn attn_of(const KArgs &a, int32_t att) {
+    return WGN_CONST_PTR(DevAttn, a.att)[(att - 1) >> 1];
 }
+__device__ __forceinline__ bool attn_is_scores(int32_t att) { return ((att - 1) & 1) == 0; }
 
 template <int B, bool CHAIN, bool TILE, int R, bool ATT>
 __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *lds) {
@@ -1632,8 +1708,12 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
         const RunHdr &h = *(const RunHdr *)rb;  // in LDS (a register copy passed by reference would go to scratch)
         const Run *runs = (const Run *)(rb + sizeof(RunHdr));
         // the gains do not depend on the previous phase: request them before
-        // waiting for it
+        // waiting for it (and an attention item's first cache rows)
         prefetch_params(ph, lds, lane);
+        if constexpr (ATT) {
+            if (ph.att && attn_is_scores(ph.att))
+                attn_prefetch(attn_of(a, ph.att), a.nb, g, lane, lds + ph.part_off + ATTN_STAGE_OFF);
+        }
         if (a.persistent && p > a.p0 && ph.wait) {
             // every workgroup's flag of phase p-1 must carry this run's value
             const __amdgpu_buffer_rsrc_t rf = rsrc_of(a.flags + (size_t)(p - 1) * flag_row(a.G));
@@ -1704,7 +1784,18 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
             issue_source_loads<B, CHAIN>(a, ph.nsrc, ph.xb, lds, xh, lane, 0, 1, true);
         }
         if constexpr (ATT) {
-            if (ph.att) attention_phase(a, ph.att, g, lane);
+            if (ph.att) {
+                if (attn_is_scores(ph.att))
+                    attn_scores(attn_of(a, ph.att), a.nb, g, a.G, lane, (float *)(lds + ph.part_off),
+                                lds + ph.part_off + ATTN_STAGE_OFF);
+                else attn_merge(attn_of(a, ph.att), a.nb, g, a.G, lane);
+                // The phase streams no weights, but its empty blocks still
+                // read x-hat (and multiply it by zero weights): zeros, not
+                // whatever an earlier phase left in LDS, which read as BF16
+                // may be a NaN pattern.
+                for (int32_t i = (int32_t)lane; i < a.nb * ph.xb / 8; i += 64)
+                    *(u32x4 *)(xh + i * 16) = (u32x4){0u, 0u, 0u, 0u};
+            }
         }
         stage_epilogue_inputs<B, CHAIN>(a, h, runs, epi, lane);
         __builtin_amdgcn_s_waitcnt(0);  // inputs, gains and epilogue values have landed

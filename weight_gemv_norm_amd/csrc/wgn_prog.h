@@ -210,6 +210,11 @@ constexpr int ATTN_PASS = 16;        // slots one wave scores per pass (4 rows o
 constexpr int ATTN_SLICE = 16;       // output dimensions per merge item
 // Floats of one partial: acc[G][D], then m[G], then l[G]; padded to 16 bytes.
 WGN_HD int32_t attn_part_floats(int32_t G) { return (G * (ATTN_D + 2) + 3) & ~3; }
+// LDS of a scores phase: the combine of the four 16-lane rows of its wave
+// ([row][head][D] FP32, then m and l per (row, head)), then the staged first
+// pass of cache rows (4 key and 4 value copies of 1 KB).
+constexpr int ATTN_STAGE_OFF = 4 * ATTN_MAX_GROUP * (ATTN_D + 2) * 4;
+constexpr int ATTN_CMB_BYTES = ATTN_STAGE_OFF + 8 * 1024;
 struct DevAttn {
     const uint16_t *q;       // [B][q_stride]: q_heads x ATTN_D (written earlier in the launch)
     const uint16_t *k_new;   // [B][k_stride]: kv_heads x ATTN_D
