@@ -533,7 +533,7 @@ def summarize_pmc(fetch_csv, write_csv, out_txt, workload, batch, copy_mib, path
         if kernel == "gemm_kernel":
             steps = sum(1 for (n, d) in per if "zero_words_kernel" in n)
             tot = sum(v for (n, d), v in per.items()
-                      if "gemm_kernel" in n or "norm_rows64_kernel" in n or "zero_words_kernel" in n)
+                      if "gemm_kernel" in n or "norm_rows64" in n or "zero_words_kernel" in n)
             kern = [tot / max(steps, 1)] if steps else []
             nk = steps
         else:
