@@ -152,6 +152,7 @@ def test_decode_attention_graph_replays():
     (True, 2, [960, 37], 1024, 0, 2),             # the 5 x 8-unit ring
     (True, 5, [960, 37, 1023, 0, 640], 1024, 0, 0),  # matrix-core path
     (True, 2, [960, 37], 1024, 1, 0),             # one launch per phase
+    (True, 2, [960, 32767], 32768, 0, 0),         # a short and a full row of a long cache
 ])
 def test_decode_step_with_attention_teacher_forced(fused, batch, pos, slots, mode, ring):
     """Two decoder blocks whose attention is computed (Q/K/V -> decode

@@ -749,8 +749,8 @@ def attn_ws(stages, att, B, grid=256):
 def test_attention_chain_plans(B):
     """A chain with attention items plans (workspace > 0) at every batch of
     both paths, and its workspace holds the partials: per (batch row,
-    key/value head) one partial of 12/2 x 130 floats per chunk, chunks of a
-    multiple of 16 slots with about one per workgroup."""
+    key/value head) one partial of 12/2 x 130 floats per chunk, about one
+    chunk per workgroup and at most one per 16 cache slots."""
     ar = Arena()
     stages, att = attn_chain(ar, B)
     ws = attn_ws(stages, att, B)
@@ -762,9 +762,7 @@ def test_attention_chain_plans(B):
     o.grid, o.no_fuse = 256, 1
     plain = L.lib().wgn_chain_workspace_bytes(arr, len(stages), B, o)
     assert 0 < plain < ws
-    per = max(1, 256 // (B * 2))
-    chunk = -(-(-(-1024 // per)) // 16) * 16
-    nchunk = -(-1024 // chunk)
+    nchunk = min(max(1, 256 // (B * 2)), 1024 // 16)
     part = B * 2 * nchunk * ((6 * 130 + 3) & ~3) * 4
     assert ws - plain >= part
 

@@ -433,8 +433,9 @@ wgn_status check_attn(const wgn_attn_stage &s, int32_t B, std::vector<Range> &re
     return WGN_OK;
 }
 
-// Device descriptor of an attention item over G workgroups: chunks of a
-// multiple of ATTN_PASS slots, about one scores item per workgroup.
+// Device descriptor of an attention item over G workgroups: about one scores
+// item per workgroup, each (batch row, key/value head) with nchunk chunks of
+// whole passes (the kernel splits each row's valid length over them).
 DevAttn make_dev_attn(const wgn_attn_stage &s, int32_t B, int32_t G) {
     DevAttn d;
     std::memset(&d, 0, sizeof d);
@@ -454,10 +455,7 @@ DevAttn make_dev_attn(const wgn_attn_stage &s, int32_t B, int32_t G) {
     d.slots = s.slots;
     const int32_t pairs = B * s.kv_heads;
     const int32_t per = std::max(1, G / pairs);
-    int32_t chunk = (s.slots + per - 1) / per;
-    chunk = (chunk + ATTN_PASS - 1) / ATTN_PASS * ATTN_PASS;
-    d.chunk = chunk;
-    d.nchunk = (s.slots + chunk - 1) / chunk;
+    d.nchunk = std::min(per, (s.slots + ATTN_PASS - 1) / ATTN_PASS);
     d.scale_log2 = (float)((double)s.scale * 1.4426950408889634);  // log2(e)
     return d;
 }

@@ -1412,6 +1412,13 @@ __device__ __forceinline__ int32_t attn_last(const DevAttn &A, int32_t b) {
     const int32_t p0 = WGN_CONST_PTR(int32_t, A.pos)[b];
     return (p0 >= 0 && p0 < A.slots) ? p0 : -1;
 }
+// Slots per chunk of a row whose last valid slot is last >= 0: its valid
+// length split over the row's nchunk partials, in whole passes (the same in
+// both phases, so the merge finds the chunks the scores phase filled).
+__device__ __forceinline__ int32_t attn_chunk(const DevAttn &A, int32_t last) {
+    const int32_t c = (last + A.nchunk) / A.nchunk;  // ceil((last + 1) / nchunk)
+    return (c + ATTN_PASS - 1) / ATTN_PASS * ATTN_PASS;
+}
 
 // The scores item of this workgroup and the first pass of its cache rows,
 // copied into LDS (stage: 4 key then 4 value copies of 1 KB, lane l's 16
@@ -1428,8 +1435,9 @@ __device__ __forceinline__ void attn_prefetch(const DevAttn &A, int32_t nb, int3
     if (g >= items) return;
     const int32_t pair = g / A.nchunk, c = g - pair * A.nchunk;
     const int32_t last = attn_last(A, pair / A.hkv);
-    const int32_t t0 = c * A.chunk;
-    if (t0 > last) return;  // no valid slot: nothing is scored
+    if (last < 0) return;  // no valid slot: nothing is scored
+    const int32_t t0 = c * attn_chunk(A, last);
+    if (t0 > last) return;
     const char *kc = (const char *)(A.k_cache + (size_t)pair * A.slots * ATTN_D);
     const char *vc = (const char *)(A.v_cache + (size_t)pair * A.slots * ATTN_D);
 #pragma unroll
@@ -1457,9 +1465,11 @@ __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_
         const int32_t pair = it / A.nchunk, c = it - pair * A.nchunk;
         const int32_t b = pair / A.hkv, kh = pair - b * A.hkv;
         const int32_t last = attn_last(A, b);
-        const int32_t t0 = c * A.chunk;
-        if (t0 > last) continue;  // no valid slot: the merge skips this chunk
-        const int32_t t1 = min(t0 + A.chunk, last + 1);
+        if (last < 0) continue;  // no valid slot: the merge writes zeros
+        const int32_t chunk = attn_chunk(A, last);
+        const int32_t t0 = c * chunk;
+        if (t0 > last) continue;  // past the valid slots: the merge skips this chunk
+        const int32_t t1 = min(t0 + chunk, last + 1);
         const __amdgpu_buffer_rsrc_t rkc = rsrc_of(A.k_cache + (size_t)pair * A.slots * ATTN_D);
         const __amdgpu_buffer_rsrc_t rvc = rsrc_of(A.v_cache + (size_t)pair * A.slots * ATTN_D);
         const __amdgpu_buffer_rsrc_t rq = rsrc_of(A.q + (size_t)b * A.q_stride + (size_t)kh * grp * ATTN_D);
@@ -1613,7 +1623,7 @@ __device__ __forceinline__ void attn_merge(const DevAttn &A, int32_t nb, int32_t
         const int32_t hq = rem / NSL, ds = rem - hq * NSL;
         const int32_t kh = hq / grp, hi = hq - kh * grp, pair = b * A.hkv + kh;
         const int32_t last = attn_last(A, b);
-        const int32_t nvalid = last < 0 ? 0 : last / A.chunk + 1;  // chunks holding a valid slot
+        const int32_t nvalid = last < 0 ? 0 : last / attn_chunk(A, last) + 1;  // chunks holding a valid slot
         const __amdgpu_buffer_rsrc_t rp = rsrc_of(A.part + (size_t)pair * A.nchunk * E);
         float mm = -INFINITY, ll = 0.0f, aa[ATTN_SLICE];
 #pragma unroll

@@ -192,8 +192,8 @@ struct DevPhase {
 // 10's split-KV kernel": (batch, head, slot, dimension) cache layout, the
 // valid length read on the device, each key/value head read once for its
 // group of query heads).
-//  * scores phase: item (batch row, key/value head, chunk of `chunk` slots),
-//    one per workgroup; the control wave scores its slots for every query
+//  * scores phase: item (batch row, key/value head, chunk of the row's valid
+//    slots), one per workgroup; the control wave scores its slots for every query
 //    head of the group, keeps a running maximum and weight sum per head
 //    (online softmax) and writes one partial: the weighted value sums, the
 //    maxima and the weight sums.  The chunk holding the new token's slot
@@ -226,8 +226,8 @@ struct DevAttn {
     float *part;             // [B * kv_heads][nchunk][attn_part_floats(G)] partials
     int64_t q_stride, k_stride, v_stride, out_stride;
     int32_t hq, hkv, slots;
-    int32_t chunk;           // slots per scores item (a multiple of ATTN_PASS)
-    int32_t nchunk;          // chunks per (batch row, key/value head)
+    int32_t nchunk;          // chunks (scores items, partials) per (batch row, key/value head); a row's
+                             // valid slots are split over them in whole passes on the device
     float scale_log2;        // score scale times log2(e): weights are 2^(s - m)
 };
 
