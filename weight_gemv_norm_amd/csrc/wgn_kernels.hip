@@ -1472,7 +1472,15 @@ __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_
         const int32_t t1 = min(t0 + chunk, last + 1);
         const __amdgpu_buffer_rsrc_t rkc = rsrc_of(A.k_cache + (size_t)pair * A.slots * ATTN_D);
         const __amdgpu_buffer_rsrc_t rvc = rsrc_of(A.v_cache + (size_t)pair * A.slots * ATTN_D);
-        const __amdgpu_buffer_rsrc_t rq = rsrc_of(A.q + (size_t)b * A.q_stride + (size_t)kh * grp * ATTN_D);
+        // the group's query rows into LDS (4 heads of 256 bytes per copy),
+        // requested with the new key and value: one round trip for all
+        const char *qg = (const char *)(A.q + (size_t)b * A.q_stride + (size_t)kh * grp * ATTN_D);
+        char *qs = (char *)cmb + ATTN_Q_OFF;
+#pragma unroll
+        for (int i = 0; i < ATTN_MAX_GROUP / 4; ++i)
+            if (4 * i + r < grp)
+                __builtin_amdgcn_global_load_lds((const WGN_GAS void *)(qg + (size_t)(4 * i + r) * ATTN_D * 2 + lo),
+                                                 (WGN_LAS void *)(qs + i * 1024), 16, 0, COH);
         const __amdgpu_buffer_rsrc_t rkn = rsrc_of(A.k_new + (size_t)b * A.k_stride + (size_t)kh * ATTN_D);
         const __amdgpu_buffer_rsrc_t rvn = rsrc_of(A.v_new + (size_t)b * A.v_stride + (size_t)kh * ATTN_D);
         const u32x4 kn = __builtin_amdgcn_raw_buffer_load_b128(rkn, (int)lo, 0, COH);
@@ -1480,13 +1488,14 @@ __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_
         // the group's query heads HS at a time (registers), each sweep over
         // every pass of the chunk; the first pass comes from the staged copies
         constexpr int HS = 4;
+        __builtin_amdgcn_s_waitcnt(0);  // query rows (and the staged cache rows) have landed
         for (int32_t h0 = 0; h0 < grp; h0 += HS) {
             u32x4 qv[HS];
             float m[HS], l[HS], acc[HS][8];
 #pragma unroll
             for (int h = 0; h < HS; ++h) {
                 const int32_t hh = h0 + h < grp ? h0 + h : 0;  // in range; heads past the group are never used
-                qv[h] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)((uint32_t)hh * ATTN_D * 2u + lo), 0, COH);
+                qv[h] = *(const u32x4 *)(qs + hh * ATTN_D * 2 + lo);
                 m[h] = -INFINITY;
                 l[h] = 0.0f;
 #pragma unroll

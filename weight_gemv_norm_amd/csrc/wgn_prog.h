@@ -212,9 +212,11 @@ constexpr int ATTN_SLICE = 16;       // output dimensions per merge item
 WGN_HD int32_t attn_part_floats(int32_t G) { return (G * (ATTN_D + 2) + 3) & ~3; }
 // LDS of a scores phase: the combine of the four 16-lane rows of its wave
 // ([row][head][D] FP32, then m and l per (row, head)), then the staged first
-// pass of cache rows (4 key and 4 value copies of 1 KB).
+// pass of cache rows (4 key and 4 value copies of 1 KB), then the group's
+// query rows ([head][D] BF16).
 constexpr int ATTN_STAGE_OFF = 4 * ATTN_MAX_GROUP * (ATTN_D + 2) * 4;
-constexpr int ATTN_CMB_BYTES = ATTN_STAGE_OFF + 8 * 1024;
+constexpr int ATTN_Q_OFF = ATTN_STAGE_OFF + 8 * 1024;
+constexpr int ATTN_CMB_BYTES = ATTN_Q_OFF + ATTN_MAX_GROUP * ATTN_D * 2;
 struct DevAttn {
     const uint16_t *q;       // [B][q_stride]: q_heads x ATTN_D (written earlier in the launch)
     const uint16_t *k_new;   // [B][k_stride]: kv_heads x ATTN_D
