@@ -1623,7 +1623,8 @@ __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_
 // the workgroups.  Lane i folds the partials of chunks i, i + 64, ... in that
 // order (running maximum), then the wave combines its lanes in a fixed order;
 // lanes 0-7 store the 16 BF16 outputs.  A row with no valid slot gets 0.
-__device__ __forceinline__ void attn_merge(const DevAttn &A, int32_t nb, int32_t g, int32_t G, uint32_t lane) {
+__device__ __forceinline__ void attn_merge(const DevAttn &A, int32_t nb, int32_t g, int32_t G, uint32_t lane,
+                                           int32_t last_g) {
     constexpr int NSL = ATTN_D / ATTN_SLICE;
     const int32_t grp = A.hq / A.hkv, E = attn_part_floats(grp);
     const int32_t items = nb * A.hq * NSL;
@@ -1631,7 +1632,7 @@ __device__ __forceinline__ void attn_merge(const DevAttn &A, int32_t nb, int32_t
         const int32_t b = it / (A.hq * NSL), rem = it - b * A.hq * NSL;
         const int32_t hq = rem / NSL, ds = rem - hq * NSL;
         const int32_t kh = hq / grp, hi = hq - kh * grp, pair = b * A.hkv + kh;
-        const int32_t last = attn_last(A, b);
+        const int32_t last = it == g ? last_g : attn_last(A, b);
         const int32_t nvalid = last < 0 ? 0 : last / attn_chunk(A, last) + 1;  // chunks holding a valid slot
         const __amdgpu_buffer_rsrc_t rp = rsrc_of(A.part + (size_t)pair * A.nchunk * E);
         float mm = -INFINITY, ll = 0.0f, aa[ATTN_SLICE];
@@ -1729,9 +1730,15 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
         // the gains do not depend on the previous phase: request them before
         // waiting for it (and an attention item's first cache rows)
         prefetch_params(ph, lds, lane);
+        // (a merge item's descriptor and position are read here too: two
+        // dependent scalar-cache misses off the path after the wait)
+        int32_t att_last = -1;
         if constexpr (ATT) {
-            if (ph.att && attn_is_scores(ph.att))
-                attn_prefetch(attn_of(a, ph.att), a.nb, g, lane, lds + ph.part_off + ATTN_STAGE_OFF);
+            if (ph.att) {
+                const DevAttn A = attn_of(a, ph.att);
+                if (attn_is_scores(ph.att)) attn_prefetch(A, a.nb, g, lane, lds + ph.part_off + ATTN_STAGE_OFF);
+                else if (g < a.nb * A.hq * (ATTN_D / ATTN_SLICE)) att_last = attn_last(A, g / (A.hq * (ATTN_D / ATTN_SLICE)));
+            }
         }
         if (a.persistent && p > a.p0 && ph.wait) {
             // every workgroup's flag of phase p-1 must carry this run's value
@@ -1807,7 +1814,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
                 if (attn_is_scores(ph.att))
                     attn_scores(attn_of(a, ph.att), a.nb, g, a.G, lane, (float *)(lds + ph.part_off),
                                 lds + ph.part_off + ATTN_STAGE_OFF);
-                else attn_merge(attn_of(a, ph.att), a.nb, g, a.G, lane);
+                else attn_merge(attn_of(a, ph.att), a.nb, g, a.G, lane, att_last);
                 // The phase streams no weights, but its empty blocks still
                 // read x-hat (and multiply it by zero weights): zeros, not
                 // whatever an earlier phase left in LDS, which read as BF16
