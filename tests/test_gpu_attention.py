@@ -230,3 +230,54 @@ def test_decode_step_with_attention_graph_replays_match_eager(fused):
                 assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (rep, k)
         assert torch.equal(step.bufs["idx"], idx), rep
         step.check()
+
+
+@pytest.mark.parametrize("hq,hkv,batch,slots,pos", [
+    (8, 1, 1, 200, [199]),          # 8 query heads per key/value head: two full sweeps of four
+    (3, 3, 2, 300, [17, 299]),      # one query head per key/value head
+    (9, 3, 3, 700, [650, 0, 64]),   # three per head, three key/value heads
+    (14, 2, 2, 129, [128, 100]),    # seven per head (a partial second sweep)
+])
+def test_attention_phases_group_sizes(hq, hkv, batch, slots, pos):
+    """Attention items inside a small chain {RMSNorm -> Q, K, V} -> attention
+    -> {O + residual} for other query/key-value head ratios than the pages'
+    model: q, k, v, the attention output (against the oracle on the GPU's own
+    q, k, v), both caches bit for bit, and O."""
+    import weight_gemv_norm_amd as W
+    from weight_gemv_norm_amd.api import make_stage, NORM_RMS, NORM_NONE
+    say("attention phases hq %d hkv %d batch %d slots %d pos %s" % (hq, hkv, batch, slots, pos))
+    dev, H, D = "cuda", 256, 128
+    s = lambda t: gen.seed_of(901, hq * 100 + hkv, t)  # noqa: E731
+    h = gen.normal((batch, H), 1.0, s(1), device=dev)
+    g1 = gen.normal((H,), 0.1, s(2), mean=1.0, device=dev)
+    wq = gen.normal((hq * D, H), 0.05, s(3), device=dev)
+    wk = gen.normal((hkv * D, H), 0.05, s(4), device=dev)
+    wv = gen.normal((hkv * D, H), 0.05, s(5), device=dev)
+    wo = gen.normal((H, hq * D), 0.02, s(6), device=dev)
+    q = torch.empty((batch, hq * D), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((batch, hkv * D), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((batch, hkv * D), dtype=torch.bfloat16, device=dev)
+    a = torch.full((batch, hq * D), float("nan"), dtype=torch.bfloat16, device=dev)
+    h1 = torch.empty((batch, H), dtype=torch.bfloat16, device=dev)
+    t = gen.make_attention_tensors(batch, slots, pos, q_heads=hq, kv_heads=hkv, seed=5, device=dev)
+    kc0, vc0 = bits(t["k_cache"]), bits(t["v_cache"])
+    stages = [make_stage(wq, h, q, norm=NORM_RMS, eps=1e-6, gamma=g1),
+              make_stage(wk, h, k, norm=NORM_RMS, eps=1e-6, gamma=g1),
+              make_stage(wv, h, v, norm=NORM_RMS, eps=1e-6, gamma=g1),
+              make_stage(wo, a, h1, norm=NORM_NONE, residual=h)]
+    att = W.make_attn_stage(q, k, v, t["k_cache"], t["v_cache"], t["pos"], a)
+    ch = W.Chain(stages, batch, attn=[(3, att)])
+    assert ch.num_phases == 4
+    ch.run()
+    torch.cuda.synchronize()
+    ch.check()
+    eps = float(np.float32(1e-6))
+    for name, wt, out in (("q", wq, q), ("k", wk, k), ("v", wv, v)):
+        ref = O.stage(bits(h), bits(wt), norm=O.NORM_RMS, eps=eps, gamma=bits(g1))
+        assert_close_bf16(bits(out), ref, name)
+    ref_a, ref_k, ref_v = O.decode_attention(bits(q).reshape(batch, hq, D), bits(k).reshape(batch, hkv, D),
+                                             bits(v).reshape(batch, hkv, D), kc0, vc0, t["pos"].cpu().numpy())
+    assert_close_bf16(bits(a).reshape(batch, hq, D), ref_a, "attention")
+    np.testing.assert_array_equal(bits(t["k_cache"]), ref_k)
+    np.testing.assert_array_equal(bits(t["v_cache"]), ref_v)
+    assert_close_bf16(bits(h1), O.stage(bits(a), bits(wo), residual=bits(h)), "O")
