@@ -943,10 +943,12 @@ int32_t opts_path(const wgn_chain_opts *opts) { return opts ? opts->path : 0; }
 bool opts_fuse(const wgn_chain_opts *opts) { return !(opts && opts->no_fuse); }
 
 // The vector path's ring for a chain, by the shape that was measured fastest
-// with each (decode step at batch 1-4, LayerNorm chain): phases that give a
-// streaming wave fewer than 4 units on average want many phases in flight
-// (ring 1); otherwise batch 2-4 streams best with interleaved refills
-// (ring 2) and batch 1 with two large bursts (ring 0).
+// with each (decode step at batch 1-4, LayerNorm chain, decode step with
+// attention phases): phases that give a streaming wave fewer than 4 units on
+// average want many phases in flight (ring 1), at batch 1 up to 12 (a decode
+// step with attention phases, 10: 1,445 against 1,487 us with ring 0);
+// otherwise batch 2-4 streams best with interleaved refills (ring 2) and
+// batch 1 with two large bursts (ring 0: the decode step, 29 units).
 int32_t auto_ring(const Program &P) {
     if (P.tile || P.phases.empty()) return 0;
     double units = 0.0;
@@ -956,7 +958,7 @@ int32_t auto_ring(const Program &P) {
             units += (double)st.N * st.parts * st.nchunks;
         }
     const double per_wave = units / ((double)P.phases.size() * P.G * STREAM_WAVES);
-    if (per_wave < 4.0) return 1;
+    if (per_wave < 4.0 || (P.B == 1 && per_wave < 12.0)) return 1;
     return P.B >= 2 ? 2 : 0;
 }
 
