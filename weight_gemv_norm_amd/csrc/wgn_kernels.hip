@@ -1619,13 +1619,15 @@ __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_
     }
 }
 
-// Merge phase: items (batch row, query head, 16-dimension slice) spread over
+// Merge phase: items (batch row, query head, SL-dimension slice) spread over
 // the workgroups.  Lane i folds the partials of chunks i, i + 64, ... in that
 // order (running maximum), then the wave combines its lanes in a fixed order;
-// lanes 0-7 store the 16 BF16 outputs.  A row with no valid slot gets 0.
+// lanes 0 .. SL/2 - 1 store the SL BF16 outputs.  A row with no valid slot
+// gets 0.
+template <int SL>
 __device__ __forceinline__ void attn_merge(const DevAttn &A, int32_t nb, int32_t g, int32_t G, uint32_t lane,
                                            int32_t last_g) {
-    constexpr int NSL = ATTN_D / ATTN_SLICE;
+    constexpr int NSL = ATTN_D / SL;
     const int32_t grp = A.hq / A.hkv, E = attn_part_floats(grp);
     const int32_t items = nb * A.hq * NSL;
     for (int32_t it = g; it < items; it += G) {
@@ -1635,24 +1637,24 @@ __device__ __forceinline__ void attn_merge(const DevAttn &A, int32_t nb, int32_t
         const int32_t last = it == g ? last_g : attn_last(A, b);
         const int32_t nvalid = last < 0 ? 0 : last / attn_chunk(A, last) + 1;  // chunks holding a valid slot
         const __amdgpu_buffer_rsrc_t rp = rsrc_of(A.part + (size_t)pair * A.nchunk * E);
-        float mm = -INFINITY, ll = 0.0f, aa[ATTN_SLICE];
+        float mm = -INFINITY, ll = 0.0f, aa[SL];
 #pragma unroll
-        for (int j = 0; j < ATTN_SLICE; ++j) aa[j] = 0.0f;
+        for (int j = 0; j < SL; ++j) aa[j] = 0.0f;
         for (int32_t i = (int32_t)lane; i < nvalid; i += 64) {
             const int32_t base = i * E;
             const float mi = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (base + grp * ATTN_D + hi) * 4, 0, COH));
             const float li =
                 __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (base + grp * ATTN_D + grp + hi) * 4, 0, COH));
-            u32x4 av[ATTN_SLICE / 4];
+            u32x4 av[SL / 4];
 #pragma unroll
-            for (int k = 0; k < ATTN_SLICE / 4; ++k)
-                av[k] = __builtin_amdgcn_raw_buffer_load_b128(rp, (base + hi * ATTN_D + ds * ATTN_SLICE + 4 * k) * 4, 0,
+            for (int k = 0; k < SL / 4; ++k)
+                av[k] = __builtin_amdgcn_raw_buffer_load_b128(rp, (base + hi * ATTN_D + ds * SL + 4 * k) * 4, 0,
                                                               COH);
             const float M = fmaxf(mm, mi);
             const float f0 = __builtin_amdgcn_exp2f(mm - M), f1 = __builtin_amdgcn_exp2f(mi - M);
             ll = ll * f0 + li * f1;
 #pragma unroll
-            for (int k = 0; k < ATTN_SLICE / 4; ++k) {
+            for (int k = 0; k < SL / 4; ++k) {
                 const f32x4 v = __builtin_bit_cast(f32x4, av[k]);
                 aa[4 * k] = aa[4 * k] * f0 + v.x * f1;
                 aa[4 * k + 1] = aa[4 * k + 1] * f0 + v.y * f1;
@@ -1666,14 +1668,14 @@ __device__ __forceinline__ void attn_merge(const DevAttn &A, int32_t nb, int32_t
         const float L = wave_sum_bcast(ll * f);
         uint32_t word = 0;
 #pragma unroll
-        for (int j = 0; j < ATTN_SLICE / 2; ++j) {
+        for (int j = 0; j < SL / 2; ++j) {
             const float o0 = wave_sum_bcast(aa[2 * j] * f), o1 = wave_sum_bcast(aa[2 * j + 1] * f);
             const uint32_t w2 = L > 0.0f ? f2bf2(o0 / L, o1 / L) : 0u;
             word = lane == (uint32_t)j ? w2 : word;
         }
-        if (lane < (uint32_t)(ATTN_SLICE / 2))
+        if (lane < (uint32_t)(SL / 2))
             __builtin_amdgcn_raw_buffer_store_b32(
-                word, rsrc_of(A.out + (size_t)b * A.out_stride + (size_t)hq * ATTN_D + ds * ATTN_SLICE),
+                word, rsrc_of(A.out + (size_t)b * A.out_stride + (size_t)hq * ATTN_D + ds * SL),
                 (int)(lane * 4u), 0, COH);
     }
 }
@@ -1737,7 +1739,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
             if (ph.att) {
                 const DevAttn A = attn_of(a, ph.att);
                 if (attn_is_scores(ph.att)) attn_prefetch(A, a.nb, g, lane, lds + ph.part_off + ATTN_STAGE_OFF);
-                else if (g < a.nb * A.hq * (ATTN_D / ATTN_SLICE)) att_last = attn_last(A, g / (A.hq * (ATTN_D / ATTN_SLICE)));
+                else if (g < a.nb * A.hq * (ATTN_D / attn_slice(B))) att_last = attn_last(A, g / (A.hq * (ATTN_D / attn_slice(B))));
             }
         }
         if (a.persistent && p > a.p0 && ph.wait) {
@@ -1814,7 +1816,7 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
                 if (attn_is_scores(ph.att))
                     attn_scores(attn_of(a, ph.att), a.nb, g, a.G, lane, (float *)(lds + ph.part_off),
                                 lds + ph.part_off + ATTN_STAGE_OFF);
-                else attn_merge(attn_of(a, ph.att), a.nb, g, a.G, lane, att_last);
+                else attn_merge<attn_slice(B)>(attn_of(a, ph.att), a.nb, g, a.G, lane, att_last);
                 // The phase streams no weights, but its empty blocks still
                 // read x-hat (and multiply it by zero weights): zeros, not
                 // whatever an earlier phase left in LDS, which read as BF16

@@ -198,8 +198,8 @@ struct DevPhase {
 //    (online softmax) and writes one partial: the weighted value sums, the
 //    maxima and the weight sums.  The chunk holding the new token's slot
 //    takes that key and value from k_new / v_new and appends them.
-//  * merge phase: item (batch row, query head, 16 dimensions), spread over
-//    the workgroups; the control wave merges the valid chunks' partials of
+//  * merge phase: item (batch row, query head, 8 or 16 dimensions), spread
+//    over the workgroups; the control wave merges the valid chunks' partials of
 //    its head (lane i takes chunks i, i + 64, ...; then a wave reduction in a
 //    fixed order) and stores 16 BF16 outputs.
 // Both phases end with the usual completion flags, so the product that reads
@@ -207,7 +207,10 @@ struct DevPhase {
 constexpr int ATTN_D = 128;          // head dimension
 constexpr int ATTN_MAX_GROUP = 8;    // query heads per key/value head
 constexpr int ATTN_PASS = 16;        // slots one wave scores per pass (4 rows of 16 lanes x 4 loads)
-constexpr int ATTN_SLICE = 16;       // output dimensions per merge item
+// Output dimensions per merge item: 8 at batch 1 (192 items of the pages'
+// 12 query heads, one round of 256 workgroups, fewer wave reductions each),
+// else 16.
+constexpr int attn_slice(int batch) { return batch == 1 ? 8 : 16; }
 // Floats of one partial: acc[G][D], then m[G], then l[G]; padded to 16 bytes.
 WGN_HD int32_t attn_part_floats(int32_t G) { return (G * (ATTN_D + 2) + 3) & ~3; }
 // LDS of a scores phase: the combine of the four 16-lane rows of its wave
