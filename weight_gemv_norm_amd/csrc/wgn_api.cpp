@@ -455,7 +455,7 @@ DevAttn make_dev_attn(const wgn_attn_stage &s, int32_t B, int32_t G) {
     d.slots = s.slots;
     const int32_t pairs = B * s.kv_heads;
     const int32_t per = std::max(1, G / pairs);
-    d.nchunk = std::min(per, (s.slots + ATTN_PASS - 1) / ATTN_PASS);
+    d.nchunk = std::min(per, (s.slots + attn_pass(B) - 1) / attn_pass(B));
     d.scale_log2 = (float)((double)s.scale * 1.4426950408889634);  // log2(e)
     return d;
 }

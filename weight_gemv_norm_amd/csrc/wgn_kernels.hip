@@ -1415,9 +1415,10 @@ __device__ __forceinline__ int32_t attn_last(const DevAttn &A, int32_t b) {
 // Slots per chunk of a row whose last valid slot is last >= 0: its valid
 // length split over the row's nchunk partials, in whole passes (the same in
 // both phases, so the merge finds the chunks the scores phase filled).
+template <int PASS>
 __device__ __forceinline__ int32_t attn_chunk(const DevAttn &A, int32_t last) {
     const int32_t c = (last + A.nchunk) / A.nchunk;  // ceil((last + 1) / nchunk)
-    return (c + ATTN_PASS - 1) / ATTN_PASS * ATTN_PASS;
+    return (c + PASS - 1) / PASS * PASS;
 }
 
 // The scores item of this workgroup and the first pass of its cache rows,
@@ -1428,6 +1429,7 @@ __device__ __forceinline__ int32_t attn_chunk(const DevAttn &A, int32_t last) {
 // dimensions 8 col .. 8 col + 7; slots past the chunk or the last valid slot
 // re-read the last valid one (never beyond it) and get weight 0.  The new
 // token's slot is read here too and replaced after the wait.
+template <int NL>
 __device__ __forceinline__ void attn_prefetch(const DevAttn &A, int32_t nb, int32_t g, uint32_t lane, char *stage) {
     const int32_t r = (int32_t)(lane >> 4);
     const uint32_t lo = (lane & 15u) * 16u;
@@ -1436,12 +1438,12 @@ __device__ __forceinline__ void attn_prefetch(const DevAttn &A, int32_t nb, int3
     const int32_t pair = g / A.nchunk, c = g - pair * A.nchunk;
     const int32_t last = attn_last(A, pair / A.hkv);
     if (last < 0) return;  // no valid slot: nothing is scored
-    const int32_t t0 = c * attn_chunk(A, last);
+    const int32_t t0 = c * attn_chunk<4 * NL>(A, last);
     if (t0 > last) return;
     const char *kc = (const char *)(A.k_cache + (size_t)pair * A.slots * ATTN_D);
     const char *vc = (const char *)(A.v_cache + (size_t)pair * A.slots * ATTN_D);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NL; ++i) {
         const size_t off = (size_t)min(t0 + 4 * i + r, last) * ATTN_D * 2 + lo;
         __builtin_amdgcn_global_load_lds((const WGN_GAS void *)(kc + off), (WGN_LAS void *)(stage + i * 1024), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const WGN_GAS void *)(vc + off), (WGN_LAS void *)(stage + (4 + i) * 1024), 16, 0,
@@ -1455,6 +1457,7 @@ __device__ __forceinline__ void attn_prefetch(const DevAttn &A, int32_t nb, int3
 // the wave are combined through LDS (cmb: [row][head][D] FP32, then m and l
 // per (row, head)) in row order, and one partial is written: acc[G][D],
 // m[G], l[G].
+template <int NL>
 __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_t g, int32_t G, uint32_t lane,
                                             float *cmb, const char *stage) {
     const int32_t grp = A.hq / A.hkv, E = attn_part_floats(grp);
@@ -1466,7 +1469,7 @@ __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_
         const int32_t b = pair / A.hkv, kh = pair - b * A.hkv;
         const int32_t last = attn_last(A, b);
         if (last < 0) continue;  // no valid slot: the merge writes zeros
-        const int32_t chunk = attn_chunk(A, last);
+        const int32_t chunk = attn_chunk<4 * NL>(A, last);
         const int32_t t0 = c * chunk;
         if (t0 > last) continue;  // past the valid slots: the merge skips this chunk
         const int32_t t1 = min(t0 + chunk, last + 1);
@@ -1501,25 +1504,25 @@ __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
             }
-            for (int32_t t = t0; t < t1; t += ATTN_PASS) {
-                u32x4 kd[4], vd[4];
+            for (int32_t t = t0; t < t1; t += 4 * NL) {
+                u32x4 kd[NL], vd[NL];
                 if (it == g && t == t0) {
                     __builtin_amdgcn_s_waitcnt(0);  // the copies into stage have landed
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
+                    for (int i = 0; i < NL; ++i) {
                         kd[i] = *(const u32x4 *)(stage + i * 1024 + lane * 16);
                         vd[i] = *(const u32x4 *)(stage + (4 + i) * 1024 + lane * 16);
                     }
                 } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
+                    for (int i = 0; i < NL; ++i) {
                         const uint32_t sl = (uint32_t)min(t + 4 * i + r, last);
                         kd[i] = __builtin_amdgcn_raw_buffer_load_b128(rkc, (int)(sl * ATTN_D * 2u + lo), 0, 0);
                         vd[i] = __builtin_amdgcn_raw_buffer_load_b128(rvc, (int)(sl * ATTN_D * 2u + lo), 0, 0);
                     }
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < NL; ++i) {
                     if (min(t + 4 * i + r, last) == last) {  // the new token: from k_new / v_new
                         kd[i] = kn;
                         vd[i] = vn;
@@ -1528,18 +1531,18 @@ __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_
 #pragma unroll
                 for (int h = 0; h < HS; ++h) {
                     if (h0 + h >= grp) break;
-                    float sc[4], mx = m[h];
+                    float sc[NL], mx = m[h];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
+                    for (int i = 0; i < NL; ++i) {
                         const float sv = group_sum(dot8(kd[i], qv[h], 0.0f), 16) * A.scale_log2;
                         sc[i] = t + 4 * i + r < t1 ? sv : -INFINITY;
                         mx = fmaxf(mx, sc[i]);
                     }
                     if (mx != -INFINITY) {  // this row has seen a valid slot
                         const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);
-                        float pw[4], lw = 0.0f;
+                        float pw[NL], lw = 0.0f;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
+                        for (int i = 0; i < NL; ++i) {
                             pw[i] = __builtin_amdgcn_exp2f(sc[i] - mx);
                             lw += pw[i];
                         }
@@ -1548,7 +1551,7 @@ __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_
                         for (int j = 0; j < 4; ++j) {
                             float e0 = acc[h][2 * j] * alpha, e1 = acc[h][2 * j + 1] * alpha;
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
+                            for (int i = 0; i < NL; ++i) {
                                 const uint32_t vw = j == 0 ? vd[i].x : j == 1 ? vd[i].y : j == 2 ? vd[i].z : vd[i].w;
                                 e0 += pw[i] * bf2f(vw & 0xFFFFu);
                                 e1 += pw[i] * bf2f(vw >> 16);
@@ -1564,7 +1567,7 @@ __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_
                 // in this launch)
                 if (h0 == 0) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
+                    for (int i = 0; i < NL; ++i) {
                         if (t + 4 * i + r == last) {
                             __builtin_amdgcn_raw_buffer_store_b128(kd[i], rkc, (int)((uint32_t)last * ATTN_D * 2u + lo),
                                                                    0, 0);
@@ -1624,7 +1627,7 @@ __device__ __forceinline__ void attn_scores(const DevAttn &A, int32_t nb, int32_
 // order (running maximum), then the wave combines its lanes in a fixed order;
 // lanes 0 .. SL/2 - 1 store the SL BF16 outputs.  A row with no valid slot
 // gets 0.
-template <int SL>
+template <int SL, int PASS>
 __device__ __forceinline__ void attn_merge(const DevAttn &A, int32_t nb, int32_t g, int32_t G, uint32_t lane,
                                            int32_t last_g) {
     constexpr int NSL = ATTN_D / SL;
@@ -1635,33 +1638,47 @@ __device__ __forceinline__ void attn_merge(const DevAttn &A, int32_t nb, int32_t
         const int32_t hq = rem / NSL, ds = rem - hq * NSL;
         const int32_t kh = hq / grp, hi = hq - kh * grp, pair = b * A.hkv + kh;
         const int32_t last = it == g ? last_g : attn_last(A, b);
-        const int32_t nvalid = last < 0 ? 0 : last / attn_chunk(A, last) + 1;  // chunks holding a valid slot
+        const int32_t nvalid = last < 0 ? 0 : last / attn_chunk<PASS>(A, last) + 1;  // chunks holding a valid slot
         const __amdgpu_buffer_rsrc_t rp = rsrc_of(A.part + (size_t)pair * A.nchunk * E);
         float mm = -INFINITY, ll = 0.0f, aa[SL];
 #pragma unroll
         for (int j = 0; j < SL; ++j) aa[j] = 0.0f;
-        for (int32_t i = (int32_t)lane; i < nvalid; i += 64) {
-            const int32_t base = i * E;
-            const float mi = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (base + grp * ATTN_D + hi) * 4, 0, COH));
-            const float li =
-                __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (base + grp * ATTN_D + grp + hi) * 4, 0, COH));
-            u32x4 av[SL / 4];
+        for (int32_t i0 = (int32_t)lane; i0 < nvalid; i0 += 128) {
+            // the partials of chunks i0 and i0 + 64, both requested before
+            // either is folded (one round trip), folded in that order
+            float mi[2], li[2];
+            u32x4 av[2][SL / 4];
 #pragma unroll
-            for (int k = 0; k < SL / 4; ++k)
-                av[k] = __builtin_amdgcn_raw_buffer_load_b128(rp, (base + hi * ATTN_D + ds * SL + 4 * k) * 4, 0,
-                                                              COH);
-            const float M = fmaxf(mm, mi);
-            const float f0 = __builtin_amdgcn_exp2f(mm - M), f1 = __builtin_amdgcn_exp2f(mi - M);
-            ll = ll * f0 + li * f1;
+            for (int u = 0; u < 2; ++u) {
+                const bool ok = i0 + 64 * u < nvalid;
+                const int32_t base = (ok ? i0 + 64 * u : i0) * E;  // in range; unused when !ok
+                mi[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (base + grp * ATTN_D + hi) * 4, 0, COH));
+                li[u] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(rp, (base + grp * ATTN_D + grp + hi) * 4, 0, COH));
 #pragma unroll
-            for (int k = 0; k < SL / 4; ++k) {
-                const f32x4 v = __builtin_bit_cast(f32x4, av[k]);
-                aa[4 * k] = aa[4 * k] * f0 + v.x * f1;
-                aa[4 * k + 1] = aa[4 * k + 1] * f0 + v.y * f1;
-                aa[4 * k + 2] = aa[4 * k + 2] * f0 + v.z * f1;
-                aa[4 * k + 3] = aa[4 * k + 3] * f0 + v.w * f1;
+                for (int k = 0; k < SL / 4; ++k)
+                    av[u][k] = __builtin_amdgcn_raw_buffer_load_b128(rp, (base + hi * ATTN_D + ds * SL + 4 * k) * 4,
+                                                                     0, COH);
+                if (!ok) {
+                    mi[u] = -INFINITY;
+                    li[u] = 0.0f;
+                }
             }
-            mm = M;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const float M = fmaxf(mm, mi[u]);  // finite: chunk i0 is valid
+                const float f0 = __builtin_amdgcn_exp2f(mm - M), f1 = __builtin_amdgcn_exp2f(mi[u] - M);
+                ll = ll * f0 + li[u] * f1;
+#pragma unroll
+                for (int k = 0; k < SL / 4; ++k) {
+                    const f32x4 v = __builtin_bit_cast(f32x4, av[u][k]);
+                    aa[4 * k] = aa[4 * k] * f0 + v.x * f1;
+                    aa[4 * k + 1] = aa[4 * k + 1] * f0 + v.y * f1;
+                    aa[4 * k + 2] = aa[4 * k + 2] * f0 + v.z * f1;
+                    aa[4 * k + 3] = aa[4 * k + 3] * f0 + v.w * f1;
+                }
+                mm = M;
+            }
         }
         const float M = wave_max_bcast(mm);
         const float f = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mm - M);
@@ -1738,7 +1755,8 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
         if constexpr (ATT) {
             if (ph.att) {
                 const DevAttn A = attn_of(a, ph.att);
-                if (attn_is_scores(ph.att)) attn_prefetch(A, a.nb, g, lane, lds + ph.part_off + ATTN_STAGE_OFF);
+                if (attn_is_scores(ph.att))
+                    attn_prefetch<attn_pass(B) / 4>(A, a.nb, g, lane, lds + ph.part_off + ATTN_STAGE_OFF);
                 else if (g < a.nb * A.hq * (ATTN_D / attn_slice(B))) att_last = attn_last(A, g / (A.hq * (ATTN_D / attn_slice(B))));
             }
         }
@@ -1814,9 +1832,9 @@ __device__ __forceinline__ void control_wave(const KArgs &a, int32_t g, char *ld
         if constexpr (ATT) {
             if (ph.att) {
                 if (attn_is_scores(ph.att))
-                    attn_scores(attn_of(a, ph.att), a.nb, g, a.G, lane, (float *)(lds + ph.part_off),
+                    attn_scores<attn_pass(B) / 4>(attn_of(a, ph.att), a.nb, g, a.G, lane, (float *)(lds + ph.part_off),
                                 lds + ph.part_off + ATTN_STAGE_OFF);
-                else attn_merge<attn_slice(B)>(attn_of(a, ph.att), a.nb, g, a.G, lane, att_last);
+                else attn_merge<attn_slice(B), attn_pass(B)>(attn_of(a, ph.att), a.nb, g, a.G, lane, att_last);
                 // The phase streams no weights, but its empty blocks still
                 // read x-hat (and multiply it by zero weights): zeros, not
                 // whatever an earlier phase left in LDS, which read as BF16

@@ -206,7 +206,10 @@ struct DevPhase {
 // `out` waits for the merge like for any earlier phase.
 constexpr int ATTN_D = 128;          // head dimension
 constexpr int ATTN_MAX_GROUP = 8;    // query heads per key/value head
-constexpr int ATTN_PASS = 16;        // slots one wave scores per pass (4 rows of 16 lanes x 4 loads)
+// Slots one wave scores per pass (4 rows of 16 lanes x pass / 4 loads): 8 at
+// batch 1 (about twice the chunks, so nearly every workgroup holds a scores
+// item, each with half the arithmetic), else 16.
+constexpr int attn_pass(int batch) { return batch == 1 ? 8 : 16; }
 // Output dimensions per merge item: 8 at batch 1 (192 items of the pages'
 // 12 query heads, one round of 256 workgroups, fewer wave reductions each),
 // else 16.
