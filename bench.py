@@ -55,8 +55,9 @@ def parse():
                     help="with --mode 1: tune an Infinity-Cache prefetch plan (touch passes on a second "
                          "stream, wgn_plan_tune) before timing, and time the plan it keeps")
     ap.add_argument("--tune-reps", type=int, default=15, help="rounds of the prefetch tuner")
-    ap.add_argument("--attn", default="fused", choices=["fused", "launches"],
-                    help="decode_step_attn: attention as phases of the one chain launch, or launches of its own")
+    ap.add_argument("--attn", default="auto", choices=["auto", "fused", "launches"],
+                    help="decode_step_attn: attention as phases of the one chain launch, launches of its own, "
+                         "or the faster of the two by batch and cache size")
     ap.add_argument("--ring", type=int, default=0, help="decode_step_attn: streaming ring (0 auto, 1..3)")
     ap.add_argument("--slots", type=int, default=None,
                     help="decode-attention workload: cache slots (all valid: the new token takes the last; default 32768); "
@@ -138,7 +139,8 @@ def main():
                                      vocab=args.vocab)
         n_layers = len(inp["layers"])
         caches = gen.make_kv_caches(B, S, [pos] * B, n_layers=n_layers, nan_tail=False, device=dev)
-        dstep = steps.DecodeStepWithAttention(inp, caches, dev, mode=args.mode, fused=args.attn == "fused",
+        dstep = steps.DecodeStepWithAttention(inp, caches, dev, mode=args.mode,
+                                              fused={"auto": None, "fused": True, "launches": False}[args.attn],
                                               ring=args.ring)
         nb = steps.decode_step_bytes(inp)
         kv = n_layers * (2 * B * gen.NKV * (pos + 1) * gen.HEAD_DIM * 2 + 2 * 2 * B * gen.NKV * gen.HEAD_DIM * 2)

@@ -20,7 +20,7 @@ on a laptop GPU", section "Beyond language models".
 """
 from __future__ import annotations
 
-from typing import Dict, List
+from typing import Dict, List, Optional
 
 import torch
 
@@ -78,9 +78,15 @@ class DecodeStepWithAttention:
     and down ("One Token, Kernel by Kernel", sections "What one block
     launches" and "The fix: Part 10's split-KV kernel").
 
-    fused=True (default): one chain, one persistent launch per step; each
-    layer's attention runs inside it as two phases without weights
+    fused=True: one chain, one persistent launch per step; each layer's
+    attention runs inside it as two phases without weights
     (wgn_chain_create_attn), between {Q, K, V} and {O}.
+    fused=None (default): the faster of the two as measured on MI355X with
+    the pages' shapes -- one launch at batch 1-2 (1,386 / 1,525 us against
+    1,538 / 1,539 with 1,024-slot caches) and for long caches (32,768 slots,
+    batch 4: 1,900 against 2,139 us); attention launches from batch 3 with
+    caches of at most 4,096 slots (1,024 slots: 1,603 / 1,739 against 1,693
+    / 1,839 us; the 4,096-slot bound itself was not measured).
     fused=False: one chain {Q, K, V of layer 0}; then per layer one
     wgn_decode_attention launch and one chain {O, gate/up, down, and the next
     layer's Q, K, V} (the last chain ends with the final norm, LM head and
@@ -88,7 +94,7 @@ class DecodeStepWithAttention:
     Buffers: q/k/v/a/h1/s/h per layer as in decoder_stages, with a [B][Hq*D]
     the attention output that feeds O."""
 
-    def __init__(self, inp: Dict, caches: List[Dict], device, mode: int = 0, fused: bool = True,
+    def __init__(self, inp: Dict, caches: List[Dict], device, mode: int = 0, fused: Optional[bool] = None,
                  ring: int = 0):
         from . import api as W
         B = inp["batch"]
@@ -122,6 +128,8 @@ class DecodeStepWithAttention:
                                maxval=mx)]
             bufs["idx"], bufs["maxval"] = idx, mx
         self.bufs = bufs
+        if fused is None:
+            fused = B <= 2 or max(c["k_cache"].shape[2] for c in caches) > 4096
         self.fused = fused
         hd = 128  # head dimension of the attention kernel
         NQ, NKV = layers[0]["wq"].shape[0] // hd, layers[0]["wk"].shape[0] // hd
